@@ -1,0 +1,146 @@
+"""CPU oracle for the KDA / CKDA recurrence — TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The HIP library never imports, links or
+falls back to it, and this package imports nothing from the HIP library.
+
+The arithmetic lives in ``kda_oracle.c`` (plain C, fp64 state and sums), which
+follows "Semidirect Fourier Delta Attention" (arXiv 2607.11897) §1 eq. (1) for
+the state update and §3 eq. (14) for the read-out, with the Complex-KDA ranges
+of "Complex KDA: Understanding and Enhancing the Expressivity of Kimi Delta
+Attention" (the abstract).  This module only marshals numpy arrays.
+
+Pins: tests/test_oracle_pins.py fixes this oracle against the pages' worked
+numbers, closed forms (Householder, rotation, beta = 0), invariants
+(non-expansiveness, linearity in the initial state, chunked = sequential) and a
+dense brute-force product of per-token affine maps on tiny inputs.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libkda_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True, cwd=_HERE)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB_PATH)
+        fp = ctypes.POINTER(ctypes.c_float)
+        dp = ctypes.POINTER(ctypes.c_double)
+        i = ctypes.c_int
+        lib.kda_oracle_forward.argtypes = [fp, fp, fp, fp, fp, fp, dp, dp,
+                                           i, i, i, i, i, i]
+        lib.kda_oracle_forward.restype = i
+        lib.kda_oracle_decode.argtypes = [fp, fp, fp, fp, fp, dp, dp,
+                                          i, i, i, i, i, i]
+        lib.kda_oracle_decode.restype = i
+        lib.kda_oracle_gate_prep.argtypes = [
+            fp, dp, ctypes.POINTER(ctypes.c_ubyte), ctypes.POINTER(ctypes.c_int),
+            dp, i, i, i, i, i]
+        lib.kda_oracle_gate_prep.restype = i
+        _lib = lib
+    return _lib
+
+
+def _f32(x):
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+
+
+def _ptr(a, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype)) if a is not None else None
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def forward(q, k, v, alpha, beta, S0=None, nthreads: int | None = None):
+    """Token-by-token forward.  q, k, alpha: [B,T,H,Dk]; v: [B,T,H,Dv];
+    beta: [B,T,H]; S0: [B,H,Dk,Dv] or None (zero).  Inputs are taken as float32
+    (exact for bf16 and fp32 values).  Returns (out [B,T,H,Dv], ST [B,H,Dk,Dv])
+    in float64."""
+    lib = _load()
+    q, k, v, alpha, beta = (_f32(x) for x in (q, k, v, alpha, beta))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    assert k.shape == (B, T, H, Dk) and alpha.shape == (B, T, H, Dk)
+    assert v.shape == (B, T, H, Dv) and beta.shape == (B, T, H)
+    s0 = None if S0 is None else _f32(S0)
+    if s0 is not None:
+        assert s0.shape == (B, H, Dk, Dv)
+    out = np.empty((B, T, H, Dv), dtype=np.float64)
+    ST = np.empty((B, H, Dk, Dv), dtype=np.float64)
+    rc = lib.kda_oracle_forward(
+        _ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float),
+        _ptr(alpha, ctypes.c_float), _ptr(beta, ctypes.c_float),
+        _ptr(s0, ctypes.c_float), _ptr(out, ctypes.c_double), _ptr(ST, ctypes.c_double),
+        B, T, H, Dk, Dv, nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError("kda_oracle_forward failed")
+    return out, ST
+
+
+def decode(q, k, v, alpha, beta, S, nthreads: int | None = None):
+    """nsteps single-token updates.  q, k, alpha: [N,B,H,Dk]; v: [N,B,H,Dv];
+    beta: [N,B,H]; S: [B,H,Dk,Dv] initial state (not modified).
+    Returns (out [N,B,H,Dv], S_final [B,H,Dk,Dv]) in float64."""
+    lib = _load()
+    q, k, v, alpha, beta = (_f32(x) for x in (q, k, v, alpha, beta))
+    N, B, H, Dk = q.shape
+    Dv = v.shape[-1]
+    assert v.shape == (N, B, H, Dv) and beta.shape == (N, B, H)
+    Sd = np.array(S, dtype=np.float64, copy=True, order="C")
+    assert Sd.shape == (B, H, Dk, Dv)
+    out = np.empty((N, B, H, Dv), dtype=np.float64)
+    rc = lib.kda_oracle_decode(
+        _ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float),
+        _ptr(alpha, ctypes.c_float), _ptr(beta, ctypes.c_float),
+        _ptr(Sd, ctypes.c_double), _ptr(out, ctypes.c_double),
+        N, B, H, Dk, Dv, nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError("kda_oracle_decode failed")
+    return out, Sd
+
+
+def gate_prep(alpha, chunk: int):
+    """Chunk-local gate summary (see kda_oracle.h).  alpha: [B,T,H,Dk].
+    Returns dict with L (float64), parity (uint8), zpos (int32) of shape
+    [B,H,NC,C,Dk] and gend (float64) [B,H,NC,Dk]."""
+    lib = _load()
+    a = _f32(alpha)
+    B, T, H, Dk = a.shape
+    NC = (T + chunk - 1) // chunk
+    L = np.zeros((B, H, NC, chunk, Dk), dtype=np.float64)
+    par = np.zeros((B, H, NC, chunk, Dk), dtype=np.uint8)
+    zp = np.zeros((B, H, NC, chunk, Dk), dtype=np.int32)
+    ge = np.zeros((B, H, NC, Dk), dtype=np.float64)
+    rc = lib.kda_oracle_gate_prep(
+        _ptr(a, ctypes.c_float), _ptr(L, ctypes.c_double), _ptr(par, ctypes.c_ubyte),
+        _ptr(zp, ctypes.c_int), _ptr(ge, ctypes.c_double), B, T, H, Dk, chunk)
+    if rc != 0:
+        raise RuntimeError("kda_oracle_gate_prep failed")
+    return {"L": L, "parity": par, "zpos": zp, "gend": ge}

@@ -1,0 +1,66 @@
+/*
+ * kda_oracle.h — CPU oracle for the Kimi Delta Attention (KDA) recurrence and
+ * its Complex-KDA (CKDA) range extension.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library.  It shares no source
+ * with the HIP library and must never be used as a fallback for it.
+ *
+ * What it computes (plain definitions, fp64 state and accumulation):
+ *   S_t = (I - beta_t k_t k_t^T) diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *       — "Semidirect Fourier Delta Attention" (arXiv 2607.11897), §1 eq. (1),
+ *         restated per token as an affine map in §2.2 eq. (9);
+ *   o_t = S_t^T q_t  (post-update state, no scale factor)
+ *       — same page, §3 eq. (14) (SFDA reduces to KDA at zero phase, Prop. 2.1).
+ * Range extension (alpha in [-1,1], beta in [0,2]) — "Complex KDA: Understanding
+ * and Enhancing the Expressivity of Kimi Delta Attention", the abstract.  The
+ * mathematics is the same for both ranges; the oracle takes any real inputs.
+ *
+ * Layouts (all row-major, contiguous):
+ *   q, k, alpha : [B, T, H, Dk]      v : [B, T, H, Dv]      beta : [B, T, H]
+ *   S0, ST      : [B, H, Dk, Dv]     out : [B, T, H, Dv]
+ * Inputs are float (bf16 and fp32 values widen to double exactly); the state
+ * and every accumulation are double; outputs are double.
+ *
+ * Return value: 0 on success, -1 on a bad argument (null pointer or size < 0).
+ */
+#ifndef KDA_ORACLE_H
+#define KDA_ORACLE_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Sequential token-by-token forward over T tokens.  S0 may be NULL (zero
+ * initial state); ST may be NULL (final state not wanted).  nthreads <= 0 uses
+ * the OpenMP default.  Parallelism is over independent (b, h) pairs only. */
+int kda_oracle_forward(const float* q, const float* k, const float* v,
+                       const float* alpha, const float* beta, const float* S0,
+                       double* out, double* ST,
+                       int B, int T, int H, int Dk, int Dv, int nthreads);
+
+/* nsteps single-token updates applied to a resident double state in place.
+ * Per-step inputs are stacked: q, k, alpha [nsteps, B, H, Dk],
+ * v [nsteps, B, H, Dv], beta [nsteps, B, H]; out [nsteps, B, H, Dv];
+ * S [B, H, Dk, Dv] (double, read and written). */
+int kda_oracle_decode(const float* q, const float* k, const float* v,
+                      const float* alpha, const float* beta, double* S,
+                      double* out, int nsteps, int B, int H, int Dk, int Dv,
+                      int nthreads);
+
+/* Chunk-local gate summary, from its definition, per (b, h, chunk n, local
+ * token r, channel c) with chunk length C (last chunk may be short):
+ *   L[.]      = sum over j <= r in the chunk with alpha_j != 0 of log2|alpha_j|
+ *   parity[.] = (number of j <= r in the chunk with alpha_j < 0) mod 2
+ *   zpos[.]   = 1 + (largest j <= r in the chunk with alpha_j == 0), 0 if none
+ *   gend[b,h,n,c] = product of alpha over the whole chunk (plain product)
+ * L, parity, zpos : [B, H, NC, C, Dk] (entries past T are left untouched);
+ * gend : [B, H, NC, Dk];  NC = ceil(T / C). */
+int kda_oracle_gate_prep(const float* alpha, double* L, unsigned char* parity,
+                         int* zpos, double* gend, int B, int T, int H, int Dk,
+                         int C);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
