@@ -1,0 +1,176 @@
+"""gated_delta_rule_forward_amd — KDA / CKDA recurrence on AMD MI355X (gfx950).
+
+Thin ctypes binding over libkda.so (C ABI in include/kda.h).  This module only
+marshals arguments: it passes tensor data pointers, sizes and the current HIP
+stream to the library, and allocates outputs / workspace with torch when the
+caller does not supply them.  Every step of the computation runs in the HIP
+kernels; there is no fallback.  If libkda.so is missing the first call raises.
+
+Recurrence ("Semidirect Fourier Delta Attention", §1 eq. (1), §3 eq. (14)):
+    S_t = (I - beta_t k_t k_t^T) diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+    o_t = S_t^T q_t
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "KDA", "CKDA", "KdaError", "library_path", "load", "abi_version", "workspace_size",
+    "chunk_forward", "decode_step", "gate_prep", "last_stage_times", "STAGE_EVENTS",
+]
+
+KDA, CKDA = 0, 1
+STAGE_EVENTS = 2
+_DT = {torch.float32: 0, torch.bfloat16: 1}
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libkda.so")
+_lib = None
+
+_STATUS = {0: "ok", 1: "null pointer", 2: "bad shape", 3: "unsupported", 4: "misaligned",
+           5: "workspace too small", 6: "alias", 7: "hip error"}
+
+
+class KdaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: status {status} ({_STATUS.get(status, 'unknown')})")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libkda.so (built by gated_delta_rule_forward_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"libkda.so not built ({_LIB_PATH}); run "
+                           "`python -m gated_delta_rule_forward_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i, u, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_size_t
+    lib.kda_abi_version.restype = i
+    lib.kda_status_string.argtypes = [i]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_chunk_forward_workspace_size.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(sz)]
+    lib.kda_chunk_forward_workspace_size.restype = i
+    lib.kda_chunk_forward.argtypes = [vp] * 8 + [i] * 8 + [u, vp, sz, vp]
+    lib.kda_chunk_forward.restype = i
+    lib.kda_decode_step.argtypes = [vp] * 7 + [i] * 6 + [u, vp]
+    lib.kda_decode_step.restype = i
+    lib.kda_gate_prep.argtypes = [vp] * 4 + [i] * 5 + [vp]
+    lib.kda_gate_prep.restype = i
+    lib.kda_last_stage_times.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                         ctypes.POINTER(ctypes.c_char_p), i, ctypes.POINTER(i)]
+    lib.kda_last_stage_times.restype = i
+    _lib = lib
+    return lib
+
+
+def abi_version() -> int:
+    return load().kda_abi_version()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise KdaError(fn, status)
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("all tensors must be on the GPU")
+            if not t.is_contiguous():
+                raise ValueError("all tensors must be contiguous")
+
+
+def workspace_size(B: int, T: int, H: int, Dk: int, Dv: int, chunk: int, dtype: torch.dtype) -> int:
+    n = ctypes.c_size_t(0)
+    _check("kda_chunk_forward_workspace_size",
+           load().kda_chunk_forward_workspace_size(B, T, H, Dk, Dv, chunk, _DT[dtype],
+                                                   ctypes.byref(n)))
+    return n.value
+
+
+def chunk_forward(q, k, v, alpha, beta, initial_state=None, *, chunk: int = 64, mode: int = CKDA,
+                  out=None, final_state=None, output_final_state: bool = True, workspace=None,
+                  stream=None, flags: int = 0):
+    """Chunked forward.  q, k: [B,T,H,Dk]; v: [B,T,H,Dv] (fp32 or bf16, same dtype);
+    alpha: [B,T,H,Dk] fp32; beta: [B,T,H] fp32; initial_state: [B,H,Dk,Dv] fp32 or None.
+    Returns (out [B,T,H,Dv], final_state [B,H,Dk,Dv] fp32 or None)."""
+    lib = load()
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if out is None:
+        out = torch.empty((B, T, H, Dv), dtype=q.dtype, device=q.device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = workspace_size(B, T, H, Dk, Dv, chunk, q.dtype)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _dev(q, k, v, alpha, beta, initial_state, out, final_state, workspace)
+    if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype or out.dtype != q.dtype:
+        raise ValueError("q, k, v and out must share one dtype (float32 or bfloat16)")
+    st = lib.kda_chunk_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                               _ptr(initial_state), _ptr(out), _ptr(final_state),
+                               B, T, H, Dk, Dv, chunk, _DT[q.dtype], mode, flags,
+                               _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               _stream(stream))
+    _check("kda_chunk_forward", st)
+    return out, final_state
+
+
+def decode_step(q, k, v, alpha, beta, state, *, out=None, mode: int = CKDA, stream=None,
+                flags: int = 0):
+    """One token for every (b, h): q, k: [B,H,Dk]; v: [B,H,Dv]; alpha: [B,H,Dk] fp32;
+    beta: [B,H] fp32; state: [B,H,Dk,Dv] fp32, updated in place.  Returns out [B,H,Dv]."""
+    lib = load()
+    B, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if out is None:
+        out = torch.empty((B, H, Dv), dtype=q.dtype, device=q.device)
+    _dev(q, k, v, alpha, beta, state, out)
+    st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state),
+                             _ptr(out), B, H, Dk, Dv, _DT[q.dtype], mode, flags, _stream(stream))
+    _check("kda_decode_step", st)
+    return out
+
+
+def gate_prep(alpha, chunk: int, *, stream=None):
+    """Chunk-local gate summary of alpha [B,T,H,Dk] fp32.  Returns (L [B,H,NC,C,Dk] fp32,
+    meta [B,H,NC,C,Dk] uint8 = zpos << 1 | parity, gend [B,H,NC,Dk] fp32)."""
+    lib = load()
+    B, T, H, Dk = alpha.shape
+    NC = (T + chunk - 1) // chunk
+    L = torch.empty((B, H, NC, chunk, Dk), dtype=torch.float32, device=alpha.device)
+    meta = torch.empty((B, H, NC, chunk, Dk), dtype=torch.uint8, device=alpha.device)
+    gend = torch.empty((B, H, NC, Dk), dtype=torch.float32, device=alpha.device)
+    _dev(alpha, L, meta, gend)
+    _check("kda_gate_prep", lib.kda_gate_prep(_ptr(alpha), _ptr(L), _ptr(meta), _ptr(gend),
+                                              B, T, H, Dk, chunk, _stream(stream)))
+    return L, meta, gend
+
+
+def last_stage_times():
+    """[(kernel name, ms)] of the last call made with flags=STAGE_EVENTS."""
+    lib = load()
+    ms = (ctypes.c_float * 8)()
+    names = (ctypes.c_char_p * 8)()
+    n = ctypes.c_int(0)
+    _check("kda_last_stage_times", lib.kda_last_stage_times(ms, names, 8, ctypes.byref(n)))
+    return [(names[i].decode(), float(ms[i])) for i in range(min(n.value, 8))]

@@ -1,0 +1,303 @@
+// kda_api.hip — the C ABI declared in include/kda.h.
+//
+// Every entry point validates all of its arguments before making any HIP call,
+// then only enqueues kernels on the caller's stream (no allocation, no
+// synchronisation).  Per-kernel HIP events are recorded only when the caller
+// passes KDA_FLAG_STAGE_EVENTS.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/kda.h"
+#include "kda_launch.hpp"
+
+namespace {
+
+using kda::ChunkShape;
+using kda::ChunkWorkspace;
+using kda::IoType;
+
+constexpr unsigned kKnownFlags = KDA_FLAG_STAGE_EVENTS;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+bool aligned16(const void* p) { return aligned(p, 16); }
+
+bool dk_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool dv_ok(int d) { return d >= 16 && d <= 128 && d % 16 == 0; }
+bool chunk_ok(int c) { return c == 16 || c == 32 || c == 64; }
+
+size_t elem_size(kda_dtype_t t) { return t == KDA_DTYPE_F32 ? 4 : 2; }
+
+// [p, p + n) and [q, q + m) intersect (n, m in bytes; empty ranges never do)
+bool overlaps(const void* p, size_t n, const void* q, size_t m)
+{
+    if (!p || !q || n == 0 || m == 0) return false;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+    return a < b + m && b < a + n;
+}
+
+// ---- per-kernel events (opt-in) ---------------------------------------------
+constexpr int kMaxStages = 8;
+struct StageEvents {
+    std::mutex mu;
+    hipEvent_t ev[kMaxStages + 1] = {};
+    const char* names[kMaxStages] = {};
+    int count = 0;
+    bool created = false;
+};
+StageEvents g_stage;
+
+hipError_t stage_begin()
+{
+    if (!g_stage.created) {
+        for (int i = 0; i <= kMaxStages; ++i) {
+            const hipError_t e = hipEventCreate(&g_stage.ev[i]);
+            if (e != hipSuccess) return e;
+        }
+        g_stage.created = true;
+    }
+    g_stage.count = 0;
+    return hipSuccess;
+}
+
+struct Recorder {
+    bool on;
+    hipStream_t stream;
+    hipError_t mark(const char* name_of_next)   // event before a kernel
+    {
+        if (!on) return hipSuccess;
+        if (g_stage.count >= kMaxStages) return hipErrorInvalidValue;
+        g_stage.names[g_stage.count] = name_of_next;
+        return hipEventRecord(g_stage.ev[g_stage.count], stream);
+    }
+    hipError_t done()   // event after that kernel
+    {
+        if (!on) return hipSuccess;
+        g_stage.count += 1;
+        return hipEventRecord(g_stage.ev[g_stage.count], stream);
+    }
+};
+
+// fields shared by the forward and its workspace query
+kda_status_t check_forward_shape(int B, int T, int H, int Dk, int Dv, int chunk,
+                                 kda_dtype_t dtype)
+{
+    if (B < 1 || H < 1 || T < 0) return KDA_ERR_BAD_SHAPE;
+    if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERR_UNSUPPORTED;
+    if (!dk_ok(Dk) || !dv_ok(Dv) || !chunk_ok(chunk)) return KDA_ERR_UNSUPPORTED;
+    if (dtype == KDA_DTYPE_F32 && (Dk > 64 || Dv > 64)) return KDA_ERR_UNSUPPORTED;
+    const long long NC = ((long long)T + chunk - 1) / chunk;
+    const long long units = (long long)B * H * NC;
+    if (units > 0x7fffffffLL || (long long)B * H * (Dv / 16) > 0x7fffffffLL)
+        return KDA_ERR_BAD_SHAPE;
+    const long long tok = (long long)B * T * H;
+    if (tok * (Dk > Dv ? Dk : Dv) > (1LL << 46)) return KDA_ERR_BAD_SHAPE;
+    return KDA_OK;
+}
+
+ChunkShape make_shape(int B, int T, int H, int Dk, int Dv, int chunk)
+{
+    return ChunkShape{B, T, H, Dk, Dv, chunk, (T + chunk - 1) / chunk};
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_status_string(int s)
+{
+    switch (s) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case KDA_ERR_BAD_SHAPE: return "a size is out of range or overflows";
+    case KDA_ERR_UNSUPPORTED: return "unsupported shape, dtype, mode or flag";
+    case KDA_ERR_MISALIGNED: return "a pointer breaks the alignment rule";
+    case KDA_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than kda_chunk_forward_workspace_size";
+    case KDA_ERR_ALIAS: return "an output overlaps an input";
+    case KDA_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+kda_status_t kda_chunk_forward_workspace_size(int B, int T, int H, int Dk, int Dv, int chunk,
+                                              kda_dtype_t dtype, size_t* bytes)
+{
+    if (!bytes) return KDA_ERR_NULL_POINTER;
+    const kda_status_t st = check_forward_shape(B, T, H, Dk, Dv, chunk, dtype);
+    if (st != KDA_OK) return st;
+    size_t off[6];
+    *bytes = T == 0 ? 0
+                    : kda::chunk_workspace_layout(make_shape(B, T, H, Dk, Dv, chunk),
+                                                  dtype == KDA_DTYPE_F32 ? IoType::F32 : IoType::BF16, off);
+    return KDA_OK;
+}
+
+kda_status_t kda_chunk_forward(const void* q, const void* k, const void* v, const float* alpha,
+                               const float* beta, const float* initial_state, void* out,
+                               float* final_state, int B, int T, int H, int Dk, int Dv, int chunk,
+                               kda_dtype_t dtype, kda_mode_t mode, unsigned flags, void* workspace,
+                               size_t workspace_bytes, void* stream)
+{
+    kda_status_t st = check_forward_shape(B, T, H, Dk, Dv, chunk, dtype);
+    if (st != KDA_OK) return st;
+    if (mode != KDA_MODE_KDA && mode != KDA_MODE_CKDA) return KDA_ERR_UNSUPPORTED;
+    if (flags & ~kKnownFlags) return KDA_ERR_UNSUPPORTED;
+    if (T > 0 && (!q || !k || !v || !alpha || !beta || !out)) return KDA_ERR_NULL_POINTER;
+
+    const size_t e = elem_size(dtype);
+    const size_t ntok = (size_t)B * T * H;
+    const size_t nstate = (size_t)B * H * Dk * Dv * 4;
+    size_t ws_need = 0;
+    kda_chunk_forward_workspace_size(B, T, H, Dk, Dv, chunk, dtype, &ws_need);
+    if (T > 0 && !workspace) return KDA_ERR_NULL_POINTER;
+    if (workspace_bytes < ws_need) return KDA_ERR_WORKSPACE_TOO_SMALL;
+
+    // q, k, alpha and the workspace are read with 16-byte vector loads; the rest
+    // element by element
+    const void* vec[] = {q, k, alpha, workspace};
+    for (const void* p : vec)
+        if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
+    const void* elt[] = {v, out, beta, initial_state, final_state};
+    const uintptr_t ea[] = {e, e, 4, 4, 4};
+    for (int i = 0; i < 5; ++i)
+        if (elt[i] && !aligned(elt[i], ea[i])) return KDA_ERR_MISALIGNED;
+
+    // aliasing: out and workspace overlap nothing; final_state may equal
+    // initial_state exactly but overlap nothing else
+    struct R { const void* p; size_t n; } in[] = {
+        {q, ntok * Dk * e}, {k, ntok * Dk * e}, {v, ntok * Dv * e},
+        {alpha, ntok * Dk * 4}, {beta, ntok * 4}, {initial_state, initial_state ? nstate : 0}};
+    const R outs[] = {{out, ntok * Dv * e}, {workspace, ws_need}};
+    for (const R& o : outs)
+        for (const R& i : in)
+            if (overlaps(o.p, o.n, i.p, i.n)) return KDA_ERR_ALIAS;
+    if (overlaps(out, ntok * Dv * e, workspace, ws_need)) return KDA_ERR_ALIAS;
+    if (final_state) {
+        const R fs{final_state, nstate};
+        for (const R& i : in) {
+            if (i.p == initial_state && final_state == initial_state) continue;
+            if (overlaps(fs.p, fs.n, i.p, i.n)) return KDA_ERR_ALIAS;
+        }
+        for (const R& o : outs)
+            if (overlaps(fs.p, fs.n, o.p, o.n)) return KDA_ERR_ALIAS;
+    }
+
+    // ---- validated: enqueue ------------------------------------------------------
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    std::unique_lock<std::mutex> lock(g_stage.mu, std::defer_lock);
+    Recorder rec{(flags & KDA_FLAG_STAGE_EVENTS) != 0, s};
+    if (rec.on) {
+        lock.lock();
+        if (stage_begin() != hipSuccess) return KDA_ERR_HIP;
+    }
+    if (T == 0) {
+        if (!final_state || final_state == initial_state) return KDA_OK;
+        if (rec.mark("state_copy") != hipSuccess) return KDA_ERR_HIP;
+        if (kda::launch_state_copy(initial_state, final_state, nstate / 4, s) != hipSuccess)
+            return KDA_ERR_HIP;
+        return rec.done() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    }
+
+    const ChunkShape sh = make_shape(B, T, H, Dk, Dv, chunk);
+    const IoType io = dtype == KDA_DTYPE_F32 ? IoType::F32 : IoType::BF16;
+    size_t off[6];
+    kda::chunk_workspace_layout(sh, io, off);
+    unsigned char* w = static_cast<unsigned char*>(workspace);
+    const ChunkWorkspace ws{w + off[0], reinterpret_cast<float*>(w + off[1]), w + off[2],
+                            w + off[3], w + off[4], reinterpret_cast<float*>(w + off[5])};
+
+    if (rec.mark("chunk_prep") != hipSuccess) return KDA_ERR_HIP;
+    if (kda::launch_chunk_prep(io, sh, q, k, v, alpha, beta, ws, s) != hipSuccess) return KDA_ERR_HIP;
+    if (rec.done() != hipSuccess) return KDA_ERR_HIP;
+    if (rec.mark("chunk_chain") != hipSuccess) return KDA_ERR_HIP;
+    if (kda::launch_chunk_chain(io, sh, ws, initial_state, out, final_state, s) != hipSuccess)
+        return KDA_ERR_HIP;
+    if (rec.done() != hipSuccess) return KDA_ERR_HIP;
+    return KDA_OK;
+}
+
+kda_status_t kda_decode_step(const void* q, const void* k, const void* v, const float* alpha,
+                             const float* beta, float* state, void* out, int B, int H, int Dk,
+                             int Dv, kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
+                             void* stream)
+{
+    if (B < 1 || H < 1) return KDA_ERR_BAD_SHAPE;
+    if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERR_UNSUPPORTED;
+    if (!dk_ok(Dk) || !dv_ok(Dv)) return KDA_ERR_UNSUPPORTED;
+    if (mode != KDA_MODE_KDA && mode != KDA_MODE_CKDA) return KDA_ERR_UNSUPPORTED;
+    if (flags & ~kKnownFlags) return KDA_ERR_UNSUPPORTED;
+    if ((long long)B * H > 0x7fffffffLL) return KDA_ERR_BAD_SHAPE;
+    if (!q || !k || !v || !alpha || !beta || !state || !out) return KDA_ERR_NULL_POINTER;
+    const size_t e = elem_size(dtype), nbh = (size_t)B * H;
+    // the state is streamed with 16-byte vectors; everything else element-wise
+    if (!aligned16(state)) return KDA_ERR_MISALIGNED;
+    const void* elt[] = {q, k, v, out, alpha, beta};
+    const uintptr_t ea[] = {e, e, e, e, 4, 4};
+    for (int i = 0; i < 6; ++i)
+        if (!aligned(elt[i], ea[i])) return KDA_ERR_MISALIGNED;
+    struct R { const void* p; size_t n; } in[] = {
+        {q, nbh * Dk * e}, {k, nbh * Dk * e}, {v, nbh * Dv * e}, {alpha, nbh * Dk * 4}, {beta, nbh * 4}};
+    const R st{state, nbh * Dk * Dv * 4}, o{out, nbh * Dv * e};
+    for (const R& i : in)
+        if (overlaps(st.p, st.n, i.p, i.n) || overlaps(o.p, o.n, i.p, i.n)) return KDA_ERR_ALIAS;
+    if (overlaps(st.p, st.n, o.p, o.n)) return KDA_ERR_ALIAS;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    std::unique_lock<std::mutex> lock(g_stage.mu, std::defer_lock);
+    Recorder rec{(flags & KDA_FLAG_STAGE_EVENTS) != 0, s};
+    if (rec.on) {
+        lock.lock();
+        if (stage_begin() != hipSuccess) return KDA_ERR_HIP;
+    }
+    if (rec.mark("decode") != hipSuccess) return KDA_ERR_HIP;
+    if (kda::launch_decode(dtype == KDA_DTYPE_F32 ? IoType::F32 : IoType::BF16, B, H, Dk, Dv, q, k,
+                           v, alpha, beta, state, out, s) != hipSuccess)
+        return KDA_ERR_HIP;
+    return rec.done() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status_t kda_gate_prep(const float* alpha, float* L, unsigned char* meta, float* gend, int B,
+                           int T, int H, int Dk, int chunk, void* stream)
+{
+    if (B < 1 || H < 1 || T < 0) return KDA_ERR_BAD_SHAPE;
+    if (!dk_ok(Dk) || !chunk_ok(chunk)) return KDA_ERR_UNSUPPORTED;
+    const long long NC = ((long long)T + chunk - 1) / chunk;
+    if ((long long)B * H * NC > 0x7fffffffLL) return KDA_ERR_BAD_SHAPE;
+    if (T == 0) return KDA_OK;
+    if (!alpha || !L || !meta || !gend) return KDA_ERR_NULL_POINTER;
+    if (!aligned(alpha, 4) || !aligned(L, 4) || !aligned(gend, 4)) return KDA_ERR_MISALIGNED;
+    const size_t nel = (size_t)B * H * NC * chunk * Dk;
+    const size_t na = (size_t)B * T * H * Dk * 4;
+    struct R { const void* p; size_t n; } rs[] = {
+        {alpha, na}, {L, nel * 4}, {meta, nel}, {gend, (size_t)B * H * NC * Dk * 4}};
+    for (int i = 0; i < 4; ++i)
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(rs[i].p, rs[i].n, rs[j].p, rs[j].n)) return KDA_ERR_ALIAS;
+    if (kda::launch_gate_prep(alpha, L, meta, gend, B, T, H, Dk, chunk,
+                              static_cast<hipStream_t>(stream)) != hipSuccess)
+        return KDA_ERR_HIP;
+    return KDA_OK;
+}
+
+kda_status_t kda_last_stage_times(float* ms, const char** names, int max, int* count)
+{
+    if (!count || (max > 0 && !ms)) return KDA_ERR_NULL_POINTER;
+    std::lock_guard<std::mutex> lock(g_stage.mu);
+    *count = g_stage.count;
+    if (!g_stage.created || g_stage.count == 0) return KDA_OK;
+    if (hipEventSynchronize(g_stage.ev[g_stage.count]) != hipSuccess) return KDA_ERR_HIP;
+    for (int i = 0; i < g_stage.count && i < max; ++i) {
+        float t = 0.f;
+        if (hipEventElapsedTime(&t, g_stage.ev[i], g_stage.ev[i + 1]) != hipSuccess) return KDA_ERR_HIP;
+        ms[i] = t;
+        if (names) names[i] = g_stage.names[i];
+    }
+    return KDA_OK;
+}
+
+}  // extern "C"

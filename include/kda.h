@@ -1,0 +1,171 @@
+/*
+ * kda.h — C ABI of libkda: Kimi Delta Attention (KDA) and its Complex-KDA
+ * (CKDA) range extension on AMD Instinct MI355X (gfx950).
+ *
+ * The recurrence (per batch b and head h):
+ *   S_t = (I - beta_t k_t k_t^T) diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *   o_t = S_t^T q_t
+ * Update: "Semidirect Fourier Delta Attention" (arXiv 2607.11897), §1 eq. (1)
+ * and the affine form §2.2 eq. (9); read-out from the post-update state with no
+ * scale factor: same page, §3 eq. (14).  Ranges: KDA has alpha in (0,1] and
+ * beta in [0,1] (same page, §3); CKDA allows alpha in [-1,1] and beta in [0,2]
+ * ("Complex KDA: Understanding and Enhancing the Expressivity of Kimi Delta
+ * Attention", the abstract).  The state S is d_k x d_v (§2.2), decayed along
+ * its d_k rows.
+ *
+ * Conventions shared by every entry point:
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller; the library
+ *    never allocates, frees or synchronises (except where a flag says so) and
+ *    never keeps a pointer after the call returns.
+ *  - Layouts are row-major and contiguous:
+ *      q, k, alpha : [B, T, H, Dk]     v, out : [B, T, H, Dv]    beta : [B, T, H]
+ *      state       : [B, H, Dk, Dv]
+ *    (decode uses the same layouts with T = 1).
+ *  - q, k, v and out share `dtype`; alpha, beta and every state are fp32.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    is asynchronous: argument errors are reported synchronously, before any
+ *    HIP call is made; launch failures come back as KDA_ERR_HIP; faults during
+ *    execution surface at the caller's next synchronisation.
+ *  - The library does not normalise q or k, applies no gate parameterisation
+ *    and no output scale.
+ *  - Supported shapes: Dk in {16, 32, 64, 128}; Dv a multiple of 16 in
+ *    [16, 128]; chunk in {16, 32, 64}; B, H >= 1.  With dtype F32 the chunked
+ *    forward additionally needs Dk <= 64 and Dv <= 64.
+ *  - Alignment: q, k and alpha of the chunked forward, its workspace and the
+ *    decode state are read with 16-byte vector accesses and must be 16-byte
+ *    aligned; every other pointer must be aligned to its element size
+ *    (KDA_ERR_MISALIGNED otherwise).
+ *  - Thread safety: calls on different streams may run concurrently.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL_POINTER = 1,        /* a required pointer is NULL */
+    KDA_ERR_BAD_SHAPE = 2,           /* a size is out of range or overflows */
+    KDA_ERR_UNSUPPORTED = 3,         /* shape / dtype / mode / flag not supported */
+    KDA_ERR_MISALIGNED = 4,          /* a pointer breaks the alignment rule below */
+    KDA_ERR_WORKSPACE_TOO_SMALL = 5, /* workspace_bytes below the queried size */
+    KDA_ERR_ALIAS = 6,               /* an output overlaps an input it must not */
+    KDA_ERR_HIP = 7                  /* a HIP runtime call or launch failed */
+} kda_status_t;
+
+typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype_t;
+
+/* Admissible input ranges.  The mathematics is identical for both; the mode
+ * states the caller's contract (KDA: alpha in (0,1], beta in [0,1]; CKDA:
+ * alpha in [-1,1] incl. exact 0 and -1, beta in [0,2]).  Inputs outside the
+ * stated range give results of the same formula but carry no accuracy
+ * guarantee. */
+typedef enum { KDA_MODE_KDA = 0, KDA_MODE_CKDA = 1 } kda_mode_t;
+
+/* flags: record a HIP event around every kernel of this call so that
+ * kda_last_stage_times() can report per-kernel durations (adds event records
+ * on `stream`; performs no extra work on the data). */
+#define KDA_FLAG_STAGE_EVENTS 2u
+
+/* ABI version of the loaded library (KDA_ABI_VERSION it was built with). */
+int kda_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* kda_status_string(int status);
+
+/*
+ * Bytes of device workspace kda_chunk_forward needs for these sizes
+ * (the per-chunk WY factors of "Semidirect Fourier Delta Attention" §2.2).
+ * Returns KDA_OK and writes *bytes, or an argument error (same rules as
+ * kda_chunk_forward).  Makes no HIP call.
+ */
+kda_status_t kda_chunk_forward_workspace_size(int B, int T, int H, int Dk, int Dv,
+                                              int chunk, kda_dtype_t dtype,
+                                              size_t* bytes);
+
+/*
+ * Chunked forward over T tokens (prefill / training forward).  Executes the
+ * chunkwise form: the state is carried from chunk to chunk and each chunk's
+ * interior is solved in parallel through a compact WY representation of the
+ * product of its diagonal-plus-rank-one transitions (triangular solve), which
+ * reproduces the sequential recurrence up to rounding ("Kimi Delta Attention:
+ * a bounded case study", Exercise 2; "Semidirect Fourier Delta Attention",
+ * §1 and §2.2).
+ *   q, k, v, alpha, beta : inputs, layouts above.  T >= 0 (T = 0 only copies
+ *                          the initial state to final_state).  T need not be
+ *                          a multiple of chunk.
+ *   initial_state        : [B,H,Dk,Dv] fp32, or NULL for a zero state.
+ *   out                  : [B,T,H,Dv] in dtype; must not overlap any input.
+ *   final_state          : [B,H,Dk,Dv] fp32, or NULL.  May be exactly the
+ *                          same pointer as initial_state (resume in place);
+ *                          any other overlap with an input is KDA_ERR_ALIAS.
+ *   workspace            : device buffer of at least the queried size; its
+ *                          contents on entry are ignored and on exit are
+ *                          unspecified.  Must not overlap any other argument.
+ *   mode, flags          : see above; unknown flag bits -> KDA_ERR_UNSUPPORTED.
+ *   stream               : hipStream_t to enqueue on.
+ */
+kda_status_t kda_chunk_forward(const void* q, const void* k, const void* v,
+                               const float* alpha, const float* beta,
+                               const float* initial_state,
+                               void* out, float* final_state,
+                               int B, int T, int H, int Dk, int Dv, int chunk,
+                               kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * One single-token step for every (b, h), applied to a resident fp32 state in
+ * place: S <- (I - beta k k^T) diag(alpha) S + beta k v^T, then out = S^T q
+ * (eq. (1) and eq. (14) with T = 1).  One read and one write of the state.
+ *   q, k : [B,H,Dk] dtype;  v : [B,H,Dv] dtype;  alpha : [B,H,Dk] fp32;
+ *   beta : [B,H] fp32;  state : [B,H,Dk,Dv] fp32 (read and written);
+ *   out  : [B,H,Dv] dtype; must not overlap state or any input.
+ */
+kda_status_t kda_decode_step(const void* q, const void* k, const void* v,
+                             const float* alpha, const float* beta,
+                             float* state, void* out,
+                             int B, int H, int Dk, int Dv,
+                             kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
+                             void* stream);
+
+/*
+ * Chunk-local gate summary (log-magnitude, sign and zero form of the
+ * per-channel decay products inside each chunk; "Kimi Delta Attention: a
+ * bounded case study", Chapter 12 §12.1 per-channel decay, with the CKDA gate
+ * range of the "Complex KDA" abstract).  For chunk n, local token r and channel
+ * c (NC = ceil(T / chunk)):
+ *   L[b,h,n,r,c]    = sum over j <= r in the chunk with alpha_j != 0 of
+ *                     log2|alpha_j|   (fp32)
+ *   meta[b,h,n,r,c] = (zpos << 1) | parity, where parity = (number of
+ *                     negative alpha_j, j <= r in the chunk) mod 2 and
+ *                     zpos = 1 + (last j <= r with alpha_j == 0), 0 if none
+ *   gend[b,h,n,c]   = product of alpha over the chunk (fp32 running product)
+ * so that prod_{j=i+1..r} alpha_j = [zpos_r <= i+1] (-1)^(parity_r - parity_i)
+ * 2^(L_r - L_i).  alpha : [B,T,H,Dk] fp32.  L : [B,H,NC,chunk,Dk] fp32,
+ * meta : [B,H,NC,chunk,Dk] uint8, gend : [B,H,NC,Dk] fp32; entries of a short
+ * last chunk past T are written as L = 0, meta = 0.  Same shape rules as the
+ * forward (Dk in {16,32,64,128}, chunk in {16,32,64}).
+ */
+kda_status_t kda_gate_prep(const float* alpha, float* L, unsigned char* meta,
+                           float* gend, int B, int T, int H, int Dk, int chunk,
+                           void* stream);
+
+/*
+ * Per-kernel durations, in milliseconds, of the most recent call on this
+ * process that passed KDA_FLAG_STAGE_EVENTS.  Waits for that call's events.
+ * Writes up to `max` entries to ms[] and (if names != NULL) static kernel names
+ * to names[]; *count receives the number of kernels of that call.
+ */
+kda_status_t kda_last_stage_times(float* ms, const char** names, int max, int* count);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H */

@@ -1,0 +1,159 @@
+"""C-ABI contract tests that need no GPU.
+
+The library must load, export every entry point include/kda.h declares, and
+reject bad arguments with the documented status code *before* any HIP call
+(so these calls use fake, never-dereferenced device addresses).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_forward_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, NULLP, SHAPE, UNSUP, MISAL, WS, ALIAS = 0, 1, 2, 3, 4, 5, 6
+F32, BF16 = 0, 1
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return kda.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    syms = declared_symbols()
+    assert {"kda_chunk_forward", "kda_decode_step", "kda_chunk_forward_workspace_size",
+            "kda_gate_prep", "kda_status_string", "kda_abi_version"} <= set(syms)
+    for s in syms:
+        assert hasattr(lib, s), s
+
+
+def test_version_and_status_strings(lib):
+    assert lib.kda_abi_version() == 1
+    for s in range(8):
+        assert lib.kda_status_string(s)
+    assert lib.kda_status_string(99) == b"unknown status"
+
+
+def ws_size(lib, B, T, H, Dk, Dv, C, dt):
+    n = ctypes.c_size_t(123)
+    st = lib.kda_chunk_forward_workspace_size(B, T, H, Dk, Dv, C, dt, ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_size(lib):
+    st, n = ws_size(lib, 1, 8192, 32, 128, 128, 64, BF16)
+    assert st == OK
+    nu = 32 * 128
+    # W, Kt, QG bf16 + U fp32 + P bf16 + chunk decay fp32, per chunk
+    assert n == nu * (3 * 64 * 128 * 2 + 64 * 128 * 4 + 64 * 64 * 2 + 128 * 4)
+    assert ws_size(lib, 1, 0, 1, 16, 16, 16, F32) == (OK, 0)
+    assert ws_size(lib, 1, 10, 1, 24, 16, 16, F32)[0] == UNSUP          # Dk not supported
+    assert ws_size(lib, 1, 10, 1, 16, 24, 16, F32)[0] == UNSUP          # Dv not a multiple of 16
+    assert ws_size(lib, 1, 10, 1, 16, 16, 48, F32)[0] == UNSUP          # chunk
+    assert ws_size(lib, 1, 10, 1, 128, 16, 16, F32)[0] == UNSUP         # fp32 needs Dk <= 64
+    assert ws_size(lib, 0, 10, 1, 16, 16, 16, F32)[0] == SHAPE
+    assert ws_size(lib, 1, -1, 1, 16, 16, 16, F32)[0] == SHAPE
+    assert ws_size(lib, 1, 10, 1, 16, 16, 16, 7)[0] == UNSUP
+    assert lib.kda_chunk_forward_workspace_size(1, 1, 1, 16, 16, 16, F32, None) == NULLP
+
+
+class Fake:
+    """Distinct, 16-byte aligned, never-dereferenced addresses."""
+    def __init__(self):
+        self.next = 0x7f0000000000
+
+    def __call__(self, nbytes=1 << 20):
+        p = self.next
+        self.next += (nbytes + 4095) // 4096 * 4096 + 4096
+        return ctypes.c_void_p(p)
+
+
+def fwd(lib, **kw):
+    f = Fake()
+    B, T, H, Dk, Dv, C = kw.get("B", 1), kw.get("T", 64), kw.get("H", 2), kw.get("Dk", 16), \
+        kw.get("Dv", 16), kw.get("C", 16)
+    dt = kw.get("dt", F32)
+    st, need = ws_size(lib, max(B, 1), max(T, 0), max(H, 1), Dk, Dv, C, dt)
+    args = dict(q=f(), k=f(), v=f(), alpha=f(), beta=f(), s0=None, out=f(), st=None,
+                ws=f(max(need, 1) + 4096), wsb=need)
+    args.update({k_: v_ for k_, v_ in kw.items() if k_ in args})
+    return lib.kda_chunk_forward(args["q"], args["k"], args["v"], args["alpha"], args["beta"],
+                                 args["s0"], args["out"], args["st"], B, T, H, Dk, Dv, C, dt,
+                                 kw.get("mode", 1), kw.get("flags", 0), args["ws"], args["wsb"],
+                                 None)
+
+
+def test_forward_validation(lib):
+    assert fwd(lib, q=None) == NULLP
+    assert fwd(lib, out=None) == NULLP
+    assert fwd(lib, ws=None) == NULLP
+    assert fwd(lib, B=0) == SHAPE
+    assert fwd(lib, T=-3) == SHAPE
+    assert fwd(lib, Dk=20) == UNSUP
+    assert fwd(lib, Dv=8) == UNSUP
+    assert fwd(lib, C=128) == UNSUP
+    assert fwd(lib, mode=2) == UNSUP
+    assert fwd(lib, flags=1 << 5) == UNSUP
+    assert fwd(lib, dt=5) == UNSUP
+    assert fwd(lib, q=ctypes.c_void_p(0x7f0000000008)) == MISAL
+    assert fwd(lib, beta=ctypes.c_void_p(0x7f0000000002)) == MISAL
+    assert fwd(lib, wsb=0) == WS
+
+
+def test_forward_alias_rules(lib):
+    f = Fake()
+    base = f(1 << 24)
+    # out overlapping q
+    assert fwd(lib, q=base, out=ctypes.c_void_p(base.value + 256)) == ALIAS
+    # final_state overlapping out
+    assert fwd(lib, out=base, st=ctypes.c_void_p(base.value)) == ALIAS
+    # workspace overlapping alpha
+    assert fwd(lib, alpha=base, ws=ctypes.c_void_p(base.value + 1024)) == ALIAS
+    # final_state == initial_state is allowed (validation passes -> would launch; so only
+    # check that a *partial* overlap is rejected)
+    s0 = f(1 << 20)
+    assert fwd(lib, s0=s0, st=ctypes.c_void_p(s0.value + 16)) == ALIAS
+
+
+def test_decode_validation(lib):
+    f = Fake()
+    a = [f() for _ in range(7)]
+
+    def dec(ptrs=a, B=2, H=2, Dk=16, Dv=16, dt=BF16, mode=1, flags=0):
+        return lib.kda_decode_step(*ptrs, B, H, Dk, Dv, dt, mode, flags, None)
+
+    assert dec(ptrs=[None] + a[1:]) == NULLP
+    assert dec(B=0) == SHAPE
+    assert dec(Dk=48) == UNSUP
+    assert dec(Dv=200) == UNSUP
+    assert dec(mode=-1) == UNSUP
+    assert dec(ptrs=a[:5] + [ctypes.c_void_p(a[5].value + 4)] + a[6:]) == MISAL   # state
+    assert dec(ptrs=a[:4] + [ctypes.c_void_p(a[4].value + 2)] + a[5:]) == MISAL   # beta
+    assert dec(ptrs=a[:6] + [a[5]]) == ALIAS          # out == state
+
+
+def test_gate_prep_validation(lib):
+    f = Fake()
+    a = [f() for _ in range(4)]
+    assert lib.kda_gate_prep(None, *a[1:], 1, 10, 1, 16, 16, None) == NULLP
+    assert lib.kda_gate_prep(*a, 1, 10, 1, 16, 20, None) == UNSUP
+    assert lib.kda_gate_prep(*a, 1, -1, 1, 16, 16, None) == SHAPE
+    assert lib.kda_gate_prep(*a, 1, 0, 1, 16, 16, None) == OK       # nothing to do
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 4, 1, 16)
+    with pytest.raises(ValueError):
+        kda.chunk_forward(x, x, x, x, torch.zeros(1, 4, 1), chunk=16, workspace=torch.zeros(1))

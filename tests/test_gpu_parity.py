@@ -1,0 +1,275 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Every case prints its name before touching the GPU.  Inputs come from
+workloads.py (seeded, synthetic); expected values come only from oracle/.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_forward_amd as kda
+import oracle
+import workloads
+from parity import TOL, np32, oracle_threads, say, slice_err_out, slice_err_state
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def to_dev(inp):
+    return {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
+
+
+def run_oracle(inp, heads=None):
+    """Oracle forward on (a subset of) heads; inputs may live on the GPU."""
+    sel = (lambda t: t) if heads is None else (lambda t: t[:, :, heads])
+    q, k, v, a = (np32(sel(inp[x])) for x in ("q", "k", "v", "alpha"))
+    b = np32(sel(inp["beta"]))
+    s0 = None
+    if inp.get("S0") is not None:
+        s0 = np32(inp["S0"] if heads is None else inp["S0"][:, heads])
+    return oracle.forward(q, k, v, a, b, s0, nthreads=oracle_threads())
+
+
+def run_gpu(inp, chunk, mode, **kw):
+    out, st = kda.chunk_forward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"],
+                                inp.get("S0"), chunk=chunk, mode=mode, **kw)
+    torch.cuda.synchronize()
+    return out, st
+
+
+# (name, base workload, overrides)
+SMALL = [
+    ("cfg0_kda_fp32_tiny", 0, {}),
+    ("cfg1_ckda_fp32", 1, {}),
+    ("f32_ckda_dk32_dv48_c32_T67_s0", 1, dict(B=1, H=3, T=67, D=32, chunk=32, s0_std=0.5)),
+    ("f32_kda_d64_c64_T5", 0, dict(B=2, H=2, T=5, D=64, chunk=64)),
+    ("f32_ckda_d16_c16_T1", 1, dict(B=1, H=1, T=1, D=16, chunk=16)),
+    ("bf16_ckda_d128_c64_T67_s0", 3, dict(B=1, H=2, T=67, chunk=64)),
+    ("bf16_kda_d64_c16_T200", 2, dict(B=2, H=3, T=200, D=64, chunk=16)),
+    ("bf16_ckda_d32_c32_T96", 3, dict(B=1, H=2, T=96, D=32, chunk=32, s0_std=None)),
+    ("bf16_kda_d128_c32_T1", 2, dict(B=1, H=1, T=1, chunk=32)),
+    ("bf16_ckda_d16_c16_T333", 3, dict(B=3, H=1, T=333, D=16, chunk=16)),
+    ("bf16_ckda_d128_c64_T1000", 3, dict(B=1, H=4, T=1000, chunk=64)),
+]
+
+
+@pytest.mark.parametrize("name,base,ov", SMALL, ids=[c[0] for c in SMALL])
+def test_forward_small(name, base, ov):
+    w = workloads.workload(base, **ov)
+    say(f"[forward] {name}: {w}")
+    inp = workloads.make_prefill(w, device="cpu")
+    o_ref, s_ref = run_oracle(inp)
+    out, st = run_gpu(to_dev(inp), w.chunk, w.mode)
+    eo, es = slice_err_out(np32(out), o_ref), slice_err_state(np32(st), s_ref)
+    say(f"  err out {eo:.3e} state {es:.3e}")
+    assert eo <= TOL[w.dtype] and es <= TOL[w.dtype]
+
+
+def test_forward_dk_ne_dv_and_zero_state_pointer():
+    """Dk != Dv (rows/columns of S must not be swapped) and an explicit zero
+    initial state gives the same result as a NULL one."""
+    w = workloads.workload(1, B=1, H=2, T=130, D=64, chunk=32)
+    inp = workloads.make_prefill(w)
+    inp["v"] = inp["v"][..., :32].contiguous()
+    say("[forward] f32 Dk=64 Dv=32")
+    o_ref, s_ref = run_oracle(inp)
+    d = to_dev(inp)
+    out, st = run_gpu(d, 32, workloads.CKDA)
+    assert slice_err_out(np32(out), o_ref) <= 1e-4
+    assert slice_err_state(np32(st), s_ref) <= 1e-4
+    d["S0"] = torch.zeros(1, 2, 64, 32, device=DEV)
+    out2, st2 = run_gpu(d, 32, workloads.CKDA)
+    assert torch.equal(out, out2) and torch.equal(st, st2)
+
+
+def test_forward_cfg2_full():
+    """KDA bf16 prefill, B=1 H=32 T=8192 d=128 chunk=64, every head."""
+    w = workloads.workload(2)
+    say(f"[forward] cfg2 full {w}")
+    inp = workloads.make_prefill(w, device=DEV)
+    out, st = run_gpu(inp, w.chunk, w.mode)
+    o_ref, s_ref = run_oracle(inp)
+    eo, es = slice_err_out(np32(out), o_ref), slice_err_state(np32(st), s_ref)
+    say(f"  err out {eo:.3e} state {es:.3e}")
+    assert eo <= 2e-2 and es <= 2e-2
+
+
+def test_forward_cfg3_sampled_heads():
+    """CKDA bf16 long context, B=1 H=16 T=65536 d=128, S0 ~ N(0, 0.02^2): the GPU
+    runs all heads; the oracle checks a sample of heads (heads are independent)."""
+    w = workloads.workload(3)
+    say(f"[forward] cfg3 full, sampled heads {w}")
+    inp = workloads.make_prefill(w, device=DEV)
+    out, st = run_gpu(inp, w.chunk, w.mode)
+    heads = [0, 7, 15]
+    o_ref, s_ref = run_oracle(inp, heads)
+    eo = slice_err_out(np32(out[:, :, heads]), o_ref)
+    es = slice_err_state(np32(st[:, heads]), s_ref)
+    say(f"  err out {eo:.3e} state {es:.3e}")
+    assert eo <= 2e-2 and es <= 2e-2
+
+
+DECODE = [
+    ("f32_d16_dv16", torch.float32, 2, 3, 16, 16, 7),
+    ("f32_d64_dv48", torch.float32, 1, 2, 64, 48, 5),
+    ("bf16_d128_dv128", torch.bfloat16, 4, 4, 128, 128, 9),
+    ("bf16_d32_dv80", torch.bfloat16, 3, 2, 32, 80, 4),
+]
+
+
+@pytest.mark.parametrize("name,dt,B,H,Dk,Dv,N", DECODE, ids=[c[0] for c in DECODE])
+def test_decode_small(name, dt, B, H, Dk, Dv, N):
+    say(f"[decode] {name}")
+    w = workloads.workload(4, B=B, H=H, D=Dk, dtype=dt, steps=N)
+    inp = workloads.make_decode(w)
+    inp["v"] = torch.randn(N, B, H, Dv, generator=torch.Generator().manual_seed(9)).to(dt)
+    inp["S0"] = inp["S0"][..., :1].expand(B, H, Dk, Dv).contiguous() * torch.linspace(1, 2, Dv)
+    o_ref, s_ref = oracle.decode(np32(inp["q"]), np32(inp["k"]), np32(inp["v"]),
+                                 np32(inp["alpha"]), np32(inp["beta"]), np32(inp["S0"]))
+    d = to_dev(inp)
+    S = d["S0"].clone()
+    outs = torch.empty(N, B, H, Dv, dtype=dt, device=DEV)
+    for s in range(N):
+        kda.decode_step(d["q"][s], d["k"][s], d["v"][s], d["alpha"][s], d["beta"][s], S,
+                        out=outs[s])
+    torch.cuda.synchronize()
+    eo = slice_err_out(np.swapaxes(np32(outs), 0, 1), np.swapaxes(o_ref, 0, 1))
+    es = slice_err_state(np32(S), s_ref)
+    say(f"  err out {eo:.3e} state {es:.3e}")
+    assert eo <= TOL[dt] and es <= TOL[dt]
+
+
+def test_decode_cfg4_sampled():
+    """CKDA decode, B=256 H=32 d=128, state [256,32,128,128] resident and updated
+    in place for 1000 steps; the oracle follows a sample of (b, h) pairs."""
+    w = workloads.workload(4)
+    say(f"[decode] cfg4 full, 1000 steps, sampled pairs")
+    inp = workloads.make_decode(w, device=DEV)
+    S = inp["S0"].clone()
+    N = w.steps
+    outs = torch.empty(N, w.B, w.H, w.D, dtype=w.dtype, device=DEV)
+    for s in range(N):
+        kda.decode_step(inp["q"][s], inp["k"][s], inp["v"][s], inp["alpha"][s], inp["beta"][s],
+                        S, out=outs[s])
+    torch.cuda.synchronize()
+    pairs = [(0, 0), (17, 5), (100, 31), (255, 12), (128, 16), (63, 1)]
+    bi = torch.tensor([p[0] for p in pairs], device=DEV)
+    hi = torch.tensor([p[1] for p in pairs], device=DEV)
+    pick = lambda t: t[:, bi, hi].unsqueeze(2)      # [N, P, 1, ...]
+    o_ref, s_ref = oracle.decode(np32(pick(inp["q"])), np32(pick(inp["k"])), np32(pick(inp["v"])),
+                                 np32(pick(inp["alpha"])), np32(pick(inp["beta"])),
+                                 np32(inp["S0"][bi, hi].unsqueeze(1)), nthreads=oracle_threads())
+    eo = slice_err_out(np.swapaxes(np32(pick(outs)), 0, 1), np.swapaxes(o_ref, 0, 1))
+    es = slice_err_state(np32(S[bi, hi].unsqueeze(1)), s_ref)
+    say(f"  err out {eo:.3e} state {es:.3e}")
+    assert eo <= 2e-2 and es <= 2e-2
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_decode_equals_forward(dt):
+    """T decode steps and one chunked forward over the same T tokens agree."""
+    say(f"[decode==forward] {dt}")
+    w = workloads.workload(1, B=2, H=2, T=40, D=32, chunk=16, dtype=dt, s0_std=0.3)
+    inp = to_dev(workloads.make_prefill(w))
+    out_f, st_f = run_gpu(inp, 16, workloads.CKDA)
+    S = inp["S0"].clone()
+    outs = []
+    for t in range(w.T):
+        sl = lambda x: x[:, t].contiguous()
+        outs.append(kda.decode_step(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["alpha"]),
+                                    sl(inp["beta"]), S))
+    out_d = torch.stack(outs, dim=1)
+    torch.cuda.synchronize()
+    tol = TOL[dt]
+    assert slice_err_out(np32(out_d), np32(out_f).astype(np.float64)) <= 2 * tol
+    assert slice_err_state(np32(S), np32(st_f).astype(np.float64)) <= 2 * tol
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_resume_and_in_place_state(dt):
+    """forward(x1 || x2) = forward(x2; S0 = S_T(x1)), with final_state written
+    over initial_state in place."""
+    say(f"[resume] {dt}")
+    w = workloads.workload(1, B=1, H=3, T=150, D=64, chunk=32, dtype=dt, s0_std=0.1)
+    inp = to_dev(workloads.make_prefill(w))
+    out_all, st_all = run_gpu(inp, 32, workloads.CKDA)
+    cut = 77
+    p1 = {k: (v[:, :cut].contiguous() if k not in ("S0",) else v) for k, v in inp.items()}
+    p2 = {k: (v[:, cut:].contiguous() if k not in ("S0",) else v) for k, v in inp.items()}
+    o1, s1 = run_gpu(p1, 32, workloads.CKDA)
+    state = s1.clone()
+    o2, s2 = kda.chunk_forward(p2["q"], p2["k"], p2["v"], p2["alpha"], p2["beta"], state,
+                               chunk=32, final_state=state)
+    torch.cuda.synchronize()
+    assert s2.data_ptr() == state.data_ptr()
+    tol = TOL[dt]
+    both = torch.cat([o1, o2], dim=1)
+    assert slice_err_out(np32(both), np32(out_all).astype(np.float64)) <= tol
+    assert slice_err_state(np32(state), np32(st_all).astype(np.float64)) <= tol
+
+
+def test_mode_flag_does_not_change_numbers():
+    """KDA-range inputs give bit-identical results in KDA and CKDA mode."""
+    say("[mode]")
+    w = workloads.workload(2, B=1, H=2, T=300)
+    inp = to_dev(workloads.make_prefill(w))
+    a = run_gpu(inp, 64, workloads.KDA)
+    b = run_gpu(inp, 64, workloads.CKDA)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_deterministic_and_nan_isolated():
+    """Two runs are bitwise equal (no LDS race), and a NaN in one head's keys
+    leaves every other head bit-identical."""
+    say("[determinism / NaN isolation]")
+    w = workloads.workload(3, B=1, H=4, T=257)
+    inp = to_dev(workloads.make_prefill(w))
+    a = run_gpu(inp, 64, workloads.CKDA)
+    b = run_gpu(inp, 64, workloads.CKDA)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    bad = dict(inp)
+    bad["k"] = inp["k"].clone()
+    bad["k"][0, 100, 2, 5] = float("nan")
+    c = run_gpu(bad, 64, workloads.CKDA)
+    others = [0, 1, 3]
+    assert torch.equal(a[0][:, :, others], c[0][:, :, others])
+    assert torch.equal(a[1][:, others], c[1][:, others])
+    assert torch.isnan(c[0][:, 100:, 2]).any()
+
+
+def test_empty_sequence_copies_state():
+    say("[T=0]")
+    s0 = torch.randn(2, 3, 16, 32, device=DEV)
+    x = torch.empty(2, 0, 3, 16, device=DEV)
+    v = torch.empty(2, 0, 3, 32, device=DEV)
+    out, st = kda.chunk_forward(x, x, v, x, torch.empty(2, 0, 3, device=DEV), s0, chunk=16)
+    torch.cuda.synchronize()
+    assert out.shape == (2, 0, 3, 32) and torch.equal(st, s0)
+
+
+def test_gate_prep_matches_oracle():
+    """Gate summary: parity and last-zero index exact; L within the fp32
+    accumulation bound; chunk decay within fp32 product rounding."""
+    say("[gate_prep]")
+    w = workloads.workload(1, B=2, H=3, T=203, D=64, chunk=64)
+    inp = workloads.make_prefill(w)
+    ref = oracle.gate_prep(np32(inp["alpha"]), 64)
+    L, meta, gend = kda.gate_prep(inp["alpha"].to(DEV), 64)
+    torch.cuda.synchronize()
+    meta = meta.cpu().numpy()
+    T, C = w.T, w.chunk
+    valid = np.zeros(ref["L"].shape, dtype=bool)
+    for n in range(ref["L"].shape[2]):
+        valid[:, :, n, :max(0, min(C, T - n * C))] = True
+    assert np.array_equal((meta & 1)[valid], ref["parity"][valid])
+    assert np.array_equal((meta >> 1)[valid], ref["zpos"][valid])
+    assert np.all(meta[~valid] == 0)
+    # per step: log2 rounding (<= 2^-22 |log2 a|) + one fp32 add (<= 2^-24 |L|)
+    Lg = L.cpu().numpy().astype(np.float64)
+    r_idx = np.arange(C)[None, None, None, :, None] + 1
+    bound = r_idx * (2.0 ** -22 * 40 + 2.0 ** -24 * np.abs(ref["L"]).max()) + 1e-7
+    assert np.all(np.abs(Lg - ref["L"])[valid] <= np.broadcast_to(bound, Lg.shape)[valid])
+    g = gend.cpu().numpy().astype(np.float64)
+    assert np.allclose(g, ref["gend"], rtol=64 * 2.0 ** -23, atol=1e-37)
