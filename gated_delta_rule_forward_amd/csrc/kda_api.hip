@@ -12,6 +12,7 @@
 #include <mutex>
 
 #include "../../include/kda.h"
+#include "kda_chunk.hpp"
 #include "kda_launch.hpp"
 
 namespace {
@@ -130,7 +131,7 @@ kda_status_t kda_chunk_forward_workspace_size(int B, int T, int H, int Dk, int D
     if (!bytes) return KDA_ERR_NULL_POINTER;
     const kda_status_t st = check_forward_shape(B, T, H, Dk, Dv, chunk, dtype);
     if (st != KDA_OK) return st;
-    size_t off[6];
+    size_t off[kda::kWorkspaceRegions];
     *bytes = T == 0 ? 0
                     : kda::chunk_workspace_layout(make_shape(B, T, H, Dk, Dv, chunk),
                                                   dtype == KDA_DTYPE_F32 ? IoType::F32 : IoType::BF16, off);
@@ -205,18 +206,33 @@ kda_status_t kda_chunk_forward(const void* q, const void* k, const void* v, cons
 
     const ChunkShape sh = make_shape(B, T, H, Dk, Dv, chunk);
     const IoType io = dtype == KDA_DTYPE_F32 ? IoType::F32 : IoType::BF16;
-    size_t off[6];
+    size_t off[kda::kWorkspaceRegions];
     kda::chunk_workspace_layout(sh, io, off);
     unsigned char* w = static_cast<unsigned char*>(workspace);
     const ChunkWorkspace ws{w + off[0], reinterpret_cast<float*>(w + off[1]), w + off[2],
-                            w + off[3], w + off[4], reinterpret_cast<float*>(w + off[5])};
+                            w + off[3], w + off[4], reinterpret_cast<float*>(w + off[5]),
+                            w + off[6]};
+    // Extra zero-segment columns of the fast prep kernel: none in KDA mode
+    // (gates in (0, 1] have no zeros; a chunk that has one goes to the exact
+    // kernel), in CKDA mode as many as fit in 160 KB of LDS (at most 128).
+    int zx = 0;
+    if (mode == KDA_MODE_CKDA) {
+        zx = 128;
+        while (zx > 0 && kda::prep_fast_lds_bytes(io, chunk, Dk, zx) > 160 * 1024) zx -= 16;
+    }
+    const kda::PrepArgs pa{q, k, v, alpha, beta, ws.W, ws.U, ws.Kt, ws.QG, ws.P, ws.GC, ws.FL,
+                           T, H, Dv, sh.NC, zx};
+    const kda::ChainArgs ca{ws.W, ws.U, ws.Kt, ws.QG, ws.P, ws.GC, initial_state, out,
+                            final_state, B, T, H, Dv, sh.NC};
 
-    if (rec.mark("chunk_prep") != hipSuccess) return KDA_ERR_HIP;
-    if (kda::launch_chunk_prep(io, sh, q, k, v, alpha, beta, ws, s) != hipSuccess) return KDA_ERR_HIP;
+    if (rec.mark("prep_fast") != hipSuccess) return KDA_ERR_HIP;
+    if (kda::launch_prep_fast(io, sh, pa, s) != hipSuccess) return KDA_ERR_HIP;
     if (rec.done() != hipSuccess) return KDA_ERR_HIP;
-    if (rec.mark("chunk_chain") != hipSuccess) return KDA_ERR_HIP;
-    if (kda::launch_chunk_chain(io, sh, ws, initial_state, out, final_state, s) != hipSuccess)
-        return KDA_ERR_HIP;
+    if (rec.mark("prep_exact") != hipSuccess) return KDA_ERR_HIP;
+    if (kda::launch_prep_exact(io, sh, pa, s) != hipSuccess) return KDA_ERR_HIP;
+    if (rec.done() != hipSuccess) return KDA_ERR_HIP;
+    if (rec.mark("chain") != hipSuccess) return KDA_ERR_HIP;
+    if (kda::launch_chain(io, sh, ca, s) != hipSuccess) return KDA_ERR_HIP;
     if (rec.done() != hipSuccess) return KDA_ERR_HIP;
     return KDA_OK;
 }

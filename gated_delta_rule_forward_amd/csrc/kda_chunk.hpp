@@ -1,0 +1,186 @@
+// kda_chunk.hpp — definitions shared by the chunked-forward kernels (internal).
+//
+// Workspace layout (per unit = one chunk of one (b, h); NU units).  The chain
+// kernel feeds W, QG, P and Kt to MFMA as A operands against B operands taken
+// straight from C-layout accumulators, so they are stored fragment-major: an
+// A-operand matrix with R rows and K columns is [R/16][K/KB][64 lanes][KB/4],
+// each (16-row tile, k block) being the 64 per-lane fragments of one MFMA, one
+// contiguous block (see frag_off).  U is stored as the C-layout accumulator
+// tiles the chain adds it to.
+//   W  [NU] A-operand, rows = tokens (C),   k = channels (Dk)   io type
+//   QG [NU] A-operand, rows = tokens (C),   k = channels (Dk)   io type
+//   P  [NU] A-operand, rows = tokens (C),   k = tokens (C)      io type
+//   Kt [NU] A-operand, rows = channels (Dk), k = tokens (C)     io type
+//   U  [NU][C/16][Dv/16][64 lanes][4]  fp32 (lane 16g+n, register i holds
+//                                      row 4g+i, column n of the tile)
+//   GC [NU][Dk]      fp32
+//   FL [NU]          uint8: 1 = the unit needs the exact fallback kernel
+//
+// Fragment slots.  With k32 blocks (bf16, 16x16x32) lane (m, g) = 16g + m of
+// block s holds, in slot j = 0..7, column 32s + 16(j/4) + 4g + (j%4) of row m:
+// the slots pair with the B fragment built from two C-layout tiles (rows 4g..
+// 4g+3 of tiles 2s and 2s+1).  k16 blocks (bf16 16x16x16, fp32 4 x 16x16x4)
+// use column 16s + 4g + j.
+#pragma once
+
+#include "kda_device.hpp"
+
+namespace kda {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+// k-block width used for a (dtype, chunk, Dk) instance: bf16 contracts 32 at a
+// time when both contraction lengths allow it, else 16; fp32 always 16.
+template <typename T, int C, int DK>
+struct KBlock {
+    static constexpr int value = (sizeof(T) == 2 && C >= 32 && DK >= 32) ? 32 : 16;
+};
+
+// Offset of element (row r, column k) of an A-operand matrix with K columns
+// in the fragment-major layout described above.
+template <int KB>
+__host__ __device__ __forceinline__ int frag_off(int r, int k, int K) {
+    constexpr int NV = KB / 4;
+    const int kk = k % KB;
+    int g, j;
+    if constexpr (KB == 32) { g = (kk & 15) >> 2; j = 4 * (kk >> 4) + (kk & 3); }
+    else { g = kk >> 2; j = kk & 3; }
+    return (((r >> 4) * (K / KB) + k / KB) * 64 + 16 * g + (r & 15)) * NV + j;
+}
+// Offset of element (row r, column c) of U (C-layout tiles, Dv columns).
+__host__ __device__ __forceinline__ int u_off(int r, int c, int Dv) {
+    return (((r >> 4) * (Dv >> 4) + (c >> 4)) * 64 + 16 * ((r & 15) >> 2) + (c & 15)) * 4 + (r & 3);
+}
+
+// ---- k-block fragments -------------------------------------------------------
+// one lane's share of a k block: KB/4 consecutive k of one A row / B column
+template <typename T, int KB> struct Frag;
+template <> struct Frag<bf16_t, 32> {
+    static constexpr int NV = 8;
+    i16x8 v;
+    __device__ __forceinline__ static Frag load(const bf16_t* p) {   // 16-byte aligned
+        return Frag{*reinterpret_cast<const i16x8*>(p)};
+    }
+    __device__ __forceinline__ static Frag from(const float* f) {
+        i16x8 r;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) r[j] = bf16_bits((bf16_t)f[j]);
+        return Frag{r};
+    }
+};
+template <> struct Frag<bf16_t, 16> {
+    static constexpr int NV = 4;
+    i16x4 v;
+    __device__ __forceinline__ static Frag load(const bf16_t* p) {   // 8-byte aligned
+        return Frag{*reinterpret_cast<const i16x4*>(p)};
+    }
+    __device__ __forceinline__ static Frag from(const float* f) {
+        i16x4 r;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r[j] = bf16_bits((bf16_t)f[j]);
+        return Frag{r};
+    }
+};
+template <> struct Frag<float, 16> {
+    static constexpr int NV = 4;
+    float v[4];
+    __device__ __forceinline__ static Frag load(const float* p) {     // 16-byte aligned
+        const float4 x = *reinterpret_cast<const float4*>(p);
+        return Frag{{x.x, x.y, x.z, x.w}};
+    }
+    __device__ __forceinline__ static Frag from(const float* f) { return Frag{{f[0], f[1], f[2], f[3]}}; }
+};
+
+__device__ __forceinline__ f32x4 mma(const Frag<bf16_t, 32>& a, const Frag<bf16_t, 32>& b, f32x4 acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a.v),
+                                                   __builtin_bit_cast(bf16x8, b.v), acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(const Frag<bf16_t, 16>& a, const Frag<bf16_t, 16>& b, f32x4 acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(const Frag<float, 16>& a, const Frag<float, 16>& b, f32x4 acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[0], b.v[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[1], b.v[1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[2], b.v[2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[3], b.v[3], acc, 0, 0, 0);
+    return acc;
+}
+
+// B fragment of k block s built from C-layout accumulator tiles (rows 4g+i of
+// column n in lane l = 16g + n): a k32 block spans tiles 2s and 2s+1 (slot j =
+// tile 2s + j/4, register j%4), a k16 block is tile s.
+template <typename T, int KB>
+__device__ __forceinline__ Frag<T, KB> frag_from_tiles(const f32x4* tiles, int s) {
+    if constexpr (KB == 32) {
+        const float f[8] = {tiles[2 * s][0], tiles[2 * s][1], tiles[2 * s][2], tiles[2 * s][3],
+                            tiles[2 * s + 1][0], tiles[2 * s + 1][1], tiles[2 * s + 1][2],
+                            tiles[2 * s + 1][3]};
+        return Frag<T, KB>::from(f);
+    } else {
+        const float f[4] = {tiles[s][0], tiles[s][1], tiles[s][2], tiles[s][3]};
+        return Frag<T, KB>::from(f);
+    }
+}
+
+// A (or Bt) fragment of one row, k block starting at k0, from a row-major
+// matrix in natural k order: lane group g takes k0 + (KB/4) g .. + KB/4 - 1,
+// which is the hardware's own k order for both operands.
+template <typename T, int KB>
+__device__ __forceinline__ Frag<T, KB> frag_row(const T* row, int k0) {
+    const int g = (threadIdx.x & 63) >> 4;
+    return Frag<T, KB>::load(row + k0 + Frag<T, KB>::NV * g);
+}
+// same from an fp32 row, converted to T
+template <typename T, int KB>
+__device__ __forceinline__ Frag<T, KB> frag_row_cvt(const float* row, int k0) {
+    const int g = (threadIdx.x & 63) >> 4;
+    constexpr int NV = Frag<T, KB>::NV;
+    float f[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) f[j] = row[k0 + NV * g + j];
+    return Frag<T, KB>::from(f);
+}
+
+// 16x16 tile of A * Bt^T, both row-major with k contiguous (natural k order);
+// row r of the tile is A + r*lda, column n is Bt + n*ldb.
+template <typename T, int KB>
+__device__ __forceinline__ f32x4 tile_tn_nat(const T* A, int lda, const T* Bt, int ldb, int K) {
+    const int r = threadIdx.x & 15;
+    f32x4 acc = zero4();
+    for (int k0 = 0; k0 < K; k0 += KB)
+        acc = mma(frag_row<T, KB>(A + r * lda, k0), frag_row<T, KB>(Bt + r * ldb, k0), acc);
+    return acc;
+}
+
+struct PrepArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* alpha;
+    const float* beta;
+    void* W;
+    float* U;
+    void* Kt;
+    void* QG;
+    void* P;
+    float* GC;
+    uint8_t* FL;
+    int T, H, Dv, NC;
+    int zx;   // extra (zero-segment) columns available to the fast prep kernel
+};
+
+struct ChainArgs {
+    const void* W;
+    const float* U;
+    const void* Kt;
+    const void* QG;
+    const void* P;
+    const float* GC;
+    const float* S0;
+    void* out;
+    float* ST;
+    int B, T, H, Dv, NC;
+};
+
+}  // namespace kda

@@ -11,30 +11,36 @@ namespace kda {
 
 enum class IoType { F32 = 0, BF16 = 1 };
 
+struct PrepArgs;
+struct ChainArgs;
+
 // Device regions of the chunked-forward workspace, one slab per chunk of each
-// (b, h): NU = B * H * NC units.
+// (b, h): NU = B * H * NC units (layout details in kda_chunk.hpp).
 struct ChunkWorkspace {
-    void* W;     // [NU][C][Dk]  io type : Tinv diag(beta) (K * Gamma)
-    float* U;    // [NU][C][Dv]  fp32    : Tinv diag(beta) V
-    void* Kt;    // [NU][Dk][C]  io type : (K * rho(end, .))^T
-    void* QG;    // [NU][C][Dk]  io type : Q * Gamma
-    void* P;     // [NU][C][C]   io type : masked decay-weighted Q K^T (incl. diagonal)
-    float* GC;   // [NU][Dk]     fp32    : decay over the whole chunk
+    void* W;      // [NU][C][Dk]  io type
+    float* U;     // [NU][C][Dv]  fp32
+    void* Kt;     // [NU][Dk][C]  io type
+    void* QG;     // [NU][C][Dk]  io type
+    void* P;      // [NU][C][C]   io type
+    float* GC;    // [NU][Dk]     fp32
+    uint8_t* FL;  // [NU]         exact-kernel flags
 };
 
 struct ChunkShape {
     int B, T, H, Dk, Dv, C, NC;
 };
 
-// Bytes of each workspace region and the total (each region 256-byte aligned).
-size_t chunk_workspace_layout(const ChunkShape& s, IoType io, size_t offsets[6]);
+constexpr int kWorkspaceRegions = 7;
 
-hipError_t launch_chunk_prep(IoType io, const ChunkShape& s, const void* q, const void* k,
-                             const void* v, const float* alpha, const float* beta,
-                             const ChunkWorkspace& ws, hipStream_t stream);
+// Byte offset of each workspace region and the total (regions 256-byte aligned).
+size_t chunk_workspace_layout(const ChunkShape& s, IoType io, size_t offsets[kWorkspaceRegions]);
 
-hipError_t launch_chunk_chain(IoType io, const ChunkShape& s, const ChunkWorkspace& ws,
-                              const float* S0, void* out, float* ST, hipStream_t stream);
+// LDS bytes the fast prep kernel needs with zx extra zero-segment columns.
+size_t prep_fast_lds_bytes(IoType io, int C, int Dk, int zx);
+
+hipError_t launch_prep_fast(IoType io, const ChunkShape& s, const PrepArgs& a, hipStream_t stream);
+hipError_t launch_prep_exact(IoType io, const ChunkShape& s, const PrepArgs& a, hipStream_t stream);
+hipError_t launch_chain(IoType io, const ChunkShape& s, const ChainArgs& a, hipStream_t stream);
 
 hipError_t launch_state_copy(const float* S0, float* ST, size_t n, hipStream_t stream);
 

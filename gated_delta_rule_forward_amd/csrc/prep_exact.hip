@@ -1,44 +1,17 @@
-// chunk_forward.hip — chunkwise KDA / CKDA forward on gfx950.
-//
-// The chunkwise form carries the state from chunk to chunk and solves each
-// chunk's interior in parallel ("Kimi Delta Attention: a bounded case study",
-// Exercise 2: an execution strategy that changes cost, never the numbers).
-// The product of a chunk's diagonal-plus-rank-one transitions is kept in a
-// compact WY form obtained from a triangular solve, never as dense d x d
-// products ("Semidirect Fourier Delta Attention", §1 and §2.2, eq. (9)-(10);
-// rank grows only inside the chunk, contribution 8 of the same page).
-//
-// Per chunk of C tokens (local r = 0..C-1, S = state entering the chunk),
-// with rho(r,i) = prod_{j=i+1..r} alpha_j (per channel) and Gamma_r = rho(r,-1):
-//   A[r,i] = beta_r sum_c k_rc k_ic rho(r,i)_c            (i < r)
-//   Tinv   = (I + A)^{-1}                                  (forward substitution)
-//   W = Tinv diag(beta) (K * Gamma),   U = Tinv diag(beta) V
-//   Delta  = U - W S                   (the delta each token writes)
-//   P[r,i] = sum_c q_rc k_ic rho(r,i)_c                     (i <= r)
-//   O      = (Q * Gamma) S + P Delta                        (eq. (14))
-//   S_next = diag(Gamma_{C-1}) S + Ktil^T Delta,  Ktil_i = k_i * rho(C-1, i)
-// Unrolling S_r = diag(alpha_r) S_{r-1} + k_r Delta_r^T (eq. (1) rewritten)
-// inside the chunk gives the unit lower-triangular system (I + A) Delta =
-// diag(beta)(V - (K * Gamma) S).
-//
-// Two kernels:
-//  * prep  — one workgroup per (b, h, chunk), all chunks in parallel: the gate
-//    summary of the chunk (decay products from fixed reference tokens, exact
-//    in sign and zero), A and P, Tinv, W, U, Q*Gamma, Ktil^T, Gamma_{C-1}.
-//    Every decay ratio is formed as a running product of gates that starts at
-//    a reference token, so |factor| <= 1 everywhere (no overflow) and a zero
-//    or negative gate is carried exactly.
-//      - off-diagonal 16x16 blocks of A and P (rows in block a, columns before
-//        it): rho(r,i) = rho(r,e) rho(e,i) with e the last token before block
-//        a, so each block is one MFMA product of (K or Q) * rho(.,e) with
-//        K * rho(e,.);
-//      - diagonal 16x16 blocks: per pair, a running product over the block.
-//  * chain — one wavefront per (b, h, 16 columns of the state): the only
-//    sequential part.  Carries its fp32 d_k x 16 state slice in registers
-//    across all chunks (columns of S evolve independently: row-side transition,
-//    column-separable write, §2.2 eq. (9)), and computes Delta, the chunk's
-//    outputs and the next state with MFMA.
-#include "kda_device.hpp"
+// prep_exact.hip — exact per-chunk WY factors for chunks the fast kernel
+// flags (a half span of the log decay too wide for the midpoint factorisation,
+// or more zero gates than extra columns).  Same outputs as prep_fast.hip, but
+// every decay ratio is a running product of gates that starts at a reference
+// token, so |factor| <= 1 everywhere and zero or negative gates are carried
+// exactly, at the cost of per-pair VALU work on the 16x16 diagonal blocks:
+//  - off-diagonal 16x16 blocks of A and P (rows in block a, columns before
+//    it): rho(r,i) = rho(r,e) rho(e,i) with e the last token before block a,
+//    one MFMA product of (K or Q) * rho(.,e) with K * rho(e,.);
+//  - diagonal 16x16 blocks: per pair, a running product over the block;
+//  - Tinv = (I + A)^{-1} by forward substitution (one wavefront, lane j owns
+//    column j).
+// A persistent grid walks all chunks and skips unflagged ones.
+#include "kda_chunk.hpp"
 #include "kda_launch.hpp"
 
 namespace kda {
@@ -72,20 +45,6 @@ struct PrepLds {
     static constexpr size_t TOTAL = al16(UNI + SZ_UNI);
 };
 
-struct PrepArgs {
-    const void* q;
-    const void* k;
-    const void* v;
-    const float* alpha;
-    const float* beta;
-    void* W;
-    float* U;
-    void* Kt;
-    void* QG;
-    void* P;
-    float* GC;
-    int T, H, Dv, NC;
-};
 
 // C = A * B with A row-major [m][k] (vector loads) and B row-major [k][n]
 // (four scalar loads per k16 block), K a multiple of 16.
@@ -105,8 +64,9 @@ __device__ __forceinline__ f32x4 tile_nn(const T* A, int lda, const T* B, int ld
 }
 
 template <typename T, int C, int DK>
-__global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(PrepArgs args)
+__global__ __launch_bounds__(kPrepThreads) void prep_exact_kernel(PrepArgs args, int NU)
 {
+    constexpr int KB = KBlock<T, C, DK>::value;
     using L = PrepLds<T, C, DK>;
     constexpr int NB = L::NB;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -126,7 +86,8 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(PrepArgs args)
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
     const int T_ = args.T, H = args.H, Dv = args.Dv, NC = args.NC;
-    const int unit = blockIdx.x;
+    for (int unit = blockIdx.x; unit < NU; unit += gridDim.x) {
+    if (args.FL[unit] == 0) continue;   // uniform across the workgroup
     const int n = unit % NC, bh = unit / NC;
     const int b = bh / H, h = bh % H;
     const int t0 = n * C;
@@ -200,7 +161,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(PrepArgs args)
             }
             // lane cg owns entry (row s+cg, column s+di)
             if (cg > di) sA[(s + cg) * C + s + di] = sBeta[s + cg] * aout;
-            Pg[(size_t)(s + cg) * C + s + di] = from_f32<T>(cg >= di ? pout : 0.f);
+            Pg[frag_off<KB>(s + cg, s + di, C)] = from_f32<T>(cg >= di ? pout : 0.f);
         }
     }
 
@@ -219,7 +180,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(PrepArgs args)
         for (int r = 0; r < C; ++r) {
             gm *= a[r];
             const float kr = to_f32(sK[r * DK + c]), qr = to_f32(sQ[r * DK + c]);
-            QGg[(size_t)r * DK + c] = from_f32<T>(qr * gm);
+            QGg[frag_off<KB>(r, c, DK)] = from_f32<T>(qr * gm);
             sX[r * DK + c] = from_f32<T>(sBeta[r] * kr * gm);
         }
         GCg[c] = gm;
@@ -232,10 +193,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(PrepArgs args)
             e *= a[i];
         }
 #pragma unroll
-        for (int i0 = 0; i0 < C; i0 += 4) {
-            const Vec4<T> w = Vec4<T>::from(kt + i0);
-            *reinterpret_cast<Vec4<T>*>(Ktg + (size_t)c * C + i0) = w;
-        }
+        for (int i = 0; i < C; ++i) Ktg[frag_off<KB>(c, i, C)] = from_f32<T>(kt[i]);
         // off-diagonal block a: rows r in block a scaled by rho(r, e_a), columns
         // i < 16a by rho(e_a, i), e_a = 16a - 1
 #pragma unroll
@@ -276,7 +234,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(PrepArgs args)
                     for (int i = 0; i < 4; ++i) {
                         const int r = 16 * ab + 4 * lg + i, col = 16 * bb + ln;
                         if (kind == 0) sA[r * C + col] = sBeta[r] * acc[i];
-                        else Pg[(size_t)r * C + col] = from_f32<T>(acc[i]);
+                        else Pg[frag_off<KB>(r, col, C)] = from_f32<T>(acc[i]);
                     }
                 }
             }
@@ -284,7 +242,7 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(PrepArgs args)
         // P above its block diagonal is zero
         for (int idx = tid; idx < C * C; idx += kPrepThreads) {
             const int r = idx / C, col = idx % C;
-            if ((col >> 4) > (r >> 4)) Pg[idx] = from_f32<T>(0.f);
+            if ((col >> 4) > (r >> 4)) Pg[frag_off<KB>(r, col, C)] = from_f32<T>(0.f);
         }
     }
     __syncthreads();
@@ -332,234 +290,67 @@ __global__ __launch_bounds__(kPrepThreads) void chunk_prep_kernel(PrepArgs args)
                 const f32x4 acc = tile_nn(sTi + 16 * mt * C, C, sX + 16 * ct, DK, C, zero4());
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    Wg[(size_t)(16 * mt + 4 * lg + i) * DK + 16 * ct + ln] = from_f32<T>(acc[i]);
+                    Wg[frag_off<KB>(16 * mt + 4 * lg + i, 16 * ct + ln, DK)] = from_f32<T>(acc[i]);
             } else {
                 const int ut = ct - NW;
                 const f32x4 acc = tile_nn(sTi + 16 * mt * C, C, sY + 16 * ut, Dv, C, zero4());
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    Ug[(size_t)(16 * mt + 4 * lg + i) * Dv + 16 * ut + ln] = acc[i];
+                    Ug[u_off(16 * mt + 4 * lg + i, 16 * ut + ln, Dv)] = acc[i];
             }
         }
     }
-}
-
-struct ChainArgs {
-    const void* W;
-    const float* U;
-    const void* Kt;
-    const void* QG;
-    const void* P;
-    const float* GC;
-    const float* S0;
-    void* out;
-    float* ST;
-    int T, H, Dv, NC;
-};
-
-template <typename T, int C, int DK>
-__global__ __launch_bounds__(64) void chunk_chain_kernel(ChainArgs args)
-{
-    constexpr int NT = DK / 16, NM = C / 16;
-    const int Dv = args.Dv, H = args.H, T_ = args.T, NC = args.NC;
-    const int NS = Dv / 16;
-    const int bh = blockIdx.x / NS, slice = blockIdx.x % NS;
-    const int b = bh / H, h = bh % H;
-    const int lane = threadIdx.x, ln = lane & 15, lg = lane >> 4;
-    const int col = slice * 16 + ln;
-
-    f32x4 S[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            S[t][i] = args.S0 ? args.S0[((size_t)bh * DK + 16 * t + 4 * lg + i) * Dv + col] : 0.f;
-
-    T* __restrict__ out = static_cast<T*>(args.out);
-    for (int nc = 0; nc < NC; ++nc) {
-        const size_t unit = (size_t)bh * NC + nc;
-        const T* Wu = static_cast<const T*>(args.W) + unit * C * DK;
-        const float* Uu = args.U + unit * C * Dv;
-        const T* Ktu = static_cast<const T*>(args.Kt) + unit * DK * C;
-        const T* QGu = static_cast<const T*>(args.QG) + unit * C * DK;
-        const T* Pu = static_cast<const T*>(args.P) + unit * C * C;
-        const float* GCu = args.GC + unit * DK;
-
-        // S as k16 blocks over its d_k rows
-        Vec4<T> sb[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const float f[4] = {S[t][0], S[t][1], S[t][2], S[t][3]};
-            sb[t] = Vec4<T>::from(f);
-        }
-        // Delta = U - W S
-        f32x4 D[NM];
-#pragma unroll
-        for (int mt = 0; mt < NM; ++mt) {
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-                acc = mma_k16(Vec4<T>::load(Wu + (16 * mt + ln) * DK + 16 * t + 4 * lg), sb[t], acc);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) D[mt][i] = Uu[(16 * mt + 4 * lg + i) * Dv + col] - acc[i];
-        }
-        Vec4<T> db[NM];
-#pragma unroll
-        for (int mt = 0; mt < NM; ++mt) {
-            const float f[4] = {D[mt][0], D[mt][1], D[mt][2], D[mt][3]};
-            db[mt] = Vec4<T>::from(f);
-        }
-        // O = (Q * Gamma) S + P Delta
-#pragma unroll
-        for (int mt = 0; mt < NM; ++mt) {
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int t = 0; t < NT; ++t)
-                acc = mma_k16(Vec4<T>::load(QGu + (16 * mt + ln) * DK + 16 * t + 4 * lg), sb[t], acc);
-#pragma unroll
-            for (int kt = 0; kt < NM; ++kt)
-                acc = mma_k16(Vec4<T>::load(Pu + (16 * mt + ln) * C + 16 * kt + 4 * lg), db[kt], acc);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tok = nc * C + 16 * mt + 4 * lg + i;
-                if (tok < T_) out[(((size_t)b * T_ + tok) * H + h) * Dv + col] = from_f32<T>(acc[i]);
-            }
-        }
-        // S <- diag(Gamma_{C-1}) S + Ktil^T Delta
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            f32x4 acc;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = GCu[16 * t + 4 * lg + i] * S[t][i];
-#pragma unroll
-            for (int kt = 0; kt < NM; ++kt)
-                acc = mma_k16(Vec4<T>::load(Ktu + (16 * t + ln) * C + 16 * kt + 4 * lg), db[kt], acc);
-            S[t] = acc;
-        }
-    }
-    if (args.ST) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                args.ST[((size_t)bh * DK + 16 * t + 4 * lg + i) * Dv + col] = S[t][i];
+    __syncthreads();   // LDS is reused by the next flagged unit
     }
 }
 
-__global__ void state_copy_kernel(const float* __restrict__ src, float* __restrict__ dst, size_t n)
-{
-    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) dst[i] = src ? src[i] : 0.f;
-}
 
 template <typename T, int C, int DK>
-hipError_t launch_prep_t(const ChunkShape& s, const PrepArgs& a, hipStream_t stream)
+hipError_t launch_exact_t(const ChunkShape& s, const PrepArgs& a, hipStream_t stream)
 {
     using L = PrepLds<T, C, DK>;
-    auto kern = chunk_prep_kernel<T, C, DK>;
-    static bool configured = false;   // benign race: the attribute is idempotent
-    if (!configured) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 (int)L::TOTAL);
-        if (e != hipSuccess) return e;
-        configured = true;
-    }
-    const unsigned nunits = (unsigned)((size_t)s.B * s.H * s.NC);
-    hipLaunchKernelGGL(kern, dim3(nunits), dim3(kPrepThreads), L::TOTAL, stream, a);
+    auto kern = prep_exact_kernel<T, C, DK>;
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)L::TOTAL);
+    if (e != hipSuccess) return e;
+    const int nu = (int)((size_t)s.B * s.H * s.NC);
+    const int grid = nu < 512 ? nu : 512;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kPrepThreads), L::TOTAL, stream, a, nu);
     return hipGetLastError();
 }
 
-template <typename T, int C, int DK>
-hipError_t launch_chain_t(const ChunkShape& s, const ChainArgs& a, hipStream_t stream)
-{
-    const unsigned nwg = (unsigned)((size_t)s.B * s.H * (s.Dv / 16));
-    hipLaunchKernelGGL((chunk_chain_kernel<T, C, DK>), dim3(nwg), dim3(64), 0, stream, a);
-    return hipGetLastError();
-}
-
-// Dispatch over the supported (C, Dk) set; fp32 stops at Dk = 64 (LDS).
-template <typename T, template <typename, int, int> class F, typename Args>
-hipError_t dispatch(const ChunkShape& s, const Args& a, hipStream_t stream);
-
-template <typename T, int C, int DK>
-struct PrepCall {
-    static hipError_t run(const ChunkShape& s, const PrepArgs& a, hipStream_t st) {
-        return launch_prep_t<T, C, DK>(s, a, st);
-    }
-};
-template <typename T, int C, int DK>
-struct ChainCall {
-    static hipError_t run(const ChunkShape& s, const ChainArgs& a, hipStream_t st) {
-        return launch_chain_t<T, C, DK>(s, a, st);
-    }
-};
-
-template <typename T, template <typename, int, int> class F, typename Args, int C>
-hipError_t dispatch_dk(const ChunkShape& s, const Args& a, hipStream_t st)
+template <typename T, int C>
+hipError_t dispatch_dk(const ChunkShape& s, const PrepArgs& a, hipStream_t st)
 {
     switch (s.Dk) {
-    case 16: return F<T, C, 16>::run(s, a, st);
-    case 32: return F<T, C, 32>::run(s, a, st);
-    case 64: return F<T, C, 64>::run(s, a, st);
+    case 16: return launch_exact_t<T, C, 16>(s, a, st);
+    case 32: return launch_exact_t<T, C, 32>(s, a, st);
+    case 64: return launch_exact_t<T, C, 64>(s, a, st);
     case 128:
-        if constexpr (sizeof(T) == 2) return F<T, C, 128>::run(s, a, st);
+        if constexpr (sizeof(T) == 2) return launch_exact_t<T, C, 128>(s, a, st);
         else return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
     }
 }
 
-template <typename T, template <typename, int, int> class F, typename Args>
-hipError_t dispatch(const ChunkShape& s, const Args& a, hipStream_t st)
+template <typename T>
+hipError_t dispatch_c(const ChunkShape& s, const PrepArgs& a, hipStream_t st)
 {
     switch (s.C) {
-    case 16: return dispatch_dk<T, F, Args, 16>(s, a, st);
-    case 32: return dispatch_dk<T, F, Args, 32>(s, a, st);
-    case 64: return dispatch_dk<T, F, Args, 64>(s, a, st);
+    case 16: return dispatch_dk<T, 16>(s, a, st);
+    case 32: return dispatch_dk<T, 32>(s, a, st);
+    case 64: return dispatch_dk<T, 64>(s, a, st);
     default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-size_t chunk_workspace_layout(const ChunkShape& s, IoType io, size_t off[6])
+hipError_t launch_prep_exact(IoType io, const ChunkShape& s, const PrepArgs& a, hipStream_t stream)
 {
-    const size_t e = io == IoType::F32 ? 4 : 2;
-    const size_t nu = (size_t)s.B * s.H * s.NC;
-    const size_t C = s.C, Dk = s.Dk, Dv = s.Dv;
-    const size_t sz[6] = {nu * C * Dk * e, nu * C * Dv * 4, nu * Dk * C * e,
-                          nu * C * Dk * e, nu * C * C * e, nu * Dk * 4};
-    size_t o = 0;
-    for (int i = 0; i < 6; ++i) {
-        off[i] = o;
-        o += (sz[i] + 255) & ~size_t(255);
-    }
-    return o;
-}
-
-hipError_t launch_chunk_prep(IoType io, const ChunkShape& s, const void* q, const void* k,
-                             const void* v, const float* alpha, const float* beta,
-                             const ChunkWorkspace& ws, hipStream_t stream)
-{
-    PrepArgs a{q, k, v, alpha, beta, ws.W, ws.U, ws.Kt, ws.QG, ws.P, ws.GC, s.T, s.H, s.Dv, s.NC};
-    if (io == IoType::F32) return dispatch<float, PrepCall>(s, a, stream);
-    return dispatch<bf16_t, PrepCall>(s, a, stream);
-}
-
-hipError_t launch_chunk_chain(IoType io, const ChunkShape& s, const ChunkWorkspace& ws,
-                              const float* S0, void* out, float* ST, hipStream_t stream)
-{
-    ChainArgs a{ws.W, ws.U, ws.Kt, ws.QG, ws.P, ws.GC, S0, out, ST, s.T, s.H, s.Dv, s.NC};
-    if (io == IoType::F32) return dispatch<float, ChainCall>(s, a, stream);
-    return dispatch<bf16_t, ChainCall>(s, a, stream);
-}
-
-hipError_t launch_state_copy(const float* S0, float* ST, size_t n, hipStream_t stream)
-{
-    if (n == 0) return hipSuccess;
-    const unsigned grid = (unsigned)((n + 255) / 256);
-    hipLaunchKernelGGL(state_copy_kernel, dim3(grid), dim3(256), 0, stream, S0, ST, n);
-    return hipGetLastError();
+    if (io == IoType::F32) return dispatch_c<float>(s, a, stream);
+    return dispatch_c<bf16_t>(s, a, stream);
 }
 
 }  // namespace kda

@@ -1,0 +1,484 @@
+// prep_fast.hip — per-chunk WY factors (the parallel part of the chunkwise
+// forward), all chunks of all (b, h) at once, one 256-thread workgroup each.
+//
+// Within a chunk of C tokens (S = state entering the chunk), with
+// rho(r,i) = prod_{j=i+1..r} alpha_j per channel and Gamma_r = rho(r,-1):
+//   A[r,i] = beta_r sum_c k_rc k_ic rho(r,i)_c   (i < r)     Tinv = (I + A)^{-1}
+//   W = Tinv diag(beta)(K * Gamma)   U = Tinv diag(beta) V
+//   P[r,i] = sum_c q_rc k_ic rho(r,i)_c          (i <= r)
+//   QG = Q * Gamma,  Ktil_i = k_i * rho(C-1, i),  GC = Gamma_{C-1}
+// (chunkwise execution and its exactness: "Kimi Delta Attention: a bounded
+// case study", Exercise 2; the compact WY form via a triangular solve:
+// "Semidirect Fourier Delta Attention", §1 and §2.2.)
+//
+// Gate summary first (the chunk-local log-magnitude / sign / zero form, per
+// channel): L_r = sum_{j<=r, alpha_j != 0} log2|alpha_j|, parity_r, and the
+// zero count seg_r = #{j <= r : alpha_j == 0}.  Then for i <= r
+//   rho(r,i) = [seg_r == seg_i] (-1)^(parity_r + parity_i) 2^(L_r - L_i).
+// A and P need every pair, so each channel is factored through its midpoint
+// M = L_{C-1} / 2:  2^(L_r - L_i) = 2^(L_r - M) 2^(M - L_i), and each zero-free
+// segment of a channel becomes its own contraction column ("virtual channel":
+// segment 0 stays in column c, later segments get extra columns), so pairs
+// across a zero gate meet only zeros and stay exactly zero.  A and P are then
+// one MFMA product each over Dk + (#zeros) columns.  A chunk whose half span
+// max|L_r - M| exceeds 96 (factors could leave the normal range) or whose zero
+// count exceeds the extra columns is flagged for the exact kernel
+// (prep_exact.hip) instead.
+//
+// Tinv is a blocked inverse over 16x16 diagonal blocks (fp32 MFMA):
+//   T_aa = (I + A_aa)^{-1} by forward substitution,
+//   T_ab = -T_aa sum_{j=b..a-1} A_aj T_jb   (a > b, by block distance).
+//
+// Outputs go out fragment-major (kda_chunk.hpp): P and W are produced as
+// transposed tiles (P^T = Y X_P^T, W^T = X_W^T Tinv^T), whose C-layout
+// accumulators are exactly the A fragments the chain kernel consumes, so each
+// lane stores one contiguous 16-byte fragment; Q*Gamma goes through LDS; the
+// thread that owns (channel, tokens) writes its Ktil fragment slots directly.
+#include "kda_chunk.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr float kHalfSpanMax = 96.f;
+
+template <typename T, int C, int DK>
+struct FastGeom {
+    static constexpr int KB = KBlock<T, C, DK>::value;
+    static constexpr int NV = KB / 4;                         // fragment slots per lane
+    static constexpr int TPB = KB / 16;                       // 16-wide tiles per k block
+    static constexpr int TPC = kThreads / DK;                 // threads per channel
+    static constexpr int TOK = C / TPC;                       // tokens per thread
+    static constexpr int PADE = 16 / (int)sizeof(T);          // 16-byte row pad
+    static constexpr int KCS = C + PADE;                      // row stride of Xt / Vt
+    static constexpr int LDF = C + 4;                         // row stride of fp32 A / Tinv
+    static constexpr int QS = DK + PADE;                      // row stride of staged Q*Gamma
+    static constexpr int NB = C / 16;
+};
+
+template <typename T, int C, int DK>
+struct FastLayout {
+    int KS;                 // operand row stride (elements)
+    size_t ops, sA, scr, total;
+    __host__ __device__ FastLayout(int zx, int dvmax) {
+        using G = FastGeom<T, C, DK>;
+        const int kp_max = ((DK + zx + G::KB - 1) / G::KB) * G::KB;
+        KS = kp_max + G::PADE;
+        const size_t e = sizeof(T);
+        const size_t opsz1 = 3 * (size_t)C * KS * e;
+        const size_t opsz2 = (size_t)C * G::LDF * 4 + (size_t)(DK + dvmax) * G::KCS * e;
+        const size_t opsz = ((opsz1 > opsz2 ? opsz1 : opsz2) + 15) & ~size_t(15);
+        const size_t asz1 = (size_t)C * G::LDF * 4, asz2 = (size_t)C * G::QS * e;
+        const size_t asz = ((asz1 > asz2 ? asz1 : asz2) + 15) & ~size_t(15);
+        ops = 0;
+        sA = ops + opsz;
+        scr = sA + asz;
+        // partL, partP, partZ [256 each], base [DK], misc [8], beta [C]
+        total = scr + (3 * kThreads + DK + 8 + C) * 4;
+        total = (total + 15) & ~size_t(15);
+    }
+};
+
+template <typename T>
+__device__ __forceinline__ float ldf(const T* p) { return to_f32(*p); }
+
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float flog2(float x) { return __builtin_amdgcn_logf(x); }
+
+// one fragment (NV slots) of an A-operand from a row-major matrix in LDS:
+// row r, k block s, lane group g -> slots j at columns of frag_off's mapping
+template <typename T, int KB>
+__device__ __forceinline__ Frag<T, KB> gather_frag(const T* row, int s, int g) {
+    constexpr int NV = KB / 4;
+    float f[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int kk = KB == 32 ? 16 * (j >> 2) + 4 * g + (j & 3) : 4 * g + j;
+        f[j] = to_f32(row[s * KB + kk]);
+    }
+    return Frag<T, KB>::from(f);
+}
+
+template <typename T, int C, int DK>
+__global__ __launch_bounds__(kThreads) void prep_fast_kernel(PrepArgs args)
+{
+    using G = FastGeom<T, C, DK>;
+    using F = Frag<T, G::KB>;
+    constexpr int KB = G::KB, NV = G::NV, TPB = G::TPB, TPC = G::TPC, TOK = G::TOK;
+    constexpr int NB = G::NB, KCS = G::KCS, LDF = G::LDF, QS = G::QS;
+    constexpr int NKD = DK / KB, NKC = C / KB;
+    const int Dv = args.Dv;
+    const FastLayout<T, C, DK> LY(args.zx, sizeof(T) == 4 ? 64 : 128);
+    const int KS = LY.KS;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    T* XA = reinterpret_cast<T*>(lds + LY.ops);
+    T* XP = XA + C * KS;
+    T* Y = XP + C * KS;
+    float* sT = reinterpret_cast<float*>(lds + LY.ops);                   // after A/P
+    T* Xt = reinterpret_cast<T*>(lds + LY.ops + (size_t)C * LDF * 4);      // [DK][KCS]
+    T* Vt = Xt + DK * KCS;                                                 // [Dv][KCS]
+    float* sA = reinterpret_cast<float*>(lds + LY.sA);
+    T* sQG = reinterpret_cast<T*>(lds + LY.sA);                            // before A/P
+    float* partL = reinterpret_cast<float*>(lds + LY.scr);
+    int* partP = reinterpret_cast<int*>(partL + kThreads);
+    int* partZ = partP + kThreads;
+    int* sBase = partZ + kThreads;
+    int* misc = sBase + DK;
+    float* sBeta = reinterpret_cast<float*>(misc + 8);
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    const int c = tid % DK, part = tid / DK;
+    const int T_ = args.T, H = args.H, NC = args.NC;
+    const int unit = blockIdx.x;
+    const int n = unit % NC, bh = unit / NC;
+    const int b = bh / H, h = bh % H;
+    const int t0 = n * C;
+    const int nvalid = min(C, T_ - t0);
+
+    const size_t tok0 = ((size_t)b * T_ + t0) * H + h;     // row of token t0, head h
+    const T* gq = static_cast<const T*>(args.q) + tok0 * DK;
+    const T* gk = static_cast<const T*>(args.k) + tok0 * DK;
+    const float* ga = args.alpha + tok0 * DK;
+    const T* gv = static_cast<const T*>(args.v) + tok0 * Dv;
+    const float* gb = args.beta + tok0;
+    const int rs = H * DK, rsv = H * Dv;                    // token strides
+    T* Wg = static_cast<T*>(args.W) + (size_t)unit * C * DK;
+    float* Ug = args.U + (size_t)unit * C * Dv;
+    T* Ktg = static_cast<T*>(args.Kt) + (size_t)unit * DK * C;
+    T* QGg = static_cast<T*>(args.QG) + (size_t)unit * C * DK;
+    T* Pg = static_cast<T*>(args.P) + (size_t)unit * C * C;
+
+    // ---- gate summary of my channel c over my tokens [part*TOK, +TOK) --------
+    float al[TOK], kk[TOK], qq[TOK], bt[TOK];
+#pragma unroll
+    for (int j = 0; j < TOK; ++j) {
+        const int r = part * TOK + j;
+        if (r < nvalid) {
+            al[j] = ga[r * rs + c];
+            kk[j] = ldf(gk + r * rs + c);
+            qq[j] = ldf(gq + r * rs + c);
+            bt[j] = gb[r * H];
+        } else {
+            al[j] = 1.f; kk[j] = 0.f; qq[j] = 0.f; bt[j] = 0.f;
+        }
+    }
+    float Lr[TOK];
+    int pr[TOK], sg[TOK];
+    {
+        float ls = 0.f;
+        int par = 0, nz = 0;
+#pragma unroll
+        for (int j = 0; j < TOK; ++j) {
+            const float a = al[j];
+            if (a == 0.f) nz += 1;
+            else ls += flog2(fabsf(a));
+            par ^= (a < 0.f) ? 1 : 0;
+            Lr[j] = ls; pr[j] = par; sg[j] = nz;
+        }
+        partL[part * DK + c] = ls;
+        partP[part * DK + c] = par;
+        partZ[part * DK + c] = nz;
+        if (c == 0) {
+#pragma unroll
+            for (int j = 0; j < TOK; ++j) sBeta[part * TOK + j] = bt[j];
+        }
+    }
+    __syncthreads();
+    float offL = 0.f, totL = 0.f;
+    int offP = 0, offZ = 0, totP = 0, totZ = 0;
+#pragma unroll
+    for (int p = 0; p < TPC; ++p) {
+        const float l = partL[p * DK + c];
+        const int pp = partP[p * DK + c], zz = partZ[p * DK + c];
+        if (p < part) { offL += l; offP ^= pp; offZ += zz; }
+        totL += l; totP ^= pp; totZ += zz;
+    }
+#pragma unroll
+    for (int j = 0; j < TOK; ++j) { Lr[j] += offL; pr[j] ^= offP; sg[j] += offZ; }
+    if (part == 0) sBase[c] = totZ;
+    __syncthreads();
+    // exclusive prefix of the per-channel zero counts -> first extra column of c
+    if (wave == 0) {
+        int carry = 0;
+        for (int c0 = 0; c0 < DK; c0 += 64) {
+            const int v = (c0 + lane < DK) ? sBase[c0 + lane] : 0;
+            int incl = v;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int y = __shfl_up(incl, off, 64);
+                if (lane >= off) incl += y;
+            }
+            if (c0 + lane < DK) sBase[c0 + lane] = carry + incl - v;
+            carry += __shfl(incl, 63, 64);
+        }
+        if (lane == 0) misc[0] = carry;
+    }
+    __syncthreads();
+    const int base_c = sBase[c];
+    const int Ztot = misc[0];
+    const float M = 0.5f * totL;
+    const bool bad = (-M > kHalfSpanMax) || (Ztot > args.zx) || !(M <= 0.f);
+    if (__syncthreads_or(bad)) {
+        if (tid == 0) args.FL[unit] = 1;
+        return;
+    }
+    if (tid == 0) args.FL[unit] = 0;
+
+    // ---- factored operands (LDS), Q*Gamma (staged), Ktil (direct) ---------------
+    const int KP = ((DK + Ztot + KB - 1) / KB) * KB;     // contraction length
+    {
+        const int ext = KP - DK;
+        for (int idx = tid; idx < 3 * C * ext; idx += kThreads) {
+            const int m = idx / (C * ext), rem = idx % (C * ext);
+            const int r = rem / ext, col = DK + rem % ext;
+            XA[m * C * KS + r * KS + col] = from_f32<T>(0.f);
+        }
+    }
+    __syncthreads();
+    float xw[TOK], kt[TOK];
+#pragma unroll
+    for (int j = 0; j < TOK; ++j) {
+        const int r = part * TOK + j;
+        const float sgn = pr[j] ? -1.f : 1.f;
+        const float F = sgn * fexp2(Lr[j] - M), Gf = sgn * fexp2(M - Lr[j]);
+        const int col = sg[j] == 0 ? c : DK + base_c + sg[j] - 1;
+        XA[r * KS + col] = from_f32<T>(bt[j] * kk[j] * F);
+        XP[r * KS + col] = from_f32<T>(qq[j] * F);
+        Y[r * KS + col] = from_f32<T>(kk[j] * Gf);
+        if (col != c) {
+            XA[r * KS + c] = from_f32<T>(0.f);
+            XP[r * KS + c] = from_f32<T>(0.f);
+            Y[r * KS + c] = from_f32<T>(0.f);
+        }
+        const float gam = sg[j] == 0 ? sgn * fexp2(Lr[j]) : 0.f;
+        sQG[r * QS + c] = from_f32<T>(qq[j] * gam);
+        xw[j] = bt[j] * kk[j] * gam;
+        const float re = (sg[j] == totZ) ? ((pr[j] ^ totP) ? -1.f : 1.f) * fexp2(totL - Lr[j]) : 0.f;
+        kt[j] = kk[j] * re;
+    }
+    // Ktil is an A operand with rows = channels, k = tokens: the 32 tokens of
+    // one k32 block that I own fill 4 whole fragments (one per lane group)
+    if constexpr (KB == 32 && TOK == 32) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            float f[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) f[j] = kt[16 * (j >> 2) + 4 * g + (j & 3)];
+            *reinterpret_cast<F*>(Ktg + frag_off<KB>(c, part * 32 + 4 * g, C)) = F::from(f);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < TOK; ++j)
+            Ktg[frag_off<KB>(c, part * TOK + j, C)] = from_f32<T>(kt[j]);
+    }
+    if (part == 0)
+        args.GC[(size_t)unit * DK + c] = totZ == 0 ? (totP ? -1.f : 1.f) * fexp2(totL) : 0.f;
+    __syncthreads();
+    // Q*Gamma fragments: 64 lanes x (C/16) x (DK/KB) per chunk
+    for (int f = tid; f < (C / 16) * NKD * 64; f += kThreads) {
+        const int l = f & 63, blk = f >> 6;
+        const int mt = blk / NKD, s = blk % NKD;
+        *reinterpret_cast<F*>(QGg + (size_t)f * NV) =
+            gather_frag<T, KB>(sQG + (16 * mt + (l & 15)) * QS, s, l >> 4);
+    }
+    __syncthreads();   // the staging area becomes sA
+
+    // ---- A (strictly lower, LDS) and P^T tiles (global, fragment-major) --------
+    // work items: A tiles (ta, tb <= ta), then P items (ta, k block s)
+    {
+        constexpr int NA = NB * (NB + 1) / 2;
+        for (int it = wave; it < NA + NB * NKC; it += 4) {
+            if (it < NA) {
+                int ta = 0;
+                while ((ta + 1) * (ta + 2) / 2 <= it) ++ta;
+                const int tb = it - ta * (ta + 1) / 2;
+                const f32x4 acc = tile_tn_nat<T, KB>(XA + 16 * ta * KS, KS, Y + 16 * tb * KS, KS, KP);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * ta + 4 * lg + i, col = 16 * tb + ln;
+                    sA[r * LDF + col] = col < r ? acc[i] : 0.f;
+                }
+            } else {
+                const int ta = (it - NA) / NKC, s = (it - NA) % NKC;
+                float f[NV];
+#pragma unroll
+                for (int u = 0; u < TPB; ++u) {
+                    const int tb = s * TPB + u;
+                    f32x4 acc = zero4();
+                    if (tb <= ta)   // P^T tile: lane (n, g) holds P[16ta + n][16tb + 4g + i]
+                        acc = tile_tn_nat<T, KB>(Y + 16 * tb * KS, KS, XP + 16 * ta * KS, KS, KP);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        f[4 * u + i] = (16 * tb + 4 * lg + i <= 16 * ta + ln) ? acc[i] : 0.f;
+                }
+                *reinterpret_cast<F*>(Pg + ((size_t)(ta * NKC + s) * 64 + lane) * NV) = F::from(f);
+            }
+        }
+    }
+    __syncthreads();   // operands dead: the region now holds sT, Xt, Vt
+
+    // ---- Tinv diagonal blocks; stage X_W^T and (diag(beta) V)^T ----------------
+    if (wave < NB && lane < 16) {
+        const int a = wave, j = lane;
+        float t[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float s = (r == j) ? 1.f : 0.f;
+#pragma unroll
+            for (int i = 0; i < r; ++i) s -= sA[(16 * a + r) * LDF + 16 * a + i] * t[i];
+            t[r] = s;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sT[(16 * a + r) * LDF + 16 * a + j] = t[r];
+    }
+    for (int idx = tid; idx < C * C; idx += kThreads) {       // upper blocks of Tinv
+        const int r = idx / C, col = idx % C;
+        if ((col >> 4) > (r >> 4)) sT[r * LDF + col] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < TOK; ++j) Xt[c * KCS + part * TOK + j] = from_f32<T>(xw[j]);
+    for (int idx = tid; idx < C * Dv; idx += kThreads) {
+        const int r = idx / Dv, cv = idx % Dv;
+        float y = 0.f;
+        if (r < nvalid) y = sBeta[r] * ldf(gv + r * rsv + cv);
+        Vt[cv * KCS + r] = from_f32<T>(y);
+    }
+    __syncthreads();
+    // ---- Tinv off-diagonal blocks by block distance (fp32 MFMA) ----------------
+    for (int d = 1; d < NB; ++d) {
+        for (int idx = wave; idx < NB - d; idx += 4) {
+            const int a = idx + d, bb = idx;
+            f32x4 inner = zero4();
+            for (int jb = bb; jb < a; ++jb) {
+                // A_{a,jb} (row-major in sA) times T_{jb,bb} (row-major [k][n] in sT)
+                const Frag<float, 16> fa =
+                    Frag<float, 16>::load(sA + (16 * a + ln) * LDF + 16 * jb + 4 * lg);
+                float fb[4];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) fb[jj] = sT[(16 * jb + 4 * lg + jj) * LDF + 16 * bb + ln];
+                inner = mma(fa, Frag<float, 16>::from(fb), inner);
+            }
+            const float fi[4] = {inner[0], inner[1], inner[2], inner[3]};
+            const Frag<float, 16> ta =
+                Frag<float, 16>::load(sT + (16 * a + ln) * LDF + 16 * a + 4 * lg);
+            const f32x4 tab = mma(ta, Frag<float, 16>::from(fi), zero4());
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sT[(16 * a + 4 * lg + i) * LDF + 16 * bb + ln] = -tab[i];
+        }
+        __syncthreads();
+    }
+
+    // ---- W^T tiles -> W fragments;  U = Tinv (diag(beta) V) tiles ---------------
+    {
+        constexpr int NM = C / 16;
+        const int NUt = Dv / 16;
+        const int nwi = NM * NKD;                       // W items (token tile, k block)
+        for (int it = wave; it < nwi + NM * NUt; it += 4) {
+            if (it < nwi) {
+                const int mt = it / NKD, s = it % NKD;
+                float f[NV];
+#pragma unroll
+                for (int u = 0; u < TPB; ++u) {
+                    const int ct = s * TPB + u;
+                    // W^T[16ct + 4g + i][16mt + n] = X_W^T rows . Tinv rows
+                    const T* arow = Xt + (16 * ct + ln) * KCS;
+                    const float* brow = sT + (16 * mt + ln) * LDF;
+                    f32x4 acc = zero4();
+#pragma unroll
+                    for (int k0 = 0; k0 < C; k0 += KB)
+                        acc = mma(frag_row<T, KB>(arow, k0), frag_row_cvt<T, KB>(brow, k0), acc);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) f[4 * u + i] = acc[i];
+                }
+                *reinterpret_cast<F*>(Wg + ((size_t)(mt * NKD + s) * 64 + lane) * NV) = F::from(f);
+            } else {
+                const int ut = it - nwi, mt = ut % NM, nt = ut / NM;
+                const float* arow = sT + (16 * mt + ln) * LDF;
+                const T* brow = Vt + (16 * nt + ln) * KCS;
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int k0 = 0; k0 < C; k0 += KB)
+                    acc = mma(frag_row_cvt<T, KB>(arow, k0), frag_row<T, KB>(brow, k0), acc);
+                *reinterpret_cast<f32x4*>(Ug + ((size_t)(mt * NUt + nt) * 64 + lane) * 4) = acc;
+            }
+        }
+    }
+}
+
+template <typename T, int C, int DK>
+hipError_t launch_fast_t(const ChunkShape& s, const PrepArgs& a, hipStream_t stream)
+{
+    const FastLayout<T, C, DK> LY(a.zx, sizeof(T) == 4 ? 64 : 128);
+    auto kern = prep_fast_kernel<T, C, DK>;
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)LY.total);
+    if (e != hipSuccess) return e;
+    const unsigned nunits = (unsigned)((size_t)s.B * s.H * s.NC);
+    hipLaunchKernelGGL(kern, dim3(nunits), dim3(kThreads), LY.total, stream, a);
+    return hipGetLastError();
+}
+
+template <typename T, int C, int DK>
+size_t fast_lds_t(int zx) { return FastLayout<T, C, DK>(zx, sizeof(T) == 4 ? 64 : 128).total; }
+
+template <typename T, int C>
+hipError_t dispatch_dk(const ChunkShape& s, const PrepArgs& a, hipStream_t st)
+{
+    switch (s.Dk) {
+    case 16: return launch_fast_t<T, C, 16>(s, a, st);
+    case 32: return launch_fast_t<T, C, 32>(s, a, st);
+    case 64: return launch_fast_t<T, C, 64>(s, a, st);
+    case 128:
+        if constexpr (sizeof(T) == 2) return launch_fast_t<T, C, 128>(s, a, st);
+        else return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T>
+hipError_t dispatch_c(const ChunkShape& s, const PrepArgs& a, hipStream_t st)
+{
+    switch (s.C) {
+    case 16: return dispatch_dk<T, 16>(s, a, st);
+    case 32: return dispatch_dk<T, 32>(s, a, st);
+    case 64: return dispatch_dk<T, 64>(s, a, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T, int C>
+size_t lds_dk(int Dk, int zx)
+{
+    switch (Dk) {
+    case 16: return fast_lds_t<T, C, 16>(zx);
+    case 32: return fast_lds_t<T, C, 32>(zx);
+    case 64: return fast_lds_t<T, C, 64>(zx);
+    default: return fast_lds_t<T, C, 128>(zx);
+    }
+}
+
+}  // namespace
+
+size_t prep_fast_lds_bytes(IoType io, int C, int Dk, int zx)
+{
+    if (io == IoType::F32) {
+        if (Dk > 64) return ~size_t(0);
+        return C == 16 ? lds_dk<float, 16>(Dk, zx) : C == 32 ? lds_dk<float, 32>(Dk, zx)
+                                                              : lds_dk<float, 64>(Dk, zx);
+    }
+    return C == 16 ? lds_dk<bf16_t, 16>(Dk, zx) : C == 32 ? lds_dk<bf16_t, 32>(Dk, zx)
+                                                           : lds_dk<bf16_t, 64>(Dk, zx);
+}
+
+hipError_t launch_prep_fast(IoType io, const ChunkShape& s, const PrepArgs& a, hipStream_t stream)
+{
+    if (io == IoType::F32) return dispatch_c<float>(s, a, stream);
+    return dispatch_c<bf16_t>(s, a, stream);
+}
+
+}  // namespace kda

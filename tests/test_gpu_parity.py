@@ -273,3 +273,26 @@ def test_gate_prep_matches_oracle():
     assert np.all(np.abs(Lg - ref["L"])[valid] <= np.broadcast_to(bound, Lg.shape)[valid])
     g = gend.cpu().numpy().astype(np.float64)
     assert np.allclose(g, ref["gend"], rtol=64 * 2.0 ** -23, atol=1e-37)
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_exact_fallback_chunks(dt):
+    """Chunks the fast prep kernel cannot factor go to the exact kernel:
+    zero gates in KDA mode (no extra zero-segment columns) and gates so small
+    that a chunk's log2 decay spans more than the midpoint factorisation allows.
+    Flagged and unflagged chunks are mixed in one call; results must still
+    match the oracle."""
+    say(f"[fallback] {dt}")
+    D = 64 if dt == torch.float32 else 128
+    w = workloads.workload(1, B=1, H=3, T=200, D=D, chunk=64, dtype=dt)
+    inp = workloads.make_prefill(w)
+    a = inp["alpha"]
+    a[0, 70:80, 1, :5] = 1e-12          # head 1, chunk 1: ~40 bits per token
+    a[0, 150:190, 2, 3] = 2.0 ** -30    # head 2, chunk 2: span >> 192 bits
+    o_ref, s_ref = run_oracle(inp)
+    d = to_dev(inp)
+    for mode in (workloads.KDA, workloads.CKDA):
+        out, st = run_gpu(d, 64, mode)
+        eo, es = slice_err_out(np32(out), o_ref), slice_err_state(np32(st), s_ref)
+        say(f"  mode {mode}: err out {eo:.3e} state {es:.3e}")
+        assert eo <= TOL[dt] and es <= TOL[dt]
