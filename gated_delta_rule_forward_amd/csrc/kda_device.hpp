@@ -42,6 +42,7 @@ template <> struct Vec4<float> {
     }
     __device__ __forceinline__ static Vec4 from(const float* f) { return Vec4{{f[0], f[1], f[2], f[3]}}; }
     __device__ __forceinline__ static Vec4 zero() { return Vec4{{0.f, 0.f, 0.f, 0.f}}; }
+    __device__ __forceinline__ float get(int i) const { return v[i]; }
 };
 template <> struct Vec4<bf16_t> {
     i16x4 v;   // raw bf16 bits
@@ -55,6 +56,9 @@ template <> struct Vec4<bf16_t> {
         return Vec4{r};
     }
     __device__ __forceinline__ static Vec4 zero() { return Vec4{i16x4{0, 0, 0, 0}}; }
+    __device__ __forceinline__ float get(int i) const {
+        return __uint_as_float((unsigned)(unsigned short)v[i] << 16);
+    }
 };
 
 // ---- one k16 block of a 16x16 MFMA tile --------------------------------------

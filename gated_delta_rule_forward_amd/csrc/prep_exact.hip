@@ -10,7 +10,10 @@
 //  - diagonal 16x16 blocks: per pair, a running product over the block;
 //  - Tinv = (I + A)^{-1} by forward substitution (one wavefront, lane j owns
 //    column j).
-// A persistent grid walks all chunks and skips unflagged ones.
+// A grid of at most 512 workgroups covers all chunks: each workgroup reads the
+// flags of its chunks (blockIdx.x, blockIdx.x + gridDim.x, ...) together,
+// lists the flagged ones in LDS and then works through that list, so a launch
+// with nothing flagged costs one round of flag loads.
 #include "kda_chunk.hpp"
 #include "kda_launch.hpp"
 
@@ -86,8 +89,20 @@ __global__ __launch_bounds__(kPrepThreads) void prep_exact_kernel(PrepArgs args,
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
     const int T_ = args.T, H = args.H, Dv = args.Dv, NC = args.NC;
-    for (int unit = blockIdx.x; unit < NU; unit += gridDim.x) {
-    if (args.FL[unit] == 0) continue;   // uniform across the workgroup
+    __shared__ int sList[kPrepThreads];
+    __shared__ int sCount;
+    const int nper = (NU - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+    for (int base = 0; base < nper; base += kPrepThreads) {
+    if (tid == 0) sCount = 0;
+    __syncthreads();
+    if (base + tid < nper) {
+        const int u = (int)blockIdx.x + (base + tid) * (int)gridDim.x;
+        if (args.FL[u] != 0) sList[atomicAdd(&sCount, 1)] = u;
+    }
+    __syncthreads();
+    const int nlist = sCount;
+    for (int li = 0; li < nlist; ++li) {
+    const int unit = sList[li];
     const int n = unit % NC, bh = unit / NC;
     const int b = bh / H, h = bh % H;
     const int t0 = n * C;
@@ -301,6 +316,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_exact_kernel(PrepArgs args,
         }
     }
     __syncthreads();   // LDS is reused by the next flagged unit
+    }
     }
 }
 

@@ -49,40 +49,46 @@ struct FastGeom {
     static constexpr int KB = KBlock<T, C, DK>::value;
     static constexpr int NV = KB / 4;                         // fragment slots per lane
     static constexpr int TPB = KB / 16;                       // 16-wide tiles per k block
-    static constexpr int TPC = kThreads / DK;                 // threads per channel
-    static constexpr int TOK = C / TPC;                       // tokens per thread
+    static constexpr int NQ = DK / 4;                         // channel quads
+    static constexpr int PARTS = (kThreads / NQ) < C ? (kThreads / NQ) : C;   // token ranges
+    static constexpr int TOK = C / PARTS;                     // tokens per thread
+    static constexpr int ACTIVE = NQ * PARTS;                 // threads that own elements
     static constexpr int PADE = 16 / (int)sizeof(T);          // 16-byte row pad
-    static constexpr int KCS = C + PADE;                      // row stride of Xt / Vt
     static constexpr int LDF = C + 4;                         // row stride of fp32 A / Tinv
-    static constexpr int QS = DK + PADE;                      // row stride of staged Q*Gamma
+    static constexpr int XWS = DK + PADE;                     // row stride of X_W, Q*Gamma staging
     static constexpr int NB = C / 16;
+    static constexpr int DVMAX = sizeof(T) == 4 ? 64 : 128;
+    static constexpr int VS = DVMAX + PADE;                   // row stride of staged V
+    static constexpr int VEC = 16 / (int)sizeof(T);           // elements per 16-byte vector
+    static constexpr int VPT = (C * DVMAX / VEC + kThreads - 1) / kThreads;   // V vectors per thread
 };
 
 template <typename T, int C, int DK>
 struct FastLayout {
     int KS;                 // operand row stride (elements)
     size_t ops, sA, scr, total;
-    __host__ __device__ FastLayout(int zx, int dvmax) {
+    __host__ __device__ FastLayout(int zx) {
         using G = FastGeom<T, C, DK>;
         const int kp_max = ((DK + zx + G::KB - 1) / G::KB) * G::KB;
         KS = kp_max + G::PADE;
         const size_t e = sizeof(T);
         const size_t opsz1 = 3 * (size_t)C * KS * e;
-        const size_t opsz2 = (size_t)C * G::LDF * 4 + (size_t)(DK + dvmax) * G::KCS * e;
+        const size_t opsz2 = (size_t)C * G::LDF * 4 + (size_t)C * G::XWS * e + (size_t)C * G::VS * e;
         const size_t opsz = ((opsz1 > opsz2 ? opsz1 : opsz2) + 15) & ~size_t(15);
-        const size_t asz1 = (size_t)C * G::LDF * 4, asz2 = (size_t)C * G::QS * e;
-        const size_t asz = ((asz1 > asz2 ? asz1 : asz2) + 15) & ~size_t(15);
+        // the sA region also holds Q*Gamma staging and, before that, the
+        // per-token-range partial gate sums (partL, partPZ: PARTS x DK each)
+        const size_t asz1 = (size_t)C * G::LDF * 4, asz2 = (size_t)C * G::XWS * e;
+        const size_t asz3 = (size_t)2 * G::PARTS * DK * 4;
+        size_t asz = asz1 > asz2 ? asz1 : asz2;
+        asz = ((asz > asz3 ? asz : asz3) + 15) & ~size_t(15);
         ops = 0;
         sA = ops + opsz;
         scr = sA + asz;
-        // partL, partP, partZ [256 each], base [DK], misc [8], beta [C]
-        total = scr + (3 * kThreads + DK + 8 + C) * 4;
+        // base [DK], misc [8], beta [C]
+        total = scr + (DK + 8 + C) * 4;
         total = (total + 15) & ~size_t(15);
     }
 };
-
-template <typename T>
-__device__ __forceinline__ float ldf(const T* p) { return to_f32(*p); }
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float flog2(float x) { return __builtin_amdgcn_logf(x); }
@@ -101,37 +107,58 @@ __device__ __forceinline__ Frag<T, KB> gather_frag(const T* row, int s, int g) {
     return Frag<T, KB>::from(f);
 }
 
+// fragment whose k index runs down a column of a row-major LDS matrix: lane
+// (m, g) takes rows k0 + NV g + x (x < NV) of column m (base = column 0 of the
+// 16-column tile, ld = row stride)
+template <typename T, int KB>
+__device__ __forceinline__ Frag<T, KB> frag_col(const T* base, int ld, int k0) {
+    const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
+    constexpr int NV = KB / 4;
+    Frag<T, KB> f;
+    if constexpr (sizeof(T) == 2) {
+        const short* b = reinterpret_cast<const short*>(base) + (k0 + NV * g) * ld + m;
+#pragma unroll
+        for (int x = 0; x < NV; ++x) f.v[x] = b[x * ld];
+    } else {
+        const float* b = reinterpret_cast<const float*>(base) + (k0 + NV * g) * ld + m;
+#pragma unroll
+        for (int x = 0; x < NV; ++x) f.v[x] = b[x * ld];
+    }
+    return f;
+}
+
 template <typename T, int C, int DK>
 __global__ __launch_bounds__(kThreads) void prep_fast_kernel(PrepArgs args)
 {
     using G = FastGeom<T, C, DK>;
     using F = Frag<T, G::KB>;
-    constexpr int KB = G::KB, NV = G::NV, TPB = G::TPB, TPC = G::TPC, TOK = G::TOK;
-    constexpr int NB = G::NB, KCS = G::KCS, LDF = G::LDF, QS = G::QS;
+    constexpr int KB = G::KB, NV = G::NV, TPB = G::TPB, PARTS = G::PARTS, TOK = G::TOK;
+    constexpr int NB = G::NB, LDF = G::LDF, XWS = G::XWS, VS = G::VS, VEC = G::VEC;
     constexpr int NKD = DK / KB, NKC = C / KB;
     const int Dv = args.Dv;
-    const FastLayout<T, C, DK> LY(args.zx, sizeof(T) == 4 ? 64 : 128);
+    const FastLayout<T, C, DK> LY(args.zx);
     const int KS = LY.KS;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     T* XA = reinterpret_cast<T*>(lds + LY.ops);
     T* XP = XA + C * KS;
     T* Y = XP + C * KS;
-    float* sT = reinterpret_cast<float*>(lds + LY.ops);                   // after A/P
-    T* Xt = reinterpret_cast<T*>(lds + LY.ops + (size_t)C * LDF * 4);      // [DK][KCS]
-    T* Vt = Xt + DK * KCS;                                                 // [Dv][KCS]
+    float* sT = reinterpret_cast<float*>(lds + LY.ops);                    // after A/P
+    T* sXW = reinterpret_cast<T*>(lds + LY.ops + (size_t)C * LDF * 4);      // [C][XWS]
+    T* sV = sXW + C * XWS;                                                  // [C][VS]
     float* sA = reinterpret_cast<float*>(lds + LY.sA);
-    T* sQG = reinterpret_cast<T*>(lds + LY.sA);                            // before A/P
-    float* partL = reinterpret_cast<float*>(lds + LY.scr);
-    int* partP = reinterpret_cast<int*>(partL + kThreads);
-    int* partZ = partP + kThreads;
-    int* sBase = partZ + kThreads;
+    T* sQG = reinterpret_cast<T*>(lds + LY.sA);                             // before A/P
+    float* partL = reinterpret_cast<float*>(lds + LY.sA);                  // before Q*Gamma
+    int* partPZ = reinterpret_cast<int*>(partL + PARTS * DK);               // nz << 1 | parity
+    int* sBase = reinterpret_cast<int*>(lds + LY.scr);
     int* misc = sBase + DK;
     float* sBeta = reinterpret_cast<float*>(misc + 8);
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, ln = lane & 15, lg = lane >> 4;
-    const int c = tid % DK, part = tid / DK;
+    const bool own = tid < G::ACTIVE;
+    const int q4 = tid % G::NQ, part = own ? tid / G::NQ : PARTS - 1;
+    const int c0 = 4 * q4;                                    // my channels c0 .. c0+3
     const int T_ = args.T, H = args.H, NC = args.NC;
     const int unit = blockIdx.x;
     const int n = unit % NC, bh = unit / NC;
@@ -152,77 +179,123 @@ __global__ __launch_bounds__(kThreads) void prep_fast_kernel(PrepArgs args)
     T* QGg = static_cast<T*>(args.QG) + (size_t)unit * C * DK;
     T* Pg = static_cast<T*>(args.P) + (size_t)unit * C * C;
 
-    // ---- gate summary of my channel c over my tokens [part*TOK, +TOK) --------
-    float al[TOK], kk[TOK], qq[TOK], bt[TOK];
+    // ---- loads: my 4 channels over my TOK tokens (k, q kept in io precision) ----
+    // (rows past the end re-read the last valid row and become no-op tokens)
+    float al[TOK][4], bt[TOK];
+    Vec4<T> kv[TOK], qv[TOK];
 #pragma unroll
     for (int j = 0; j < TOK; ++j) {
-        const int r = part * TOK + j;
-        if (r < nvalid) {
-            al[j] = ga[r * rs + c];
-            kk[j] = ldf(gk + r * rs + c);
-            qq[j] = ldf(gq + r * rs + c);
-            bt[j] = gb[r * H];
-        } else {
-            al[j] = 1.f; kk[j] = 0.f; qq[j] = 0.f; bt[j] = 0.f;
+        const int r = min(part * TOK + j, nvalid - 1);
+        const float4 a4 = *reinterpret_cast<const float4*>(ga + r * rs + c0);
+        kv[j] = Vec4<T>::load(gk + r * rs + c0);
+        qv[j] = Vec4<T>::load(gq + r * rs + c0);
+        al[j][0] = a4.x; al[j][1] = a4.y; al[j][2] = a4.z; al[j][3] = a4.w;
+        bt[j] = gb[r * H];
+    }
+#pragma unroll
+    for (int j = 0; j < TOK; ++j) {
+        if (part * TOK + j >= nvalid) {
+            bt[j] = 0.f;
+            kv[j] = Vec4<T>::zero();
+            qv[j] = Vec4<T>::zero();
+#pragma unroll
+            for (int x = 0; x < 4; ++x) al[j][x] = 1.f;
         }
     }
-    float Lr[TOK];
-    int pr[TOK], sg[TOK];
+
+    // ---- gate summary: per channel, L (log2 magnitude), parity and zero count
+    //      cumulated over my tokens, then offset by the earlier token ranges ------
+    float Lr[TOK][4];
+    unsigned ps[TOK];                  // byte x: (seg << 1 | parity) of channel c0 + x
     {
-        float ls = 0.f;
-        int par = 0, nz = 0;
+        float ls[4] = {0.f, 0.f, 0.f, 0.f};
+        int pz[4] = {0, 0, 0, 0};
 #pragma unroll
         for (int j = 0; j < TOK; ++j) {
-            const float a = al[j];
-            if (a == 0.f) nz += 1;
-            else ls += flog2(fabsf(a));
-            par ^= (a < 0.f) ? 1 : 0;
-            Lr[j] = ls; pr[j] = par; sg[j] = nz;
-        }
-        partL[part * DK + c] = ls;
-        partP[part * DK + c] = par;
-        partZ[part * DK + c] = nz;
-        if (c == 0) {
+            ps[j] = 0;
 #pragma unroll
-            for (int j = 0; j < TOK; ++j) sBeta[part * TOK + j] = bt[j];
+            for (int x = 0; x < 4; ++x) {
+                const float a = al[j][x];
+                if (a == 0.f) pz[x] += 2;
+                else ls[x] += flog2(fabsf(a));
+                pz[x] ^= (a < 0.f) ? 1 : 0;
+                Lr[j][x] = ls[x];
+                ps[j] |= (unsigned)pz[x] << (8 * x);
+            }
+        }
+        if (own) {
+            *reinterpret_cast<float4*>(partL + part * DK + c0) = make_float4(ls[0], ls[1], ls[2], ls[3]);
+            *reinterpret_cast<int4*>(partPZ + part * DK + c0) = make_int4(pz[0], pz[1], pz[2], pz[3]);
+            if (q4 == 0) {
+#pragma unroll
+                for (int j = 0; j < TOK; ++j) sBeta[part * TOK + j] = bt[j];
+            }
         }
     }
     __syncthreads();
-    float offL = 0.f, totL = 0.f;
-    int offP = 0, offZ = 0, totP = 0, totZ = 0;
+    float offL[4] = {0.f, 0.f, 0.f, 0.f}, totL[4] = {0.f, 0.f, 0.f, 0.f};
+    int offPZ[4] = {0, 0, 0, 0}, totPZ[4] = {0, 0, 0, 0};   // (seg sum) << 1 | parity
+#pragma unroll 8
+    for (int p = 0; p < PARTS; ++p) {
+        const float4 l = *reinterpret_cast<const float4*>(partL + p * DK + c0);
+        const int4 z = *reinterpret_cast<const int4*>(partPZ + p * DK + c0);
+        const float lv[4] = {l.x, l.y, l.z, l.w};
+        const int zv[4] = {z.x, z.y, z.z, z.w};
 #pragma unroll
-    for (int p = 0; p < TPC; ++p) {
-        const float l = partL[p * DK + c];
-        const int pp = partP[p * DK + c], zz = partZ[p * DK + c];
-        if (p < part) { offL += l; offP ^= pp; offZ += zz; }
-        totL += l; totP ^= pp; totZ += zz;
+        for (int x = 0; x < 4; ++x) {
+            const int comb = ((zv[x] >> 1) << 1) + (zv[x] & 1);   // same encoding
+            if (p < part) { offL[x] += lv[x]; offPZ[x] = ((offPZ[x] >> 1) + (comb >> 1)) << 1 | ((offPZ[x] ^ comb) & 1); }
+            totL[x] += lv[x];
+            totPZ[x] = ((totPZ[x] >> 1) + (comb >> 1)) << 1 | ((totPZ[x] ^ comb) & 1);
+        }
     }
+    {
+        // bytes hold 2 seg + parity <= 2 C + 1 < 256: add the even part, xor the parity
+        unsigned addp = 0, xorp = 0;
 #pragma unroll
-    for (int j = 0; j < TOK; ++j) { Lr[j] += offL; pr[j] ^= offP; sg[j] += offZ; }
-    if (part == 0) sBase[c] = totZ;
+        for (int x = 0; x < 4; ++x) {
+            addp |= (unsigned)(offPZ[x] & ~1) << (8 * x);
+            xorp |= (unsigned)(offPZ[x] & 1) << (8 * x);
+        }
+#pragma unroll
+        for (int j = 0; j < TOK; ++j) {
+            ps[j] = (ps[j] + addp) ^ xorp;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) Lr[j][x] += offL[x];
+        }
+    }
+    if (own && part == 0) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) sBase[c0 + x] = totPZ[x] >> 1;
+    }
     __syncthreads();
-    // exclusive prefix of the per-channel zero counts -> first extra column of c
+    // exclusive prefix of the per-channel zero counts -> first extra column of a channel
     if (wave == 0) {
         int carry = 0;
-        for (int c0 = 0; c0 < DK; c0 += 64) {
-            const int v = (c0 + lane < DK) ? sBase[c0 + lane] : 0;
+        for (int cc = 0; cc < DK; cc += 64) {
+            const int v = (cc + lane < DK) ? sBase[cc + lane] : 0;
             int incl = v;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const int y = __shfl_up(incl, off, 64);
                 if (lane >= off) incl += y;
             }
-            if (c0 + lane < DK) sBase[c0 + lane] = carry + incl - v;
+            if (cc + lane < DK) sBase[cc + lane] = carry + incl - v;
             carry += __shfl(incl, 63, 64);
         }
         if (lane == 0) misc[0] = carry;
     }
     __syncthreads();
-    const int base_c = sBase[c];
     const int Ztot = misc[0];
-    const float M = 0.5f * totL;
-    const bool bad = (-M > kHalfSpanMax) || (Ztot > args.zx) || !(M <= 0.f);
-    if (__syncthreads_or(bad)) {
+    float M[4], E[4];
+    bool bad = Ztot > args.zx;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+        M[x] = 0.5f * totL[x];
+        bad = bad || (-M[x] > kHalfSpanMax) || !(M[x] <= 0.f);
+        E[x] = fexp2(M[x]);
+    }
+    if (__syncthreads_or(bad && own)) {
         if (tid == 0) args.FL[unit] = 1;
         return;
     }
@@ -230,60 +303,107 @@ __global__ __launch_bounds__(kThreads) void prep_fast_kernel(PrepArgs args)
 
     // ---- factored operands (LDS), Q*Gamma (staged), Ktil (direct) ---------------
     const int KP = ((DK + Ztot + KB - 1) / KB) * KB;     // contraction length
-    {
+    if (KP > DK) {
         const int ext = KP - DK;
         for (int idx = tid; idx < 3 * C * ext; idx += kThreads) {
             const int m = idx / (C * ext), rem = idx % (C * ext);
             const int r = rem / ext, col = DK + rem % ext;
             XA[m * C * KS + r * KS + col] = from_f32<T>(0.f);
         }
+        __syncthreads();
     }
-    __syncthreads();
-    float xw[TOK], kt[TOK];
+    Vec4<T> xw[TOK];
+    float kt[TOK][4];
 #pragma unroll
     for (int j = 0; j < TOK; ++j) {
         const int r = part * TOK + j;
-        const float sgn = pr[j] ? -1.f : 1.f;
-        const float F = sgn * fexp2(Lr[j] - M), Gf = sgn * fexp2(M - Lr[j]);
-        const int col = sg[j] == 0 ? c : DK + base_c + sg[j] - 1;
-        XA[r * KS + col] = from_f32<T>(bt[j] * kk[j] * F);
-        XP[r * KS + col] = from_f32<T>(qq[j] * F);
-        Y[r * KS + col] = from_f32<T>(kk[j] * Gf);
-        if (col != c) {
-            XA[r * KS + c] = from_f32<T>(0.f);
-            XP[r * KS + c] = from_f32<T>(0.f);
-            Y[r * KS + c] = from_f32<T>(0.f);
+        float fa[4], fp[4], fy[4], fq[4], fw[4];
+        int segs[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const unsigned pb = (ps[j] >> (8 * x)) & 0xffu;
+            const int seg = (int)(pb >> 1);
+            const float sgn = (pb & 1u) ? -1.f : 1.f;
+            const float kx = kv[j].get(x), qx = qv[j].get(x);
+            const float Fv = sgn * fexp2(Lr[j][x] - M[x]), Gv = sgn * fexp2(M[x] - Lr[j][x]);
+            fa[x] = bt[j] * kx * Fv;
+            fp[x] = qx * Fv;
+            fy[x] = kx * Gv;
+            const float gam = seg == 0 ? Fv * E[x] : 0.f;                     // Gamma_r
+            fq[x] = qx * gam;
+            fw[x] = bt[j] * kx * gam;
+            const float stot = (totPZ[x] & 1) ? -1.f : 1.f;
+            const float re = (seg == (totPZ[x] >> 1)) ? stot * E[x] * Gv : 0.f;   // rho(C-1, r)
+            kt[j][x] = kx * re;
+            segs[x] = seg;
         }
-        const float gam = sg[j] == 0 ? sgn * fexp2(Lr[j]) : 0.f;
-        sQG[r * QS + c] = from_f32<T>(qq[j] * gam);
-        xw[j] = bt[j] * kk[j] * gam;
-        const float re = (sg[j] == totZ) ? ((pr[j] ^ totP) ? -1.f : 1.f) * fexp2(totL - Lr[j]) : 0.f;
-        kt[j] = kk[j] * re;
-    }
-    // Ktil is an A operand with rows = channels, k = tokens: the 32 tokens of
-    // one k32 block that I own fill 4 whole fragments (one per lane group)
-    if constexpr (KB == 32 && TOK == 32) {
+        xw[j] = Vec4<T>::from(fw);
+        if (own) {
+            *reinterpret_cast<Vec4<T>*>(sQG + r * XWS + c0) = Vec4<T>::from(fq);
+            if (Ztot == 0) {
+                *reinterpret_cast<Vec4<T>*>(XA + r * KS + c0) = Vec4<T>::from(fa);
+                *reinterpret_cast<Vec4<T>*>(XP + r * KS + c0) = Vec4<T>::from(fp);
+                *reinterpret_cast<Vec4<T>*>(Y + r * KS + c0) = Vec4<T>::from(fy);
+            } else {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            float f[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) f[j] = kt[16 * (j >> 2) + 4 * g + (j & 3)];
-            *reinterpret_cast<F*>(Ktg + frag_off<KB>(c, part * 32 + 4 * g, C)) = F::from(f);
+                for (int x = 0; x < 4; ++x) {
+                    const int c = c0 + x;
+                    const int col = segs[x] == 0 ? c : DK + sBase[c] + segs[x] - 1;
+                    XA[r * KS + col] = from_f32<T>(fa[x]);
+                    XP[r * KS + col] = from_f32<T>(fp[x]);
+                    Y[r * KS + col] = from_f32<T>(fy[x]);
+                    if (col != c) {
+                        XA[r * KS + c] = from_f32<T>(0.f);
+                        XP[r * KS + c] = from_f32<T>(0.f);
+                        Y[r * KS + c] = from_f32<T>(0.f);
+                    }
+                }
+            }
         }
-    } else {
-#pragma unroll
-        for (int j = 0; j < TOK; ++j)
-            Ktg[frag_off<KB>(c, part * TOK + j, C)] = from_f32<T>(kt[j]);
     }
-    if (part == 0)
-        args.GC[(size_t)unit * DK + c] = totZ == 0 ? (totP ? -1.f : 1.f) * fexp2(totL) : 0.f;
+    if (own) {
+        // Ktil: A operand with rows = channels, k = tokens; 4 consecutive tokens
+        // starting at a multiple of 4 are 4 consecutive slots of one fragment
+        if constexpr (TOK % 4 == 0) {
+#pragma unroll
+            for (int j0 = 0; j0 < TOK; j0 += 4)
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const float f4[4] = {kt[j0][x], kt[j0 + 1][x], kt[j0 + 2][x], kt[j0 + 3][x]};
+                    *reinterpret_cast<Vec4<T>*>(Ktg + frag_off<KB>(c0 + x, part * TOK + j0, C)) =
+                        Vec4<T>::from(f4);
+                }
+        } else {
+#pragma unroll
+            for (int j = 0; j < TOK; ++j)
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+                    Ktg[frag_off<KB>(c0 + x, part * TOK + j, C)] = from_f32<T>(kt[j][x]);
+        }
+        if (part == 0) {
+            float g4[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+                g4[x] = (totPZ[x] >> 1) == 0 ? ((totPZ[x] & 1) ? -1.f : 1.f) * E[x] * E[x] : 0.f;
+            *reinterpret_cast<float4*>(args.GC + (size_t)unit * DK + c0) = make_float4(g4[0], g4[1], g4[2], g4[3]);
+        }
+    }
     __syncthreads();
+    // V tile loads: in flight during the Q*Gamma emission and the A / P tiles
+    const int vpr = Dv / VEC, nvv = C * vpr;
+    uint4 vreg[G::VPT];
+#pragma unroll
+    for (int x = 0; x < G::VPT; ++x) {
+        const int idx = min(tid + x * kThreads, nvv - 1);
+        const int r = min(idx / vpr, nvalid - 1);
+        vreg[x] = *reinterpret_cast<const uint4*>(gv + r * rsv + (idx % vpr) * VEC);
+    }
     // Q*Gamma fragments: 64 lanes x (C/16) x (DK/KB) per chunk
     for (int f = tid; f < (C / 16) * NKD * 64; f += kThreads) {
         const int l = f & 63, blk = f >> 6;
         const int mt = blk / NKD, s = blk % NKD;
         *reinterpret_cast<F*>(QGg + (size_t)f * NV) =
-            gather_frag<T, KB>(sQG + (16 * mt + (l & 15)) * QS, s, l >> 4);
+            gather_frag<T, KB>(sQG + (16 * mt + (l & 15)) * XWS, s, l >> 4);
     }
     __syncthreads();   // the staging area becomes sA
 
@@ -319,9 +439,9 @@ __global__ __launch_bounds__(kThreads) void prep_fast_kernel(PrepArgs args)
             }
         }
     }
-    __syncthreads();   // operands dead: the region now holds sT, Xt, Vt
+    __syncthreads();   // operands dead: the region now holds sT, sXW, sV
 
-    // ---- Tinv diagonal blocks; stage X_W^T and (diag(beta) V)^T ----------------
+    // ---- Tinv diagonal blocks; stage X_W and diag(beta) V row-major -------------
     if (wave < NB && lane < 16) {
         const int a = wave, j = lane;
         float t[16];
@@ -339,13 +459,25 @@ __global__ __launch_bounds__(kThreads) void prep_fast_kernel(PrepArgs args)
         const int r = idx / C, col = idx % C;
         if ((col >> 4) > (r >> 4)) sT[r * LDF + col] = 0.f;
     }
+    if (own) {
 #pragma unroll
-    for (int j = 0; j < TOK; ++j) Xt[c * KCS + part * TOK + j] = from_f32<T>(xw[j]);
-    for (int idx = tid; idx < C * Dv; idx += kThreads) {
-        const int r = idx / Dv, cv = idx % Dv;
-        float y = 0.f;
-        if (r < nvalid) y = sBeta[r] * ldf(gv + r * rsv + cv);
-        Vt[cv * KCS + r] = from_f32<T>(y);
+        for (int j = 0; j < TOK; ++j)
+            *reinterpret_cast<Vec4<T>*>(sXW + (part * TOK + j) * XWS + c0) = xw[j];
+    }
+#pragma unroll
+    for (int x = 0; x < G::VPT; ++x) {
+        const int idx = tid + x * kThreads;
+        if (idx < nvv) {
+            const int r = idx / vpr, cv = (idx % vpr) * VEC;
+            const float bsc = r < nvalid ? sBeta[r] : 0.f;
+            const T* e = reinterpret_cast<const T*>(&vreg[x]);
+            float y[VEC];
+#pragma unroll
+            for (int z = 0; z < VEC; ++z) y[z] = bsc * to_f32(e[z]);
+#pragma unroll
+            for (int z = 0; z < VEC; z += 4)
+                *reinterpret_cast<Vec4<T>*>(sV + r * VS + cv + z) = Vec4<T>::from(y + z);
+        }
     }
     __syncthreads();
     // ---- Tinv off-diagonal blocks by block distance (fp32 MFMA) ----------------
@@ -384,13 +516,12 @@ __global__ __launch_bounds__(kThreads) void prep_fast_kernel(PrepArgs args)
 #pragma unroll
                 for (int u = 0; u < TPB; ++u) {
                     const int ct = s * TPB + u;
-                    // W^T[16ct + 4g + i][16mt + n] = X_W^T rows . Tinv rows
-                    const T* arow = Xt + (16 * ct + ln) * KCS;
+                    // W^T[16ct + 4g + i][16mt + n] = sum_j X_W[j][16ct + .] Tinv[16mt + n][j]
                     const float* brow = sT + (16 * mt + ln) * LDF;
                     f32x4 acc = zero4();
 #pragma unroll
                     for (int k0 = 0; k0 < C; k0 += KB)
-                        acc = mma(frag_row<T, KB>(arow, k0), frag_row_cvt<T, KB>(brow, k0), acc);
+                        acc = mma(frag_col<T, KB>(sXW + 16 * ct, XWS, k0), frag_row_cvt<T, KB>(brow, k0), acc);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) f[4 * u + i] = acc[i];
                 }
@@ -398,11 +529,10 @@ __global__ __launch_bounds__(kThreads) void prep_fast_kernel(PrepArgs args)
             } else {
                 const int ut = it - nwi, mt = ut % NM, nt = ut / NM;
                 const float* arow = sT + (16 * mt + ln) * LDF;
-                const T* brow = Vt + (16 * nt + ln) * KCS;
                 f32x4 acc = zero4();
 #pragma unroll
                 for (int k0 = 0; k0 < C; k0 += KB)
-                    acc = mma(frag_row_cvt<T, KB>(arow, k0), frag_row<T, KB>(brow, k0), acc);
+                    acc = mma(frag_row_cvt<T, KB>(arow, k0), frag_col<T, KB>(sV + 16 * nt, VS, k0), acc);
                 *reinterpret_cast<f32x4*>(Ug + ((size_t)(mt * NUt + nt) * 64 + lane) * 4) = acc;
             }
         }
@@ -412,7 +542,7 @@ __global__ __launch_bounds__(kThreads) void prep_fast_kernel(PrepArgs args)
 template <typename T, int C, int DK>
 hipError_t launch_fast_t(const ChunkShape& s, const PrepArgs& a, hipStream_t stream)
 {
-    const FastLayout<T, C, DK> LY(a.zx, sizeof(T) == 4 ? 64 : 128);
+    const FastLayout<T, C, DK> LY(a.zx);
     auto kern = prep_fast_kernel<T, C, DK>;
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -424,7 +554,7 @@ hipError_t launch_fast_t(const ChunkShape& s, const PrepArgs& a, hipStream_t str
 }
 
 template <typename T, int C, int DK>
-size_t fast_lds_t(int zx) { return FastLayout<T, C, DK>(zx, sizeof(T) == 4 ? 64 : 128).total; }
+size_t fast_lds_t(int zx) { return FastLayout<T, C, DK>(zx).total; }
 
 template <typename T, int C>
 hipError_t dispatch_dk(const ChunkShape& s, const PrepArgs& a, hipStream_t st)
