@@ -179,19 +179,23 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
     };
 
     // operand ring: chunk nc uses ops[nc % 3]; the loads of chunks nc+1 and
-    // nc+2 are in flight while chunk nc computes
+    // nc+2 are in flight while chunk nc computes.  Past the last chunk the
+    // ring re-reads the last chunk instead of skipping the loads: every path
+    // through the loop then issues the same loads, so the compiler's wait
+    // counts stay exact and the waits only cover the chunk being used.
     ChainOps<T, C, DK> ops[3];
     const size_t u0 = (size_t)bh * NC;
+    const int last = NC - 1;
     load_ops(ops[0], a, u0, wave, lane, lg, slice);
-    if (NC > 1) load_ops(ops[1], a, u0 + 1, wave, lane, lg, slice);
+    load_ops(ops[1], a, u0 + min(1, last), wave, lane, lg, slice);
     for (int nc = 0; nc < NC; nc += 3) {
-        if (nc + 2 < NC) load_ops(ops[2], a, u0 + nc + 2, wave, lane, lg, slice);
+        load_ops(ops[2], a, u0 + min(nc + 2, last), wave, lane, lg, slice);
         step(ops[0], nc);
         if (nc + 1 >= NC) break;
-        if (nc + 3 < NC) load_ops(ops[0], a, u0 + nc + 3, wave, lane, lg, slice);
+        load_ops(ops[0], a, u0 + min(nc + 3, last), wave, lane, lg, slice);
         step(ops[1], nc + 1);
         if (nc + 2 >= NC) break;
-        if (nc + 4 < NC) load_ops(ops[1], a, u0 + nc + 4, wave, lane, lg, slice);
+        load_ops(ops[1], a, u0 + min(nc + 4, last), wave, lane, lg, slice);
         step(ops[2], nc + 2);
     }
 
@@ -214,8 +218,7 @@ hipError_t launch_chain_t(const ChunkShape& s, const ChainArgs& a, hipStream_t s
     const int NS = s.Dv / 16;
     const int bh = s.B * s.H;
     const unsigned grid = (unsigned)(kXcds * NS * ((bh + kXcds - 1) / kXcds));
-    hipLaunchKernelGGL((chain_kernel<T, C, DK>), dim3(grid), dim3(kChainThreads), 0, stream, a);
-    return hipGetLastError();
+    return launch_kernel(chain_kernel<T, C, DK>, dim3(grid), dim3(kChainThreads), 0, stream, a);
 }
 
 template <typename T, int C>

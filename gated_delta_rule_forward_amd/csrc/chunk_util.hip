@@ -4,6 +4,8 @@
 
 namespace kda {
 
+thread_local LaunchTimer g_launch_timer;
+
 namespace {
 
 __global__ void state_copy_kernel(const float* __restrict__ src, float* __restrict__ dst, size_t n)
@@ -33,8 +35,7 @@ hipError_t launch_state_copy(const float* S0, float* ST, size_t n, hipStream_t s
 {
     if (n == 0) return hipSuccess;
     const unsigned grid = (unsigned)((n + 255) / 256);
-    hipLaunchKernelGGL(state_copy_kernel, dim3(grid), dim3(256), 0, stream, S0, ST, n);
-    return hipGetLastError();
+    return launch_kernel(state_copy_kernel, dim3(grid), dim3(256), 0, stream, S0, ST, n);
 }
 
 }  // namespace kda

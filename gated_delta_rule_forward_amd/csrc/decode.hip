@@ -126,13 +126,12 @@ hipError_t launch_decode_t(int B, int H, int Dk, int Dv, const void* q, const vo
     const T* vv = static_cast<const T*>(v);
     T* oo = static_cast<T*>(out);
     switch (Dk) {
-    case 16: hipLaunchKernelGGL((decode_kernel<T, 16>), grid, block, 0, stream, qq, kk, vv, alpha, beta, state, oo, Dv); break;
-    case 32: hipLaunchKernelGGL((decode_kernel<T, 32>), grid, block, 0, stream, qq, kk, vv, alpha, beta, state, oo, Dv); break;
-    case 64: hipLaunchKernelGGL((decode_kernel<T, 64>), grid, block, 0, stream, qq, kk, vv, alpha, beta, state, oo, Dv); break;
-    case 128: hipLaunchKernelGGL((decode_kernel<T, 128>), grid, block, 0, stream, qq, kk, vv, alpha, beta, state, oo, Dv); break;
+    case 16: return launch_kernel(decode_kernel<T, 16>, grid, block, 0, stream, qq, kk, vv, alpha, beta, state, oo, Dv);
+    case 32: return launch_kernel(decode_kernel<T, 32>, grid, block, 0, stream, qq, kk, vv, alpha, beta, state, oo, Dv);
+    case 64: return launch_kernel(decode_kernel<T, 64>, grid, block, 0, stream, qq, kk, vv, alpha, beta, state, oo, Dv);
+    case 128: return launch_kernel(decode_kernel<T, 128>, grid, block, 0, stream, qq, kk, vv, alpha, beta, state, oo, Dv);
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace

@@ -66,9 +66,8 @@ hipError_t launch_gate_prep(const float* alpha, float* L, uint8_t* meta, float* 
 {
     const int NC = (T + C - 1) / C;
     const dim3 grid((unsigned)((size_t)B * H * NC)), block(128);
-    hipLaunchKernelGGL(gate_prep_kernel, grid, block, 0, stream, alpha, L, meta, gend, T, H, Dk,
-                       C, NC);
-    return hipGetLastError();
+    return launch_kernel(gate_prep_kernel, grid, block, 0, stream, alpha, L, meta, gend, T, H, Dk,
+                         C, NC);
 }
 
 }  // namespace kda

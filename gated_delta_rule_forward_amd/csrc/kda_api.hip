@@ -41,10 +41,12 @@ bool overlaps(const void* p, size_t n, const void* q, size_t m)
 }
 
 // ---- per-kernel events (opt-in) ---------------------------------------------
+// Stage i owns events 2i and 2i+1, attached to its kernel launch: the elapsed
+// time between them is that kernel's own duration.
 constexpr int kMaxStages = 8;
 struct StageEvents {
     std::mutex mu;
-    hipEvent_t ev[kMaxStages + 1] = {};
+    hipEvent_t ev[2 * kMaxStages] = {};
     const char* names[kMaxStages] = {};
     int count = 0;
     bool created = false;
@@ -54,7 +56,7 @@ StageEvents g_stage;
 hipError_t stage_begin()
 {
     if (!g_stage.created) {
-        for (int i = 0; i <= kMaxStages; ++i) {
+        for (int i = 0; i < 2 * kMaxStages; ++i) {
             const hipError_t e = hipEventCreate(&g_stage.ev[i]);
             if (e != hipSuccess) return e;
         }
@@ -67,19 +69,22 @@ hipError_t stage_begin()
 struct Recorder {
     bool on;
     hipStream_t stream;
-    hipError_t mark(const char* name_of_next)   // event before a kernel
+    hipError_t mark(const char* name_of_next)   // the next launch is stage `name`
     {
         if (!on) return hipSuccess;
         if (g_stage.count >= kMaxStages) return hipErrorInvalidValue;
         g_stage.names[g_stage.count] = name_of_next;
-        return hipEventRecord(g_stage.ev[g_stage.count], stream);
+        kda::g_launch_timer = {g_stage.ev[2 * g_stage.count], g_stage.ev[2 * g_stage.count + 1]};
+        return hipSuccess;
     }
-    hipError_t done()   // event after that kernel
+    hipError_t done()   // that launch has been enqueued
     {
         if (!on) return hipSuccess;
+        kda::g_launch_timer = {};
         g_stage.count += 1;
-        return hipEventRecord(g_stage.ev[g_stage.count], stream);
+        return hipSuccess;
     }
+    ~Recorder() { if (on) kda::g_launch_timer = {}; }
 };
 
 // fields shared by the forward and its workspace query
@@ -306,10 +311,11 @@ kda_status_t kda_last_stage_times(float* ms, const char** names, int max, int* c
     std::lock_guard<std::mutex> lock(g_stage.mu);
     *count = g_stage.count;
     if (!g_stage.created || g_stage.count == 0) return KDA_OK;
-    if (hipEventSynchronize(g_stage.ev[g_stage.count]) != hipSuccess) return KDA_ERR_HIP;
+    if (hipEventSynchronize(g_stage.ev[2 * g_stage.count - 1]) != hipSuccess) return KDA_ERR_HIP;
     for (int i = 0; i < g_stage.count && i < max; ++i) {
         float t = 0.f;
-        if (hipEventElapsedTime(&t, g_stage.ev[i], g_stage.ev[i + 1]) != hipSuccess) return KDA_ERR_HIP;
+        if (hipEventElapsedTime(&t, g_stage.ev[2 * i], g_stage.ev[2 * i + 1]) != hipSuccess)
+            return KDA_ERR_HIP;
         ms[i] = t;
         if (names) names[i] = g_stage.names[i];
     }

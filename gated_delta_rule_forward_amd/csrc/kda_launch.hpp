@@ -4,12 +4,30 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stddef.h>
 #include <stdint.h>
 
 namespace kda {
 
 enum class IoType { F32 = 0, BF16 = 1 };
+
+// Events attached to the next kernel launch of this thread (both null = none).
+// Launchers pass them to hipExtLaunchKernelGGL, which stamps them with the
+// kernel's own start and end, so a stage time is the kernel's duration.
+struct LaunchTimer {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+extern thread_local LaunchTimer g_launch_timer;
+
+template <typename K, typename... Args>
+inline hipError_t launch_kernel(K kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t stream,
+                                Args... args)
+{
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, g_launch_timer.start,
+                          g_launch_timer.stop, 0, args...);
+    return hipGetLastError();
+}
 
 struct PrepArgs;
 struct ChainArgs;

@@ -332,8 +332,7 @@ hipError_t launch_exact_t(const ChunkShape& s, const PrepArgs& a, hipStream_t st
     if (e != hipSuccess) return e;
     const int nu = (int)((size_t)s.B * s.H * s.NC);
     const int grid = nu < 512 ? nu : 512;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kPrepThreads), L::TOTAL, stream, a, nu);
-    return hipGetLastError();
+    return launch_kernel(kern, dim3(grid), dim3(kPrepThreads), (uint32_t)L::TOTAL, stream, a, nu);
 }
 
 template <typename T, int C>

@@ -549,8 +549,7 @@ hipError_t launch_fast_t(const ChunkShape& s, const PrepArgs& a, hipStream_t str
                                              (int)LY.total);
     if (e != hipSuccess) return e;
     const unsigned nunits = (unsigned)((size_t)s.B * s.H * s.NC);
-    hipLaunchKernelGGL(kern, dim3(nunits), dim3(kThreads), LY.total, stream, a);
-    return hipGetLastError();
+    return launch_kernel(kern, dim3(nunits), dim3(kThreads), (uint32_t)LY.total, stream, a);
 }
 
 template <typename T, int C, int DK>

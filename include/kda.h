@@ -68,9 +68,10 @@ typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype_t;
  * guarantee. */
 typedef enum { KDA_MODE_KDA = 0, KDA_MODE_CKDA = 1 } kda_mode_t;
 
-/* flags: record a HIP event around every kernel of this call so that
- * kda_last_stage_times() can report per-kernel durations (adds event records
- * on `stream`; performs no extra work on the data). */
+/* flags: attach a pair of HIP events to every kernel launch of this call
+ * (hipExtLaunchKernelGGL start/stop events, stamped by the kernel's own start
+ * and end) so that kda_last_stage_times() can report per-kernel durations;
+ * performs no extra work on the data. */
 #define KDA_FLAG_STAGE_EVENTS 2u
 
 /* ABI version of the loaded library (KDA_ABI_VERSION it was built with). */
