@@ -13,11 +13,22 @@
 // state row tiles w, w+4, ...; the state and Delta are exchanged through LDS
 // already in MFMA B-fragment form (one 8- or 16-byte slot per lane).  Two
 // barriers per chunk.  The fp32 state slice stays in registers for the whole
-// sequence.  Operand fragments of chunks c+1 and c+2 are in flight while
-// chunk c computes; the prep kernels store them fragment-major, so each
-// wavefront's fragment of one MFMA is one contiguous 1 KB block.  Workgroups are numbered so that the column slices
-// of one (b, h) land on the same XCD (consecutive workgroup ids go to
-// consecutive XCDs) and share that XCD's L2 for the chunk operands.
+// sequence.
+//
+// Operands reach the wavefronts through a two-stage LDS FIFO per wavefront,
+// filled with direct global-to-LDS loads (no registers held while in flight):
+// the prep kernels store every operand fragment-major, so one wavefront's
+// fragment of one MFMA is one contiguous block that a single 16-byte-per-lane
+// load copies verbatim.  At the start of chunk c the wave waits for chunk c's
+// stage, moves its fragments into registers and refills the same stage with
+// chunk c+2, so chunk c+1's loads are in flight for a whole step and chunk
+// c+2's for most of one.  The loads are not visible to the compiler's wait
+// counting, so the waits are explicit: every step issues exactly NDMA loads,
+// hence "at most NDMA outstanding" means the older stage has landed.
+//
+// Workgroups are numbered so that the column slices of one (b, h) land on the
+// same XCD (consecutive workgroup ids go to consecutive XCDs) and share that
+// XCD's L2 for the chunk operands.
 #include "kda_chunk.hpp"
 #include "kda_launch.hpp"
 
@@ -25,7 +36,8 @@ namespace kda {
 
 namespace {
 
-constexpr int kChainThreads = 256;
+constexpr int kChainWaves = 4;                        // compute wavefronts
+constexpr int kChainThreads = 64 * 2 * kChainWaves;   // + one loader wavefront each
 constexpr int kXcds = 8;
 
 template <typename T, int C, int DK>
@@ -37,51 +49,182 @@ struct ChainGeom {
     static constexpr int NKC = C / KB;           // k blocks over tokens
     static constexpr int SPW = (NT + 3) / 4;     // state tiles per wave
     static constexpr int TPB = KB / 16;          // tiles per k block
+    static constexpr int FB = 64 * (KB / 4) * (int)sizeof(T);   // bytes of one 64-lane fragment
+    // one wavefront's share of a chunk's operands in an LDS stage (byte offsets)
+    static constexpr int OW = 0;                      // W, its token tile      [NKD]
+    static constexpr int OQ = OW + NKD * FB;          // Q * Gamma              [NKD]
+    static constexpr int OP = OQ + NKD * FB;          // P                      [NKC]
+    static constexpr int OU = OP + NKC * FB;          // U tile (64 x 16 B)
+    static constexpr int OK = OU + 1024;              // Ktil, its state tiles  [SPW][NKC]
+    static constexpr int OG = OK + SPW * NKC * FB;    // Gamma_C rows of its state tiles [SPW][4][16 B]
+    static constexpr int STAGE = OG + SPW * 64;
+    static constexpr int runs(int bytes) { return (bytes + 1023) / 1024; }
+    // 16-byte-per-lane direct-to-LDS loads one wavefront issues per chunk
+    static constexpr int NDMA = 2 * runs(NKD * FB) + runs(NKC * FB) + 1 + SPW * runs(NKC * FB) + 1;
+    static constexpr size_t LDS = 2 * 4 * (size_t)STAGE;     // two stages, four waves
+    // plus the S and Delta exchange fragments and a 1 KB sink for L2 prefetches
+    static constexpr size_t XCH = LDS;
+    static constexpr size_t SINK = XCH + (size_t)(NKD + NKC) * 64 * (KB / 4) * sizeof(T);
+    static constexpr size_t LDS_TOTAL = SINK + 1024;
+    // L2 prefetch: 1 KB pieces of a chunk's blocks shared by the column slices
+    // (W, Q * Gamma, Ktil, P; only when whole kilobytes), plus each slice's U
+    // tiles; KPF prefetch loads per loader wavefront and step
+    static constexpr int PW = C * DK * (int)sizeof(T) / 1024, PP = C * C * (int)sizeof(T) / 1024;
+    static constexpr bool PREFETCH =
+        (C * DK * (int)sizeof(T)) % 1024 == 0 && (C * C * (int)sizeof(T)) % 1024 == 0;
+    static constexpr int PTOT = 3 * PW + PP;
+    static constexpr int KPF = PREFETCH ? 3 : 0;
+    static_assert(NDMA <= 63, "vmcnt holds at most 63 outstanding loads");
 };
 
+using lds_void = __attribute__((address_space(3))) void;
+
+// One 16-byte-per-lane direct global-to-LDS load: lane l's 16 bytes from its
+// own address land at LDS byte address dst + 16 l (dst wave-uniform, in M0).
+// Written as asm so that the compiler's wait insertion does not treat every
+// later LDS access as dependent on it (it would wait for all of them); the
+// kernel orders these loads with explicit waits instead.  No register is
+// written by the instruction.
+__device__ __forceinline__ void dma16(const void* src, const unsigned char* dst)
+{
+    const unsigned m0 = (unsigned)(uintptr_t)(const lds_void*)dst;
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(src), "s"(m0) : "memory", "m0");
+}
+
+// copy `bytes` (a multiple of 512) contiguous global bytes into LDS;
+// lane l of each 1 KB step lands at +16 l
+template <int BYTES>
+__device__ __forceinline__ void dma_run(const unsigned char* src, unsigned char* dst, int lane)
+{
+#pragma unroll
+    for (int off = 0; off < BYTES; off += 1024) {
+        if (off + 1024 <= BYTES || lane < 32) dma16(src + off + 16 * lane, dst + off);
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// workgroup barrier for the S / Delta exchange: waits for this wave's LDS
+// accesses only.  __syncthreads() would also wait for the in-flight
+// direct-to-LDS loads (they count as LDS writes), draining the FIFO.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// enqueue one chunk's operands for this wavefront into its stage region, in
+// three parts spread over a step (PART 0: W, Q*Gamma; 1: P, U; 2: Ktil,
+// Gamma_C) so the load pipe drains while the wave computes.  Waves without a
+// token tile or state tile load the last one instead, so every wavefront
+// issues exactly NDMA loads per chunk.
+template <typename T, int C, int DK, int PART>
+__device__ __forceinline__ void issue_chunk(unsigned char* st, const ChainArgs& a, size_t unit,
+                                            int wave, int lane, int slice)
+{
+    using G = ChainGeom<T, C, DK>;
+    const int mt = wave < G::NM ? wave : G::NM - 1;
+    const int Dv = a.Dv;
+    if constexpr (PART == 0) {
+        const size_t off = (unit * C * DK + (size_t)mt * G::NKD * 64 * (G::KB / 4)) * sizeof(T);
+        dma_run<G::NKD * G::FB>(static_cast<const unsigned char*>(a.W) + off, st + G::OW, lane);
+        dma_run<G::NKD * G::FB>(static_cast<const unsigned char*>(a.QG) + off, st + G::OQ, lane);
+    } else if constexpr (PART == 1) {
+        const unsigned char* P = static_cast<const unsigned char*>(a.P) +
+                                 (unit * C * C + (size_t)mt * G::NKC * 64 * (G::KB / 4)) * sizeof(T);
+        const unsigned char* U = reinterpret_cast<const unsigned char*>(
+            a.U + unit * C * Dv + (size_t)(mt * (Dv / 16) + slice) * 64 * 4);
+        dma_run<G::NKC * G::FB>(P, st + G::OP, lane);
+        dma_run<1024>(U, st + G::OU, lane);
+    } else {
+#pragma unroll
+        for (int u = 0; u < G::SPW; ++u) {
+            const int t = (wave + 4 * u) < G::NT ? wave + 4 * u : G::NT - 1;
+            const unsigned char* Kt = static_cast<const unsigned char*>(a.Kt) +
+                                      (unit * DK * C + (size_t)t * G::NKC * 64 * (G::KB / 4)) * sizeof(T);
+            dma_run<G::NKC * G::FB>(Kt, st + G::OK + u * G::NKC * G::FB, lane);
+        }
+        // Gamma_C: lane j < 4 SPW fetches rows 16t + 4(j % 4) .. +3 of state tile
+        // u = j / 4; they land at OG + 16 j
+        if (lane < 4 * G::SPW) {
+            const int u = lane >> 2;
+            const int t = (wave + 4 * u) < G::NT ? wave + 4 * u : G::NT - 1;
+            dma16(a.GC + unit * DK + 16 * t + 4 * (lane & 3), st + G::OG);
+        }
+    }
+}
+
+template <typename T, int C, int DK>
+__device__ __forceinline__ void issue_all(unsigned char* st, const ChainArgs& a, size_t unit,
+                                          int wave, int lane, int slice)
+{
+    issue_chunk<T, C, DK, 0>(st, a, unit, wave, lane, slice);
+    issue_chunk<T, C, DK, 1>(st, a, unit, wave, lane, slice);
+    issue_chunk<T, C, DK, 2>(st, a, unit, wave, lane, slice);
+}
+
+// KPF L2 prefetch loads of one chunk by loader `cw` of column slice `slice`
+// (of NS): the slice's pieces are every NS-th kilobyte of the shared blocks and
+// its own U tiles; the four loaders of a workgroup take every fourth piece.
+// The data lands in an LDS sink; the point is the L2 fill.  The column slices
+// of one (b, h) run on one XCD, so together they prefetch the whole chunk.
+template <typename T, int C, int DK>
+__device__ __forceinline__ void prefetch_chunk(const ChainArgs& a, size_t unit, int slice, int NS,
+                                               int cw, int lane, unsigned char* sink)
+{
+    using G = ChainGeom<T, C, DK>;
+    const int ps = (G::PTOT - slice + NS - 1) / NS;   // shared pieces of this slice
+    const int npw = ps + G::NM;
+    const size_t blk = (size_t)C * DK * sizeof(T);
+#pragma unroll
+    for (int i = 0; i < G::KPF; ++i) {
+        const int k = min(cw + kChainWaves * i, npw - 1);
+        const unsigned char* src;
+        if (k < ps) {
+            const int p = slice + NS * k;
+            if (p < G::PW) src = static_cast<const unsigned char*>(a.W) + unit * blk + (size_t)p * 1024;
+            else if (p < 2 * G::PW)
+                src = static_cast<const unsigned char*>(a.QG) + unit * blk + (size_t)(p - G::PW) * 1024;
+            else if (p < 3 * G::PW)
+                src = static_cast<const unsigned char*>(a.Kt) + unit * blk + (size_t)(p - 2 * G::PW) * 1024;
+            else
+                src = static_cast<const unsigned char*>(a.P) + unit * C * C * sizeof(T) +
+                      (size_t)(p - 3 * G::PW) * 1024;
+        } else {
+            src = reinterpret_cast<const unsigned char*>(
+                a.U + unit * C * a.Dv + (size_t)((k - ps) * NS + slice) * 64 * 4);
+        }
+        dma16(src + 16 * lane, sink);
+    }
+}
+
+// one chunk's operands of one wavefront, in registers
 template <typename T, int C, int DK>
 struct ChainOps {
     using G = ChainGeom<T, C, DK>;
     using F = Frag<T, G::KB>;
-    F w[G::NKD], qg[G::NKD], p[G::NKC];
-    float u[4];
-    F kt[G::SPW][G::NKC];
-    float gc[G::SPW][4];
+    F w[G::NKD], qg[G::NKD], p[G::NKC], kt[G::SPW][G::NKC];
+    f32x4 u, gc[G::SPW];
 };
 
 template <typename T, int C, int DK>
-__device__ __forceinline__ void load_ops(ChainOps<T, C, DK>& o, const ChainArgs& a, size_t unit,
-                                         int wave, int lane, int lg, int slice)
+__device__ __forceinline__ void read_ops(ChainOps<T, C, DK>& o, const unsigned char* st, int lane, int lg)
 {
     using G = ChainGeom<T, C, DK>;
     using F = Frag<T, G::KB>;
-    constexpr int NV = F::NV;
-    const int Dv = a.Dv;
-    if (G::NM == 4 || wave < G::NM) {
-        const T* W = static_cast<const T*>(a.W) + unit * C * DK + (size_t)wave * G::NKD * 64 * NV;
-        const T* QG = static_cast<const T*>(a.QG) + unit * C * DK + (size_t)wave * G::NKD * 64 * NV;
-        const T* P = static_cast<const T*>(a.P) + unit * C * C + (size_t)wave * G::NKC * 64 * NV;
 #pragma unroll
-        for (int s = 0; s < G::NKD; ++s) {
-            o.w[s] = F::load(W + (s * 64 + lane) * NV);
-            o.qg[s] = F::load(QG + (s * 64 + lane) * NV);
-        }
-#pragma unroll
-        for (int s = 0; s < G::NKC; ++s) o.p[s] = F::load(P + (s * 64 + lane) * NV);
-        const float4 u = *reinterpret_cast<const float4*>(
-            a.U + unit * C * Dv + ((size_t)(wave * (Dv / 16) + slice) * 64 + lane) * 4);
-        o.u[0] = u.x; o.u[1] = u.y; o.u[2] = u.z; o.u[3] = u.w;
+    for (int s = 0; s < G::NKD; ++s) {
+        o.w[s] = *reinterpret_cast<const F*>(st + G::OW + s * G::FB + lane * sizeof(F));
+        o.qg[s] = *reinterpret_cast<const F*>(st + G::OQ + s * G::FB + lane * sizeof(F));
     }
 #pragma unroll
-    for (int u = 0; u < G::SPW; ++u) {
-        const int t = wave + 4 * u;
-        if (G::NT % 4 == 0 || t < G::NT) {
-            const T* Kt = static_cast<const T*>(a.Kt) + unit * DK * C + (size_t)t * G::NKC * 64 * NV;
+    for (int s = 0; s < G::NKC; ++s)
+        o.p[s] = *reinterpret_cast<const F*>(st + G::OP + s * G::FB + lane * sizeof(F));
+    o.u = *reinterpret_cast<const f32x4*>(st + G::OU + lane * 16);
 #pragma unroll
-            for (int s = 0; s < G::NKC; ++s) o.kt[u][s] = F::load(Kt + (s * 64 + lane) * NV);
-            const float4 g = *reinterpret_cast<const float4*>(a.GC + unit * DK + 16 * t + 4 * lg);
-            o.gc[u][0] = g.x; o.gc[u][1] = g.y; o.gc[u][2] = g.z; o.gc[u][3] = g.w;
-        }
+    for (int u = 0; u < G::SPW; ++u) {
+#pragma unroll
+        for (int s = 0; s < G::NKC; ++s)
+            o.kt[u][s] = *reinterpret_cast<const F*>(st + G::OK + (u * G::NKC + s) * G::FB + lane * sizeof(F));
+        o.gc[u] = *reinterpret_cast<const f32x4*>(st + G::OG + (u * 4 + lg) * 16);
     }
 }
 
@@ -101,8 +244,9 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
 {
     using G = ChainGeom<T, C, DK>;
     using F = Frag<T, G::KB>;
-    __shared__ F sSf[G::NKD * 64];
-    __shared__ F sDf[G::NKC * 64];
+    extern __shared__ __attribute__((aligned(16))) unsigned char stages[];
+    F* sSf = reinterpret_cast<F*>(stages + G::XCH);
+    F* sDf = sSf + G::NKD * 64;
 
     const int Dv = a.Dv, H = a.H, T_ = a.T, NC = a.NC;
     const int NS = Dv / 16;
@@ -114,6 +258,38 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = slice * 16 + ln;
 
+    // Operand FIFO.  Chunk c is loaded into stage c & 1 by the loader
+    // wavefronts (wave 4 + w fills compute wave w's region) at the start of
+    // step c - 2 and moved into registers by the compute wavefronts at the end
+    // of step c - 1, between the step's two barriers: the loader waits for
+    // chunk c before barrier 1 of step c - 1, and stage c & 1 is free again
+    // after barrier 2 of step c - 1.  Past the last chunk the last one is
+    // re-read, so every step issues the same NDMA loads per loader.
+    const size_t u0 = (size_t)bh * NC;
+    const int last = NC - 1;
+    const int cw = wave & (kChainWaves - 1);     // the compute wave a loader serves
+    auto stg = [&](int c) { return stages + (size_t)((c & 1) * kChainWaves + cw) * G::STAGE; };
+    if (wave >= kChainWaves) {
+        // chunk c is also prefetched into L2 at step c - 5; the waits below
+        // let the two youngest prefetch rounds stay in flight
+        unsigned char* sink = stages + G::SINK;
+        issue_all<T, C, DK>(stg(0), a, u0, cw, lane, slice);
+        issue_all<T, C, DK>(stg(1), a, u0 + min(1, last), cw, lane, slice);
+        for (int c = 2; c < 5; ++c) prefetch_chunk<T, C, DK>(a, u0 + min(c, last), slice, NS, cw, lane, sink);
+        wait_vm<G::NDMA + 3 * G::KPF>();             // chunk 0 landed
+        lds_barrier();                               // B0: compute reads chunk 0
+        lds_barrier();                               // B1: stage 0 free
+        for (int nc = 0; nc < NC; ++nc) {
+            issue_all<T, C, DK>(stg(nc), a, u0 + min(nc + 2, last), cw, lane, slice);
+            prefetch_chunk<T, C, DK>(a, u0 + min(nc + 5, last), slice, NS, cw, lane, sink);
+            wait_vm<G::NDMA + 2 * G::KPF>();         // chunk nc + 1 landed
+            lds_barrier();
+            lds_barrier();
+        }
+        wait_vm<0>();   // no load may land in LDS after the workgroup ends
+        return;
+    }
+
     f32x4 S[G::SPW];
 #pragma unroll
     for (int u = 0; u < G::SPW; ++u) {
@@ -123,16 +299,44 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
             S[u][i] = (a.S0 && t < G::NT) ? a.S0[((size_t)bh * DK + 16 * t + 4 * lg + i) * Dv + col] : 0.f;
         if (t < G::NT) put_tile<T, G::KB>(sSf, t, lane, S[u]);
     }
-    __syncthreads();
+
+    ChainOps<T, C, DK> cur;
+    lds_barrier();                                   // B0: chunk 0 is in stage 0
+    read_ops<T, C, DK>(cur, stg(0), lane, lg);
+    lds_barrier();                                   // B1: stage 0 may be refilled
 
     T* out = static_cast<T*>(a.out);
     const size_t ostride = (size_t)H * Dv;                      // one token
     T* obase = out + (((size_t)b * T_ + 16 * wave + 4 * lg) * H + h) * Dv + col;
+    // outputs of chunk n: O = (Q * Gamma) S_n + P Delta_n (off the state's
+    // critical path, so computed during the next chunk's first phase)
+    F pqg[G::NKD], pp[G::NKC], psf[G::NKD], pdf[G::NKC];
+    auto emit = [&](int n) {
+        if (G::NM == 4 || wave < G::NM) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int s = 0; s < G::NKD; ++s) acc = mma(pqg[s], psf[s], acc);
+#pragma unroll
+            for (int s = 0; s < G::NKC; ++s) acc = mma(pp[s], pdf[s], acc);
+            T* o = obase + (size_t)n * C * ostride;
+            if (n * C + C <= T_) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[i * ostride] = from_f32<T>(acc[i]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (n * C + 16 * wave + 4 * lg + i < T_) o[i * ostride] = from_f32<T>(acc[i]);
+            }
+        }
+    };
 
-    auto step = [&](const ChainOps<T, C, DK>& cur, int nc) {
+    for (int nc = 0; nc < NC; ++nc) {
         F sf[G::NKD];
 #pragma unroll
         for (int s = 0; s < G::NKD; ++s) sf[s] = sSf[s * 64 + lane];
+        if (nc > 0) emit(nc - 1);
+
+        // Delta = U - W S for this wave's token tile
         if (G::NM == 4 || wave < G::NM) {
             f32x4 acc = zero4();
 #pragma unroll
@@ -142,26 +346,11 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
             for (int i = 0; i < 4; ++i) dl[i] = cur.u[i] - acc[i];
             put_tile<T, G::KB>(sDf, wave, lane, dl);
         }
-        __syncthreads();
+        lds_barrier();
         F df[G::NKC];
 #pragma unroll
         for (int s = 0; s < G::NKC; ++s) df[s] = sDf[s * 64 + lane];
-        if (G::NM == 4 || wave < G::NM) {
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int s = 0; s < G::NKD; ++s) acc = mma(cur.qg[s], sf[s], acc);
-#pragma unroll
-            for (int s = 0; s < G::NKC; ++s) acc = mma(cur.p[s], df[s], acc);
-            T* o = obase + (size_t)nc * C * ostride;
-            if (nc * C + C <= T_) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) o[i * ostride] = from_f32<T>(acc[i]);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (nc * C + 16 * wave + 4 * lg + i < T_) o[i * ostride] = from_f32<T>(acc[i]);
-            }
-        }
+        // S_next = diag(Gamma_C) S + Ktil^T Delta for this wave's state tiles
 #pragma unroll
         for (int u = 0; u < G::SPW; ++u) {
             const int t = wave + 4 * u;
@@ -175,29 +364,15 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
                 put_tile<T, G::KB>(sSf, t, lane, acc);
             }
         }
-        __syncthreads();
-    };
-
-    // operand ring: chunk nc uses ops[nc % 3]; the loads of chunks nc+1 and
-    // nc+2 are in flight while chunk nc computes.  Past the last chunk the
-    // ring re-reads the last chunk instead of skipping the loads: every path
-    // through the loop then issues the same loads, so the compiler's wait
-    // counts stay exact and the waits only cover the chunk being used.
-    ChainOps<T, C, DK> ops[3];
-    const size_t u0 = (size_t)bh * NC;
-    const int last = NC - 1;
-    load_ops(ops[0], a, u0, wave, lane, lg, slice);
-    load_ops(ops[1], a, u0 + min(1, last), wave, lane, lg, slice);
-    for (int nc = 0; nc < NC; nc += 3) {
-        load_ops(ops[2], a, u0 + min(nc + 2, last), wave, lane, lg, slice);
-        step(ops[0], nc);
-        if (nc + 1 >= NC) break;
-        load_ops(ops[0], a, u0 + min(nc + 3, last), wave, lane, lg, slice);
-        step(ops[1], nc + 1);
-        if (nc + 2 >= NC) break;
-        load_ops(ops[1], a, u0 + min(nc + 4, last), wave, lane, lg, slice);
-        step(ops[2], nc + 2);
+#pragma unroll
+        for (int s = 0; s < G::NKD; ++s) { pqg[s] = cur.qg[s]; psf[s] = sf[s]; }
+#pragma unroll
+        for (int s = 0; s < G::NKC; ++s) { pp[s] = cur.p[s]; pdf[s] = df[s]; }
+        // next chunk's operands (its loader waited for them before barrier 1)
+        read_ops<T, C, DK>(cur, stg(nc + 1), lane, lg);
+        lds_barrier();
     }
+    emit(NC - 1);
 
     if (a.ST) {
 #pragma unroll
@@ -215,10 +390,15 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
 template <typename T, int C, int DK>
 hipError_t launch_chain_t(const ChunkShape& s, const ChainArgs& a, hipStream_t stream)
 {
+    using G = ChainGeom<T, C, DK>;
+    auto kern = chain_kernel<T, C, DK>;
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)G::LDS_TOTAL);
+    if (e != hipSuccess) return e;
     const int NS = s.Dv / 16;
     const int bh = s.B * s.H;
     const unsigned grid = (unsigned)(kXcds * NS * ((bh + kXcds - 1) / kXcds));
-    return launch_kernel(chain_kernel<T, C, DK>, dim3(grid), dim3(kChainThreads), 0, stream, a);
+    return launch_kernel(kern, dim3(grid), dim3(kChainThreads), (uint32_t)G::LDS_TOTAL, stream, a);
 }
 
 template <typename T, int C>
