@@ -43,6 +43,7 @@ template <> struct Vec4<float> {
     __device__ __forceinline__ static Vec4 from(const float* f) { return Vec4{{f[0], f[1], f[2], f[3]}}; }
     __device__ __forceinline__ static Vec4 zero() { return Vec4{{0.f, 0.f, 0.f, 0.f}}; }
     __device__ __forceinline__ float get(int i) const { return v[i]; }
+    __device__ __forceinline__ float elem(int i) const { return v[i]; }
 };
 template <> struct Vec4<bf16_t> {
     i16x4 v;   // raw bf16 bits
@@ -59,6 +60,7 @@ template <> struct Vec4<bf16_t> {
     __device__ __forceinline__ float get(int i) const {
         return __uint_as_float((unsigned)(unsigned short)v[i] << 16);
     }
+    __device__ __forceinline__ bf16_t elem(int i) const { return __builtin_bit_cast(bf16_t, (short)v[i]); }
 };
 
 // ---- one k16 block of a 16x16 MFMA tile --------------------------------------

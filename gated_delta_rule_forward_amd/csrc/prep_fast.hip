@@ -58,9 +58,10 @@ struct FastGeom {
     static constexpr int XWS = DK + PADE;                     // row stride of X_W, Q*Gamma staging
     static constexpr int NB = C / 16;
     static constexpr int DVMAX = sizeof(T) == 4 ? 64 : 128;
-    static constexpr int VS = DVMAX + PADE;                   // row stride of staged V
-    static constexpr int VEC = 16 / (int)sizeof(T);           // elements per 16-byte vector
-    static constexpr int VPT = (C * DVMAX / VEC + kThreads - 1) / kThreads;   // V vectors per thread
+    static constexpr int XTS = C + PADE;                      // row stride of X_W^T, (beta V)^T
+    static constexpr int TV = 16 / (int)sizeof(T);            // tokens per 16-byte run of a V^T row
+    // V items: (column quad, run of TV tokens); at most VIT per thread
+    static constexpr int VIT = ((DVMAX / 4) * (C / TV) + kThreads - 1) / kThreads;
 };
 
 template <typename T, int C, int DK>
@@ -73,7 +74,7 @@ struct FastLayout {
         KS = kp_max + G::PADE;
         const size_t e = sizeof(T);
         const size_t opsz1 = 3 * (size_t)C * KS * e;
-        const size_t opsz2 = (size_t)C * G::LDF * 4 + (size_t)C * G::XWS * e + (size_t)C * G::VS * e;
+        const size_t opsz2 = (size_t)C * G::LDF * 4 + (size_t)(DK + G::DVMAX) * G::XTS * e;
         const size_t opsz = ((opsz1 > opsz2 ? opsz1 : opsz2) + 15) & ~size_t(15);
         // the sA region also holds Q*Gamma staging and, before that, the
         // per-token-range partial gate sums (partL, partPZ: PARTS x DK each)
@@ -128,12 +129,12 @@ __device__ __forceinline__ Frag<T, KB> frag_col(const T* base, int ld, int k0) {
 }
 
 template <typename T, int C, int DK>
-__global__ __launch_bounds__(kThreads) void prep_fast_kernel(PrepArgs args)
+__global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
 {
     using G = FastGeom<T, C, DK>;
     using F = Frag<T, G::KB>;
     constexpr int KB = G::KB, NV = G::NV, TPB = G::TPB, PARTS = G::PARTS, TOK = G::TOK;
-    constexpr int NB = G::NB, LDF = G::LDF, XWS = G::XWS, VS = G::VS, VEC = G::VEC;
+    constexpr int NB = G::NB, LDF = G::LDF, XWS = G::XWS, XTS = G::XTS, TV = G::TV;
     constexpr int NKD = DK / KB, NKC = C / KB;
     const int Dv = args.Dv;
     const FastLayout<T, C, DK> LY(args.zx);
@@ -143,8 +144,8 @@ __global__ __launch_bounds__(kThreads) void prep_fast_kernel(PrepArgs args)
     T* XP = XA + C * KS;
     T* Y = XP + C * KS;
     float* sT = reinterpret_cast<float*>(lds + LY.ops);                    // after A/P
-    T* sXW = reinterpret_cast<T*>(lds + LY.ops + (size_t)C * LDF * 4);      // [C][XWS]
-    T* sV = sXW + C * XWS;                                                  // [C][VS]
+    T* sXWt = reinterpret_cast<T*>(lds + LY.ops + (size_t)C * LDF * 4);     // X_W^T [DK][XTS]
+    T* sVt = sXWt + DK * XTS;                                               // (beta V)^T [Dv][XTS]
     float* sA = reinterpret_cast<float*>(lds + LY.sA);
     T* sQG = reinterpret_cast<T*>(lds + LY.sA);                             // before A/P
     float* partL = reinterpret_cast<float*>(lds + LY.sA);                  // before Q*Gamma
@@ -264,31 +265,39 @@ __global__ __launch_bounds__(kThreads) void prep_fast_kernel(PrepArgs args)
             for (int x = 0; x < 4; ++x) Lr[j][x] += offL[x];
         }
     }
-    if (own && part == 0) {
+    int Ztot = 0;
+    bool bad = false;
+    if (args.zx > 0) {
+        if (own && part == 0) {
 #pragma unroll
-        for (int x = 0; x < 4; ++x) sBase[c0 + x] = totPZ[x] >> 1;
-    }
-    __syncthreads();
-    // exclusive prefix of the per-channel zero counts -> first extra column of a channel
-    if (wave == 0) {
-        int carry = 0;
-        for (int cc = 0; cc < DK; cc += 64) {
-            const int v = (cc + lane < DK) ? sBase[cc + lane] : 0;
-            int incl = v;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const int y = __shfl_up(incl, off, 64);
-                if (lane >= off) incl += y;
-            }
-            if (cc + lane < DK) sBase[cc + lane] = carry + incl - v;
-            carry += __shfl(incl, 63, 64);
+            for (int x = 0; x < 4; ++x) sBase[c0 + x] = totPZ[x] >> 1;
         }
-        if (lane == 0) misc[0] = carry;
+        __syncthreads();
+        // exclusive prefix of the per-channel zero counts -> first extra column of a channel
+        if (wave == 0) {
+            int carry = 0;
+            for (int cc = 0; cc < DK; cc += 64) {
+                const int v = (cc + lane < DK) ? sBase[cc + lane] : 0;
+                int incl = v;
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const int y = __shfl_up(incl, off, 64);
+                    if (lane >= off) incl += y;
+                }
+                if (cc + lane < DK) sBase[cc + lane] = carry + incl - v;
+                carry += __shfl(incl, 63, 64);
+            }
+            if (lane == 0) misc[0] = carry;
+        }
+        __syncthreads();
+        Ztot = misc[0];
+        bad = Ztot > args.zx;
+    } else {
+        // no extra columns: any zero gate sends the chunk to the exact kernel
+#pragma unroll
+        for (int x = 0; x < 4; ++x) bad = bad || (totPZ[x] >> 1) != 0;
     }
-    __syncthreads();
-    const int Ztot = misc[0];
     float M[4], E[4];
-    bool bad = Ztot > args.zx;
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
         M[x] = 0.5f * totL[x];
@@ -390,13 +399,17 @@ __global__ __launch_bounds__(kThreads) void prep_fast_kernel(PrepArgs args)
     }
     __syncthreads();
     // V tile loads: in flight during the Q*Gamma emission and the A / P tiles
-    const int vpr = Dv / VEC, nvv = C * vpr;
-    uint4 vreg[G::VPT];
+    // item (column quad vq, token run tg): 4 columns x TV tokens, stored later
+    // as 4 rows of (beta V)^T; rows past the end re-read the last valid row
+    const int nvq = Dv / 4, nvit = nvq * (C / TV);
+    Vec4<T> vreg[G::VIT][TV];
 #pragma unroll
-    for (int x = 0; x < G::VPT; ++x) {
-        const int idx = min(tid + x * kThreads, nvv - 1);
-        const int r = min(idx / vpr, nvalid - 1);
-        vreg[x] = *reinterpret_cast<const uint4*>(gv + r * rsv + (idx % vpr) * VEC);
+    for (int x = 0; x < G::VIT; ++x) {
+        const int it = min(tid + x * kThreads, nvit - 1);
+        const int vq = it % nvq, tg = it / nvq;
+#pragma unroll
+        for (int z = 0; z < TV; ++z)
+            vreg[x][z] = Vec4<T>::load(gv + min(tg * TV + z, nvalid - 1) * rsv + 4 * vq);
     }
     // Q*Gamma fragments: 64 lanes x (C/16) x (DK/KB) per chunk
     for (int f = tid; f < (C / 16) * NKD * 64; f += kThreads) {
@@ -408,42 +421,88 @@ __global__ __launch_bounds__(kThreads) void prep_fast_kernel(PrepArgs args)
     __syncthreads();   // the staging area becomes sA
 
     // ---- A (strictly lower, LDS) and P^T tiles (global, fragment-major) --------
-    // work items: A tiles (ta, tb <= ta), then P items (ta, k block s)
-    {
-        constexpr int NA = NB * (NB + 1) / 2;
-        for (int it = wave; it < NA + NB * NKC; it += 4) {
-            if (it < NA) {
-                int ta = 0;
-                while ((ta + 1) * (ta + 2) / 2 <= it) ++ta;
-                const int tb = it - ta * (ta + 1) / 2;
-                const f32x4 acc = tile_tn_nat<T, KB>(XA + 16 * ta * KS, KS, Y + 16 * tb * KS, KS, KP);
+    // wave w takes row tile ta = w: over the contraction it keeps the row's
+    // (beta K * F) and (Q * F) fragments and streams (K * G) of tiles tb <= ta
+    for (int ta = wave; ta < NB; ta += 4) {
+        f32x4 accA[NB], accP[NB];
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb) { accA[tb] = zero4(); accP[tb] = zero4(); }
+        for (int k0 = 0; k0 < KP; k0 += KB) {
+            const F xa = frag_row<T, KB>(XA + (16 * ta + ln) * KS, k0);
+            const F xp = frag_row<T, KB>(XP + (16 * ta + ln) * KS, k0);
+#pragma unroll
+            for (int tb = 0; tb < NB; ++tb) {
+                if (tb <= ta) {
+                    const F y = frag_row<T, KB>(Y + (16 * tb + ln) * KS, k0);
+                    accA[tb] = mma(xa, y, accA[tb]);    // A[16ta + 4g + i][16tb + n]
+                    accP[tb] = mma(y, xp, accP[tb]);    // P[16ta + n][16tb + 4g + i]
+                }
+            }
+        }
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb) {
+            if (tb <= ta) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = 16 * ta + 4 * lg + i, col = 16 * tb + ln;
-                    sA[r * LDF + col] = col < r ? acc[i] : 0.f;
+                    sA[r * LDF + col] = col < r ? accA[tb][i] : 0.f;
                 }
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < NKC; ++s) {
+            float f[NV];
+#pragma unroll
+            for (int u = 0; u < TPB; ++u) {
+                const int tb = s * TPB + u;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    f[4 * u + i] = (tb <= ta && 16 * tb + 4 * lg + i <= 16 * ta + ln) ? accP[tb][i] : 0.f;
+            }
+            *reinterpret_cast<F*>(Pg + ((size_t)(ta * NKC + s) * 64 + lane) * NV) = F::from(f);
+        }
+    }
+    __syncthreads();   // operands dead: the region now holds sT, sXWt, sVt
+
+    // ---- stage X_W^T and (diag(beta) V)^T; Tinv diagonal blocks ----------------
+    // X_W^T row c holds this thread's TOK tokens of channel c contiguously
+    if (own) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            T* dst = sXWt + (c0 + x) * XTS + part * TOK;
+            if constexpr (TOK * sizeof(T) == 16) {
+                T v[TOK];
+#pragma unroll
+                for (int j = 0; j < TOK; ++j) v[j] = xw[j].elem(x);
+                *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(v);
             } else {
-                const int ta = (it - NA) / NKC, s = (it - NA) % NKC;
-                float f[NV];
 #pragma unroll
-                for (int u = 0; u < TPB; ++u) {
-                    const int tb = s * TPB + u;
-                    f32x4 acc = zero4();
-                    if (tb <= ta)   // P^T tile: lane (n, g) holds P[16ta + n][16tb + 4g + i]
-                        acc = tile_tn_nat<T, KB>(Y + 16 * tb * KS, KS, XP + 16 * ta * KS, KS, KP);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        f[4 * u + i] = (16 * tb + 4 * lg + i <= 16 * ta + ln) ? acc[i] : 0.f;
-                }
-                *reinterpret_cast<F*>(Pg + ((size_t)(ta * NKC + s) * 64 + lane) * NV) = F::from(f);
+                for (int j = 0; j < TOK; ++j) dst[j] = xw[j].elem(x);
             }
         }
     }
-    __syncthreads();   // operands dead: the region now holds sT, sXW, sV
-
-    // ---- Tinv diagonal blocks; stage X_W and diag(beta) V row-major -------------
-    if (wave < NB && lane < 16) {
-        const int a = wave, j = lane;
+#pragma unroll
+    for (int x = 0; x < G::VIT; ++x) {
+        const int it = tid + x * kThreads;
+        if (it < nvit) {
+            const int vq = it % nvq, tg = it / nvq;
+#pragma unroll
+            for (int y = 0; y < 4; ++y) {
+                T v[TV];
+#pragma unroll
+                for (int z = 0; z < TV; ++z) v[z] = from_f32<T>(sBeta[tg * TV + z] * vreg[x][z].get(y));
+                *reinterpret_cast<uint4*>(sVt + (4 * vq + y) * XTS + tg * TV) = *reinterpret_cast<const uint4*>(v);
+            }
+        }
+    }
+    for (int idx = tid; idx < C * C; idx += kThreads) {       // upper blocks of Tinv
+        const int r = idx / C, col = idx % C;
+        if ((col >> 4) > (r >> 4)) sT[r * LDF + col] = 0.f;
+    }
+    // forward substitution on the 16x16 diagonal blocks: wave 0, lane 16a + j
+    // owns column j of block a
+    if (wave == 0 && (lane >> 4) < NB) {
+        const int a = lane >> 4, j = lane & 15;
         float t[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -454,30 +513,6 @@ __global__ __launch_bounds__(kThreads) void prep_fast_kernel(PrepArgs args)
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) sT[(16 * a + r) * LDF + 16 * a + j] = t[r];
-    }
-    for (int idx = tid; idx < C * C; idx += kThreads) {       // upper blocks of Tinv
-        const int r = idx / C, col = idx % C;
-        if ((col >> 4) > (r >> 4)) sT[r * LDF + col] = 0.f;
-    }
-    if (own) {
-#pragma unroll
-        for (int j = 0; j < TOK; ++j)
-            *reinterpret_cast<Vec4<T>*>(sXW + (part * TOK + j) * XWS + c0) = xw[j];
-    }
-#pragma unroll
-    for (int x = 0; x < G::VPT; ++x) {
-        const int idx = tid + x * kThreads;
-        if (idx < nvv) {
-            const int r = idx / vpr, cv = (idx % vpr) * VEC;
-            const float bsc = r < nvalid ? sBeta[r] : 0.f;
-            const T* e = reinterpret_cast<const T*>(&vreg[x]);
-            float y[VEC];
-#pragma unroll
-            for (int z = 0; z < VEC; ++z) y[z] = bsc * to_f32(e[z]);
-#pragma unroll
-            for (int z = 0; z < VEC; z += 4)
-                *reinterpret_cast<Vec4<T>*>(sV + r * VS + cv + z) = Vec4<T>::from(y + z);
-        }
     }
     __syncthreads();
     // ---- Tinv off-diagonal blocks by block distance (fp32 MFMA) ----------------
@@ -504,35 +539,41 @@ __global__ __launch_bounds__(kThreads) void prep_fast_kernel(PrepArgs args)
         __syncthreads();
     }
 
-    // ---- W^T tiles -> W fragments;  U = Tinv (diag(beta) V) tiles ---------------
+    // ---- W = Tinv X_W and U = Tinv (diag(beta) V): wave w takes token tile
+    //      mt = w; its Tinv rows serve as the A operand of U and the B operand
+    //      of W^T (same per-lane data).  Tinv[16mt + i][k] = 0 for k beyond
+    //      the tile, so k blocks past it are skipped.
     {
         constexpr int NM = C / 16;
         const int NUt = Dv / 16;
-        const int nwi = NM * NKD;                       // W items (token tile, k block)
-        for (int it = wave; it < nwi + NM * NUt; it += 4) {
-            if (it < nwi) {
-                const int mt = it / NKD, s = it % NKD;
+        for (int mt = wave; mt < NM; mt += 4) {
+            const int nkb = (16 * (mt + 1) + KB - 1) / KB;
+            F tf[NKC];
+#pragma unroll
+            for (int kb = 0; kb < NKC; ++kb)
+                tf[kb] = frag_row_cvt<T, KB>(sT + (16 * mt + ln) * LDF, kb * KB);
+#pragma unroll
+            for (int s = 0; s < NKD; ++s) {
                 float f[NV];
 #pragma unroll
                 for (int u = 0; u < TPB; ++u) {
                     const int ct = s * TPB + u;
-                    // W^T[16ct + 4g + i][16mt + n] = sum_j X_W[j][16ct + .] Tinv[16mt + n][j]
-                    const float* brow = sT + (16 * mt + ln) * LDF;
+                    // W^T[16ct + 4g + i][16mt + n] = sum_k X_W^T[16ct + .][k] Tinv[16mt + n][k]
                     f32x4 acc = zero4();
 #pragma unroll
-                    for (int k0 = 0; k0 < C; k0 += KB)
-                        acc = mma(frag_col<T, KB>(sXW + 16 * ct, XWS, k0), frag_row_cvt<T, KB>(brow, k0), acc);
+                    for (int kb = 0; kb < NKC; ++kb)
+                        if (kb < nkb)
+                            acc = mma(frag_row<T, KB>(sXWt + (16 * ct + ln) * XTS, kb * KB), tf[kb], acc);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) f[4 * u + i] = acc[i];
                 }
                 *reinterpret_cast<F*>(Wg + ((size_t)(mt * NKD + s) * 64 + lane) * NV) = F::from(f);
-            } else {
-                const int ut = it - nwi, mt = ut % NM, nt = ut / NM;
-                const float* arow = sT + (16 * mt + ln) * LDF;
+            }
+            for (int nt = 0; nt < NUt; ++nt) {
                 f32x4 acc = zero4();
 #pragma unroll
-                for (int k0 = 0; k0 < C; k0 += KB)
-                    acc = mma(frag_row_cvt<T, KB>(arow, k0), frag_col<T, KB>(sV + 16 * nt, VS, k0), acc);
+                for (int kb = 0; kb < NKC; ++kb)
+                    if (kb < nkb) acc = mma(tf[kb], frag_row<T, KB>(sVt + (16 * nt + ln) * XTS, kb * KB), acc);
                 *reinterpret_cast<f32x4*>(Ug + ((size_t)(mt * NUt + nt) * 64 + lane) * 4) = acc;
             }
         }
