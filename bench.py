@@ -43,6 +43,39 @@ def algorithmic_bytes(w, io_bytes, with_s0: bool, with_st: bool):
             "path": read_in + s0 + out + st}
 
 
+KERNEL_SOURCES = {
+    # files whose contents determine each kernel's code
+    "prep_fast": ["prep_fast.hip", "kda_chunk.hpp", "kda_device.hpp", "kda_launch.hpp"],
+    "chain": ["chain.hip", "kda_chunk.hpp", "kda_device.hpp", "kda_launch.hpp"],
+    "prep_exact": ["prep_exact.hip", "kda_chunk.hpp", "kda_device.hpp", "kda_launch.hpp"],
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_kda_bf16_prefill.md")
+
+
+def kernel_source_hash(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "gated_delta_rule_forward_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, calibrated) recorded in
+    the rocprofv3 counter summary, or None when the summary is missing or the
+    kernel's sources changed since the counters were taken."""
+    import re
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m = re.search(r"^\| %s \| ([0-9a-f]{16}) \| ([0-9.]+) \| ([0-9.]+) \|" % re.escape(kernel), text, re.M)
+    if not m or m.group(1) != kernel_source_hash(kernel):
+        return None
+    return float(m.group(2)) + float(m.group(3))
+
+
 def chunk_flops(w):
     """Dense per-chunk contractions of the chunkwise form (per token-head:
     2*(3 Dk Dv + C (Dk + Dk + Dv) ...) ), counted as in the design notes."""
@@ -84,7 +117,7 @@ def time_forward(kda, torch, w, inp, steps, warmup):
     return ms, per, out, st
 
 
-def cpu_baseline(oracle, w, inp, max_heads=None):
+def cpu_baseline(oracle, w, inp, max_heads=None, min_seconds=10.0):
     import numpy as np
     heads = list(range(w.H if max_heads is None else min(w.H, max_heads)))
     f = lambda t: t[:, :, heads].float().cpu().numpy()
@@ -93,14 +126,21 @@ def cpu_baseline(oracle, w, inp, max_heads=None):
     s0 = None if inp["S0"] is None else inp["S0"][:, heads].float().cpu().numpy()
     nthreads = oracle.default_threads()
     nthreads = min(nthreads, 16)
-    t0 = time.perf_counter()
-    o, s = oracle.forward(*args, beta, s0, nthreads=nthreads)
-    dt = time.perf_counter() - t0
-    toks = w.B * w.T * len(heads) / w.H        # tokens of the full batch equivalent
+    # repeat the same forward until about min_seconds of wall time have passed
+    reps, dt = 0, 0.0
+    while True:
+        t0 = time.perf_counter()
+        o, s = oracle.forward(*args, beta, s0, nthreads=nthreads)
+        dt += time.perf_counter() - t0
+        reps += 1
+        if dt >= min_seconds or reps >= 200:
+            break
+    toks = reps * w.B * w.T * len(heads) / w.H        # tokens of the full batch equivalent
     return {"value": toks / dt, "unit": "tokens/s", "cores": min(nthreads, len(heads) * w.B),
             "kind": "oracle",
             "sample": f"{w.name}: B={w.B} T={w.T} heads {len(heads)}/{w.H}, fp64 sequential "
-                      f"recurrence, {dt:.1f} s wall; tokens/s scaled to all {w.H} heads"}, (o, s, heads)
+                      f"recurrence, {reps} passes in {dt:.1f} s wall; tokens/s scaled to all "
+                      f"{w.H} heads"}, (o, s, heads)
 
 
 def decode_bench(kda, torch, workloads, steps_cap=None):
@@ -178,7 +218,7 @@ def main():
                    "B": w.B, "H": w.H, "T": w.T, "Dk": w.Dk, "Dv": w.Dv, "chunk": w.chunk,
                    "mode": "KDA", "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": dom,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(dom), "kernel": dom,
                      "kernel_ms": dom_ms, "algorithmic_bytes": ab[dom]},
         "path_roofline": {"bound": "hbm", "algorithmic_bytes": ab["path"],
                           "achieved": ab["path"] / (ms / 1e3) / 1e9,
