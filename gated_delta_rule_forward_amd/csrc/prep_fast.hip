@@ -43,6 +43,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr float kHalfSpanMax = 96.f;
+constexpr float kMinPart = 0x1p-120f;   // smallest product of one token range's gates
 
 template <typename T, int C, int DK>
 struct FastGeom {
@@ -93,6 +94,7 @@ struct FastLayout {
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float flog2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float frcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
 // one fragment (NV slots) of an A-operand from a row-major matrix in LDS:
 // row r, k block s, lane group g -> slots j at columns of frag_off's mapping
@@ -128,7 +130,10 @@ __device__ __forceinline__ Frag<T, KB> frag_col(const T* base, int ld, int k0) {
     return f;
 }
 
-template <typename T, int C, int DK>
+// ZS: the chunk may hold zero gates, placed in extra contraction columns (the
+// launch passes ZS = true exactly when extra columns are allotted); without
+// them a zero gate makes a part product vanish and flags the chunk.
+template <typename T, int C, int DK, bool ZS>
 __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
 {
     using G = FastGeom<T, C, DK>;
@@ -204,28 +209,45 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
         }
     }
 
-    // ---- gate summary: per channel, L (log2 magnitude), parity and zero count
-    //      cumulated over my tokens, then offset by the earlier token ranges ------
-    float Lr[TOK][4];
-    unsigned ps[TOK];                  // byte x: (seg << 1 | parity) of channel c0 + x
+    // ---- gate summary in product form: per channel, the running product of the
+    //      (nonzero) gates over my tokens, signs included, and the zero count;
+    //      the part totals enter a log2 magnitude / parity / zero-count summary
+    //      combined across token ranges through LDS -------------------------------
+    float pr[TOK][4];
+    unsigned zc[TOK];                  // (ZS) byte x: zeros of channel c0 + x so far in my range
+    float cur[4] = {1.f, 1.f, 1.f, 1.f};
+    bool badp = false;
     {
-        float ls[4] = {0.f, 0.f, 0.f, 0.f};
-        int pz[4] = {0, 0, 0, 0};
+        int zn[4] = {0, 0, 0, 0};
 #pragma unroll
         for (int j = 0; j < TOK; ++j) {
-            ps[j] = 0;
+            zc[j] = 0;
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
                 const float a = al[j][x];
-                if (a == 0.f) pz[x] += 2;
-                else ls[x] += flog2(fabsf(a));
-                pz[x] ^= (a < 0.f) ? 1 : 0;
-                Lr[j][x] = ls[x];
-                ps[j] |= (unsigned)pz[x] << (8 * x);
+                if constexpr (ZS) {
+                    const bool z = a == 0.f;
+                    cur[x] *= z ? 1.f : a;
+                    zn[x] += z ? 1 : 0;
+                    zc[j] |= (unsigned)zn[x] << (8 * x);
+                } else {
+                    cur[x] *= a;
+                }
+                pr[j][x] = cur[x];
             }
         }
+        float lp[4];
+        int pz[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const float m = fabsf(cur[x]);
+            // the magnitude must stay a normal float no larger than one (NaN fails too)
+            badp = badp || !(m >= kMinPart && m <= 1.f);
+            lp[x] = flog2(m);
+            pz[x] = (zn[x] << 1) | (cur[x] < 0.f ? 1 : 0);
+        }
         if (own) {
-            *reinterpret_cast<float4*>(partL + part * DK + c0) = make_float4(ls[0], ls[1], ls[2], ls[3]);
+            *reinterpret_cast<float4*>(partL + part * DK + c0) = make_float4(lp[0], lp[1], lp[2], lp[3]);
             *reinterpret_cast<int4*>(partPZ + part * DK + c0) = make_int4(pz[0], pz[1], pz[2], pz[3]);
             if (q4 == 0) {
 #pragma unroll
@@ -235,7 +257,7 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
     }
     __syncthreads();
     float offL[4] = {0.f, 0.f, 0.f, 0.f}, totL[4] = {0.f, 0.f, 0.f, 0.f};
-    int offPZ[4] = {0, 0, 0, 0}, totPZ[4] = {0, 0, 0, 0};   // (seg sum) << 1 | parity
+    int offPZ[4] = {0, 0, 0, 0}, totPZ[4] = {0, 0, 0, 0};   // (zero count) << 1 | parity
 #pragma unroll 8
     for (int p = 0; p < PARTS; ++p) {
         const float4 l = *reinterpret_cast<const float4*>(partL + p * DK + c0);
@@ -244,30 +266,14 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
         const int zv[4] = {z.x, z.y, z.z, z.w};
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-            const int comb = ((zv[x] >> 1) << 1) + (zv[x] & 1);   // same encoding
-            if (p < part) { offL[x] += lv[x]; offPZ[x] = ((offPZ[x] >> 1) + (comb >> 1)) << 1 | ((offPZ[x] ^ comb) & 1); }
+            if (p < part) { offL[x] += lv[x]; offPZ[x] = (((offPZ[x] >> 1) + (zv[x] >> 1)) << 1) | ((offPZ[x] ^ zv[x]) & 1); }
             totL[x] += lv[x];
-            totPZ[x] = ((totPZ[x] >> 1) + (comb >> 1)) << 1 | ((totPZ[x] ^ comb) & 1);
-        }
-    }
-    {
-        // bytes hold 2 seg + parity <= 2 C + 1 < 256: add the even part, xor the parity
-        unsigned addp = 0, xorp = 0;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            addp |= (unsigned)(offPZ[x] & ~1) << (8 * x);
-            xorp |= (unsigned)(offPZ[x] & 1) << (8 * x);
-        }
-#pragma unroll
-        for (int j = 0; j < TOK; ++j) {
-            ps[j] = (ps[j] + addp) ^ xorp;
-#pragma unroll
-            for (int x = 0; x < 4; ++x) Lr[j][x] += offL[x];
+            totPZ[x] = (((totPZ[x] >> 1) + (zv[x] >> 1)) << 1) | ((totPZ[x] ^ zv[x]) & 1);
         }
     }
     int Ztot = 0;
-    bool bad = false;
-    if (args.zx > 0) {
+    bool bad = badp;
+    if constexpr (ZS) {
         if (own && part == 0) {
 #pragma unroll
             for (int x = 0; x < 4; ++x) sBase[c0 + x] = totPZ[x] >> 1;
@@ -292,17 +298,18 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
         __syncthreads();
         Ztot = misc[0];
         bad = Ztot > args.zx;
-    } else {
-        // no extra columns: any zero gate sends the chunk to the exact kernel
-#pragma unroll
-        for (int x = 0; x < 4; ++x) bad = bad || (totPZ[x] >> 1) != 0;
     }
-    float M[4], E[4];
+    // midpoint M = L_total / 2;  F_r = F0 pr_r and G_r = G0 / pr_r, where F0, G0
+    // carry the sign and magnitude of the earlier token ranges
+    float M[4], E[4], F0[4], G0[4];
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
         M[x] = 0.5f * totL[x];
         bad = bad || (-M[x] > kHalfSpanMax) || !(M[x] <= 0.f);
         E[x] = fexp2(M[x]);
+        const float so = (offPZ[x] & 1) ? -1.f : 1.f;
+        F0[x] = so * fexp2(offL[x] - M[x]);
+        G0[x] = so * fexp2(M[x] - offL[x]);
     }
     if (__syncthreads_or(bad && own)) {
         if (tid == 0) args.FL[unit] = 1;
@@ -330,26 +337,32 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
         int segs[4];
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-            const unsigned pb = (ps[j] >> (8 * x)) & 0xffu;
-            const int seg = (int)(pb >> 1);
-            const float sgn = (pb & 1u) ? -1.f : 1.f;
             const float kx = kv[j].get(x), qx = qv[j].get(x);
-            const float Fv = sgn * fexp2(Lr[j][x] - M[x]), Gv = sgn * fexp2(M[x] - Lr[j][x]);
-            fa[x] = bt[j] * kx * Fv;
+            const float Fv = F0[x] * pr[j][x];
+            const float Gv = G0[x] * frcp(pr[j][x]);
+            const float bk = bt[j] * kx;
+            fa[x] = bk * Fv;
             fp[x] = qx * Fv;
             fy[x] = kx * Gv;
-            const float gam = seg == 0 ? Fv * E[x] : 0.f;                     // Gamma_r
-            fq[x] = qx * gam;
-            fw[x] = bt[j] * kx * gam;
+            // Gamma_r = F_r E in the first zero segment; rho(C-1, r) = stot E G_r
+            // in the last one (stot: sign of the whole chunk's product)
             const float stot = (totPZ[x] & 1) ? -1.f : 1.f;
-            const float re = (seg == (totPZ[x] >> 1)) ? stot * E[x] * Gv : 0.f;   // rho(C-1, r)
-            kt[j][x] = kx * re;
+            float ge = E[x], re = stot * E[x];
+            int seg = 0;
+            if constexpr (ZS) {
+                seg = (offPZ[x] >> 1) + (int)((zc[j] >> (8 * x)) & 0xffu);
+                ge = seg == 0 ? ge : 0.f;
+                re = seg == (totPZ[x] >> 1) ? re : 0.f;
+            }
+            fq[x] = fp[x] * ge;
+            fw[x] = fa[x] * ge;
+            kt[j][x] = fy[x] * re;
             segs[x] = seg;
         }
         xw[j] = Vec4<T>::from(fw);
         if (own) {
             *reinterpret_cast<Vec4<T>*>(sQG + r * XWS + c0) = Vec4<T>::from(fq);
-            if (Ztot == 0) {
+            if (!ZS || Ztot == 0) {
                 *reinterpret_cast<Vec4<T>*>(XA + r * KS + c0) = Vec4<T>::from(fa);
                 *reinterpret_cast<Vec4<T>*>(XP + r * KS + c0) = Vec4<T>::from(fp);
                 *reinterpret_cast<Vec4<T>*>(Y + r * KS + c0) = Vec4<T>::from(fy);
@@ -584,7 +597,7 @@ template <typename T, int C, int DK>
 hipError_t launch_fast_t(const ChunkShape& s, const PrepArgs& a, hipStream_t stream)
 {
     const FastLayout<T, C, DK> LY(a.zx);
-    auto kern = prep_fast_kernel<T, C, DK>;
+    auto kern = a.zx > 0 ? prep_fast_kernel<T, C, DK, true> : prep_fast_kernel<T, C, DK, false>;
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              (int)LY.total);
