@@ -10,10 +10,10 @@
 //  - diagonal 16x16 blocks: per pair, a running product over the block;
 //  - Tinv = (I + A)^{-1} by forward substitution (one wavefront, lane j owns
 //    column j).
-// A grid of at most 512 workgroups covers all chunks: each workgroup reads the
-// flags of its chunks (blockIdx.x, blockIdx.x + gridDim.x, ...) together,
-// lists the flagged ones in LDS and then works through that list, so a launch
-// with nothing flagged costs one round of flag loads.
+// A grid of at most 256 workgroups (one per CU) covers all chunks: each
+// workgroup reads the flags of its chunks (blockIdx.x, blockIdx.x + gridDim.x,
+// ...) together, lists the flagged ones in LDS and then works through that
+// list, so a launch with nothing flagged costs one round of flag loads.
 #include "kda_chunk.hpp"
 #include "kda_launch.hpp"
 
@@ -331,7 +331,7 @@ hipError_t launch_exact_t(const ChunkShape& s, const PrepArgs& a, hipStream_t st
                                              (int)L::TOTAL);
     if (e != hipSuccess) return e;
     const int nu = (int)((size_t)s.B * s.H * s.NC);
-    const int grid = nu < 512 ? nu : 512;
+    const int grid = nu < 256 ? nu : 256;   // one workgroup per CU (LDS-bound)
     return launch_kernel(kern, dim3(grid), dim3(kPrepThreads), (uint32_t)L::TOTAL, stream, a, nu);
 }
 
