@@ -55,12 +55,13 @@ struct ChainGeom {
     static constexpr int OQ = OW + NKD * FB;          // Q * Gamma              [NKD]
     static constexpr int OP = OQ + NKD * FB;          // P                      [NKC]
     static constexpr int OU = OP + NKC * FB;          // U tile (64 x 16 B)
+    static constexpr int UB = 64 * 4 * (int)sizeof(T);     // bytes of one U tile
     static constexpr int OK = OU + 1024;              // Ktil, its state tiles  [SPW][NKC]
     static constexpr int OG = OK + SPW * NKC * FB;    // Gamma_C rows of its state tiles [SPW][4][16 B]
     static constexpr int STAGE = OG + SPW * 64;
     static constexpr int runs(int bytes) { return (bytes + 1023) / 1024; }
     // 16-byte-per-lane direct-to-LDS loads one wavefront issues per chunk
-    static constexpr int NDMA = 2 * runs(NKD * FB) + runs(NKC * FB) + 1 + SPW * runs(NKC * FB) + 1;
+    static constexpr int NDMA = 2 * runs(NKD * FB) + runs(NKC * FB) + runs(UB) + SPW * runs(NKC * FB) + 1;
     static constexpr size_t LDS = 2 * 4 * (size_t)STAGE;     // two stages, four waves
     // plus the S and Delta exchange fragments and a 1 KB sink for L2 prefetches
     static constexpr size_t XCH = LDS;
@@ -131,9 +132,9 @@ __device__ __forceinline__ void issue_chunk(unsigned char* st, const ChainArgs& 
         const unsigned char* P = static_cast<const unsigned char*>(a.P) +
                                  (unit * C * C + (size_t)mt * G::NKC * 64 * (G::KB / 4)) * sizeof(T);
         const unsigned char* U = reinterpret_cast<const unsigned char*>(
-            a.U + unit * C * Dv + (size_t)(mt * (Dv / 16) + slice) * 64 * 4);
+            static_cast<const T*>(a.U) + unit * C * Dv + (size_t)(mt * (Dv / 16) + slice) * 64 * 4);
         dma_run<G::NKC * G::FB>(P, st + G::OP, lane);
-        dma_run<1024>(U, st + G::OU, lane);
+        dma_run<G::UB>(U, st + G::OU, lane);
     } else {
 #pragma unroll
         for (int u = 0; u < G::SPW; ++u) {
@@ -190,9 +191,10 @@ __device__ __forceinline__ void prefetch_chunk(const ChainArgs& a, size_t unit, 
                       (size_t)(p - 3 * G::PW) * 1024;
         } else {
             src = reinterpret_cast<const unsigned char*>(
-                a.U + unit * C * a.Dv + (size_t)((k - ps) * NS + slice) * 64 * 4);
+                static_cast<const T*>(a.U) + unit * C * a.Dv + (size_t)((k - ps) * NS + slice) * 64 * 4);
         }
-        dma16(src + 16 * lane, sink);
+        // (a U tile may be 512 bytes: lanes past it re-read its start)
+        dma16(src + 16 * (k < ps ? lane : lane % (G::UB / 16)), sink);
     }
 }
 
@@ -218,7 +220,10 @@ __device__ __forceinline__ void read_ops(ChainOps<T, C, DK>& o, const unsigned c
 #pragma unroll
     for (int s = 0; s < G::NKC; ++s)
         o.p[s] = *reinterpret_cast<const F*>(st + G::OP + s * G::FB + lane * sizeof(F));
-    o.u = *reinterpret_cast<const f32x4*>(st + G::OU + lane * 16);
+    {
+        const Vec4<T> u4 = *reinterpret_cast<const Vec4<T>*>(st + G::OU + lane * 4 * sizeof(T));
+        o.u = f32x4{u4.get(0), u4.get(1), u4.get(2), u4.get(3)};
+    }
 #pragma unroll
     for (int u = 0; u < G::SPW; ++u) {
 #pragma unroll

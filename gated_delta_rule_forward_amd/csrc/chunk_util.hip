@@ -21,7 +21,7 @@ size_t chunk_workspace_layout(const ChunkShape& s, IoType io, size_t off[kWorksp
     const size_t e = io == IoType::F32 ? 4 : 2;
     const size_t nu = (size_t)s.B * s.H * s.NC;
     const size_t C = s.C, Dk = s.Dk, Dv = s.Dv;
-    const size_t sz[kWorkspaceRegions] = {nu * C * Dk * e, nu * C * Dv * 4, nu * Dk * C * e,
+    const size_t sz[kWorkspaceRegions] = {nu * C * Dk * e, nu * C * Dv * e, nu * Dk * C * e,
                                           nu * C * Dk * e, nu * C * C * e,  nu * Dk * 4, nu};
     size_t o = 0;
     for (int i = 0; i < kWorkspaceRegions; ++i) {

@@ -214,7 +214,7 @@ kda_status_t kda_chunk_forward(const void* q, const void* k, const void* v, cons
     size_t off[kda::kWorkspaceRegions];
     kda::chunk_workspace_layout(sh, io, off);
     unsigned char* w = static_cast<unsigned char*>(workspace);
-    const ChunkWorkspace ws{w + off[0], reinterpret_cast<float*>(w + off[1]), w + off[2],
+    const ChunkWorkspace ws{w + off[0], w + off[1], w + off[2],
                             w + off[3], w + off[4], reinterpret_cast<float*>(w + off[5]),
                             w + off[6]};
     // Extra zero-segment columns of the fast prep kernel: none in KDA mode

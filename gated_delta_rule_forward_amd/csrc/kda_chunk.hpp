@@ -11,7 +11,7 @@
 //   QG [NU] A-operand, rows = tokens (C),   k = channels (Dk)   io type
 //   P  [NU] A-operand, rows = tokens (C),   k = tokens (C)      io type
 //   Kt [NU] A-operand, rows = channels (Dk), k = tokens (C)     io type
-//   U  [NU][C/16][Dv/16][64 lanes][4]  fp32 (lane 16g+n, register i holds
+//   U  [NU][C/16][Dv/16][64 lanes][4]  io type (lane 16g+n, element i holds
 //                                      row 4g+i, column n of the tile)
 //   GC [NU][Dk]      fp32
 //   FL [NU]          uint8: 1 = the unit needs the exact fallback kernel
@@ -160,7 +160,7 @@ struct PrepArgs {
     const float* alpha;
     const float* beta;
     void* W;
-    float* U;
+    void* U;
     void* Kt;
     void* QG;
     void* P;
@@ -172,7 +172,7 @@ struct PrepArgs {
 
 struct ChainArgs {
     const void* W;
-    const float* U;
+    const void* U;
     const void* Kt;
     const void* QG;
     const void* P;

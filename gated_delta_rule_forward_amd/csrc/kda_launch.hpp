@@ -36,7 +36,7 @@ struct ChainArgs;
 // (b, h): NU = B * H * NC units (layout details in kda_chunk.hpp).
 struct ChunkWorkspace {
     void* W;      // [NU][C][Dk]  io type
-    float* U;     // [NU][C][Dv]  fp32
+    void* U;      // [NU][C][Dv]  io type
     void* Kt;     // [NU][Dk][C]  io type
     void* QG;     // [NU][C][Dk]  io type
     void* P;      // [NU][C][C]   io type

@@ -112,7 +112,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_exact_kernel(PrepArgs args,
     const T* __restrict__ gk = static_cast<const T*>(args.k);
     const T* __restrict__ gv = static_cast<const T*>(args.v);
     T* __restrict__ Wg = static_cast<T*>(args.W) + (size_t)unit * C * DK;
-    float* __restrict__ Ug = args.U + (size_t)unit * C * Dv;
+    T* __restrict__ Ug = static_cast<T*>(args.U) + (size_t)unit * C * Dv;
     T* __restrict__ Ktg = static_cast<T*>(args.Kt) + (size_t)unit * DK * C;
     T* __restrict__ QGg = static_cast<T*>(args.QG) + (size_t)unit * C * DK;
     T* __restrict__ Pg = static_cast<T*>(args.P) + (size_t)unit * C * C;
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_exact_kernel(PrepArgs args,
                 const f32x4 acc = tile_nn(sTi + 16 * mt * C, C, sY + 16 * ut, Dv, C, zero4());
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    Ug[u_off(16 * mt + 4 * lg + i, 16 * ut + ln, Dv)] = acc[i];
+                    Ug[u_off(16 * mt + 4 * lg + i, 16 * ut + ln, Dv)] = from_f32<T>(acc[i]);
             }
         }
     }

@@ -180,7 +180,7 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
     const float* gb = args.beta + tok0;
     const int rs = H * DK, rsv = H * Dv;                    // token strides
     T* Wg = static_cast<T*>(args.W) + (size_t)unit * C * DK;
-    float* Ug = args.U + (size_t)unit * C * Dv;
+    T* Ug = static_cast<T*>(args.U) + (size_t)unit * C * Dv;
     T* Ktg = static_cast<T*>(args.Kt) + (size_t)unit * DK * C;
     T* QGg = static_cast<T*>(args.QG) + (size_t)unit * C * DK;
     T* Pg = static_cast<T*>(args.P) + (size_t)unit * C * C;
@@ -587,7 +587,10 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
 #pragma unroll
                 for (int kb = 0; kb < NKC; ++kb)
                     if (kb < nkb) acc = mma(tf[kb], frag_row<T, KB>(sVt + (16 * nt + ln) * XTS, kb * KB), acc);
-                *reinterpret_cast<f32x4*>(Ug + ((size_t)(mt * NUt + nt) * 64 + lane) * 4) = acc;
+                {
+                    const float u4[4] = {acc[0], acc[1], acc[2], acc[3]};
+                    *reinterpret_cast<Vec4<T>*>(Ug + ((size_t)(mt * NUt + nt) * 64 + lane) * 4) = Vec4<T>::from(u4);
+                }
             }
         }
     }

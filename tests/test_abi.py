@@ -55,8 +55,8 @@ def test_workspace_size(lib):
     st, n = ws_size(lib, 1, 8192, 32, 128, 128, 64, BF16)
     assert st == OK
     nu = 32 * 128
-    # W, Kt, QG bf16 + U fp32 + P bf16 + chunk decay fp32 + one flag byte, per chunk
-    assert n == nu * (3 * 64 * 128 * 2 + 64 * 128 * 4 + 64 * 64 * 2 + 128 * 4 + 1)
+    # W, Kt, QG, U, P bf16 + chunk decay fp32 + one flag byte, per chunk
+    assert n == nu * (3 * 64 * 128 * 2 + 64 * 128 * 2 + 64 * 64 * 2 + 128 * 4 + 1)
     assert ws_size(lib, 1, 0, 1, 16, 16, 16, F32) == (OK, 0)
     assert ws_size(lib, 1, 10, 1, 24, 16, 16, F32)[0] == UNSUP          # Dk not supported
     assert ws_size(lib, 1, 10, 1, 16, 24, 16, F32)[0] == UNSUP          # Dv not a multiple of 16
