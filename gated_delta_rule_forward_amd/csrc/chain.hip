@@ -74,7 +74,7 @@ struct ChainGeom {
     static constexpr bool PREFETCH =
         (C * DK * (int)sizeof(T)) % 1024 == 0 && (C * C * (int)sizeof(T)) % 1024 == 0;
     static constexpr int PTOT = 3 * PW + PP;
-    static constexpr int KPF = PREFETCH ? 3 : 0;
+    static constexpr int KPF = PREFETCH ? 2 : 0;
     static_assert(NDMA <= 63, "vmcnt holds at most 63 outstanding loads");
 };
 
@@ -264,31 +264,41 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
     const int col = slice * 16 + ln;
 
     // Operand FIFO.  Chunk c is loaded into stage c & 1 by the loader
-    // wavefronts (wave 4 + w fills compute wave w's region) at the start of
-    // step c - 2 and moved into registers by the compute wavefronts at the end
-    // of step c - 1, between the step's two barriers: the loader waits for
-    // chunk c before barrier 1 of step c - 1, and stage c & 1 is free again
-    // after barrier 2 of step c - 1.  Past the last chunk the last one is
-    // re-read, so every step issues the same NDMA loads per loader.
+    // wavefronts (wave 4 + w fills compute wave w's region) during step c - 2
+    // (part 0 before its barrier 1, the rest after it) and moved into
+    // registers by the compute wavefronts at the end of step c - 1, between
+    // the step's two barriers: the loader waits for chunk c before barrier 1
+    // of step c - 1, and stage c & 1 is free again after barrier 2 of step
+    // c - 1.  Past the last chunk the last one is re-read, so every step
+    // issues the same NDMA loads per loader.
     const size_t u0 = (size_t)bh * NC;
     const int last = NC - 1;
     const int cw = wave & (kChainWaves - 1);     // the compute wave a loader serves
     auto stg = [&](int c) { return stages + (size_t)((c & 1) * kChainWaves + cw) * G::STAGE; };
     if (wave >= kChainWaves) {
-        // chunk c is also prefetched into L2 at step c - 5; the waits below
-        // let the two youngest prefetch rounds stay in flight
+        // chunk c is also prefetched into L2 at step c - 5 (KPF loads per
+        // loader and step)
         unsigned char* sink = stages + G::SINK;
         issue_all<T, C, DK>(stg(0), a, u0, cw, lane, slice);
+        prefetch_chunk<T, C, DK>(a, u0 + min(2, last), slice, NS, cw, lane, sink);
+        prefetch_chunk<T, C, DK>(a, u0 + min(3, last), slice, NS, cw, lane, sink);
         issue_all<T, C, DK>(stg(1), a, u0 + min(1, last), cw, lane, slice);
-        for (int c = 2; c < 5; ++c) prefetch_chunk<T, C, DK>(a, u0 + min(c, last), slice, NS, cw, lane, sink);
+        prefetch_chunk<T, C, DK>(a, u0 + min(4, last), slice, NS, cw, lane, sink);
         wait_vm<G::NDMA + 3 * G::KPF>();             // chunk 0 landed
         lds_barrier();                               // B0: compute reads chunk 0
         lds_barrier();                               // B1: stage 0 free
+        constexpr int N0 = 2 * G::runs(G::NKD * G::FB);   // loads of part 0
         for (int nc = 0; nc < NC; ++nc) {
-            issue_all<T, C, DK>(stg(nc), a, u0 + min(nc + 2, last), cw, lane, slice);
-            prefetch_chunk<T, C, DK>(a, u0 + min(nc + 5, last), slice, NS, cw, lane, sink);
-            wait_vm<G::NDMA + 2 * G::KPF>();         // chunk nc + 1 landed
+            // part 0 of chunk nc + 2 before barrier 1 and the rest after it:
+            // issuing blocks while the load pipe is full, so the compute
+            // wavefronts must not wait at barrier 1 for all of it.  Loads
+            // issued after chunk nc + 1: the previous step's prefetch and part 0.
+            issue_chunk<T, C, DK, 0>(stg(nc), a, u0 + min(nc + 2, last), cw, lane, slice);
+            wait_vm<N0 + G::KPF>();                  // chunk nc + 1 landed
             lds_barrier();
+            issue_chunk<T, C, DK, 1>(stg(nc), a, u0 + min(nc + 2, last), cw, lane, slice);
+            issue_chunk<T, C, DK, 2>(stg(nc), a, u0 + min(nc + 2, last), cw, lane, slice);
+            prefetch_chunk<T, C, DK>(a, u0 + min(nc + 5, last), slice, NS, cw, lane, sink);
             lds_barrier();
         }
         wait_vm<0>();   // no load may land in LDS after the workgroup ends

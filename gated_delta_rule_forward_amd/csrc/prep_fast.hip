@@ -32,8 +32,12 @@
 // Outputs go out fragment-major (kda_chunk.hpp): P and W are produced as
 // transposed tiles (P^T = Y X_P^T, W^T = X_W^T Tinv^T), whose C-layout
 // accumulators are exactly the A fragments the chain kernel consumes, so each
-// lane stores one contiguous 16-byte fragment; Q*Gamma goes through LDS; the
-// thread that owns (channel, tokens) writes its Ktil fragment slots directly.
+// lane stores one contiguous 16-byte fragment; the thread that owns
+// (channel quad, tokens) writes its Q*Gamma and Ktil fragment slots directly.
+//
+// LDS is one region reused phase by phase (gate summary, A/P operands, A and
+// Tinv, X_W^T and (beta V)^T), about 52 KB for bf16 C = 64, Dk = 128 without
+// extra columns, so three workgroups share a CU.
 #include "kda_chunk.hpp"
 #include "kda_launch.hpp"
 
@@ -56,7 +60,6 @@ struct FastGeom {
     static constexpr int ACTIVE = NQ * PARTS;                 // threads that own elements
     static constexpr int PADE = 16 / (int)sizeof(T);          // 16-byte row pad
     static constexpr int LDF = C + 4;                         // row stride of fp32 A / Tinv
-    static constexpr int XWS = DK + PADE;                     // row stride of X_W, Q*Gamma staging
     static constexpr int NB = C / 16;
     static constexpr int DVMAX = sizeof(T) == 4 ? 64 : 128;
     static constexpr int XTS = C + PADE;                      // row stride of X_W^T, (beta V)^T
@@ -68,24 +71,25 @@ struct FastGeom {
 template <typename T, int C, int DK>
 struct FastLayout {
     int KS;                 // operand row stride (elements)
-    size_t ops, sA, scr, total;
+    size_t scr, total;
+    // one region reused phase by phase (offsets from 0):
+    //   gate summary: partL, partPZ [PARTS][DK] fp32 / int
+    //   A / P:        XA, XP, Y [C][KS] io type
+    //   Tinv:         A, Tinv [C][LDF] fp32
+    //   W / U:        X_W^T [DK][XTS], (beta V)^T [DVMAX][XTS] io type
     __host__ __device__ FastLayout(int zx) {
         using G = FastGeom<T, C, DK>;
         const int kp_max = ((DK + zx + G::KB - 1) / G::KB) * G::KB;
         KS = kp_max + G::PADE;
         const size_t e = sizeof(T);
-        const size_t opsz1 = 3 * (size_t)C * KS * e;
-        const size_t opsz2 = (size_t)C * G::LDF * 4 + (size_t)(DK + G::DVMAX) * G::XTS * e;
-        const size_t opsz = ((opsz1 > opsz2 ? opsz1 : opsz2) + 15) & ~size_t(15);
-        // the sA region also holds Q*Gamma staging and, before that, the
-        // per-token-range partial gate sums (partL, partPZ: PARTS x DK each)
-        const size_t asz1 = (size_t)C * G::LDF * 4, asz2 = (size_t)C * G::XWS * e;
-        const size_t asz3 = (size_t)2 * G::PARTS * DK * 4;
-        size_t asz = asz1 > asz2 ? asz1 : asz2;
-        asz = ((asz > asz3 ? asz : asz3) + 15) & ~size_t(15);
-        ops = 0;
-        sA = ops + opsz;
-        scr = sA + asz;
+        const size_t r1 = (size_t)2 * G::PARTS * DK * 4;
+        const size_t r2 = 3 * (size_t)C * KS * e;
+        const size_t r3 = (size_t)2 * C * G::LDF * 4;
+        const size_t r4 = (size_t)(DK + G::DVMAX) * G::XTS * e;
+        size_t r = r1 > r2 ? r1 : r2;
+        r = r > r3 ? r : r3;
+        r = r > r4 ? r : r4;
+        scr = (r + 15) & ~size_t(15);
         // base [DK], misc [8], beta [C]
         total = scr + (DK + 8 + C) * 4;
         total = (total + 15) & ~size_t(15);
@@ -96,40 +100,6 @@ __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(
 __device__ __forceinline__ float flog2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float frcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// one fragment (NV slots) of an A-operand from a row-major matrix in LDS:
-// row r, k block s, lane group g -> slots j at columns of frag_off's mapping
-template <typename T, int KB>
-__device__ __forceinline__ Frag<T, KB> gather_frag(const T* row, int s, int g) {
-    constexpr int NV = KB / 4;
-    float f[NV];
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-        const int kk = KB == 32 ? 16 * (j >> 2) + 4 * g + (j & 3) : 4 * g + j;
-        f[j] = to_f32(row[s * KB + kk]);
-    }
-    return Frag<T, KB>::from(f);
-}
-
-// fragment whose k index runs down a column of a row-major LDS matrix: lane
-// (m, g) takes rows k0 + NV g + x (x < NV) of column m (base = column 0 of the
-// 16-column tile, ld = row stride)
-template <typename T, int KB>
-__device__ __forceinline__ Frag<T, KB> frag_col(const T* base, int ld, int k0) {
-    const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
-    constexpr int NV = KB / 4;
-    Frag<T, KB> f;
-    if constexpr (sizeof(T) == 2) {
-        const short* b = reinterpret_cast<const short*>(base) + (k0 + NV * g) * ld + m;
-#pragma unroll
-        for (int x = 0; x < NV; ++x) f.v[x] = b[x * ld];
-    } else {
-        const float* b = reinterpret_cast<const float*>(base) + (k0 + NV * g) * ld + m;
-#pragma unroll
-        for (int x = 0; x < NV; ++x) f.v[x] = b[x * ld];
-    }
-    return f;
-}
-
 // ZS: the chunk may hold zero gates, placed in extra contraction columns (the
 // launch passes ZS = true exactly when extra columns are allotted); without
 // them a zero gate makes a part product vanish and flags the chunk.
@@ -139,22 +109,21 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
     using G = FastGeom<T, C, DK>;
     using F = Frag<T, G::KB>;
     constexpr int KB = G::KB, NV = G::NV, TPB = G::TPB, PARTS = G::PARTS, TOK = G::TOK;
-    constexpr int NB = G::NB, LDF = G::LDF, XWS = G::XWS, XTS = G::XTS, TV = G::TV;
+    constexpr int NB = G::NB, LDF = G::LDF, XTS = G::XTS, TV = G::TV;
     constexpr int NKD = DK / KB, NKC = C / KB;
     const int Dv = args.Dv;
     const FastLayout<T, C, DK> LY(args.zx);
     const int KS = LY.KS;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
-    T* XA = reinterpret_cast<T*>(lds + LY.ops);
+    float* partL = reinterpret_cast<float*>(lds);                           // gate summary
+    int* partPZ = reinterpret_cast<int*>(partL + PARTS * DK);               // nz << 1 | parity
+    T* XA = reinterpret_cast<T*>(lds);                                      // A / P operands
     T* XP = XA + C * KS;
     T* Y = XP + C * KS;
-    float* sT = reinterpret_cast<float*>(lds + LY.ops);                    // after A/P
-    T* sXWt = reinterpret_cast<T*>(lds + LY.ops + (size_t)C * LDF * 4);     // X_W^T [DK][XTS]
+    float* sA = reinterpret_cast<float*>(lds);                              // Tinv phase
+    float* sT = sA + C * LDF;
+    T* sXWt = reinterpret_cast<T*>(lds);                                    // X_W^T [DK][XTS]
     T* sVt = sXWt + DK * XTS;                                               // (beta V)^T [Dv][XTS]
-    float* sA = reinterpret_cast<float*>(lds + LY.sA);
-    T* sQG = reinterpret_cast<T*>(lds + LY.sA);                             // before A/P
-    float* partL = reinterpret_cast<float*>(lds + LY.sA);                  // before Q*Gamma
-    int* partPZ = reinterpret_cast<int*>(partL + PARTS * DK);               // nz << 1 | parity
     int* sBase = reinterpret_cast<int*>(lds + LY.scr);
     int* misc = sBase + DK;
     float* sBeta = reinterpret_cast<float*>(misc + 8);
@@ -361,7 +330,7 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
         }
         xw[j] = Vec4<T>::from(fw);
         if (own) {
-            *reinterpret_cast<Vec4<T>*>(sQG + r * XWS + c0) = Vec4<T>::from(fq);
+            *reinterpret_cast<Vec4<T>*>(QGg + frag_off<KB>(r, c0, DK)) = Vec4<T>::from(fq);
             if (!ZS || Ztot == 0) {
                 *reinterpret_cast<Vec4<T>*>(XA + r * KS + c0) = Vec4<T>::from(fa);
                 *reinterpret_cast<Vec4<T>*>(XP + r * KS + c0) = Vec4<T>::from(fp);
@@ -411,7 +380,7 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
         }
     }
     __syncthreads();
-    // V tile loads: in flight during the Q*Gamma emission and the A / P tiles
+    // V tile loads: in flight during the A / P tiles and Tinv
     // item (column quad vq, token run tg): 4 columns x TV tokens, stored later
     // as 4 rows of (beta V)^T; rows past the end re-read the last valid row
     const int nvq = Dv / 4, nvit = nvq * (C / TV);
@@ -424,22 +393,21 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
         for (int z = 0; z < TV; ++z)
             vreg[x][z] = Vec4<T>::load(gv + min(tg * TV + z, nvalid - 1) * rsv + 4 * vq);
     }
-    // Q*Gamma fragments: 64 lanes x (C/16) x (DK/KB) per chunk
-    for (int f = tid; f < (C / 16) * NKD * 64; f += kThreads) {
-        const int l = f & 63, blk = f >> 6;
-        const int mt = blk / NKD, s = blk % NKD;
-        *reinterpret_cast<F*>(QGg + (size_t)f * NV) =
-            gather_frag<T, KB>(sQG + (16 * mt + (l & 15)) * XWS, s, l >> 4);
-    }
-    __syncthreads();   // the staging area becomes sA
 
     // ---- A (strictly lower, LDS) and P^T tiles (global, fragment-major) --------
     // wave w takes row tile ta = w: over the contraction it keeps the row's
     // (beta K * F) and (Q * F) fragments and streams (K * G) of tiles tb <= ta
-    for (int ta = wave; ta < NB; ta += 4) {
-        f32x4 accA[NB], accP[NB];
+    // (NB <= 4: each wavefront has at most one row tile; its A tiles stay in
+    // registers until the operands are dead and the region becomes A, Tinv)
+    static_assert(NB <= 4, "one row tile per wavefront");
+    const int ta = wave;
+    f32x4 accA[NB];
 #pragma unroll
-        for (int tb = 0; tb < NB; ++tb) { accA[tb] = zero4(); accP[tb] = zero4(); }
+    for (int tb = 0; tb < NB; ++tb) accA[tb] = zero4();
+    if (ta < NB) {
+        f32x4 accP[NB];
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb) accP[tb] = zero4();
         for (int k0 = 0; k0 < KP; k0 += KB) {
             const F xa = frag_row<T, KB>(XA + (16 * ta + ln) * KS, k0);
             const F xp = frag_row<T, KB>(XP + (16 * ta + ln) * KS, k0);
@@ -449,16 +417,6 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
                     const F y = frag_row<T, KB>(Y + (16 * tb + ln) * KS, k0);
                     accA[tb] = mma(xa, y, accA[tb]);    // A[16ta + 4g + i][16tb + n]
                     accP[tb] = mma(y, xp, accP[tb]);    // P[16ta + n][16tb + 4g + i]
-                }
-            }
-        }
-#pragma unroll
-        for (int tb = 0; tb < NB; ++tb) {
-            if (tb <= ta) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * ta + 4 * lg + i, col = 16 * tb + ln;
-                    sA[r * LDF + col] = col < r ? accA[tb][i] : 0.f;
                 }
             }
         }
@@ -475,36 +433,16 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
             *reinterpret_cast<F*>(Pg + ((size_t)(ta * NKC + s) * 64 + lane) * NV) = F::from(f);
         }
     }
-    __syncthreads();   // operands dead: the region now holds sT, sXWt, sVt
-
-    // ---- stage X_W^T and (diag(beta) V)^T; Tinv diagonal blocks ----------------
-    // X_W^T row c holds this thread's TOK tokens of channel c contiguously
-    if (own) {
+    __syncthreads();   // operands dead: the region now holds A and Tinv
+    if (ta < NB) {
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            T* dst = sXWt + (c0 + x) * XTS + part * TOK;
-            if constexpr (TOK * sizeof(T) == 16) {
-                T v[TOK];
+        for (int tb = 0; tb < NB; ++tb) {
+            if (tb <= ta) {
 #pragma unroll
-                for (int j = 0; j < TOK; ++j) v[j] = xw[j].elem(x);
-                *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(v);
-            } else {
-#pragma unroll
-                for (int j = 0; j < TOK; ++j) dst[j] = xw[j].elem(x);
-            }
-        }
-    }
-#pragma unroll
-    for (int x = 0; x < G::VIT; ++x) {
-        const int it = tid + x * kThreads;
-        if (it < nvit) {
-            const int vq = it % nvq, tg = it / nvq;
-#pragma unroll
-            for (int y = 0; y < 4; ++y) {
-                T v[TV];
-#pragma unroll
-                for (int z = 0; z < TV; ++z) v[z] = from_f32<T>(sBeta[tg * TV + z] * vreg[x][z].get(y));
-                *reinterpret_cast<uint4*>(sVt + (4 * vq + y) * XTS + tg * TV) = *reinterpret_cast<const uint4*>(v);
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * ta + 4 * lg + i, col = 16 * tb + ln;
+                    sA[r * LDF + col] = col < r ? accA[tb][i] : 0.f;
+                }
             }
         }
     }
@@ -512,6 +450,9 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
         const int r = idx / C, col = idx % C;
         if ((col >> 4) > (r >> 4)) sT[r * LDF + col] = 0.f;
     }
+    __syncthreads();
+
+    // ---- Tinv diagonal blocks ---------------------------------------------------
     // forward substitution on the 16x16 diagonal blocks: wave 0, lane 16a + j
     // owns column j of block a
     if (wave == 0 && (lane >> 4) < NB) {
@@ -543,9 +484,9 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
                 inner = mma(fa, Frag<float, 16>::from(fb), inner);
             }
             const float fi[4] = {inner[0], inner[1], inner[2], inner[3]};
-            const Frag<float, 16> ta =
+            const Frag<float, 16> taa =
                 Frag<float, 16>::load(sT + (16 * a + ln) * LDF + 16 * a + 4 * lg);
-            const f32x4 tab = mma(ta, Frag<float, 16>::from(fi), zero4());
+            const f32x4 tab = mma(taa, Frag<float, 16>::from(fi), zero4());
 #pragma unroll
             for (int i = 0; i < 4; ++i) sT[(16 * a + 4 * lg + i) * LDF + 16 * bb + ln] = -tab[i];
         }
@@ -559,12 +500,48 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
     {
         constexpr int NM = C / 16;
         const int NUt = Dv / 16;
-        for (int mt = wave; mt < NM; mt += 4) {
-            const int nkb = (16 * (mt + 1) + KB - 1) / KB;
-            F tf[NKC];
+        const int mt = wave;
+        F tf[NKC];
+        if (mt < NM) {
 #pragma unroll
             for (int kb = 0; kb < NKC; ++kb)
                 tf[kb] = frag_row_cvt<T, KB>(sT + (16 * mt + ln) * LDF, kb * KB);
+        }
+        __syncthreads();   // A and Tinv dead: the region now holds X_W^T, (beta V)^T
+        // ---- stage X_W^T and (diag(beta) V)^T ------------------------------------
+        // X_W^T row c holds this thread's TOK tokens of channel c contiguously
+        if (own) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                T* dst = sXWt + (c0 + x) * XTS + part * TOK;
+                if constexpr (TOK * sizeof(T) == 16) {
+                    T v[TOK];
+#pragma unroll
+                    for (int j = 0; j < TOK; ++j) v[j] = xw[j].elem(x);
+                    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(v);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < TOK; ++j) dst[j] = xw[j].elem(x);
+                }
+            }
+        }
+#pragma unroll
+        for (int x = 0; x < G::VIT; ++x) {
+            const int it = tid + x * kThreads;
+            if (it < nvit) {
+                const int vq = it % nvq, tg = it / nvq;
+#pragma unroll
+                for (int y = 0; y < 4; ++y) {
+                    T v[TV];
+#pragma unroll
+                    for (int z = 0; z < TV; ++z) v[z] = from_f32<T>(sBeta[tg * TV + z] * vreg[x][z].get(y));
+                    *reinterpret_cast<uint4*>(sVt + (4 * vq + y) * XTS + tg * TV) = *reinterpret_cast<const uint4*>(v);
+                }
+            }
+        }
+        __syncthreads();
+        if (mt < NM) {
+            const int nkb = (16 * (mt + 1) + KB - 1) / KB;
 #pragma unroll
             for (int s = 0; s < NKD; ++s) {
                 float f[NV];
