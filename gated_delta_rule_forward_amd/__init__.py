@@ -60,6 +60,8 @@ def load():
     lib.kda_chunk_forward_workspace_size.restype = i
     lib.kda_chunk_forward.argtypes = [vp] * 8 + [i] * 8 + [u, vp, sz, vp]
     lib.kda_chunk_forward.restype = i
+    lib.kda_chunk_forward_states.argtypes = [vp] * 9 + [i] * 8 + [u, vp, sz, vp]
+    lib.kda_chunk_forward_states.restype = i
     lib.kda_decode_step.argtypes = [vp] * 7 + [i] * 6 + [u, vp]
     lib.kda_decode_step.restype = i
     lib.kda_gate_prep.argtypes = [vp] * 4 + [i] * 5 + [vp]
@@ -109,9 +111,11 @@ def workspace_size(B: int, T: int, H: int, Dk: int, Dv: int, chunk: int, dtype: 
 
 def chunk_forward(q, k, v, alpha, beta, initial_state=None, *, chunk: int = 64, mode: int = CKDA,
                   out=None, final_state=None, output_final_state: bool = True, workspace=None,
-                  stream=None, flags: int = 0):
+                  chunk_states=None, stream=None, flags: int = 0):
     """Chunked forward.  q, k: [B,T,H,Dk]; v: [B,T,H,Dv] (fp32 or bf16, same dtype);
     alpha: [B,T,H,Dk] fp32; beta: [B,T,H] fp32; initial_state: [B,H,Dk,Dv] fp32 or None.
+    chunk_states: None, or a [B,H,ceil(T/chunk),Dk,Dv] tensor of q's dtype that
+    receives the state entering every chunk (kda_chunk_forward_states).
     Returns (out [B,T,H,Dv], final_state [B,H,Dk,Dv] fp32 or None)."""
     lib = load()
     B, T, H, Dk = q.shape
@@ -123,15 +127,26 @@ def chunk_forward(q, k, v, alpha, beta, initial_state=None, *, chunk: int = 64, 
     if workspace is None:
         nbytes = workspace_size(B, T, H, Dk, Dv, chunk, q.dtype)
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
-    _dev(q, k, v, alpha, beta, initial_state, out, final_state, workspace)
+    _dev(q, k, v, alpha, beta, initial_state, out, final_state, workspace, chunk_states)
     if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype or out.dtype != q.dtype:
         raise ValueError("q, k, v and out must share one dtype (float32 or bfloat16)")
-    st = lib.kda_chunk_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
-                               _ptr(initial_state), _ptr(out), _ptr(final_state),
-                               B, T, H, Dk, Dv, chunk, _DT[q.dtype], mode, flags,
-                               _ptr(workspace), workspace.numel() * workspace.element_size(),
-                               _stream(stream))
-    _check("kda_chunk_forward", st)
+    wsb = workspace.numel() * workspace.element_size()
+    if chunk_states is None:
+        st = lib.kda_chunk_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                   _ptr(initial_state), _ptr(out), _ptr(final_state),
+                                   B, T, H, Dk, Dv, chunk, _DT[q.dtype], mode, flags,
+                                   _ptr(workspace), wsb, _stream(stream))
+        _check("kda_chunk_forward", st)
+    else:
+        nc = (T + chunk - 1) // chunk
+        if chunk_states.dtype != q.dtype or tuple(chunk_states.shape) != (B, H, nc, Dk, Dv):
+            raise ValueError("chunk_states must be [B,H,ceil(T/chunk),Dk,Dv] in q's dtype")
+        st = lib.kda_chunk_forward_states(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                          _ptr(initial_state), _ptr(out), _ptr(final_state),
+                                          _ptr(chunk_states), B, T, H, Dk, Dv, chunk,
+                                          _DT[q.dtype], mode, flags, _ptr(workspace), wsb,
+                                          _stream(stream))
+        _check("kda_chunk_forward_states", st)
     return out, final_state
 
 

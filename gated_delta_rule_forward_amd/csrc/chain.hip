@@ -346,6 +346,18 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
     };
 
     for (int nc = 0; nc < NC; ++nc) {
+        if (a.CS) {
+            // the state entering chunk nc (this wave's tiles, rounded to T)
+            T* cs = static_cast<T*>(a.CS) + ((size_t)bh * NC + nc) * DK * Dv + col;
+#pragma unroll
+            for (int u = 0; u < G::SPW; ++u) {
+                const int t = wave + 4 * u;
+                if (t < G::NT) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) cs[(size_t)(16 * t + 4 * lg + i) * Dv] = from_f32<T>(S[u][i]);
+                }
+            }
+        }
         F sf[G::NKD];
 #pragma unroll
         for (int s = 0; s < G::NKD; ++s) sf[s] = sSf[s * 64 + lane];

@@ -109,45 +109,13 @@ ChunkShape make_shape(int B, int T, int H, int Dk, int Dv, int chunk)
     return ChunkShape{B, T, H, Dk, Dv, chunk, (T + chunk - 1) / chunk};
 }
 
-}  // namespace
-
-extern "C" {
-
-int kda_abi_version(void) { return KDA_ABI_VERSION; }
-
-const char* kda_status_string(int s)
-{
-    switch (s) {
-    case KDA_OK: return "ok";
-    case KDA_ERR_NULL_POINTER: return "a required pointer is NULL";
-    case KDA_ERR_BAD_SHAPE: return "a size is out of range or overflows";
-    case KDA_ERR_UNSUPPORTED: return "unsupported shape, dtype, mode or flag";
-    case KDA_ERR_MISALIGNED: return "a pointer breaks the alignment rule";
-    case KDA_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than kda_chunk_forward_workspace_size";
-    case KDA_ERR_ALIAS: return "an output overlaps an input";
-    case KDA_ERR_HIP: return "a HIP runtime call or kernel launch failed";
-    default: return "unknown status";
-    }
-}
-
-kda_status_t kda_chunk_forward_workspace_size(int B, int T, int H, int Dk, int Dv, int chunk,
-                                              kda_dtype_t dtype, size_t* bytes)
-{
-    if (!bytes) return KDA_ERR_NULL_POINTER;
-    const kda_status_t st = check_forward_shape(B, T, H, Dk, Dv, chunk, dtype);
-    if (st != KDA_OK) return st;
-    size_t off[kda::kWorkspaceRegions];
-    *bytes = T == 0 ? 0
-                    : kda::chunk_workspace_layout(make_shape(B, T, H, Dk, Dv, chunk),
-                                                  dtype == KDA_DTYPE_F32 ? IoType::F32 : IoType::BF16, off);
-    return KDA_OK;
-}
-
-kda_status_t kda_chunk_forward(const void* q, const void* k, const void* v, const float* alpha,
-                               const float* beta, const float* initial_state, void* out,
-                               float* final_state, int B, int T, int H, int Dk, int Dv, int chunk,
-                               kda_dtype_t dtype, kda_mode_t mode, unsigned flags, void* workspace,
-                               size_t workspace_bytes, void* stream)
+// the chunked forward; chunk_states (may be null) receives the state entering
+// every chunk
+kda_status_t chunk_forward(const void* q, const void* k, const void* v, const float* alpha,
+                           const float* beta, const float* initial_state, void* out,
+                           float* final_state, void* chunk_states, int B, int T, int H, int Dk,
+                           int Dv, int chunk, kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
+                           void* workspace, size_t workspace_bytes, void* stream)
 {
     kda_status_t st = check_forward_shape(B, T, H, Dk, Dv, chunk, dtype);
     if (st != KDA_OK) return st;
@@ -168,21 +136,24 @@ kda_status_t kda_chunk_forward(const void* q, const void* k, const void* v, cons
     const void* vec[] = {q, k, alpha, workspace};
     for (const void* p : vec)
         if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
-    const void* elt[] = {v, out, beta, initial_state, final_state};
-    const uintptr_t ea[] = {e, e, 4, 4, 4};
-    for (int i = 0; i < 5; ++i)
+    const void* elt[] = {v, out, beta, initial_state, final_state, chunk_states};
+    const uintptr_t ea[] = {e, e, 4, 4, 4, e};
+    for (int i = 0; i < 6; ++i)
         if (elt[i] && !aligned(elt[i], ea[i])) return KDA_ERR_MISALIGNED;
 
-    // aliasing: out and workspace overlap nothing; final_state may equal
-    // initial_state exactly but overlap nothing else
+    // aliasing: out, workspace and chunk_states overlap nothing; final_state
+    // may equal initial_state exactly but overlap nothing else
+    const size_t ncs = chunk_states ? (size_t)B * H * ((T + chunk - 1) / chunk) * Dk * Dv * e : 0;
     struct R { const void* p; size_t n; } in[] = {
         {q, ntok * Dk * e}, {k, ntok * Dk * e}, {v, ntok * Dv * e},
         {alpha, ntok * Dk * 4}, {beta, ntok * 4}, {initial_state, initial_state ? nstate : 0}};
-    const R outs[] = {{out, ntok * Dv * e}, {workspace, ws_need}};
+    const R outs[] = {{out, ntok * Dv * e}, {workspace, ws_need}, {chunk_states, ncs}};
     for (const R& o : outs)
         for (const R& i : in)
             if (overlaps(o.p, o.n, i.p, i.n)) return KDA_ERR_ALIAS;
-    if (overlaps(out, ntok * Dv * e, workspace, ws_need)) return KDA_ERR_ALIAS;
+    for (int x = 0; x < 3; ++x)
+        for (int y = x + 1; y < 3; ++y)
+            if (overlaps(outs[x].p, outs[x].n, outs[y].p, outs[y].n)) return KDA_ERR_ALIAS;
     if (final_state) {
         const R fs{final_state, nstate};
         for (const R& i : in) {
@@ -228,7 +199,7 @@ kda_status_t kda_chunk_forward(const void* q, const void* k, const void* v, cons
     const kda::PrepArgs pa{q, k, v, alpha, beta, ws.W, ws.U, ws.Kt, ws.QG, ws.P, ws.GC, ws.FL,
                            T, H, Dv, sh.NC, zx};
     const kda::ChainArgs ca{ws.W, ws.U, ws.Kt, ws.QG, ws.P, ws.GC, initial_state, out,
-                            final_state, B, T, H, Dv, sh.NC};
+                            final_state, chunk_states, B, T, H, Dv, sh.NC};
 
     if (rec.mark("prep_fast") != hipSuccess) return KDA_ERR_HIP;
     if (kda::launch_prep_fast(io, sh, pa, s) != hipSuccess) return KDA_ERR_HIP;
@@ -240,6 +211,64 @@ kda_status_t kda_chunk_forward(const void* q, const void* k, const void* v, cons
     if (kda::launch_chain(io, sh, ca, s) != hipSuccess) return KDA_ERR_HIP;
     if (rec.done() != hipSuccess) return KDA_ERR_HIP;
     return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_status_string(int s)
+{
+    switch (s) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case KDA_ERR_BAD_SHAPE: return "a size is out of range or overflows";
+    case KDA_ERR_UNSUPPORTED: return "unsupported shape, dtype, mode or flag";
+    case KDA_ERR_MISALIGNED: return "a pointer breaks the alignment rule";
+    case KDA_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than kda_chunk_forward_workspace_size";
+    case KDA_ERR_ALIAS: return "an output overlaps an input";
+    case KDA_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+kda_status_t kda_chunk_forward_workspace_size(int B, int T, int H, int Dk, int Dv, int chunk,
+                                              kda_dtype_t dtype, size_t* bytes)
+{
+    if (!bytes) return KDA_ERR_NULL_POINTER;
+    const kda_status_t st = check_forward_shape(B, T, H, Dk, Dv, chunk, dtype);
+    if (st != KDA_OK) return st;
+    size_t off[kda::kWorkspaceRegions];
+    *bytes = T == 0 ? 0
+                    : kda::chunk_workspace_layout(make_shape(B, T, H, Dk, Dv, chunk),
+                                                  dtype == KDA_DTYPE_F32 ? IoType::F32 : IoType::BF16, off);
+    return KDA_OK;
+}
+
+kda_status_t kda_chunk_forward(const void* q, const void* k, const void* v, const float* alpha,
+                               const float* beta, const float* initial_state, void* out,
+                               float* final_state, int B, int T, int H, int Dk, int Dv, int chunk,
+                               kda_dtype_t dtype, kda_mode_t mode, unsigned flags, void* workspace,
+                               size_t workspace_bytes, void* stream)
+{
+    return chunk_forward(q, k, v, alpha, beta, initial_state, out, final_state, nullptr, B, T, H,
+                         Dk, Dv, chunk, dtype, mode, flags, workspace, workspace_bytes, stream);
+}
+
+kda_status_t kda_chunk_forward_states(const void* q, const void* k, const void* v,
+                                      const float* alpha, const float* beta,
+                                      const float* initial_state, void* out, float* final_state,
+                                      void* chunk_states, int B, int T, int H, int Dk, int Dv,
+                                      int chunk, kda_dtype_t dtype, kda_mode_t mode,
+                                      unsigned flags, void* workspace, size_t workspace_bytes,
+                                      void* stream)
+{
+    if (T > 0 && !chunk_states) return KDA_ERR_NULL_POINTER;
+    return chunk_forward(q, k, v, alpha, beta, initial_state, out, final_state, chunk_states, B,
+                         T, H, Dk, Dv, chunk, dtype, mode, flags, workspace, workspace_bytes,
+                         stream);
 }
 
 kda_status_t kda_decode_step(const void* q, const void* k, const void* v, const float* alpha,

@@ -180,6 +180,7 @@ struct ChainArgs {
     const float* S0;
     void* out;
     float* ST;
+    void* CS;          // chunk-start states [B,H,NC,Dk,Dv] in the io type, or null
     int B, T, H, Dv, NC;
 };
 

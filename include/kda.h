@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 typedef enum {
     KDA_OK = 0,
@@ -120,6 +120,27 @@ kda_status_t kda_chunk_forward(const void* q, const void* k, const void* v,
                                kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
                                void* workspace, size_t workspace_bytes,
                                void* stream);
+
+/*
+ * kda_chunk_forward that also stores the chunk-start states: the state carried
+ * from chunk to chunk in the chunkwise form ("Kimi Delta Attention: a bounded
+ * case study", Exercise 2), i.e. for chunk n the state after tokens
+ * 0 .. n*chunk - 1 (n = 0: initial_state, or zero), which a backward pass or a
+ * resumed segment starts from.
+ *   chunk_states : [B,H,NC,Dk,Dv] in dtype (NC = ceil(T / chunk)), rounded
+ *                  to nearest even from the fp32 carried state for bf16;
+ *                  required when T > 0; must not overlap any other argument.
+ * Every other argument, rule and error is that of kda_chunk_forward.  The
+ * states cost one extra write of B*H*NC*Dk*Dv elements.
+ */
+kda_status_t kda_chunk_forward_states(const void* q, const void* k, const void* v,
+                                      const float* alpha, const float* beta,
+                                      const float* initial_state,
+                                      void* out, float* final_state, void* chunk_states,
+                                      int B, int T, int H, int Dk, int Dv, int chunk,
+                                      kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
+                                      void* workspace, size_t workspace_bytes,
+                                      void* stream);
 
 /*
  * One single-token step for every (b, h), applied to a resident fp32 state in

@@ -49,7 +49,7 @@ def _load():
         fp = ctypes.POINTER(ctypes.c_float)
         dp = ctypes.POINTER(ctypes.c_double)
         i = ctypes.c_int
-        lib.kda_oracle_forward.argtypes = [fp, fp, fp, fp, fp, fp, dp, dp,
+        lib.kda_oracle_forward.argtypes = [fp, fp, fp, fp, fp, fp, dp, dp, dp, i,
                                            i, i, i, i, i, i]
         lib.kda_oracle_forward.restype = i
         lib.kda_oracle_decode.argtypes = [fp, fp, fp, fp, fp, dp, dp,
@@ -78,11 +78,12 @@ def default_threads() -> int:
         return os.cpu_count() or 1
 
 
-def forward(q, k, v, alpha, beta, S0=None, nthreads: int | None = None):
+def forward(q, k, v, alpha, beta, S0=None, nthreads: int | None = None, chunk: int | None = None):
     """Token-by-token forward.  q, k, alpha: [B,T,H,Dk]; v: [B,T,H,Dv];
     beta: [B,T,H]; S0: [B,H,Dk,Dv] or None (zero).  Inputs are taken as float32
     (exact for bf16 and fp32 values).  Returns (out [B,T,H,Dv], ST [B,H,Dk,Dv])
-    in float64."""
+    in float64; with chunk given, also CS [B,H,ceil(T/chunk),Dk,Dv], the state
+    before token n*chunk for every n."""
     lib = _load()
     q, k, v, alpha, beta = (_f32(x) for x in (q, k, v, alpha, beta))
     B, T, H, Dk = q.shape
@@ -94,14 +95,19 @@ def forward(q, k, v, alpha, beta, S0=None, nthreads: int | None = None):
         assert s0.shape == (B, H, Dk, Dv)
     out = np.empty((B, T, H, Dv), dtype=np.float64)
     ST = np.empty((B, H, Dk, Dv), dtype=np.float64)
+    CS = None
+    if chunk is not None:
+        assert chunk > 0
+        CS = np.empty((B, H, (T + chunk - 1) // chunk, Dk, Dv), dtype=np.float64)
     rc = lib.kda_oracle_forward(
         _ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float),
         _ptr(alpha, ctypes.c_float), _ptr(beta, ctypes.c_float),
         _ptr(s0, ctypes.c_float), _ptr(out, ctypes.c_double), _ptr(ST, ctypes.c_double),
+        _ptr(CS, ctypes.c_double), chunk or 0,
         B, T, H, Dk, Dv, nthreads or default_threads())
     if rc != 0:
         raise RuntimeError("kda_oracle_forward failed")
-    return out, ST
+    return (out, ST) if chunk is None else (out, ST, CS)
 
 
 def decode(q, k, v, alpha, beta, S, nthreads: int | None = None):

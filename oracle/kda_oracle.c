@@ -73,11 +73,13 @@ static void set_threads(int nthreads)
 
 int kda_oracle_forward(const float* q, const float* k, const float* v,
                        const float* alpha, const float* beta, const float* S0,
-                       double* out, double* ST,
+                       double* out, double* ST, double* CS, int chunk,
                        int B, int T, int H, int Dk, int Dv, int nthreads)
 {
     if (!q || !k || !v || !alpha || !beta || !out) return -1;
     if (B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return -1;
+    if (CS && chunk <= 0) return -1;
+    const long nchunks = CS ? (T + chunk - 1) / chunk : 0;
     set_threads(nthreads);
     const long nbh = (long)B * H;
     int failed = 0;
@@ -100,6 +102,9 @@ int kda_oracle_forward(const float* q, const float* k, const float* v,
         }
         for (int t = 0; t < T; ++t) {
             const size_t tok = ((size_t)b * T + t) * H + h;
+            if (CS && t % chunk == 0)
+                memcpy(CS + ((size_t)bh * nchunks + t / chunk) * Dk * Dv, S,
+                       sizeof(double) * (size_t)Dk * Dv);
             token_update(S, q + tok * Dk, k + tok * Dk, v + tok * Dv,
                          alpha + tok * Dk, (double)beta[tok], out + tok * Dv,
                          Dk, Dv, pred);

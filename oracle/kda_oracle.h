@@ -32,11 +32,15 @@ extern "C" {
 #endif
 
 /* Sequential token-by-token forward over T tokens.  S0 may be NULL (zero
- * initial state); ST may be NULL (final state not wanted).  nthreads <= 0 uses
- * the OpenMP default.  Parallelism is over independent (b, h) pairs only. */
+ * initial state); ST may be NULL (final state not wanted).  CS may be NULL;
+ * otherwise chunk > 0 and CS [B, H, ceil(T/chunk), Dk, Dv] receives, for every
+ * n, the state before token n*chunk (the state a chunk of the chunkwise form
+ * starts from; "Kimi Delta Attention: a bounded case study", Exercise 2).
+ * nthreads <= 0 uses the OpenMP default.  Parallelism is over independent
+ * (b, h) pairs only. */
 int kda_oracle_forward(const float* q, const float* k, const float* v,
                        const float* alpha, const float* beta, const float* S0,
-                       double* out, double* ST,
+                       double* out, double* ST, double* CS, int chunk,
                        int B, int T, int H, int Dk, int Dv, int nthreads);
 
 /* nsteps single-token updates applied to a resident double state in place.

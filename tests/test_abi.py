@@ -32,14 +32,14 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     syms = declared_symbols()
-    assert {"kda_chunk_forward", "kda_decode_step", "kda_chunk_forward_workspace_size",
+    assert {"kda_chunk_forward", "kda_chunk_forward_states", "kda_decode_step", "kda_chunk_forward_workspace_size",
             "kda_gate_prep", "kda_status_string", "kda_abi_version"} <= set(syms)
     for s in syms:
         assert hasattr(lib, s), s
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 1
+    assert lib.kda_abi_version() == 2
     for s in range(8):
         assert lib.kda_status_string(s)
     assert lib.kda_status_string(99) == b"unknown status"
@@ -124,6 +124,29 @@ def test_forward_alias_rules(lib):
     # check that a *partial* overlap is rejected)
     s0 = f(1 << 20)
     assert fwd(lib, s0=s0, st=ctypes.c_void_p(s0.value + 16)) == ALIAS
+
+
+def fwd_states(lib, cs, **kw):
+    f = Fake()
+    B, T, H, Dk, Dv, C = 1, kw.get("T", 64), 2, 16, 16, 16
+    st, need = ws_size(lib, B, max(T, 0), H, Dk, Dv, C, F32)
+    a = dict(q=f(), k=f(), v=f(), alpha=f(), beta=f(), out=f(), ws=f(max(need, 1) + 4096))
+    a.update({k_: v_ for k_, v_ in kw.items() if k_ in a})
+    return lib.kda_chunk_forward_states(a["q"], a["k"], a["v"], a["alpha"], a["beta"], None,
+                                        a["out"], None, cs, B, T, H, Dk, Dv, C, F32, 1, 0,
+                                        a["ws"], need, None)
+
+
+def test_forward_states_validation(lib):
+    f = Fake()
+    assert fwd_states(lib, None) == NULLP                       # states required when T > 0
+    assert fwd_states(lib, ctypes.c_void_p(0x7f0000000002)) == MISAL
+    base = f(1 << 24)
+    # the states region (1 x 2 x 4 x 16 x 16 fp32 = 8 KiB) overlapping q, out or workspace
+    assert fwd_states(lib, ctypes.c_void_p(base.value + 4096), q=base) == ALIAS
+    assert fwd_states(lib, ctypes.c_void_p(base.value), out=ctypes.c_void_p(base.value + 8188)) == ALIAS
+    assert fwd_states(lib, ctypes.c_void_p(base.value + 64), ws=base) == ALIAS
+    assert fwd_states(lib, f(), T=-1) == SHAPE
 
 
 def test_decode_validation(lib):

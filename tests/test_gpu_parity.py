@@ -84,6 +84,37 @@ def test_forward_dk_ne_dv_and_zero_state_pointer():
     assert torch.equal(out, out2) and torch.equal(st, st2)
 
 
+STATES = [
+    ("f32_ckda_dk32_dv48_c32_T67_s0", 1, dict(B=1, H=3, T=67, D=32, chunk=32, s0_std=0.5)),
+    ("bf16_kda_d64_c16_T200", 2, dict(B=2, H=3, T=200, D=64, chunk=16)),
+    ("bf16_ckda_d128_c64_T1000_s0", 3, dict(B=1, H=4, T=1000, chunk=64)),
+]
+
+
+@pytest.mark.parametrize("name,base,ov", STATES, ids=[c[0] for c in STATES])
+def test_forward_chunk_states(name, base, ov):
+    """kda_chunk_forward_states: the state entering every chunk, in the io
+    dtype, against the oracle's state before token n*chunk; outputs and final
+    state identical to kda_chunk_forward's."""
+    w = workloads.workload(base, **ov)
+    say(f"[forward states] {name}: {w}")
+    inp = workloads.make_prefill(w, device="cpu")
+    q, k, v, a = (np32(inp[x]) for x in ("q", "k", "v", "alpha"))
+    s0 = None if inp.get("S0") is None else np32(inp["S0"])
+    o_ref, s_ref, cs_ref = oracle.forward(q, k, v, a, np32(inp["beta"]), s0,
+                                          nthreads=oracle_threads(), chunk=w.chunk)
+    d = to_dev(inp)
+    nc = (w.T + w.chunk - 1) // w.chunk
+    cs = torch.full((w.B, w.H, nc, w.D, w.D), float("nan"), dtype=w.dtype, device=DEV)
+    out, st = run_gpu(d, w.chunk, w.mode, chunk_states=cs)
+    out_plain, st_plain = run_gpu(d, w.chunk, w.mode)
+    ec = slice_err_state(np32(cs).reshape(w.B, w.H * nc, w.D, w.D),
+                         cs_ref.reshape(w.B, w.H * nc, w.D, w.D))
+    say(f"  err chunk states {ec:.3e}")
+    assert ec <= TOL[w.dtype]
+    assert torch.equal(out, out_plain) and torch.equal(st, st_plain)
+
+
 def test_forward_cfg2_full():
     """KDA bf16 prefill, B=1 H=32 T=8192 d=128 chunk=64, every head."""
     w = workloads.workload(2)

@@ -386,3 +386,36 @@ def test_gate_summary_ratios(oracle_lib):
             rec = np.where(zp[r] > i + 1, 0.0,
                            np.where((par[r] - par[i]) % 2 == 1, -1.0, 1.0) * np.exp2(L[r] - L[i]))
             assert np.allclose(rec, prod, rtol=1e-12, atol=0)
+
+
+def test_chunk_start_states_are_prefix_states(oracle_lib):
+    """Chunk-start states (the state entering each chunk of the chunkwise form):
+    entry 0 is the initial state exactly, and entry n equals the final state of
+    the same recurrence run on the first n*chunk tokens only; a recording
+    before/after the wrong token, in the wrong slot or for the wrong (b, h)
+    breaks the equality.  CKDA gates with exact zeros and -1, beta up to 2,
+    a ragged last chunk and B, H > 1."""
+    rng = np.random.default_rng(11)
+    B, T, H, Dk, Dv, chunk = 2, 29, 3, 8, 5, 8
+    q = rng.standard_normal((B, T, H, Dk)).astype(np.float32) * 0.5
+    k = rng.standard_normal((B, T, H, Dk)).astype(np.float32) * 0.5
+    v = rng.standard_normal((B, T, H, Dv)).astype(np.float32)
+    a = rng.uniform(-1, 1, (B, T, H, Dk)).astype(np.float32)
+    a[0, 3, 1, 2] = 0.0
+    a[1, 17, 0, 5] = -1.0
+    b = rng.uniform(0, 2, (B, T, H)).astype(np.float32)
+    S0 = rng.standard_normal((B, H, Dk, Dv)).astype(np.float32)
+    out, ST, CS = oracle_lib.forward(q, k, v, a, b, S0, chunk=chunk)
+    NC = (T + chunk - 1) // chunk
+    assert CS.shape == (B, H, NC, Dk, Dv)
+    assert np.array_equal(CS[:, :, 0], S0.astype(np.float64))
+    for n in range(1, NC):
+        t = n * chunk
+        _, S_pre = oracle_lib.forward(q[:, :t], k[:, :t], v[:, :t], a[:, :t], b[:, :t], S0)
+        assert np.array_equal(CS[:, :, n], S_pre), n
+    # the outputs and final state do not depend on whether states are recorded
+    out2, ST2 = oracle_lib.forward(q, k, v, a, b, S0)
+    assert np.array_equal(out, out2) and np.array_equal(ST, ST2)
+    # zero initial state: entry 0 is zero
+    _, _, CS0 = oracle_lib.forward(q, k, v, a, b, None, chunk=chunk)
+    assert not CS0[:, :, 0].any()
