@@ -19,7 +19,8 @@ import torch
 
 __all__ = [
     "KDA", "CKDA", "KdaError", "library_path", "load", "abi_version", "workspace_size",
-    "chunk_forward", "decode_step", "gate_prep", "last_stage_times", "STAGE_EVENTS",
+    "chunk_forward", "chunk_forward_prologue", "decode_step", "gate_prep", "last_stage_times",
+    "STAGE_EVENTS",
 ]
 
 KDA, CKDA = 0, 1
@@ -37,6 +38,13 @@ class KdaError(RuntimeError):
     def __init__(self, fn: str, status: int):
         self.status = status
         super().__init__(f"{fn} failed: status {status} ({_STATUS.get(status, 'unknown')})")
+
+
+class Prologue(ctypes.Structure):
+    """kda_prologue_t (include/kda.h)."""
+    _fields_ = [("alpha_min", ctypes.c_float), ("alpha_max", ctypes.c_float),
+                ("beta_max", ctypes.c_float), ("eps", ctypes.c_float),
+                ("normalize_q", ctypes.c_int)]
 
 
 def library_path() -> str:
@@ -62,6 +70,9 @@ def load():
     lib.kda_chunk_forward.restype = i
     lib.kda_chunk_forward_states.argtypes = [vp] * 9 + [i] * 8 + [u, vp, sz, vp]
     lib.kda_chunk_forward_states.restype = i
+    lib.kda_chunk_forward_prologue.argtypes = [vp] * 5 + [ctypes.POINTER(Prologue)] + [vp] * 3 + \
+        [i] * 8 + [u, vp, sz, vp]
+    lib.kda_chunk_forward_prologue.restype = i
     lib.kda_decode_step.argtypes = [vp] * 7 + [i] * 6 + [u, vp]
     lib.kda_decode_step.restype = i
     lib.kda_gate_prep.argtypes = [vp] * 4 + [i] * 5 + [vp]
@@ -147,6 +158,43 @@ def chunk_forward(q, k, v, alpha, beta, initial_state=None, *, chunk: int = 64, 
                                           _DT[q.dtype], mode, flags, _ptr(workspace), wsb,
                                           _stream(stream))
         _check("kda_chunk_forward_states", st)
+    return out, final_state
+
+
+def chunk_forward_prologue(q_raw, k_raw, v, gate, beta_logit, initial_state=None, *,
+                           alpha_min: float, alpha_max: float, beta_max: float,
+                           eps: float = 1e-6, normalize_q: bool = True, chunk: int = 64,
+                           mode: int = CKDA, out=None, final_state=None,
+                           output_final_state: bool = True, workspace=None, stream=None,
+                           flags: int = 0):
+    """Chunked forward from raw inputs (kda_chunk_forward_prologue): gate
+    [B,T,H,Dk] fp32 and beta_logit [B,T,H] fp32 logits, q_raw / k_raw
+    unnormalised; alpha = alpha_min + (alpha_max - alpha_min) sigmoid(gate),
+    beta = beta_max sigmoid(beta_logit), k = k_raw / (|k_raw| + eps) and q
+    likewise when normalize_q.  Returns (out, final_state)."""
+    lib = load()
+    B, T, H, Dk = q_raw.shape
+    Dv = v.shape[-1]
+    if out is None:
+        out = torch.empty((B, T, H, Dv), dtype=q_raw.dtype, device=q_raw.device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q_raw.device)
+    if workspace is None:
+        nbytes = workspace_size(B, T, H, Dk, Dv, chunk, q_raw.dtype)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q_raw.device)
+    _dev(q_raw, k_raw, v, gate, beta_logit, initial_state, out, final_state, workspace)
+    if q_raw.dtype not in _DT or k_raw.dtype != q_raw.dtype or v.dtype != q_raw.dtype or \
+            out.dtype != q_raw.dtype:
+        raise ValueError("q_raw, k_raw, v and out must share one dtype (float32 or bfloat16)")
+    pro = Prologue(alpha_min, alpha_max, beta_max, eps, int(bool(normalize_q)))
+    st = lib.kda_chunk_forward_prologue(_ptr(q_raw), _ptr(k_raw), _ptr(v), _ptr(gate),
+                                        _ptr(beta_logit), ctypes.byref(pro),
+                                        _ptr(initial_state), _ptr(out), _ptr(final_state),
+                                        B, T, H, Dk, Dv, chunk, _DT[q_raw.dtype], mode, flags,
+                                        _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(),
+                                        _stream(stream))
+    _check("kda_chunk_forward_prologue", st)
     return out, final_state
 
 

@@ -109,19 +109,31 @@ ChunkShape make_shape(int B, int T, int H, int Dk, int Dv, int chunk)
     return ChunkShape{B, T, H, Dk, Dv, chunk, (T + chunk - 1) / chunk};
 }
 
+// prologue parameters inside the mode's ranges (KDA: gates in [0, 1], beta in
+// [0, 1]; CKDA: gates in [-1, 1], beta in [0, 2]), finite, eps >= 0
+bool prologue_ok(const kda_prologue_t& p, kda_mode_t mode)
+{
+    const float lo = mode == KDA_MODE_CKDA ? -1.f : 0.f, bhi = mode == KDA_MODE_CKDA ? 2.f : 1.f;
+    return p.alpha_min >= lo && p.alpha_min <= p.alpha_max && p.alpha_max <= 1.f &&
+           p.beta_max >= 0.f && p.beta_max <= bhi && p.eps >= 0.f && p.eps < 1e30f &&
+           (p.normalize_q == 0 || p.normalize_q == 1);
+}
+
 // the chunked forward; chunk_states (may be null) receives the state entering
-// every chunk
+// every chunk; pro (may be null) makes alpha / beta logits and q, k raw
 kda_status_t chunk_forward(const void* q, const void* k, const void* v, const float* alpha,
                            const float* beta, const float* initial_state, void* out,
-                           float* final_state, void* chunk_states, int B, int T, int H, int Dk,
-                           int Dv, int chunk, kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
-                           void* workspace, size_t workspace_bytes, void* stream)
+                           float* final_state, void* chunk_states, const kda_prologue_t* pro,
+                           int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype_t dtype,
+                           kda_mode_t mode, unsigned flags, void* workspace,
+                           size_t workspace_bytes, void* stream)
 {
     kda_status_t st = check_forward_shape(B, T, H, Dk, Dv, chunk, dtype);
     if (st != KDA_OK) return st;
     if (mode != KDA_MODE_KDA && mode != KDA_MODE_CKDA) return KDA_ERR_UNSUPPORTED;
     if (flags & ~kKnownFlags) return KDA_ERR_UNSUPPORTED;
     if (T > 0 && (!q || !k || !v || !alpha || !beta || !out)) return KDA_ERR_NULL_POINTER;
+    if (pro && !prologue_ok(*pro, mode)) return KDA_ERR_UNSUPPORTED;
 
     const size_t e = elem_size(dtype);
     const size_t ntok = (size_t)B * T * H;
@@ -197,7 +209,13 @@ kda_status_t chunk_forward(const void* q, const void* k, const void* v, const fl
         while (zx > 0 && kda::prep_fast_lds_bytes(io, chunk, Dk, zx) > 160 * 1024) zx -= 16;
     }
     const kda::PrepArgs pa{q, k, v, alpha, beta, ws.W, ws.U, ws.Kt, ws.QG, ws.P, ws.GC, ws.FL,
-                           T, H, Dv, sh.NC, zx};
+                           T, H, Dv, sh.NC, zx,
+                           pro ? 1 : 0,
+                           pro ? pro->alpha_min : 0.f,
+                           pro ? pro->alpha_max - pro->alpha_min : 0.f,
+                           pro ? pro->beta_max : 0.f,
+                           pro ? pro->eps : 0.f,
+                           pro ? pro->normalize_q : 0};
     const kda::ChainArgs ca{ws.W, ws.U, ws.Kt, ws.QG, ws.P, ws.GC, initial_state, out,
                             final_state, chunk_states, B, T, H, Dv, sh.NC};
 
@@ -253,8 +271,23 @@ kda_status_t kda_chunk_forward(const void* q, const void* k, const void* v, cons
                                kda_dtype_t dtype, kda_mode_t mode, unsigned flags, void* workspace,
                                size_t workspace_bytes, void* stream)
 {
-    return chunk_forward(q, k, v, alpha, beta, initial_state, out, final_state, nullptr, B, T, H,
-                         Dk, Dv, chunk, dtype, mode, flags, workspace, workspace_bytes, stream);
+    return chunk_forward(q, k, v, alpha, beta, initial_state, out, final_state, nullptr, nullptr,
+                         B, T, H, Dk, Dv, chunk, dtype, mode, flags, workspace, workspace_bytes,
+                         stream);
+}
+
+kda_status_t kda_chunk_forward_prologue(const void* q_raw, const void* k_raw, const void* v,
+                                        const float* gate, const float* beta_logit,
+                                        const kda_prologue_t* prologue,
+                                        const float* initial_state, void* out, float* final_state,
+                                        int B, int T, int H, int Dk, int Dv, int chunk,
+                                        kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
+                                        void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!prologue) return KDA_ERR_NULL_POINTER;
+    return chunk_forward(q_raw, k_raw, v, gate, beta_logit, initial_state, out, final_state,
+                         nullptr, prologue, B, T, H, Dk, Dv, chunk, dtype, mode, flags, workspace,
+                         workspace_bytes, stream);
 }
 
 kda_status_t kda_chunk_forward_states(const void* q, const void* k, const void* v,
@@ -266,9 +299,9 @@ kda_status_t kda_chunk_forward_states(const void* q, const void* k, const void* 
                                       void* stream)
 {
     if (T > 0 && !chunk_states) return KDA_ERR_NULL_POINTER;
-    return chunk_forward(q, k, v, alpha, beta, initial_state, out, final_state, chunk_states, B,
-                         T, H, Dk, Dv, chunk, dtype, mode, flags, workspace, workspace_bytes,
-                         stream);
+    return chunk_forward(q, k, v, alpha, beta, initial_state, out, final_state, chunk_states,
+                         nullptr, B, T, H, Dk, Dv, chunk, dtype, mode, flags, workspace,
+                         workspace_bytes, stream);
 }
 
 kda_status_t kda_decode_step(const void* q, const void* k, const void* v, const float* alpha,

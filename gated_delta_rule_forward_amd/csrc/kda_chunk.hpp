@@ -168,7 +168,20 @@ struct PrepArgs {
     uint8_t* FL;
     int T, H, Dv, NC;
     int zx;   // extra (zero-segment) columns available to the fast prep kernel
+    // input parameterisation ("Semidirect Fourier Delta Attention" §3, eqs.
+    // (15), (17), (18)); when pro != 0, alpha holds gate logits, beta holds
+    // beta logits and q, k are raw:  alpha = amin + arange * sigmoid(gate),
+    // beta = bmax * sigmoid(logit), k = k / (|k| + eps), q likewise if normq
+    int pro;
+    float amin, arange, bmax, eps;
+    int normq;
 };
+
+// logistic function in fp32 (exp2 of the scaled argument; saturates to 0 / 1)
+__device__ __forceinline__ float sigmoid_f32(float x)
+{
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
+}
 
 struct ChainArgs {
     const void* W;

@@ -145,6 +145,27 @@ __global__ __launch_bounds__(kPrepThreads) void prep_exact_kernel(PrepArgs args,
             sBeta[r] = r < nvalid ? args.beta[((size_t)b * T_ + t0 + r) * H + h] : 0.f;
     }
     __syncthreads();
+    if (args.pro) {
+        // raw inputs: gate range eq. (15), beta eq. (17), unit-norm keys (and
+        // queries) eq. (18) ("Semidirect Fourier Delta Attention" §3), on the
+        // valid rows only (tail rows stay no-ops)
+        for (int idx = tid; idx < nvalid * DK; idx += kPrepThreads)
+            sAl[idx] = args.amin + args.arange * sigmoid_f32(sAl[idx]);
+        for (int r = tid; r < nvalid; r += kPrepThreads) sBeta[r] = args.bmax * sigmoid_f32(sBeta[r]);
+        for (int r = wave; r < nvalid; r += kPrepThreads / 64) {
+            for (int m = 0; m < (args.normq ? 2 : 1); ++m) {
+                T* row = (m == 0 ? sK : sQ) + r * DK;
+                float ss = 0.f;
+                for (int c = lane; c < DK; c += 64) ss += to_f32(row[c]) * to_f32(row[c]);
+#pragma unroll
+                for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+                const float nrm = __builtin_sqrtf(ss) + args.eps;
+                const float inv = nrm > 0.f ? 1.f / nrm : 0.f;
+                for (int c = lane; c < DK; c += 64) row[c] = from_f32<T>(to_f32(row[c]) * inv);
+            }
+        }
+        __syncthreads();
+    }
 
     // ---- phase 2: diagonal 16x16 blocks of A and P, one running product per
     //      (column i, channel): thread (i = tid/16, channel group tid%16) ----------

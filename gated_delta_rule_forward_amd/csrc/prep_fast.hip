@@ -100,10 +100,36 @@ __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(
 __device__ __forceinline__ float flog2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float frcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
+// sum over the NQ consecutive lanes that hold one token's channel quads
+template <int NQ>
+__device__ __forceinline__ float quad_group_sum(float x)
+{
+#pragma unroll
+    for (int off = NQ / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, NQ);
+    return x;
+}
+
+// x / (|x|_2 + eps) for one token whose Dk channels are spread as quads over NQ
+// consecutive lanes (a zero vector stays zero)
+template <typename T, int NQ>
+__device__ __forceinline__ Vec4<T> l2_normalised(const Vec4<T>& v, float eps)
+{
+    float f[4], ss = 0.f;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) { f[x] = v.get(x); ss += f[x] * f[x]; }
+    const float nrm = __builtin_sqrtf(quad_group_sum<NQ>(ss)) + eps;
+    const float inv = nrm > 0.f ? 1.f / nrm : 0.f;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) f[x] *= inv;
+    return Vec4<T>::from(f);
+}
+
 // ZS: the chunk may hold zero gates, placed in extra contraction columns (the
 // launch passes ZS = true exactly when extra columns are allotted); without
 // them a zero gate makes a part product vanish and flags the chunk.
-template <typename T, int C, int DK, bool ZS>
+// PRO: the inputs are raw (gate and beta logits, unnormalised q and k) and go
+// through the parameterisation first.
+template <typename T, int C, int DK, bool ZS, bool PRO>
 __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
 {
     using G = FastGeom<T, C, DK>;
@@ -166,6 +192,17 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
         qv[j] = Vec4<T>::load(gq + r * rs + c0);
         al[j][0] = a4.x; al[j][1] = a4.y; al[j][2] = a4.z; al[j][3] = a4.w;
         bt[j] = gb[r * H];
+    }
+    if constexpr (PRO) {
+        // eq. (15) gate range, eq. (17) beta, eq. (18) unit-norm keys (and queries)
+#pragma unroll
+        for (int j = 0; j < TOK; ++j) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) al[j][x] = args.amin + args.arange * sigmoid_f32(al[j][x]);
+            bt[j] = args.bmax * sigmoid_f32(bt[j]);
+            kv[j] = l2_normalised<T, G::NQ>(kv[j], args.eps);
+            if (args.normq) qv[j] = l2_normalised<T, G::NQ>(qv[j], args.eps);
+        }
     }
 #pragma unroll
     for (int j = 0; j < TOK; ++j) {
@@ -577,7 +614,8 @@ template <typename T, int C, int DK>
 hipError_t launch_fast_t(const ChunkShape& s, const PrepArgs& a, hipStream_t stream)
 {
     const FastLayout<T, C, DK> LY(a.zx);
-    auto kern = a.zx > 0 ? prep_fast_kernel<T, C, DK, true> : prep_fast_kernel<T, C, DK, false>;
+    auto kern = a.zx > 0 ? (a.pro ? prep_fast_kernel<T, C, DK, true, true> : prep_fast_kernel<T, C, DK, true, false>)
+                         : (a.pro ? prep_fast_kernel<T, C, DK, false, true> : prep_fast_kernel<T, C, DK, false, false>);
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              (int)LY.total);

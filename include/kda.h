@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 typedef enum {
     KDA_OK = 0,
@@ -141,6 +141,46 @@ kda_status_t kda_chunk_forward_states(const void* q, const void* k, const void* 
                                       kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
                                       void* workspace, size_t workspace_bytes,
                                       void* stream);
+
+/*
+ * Input parameterisation fused into the chunked forward ("Semidirect Fourier
+ * Delta Attention" §3, the stable parameterisation, eqs. (15), (17), (18)):
+ *   alpha = alpha_min + (alpha_max - alpha_min) * sigmoid(gate)        (15)
+ *   beta  = beta_max * sigmoid(beta_logit)                             (17)
+ *   k     = k_raw / (||k_raw||_2 + eps), over the Dk channels          (18)
+ *   q     = q_raw / (||q_raw||_2 + eps) when normalize_q, else q_raw
+ * computed in fp32 per token inside the kernels (a zero vector with eps = 0
+ * stays zero; normalised q, k are rounded to dtype once).  The parameters
+ * must lie in the mode's ranges: KDA 0 <= alpha_min <= alpha_max <= 1 and
+ * 0 <= beta_max <= 1; CKDA -1 <= alpha_min <= alpha_max <= 1 (the gate range
+ * of the "Complex KDA" abstract; alpha_min = -1, alpha_max = 1 gives
+ * 2 sigmoid - 1) and 0 <= beta_max <= 2; eps >= 0; normalize_q 0 or 1.
+ */
+typedef struct {
+    float alpha_min, alpha_max;
+    float beta_max;
+    float eps;
+    int normalize_q;
+} kda_prologue_t;
+
+/*
+ * kda_chunk_forward from raw inputs through the parameterisation above: gate
+ * takes alpha's place ([B,T,H,Dk] fp32 logits), beta_logit beta's ([B,T,H]
+ * fp32), q_raw and k_raw those of q and k.  Every other argument, rule and
+ * error is that of kda_chunk_forward; prologue == NULL is
+ * KDA_ERR_NULL_POINTER and parameters outside the mode's ranges are
+ * KDA_ERR_UNSUPPORTED.  Costs no extra pass over memory: the transforms run
+ * where the kernels load the inputs.
+ */
+kda_status_t kda_chunk_forward_prologue(const void* q_raw, const void* k_raw, const void* v,
+                                        const float* gate, const float* beta_logit,
+                                        const kda_prologue_t* prologue,
+                                        const float* initial_state, void* out,
+                                        float* final_state,
+                                        int B, int T, int H, int Dk, int Dv, int chunk,
+                                        kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
+                                        void* workspace, size_t workspace_bytes,
+                                        void* stream);
 
 /*
  * One single-token step for every (b, h), applied to a resident fp32 state in

@@ -52,6 +52,10 @@ def _load():
         lib.kda_oracle_forward.argtypes = [fp, fp, fp, fp, fp, fp, dp, dp, dp, i,
                                            i, i, i, i, i, i]
         lib.kda_oracle_forward.restype = i
+        d = ctypes.c_double
+        lib.kda_oracle_forward_prologue.argtypes = [fp, fp, fp, fp, fp, fp, d, d, d, d, i,
+                                                    dp, dp, i, i, i, i, i, i]
+        lib.kda_oracle_forward_prologue.restype = i
         lib.kda_oracle_decode.argtypes = [fp, fp, fp, fp, fp, dp, dp,
                                           i, i, i, i, i, i]
         lib.kda_oracle_decode.restype = i
@@ -108,6 +112,34 @@ def forward(q, k, v, alpha, beta, S0=None, nthreads: int | None = None, chunk: i
     if rc != 0:
         raise RuntimeError("kda_oracle_forward failed")
     return (out, ST) if chunk is None else (out, ST, CS)
+
+
+def forward_prologue(q_raw, k_raw, v, gate, beta_logit, S0=None, *, alpha_min: float,
+                     alpha_max: float, beta_max: float, eps: float, normalize_q: bool,
+                     nthreads: int | None = None):
+    """Forward from raw inputs through the stable parameterisation ("Semidirect
+    Fourier Delta Attention" §3, eqs. (15), (17), (18)), in float64:
+    alpha = alpha_min + (alpha_max - alpha_min) sigmoid(gate), beta = beta_max
+    sigmoid(beta_logit), k = k_raw / (|k_raw| + eps) and q likewise when
+    normalize_q.  Layouts as forward(); returns (out, ST) in float64."""
+    lib = _load()
+    q, k, v, g, c = (_f32(x) for x in (q_raw, k_raw, v, gate, beta_logit))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    assert k.shape == (B, T, H, Dk) and g.shape == (B, T, H, Dk)
+    assert v.shape == (B, T, H, Dv) and c.shape == (B, T, H)
+    s0 = None if S0 is None else _f32(S0)
+    out = np.empty((B, T, H, Dv), dtype=np.float64)
+    ST = np.empty((B, H, Dk, Dv), dtype=np.float64)
+    rc = lib.kda_oracle_forward_prologue(
+        _ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float),
+        _ptr(g, ctypes.c_float), _ptr(c, ctypes.c_float), _ptr(s0, ctypes.c_float),
+        float(alpha_min), float(alpha_max), float(beta_max), float(eps), int(bool(normalize_q)),
+        _ptr(out, ctypes.c_double), _ptr(ST, ctypes.c_double),
+        B, T, H, Dk, Dv, nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError("kda_oracle_forward_prologue failed")
+    return out, ST
 
 
 def decode(q, k, v, alpha, beta, S, nthreads: int | None = None):

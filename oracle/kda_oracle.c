@@ -32,30 +32,30 @@
  * matrix expression expanded by distributivity.  pred is Dv doubles of
  * scratch.  o may be NULL.
  */
-static void token_update(double* S, const float* q, const float* k,
-                         const float* v, const float* alpha, double beta,
+static void token_update(double* S, const double* q, const double* k,
+                         const double* v, const double* alpha, double beta,
                          double* o, int Dk, int Dv, double* pred)
 {
     for (int c = 0; c < Dk; ++c) {
-        const double a = (double)alpha[c];
+        const double a = alpha[c];
         double* row = S + (size_t)c * Dv;
         for (int j = 0; j < Dv; ++j) row[j] *= a;
     }
     for (int j = 0; j < Dv; ++j) pred[j] = 0.0;
     for (int c = 0; c < Dk; ++c) {
-        const double kc = (double)k[c];
+        const double kc = k[c];
         const double* row = S + (size_t)c * Dv;
         for (int j = 0; j < Dv; ++j) pred[j] += kc * row[j];
     }
     for (int c = 0; c < Dk; ++c) {
-        const double bk = beta * (double)k[c];
+        const double bk = beta * k[c];
         double* row = S + (size_t)c * Dv;
-        for (int j = 0; j < Dv; ++j) row[j] += bk * ((double)v[j] - pred[j]);
+        for (int j = 0; j < Dv; ++j) row[j] += bk * (v[j] - pred[j]);
     }
     if (o) {
         for (int j = 0; j < Dv; ++j) o[j] = 0.0;
         for (int c = 0; c < Dk; ++c) {
-            const double qc = (double)q[c];
+            const double qc = q[c];
             const double* row = S + (size_t)c * Dv;
             for (int j = 0; j < Dv; ++j) o[j] += qc * row[j];
         }
@@ -71,10 +71,60 @@ static void set_threads(int nthreads)
 #endif
 }
 
-int kda_oracle_forward(const float* q, const float* k, const float* v,
-                       const float* alpha, const float* beta, const float* S0,
-                       double* out, double* ST, double* CS, int chunk,
-                       int B, int T, int H, int Dk, int Dv, int nthreads)
+/* Logistic function, 1 / (1 + e^{-x}), written so that exp never overflows. */
+static double sigmoid(double x)
+{
+    if (x >= 0.0) return 1.0 / (1.0 + exp(-x));
+    const double e = exp(x);
+    return e / (1.0 + e);
+}
+
+/* Per-token input parameterisation, or NULL for inputs taken as given. */
+struct prologue {
+    double amin, amax, bmax, eps;
+    int normalize_q;
+};
+
+/*
+ * One token's inputs in double.  With a prologue ("Semidirect Fourier Delta
+ * Attention", §3, the stable parameterisation):
+ *   alpha = amin + (amax - amin) * sigmoid(a)          eq. (15)
+ *   beta  = bmax * sigmoid(c)                           eq. (17) (bmax = 1; 2 for
+ *                                                       the CKDA beta range)
+ *   k     = k_raw / (||k_raw||_2 + eps)                 eq. (18); q likewise
+ *                                                       when normalize_q
+ * A zero vector with eps = 0 stays zero (the quotient is read as 0).
+ */
+static double load_token(const struct prologue* pro, const float* q, const float* k,
+                         const float* v, const float* alpha, float beta, double* qd,
+                         double* kd, double* vd, double* ad, int Dk, int Dv)
+{
+    for (int c = 0; c < Dk; ++c) {
+        qd[c] = (double)q[c];
+        kd[c] = (double)k[c];
+        ad[c] = (double)alpha[c];
+    }
+    for (int j = 0; j < Dv; ++j) vd[j] = (double)v[j];
+    if (!pro) return (double)beta;
+    double nk = 0.0, nq = 0.0;
+    for (int c = 0; c < Dk; ++c) {
+        nk += kd[c] * kd[c];
+        nq += qd[c] * qd[c];
+    }
+    nk = sqrt(nk) + pro->eps;
+    nq = sqrt(nq) + pro->eps;
+    for (int c = 0; c < Dk; ++c) {
+        kd[c] = nk > 0.0 ? kd[c] / nk : 0.0;
+        if (pro->normalize_q) qd[c] = nq > 0.0 ? qd[c] / nq : 0.0;
+        ad[c] = pro->amin + (pro->amax - pro->amin) * sigmoid(ad[c]);
+    }
+    return pro->bmax * sigmoid((double)beta);
+}
+
+static int forward_impl(const struct prologue* pro, const float* q, const float* k,
+                        const float* v, const float* alpha, const float* beta,
+                        const float* S0, double* out, double* ST, double* CS, int chunk,
+                        int B, int T, int H, int Dk, int Dv, int nthreads)
 {
     if (!q || !k || !v || !alpha || !beta || !out) return -1;
     if (B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return -1;
@@ -87,13 +137,18 @@ int kda_oracle_forward(const float* q, const float* k, const float* v,
 #pragma omp parallel for schedule(dynamic, 1)
     for (long bh = 0; bh < nbh; ++bh) {
         const int b = (int)(bh / H), h = (int)(bh % H);
-        double* S = (double*)malloc(sizeof(double) * ((size_t)Dk * Dv + Dv));
+        const size_t nscr = (size_t)Dk * Dv + 2 * (size_t)Dv + 3 * (size_t)Dk;
+        double* S = (double*)malloc(sizeof(double) * nscr);
         if (!S) {
 #pragma omp atomic write
             failed = 1;
             continue;
         }
         double* pred = S + (size_t)Dk * Dv;
+        double* vd = pred + Dv;
+        double* qd = vd + Dv;
+        double* kd = qd + Dk;
+        double* ad = kd + Dk;
         if (S0) {
             const float* s0 = S0 + (size_t)bh * Dk * Dv;
             for (size_t e = 0; e < (size_t)Dk * Dv; ++e) S[e] = (double)s0[e];
@@ -105,14 +160,35 @@ int kda_oracle_forward(const float* q, const float* k, const float* v,
             if (CS && t % chunk == 0)
                 memcpy(CS + ((size_t)bh * nchunks + t / chunk) * Dk * Dv, S,
                        sizeof(double) * (size_t)Dk * Dv);
-            token_update(S, q + tok * Dk, k + tok * Dk, v + tok * Dv,
-                         alpha + tok * Dk, (double)beta[tok], out + tok * Dv,
-                         Dk, Dv, pred);
+            const double bt = load_token(pro, q + tok * Dk, k + tok * Dk, v + tok * Dv,
+                                         alpha + tok * Dk, beta[tok], qd, kd, vd, ad, Dk, Dv);
+            token_update(S, qd, kd, vd, ad, bt, out + tok * Dv, Dk, Dv, pred);
         }
         if (ST) memcpy(ST + (size_t)bh * Dk * Dv, S, sizeof(double) * (size_t)Dk * Dv);
         free(S);
     }
     return failed ? -1 : 0;
+}
+
+int kda_oracle_forward(const float* q, const float* k, const float* v,
+                       const float* alpha, const float* beta, const float* S0,
+                       double* out, double* ST, double* CS, int chunk,
+                       int B, int T, int H, int Dk, int Dv, int nthreads)
+{
+    return forward_impl(NULL, q, k, v, alpha, beta, S0, out, ST, CS, chunk, B, T, H, Dk, Dv,
+                        nthreads);
+}
+
+int kda_oracle_forward_prologue(const float* q_raw, const float* k_raw, const float* v,
+                                const float* gate, const float* beta_logit, const float* S0,
+                                double amin, double amax, double bmax, double eps,
+                                int normalize_q, double* out, double* ST,
+                                int B, int T, int H, int Dk, int Dv, int nthreads)
+{
+    if (!(eps >= 0.0)) return -1;
+    const struct prologue pro = {amin, amax, bmax, eps, normalize_q};
+    return forward_impl(&pro, q_raw, k_raw, v, gate, beta_logit, S0, out, ST, NULL, 0, B, T,
+                        H, Dk, Dv, nthreads);
 }
 
 int kda_oracle_decode(const float* q, const float* k, const float* v,
@@ -128,18 +204,22 @@ int kda_oracle_decode(const float* q, const float* k, const float* v,
 
 #pragma omp parallel for schedule(dynamic, 1)
     for (long bh = 0; bh < nbh; ++bh) {
-        double* pred = (double*)malloc(sizeof(double) * (size_t)Dv);
+        double* pred = (double*)malloc(sizeof(double) * (2 * (size_t)Dv + 3 * (size_t)Dk));
         if (!pred) {
 #pragma omp atomic write
             failed = 1;
             continue;
         }
+        double* vd = pred + Dv;
+        double* qd = vd + Dv;
+        double* kd = qd + Dk;
+        double* ad = kd + Dk;
         double* Sbh = S + (size_t)bh * Dk * Dv;
         for (int s = 0; s < nsteps; ++s) {
             const size_t tok = (size_t)s * nbh + bh;
-            token_update(Sbh, q + tok * Dk, k + tok * Dk, v + tok * Dv,
-                         alpha + tok * Dk, (double)beta[tok], out + tok * Dv,
-                         Dk, Dv, pred);
+            const double bt = load_token(NULL, q + tok * Dk, k + tok * Dk, v + tok * Dv,
+                                         alpha + tok * Dk, beta[tok], qd, kd, vd, ad, Dk, Dv);
+            token_update(Sbh, qd, kd, vd, ad, bt, out + tok * Dv, Dk, Dv, pred);
         }
         free(pred);
     }

@@ -43,6 +43,20 @@ int kda_oracle_forward(const float* q, const float* k, const float* v,
                        double* out, double* ST, double* CS, int chunk,
                        int B, int T, int H, int Dk, int Dv, int nthreads);
 
+/* The same forward from raw inputs through the stable parameterisation of
+ * "Semidirect Fourier Delta Attention" §3: per token, in double,
+ *   alpha = amin + (amax - amin) * sigmoid(gate)                eq. (15)
+ *   beta  = bmax * sigmoid(beta_logit)                           eq. (17)
+ *   k     = k_raw / (||k_raw||_2 + eps), and q likewise when normalize_q
+ *                                                                eq. (18)
+ * (a zero vector with eps = 0 stays zero).  gate has alpha's layout,
+ * beta_logit beta's.  eps < 0 or NaN is a bad argument. */
+int kda_oracle_forward_prologue(const float* q_raw, const float* k_raw, const float* v,
+                                const float* gate, const float* beta_logit, const float* S0,
+                                double amin, double amax, double bmax, double eps,
+                                int normalize_q, double* out, double* ST,
+                                int B, int T, int H, int Dk, int Dv, int nthreads);
+
 /* nsteps single-token updates applied to a resident double state in place.
  * Per-step inputs are stacked: q, k, alpha [nsteps, B, H, Dk],
  * v [nsteps, B, H, Dv], beta [nsteps, B, H]; out [nsteps, B, H, Dv];

@@ -32,14 +32,14 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     syms = declared_symbols()
-    assert {"kda_chunk_forward", "kda_chunk_forward_states", "kda_decode_step", "kda_chunk_forward_workspace_size",
+    assert {"kda_chunk_forward", "kda_chunk_forward_states", "kda_chunk_forward_prologue", "kda_decode_step", "kda_chunk_forward_workspace_size",
             "kda_gate_prep", "kda_status_string", "kda_abi_version"} <= set(syms)
     for s in syms:
         assert hasattr(lib, s), s
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 2
+    assert lib.kda_abi_version() == 3
     for s in range(8):
         assert lib.kda_status_string(s)
     assert lib.kda_status_string(99) == b"unknown status"
@@ -147,6 +147,28 @@ def test_forward_states_validation(lib):
     assert fwd_states(lib, ctypes.c_void_p(base.value), out=ctypes.c_void_p(base.value + 8188)) == ALIAS
     assert fwd_states(lib, ctypes.c_void_p(base.value + 64), ws=base) == ALIAS
     assert fwd_states(lib, f(), T=-1) == SHAPE
+
+
+def fwd_prologue(lib, pro, mode=1, **kw):
+    f = Fake()
+    B, T, H, Dk, Dv, C = 1, 64, 2, 16, 16, 16
+    st, need = ws_size(lib, B, T, H, Dk, Dv, C, F32)
+    p = None if pro is None else ctypes.byref(kda.Prologue(*pro))
+    return lib.kda_chunk_forward_prologue(f(), f(), f(), f(), f(), p, None, f(), None,
+                                          B, T, H, Dk, Dv, C, F32, mode, 0,
+                                          f(max(need, 1) + 4096), need, None)
+
+
+def test_forward_prologue_validation(lib):
+    assert fwd_prologue(lib, None) == NULLP
+    assert fwd_prologue(lib, (-1.5, 1.0, 1.0, 1e-6, 1)) == UNSUP       # gate below -1
+    assert fwd_prologue(lib, (0.5, 0.25, 1.0, 1e-6, 1)) == UNSUP       # alpha_min > alpha_max
+    assert fwd_prologue(lib, (0.0, 1.0, 2.5, 1e-6, 1)) == UNSUP        # beta above 2
+    assert fwd_prologue(lib, (0.0, 1.0, 1.0, -1.0, 1)) == UNSUP        # eps < 0
+    assert fwd_prologue(lib, (0.0, 1.0, 1.0, float("nan"), 1)) == UNSUP
+    assert fwd_prologue(lib, (0.0, 1.0, 1.0, 1e-6, 2)) == UNSUP        # normalize_q not 0/1
+    assert fwd_prologue(lib, (-1.0, 1.0, 1.0, 1e-6, 1), mode=0) == UNSUP   # KDA: gates >= 0
+    assert fwd_prologue(lib, (0.0, 1.0, 2.0, 1e-6, 1), mode=0) == UNSUP    # KDA: beta <= 1
 
 
 def test_decode_validation(lib):

@@ -115,6 +115,44 @@ def test_forward_chunk_states(name, base, ov):
     assert torch.equal(out, out_plain) and torch.equal(st, st_plain)
 
 
+# (name, base workload, overrides, (alpha_min, alpha_max, beta_max, eps, normalize_q), forget)
+PROLOGUE = [
+    ("f32_kda_d32_c32_T67", 0, dict(B=1, H=3, T=67, D=32, chunk=32), (0.0, 1.0, 1.0, 1e-6, 1), 0.0),
+    ("f32_ckda_d64_c64_T130_s0", 1, dict(B=2, H=1, T=130, D=64, chunk=64, s0_std=0.3),
+     (-1.0, 1.0, 2.0, 1e-6, 1), 0.0),
+    ("bf16_kda_d64_c16_T200_rawq", 2, dict(B=2, H=2, T=200, D=64, chunk=16),
+     (0.2, 0.99, 1.0, 1e-5, 0), 0.0),
+    ("bf16_ckda_d128_c64_T300_s0", 3, dict(B=1, H=2, T=300, chunk=64), (-1.0, 1.0, 2.0, 1e-6, 1), 0.0),
+    # KDA gates of exactly 0 (logit -200): their chunks go through the exact kernel
+    ("bf16_kda_d128_c64_T256_zero_gates", 2, dict(B=1, H=2, T=256, chunk=64),
+     (0.0, 1.0, 1.0, 1e-6, 1), 0.002),
+]
+
+
+@pytest.mark.parametrize("name,base,ov,pro,forget", PROLOGUE, ids=[c[0] for c in PROLOGUE])
+def test_forward_prologue(name, base, ov, pro, forget):
+    """kda_chunk_forward_prologue (gate range, beta and key / query
+    normalisation fused into the kernels) against the oracle's forward from
+    the same raw inputs."""
+    w = workloads.workload(base, **ov)
+    say(f"[forward prologue] {name}: {w} {pro}")
+    inp = workloads.make_prefill_raw(w, device="cpu", forget_frac=forget)
+    amin, amax, bmax, eps, nq = pro
+    o_ref, s_ref = oracle.forward_prologue(
+        np32(inp["q"]), np32(inp["k"]), np32(inp["v"]), np32(inp["gate"]),
+        np32(inp["beta_logit"]), None if inp["S0"] is None else np32(inp["S0"]),
+        alpha_min=amin, alpha_max=amax, beta_max=bmax, eps=eps, normalize_q=bool(nq),
+        nthreads=oracle_threads())
+    d = to_dev(inp)
+    out, st = kda.chunk_forward_prologue(d["q"], d["k"], d["v"], d["gate"], d["beta_logit"],
+                                         d["S0"], alpha_min=amin, alpha_max=amax, beta_max=bmax,
+                                         eps=eps, normalize_q=bool(nq), chunk=w.chunk, mode=w.mode)
+    torch.cuda.synchronize()
+    eo, es = slice_err_out(np32(out), o_ref), slice_err_state(np32(st), s_ref)
+    say(f"  err out {eo:.3e} state {es:.3e}")
+    assert eo <= TOL[w.dtype] and es <= TOL[w.dtype]
+
+
 def test_forward_cfg2_full():
     """KDA bf16 prefill, B=1 H=32 T=8192 d=128 chunk=64, every head."""
     w = workloads.workload(2)

@@ -419,3 +419,82 @@ def test_chunk_start_states_are_prefix_states(oracle_lib):
     # zero initial state: entry 0 is zero
     _, _, CS0 = oracle_lib.forward(q, k, v, a, b, None, chunk=chunk)
     assert not CS0[:, :, 0].any()
+
+
+def _raw_inputs(seed, B=1, T=23, H=2, Dk=8, Dv=5, unit=False):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, T, H, Dk)).astype(np.float32) * 1.7
+    k = rng.standard_normal((B, T, H, Dk)).astype(np.float32) * 0.6
+    if unit:
+        q = (q / np.linalg.norm(q.astype(np.float64), axis=-1, keepdims=True)).astype(np.float32)
+        k = (k / np.linalg.norm(k.astype(np.float64), axis=-1, keepdims=True)).astype(np.float32)
+    v = rng.standard_normal((B, T, H, Dv)).astype(np.float32)
+    g = (rng.standard_normal((B, T, H, Dk)) * 2).astype(np.float32)
+    c = rng.standard_normal((B, T, H)).astype(np.float32)
+    S0 = (rng.standard_normal((B, H, Dk, Dv)) * 0.3).astype(np.float32)
+    return q, k, v, g, c, S0
+
+
+def test_prologue_degenerate_gate_range_and_zero_logit_beta(oracle_lib):
+    """Eq. (15) with alpha_min = alpha_max = 0.75 gives alpha = 0.75 for any
+    logit; eq. (17) at logit 0 gives beta = beta_max / 2 = 1; unit-norm q, k
+    pass eq. (18) unchanged (eps = 0).  Must equal the plain recurrence with
+    those constants."""
+    q, k, v, g, c, S0 = _raw_inputs(3, unit=True)
+    c[:] = 0.0
+    o, s = oracle_lib.forward_prologue(q, k, v, g, c, S0, alpha_min=0.75, alpha_max=0.75,
+                                       beta_max=2.0, eps=0.0, normalize_q=True)
+    o_ref, s_ref = oracle_lib.forward(q, k, v, np.full_like(g, 0.75), np.ones_like(c), S0)
+    assert np.abs(o - o_ref).max() < 1e-6 and np.abs(s - s_ref).max() < 1e-6
+
+
+def test_prologue_gate_midpoint_forgets(oracle_lib):
+    """Gate logits 0 with the CKDA range [-1, 1] give alpha = 0 exactly (the
+    midpoint of eq. (15)), so every token forgets the state: S_t = beta k v^T
+    and o_t = beta (q.k) v_t with the normalised q, k, i.e. beta times the
+    cosine similarity of the raw vectors (eps = 0, beta logit 0, beta_max 2
+    -> beta = 1)."""
+    q, k, v, g, c, S0 = _raw_inputs(4)
+    g[:] = 0.0
+    c[:] = 0.0
+    o, s = oracle_lib.forward_prologue(q, k, v, g, c, S0, alpha_min=-1.0, alpha_max=1.0,
+                                       beta_max=2.0, eps=0.0, normalize_q=True)
+    q64, k64 = q.astype(np.float64), k.astype(np.float64)
+    cos = (q64 * k64).sum(-1) / (np.linalg.norm(q64, axis=-1) * np.linalg.norm(k64, axis=-1))
+    assert np.abs(o - cos[..., None] * v).max() < 1e-12
+    kn = k64[:, -1] / np.linalg.norm(k64[:, -1], axis=-1, keepdims=True)
+    assert np.abs(s - kn[..., :, None] * v[:, -1][..., None, :]).max() < 1e-12
+
+
+def test_prologue_scale_invariance(oracle_lib):
+    """Eq. (18) with eps = 0 makes the result independent of the scale of k_raw
+    (and of q_raw when q is normalised); without q normalisation the output
+    scales with q_raw."""
+    q, k, v, g, c, S0 = _raw_inputs(5)
+    kw = dict(alpha_min=0.0, alpha_max=1.0, beta_max=1.0, eps=0.0)
+    o1, s1 = oracle_lib.forward_prologue(q, k, v, g, c, S0, normalize_q=True, **kw)
+    o2, s2 = oracle_lib.forward_prologue(q * 0.25, k * 4.0, v, g, c, S0, normalize_q=True, **kw)
+    assert np.abs(o1 - o2).max() < 1e-12 and np.abs(s1 - s2).max() < 1e-12
+    o3, _ = oracle_lib.forward_prologue(q, k, v, g, c, S0, normalize_q=False, **kw)
+    o4, _ = oracle_lib.forward_prologue(q * 0.25, k * 4.0, v, g, c, S0, normalize_q=False, **kw)
+    assert np.abs(o4 - 0.25 * o3).max() < 1e-12
+    assert np.abs(o3 - o1).max() > 1e-3          # q normalisation does something here
+
+
+def test_prologue_gate_symmetry_and_limits(oracle_lib):
+    """sigmoid(-x) = 1 - sigmoid(x): eq. (15) with the range reversed and the
+    logits negated gives the same gates; logits of +-40 reach the range ends
+    (alpha = alpha_max, or alpha_min) to double precision."""
+    q, k, v, g, c, S0 = _raw_inputs(6)
+    kw = dict(beta_max=2.0, eps=1e-3, normalize_q=True)
+    o1, s1 = oracle_lib.forward_prologue(q, k, v, g, c, S0, alpha_min=-0.5, alpha_max=0.9, **kw)
+    o2, s2 = oracle_lib.forward_prologue(q, k, v, -g, c, S0, alpha_min=0.9, alpha_max=-0.5, **kw)
+    assert np.abs(o1 - o2).max() < 1e-12 and np.abs(s1 - s2).max() < 1e-12
+    # limits: the same run with gate logits +40 and with alpha fixed at the range end
+    hi = np.full_like(g, 40.0)
+    o_hi, _ = oracle_lib.forward_prologue(q, k, v, hi, c, S0, alpha_min=-0.5, alpha_max=0.9, **kw)
+    o_end, _ = oracle_lib.forward_prologue(q, k, v, g, c, S0, alpha_min=0.9, alpha_max=0.9, **kw)
+    assert np.abs(o_hi - o_end).max() < 1e-12
+    o_lo, _ = oracle_lib.forward_prologue(q, k, v, -hi, c, S0, alpha_min=-0.5, alpha_max=0.9, **kw)
+    o_end2, _ = oracle_lib.forward_prologue(q, k, v, g, c, S0, alpha_min=-0.5, alpha_max=-0.5, **kw)
+    assert np.abs(o_lo - o_end2).max() < 1e-12

@@ -127,6 +127,32 @@ def make_prefill(w: Workload, device="cpu", seed: int | None = None):
             "alpha": alpha, "beta": beta, "S0": S0}
 
 
+def make_prefill_raw(w: Workload, device="cpu", seed: int | None = None, gate_std: float = 2.0,
+                     forget_frac: float = 0.0):
+    """Raw inputs for the forward with the fused input parameterisation: q, k
+    N(0,1) per element (not normalised) and v N(0,1), all rounded to w.dtype;
+    gate logits N(0, gate_std^2) fp32 [B,T,H,D], with a fraction forget_frac
+    of them set to -200 (a gate of 0 after any range-sigmoid with alpha_min =
+    0); beta logits N(0,1) fp32 [B,T,H]; S0 as in make_prefill."""
+    g = _gen(w.seed if seed is None else seed, device)
+    B, T, H, D = w.B, w.T, w.H, w.D
+    f32 = torch.float32
+    q = torch.randn((B, T, H, D), generator=g, device=device, dtype=f32).to(w.dtype)
+    k = torch.randn((B, T, H, D), generator=g, device=device, dtype=f32).to(w.dtype)
+    v = torch.randn((B, T, H, D), generator=g, device=device, dtype=f32).to(w.dtype)
+    gate = gate_std * torch.randn((B, T, H, D), generator=g, device=device, dtype=f32)
+    if forget_frac > 0:
+        u = torch.rand((B, T, H, D), generator=g, device=device)
+        gate = torch.where(u < forget_frac, torch.full_like(gate, -200.0), gate)
+    blog = torch.randn((B, T, H), generator=g, device=device, dtype=f32)
+    S0 = None
+    if w.s0_std is not None:
+        S0 = (w.s0_std * torch.randn((B, H, D, D), generator=g, device=device,
+                                     dtype=f32)).contiguous()
+    return {"q": q.contiguous(), "k": k.contiguous(), "v": v.contiguous(),
+            "gate": gate.contiguous(), "beta_logit": blog.contiguous(), "S0": S0}
+
+
 def make_decode(w: Workload, steps: int | None = None, device="cpu", seed: int | None = None):
     """Inputs for stacked decode steps: S0 [B,H,D,D] fp32, then per step
     q, k, v [N,B,H,D] (w.dtype), alpha [N,B,H,D] fp32, beta [N,B,H] fp32."""
