@@ -19,7 +19,7 @@ import torch
 
 __all__ = [
     "KDA", "CKDA", "KdaError", "library_path", "load", "abi_version", "workspace_size",
-    "chunk_forward", "chunk_forward_prologue", "decode_step", "gate_prep", "last_stage_times",
+    "chunk_forward", "chunk_forward_prologue", "chunk_forward_varlen", "decode_step", "gate_prep", "last_stage_times",
     "STAGE_EVENTS",
 ]
 
@@ -73,6 +73,11 @@ def load():
     lib.kda_chunk_forward_prologue.argtypes = [vp] * 5 + [ctypes.POINTER(Prologue)] + [vp] * 3 + \
         [i] * 8 + [u, vp, sz, vp]
     lib.kda_chunk_forward_prologue.restype = i
+    lib.kda_chunk_forward_varlen_workspace_size.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(sz)]
+    lib.kda_chunk_forward_varlen_workspace_size.restype = i
+    lib.kda_chunk_forward_varlen.argtypes = [vp] * 5 + [ctypes.POINTER(Prologue), vp, i, vp, vp,
+                                                         vp] + [i] * 7 + [u, vp, sz, vp]
+    lib.kda_chunk_forward_varlen.restype = i
     lib.kda_decode_step.argtypes = [vp] * 7 + [i] * 6 + [u, vp]
     lib.kda_decode_step.restype = i
     lib.kda_gate_prep.argtypes = [vp] * 4 + [i] * 5 + [vp]
@@ -195,6 +200,49 @@ def chunk_forward_prologue(q_raw, k_raw, v, gate, beta_logit, initial_state=None
                                         workspace.numel() * workspace.element_size(),
                                         _stream(stream))
     _check("kda_chunk_forward_prologue", st)
+    return out, final_state
+
+
+def chunk_forward_varlen(q, k, v, alpha, beta, cu_seqlens, initial_state=None, *,
+                         chunk: int = 64, mode: int = CKDA, prologue: dict | None = None,
+                         out=None, final_state=None, output_final_state: bool = True,
+                         workspace=None, stream=None, flags: int = 0):
+    """Packed batch (kda_chunk_forward_varlen): q, k, alpha [total_T,H,Dk]
+    (or [1,total_T,H,Dk]); v [.., total_T,H,Dv]; beta [.., total_T,H];
+    cu_seqlens int32 [N+1] on the GPU; initial_state [N,H,Dk,Dv] fp32 or
+    None.  prologue: None or dict(alpha_min=, alpha_max=, beta_max=, eps=,
+    normalize_q=) (alpha, beta are then logits).  Returns (out shaped like v,
+    final_state [N,H,Dk,Dv] or None)."""
+    lib = load()
+    H, Dk = q.shape[-2], q.shape[-1]
+    total_T = q.shape[-3]
+    Dv = v.shape[-1]
+    N = cu_seqlens.numel() - 1
+    if cu_seqlens.dtype != torch.int32 or N < 1:
+        raise ValueError("cu_seqlens must be an int32 tensor of N + 1 offsets, N >= 1")
+    if out is None:
+        out = torch.empty(v.shape, dtype=q.dtype, device=q.device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        n = ctypes.c_size_t(0)
+        _check("kda_chunk_forward_varlen_workspace_size",
+               lib.kda_chunk_forward_varlen_workspace_size(N, total_T, H, Dk, Dv, chunk,
+                                                           _DT[q.dtype], ctypes.byref(n)))
+        workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=q.device)
+    _dev(q, k, v, alpha, beta, cu_seqlens, initial_state, out, final_state, workspace)
+    if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype or out.dtype != q.dtype:
+        raise ValueError("q, k, v and out must share one dtype (float32 or bfloat16)")
+    pro = None if prologue is None else ctypes.byref(Prologue(
+        prologue["alpha_min"], prologue["alpha_max"], prologue["beta_max"],
+        prologue.get("eps", 1e-6), int(bool(prologue.get("normalize_q", True)))))
+    st = lib.kda_chunk_forward_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), pro,
+                                      _ptr(cu_seqlens), N, _ptr(initial_state), _ptr(out),
+                                      _ptr(final_state), total_T, H, Dk, Dv, chunk, _DT[q.dtype],
+                                      mode, flags, _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(),
+                                      _stream(stream))
+    _check("kda_chunk_forward_varlen", st)
     return out, final_state
 
 

@@ -253,12 +253,15 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
     F* sSf = reinterpret_cast<F*>(stages + G::XCH);
     F* sDf = sSf + G::NKD * 64;
 
-    const int Dv = a.Dv, H = a.H, T_ = a.T, NC = a.NC;
+    const int Dv = a.Dv, H = a.H;
     const int NS = Dv / 16;
     const int g = blockIdx.x, xcd = g % kXcds, jx = g / kXcds;
     const int bh = (jx / NS) * kXcds + xcd, slice = jx % NS;
     if (bh >= a.B * H) return;
-    const int b = bh / H, h = bh % H;
+    const int h = bh % H;
+    // this (sequence, head): chunk count, first token row, length, first unit
+    const SeqPos sp = locate_seq(bh, H, a.T, a.NC, a.cu, a.cs);
+    const int NC = sp.nc, T_ = sp.len;
     const int tid = threadIdx.x, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = slice * 16 + ln;
@@ -271,8 +274,25 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
     // of step c - 1, and stage c & 1 is free again after barrier 2 of step
     // c - 1.  Past the last chunk the last one is re-read, so every step
     // issues the same NDMA loads per loader.
-    const size_t u0 = (size_t)bh * NC;
+    const size_t u0 = sp.ubase;
     const int last = NC - 1;
+    if (NC == 0) {
+        // an empty sequence of a packed batch: the state passes through
+        if (a.ST && wave < kChainWaves) {
+#pragma unroll
+            for (int u = 0; u < G::SPW; ++u) {
+                const int t = wave + 4 * u;
+                if (t < G::NT) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const size_t e = ((size_t)bh * DK + 16 * t + 4 * lg + i) * Dv + col;
+                        a.ST[e] = a.S0 ? a.S0[e] : 0.f;
+                    }
+                }
+            }
+        }
+        return;
+    }
     const int cw = wave & (kChainWaves - 1);     // the compute wave a loader serves
     auto stg = [&](int c) { return stages + (size_t)((c & 1) * kChainWaves + cw) * G::STAGE; };
     if (wave >= kChainWaves) {
@@ -322,7 +342,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
 
     T* out = static_cast<T*>(a.out);
     const size_t ostride = (size_t)H * Dv;                      // one token
-    T* obase = out + (((size_t)b * T_ + 16 * wave + 4 * lg) * H + h) * Dv + col;
+    T* obase = out + (((size_t)sp.row0 + 16 * wave + 4 * lg) * H + h) * Dv + col;
     // outputs of chunk n: O = (Q * Gamma) S_n + P Delta_n (off the state's
     // critical path, so computed during the next chunk's first phase)
     F pqg[G::NKD], pp[G::NKC], psf[G::NKD], pdf[G::NKC];

@@ -14,7 +14,67 @@ __global__ void state_copy_kernel(const float* __restrict__ src, float* __restri
     if (i < n) dst[i] = src ? src[i] : 0.f;
 }
 
+// Sanitised tables of a packed batch (one workgroup of 256 threads):
+//   cu_s[0] = 0, cu_s[i] = max(cu_s[i-1], clamp(cu[i], 0, total_T))
+//   cs[0] = 0,  cs[i+1] = min(cs[i] + ceil((cu_s[i+1] - cu_s[i]) / C), umax)
+// so the kernels index inside the inputs whatever cu holds.
+__global__ __launch_bounds__(256) void varlen_table_kernel(const int* __restrict__ cu, int N,
+                                                           int total_T, int C, int umax,
+                                                           int* __restrict__ cu_s,
+                                                           int* __restrict__ cs)
+{
+    __shared__ int sv[256];
+    __shared__ int carry;
+    const int tid = threadIdx.x;
+    if (tid == 0) carry = 0;
+    __syncthreads();
+    for (int base = 0; base <= N; base += 256) {             // running maximum
+        const int i = base + tid;
+        int x = 0;
+        if (i <= N && i > 0) x = min(max(cu[i], 0), total_T);
+        sv[tid] = x;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {
+            const int y = tid >= off ? sv[tid - off] : 0;
+            __syncthreads();
+            sv[tid] = max(sv[tid], y);
+            __syncthreads();
+        }
+        const int m = max(sv[tid], carry);
+        if (i <= N) cu_s[i] = m;
+        __syncthreads();
+        if (tid == 255) carry = m;
+        __syncthreads();
+    }
+    if (tid == 0) { carry = 0; cs[0] = 0; }
+    __syncthreads();
+    for (int base = 0; base < N; base += 256) {              // chunk prefix
+        const int i = base + tid;
+        const int x = i < N ? (cu_s[i + 1] - cu_s[i] + C - 1) / C : 0;
+        sv[tid] = x;
+        __syncthreads();
+        for (int off = 1; off < 256; off <<= 1) {
+            const int y = tid >= off ? sv[tid - off] : 0;
+            __syncthreads();
+            sv[tid] += y;
+            __syncthreads();
+        }
+        const int c = carry + sv[tid];
+        if (i < N) cs[i + 1] = min(c, umax);
+        __syncthreads();
+        if (tid == 255) carry = c;
+        __syncthreads();
+    }
+}
+
 }  // namespace
+
+hipError_t launch_varlen_table(const int* cu, int N, int total_T, int C, int umax, int* cu_s,
+                               int* cs, hipStream_t stream)
+{
+    return launch_kernel(varlen_table_kernel, dim3(1), dim3(256), 0, stream, cu, N, total_T, C,
+                         umax, cu_s, cs);
+}
 
 size_t chunk_workspace_layout(const ChunkShape& s, IoType io, size_t off[kWorkspaceRegions])
 {

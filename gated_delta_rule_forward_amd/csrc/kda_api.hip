@@ -215,9 +215,10 @@ kda_status_t chunk_forward(const void* q, const void* k, const void* v, const fl
                            pro ? pro->alpha_max - pro->alpha_min : 0.f,
                            pro ? pro->beta_max : 0.f,
                            pro ? pro->eps : 0.f,
-                           pro ? pro->normalize_q : 0};
+                           pro ? pro->normalize_q : 0,
+                           nullptr, nullptr, 0};
     const kda::ChainArgs ca{ws.W, ws.U, ws.Kt, ws.QG, ws.P, ws.GC, initial_state, out,
-                            final_state, chunk_states, B, T, H, Dv, sh.NC};
+                            final_state, chunk_states, B, T, H, Dv, sh.NC, nullptr, nullptr};
 
     if (rec.mark("prep_fast") != hipSuccess) return KDA_ERR_HIP;
     if (kda::launch_prep_fast(io, sh, pa, s) != hipSuccess) return KDA_ERR_HIP;
@@ -229,6 +230,35 @@ kda_status_t chunk_forward(const void* q, const void* k, const void* v, const fl
     if (kda::launch_chain(io, sh, ca, s) != hipSuccess) return KDA_ERR_HIP;
     if (rec.done() != hipSuccess) return KDA_ERR_HIP;
     return KDA_OK;
+}
+
+// packed batches: an upper bound of the chunk count (each sequence adds at most
+// one partial chunk), the shape the prep kernels and the workspace use
+// (B = 1, NC = that bound), and the tables after the per-unit regions
+long long varlen_max_chunks(int N, int total_T, int chunk)
+{
+    return ((long long)total_T + chunk - 1) / chunk + N;
+}
+
+kda_status_t check_varlen_shape(int N, int total_T, int H, int Dk, int Dv, int chunk,
+                                kda_dtype_t dtype)
+{
+    if (N < 1 || N > (1 << 24) || total_T < 0 || H < 1) return KDA_ERR_BAD_SHAPE;
+    const kda_status_t st = check_forward_shape(1, total_T, H, Dk, Dv, chunk, dtype);
+    if (st != KDA_OK) return st;
+    const long long umax = varlen_max_chunks(N, total_T, chunk);
+    if (umax * H > 0x7fffffffLL || (long long)N * H * (Dv / 16) > 0x7fffffffLL) return KDA_ERR_BAD_SHAPE;
+    return KDA_OK;
+}
+
+size_t varlen_layout(int N, int total_T, int H, int Dk, int Dv, int chunk, IoType io,
+                     size_t off[kda::kWorkspaceRegions], size_t* table_off)
+{
+    const int umax = (int)varlen_max_chunks(N, total_T, chunk);
+    const size_t units = kda::chunk_workspace_layout(ChunkShape{1, total_T, H, Dk, Dv, chunk, umax},
+                                                     io, off);
+    *table_off = units;
+    return units + ((2 * ((size_t)N + 1) * sizeof(int) + 255) & ~size_t(255));
 }
 
 }  // namespace
@@ -302,6 +332,119 @@ kda_status_t kda_chunk_forward_states(const void* q, const void* k, const void* 
     return chunk_forward(q, k, v, alpha, beta, initial_state, out, final_state, chunk_states,
                          nullptr, B, T, H, Dk, Dv, chunk, dtype, mode, flags, workspace,
                          workspace_bytes, stream);
+}
+
+kda_status_t kda_chunk_forward_varlen_workspace_size(int N, int total_T, int H, int Dk, int Dv,
+                                                     int chunk, kda_dtype_t dtype, size_t* bytes)
+{
+    if (!bytes) return KDA_ERR_NULL_POINTER;
+    const kda_status_t st = check_varlen_shape(N, total_T, H, Dk, Dv, chunk, dtype);
+    if (st != KDA_OK) return st;
+    size_t off[kda::kWorkspaceRegions], toff;
+    *bytes = varlen_layout(N, total_T, H, Dk, Dv, chunk,
+                           dtype == KDA_DTYPE_F32 ? IoType::F32 : IoType::BF16, off, &toff);
+    return KDA_OK;
+}
+
+kda_status_t kda_chunk_forward_varlen(const void* q, const void* k, const void* v,
+                                      const float* alpha, const float* beta,
+                                      const kda_prologue_t* prologue, const int* cu_seqlens,
+                                      int N, const float* initial_state, void* out,
+                                      float* final_state, int total_T, int H, int Dk, int Dv,
+                                      int chunk, kda_dtype_t dtype, kda_mode_t mode,
+                                      unsigned flags, void* workspace, size_t workspace_bytes,
+                                      void* stream)
+{
+    kda_status_t st = check_varlen_shape(N, total_T, H, Dk, Dv, chunk, dtype);
+    if (st != KDA_OK) return st;
+    if (mode != KDA_MODE_KDA && mode != KDA_MODE_CKDA) return KDA_ERR_UNSUPPORTED;
+    if (flags & ~kKnownFlags) return KDA_ERR_UNSUPPORTED;
+    if (prologue && !prologue_ok(*prologue, mode)) return KDA_ERR_UNSUPPORTED;
+    if (!cu_seqlens || !workspace || !out) return KDA_ERR_NULL_POINTER;
+    if (total_T > 0 && (!q || !k || !v || !alpha || !beta)) return KDA_ERR_NULL_POINTER;
+
+    const IoType io = dtype == KDA_DTYPE_F32 ? IoType::F32 : IoType::BF16;
+    const size_t e = elem_size(dtype);
+    const size_t ntok = (size_t)total_T * H;
+    const size_t nstate = (size_t)N * H * Dk * Dv * 4;
+    size_t off[kda::kWorkspaceRegions], toff;
+    const size_t ws_need = varlen_layout(N, total_T, H, Dk, Dv, chunk, io, off, &toff);
+    if (workspace_bytes < ws_need) return KDA_ERR_WORKSPACE_TOO_SMALL;
+
+    const void* vec[] = {q, k, alpha, workspace};
+    for (const void* p : vec)
+        if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
+    const void* elt[] = {v, out, beta, initial_state, final_state, cu_seqlens};
+    const uintptr_t ea[] = {e, e, 4, 4, 4, 4};
+    for (int i = 0; i < 6; ++i)
+        if (elt[i] && !aligned(elt[i], ea[i])) return KDA_ERR_MISALIGNED;
+
+    struct R { const void* p; size_t n; } in[] = {
+        {q, ntok * Dk * e}, {k, ntok * Dk * e}, {v, ntok * Dv * e},
+        {alpha, ntok * Dk * 4}, {beta, ntok * 4}, {initial_state, initial_state ? nstate : 0},
+        {cu_seqlens, ((size_t)N + 1) * 4}};
+    const R outs[] = {{out, ntok * Dv * e}, {workspace, ws_need}};
+    for (const R& o : outs)
+        for (const R& i : in)
+            if (overlaps(o.p, o.n, i.p, i.n)) return KDA_ERR_ALIAS;
+    if (overlaps(out, ntok * Dv * e, workspace, ws_need)) return KDA_ERR_ALIAS;
+    if (final_state) {
+        const R fs{final_state, nstate};
+        for (const R& i : in) {
+            if (i.p == initial_state && final_state == initial_state) continue;
+            if (overlaps(fs.p, fs.n, i.p, i.n)) return KDA_ERR_ALIAS;
+        }
+        for (const R& o : outs)
+            if (overlaps(fs.p, fs.n, o.p, o.n)) return KDA_ERR_ALIAS;
+    }
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    std::unique_lock<std::mutex> lock(g_stage.mu, std::defer_lock);
+    Recorder rec{(flags & KDA_FLAG_STAGE_EVENTS) != 0, s};
+    if (rec.on) {
+        lock.lock();
+        if (stage_begin() != hipSuccess) return KDA_ERR_HIP;
+    }
+    const int umax = (int)varlen_max_chunks(N, total_T, chunk);
+    unsigned char* w = static_cast<unsigned char*>(workspace);
+    int* cu_s = reinterpret_cast<int*>(w + toff);
+    int* cs = cu_s + (N + 1);
+    if (rec.mark("varlen_table") != hipSuccess) return KDA_ERR_HIP;
+    if (kda::launch_varlen_table(cu_seqlens, N, total_T, chunk, umax, cu_s, cs, s) != hipSuccess)
+        return KDA_ERR_HIP;
+    if (rec.done() != hipSuccess) return KDA_ERR_HIP;
+
+    const ChunkShape shp{1, total_T, H, Dk, Dv, chunk, umax};      // prep: all units
+    const ChunkShape shc{N, total_T, H, Dk, Dv, chunk, umax};      // chain: N x H chains
+    const ChunkWorkspace ws{w + off[0], w + off[1], w + off[2],
+                            w + off[3], w + off[4], reinterpret_cast<float*>(w + off[5]),
+                            w + off[6]};
+    int zx = 0;
+    if (mode == KDA_MODE_CKDA) {
+        zx = 128;
+        while (zx > 0 && kda::prep_fast_lds_bytes(io, chunk, Dk, zx) > 160 * 1024) zx -= 16;
+    }
+    const kda::PrepArgs pa{q, k, v, alpha, beta, ws.W, ws.U, ws.Kt, ws.QG, ws.P, ws.GC, ws.FL,
+                           total_T, H, Dv, umax, zx,
+                           prologue ? 1 : 0,
+                           prologue ? prologue->alpha_min : 0.f,
+                           prologue ? prologue->alpha_max - prologue->alpha_min : 0.f,
+                           prologue ? prologue->beta_max : 0.f,
+                           prologue ? prologue->eps : 0.f,
+                           prologue ? prologue->normalize_q : 0,
+                           cu_s, cs, N};
+    const kda::ChainArgs ca{ws.W, ws.U, ws.Kt, ws.QG, ws.P, ws.GC, initial_state, out,
+                            final_state, nullptr, N, total_T, H, Dv, umax, cu_s, cs};
+    if (rec.mark("prep_fast") != hipSuccess) return KDA_ERR_HIP;
+    if (kda::launch_prep_fast(io, shp, pa, s) != hipSuccess) return KDA_ERR_HIP;
+    if (rec.done() != hipSuccess) return KDA_ERR_HIP;
+    if (rec.mark("prep_exact") != hipSuccess) return KDA_ERR_HIP;
+    if (kda::launch_prep_exact(io, shp, pa, s) != hipSuccess) return KDA_ERR_HIP;
+    if (rec.done() != hipSuccess) return KDA_ERR_HIP;
+    if (rec.mark("chain") != hipSuccess) return KDA_ERR_HIP;
+    if (kda::launch_chain(io, shc, ca, s) != hipSuccess) return KDA_ERR_HIP;
+    if (rec.done() != hipSuccess) return KDA_ERR_HIP;
+    return KDA_OK;
 }
 
 kda_status_t kda_decode_step(const void* q, const void* k, const void* v, const float* alpha,

@@ -175,6 +175,11 @@ struct PrepArgs {
     int pro;
     float amin, arange, bmax, eps;
     int normq;
+    // packed (variable-length) batches: cu [N + 1] token offsets and cs [N + 1]
+    // chunk offsets of the N sequences (sanitised copies), or null for dense
+    const int* cu;
+    const int* cs;
+    int N;
 };
 
 // logistic function in fp32 (exp2 of the scaled argument; saturates to 0 / 1)
@@ -195,6 +200,66 @@ struct ChainArgs {
     float* ST;
     void* CS;          // chunk-start states [B,H,NC,Dk,Dv] in the io type, or null
     int B, T, H, Dv, NC;
+    const int* cu;     // packed batches (B = number of sequences): see PrepArgs
+    const int* cs;
 };
+
+// Where one unit (one chunk of one sequence and head) lives.  Dense batches:
+// unit = (b H + h) NC + n, tokens from row b T + n C.  Packed batches:
+// sequence i owns units [cs[i] H, cs[i+1] H) ordered (head, chunk), tokens
+// from row cu[i] + n C; the same numbering as the dense one when every
+// sequence has the same length.  Units past the last sequence are invalid.
+struct UnitPos { int bh, h, n, row0, nvalid; bool valid; };
+__device__ __forceinline__ UnitPos locate_unit(int unit, int H, int T, int NC, int C,
+                                               const int* cu, const int* cs, int N)
+{
+    UnitPos p;
+    if (!cu) {
+        p.n = unit % NC;
+        p.bh = unit / NC;
+        p.h = p.bh % H;
+        p.row0 = (p.bh / H) * T + p.n * C;
+        p.nvalid = min(C, T - p.n * C);
+        p.valid = true;
+        return p;
+    }
+    p.valid = unit < cs[N] * H;
+    int lo = 0, hi = N;               // cs[lo] H <= unit < cs[hi] H
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (cs[mid] * H <= unit) lo = mid; else hi = mid;
+    }
+    const int nci = max(cs[lo + 1] - cs[lo], 1);
+    const int rem = unit - cs[lo] * H;
+    p.h = min(rem / nci, H - 1);
+    p.n = rem % nci;
+    p.bh = lo * H + p.h;
+    p.row0 = cu[lo] + p.n * C;
+    p.nvalid = min(C, cu[lo + 1] - cu[lo] - p.n * C);
+    p.valid = p.valid && p.nvalid > 0;
+    return p;
+}
+
+// One (sequence, head) chain: its chunk count, first token row, length and
+// first unit.
+struct SeqPos { int nc, row0, len; size_t ubase; };
+__device__ __forceinline__ SeqPos locate_seq(int bh, int H, int T, int NC, const int* cu,
+                                             const int* cs)
+{
+    SeqPos p;
+    if (!cu) {
+        p.nc = NC;
+        p.row0 = (bh / H) * T;
+        p.len = T;
+        p.ubase = (size_t)bh * NC;
+        return p;
+    }
+    const int i = bh / H, h = bh % H;
+    p.nc = cs[i + 1] - cs[i];
+    p.row0 = cu[i];
+    p.len = cu[i + 1] - cu[i];
+    p.ubase = (size_t)cs[i] * H + (size_t)h * p.nc;
+    return p;
+}
 
 }  // namespace kda

@@ -61,6 +61,8 @@ hipError_t launch_prep_exact(IoType io, const ChunkShape& s, const PrepArgs& a, 
 hipError_t launch_chain(IoType io, const ChunkShape& s, const ChainArgs& a, hipStream_t stream);
 
 hipError_t launch_state_copy(const float* S0, float* ST, size_t n, hipStream_t stream);
+hipError_t launch_varlen_table(const int* cu, int N, int total_T, int C, int umax, int* cu_s,
+                               int* cs, hipStream_t stream);
 
 hipError_t launch_decode(IoType io, int B, int H, int Dk, int Dv, const void* q,
                          const void* k, const void* v, const float* alpha,

@@ -103,10 +103,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_exact_kernel(PrepArgs args,
     const int nlist = sCount;
     for (int li = 0; li < nlist; ++li) {
     const int unit = sList[li];
-    const int n = unit % NC, bh = unit / NC;
-    const int b = bh / H, h = bh % H;
-    const int t0 = n * C;
-    const int nvalid = min(C, T_ - t0);
+    const UnitPos up = locate_unit(unit, H, T_, NC, C, args.cu, args.cs, args.N);
+    const int h = up.h, nvalid = up.nvalid, row0 = up.row0;
 
     const T* __restrict__ gq = static_cast<const T*>(args.q);
     const T* __restrict__ gk = static_cast<const T*>(args.k);
@@ -126,7 +124,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_exact_kernel(PrepArgs args,
             const int r = idx / VPR, vi = idx % VPR;
             uint4 kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
             if (r < nvalid) {
-                const size_t g = (((size_t)b * T_ + t0 + r) * H + h) * DK;
+                const size_t g = (((size_t)row0 + r) * H + h) * DK;
                 kv = reinterpret_cast<const uint4*>(gk + g)[vi];
                 qv = reinterpret_cast<const uint4*>(gq + g)[vi];
             }
@@ -138,11 +136,11 @@ __global__ __launch_bounds__(kPrepThreads) void prep_exact_kernel(PrepArgs args,
             const int r = idx / VPA, vi = idx % VPA;
             float4 av = make_float4(1.f, 1.f, 1.f, 1.f);
             if (r < nvalid)
-                av = reinterpret_cast<const float4*>(args.alpha + (((size_t)b * T_ + t0 + r) * H + h) * DK)[vi];
+                av = reinterpret_cast<const float4*>(args.alpha + (((size_t)row0 + r) * H + h) * DK)[vi];
             reinterpret_cast<float4*>(sAl + r * DK)[vi] = av;
         }
         for (int r = tid; r < C; r += kPrepThreads)
-            sBeta[r] = r < nvalid ? args.beta[((size_t)b * T_ + t0 + r) * H + h] : 0.f;
+            sBeta[r] = r < nvalid ? args.beta[((size_t)row0 + r) * H + h] : 0.f;
     }
     __syncthreads();
     if (args.pro) {
@@ -305,7 +303,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_exact_kernel(PrepArgs args,
             const int r = idx / VPR, c4 = (idx % VPR) * 4;
             float y[4] = {0.f, 0.f, 0.f, 0.f};
             if (r < nvalid) {
-                const T* src = gv + (((size_t)b * T_ + t0 + r) * H + h) * Dv + c4;
+                const T* src = gv + (((size_t)row0 + r) * H + h) * Dv + c4;
                 const float bt = sBeta[r];
 #pragma unroll
                 for (int x = 0; x < 4; ++x) y[x] = bt * to_f32(src[x]);

@@ -162,12 +162,14 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
     const int c0 = 4 * q4;                                    // my channels c0 .. c0+3
     const int T_ = args.T, H = args.H, NC = args.NC;
     const int unit = blockIdx.x;
-    const int n = unit % NC, bh = unit / NC;
-    const int b = bh / H, h = bh % H;
-    const int t0 = n * C;
-    const int nvalid = min(C, T_ - t0);
+    const UnitPos up = locate_unit(unit, H, T_, NC, C, args.cu, args.cs, args.N);
+    if (!up.valid) {                  // past the last sequence of a packed batch
+        if (tid == 0) args.FL[unit] = 0;
+        return;
+    }
+    const int h = up.h, nvalid = up.nvalid;
 
-    const size_t tok0 = ((size_t)b * T_ + t0) * H + h;     // row of token t0, head h
+    const size_t tok0 = (size_t)up.row0 * H + h;          // first token of the unit, head h
     const T* gq = static_cast<const T*>(args.q) + tok0 * DK;
     const T* gk = static_cast<const T*>(args.k) + tok0 * DK;
     const float* ga = args.alpha + tok0 * DK;

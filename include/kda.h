@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 typedef enum {
     KDA_OK = 0,
@@ -181,6 +181,38 @@ kda_status_t kda_chunk_forward_prologue(const void* q_raw, const void* k_raw, co
                                         kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
                                         void* workspace, size_t workspace_bytes,
                                         void* stream);
+
+/*
+ * Packed (variable-length) batches: N sequences stored back to back, sequence
+ * i on token rows cu_seqlens[i] .. cu_seqlens[i+1] - 1 of q, k, alpha
+ * [total_T,H,Dk], v, out [total_T,H,Dv] and beta [total_T,H]; every sequence
+ * is chunked from its own start and carries its own state
+ * (initial_state / final_state [N,H,Dk,Dv] fp32, either may be NULL).
+ *   cu_seqlens : device int32 [N + 1], 0 = cu[0] <= cu[1] <= ... <= cu[N] =
+ *                total_T.  It is read on the device only: a table that breaks
+ *                this rule is clamped (offsets into [0, total_T], made
+ *                nondecreasing), so the kernels stay inside the buffers, but
+ *                the results for the affected rows are unspecified and rows
+ *                past cu[N] are not written.
+ *   prologue   : NULL (alpha, beta, q, k as given) or the parameterisation of
+ *                kda_chunk_forward_prologue (alpha, beta then hold logits).
+ *   workspace  : at least kda_chunk_forward_varlen_workspace_size() bytes.
+ * Empty sequences are allowed (their state passes through).  Every other rule
+ * and error is that of kda_chunk_forward; N in [1, 2^24].
+ */
+kda_status_t kda_chunk_forward_varlen_workspace_size(int N, int total_T, int H, int Dk, int Dv,
+                                                     int chunk, kda_dtype_t dtype,
+                                                     size_t* bytes);
+kda_status_t kda_chunk_forward_varlen(const void* q, const void* k, const void* v,
+                                      const float* alpha, const float* beta,
+                                      const kda_prologue_t* prologue,
+                                      const int* cu_seqlens, int N,
+                                      const float* initial_state, void* out,
+                                      float* final_state,
+                                      int total_T, int H, int Dk, int Dv, int chunk,
+                                      kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
+                                      void* workspace, size_t workspace_bytes,
+                                      void* stream);
 
 /*
  * One single-token step for every (b, h), applied to a resident fp32 state in

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 3
+    assert lib.kda_abi_version() == 4
     for s in range(8):
         assert lib.kda_status_string(s)
     assert lib.kda_status_string(99) == b"unknown status"
@@ -169,6 +169,29 @@ def test_forward_prologue_validation(lib):
     assert fwd_prologue(lib, (0.0, 1.0, 1.0, 1e-6, 2)) == UNSUP        # normalize_q not 0/1
     assert fwd_prologue(lib, (-1.0, 1.0, 1.0, 1e-6, 1), mode=0) == UNSUP   # KDA: gates >= 0
     assert fwd_prologue(lib, (0.0, 1.0, 2.0, 1e-6, 1), mode=0) == UNSUP    # KDA: beta <= 1
+
+
+def test_varlen_workspace_and_validation(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.kda_chunk_forward_varlen_workspace_size(3, 300, 2, 64, 64, 32, BF16, ctypes.byref(n)) == OK
+    # per-unit regions for ceil(300 / 32) + 3 = 13 chunks x 2 heads, then the two tables
+    per_unit = 3 * 32 * 64 * 2 + 32 * 64 * 2 + 32 * 32 * 2 + 64 * 4 + 1
+    assert n.value >= 26 * per_unit and n.value < 26 * per_unit + 26 * 7 * 256 + 512
+    assert lib.kda_chunk_forward_varlen_workspace_size(0, 10, 1, 16, 16, 16, F32, ctypes.byref(n)) == SHAPE
+    f = Fake()
+
+    def vl(cu=True, N=2, total=40, ws=True, q=True):
+        need = ctypes.c_size_t(0)
+        lib.kda_chunk_forward_varlen_workspace_size(max(N, 1), total, 2, 16, 16, 16, F32, ctypes.byref(need))
+        return lib.kda_chunk_forward_varlen(f() if q else None, f(), f(), f(), f(), None,
+                                            f() if cu else None, N, None, f(), None, total, 2, 16,
+                                            16, 16, F32, 1, 0, f(need.value + 4096) if ws else None,
+                                            need.value, None)
+    assert vl(cu=False) == NULLP
+    assert vl(ws=False) == NULLP
+    assert vl(q=False) == NULLP
+    assert vl(N=0) == SHAPE
+    assert vl(total=-1) == SHAPE
 
 
 def test_decode_validation(lib):

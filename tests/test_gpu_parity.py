@@ -153,6 +153,86 @@ def test_forward_prologue(name, base, ov, pro, forget):
     assert eo <= TOL[w.dtype] and es <= TOL[w.dtype]
 
 
+# (name, base workload, overrides, sequence lengths)
+VARLEN = [
+    ("bf16_kda_d64_c32_mixed", 2, dict(H=2, D=64, chunk=32, s0_std=0.3), [0, 1, 64, 130, 37, 200]),
+    ("f32_ckda_d32_c16_mixed", 1, dict(H=3, D=32, chunk=16, s0_std=0.5), [5, 0, 48, 17]),
+    ("bf16_ckda_d128_c64_long", 3, dict(H=2, chunk=64), [300, 64, 1, 129]),
+]
+
+
+@pytest.mark.parametrize("name,base,ov,lengths", VARLEN, ids=[c[0] for c in VARLEN])
+def test_forward_varlen(name, base, ov, lengths):
+    """kda_chunk_forward_varlen: every sequence of the packed batch against the
+    oracle run on that sequence alone with its own initial state."""
+    w = workloads.workload(base, **ov)
+    say(f"[forward varlen] {name}: {w} lengths {lengths}")
+    inp = workloads.make_varlen(w, lengths)
+    d = to_dev(inp)
+    out, st = kda.chunk_forward_varlen(d["q"][0], d["k"][0], d["v"][0], d["alpha"][0],
+                                       d["beta"][0], d["cu_seqlens"], d["S0"], chunk=w.chunk,
+                                       mode=w.mode)
+    torch.cuda.synchronize()
+    cu = inp["cu_seqlens"].tolist()
+    worst_o = worst_s = 0.0
+    for i, L in enumerate(lengths):
+        sl = slice(cu[i], cu[i + 1])
+        sub = {x: inp[x][:, sl] for x in ("q", "k", "v", "alpha", "beta")}
+        sub["S0"] = None if inp["S0"] is None else inp["S0"][i:i + 1]
+        o_ref, s_ref = run_oracle(sub)
+        if L > 0:
+            worst_o = max(worst_o, slice_err_out(np32(out[sl])[None], o_ref))
+        worst_s = max(worst_s, slice_err_state(np32(st[i:i + 1]), s_ref))
+    say(f"  err out {worst_o:.3e} state {worst_s:.3e}")
+    assert worst_o <= TOL[w.dtype] and worst_s <= TOL[w.dtype]
+
+
+def test_forward_varlen_uniform_equals_dense():
+    """Equal lengths: the packed batch numbers its chunks exactly like the
+    dense batch, so outputs and states are bit-identical to kda_chunk_forward."""
+    w = workloads.workload(2, B=3, H=2, T=100, chunk=64, s0_std=0.2)
+    say(f"[forward varlen] uniform vs dense {w}")
+    d = to_dev(workloads.make_prefill(w))
+    out, st = run_gpu(d, w.chunk, w.mode)
+    cu = torch.arange(0, 301, 100, dtype=torch.int32, device=DEV)
+    flat = lambda t: t.reshape((1, -1) + tuple(t.shape[2:]))[0]
+    out2, st2 = kda.chunk_forward_varlen(flat(d["q"]), flat(d["k"]), flat(d["v"]), flat(d["alpha"]),
+                                         flat(d["beta"]), cu, d["S0"], chunk=w.chunk, mode=w.mode)
+    torch.cuda.synchronize()
+    assert torch.equal(out2.reshape(out.shape), out) and torch.equal(st2, st)
+
+
+def test_forward_varlen_prologue():
+    """Packed batch with the fused parameterisation, per sequence against the
+    oracle's forward from raw inputs."""
+    w = workloads.workload(3, H=2, chunk=64, s0_std=None)
+    lengths = [70, 33, 0, 128]
+    say(f"[forward varlen prologue] {w} lengths {lengths}")
+    total = sum(lengths)
+    inp = workloads.make_prefill_raw(workloads.workload(3, B=1, H=2, T=total, chunk=64, s0_std=None))
+    cu = [0]
+    for L in lengths:
+        cu.append(cu[-1] + L)
+    pro = dict(alpha_min=-1.0, alpha_max=1.0, beta_max=2.0, eps=1e-6, normalize_q=True)
+    d = to_dev(inp)
+    out, st = kda.chunk_forward_varlen(d["q"][0], d["k"][0], d["v"][0], d["gate"][0],
+                                       d["beta_logit"][0], torch.tensor(cu, dtype=torch.int32, device=DEV),
+                                       None, chunk=64, mode=workloads.CKDA, prologue=pro)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for i, L in enumerate(lengths):
+        sl = slice(cu[i], cu[i + 1])
+        o_ref, s_ref = oracle.forward_prologue(
+            np32(inp["q"][:, sl]), np32(inp["k"][:, sl]), np32(inp["v"][:, sl]),
+            np32(inp["gate"][:, sl]), np32(inp["beta_logit"][:, sl]), None,
+            nthreads=oracle_threads(), **pro)
+        if L > 0:
+            worst = max(worst, slice_err_out(np32(out[sl])[None], o_ref))
+        worst = max(worst, slice_err_state(np32(st[i:i + 1]), s_ref))
+    say(f"  err {worst:.3e}")
+    assert worst <= 2e-2
+
+
 def test_forward_cfg2_full():
     """KDA bf16 prefill, B=1 H=32 T=8192 d=128 chunk=64, every head."""
     w = workloads.workload(2)

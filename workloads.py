@@ -153,6 +153,23 @@ def make_prefill_raw(w: Workload, device="cpu", seed: int | None = None, gate_st
             "gate": gate.contiguous(), "beta_logit": blog.contiguous(), "S0": S0}
 
 
+def make_varlen(w: Workload, lengths, device="cpu", seed: int | None = None):
+    """A packed batch of len(lengths) sequences (w.B is ignored): the inputs of
+    make_prefill for B = 1, T = sum(lengths), plus cu_seqlens (int32 [N+1])
+    and, when w.s0_std is set, one initial state per sequence [N,H,D,D]."""
+    total = int(sum(lengths))
+    inp = make_prefill(replace(w, B=1, T=total, s0_std=None), device=device, seed=seed)
+    cu = torch.zeros(len(lengths) + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
+    inp["cu_seqlens"] = cu.to(device)
+    inp["S0"] = None
+    if w.s0_std is not None:
+        g = _gen((w.seed if seed is None else seed) + 1000, device)
+        inp["S0"] = (w.s0_std * torch.randn((len(lengths), w.H, w.D, w.D), generator=g,
+                                            device=device, dtype=torch.float32)).contiguous()
+    return inp
+
+
 def make_decode(w: Workload, steps: int | None = None, device="cpu", seed: int | None = None):
     """Inputs for stacked decode steps: S0 [B,H,D,D] fp32, then per step
     q, k, v [N,B,H,D] (w.dtype), alpha [N,B,H,D] fp32, beta [N,B,H] fp32."""
