@@ -56,6 +56,9 @@ def _load():
         lib.kda_oracle_forward_prologue.argtypes = [fp, fp, fp, fp, fp, fp, d, d, d, d, i,
                                                     dp, dp, i, i, i, i, i, i]
         lib.kda_oracle_forward_prologue.restype = i
+        lib.kda_oracle_forward_phase.argtypes = [fp, fp, fp, fp, fp, fp, fp, dp, dp,
+                                                 i, i, i, i, i, i]
+        lib.kda_oracle_forward_phase.restype = i
         lib.kda_oracle_decode.argtypes = [fp, fp, fp, fp, fp, dp, dp,
                                           i, i, i, i, i, i]
         lib.kda_oracle_decode.restype = i
@@ -139,6 +142,29 @@ def forward_prologue(q_raw, k_raw, v, gate, beta_logit, S0=None, *, alpha_min: f
         B, T, H, Dk, Dv, nthreads or default_threads())
     if rc != 0:
         raise RuntimeError("kda_oracle_forward_prologue failed")
+    return out, ST
+
+
+def forward_phase(q, k, v, alpha, theta, beta, S0=None, nthreads: int | None = None):
+    """Phase-variant forward ("Semidirect Fourier Delta Attention" §3 eq. (13)):
+    channel pairs (2p, 2p+1) decay by alpha_p R(theta_p).  q, k [B,T,H,Dk];
+    v [B,T,H,Dv]; alpha, theta [B,T,H,Dk/2]; beta [B,T,H]; S0 [B,H,Dk,Dv] or
+    None.  Returns (out, ST) in float64."""
+    lib = _load()
+    q, k, v, a, th, b = (_f32(x) for x in (q, k, v, alpha, theta, beta))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    assert Dk % 2 == 0 and a.shape == (B, T, H, Dk // 2) and th.shape == a.shape
+    s0 = None if S0 is None else _f32(S0)
+    out = np.empty((B, T, H, Dv), dtype=np.float64)
+    ST = np.empty((B, H, Dk, Dv), dtype=np.float64)
+    rc = lib.kda_oracle_forward_phase(
+        _ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float),
+        _ptr(a, ctypes.c_float), _ptr(th, ctypes.c_float), _ptr(b, ctypes.c_float),
+        _ptr(s0, ctypes.c_float), _ptr(out, ctypes.c_double), _ptr(ST, ctypes.c_double),
+        B, T, H, Dk, Dv, nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError("kda_oracle_forward_phase failed")
     return out, ST
 
 

@@ -24,7 +24,9 @@
 
 /*
  * One token of eq. (1) followed by eq. (14), on a double state S [Dk][Dv]:
- *   S <- diag(alpha) S                          (channel-wise decay)
+ *   S <- diag(alpha) S                          (channel-wise decay; with
+ *                                                theta, the phase decay of
+ *                                                eq. (13): see below)
  *   S <- (I - beta k k^T) S + beta k v^T         (delta correction of the
  *                                                 decayed state)
  *   o  = S^T q                                   (post-update read-out)
@@ -33,13 +35,29 @@
  * scratch.  o may be NULL.
  */
 static void token_update(double* S, const double* q, const double* k,
-                         const double* v, const double* alpha, double beta,
-                         double* o, int Dk, int Dv, double* pred)
+                         const double* v, const double* alpha, const double* theta,
+                         double beta, double* o, int Dk, int Dv, double* pred)
 {
-    for (int c = 0; c < Dk; ++c) {
-        const double a = alpha[c];
-        double* row = S + (size_t)c * Dv;
-        for (int j = 0; j < Dv; ++j) row[j] *= a;
+    if (!theta) {
+        for (int c = 0; c < Dk; ++c) {
+            const double a = alpha[c];
+            double* row = S + (size_t)c * Dv;
+            for (int j = 0; j < Dv; ++j) row[j] *= a;
+        }
+    } else {
+        /* phase variant: channels 2p, 2p+1 form one complex coordinate and the
+         * decay is alpha_p e^{i theta_p}, the 2x2 block alpha_p R(theta_p)
+         * with R = [[cos, -sin], [sin, cos]] acting on that pair of rows */
+        for (int p = 0; p < Dk / 2; ++p) {
+            const double c = alpha[p] * cos(theta[p]), sn = alpha[p] * sin(theta[p]);
+            double* r0 = S + (size_t)(2 * p) * Dv;
+            double* r1 = r0 + Dv;
+            for (int j = 0; j < Dv; ++j) {
+                const double x = r0[j], y = r1[j];
+                r0[j] = c * x - sn * y;
+                r1[j] = sn * x + c * y;
+            }
+        }
     }
     for (int j = 0; j < Dv; ++j) pred[j] = 0.0;
     for (int c = 0; c < Dk; ++c) {
@@ -97,13 +115,13 @@ struct prologue {
  */
 static double load_token(const struct prologue* pro, const float* q, const float* k,
                          const float* v, const float* alpha, float beta, double* qd,
-                         double* kd, double* vd, double* ad, int Dk, int Dv)
+                         double* kd, double* vd, double* ad, int Dk, int Dv, int na)
 {
     for (int c = 0; c < Dk; ++c) {
         qd[c] = (double)q[c];
         kd[c] = (double)k[c];
-        ad[c] = (double)alpha[c];
     }
+    for (int c = 0; c < na; ++c) ad[c] = (double)alpha[c];
     for (int j = 0; j < Dv; ++j) vd[j] = (double)v[j];
     if (!pro) return (double)beta;
     double nk = 0.0, nq = 0.0;
@@ -122,12 +140,15 @@ static double load_token(const struct prologue* pro, const float* q, const float
 }
 
 static int forward_impl(const struct prologue* pro, const float* q, const float* k,
-                        const float* v, const float* alpha, const float* beta,
-                        const float* S0, double* out, double* ST, double* CS, int chunk,
-                        int B, int T, int H, int Dk, int Dv, int nthreads)
+                        const float* v, const float* alpha, const float* theta,
+                        const float* beta, const float* S0, double* out, double* ST,
+                        double* CS, int chunk, int B, int T, int H, int Dk, int Dv,
+                        int nthreads)
 {
     if (!q || !k || !v || !alpha || !beta || !out) return -1;
     if (B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return -1;
+    if (theta && Dk % 2 != 0) return -1;
+    const int na = theta ? Dk / 2 : Dk;      /* gates per token */
     if (CS && chunk <= 0) return -1;
     const long nchunks = CS ? (T + chunk - 1) / chunk : 0;
     set_threads(nthreads);
@@ -137,7 +158,7 @@ static int forward_impl(const struct prologue* pro, const float* q, const float*
 #pragma omp parallel for schedule(dynamic, 1)
     for (long bh = 0; bh < nbh; ++bh) {
         const int b = (int)(bh / H), h = (int)(bh % H);
-        const size_t nscr = (size_t)Dk * Dv + 2 * (size_t)Dv + 3 * (size_t)Dk;
+        const size_t nscr = (size_t)Dk * Dv + 2 * (size_t)Dv + 4 * (size_t)Dk;
         double* S = (double*)malloc(sizeof(double) * nscr);
         if (!S) {
 #pragma omp atomic write
@@ -149,6 +170,7 @@ static int forward_impl(const struct prologue* pro, const float* q, const float*
         double* qd = vd + Dv;
         double* kd = qd + Dk;
         double* ad = kd + Dk;
+        double* td = ad + Dk;
         if (S0) {
             const float* s0 = S0 + (size_t)bh * Dk * Dv;
             for (size_t e = 0; e < (size_t)Dk * Dv; ++e) S[e] = (double)s0[e];
@@ -161,8 +183,10 @@ static int forward_impl(const struct prologue* pro, const float* q, const float*
                 memcpy(CS + ((size_t)bh * nchunks + t / chunk) * Dk * Dv, S,
                        sizeof(double) * (size_t)Dk * Dv);
             const double bt = load_token(pro, q + tok * Dk, k + tok * Dk, v + tok * Dv,
-                                         alpha + tok * Dk, beta[tok], qd, kd, vd, ad, Dk, Dv);
-            token_update(S, qd, kd, vd, ad, bt, out + tok * Dv, Dk, Dv, pred);
+                                         alpha + tok * na, beta[tok], qd, kd, vd, ad, Dk, Dv, na);
+            if (theta)
+                for (int p = 0; p < na; ++p) td[p] = (double)theta[tok * na + p];
+            token_update(S, qd, kd, vd, ad, theta ? td : NULL, bt, out + tok * Dv, Dk, Dv, pred);
         }
         if (ST) memcpy(ST + (size_t)bh * Dk * Dv, S, sizeof(double) * (size_t)Dk * Dv);
         free(S);
@@ -175,8 +199,8 @@ int kda_oracle_forward(const float* q, const float* k, const float* v,
                        double* out, double* ST, double* CS, int chunk,
                        int B, int T, int H, int Dk, int Dv, int nthreads)
 {
-    return forward_impl(NULL, q, k, v, alpha, beta, S0, out, ST, CS, chunk, B, T, H, Dk, Dv,
-                        nthreads);
+    return forward_impl(NULL, q, k, v, alpha, NULL, beta, S0, out, ST, CS, chunk, B, T, H, Dk,
+                        Dv, nthreads);
 }
 
 int kda_oracle_forward_prologue(const float* q_raw, const float* k_raw, const float* v,
@@ -187,8 +211,18 @@ int kda_oracle_forward_prologue(const float* q_raw, const float* k_raw, const fl
 {
     if (!(eps >= 0.0)) return -1;
     const struct prologue pro = {amin, amax, bmax, eps, normalize_q};
-    return forward_impl(&pro, q_raw, k_raw, v, gate, beta_logit, S0, out, ST, NULL, 0, B, T,
-                        H, Dk, Dv, nthreads);
+    return forward_impl(&pro, q_raw, k_raw, v, gate, NULL, beta_logit, S0, out, ST, NULL, 0, B,
+                        T, H, Dk, Dv, nthreads);
+}
+
+int kda_oracle_forward_phase(const float* q, const float* k, const float* v,
+                             const float* alpha, const float* theta, const float* beta,
+                             const float* S0, double* out, double* ST,
+                             int B, int T, int H, int Dk, int Dv, int nthreads)
+{
+    if (!theta) return -1;
+    return forward_impl(NULL, q, k, v, alpha, theta, beta, S0, out, ST, NULL, 0, B, T, H, Dk,
+                        Dv, nthreads);
 }
 
 int kda_oracle_decode(const float* q, const float* k, const float* v,
@@ -204,7 +238,7 @@ int kda_oracle_decode(const float* q, const float* k, const float* v,
 
 #pragma omp parallel for schedule(dynamic, 1)
     for (long bh = 0; bh < nbh; ++bh) {
-        double* pred = (double*)malloc(sizeof(double) * (2 * (size_t)Dv + 3 * (size_t)Dk));
+        double* pred = (double*)malloc(sizeof(double) * (2 * (size_t)Dv + 4 * (size_t)Dk));
         if (!pred) {
 #pragma omp atomic write
             failed = 1;
@@ -218,8 +252,8 @@ int kda_oracle_decode(const float* q, const float* k, const float* v,
         for (int s = 0; s < nsteps; ++s) {
             const size_t tok = (size_t)s * nbh + bh;
             const double bt = load_token(NULL, q + tok * Dk, k + tok * Dk, v + tok * Dv,
-                                         alpha + tok * Dk, beta[tok], qd, kd, vd, ad, Dk, Dv);
-            token_update(Sbh, qd, kd, vd, ad, bt, out + tok * Dv, Dk, Dv, pred);
+                                         alpha + tok * Dk, beta[tok], qd, kd, vd, ad, Dk, Dv, Dk);
+            token_update(Sbh, qd, kd, vd, ad, NULL, bt, out + tok * Dv, Dk, Dv, pred);
         }
         free(pred);
     }

@@ -57,6 +57,17 @@ int kda_oracle_forward_prologue(const float* q_raw, const float* k_raw, const fl
                                 int normalize_q, double* out, double* ST,
                                 int B, int T, int H, int Dk, int Dv, int nthreads);
 
+/* Phase variant ("Semidirect Fourier Delta Attention", §3 eq. (13), real
+ * form eq. (2) with the 2x2 rotation blocks of eq. (12)): channels 2p, 2p+1
+ * form complex coordinate p and the decay is Lambda_t = diag(alpha_t e^{i
+ * theta_t}), i.e. the block alpha_p R(theta_p), R = [[cos, -sin], [sin, cos]],
+ * on that pair of state rows, then the same delta correction and read-out.
+ * alpha, theta: [B, T, H, Dk/2] (one per pair); Dk must be even. */
+int kda_oracle_forward_phase(const float* q, const float* k, const float* v,
+                             const float* alpha, const float* theta, const float* beta,
+                             const float* S0, double* out, double* ST,
+                             int B, int T, int H, int Dk, int Dv, int nthreads);
+
 /* nsteps single-token updates applied to a resident double state in place.
  * Per-step inputs are stacked: q, k, alpha [nsteps, B, H, Dk],
  * v [nsteps, B, H, Dv], beta [nsteps, B, H]; out [nsteps, B, H, Dv];

@@ -498,3 +498,72 @@ def test_prologue_gate_symmetry_and_limits(oracle_lib):
     o_lo, _ = oracle_lib.forward_prologue(q, k, v, -hi, c, S0, alpha_min=-0.5, alpha_max=0.9, **kw)
     o_end2, _ = oracle_lib.forward_prologue(q, k, v, g, c, S0, alpha_min=-0.5, alpha_max=-0.5, **kw)
     assert np.abs(o_lo - o_end2).max() < 1e-12
+
+
+def _phase_inputs(seed, B=1, T=19, H=2, Dk=8, Dv=5):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, T, H, Dk)).astype(np.float32) * 0.5
+    k = rng.standard_normal((B, T, H, Dk)).astype(np.float32) * 0.5
+    v = rng.standard_normal((B, T, H, Dv)).astype(np.float32)
+    a = rng.uniform(0.5, 1.0, (B, T, H, Dk // 2)).astype(np.float32)
+    th = rng.uniform(-3.0, 3.0, (B, T, H, Dk // 2)).astype(np.float32)
+    b = rng.uniform(0, 1, (B, T, H)).astype(np.float32)
+    S0 = rng.standard_normal((B, H, Dk, Dv)).astype(np.float32)
+    return q, k, v, a, th, b, S0
+
+
+def test_phase_zero_is_kda(oracle_lib):
+    """Phase variant with theta = 0 is KDA with each pair's decay on both of its
+    channels ("Semidirect Fourier Delta Attention", Prop. 2.1)."""
+    q, k, v, a, th, b, S0 = _phase_inputs(21)
+    o1, s1 = oracle_lib.forward_phase(q, k, v, a, np.zeros_like(th), b, S0)
+    o2, s2 = oracle_lib.forward(q, k, v, np.repeat(a, 2, axis=-1), b, S0)
+    assert np.array_equal(o1, o2) and np.array_equal(s1, s2)
+
+
+def test_phase_beta_zero_is_diagonal_ssm(oracle_lib):
+    """beta = 0 leaves S_t = Lambda_t S_{t-1} (Prop. 2.1): per pair, the product
+    of the decays times the rotation by the summed phases (rotations of the
+    plane compose by adding angles), applied to S0; o_t = S_t^T q_t."""
+    q, k, v, a, th, b, S0 = _phase_inputs(22)
+    b[:] = 0.0
+    o, s = oracle_lib.forward_phase(q, k, v, a, th, b, S0)
+    B, T, H, Dk = q.shape
+    for t in range(T):
+        amp = np.prod(a[:, :t + 1].astype(np.float64), axis=1)         # [B,H,Dk/2]
+        ang = np.sum(th[:, :t + 1].astype(np.float64), axis=1)
+        S = np.empty(S0.shape, dtype=np.float64)
+        x, y = S0[:, :, 0::2].astype(np.float64), S0[:, :, 1::2].astype(np.float64)
+        c, sn = (amp * np.cos(ang))[..., None], (amp * np.sin(ang))[..., None]
+        S[:, :, 0::2] = c * x - sn * y
+        S[:, :, 1::2] = sn * x + c * y
+        o_exp = np.einsum("bhkv,bhk->bhv", S, q[:, t].astype(np.float64))
+        assert np.abs(o[:, t] - o_exp).max() < 1e-12
+    assert np.abs(s - S).max() < 1e-12
+
+
+def test_phase_pi_is_negative_gate(oracle_lib):
+    """theta = pi turns each pair's block into -alpha I: the same recurrence as
+    the gate -alpha on both channels (the CKDA range).  The phases are fp32, so
+    pi carries a sine of about 9e-8; the bound allows for that."""
+    q, k, v, a, th, b, S0 = _phase_inputs(23)
+    o1, s1 = oracle_lib.forward_phase(q, k, v, a, np.full_like(th, np.pi), b, S0)
+    o2, s2 = oracle_lib.forward(q, k, v, -np.repeat(a, 2, axis=-1), b, S0)
+    assert np.abs(o1 - o2).max() < 1e-5 and np.abs(s1 - s2).max() < 1e-5
+    # ... while theta = 0 against the gate -alpha differs at order one
+    o3, _ = oracle_lib.forward_phase(q, k, v, a, np.zeros_like(th), b, S0)
+    assert np.abs(o3 - o2).max() > 1e-2
+
+
+def test_phase_rotation_preserves_norm(oracle_lib):
+    """alpha = 1, beta = 0: every step is a rotation of each row pair, so the
+    Frobenius norm of the state never changes."""
+    q, k, v, a, th, b, S0 = _phase_inputs(24, T=40)
+    a[:] = 1.0
+    b[:] = 0.0
+    for T in (1, 7, 40):
+        _, s = oracle_lib.forward_phase(q[:, :T], k[:, :T], v[:, :T], a[:, :T], th[:, :T],
+                                        b[:, :T], S0)
+        n0 = np.sqrt((S0.astype(np.float64) ** 2).sum(axis=(-2, -1)))
+        n1 = np.sqrt((s ** 2).sum(axis=(-2, -1)))
+        assert np.abs(n1 - n0).max() < 1e-12 * n0.max()
