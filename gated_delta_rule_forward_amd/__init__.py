@@ -19,7 +19,8 @@ import torch
 
 __all__ = [
     "KDA", "CKDA", "KdaError", "library_path", "load", "abi_version", "workspace_size",
-    "chunk_forward", "chunk_forward_prologue", "chunk_forward_varlen", "decode_step", "gate_prep", "last_stage_times",
+    "chunk_forward", "chunk_forward_prologue", "chunk_forward_varlen", "chunk_forward_phase",
+    "decode_step", "decode_step_phase", "gate_prep", "last_stage_times",
     "STAGE_EVENTS",
 ]
 
@@ -73,6 +74,10 @@ def load():
     lib.kda_chunk_forward_prologue.argtypes = [vp] * 5 + [ctypes.POINTER(Prologue)] + [vp] * 3 + \
         [i] * 8 + [u, vp, sz, vp]
     lib.kda_chunk_forward_prologue.restype = i
+    lib.kda_chunk_forward_phase.argtypes = [vp] * 9 + [i] * 8 + [u, vp, sz, vp]
+    lib.kda_chunk_forward_phase.restype = i
+    lib.kda_decode_step_phase.argtypes = [vp] * 8 + [i] * 6 + [u, vp]
+    lib.kda_decode_step_phase.restype = i
     lib.kda_chunk_forward_varlen_workspace_size.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(sz)]
     lib.kda_chunk_forward_varlen_workspace_size.restype = i
     lib.kda_chunk_forward_varlen.argtypes = [vp] * 5 + [ctypes.POINTER(Prologue), vp, i, vp, vp,
@@ -244,6 +249,50 @@ def chunk_forward_varlen(q, k, v, alpha, beta, cu_seqlens, initial_state=None, *
                                       _stream(stream))
     _check("kda_chunk_forward_varlen", st)
     return out, final_state
+
+
+def chunk_forward_phase(q, k, v, alpha, theta, beta, initial_state=None, *, chunk: int = 64,
+                        mode: int = CKDA, out=None, final_state=None,
+                        output_final_state: bool = True, workspace=None, stream=None,
+                        flags: int = 0):
+    """Phase variant (kda_chunk_forward_phase): alpha and theta [B,T,H,Dk/2]
+    fp32, one decay and one phase per channel pair; everything else as
+    chunk_forward.  Returns (out, final_state)."""
+    lib = load()
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if out is None:
+        out = torch.empty((B, T, H, Dv), dtype=q.dtype, device=q.device)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = workspace_size(B, T, H, Dk, Dv, chunk, q.dtype)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _dev(q, k, v, alpha, theta, beta, initial_state, out, final_state, workspace)
+    st = lib.kda_chunk_forward_phase(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(theta),
+                                     _ptr(beta), _ptr(initial_state), _ptr(out), _ptr(final_state),
+                                     B, T, H, Dk, Dv, chunk, _DT[q.dtype], mode, flags,
+                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream(stream))
+    _check("kda_chunk_forward_phase", st)
+    return out, final_state
+
+
+def decode_step_phase(q, k, v, alpha, theta, beta, state, *, out=None, mode: int = CKDA,
+                      stream=None, flags: int = 0):
+    """Phase-variant decode (kda_decode_step_phase): alpha, theta [B,H,Dk/2];
+    state [B,H,Dk,Dv] fp32 updated in place.  Returns out [B,H,Dv]."""
+    lib = load()
+    B, H, Dk = q.shape
+    Dv = v.shape[-1]
+    if out is None:
+        out = torch.empty((B, H, Dv), dtype=q.dtype, device=q.device)
+    _dev(q, k, v, alpha, theta, beta, state, out)
+    st = lib.kda_decode_step_phase(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(theta),
+                                   _ptr(beta), _ptr(state), _ptr(out), B, H, Dk, Dv,
+                                   _DT[q.dtype], mode, flags, _stream(stream))
+    _check("kda_decode_step_phase", st)
+    return out
 
 
 def decode_step(q, k, v, alpha, beta, state, *, out=None, mode: int = CKDA, stream=None,

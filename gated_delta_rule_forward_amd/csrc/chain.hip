@@ -403,8 +403,19 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
             const int t = wave + 4 * u;
             if (G::NT % 4 == 0 || t < G::NT) {
                 f32x4 acc;
+                if (a.ph) {
+                    // phase variant: rows 2p, 2p+1 turn by Gamma's 2x2 block
+                    // (g0 = |G| cos, g1 = |G| sin)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = cur.gc[u][i] * S[u][i];
+                    for (int i = 0; i < 4; i += 2) {
+                        const float g0 = cur.gc[u][i], g1 = cur.gc[u][i + 1];
+                        acc[i] = g0 * S[u][i] - g1 * S[u][i + 1];
+                        acc[i + 1] = g1 * S[u][i] + g0 * S[u][i + 1];
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[i] = cur.gc[u][i] * S[u][i];
+                }
 #pragma unroll
                 for (int s = 0; s < G::NKC; ++s) acc = mma(cur.kt[u][s], df[s], acc);
                 S[u] = acc;

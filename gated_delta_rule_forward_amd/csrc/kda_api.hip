@@ -126,7 +126,7 @@ kda_status_t chunk_forward(const void* q, const void* k, const void* v, const fl
                            float* final_state, void* chunk_states, const kda_prologue_t* pro,
                            int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype_t dtype,
                            kda_mode_t mode, unsigned flags, void* workspace,
-                           size_t workspace_bytes, void* stream)
+                           size_t workspace_bytes, void* stream, const float* theta = nullptr)
 {
     kda_status_t st = check_forward_shape(B, T, H, Dk, Dv, chunk, dtype);
     if (st != KDA_OK) return st;
@@ -134,9 +134,11 @@ kda_status_t chunk_forward(const void* q, const void* k, const void* v, const fl
     if (flags & ~kKnownFlags) return KDA_ERR_UNSUPPORTED;
     if (T > 0 && (!q || !k || !v || !alpha || !beta || !out)) return KDA_ERR_NULL_POINTER;
     if (pro && !prologue_ok(*pro, mode)) return KDA_ERR_UNSUPPORTED;
+    if (pro && theta) return KDA_ERR_UNSUPPORTED;
 
     const size_t e = elem_size(dtype);
     const size_t ntok = (size_t)B * T * H;
+    const size_t na = theta ? (size_t)Dk / 2 : (size_t)Dk;     // gates per token
     const size_t nstate = (size_t)B * H * Dk * Dv * 4;
     size_t ws_need = 0;
     kda_chunk_forward_workspace_size(B, T, H, Dk, Dv, chunk, dtype, &ws_need);
@@ -145,12 +147,14 @@ kda_status_t chunk_forward(const void* q, const void* k, const void* v, const fl
 
     // q, k, alpha and the workspace are read with 16-byte vector loads; the rest
     // element by element
-    const void* vec[] = {q, k, alpha, workspace};
+    const void* vec[] = {q, k, theta ? nullptr : alpha, workspace};
     for (const void* p : vec)
         if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
-    const void* elt[] = {v, out, beta, initial_state, final_state, chunk_states};
-    const uintptr_t ea[] = {e, e, 4, 4, 4, e};
-    for (int i = 0; i < 6; ++i)
+    // (phase variant: alpha and theta are read as pairs of floats)
+    const void* elt[] = {v, out, beta, initial_state, final_state, chunk_states,
+                         theta ? alpha : nullptr, theta};
+    const uintptr_t ea[] = {e, e, 4, 4, 4, e, 8, 8};
+    for (int i = 0; i < 8; ++i)
         if (elt[i] && !aligned(elt[i], ea[i])) return KDA_ERR_MISALIGNED;
 
     // aliasing: out, workspace and chunk_states overlap nothing; final_state
@@ -158,7 +162,8 @@ kda_status_t chunk_forward(const void* q, const void* k, const void* v, const fl
     const size_t ncs = chunk_states ? (size_t)B * H * ((T + chunk - 1) / chunk) * Dk * Dv * e : 0;
     struct R { const void* p; size_t n; } in[] = {
         {q, ntok * Dk * e}, {k, ntok * Dk * e}, {v, ntok * Dv * e},
-        {alpha, ntok * Dk * 4}, {beta, ntok * 4}, {initial_state, initial_state ? nstate : 0}};
+        {alpha, ntok * na * 4}, {beta, ntok * 4}, {initial_state, initial_state ? nstate : 0},
+        {theta, theta ? ntok * na * 4 : 0}};
     const R outs[] = {{out, ntok * Dv * e}, {workspace, ws_need}, {chunk_states, ncs}};
     for (const R& o : outs)
         for (const R& i : in)
@@ -216,9 +221,10 @@ kda_status_t chunk_forward(const void* q, const void* k, const void* v, const fl
                            pro ? pro->beta_max : 0.f,
                            pro ? pro->eps : 0.f,
                            pro ? pro->normalize_q : 0,
-                           nullptr, nullptr, 0};
+                           nullptr, nullptr, 0, theta};
     const kda::ChainArgs ca{ws.W, ws.U, ws.Kt, ws.QG, ws.P, ws.GC, initial_state, out,
-                            final_state, chunk_states, B, T, H, Dv, sh.NC, nullptr, nullptr};
+                            final_state, chunk_states, B, T, H, Dv, sh.NC, nullptr, nullptr,
+                            theta ? 1 : 0};
 
     if (rec.mark("prep_fast") != hipSuccess) return KDA_ERR_HIP;
     if (kda::launch_prep_fast(io, sh, pa, s) != hipSuccess) return KDA_ERR_HIP;
@@ -259,6 +265,50 @@ size_t varlen_layout(int N, int total_T, int H, int Dk, int Dv, int chunk, IoTyp
                                                      io, off);
     *table_off = units;
     return units + ((2 * ((size_t)N + 1) * sizeof(int) + 255) & ~size_t(255));
+}
+
+// one token per (b, h); theta (may be null) selects the phase variant, whose
+// alpha and theta hold one value per channel pair
+kda_status_t decode_step(const void* q, const void* k, const void* v, const float* alpha,
+                         const float* theta, const float* beta, float* state, void* out, int B,
+                         int H, int Dk, int Dv, kda_dtype_t dtype, kda_mode_t mode,
+                         unsigned flags, void* stream)
+{
+    if (B < 1 || H < 1) return KDA_ERR_BAD_SHAPE;
+    if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERR_UNSUPPORTED;
+    if (!dk_ok(Dk) || !dv_ok(Dv)) return KDA_ERR_UNSUPPORTED;
+    if (mode != KDA_MODE_KDA && mode != KDA_MODE_CKDA) return KDA_ERR_UNSUPPORTED;
+    if (flags & ~kKnownFlags) return KDA_ERR_UNSUPPORTED;
+    if ((long long)B * H > 0x7fffffffLL) return KDA_ERR_BAD_SHAPE;
+    if (!q || !k || !v || !alpha || !beta || !state || !out) return KDA_ERR_NULL_POINTER;
+    const size_t e = elem_size(dtype), nbh = (size_t)B * H;
+    // the state is streamed with 16-byte vectors; everything else element-wise
+    if (!aligned16(state)) return KDA_ERR_MISALIGNED;
+    const size_t na = theta ? (size_t)Dk / 2 : (size_t)Dk;
+    const void* elt[] = {q, k, v, out, alpha, beta, theta};
+    const uintptr_t ea[] = {e, e, e, e, 4, 4, 4};
+    for (int i = 0; i < 7; ++i)
+        if (elt[i] && !aligned(elt[i], ea[i])) return KDA_ERR_MISALIGNED;
+    struct R { const void* p; size_t n; } in[] = {
+        {q, nbh * Dk * e}, {k, nbh * Dk * e}, {v, nbh * Dv * e}, {alpha, nbh * na * 4},
+        {beta, nbh * 4}, {theta, theta ? nbh * na * 4 : 0}};
+    const R st{state, nbh * Dk * Dv * 4}, o{out, nbh * Dv * e};
+    for (const R& i : in)
+        if (overlaps(st.p, st.n, i.p, i.n) || overlaps(o.p, o.n, i.p, i.n)) return KDA_ERR_ALIAS;
+    if (overlaps(st.p, st.n, o.p, o.n)) return KDA_ERR_ALIAS;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    std::unique_lock<std::mutex> lock(g_stage.mu, std::defer_lock);
+    Recorder rec{(flags & KDA_FLAG_STAGE_EVENTS) != 0, s};
+    if (rec.on) {
+        lock.lock();
+        if (stage_begin() != hipSuccess) return KDA_ERR_HIP;
+    }
+    if (rec.mark("decode") != hipSuccess) return KDA_ERR_HIP;
+    if (kda::launch_decode(dtype == KDA_DTYPE_F32 ? IoType::F32 : IoType::BF16, B, H, Dk, Dv, q, k,
+                           v, alpha, beta, state, out, s, theta) != hipSuccess)
+        return KDA_ERR_HIP;
+    return rec.done() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 }  // namespace
@@ -332,6 +382,20 @@ kda_status_t kda_chunk_forward_states(const void* q, const void* k, const void* 
     return chunk_forward(q, k, v, alpha, beta, initial_state, out, final_state, chunk_states,
                          nullptr, B, T, H, Dk, Dv, chunk, dtype, mode, flags, workspace,
                          workspace_bytes, stream);
+}
+
+kda_status_t kda_chunk_forward_phase(const void* q, const void* k, const void* v,
+                                     const float* alpha, const float* theta, const float* beta,
+                                     const float* initial_state, void* out, float* final_state,
+                                     int B, int T, int H, int Dk, int Dv, int chunk,
+                                     kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
+                                     void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (T > 0 && !theta) return KDA_ERR_NULL_POINTER;
+    if (T == 0) theta = nullptr;
+    return chunk_forward(q, k, v, alpha, beta, initial_state, out, final_state, nullptr, nullptr,
+                         B, T, H, Dk, Dv, chunk, dtype, mode, flags, workspace, workspace_bytes,
+                         stream, theta);
 }
 
 kda_status_t kda_chunk_forward_varlen_workspace_size(int N, int total_T, int H, int Dk, int Dv,
@@ -432,9 +496,9 @@ kda_status_t kda_chunk_forward_varlen(const void* q, const void* k, const void* 
                            prologue ? prologue->beta_max : 0.f,
                            prologue ? prologue->eps : 0.f,
                            prologue ? prologue->normalize_q : 0,
-                           cu_s, cs, N};
+                           cu_s, cs, N, nullptr};
     const kda::ChainArgs ca{ws.W, ws.U, ws.Kt, ws.QG, ws.P, ws.GC, initial_state, out,
-                            final_state, nullptr, N, total_T, H, Dv, umax, cu_s, cs};
+                            final_state, nullptr, N, total_T, H, Dv, umax, cu_s, cs, 0};
     if (rec.mark("prep_fast") != hipSuccess) return KDA_ERR_HIP;
     if (kda::launch_prep_fast(io, shp, pa, s) != hipSuccess) return KDA_ERR_HIP;
     if (rec.done() != hipSuccess) return KDA_ERR_HIP;
@@ -452,39 +516,19 @@ kda_status_t kda_decode_step(const void* q, const void* k, const void* v, const 
                              int Dv, kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
                              void* stream)
 {
-    if (B < 1 || H < 1) return KDA_ERR_BAD_SHAPE;
-    if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERR_UNSUPPORTED;
-    if (!dk_ok(Dk) || !dv_ok(Dv)) return KDA_ERR_UNSUPPORTED;
-    if (mode != KDA_MODE_KDA && mode != KDA_MODE_CKDA) return KDA_ERR_UNSUPPORTED;
-    if (flags & ~kKnownFlags) return KDA_ERR_UNSUPPORTED;
-    if ((long long)B * H > 0x7fffffffLL) return KDA_ERR_BAD_SHAPE;
-    if (!q || !k || !v || !alpha || !beta || !state || !out) return KDA_ERR_NULL_POINTER;
-    const size_t e = elem_size(dtype), nbh = (size_t)B * H;
-    // the state is streamed with 16-byte vectors; everything else element-wise
-    if (!aligned16(state)) return KDA_ERR_MISALIGNED;
-    const void* elt[] = {q, k, v, out, alpha, beta};
-    const uintptr_t ea[] = {e, e, e, e, 4, 4};
-    for (int i = 0; i < 6; ++i)
-        if (!aligned(elt[i], ea[i])) return KDA_ERR_MISALIGNED;
-    struct R { const void* p; size_t n; } in[] = {
-        {q, nbh * Dk * e}, {k, nbh * Dk * e}, {v, nbh * Dv * e}, {alpha, nbh * Dk * 4}, {beta, nbh * 4}};
-    const R st{state, nbh * Dk * Dv * 4}, o{out, nbh * Dv * e};
-    for (const R& i : in)
-        if (overlaps(st.p, st.n, i.p, i.n) || overlaps(o.p, o.n, i.p, i.n)) return KDA_ERR_ALIAS;
-    if (overlaps(st.p, st.n, o.p, o.n)) return KDA_ERR_ALIAS;
+    return decode_step(q, k, v, alpha, nullptr, beta, state, out, B, H, Dk, Dv, dtype, mode, flags,
+                       stream);
+}
 
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    std::unique_lock<std::mutex> lock(g_stage.mu, std::defer_lock);
-    Recorder rec{(flags & KDA_FLAG_STAGE_EVENTS) != 0, s};
-    if (rec.on) {
-        lock.lock();
-        if (stage_begin() != hipSuccess) return KDA_ERR_HIP;
-    }
-    if (rec.mark("decode") != hipSuccess) return KDA_ERR_HIP;
-    if (kda::launch_decode(dtype == KDA_DTYPE_F32 ? IoType::F32 : IoType::BF16, B, H, Dk, Dv, q, k,
-                           v, alpha, beta, state, out, s) != hipSuccess)
-        return KDA_ERR_HIP;
-    return rec.done() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+kda_status_t kda_decode_step_phase(const void* q, const void* k, const void* v,
+                                   const float* alpha, const float* theta, const float* beta,
+                                   float* state, void* out, int B, int H, int Dk, int Dv,
+                                   kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
+                                   void* stream)
+{
+    if (!theta) return KDA_ERR_NULL_POINTER;
+    return decode_step(q, k, v, alpha, theta, beta, state, out, B, H, Dk, Dv, dtype, mode, flags,
+                       stream);
 }
 
 kda_status_t kda_gate_prep(const float* alpha, float* L, unsigned char* meta, float* gend, int B,

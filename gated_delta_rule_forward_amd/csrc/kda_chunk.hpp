@@ -180,6 +180,9 @@ struct PrepArgs {
     const int* cu;
     const int* cs;
     int N;
+    // phase variant ("Semidirect Fourier Delta Attention" eq. (13)): theta
+    // [..., Dk/2] per channel pair and alpha then also per pair; null = KDA
+    const float* theta;
 };
 
 // logistic function in fp32 (exp2 of the scaled argument; saturates to 0 / 1)
@@ -202,6 +205,7 @@ struct ChainArgs {
     int B, T, H, Dv, NC;
     const int* cu;     // packed batches (B = number of sequences): see PrepArgs
     const int* cs;
+    int ph;            // GC holds (magnitude cos, magnitude sin) per channel pair
 };
 
 // Where one unit (one chunk of one sequence and head) lives.  Dense batches:

@@ -66,7 +66,8 @@ hipError_t launch_varlen_table(const int* cu, int N, int total_T, int C, int uma
 
 hipError_t launch_decode(IoType io, int B, int H, int Dk, int Dv, const void* q,
                          const void* k, const void* v, const float* alpha,
-                         const float* beta, float* state, void* out, hipStream_t stream);
+                         const float* beta, float* state, void* out, hipStream_t stream,
+                         const float* theta = nullptr);
 
 hipError_t launch_gate_prep(const float* alpha, float* L, uint8_t* meta, float* gend, int B,
                             int T, int H, int Dk, int C, hipStream_t stream);

@@ -135,14 +135,45 @@ __global__ __launch_bounds__(kPrepThreads) void prep_exact_kernel(PrepArgs args,
         for (int idx = tid; idx < C * VPA; idx += kPrepThreads) {
             const int r = idx / VPA, vi = idx % VPA;
             float4 av = make_float4(1.f, 1.f, 1.f, 1.f);
-            if (r < nvalid)
-                av = reinterpret_cast<const float4*>(args.alpha + (((size_t)row0 + r) * H + h) * DK)[vi];
+            if (r < nvalid) {
+                if (args.theta) {        // phase variant: one gate per channel pair
+                    const float2 a2 = reinterpret_cast<const float2*>(
+                        args.alpha + (((size_t)row0 + r) * H + h) * (DK / 2))[vi];
+                    av = make_float4(a2.x, a2.x, a2.y, a2.y);
+                } else {
+                    av = reinterpret_cast<const float4*>(args.alpha + (((size_t)row0 + r) * H + h) * DK)[vi];
+                }
+            }
             reinterpret_cast<float4*>(sAl + r * DK)[vi] = av;
         }
         for (int r = tid; r < C; r += kPrepThreads)
             sBeta[r] = r < nvalid ? args.beta[((size_t)row0 + r) * H + h] : 0.f;
     }
     __syncthreads();
+    __shared__ float sPhEnd[64];       // (phase variant) summed phase of each pair
+    if (args.theta) {
+        // rotate k_r, q_r of every pair by -phi_r (phi_r: the pair's phases
+        // summed over tokens 0..r of the chunk), so that the decay-weighted
+        // products below are the plain ones of the rotated vectors; Ktil and
+        // Gamma_{C-1} are rotated back by phi_{C-1} when they are stored
+        for (int p = tid; p < DK / 2; p += kPrepThreads) {
+            float ph = 0.f;
+            for (int r = 0; r < nvalid; ++r) {
+                ph += args.theta[(((size_t)row0 + r) * H + h) * (DK / 2) + p];
+                float sn, cs;
+                __sincosf(ph, &sn, &cs);
+                T* kr = sK + r * DK + 2 * p;
+                T* qr = sQ + r * DK + 2 * p;
+                const float k0 = to_f32(kr[0]), k1 = to_f32(kr[1]), q0 = to_f32(qr[0]), q1 = to_f32(qr[1]);
+                kr[0] = from_f32<T>(cs * k0 + sn * k1);
+                kr[1] = from_f32<T>(cs * k1 - sn * k0);
+                qr[0] = from_f32<T>(cs * q0 + sn * q1);
+                qr[1] = from_f32<T>(cs * q1 - sn * q0);
+            }
+            sPhEnd[p] = ph;
+        }
+        __syncthreads();
+    }
     if (args.pro) {
         // raw inputs: gate range eq. (15), beta eq. (17), unit-norm keys (and
         // queries) eq. (18) ("Semidirect Fourier Delta Attention" §3), on the
@@ -217,7 +248,6 @@ __global__ __launch_bounds__(kPrepThreads) void prep_exact_kernel(PrepArgs args,
             QGg[frag_off<KB>(r, c, DK)] = from_f32<T>(qr * gm);
             sX[r * DK + c] = from_f32<T>(sBeta[r] * kr * gm);
         }
-        GCg[c] = gm;
         // Ktil_i = k_i rho(C-1, i), stored transposed (row c), 16-byte stores
         float kt[C];
         float e = 1.f;
@@ -226,6 +256,20 @@ __global__ __launch_bounds__(kPrepThreads) void prep_exact_kernel(PrepArgs args,
             kt[i] = to_f32(sK[i * DK + c]) * e;
             e *= a[i];
         }
+        if (args.theta) {
+            // rotate back by phi_{C-1}: channel c pairs with lane c ^ 1
+            float sn, cs;
+            __sincosf(sPhEnd[c >> 1], &sn, &cs);
+            const float sg = (c & 1) ? 1.f : -1.f;    // even: c x0 - s x1, odd: s x0 + c x1
+#pragma unroll
+            for (int i = 0; i < C; ++i) {
+                const float other = __shfl_xor(kt[i], 1);
+                kt[i] = cs * kt[i] + sg * sn * other;
+            }
+            const float go = __shfl_xor(gm, 1);
+            gm = (c & 1) ? sn * go : cs * gm;           // (|G| cos, |G| sin); |G| equal in a pair
+        }
+        GCg[c] = gm;
 #pragma unroll
         for (int i = 0; i < C; ++i) Ktg[frag_off<KB>(c, i, C)] = from_f32<T>(kt[i]);
         // off-diagonal block a: rows r in block a scaled by rho(r, e_a), columns

@@ -82,7 +82,7 @@ struct FastLayout {
         const int kp_max = ((DK + zx + G::KB - 1) / G::KB) * G::KB;
         KS = kp_max + G::PADE;
         const size_t e = sizeof(T);
-        const size_t r1 = (size_t)2 * G::PARTS * DK * 4;
+        const size_t r1 = (size_t)2 * G::PARTS * DK * 4 + (size_t)G::PARTS * (DK / 2) * 4;
         const size_t r2 = 3 * (size_t)C * KS * e;
         const size_t r3 = (size_t)2 * C * G::LDF * 4;
         const size_t r4 = (size_t)(DK + G::DVMAX) * G::XTS * e;
@@ -129,7 +129,13 @@ __device__ __forceinline__ Vec4<T> l2_normalised(const Vec4<T>& v, float eps)
 // them a zero gate makes a part product vanish and flags the chunk.
 // PRO: the inputs are raw (gate and beta logits, unnormalised q and k) and go
 // through the parameterisation first.
-template <typename T, int C, int DK, bool ZS, bool PRO>
+// PH: phase variant: channels 2p, 2p+1 decay by alpha_p R(theta_p) (gates and
+// phases per pair).  With phi_r the summed phase of the chunk's tokens up to
+// r, rho(r, i) = |rho| R(phi_r - phi_i), so rotating every k_r and q_r by
+// -phi_r turns every decay-weighted product into the real one of the plain
+// kernel on the rotated vectors; Ktil is rotated back by phi_{C-1} and
+// Gamma_{C-1} is stored as (|Gamma| cos phi_{C-1}, |Gamma| sin phi_{C-1}).
+template <typename T, int C, int DK, bool ZS, bool PRO, bool PH>
 __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
 {
     using G = FastGeom<T, C, DK>;
@@ -143,6 +149,7 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     float* partL = reinterpret_cast<float*>(lds);                           // gate summary
     int* partPZ = reinterpret_cast<int*>(partL + PARTS * DK);               // nz << 1 | parity
+    float* partPh = partL + 2 * PARTS * DK;                                 // (PH) [PARTS][DK/2]
     T* XA = reinterpret_cast<T*>(lds);                                      // A / P operands
     T* XP = XA + C * KS;
     T* Y = XP + C * KS;
@@ -185,14 +192,24 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
     // ---- loads: my 4 channels over my TOK tokens (k, q kept in io precision) ----
     // (rows past the end re-read the last valid row and become no-op tokens)
     float al[TOK][4], bt[TOK];
+    float th[TOK][2];                  // (PH) the phases of my two channel pairs
     Vec4<T> kv[TOK], qv[TOK];
 #pragma unroll
     for (int j = 0; j < TOK; ++j) {
         const int r = min(part * TOK + j, nvalid - 1);
-        const float4 a4 = *reinterpret_cast<const float4*>(ga + r * rs + c0);
+        if constexpr (PH) {
+            const float2 a2 = *reinterpret_cast<const float2*>(args.alpha + (tok0 + (size_t)r * H) * (DK / 2) + c0 / 2);
+            const float2 t2 = *reinterpret_cast<const float2*>(args.theta + (tok0 + (size_t)r * H) * (DK / 2) + c0 / 2);
+            al[j][0] = al[j][1] = a2.x;
+            al[j][2] = al[j][3] = a2.y;
+            th[j][0] = t2.x;
+            th[j][1] = t2.y;
+        } else {
+            const float4 a4 = *reinterpret_cast<const float4*>(ga + r * rs + c0);
+            al[j][0] = a4.x; al[j][1] = a4.y; al[j][2] = a4.z; al[j][3] = a4.w;
+        }
         kv[j] = Vec4<T>::load(gk + r * rs + c0);
         qv[j] = Vec4<T>::load(gq + r * rs + c0);
-        al[j][0] = a4.x; al[j][1] = a4.y; al[j][2] = a4.z; al[j][3] = a4.w;
         bt[j] = gb[r * H];
     }
     if constexpr (PRO) {
@@ -212,6 +229,7 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
             bt[j] = 0.f;
             kv[j] = Vec4<T>::zero();
             qv[j] = Vec4<T>::zero();
+            if constexpr (PH) { th[j][0] = 0.f; th[j][1] = 0.f; }
 #pragma unroll
             for (int x = 0; x < 4; ++x) al[j][x] = 1.f;
         }
@@ -254,6 +272,14 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
             lp[x] = flog2(m);
             pz[x] = (zn[x] << 1) | (cur[x] < 0.f ? 1 : 0);
         }
+        if constexpr (PH) {
+            // running phase sums of my two pairs over my tokens
+#pragma unroll
+            for (int j = 1; j < TOK; ++j) { th[j][0] += th[j - 1][0]; th[j][1] += th[j - 1][1]; }
+            if (own)
+                *reinterpret_cast<float2*>(partPh + part * (DK / 2) + c0 / 2) =
+                    make_float2(th[TOK - 1][0], th[TOK - 1][1]);
+        }
         if (own) {
             *reinterpret_cast<float4*>(partL + part * DK + c0) = make_float4(lp[0], lp[1], lp[2], lp[3]);
             *reinterpret_cast<int4*>(partPZ + part * DK + c0) = make_int4(pz[0], pz[1], pz[2], pz[3]);
@@ -277,6 +303,15 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
             if (p < part) { offL[x] += lv[x]; offPZ[x] = (((offPZ[x] >> 1) + (zv[x] >> 1)) << 1) | ((offPZ[x] ^ zv[x]) & 1); }
             totL[x] += lv[x];
             totPZ[x] = (((totPZ[x] >> 1) + (zv[x] >> 1)) << 1) | ((totPZ[x] ^ zv[x]) & 1);
+        }
+    }
+    float offPh[2] = {0.f, 0.f}, totPh[2] = {0.f, 0.f};     // (PH) phases before my range, in the chunk
+    if constexpr (PH) {
+        for (int p = 0; p < PARTS; ++p) {
+            const float2 t2 = *reinterpret_cast<const float2*>(partPh + p * (DK / 2) + c0 / 2);
+            if (p < part) { offPh[0] += t2.x; offPh[1] += t2.y; }
+            totPh[0] += t2.x;
+            totPh[1] += t2.y;
         }
     }
     int Ztot = 0;
@@ -324,6 +359,28 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
         return;
     }
     if (tid == 0) args.FL[unit] = 0;
+
+    if constexpr (PH) {
+        // k_r, q_r <- R(-phi_r) k_r, R(-phi_r) q_r per channel pair
+#pragma unroll
+        for (int j = 0; j < TOK; ++j) {
+            float kf[4], qf[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) { kf[x] = kv[j].get(x); qf[x] = qv[j].get(x); }
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+                float sn, cs;
+                __sincosf(offPh[pp] + th[j][pp], &sn, &cs);
+                const float k0 = kf[2 * pp], k1 = kf[2 * pp + 1], q0 = qf[2 * pp], q1 = qf[2 * pp + 1];
+                kf[2 * pp] = cs * k0 + sn * k1;
+                kf[2 * pp + 1] = cs * k1 - sn * k0;
+                qf[2 * pp] = cs * q0 + sn * q1;
+                qf[2 * pp + 1] = cs * q1 - sn * q0;
+            }
+            kv[j] = Vec4<T>::from(kf);
+            qv[j] = Vec4<T>::from(qf);
+        }
+    }
 
     // ---- factored operands (LDS), Q*Gamma (staged), Ktil (direct) ---------------
     const int KP = ((DK + Ztot + KB - 1) / KB) * KB;     // contraction length
@@ -392,6 +449,20 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
         }
     }
     if (own) {
+        float ce[2] = {1.f, 1.f}, se[2] = {0.f, 0.f};     // (PH) cos, sin of phi_{C-1}
+        if constexpr (PH) {
+            // Ktil_i = |rho(C-1, i)| R(phi_{C-1}) R(-phi_i) k_i: rotate back
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) __sincosf(totPh[pp], &se[pp], &ce[pp]);
+#pragma unroll
+            for (int j = 0; j < TOK; ++j)
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp) {
+                    const float x0 = kt[j][2 * pp], x1 = kt[j][2 * pp + 1];
+                    kt[j][2 * pp] = ce[pp] * x0 - se[pp] * x1;
+                    kt[j][2 * pp + 1] = se[pp] * x0 + ce[pp] * x1;
+                }
+        }
         // Ktil: A operand with rows = channels, k = tokens; 4 consecutive tokens
         // starting at a multiple of 4 are 4 consecutive slots of one fragment
         if constexpr (TOK % 4 == 0) {
@@ -415,6 +486,15 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
 #pragma unroll
             for (int x = 0; x < 4; ++x)
                 g4[x] = (totPZ[x] >> 1) == 0 ? ((totPZ[x] & 1) ? -1.f : 1.f) * E[x] * E[x] : 0.f;
+            if constexpr (PH) {
+                // Gamma_{C-1} of pair p as (|Gamma| cos phi, |Gamma| sin phi)
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp) {
+                    const float gm = g4[2 * pp];
+                    g4[2 * pp] = gm * ce[pp];
+                    g4[2 * pp + 1] = gm * se[pp];
+                }
+            }
             *reinterpret_cast<float4*>(args.GC + (size_t)unit * DK + c0) = make_float4(g4[0], g4[1], g4[2], g4[3]);
         }
     }
@@ -616,8 +696,13 @@ template <typename T, int C, int DK>
 hipError_t launch_fast_t(const ChunkShape& s, const PrepArgs& a, hipStream_t stream)
 {
     const FastLayout<T, C, DK> LY(a.zx);
-    auto kern = a.zx > 0 ? (a.pro ? prep_fast_kernel<T, C, DK, true, true> : prep_fast_kernel<T, C, DK, true, false>)
-                         : (a.pro ? prep_fast_kernel<T, C, DK, false, true> : prep_fast_kernel<T, C, DK, false, false>);
+    // (the input parameterisation and the phase variant are not combined)
+    auto kern = a.theta ? (a.zx > 0 ? prep_fast_kernel<T, C, DK, true, false, true>
+                                    : prep_fast_kernel<T, C, DK, false, false, true>)
+              : a.zx > 0 ? (a.pro ? prep_fast_kernel<T, C, DK, true, true, false>
+                                  : prep_fast_kernel<T, C, DK, true, false, false>)
+                         : (a.pro ? prep_fast_kernel<T, C, DK, false, true, false>
+                                  : prep_fast_kernel<T, C, DK, false, false, false>);
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              (int)LY.total);

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 4
+#define KDA_ABI_VERSION 5
 
 typedef enum {
     KDA_OK = 0,
@@ -183,6 +183,27 @@ kda_status_t kda_chunk_forward_prologue(const void* q_raw, const void* k_raw, co
                                         void* stream);
 
 /*
+ * Phase variant ("Semidirect Fourier Delta Attention", §3 eq. (13) in the real
+ * form of eq. (2) with the 2x2 rotation blocks of eq. (12)): channels 2p and
+ * 2p+1 form one complex coordinate and the decay is
+ *   Lambda_t = diag(alpha_t e^{i theta_t}), i.e. the block alpha_p R(theta_p),
+ *   R(t) = [[cos t, -sin t], [sin t, cos t]], on state rows 2p, 2p+1;
+ * the delta correction and the read-out are those of kda_chunk_forward
+ * (theta = 0 is KDA; beta = 0 the rotating diagonal recurrence, Prop. 2.1).
+ *   alpha, theta : [B,T,H,Dk/2] fp32, one decay and one phase (radians) per
+ *                  channel pair; alpha follows the mode's gate range.
+ * Every other argument, rule and error is that of kda_chunk_forward (the
+ * workspace query is the same); theta == NULL with T > 0 is
+ * KDA_ERR_NULL_POINTER.
+ */
+kda_status_t kda_chunk_forward_phase(const void* q, const void* k, const void* v,
+                                     const float* alpha, const float* theta, const float* beta,
+                                     const float* initial_state, void* out, float* final_state,
+                                     int B, int T, int H, int Dk, int Dv, int chunk,
+                                     kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Packed (variable-length) batches: N sequences stored back to back, sequence
  * i on token rows cu_seqlens[i] .. cu_seqlens[i+1] - 1 of q, k, alpha
  * [total_T,H,Dk], v, out [total_T,H,Dv] and beta [total_T,H]; every sequence
@@ -228,6 +249,18 @@ kda_status_t kda_decode_step(const void* q, const void* k, const void* v,
                              int B, int H, int Dk, int Dv,
                              kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
                              void* stream);
+
+/*
+ * kda_decode_step for the phase variant (see kda_chunk_forward_phase):
+ * alpha, theta : [B,H,Dk/2] fp32, one per channel pair; S <- (I - beta k k^T)
+ * Lambda S + beta k v^T with Lambda's 2x2 blocks on row pairs, out = S^T q.
+ */
+kda_status_t kda_decode_step_phase(const void* q, const void* k, const void* v,
+                                   const float* alpha, const float* theta, const float* beta,
+                                   float* state, void* out,
+                                   int B, int H, int Dk, int Dv,
+                                   kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
+                                   void* stream);
 
 /*
  * Chunk-local gate summary (log-magnitude, sign and zero form of the

@@ -32,14 +32,15 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     syms = declared_symbols()
-    assert {"kda_chunk_forward", "kda_chunk_forward_states", "kda_chunk_forward_prologue", "kda_decode_step", "kda_chunk_forward_workspace_size",
+    assert {"kda_chunk_forward", "kda_chunk_forward_states", "kda_chunk_forward_prologue",
+            "kda_chunk_forward_phase", "kda_decode_step_phase", "kda_chunk_forward_varlen", "kda_decode_step", "kda_chunk_forward_workspace_size",
             "kda_gate_prep", "kda_status_string", "kda_abi_version"} <= set(syms)
     for s in syms:
         assert hasattr(lib, s), s
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 4
+    assert lib.kda_abi_version() == 5
     for s in range(8):
         assert lib.kda_status_string(s)
     assert lib.kda_status_string(99) == b"unknown status"
@@ -192,6 +193,20 @@ def test_varlen_workspace_and_validation(lib):
     assert vl(q=False) == NULLP
     assert vl(N=0) == SHAPE
     assert vl(total=-1) == SHAPE
+
+
+def test_phase_validation(lib):
+    f = Fake()
+    st, need = ws_size(lib, 1, 64, 2, 16, 16, 16, F32)
+    call = lambda theta, out=None: lib.kda_chunk_forward_phase(
+        f(), f(), f(), f(), theta, f(), None, out or f(), None, 1, 64, 2, 16, 16, 16, F32, 1, 0,
+        f(need + 4096), need, None)
+    assert call(None) == NULLP
+    assert call(ctypes.c_void_p(0x7f0000000004)) == MISAL            # pairs of floats: 8-byte rule
+    base = f(1 << 20)
+    assert call(ctypes.c_void_p(base.value + 16), out=base) == ALIAS     # out overlapping theta
+    assert lib.kda_decode_step_phase(f(), f(), f(), f(), None, f(), f(), f(), 1, 1, 16, 16, F32,
+                                     1, 0, None) == NULLP
 
 
 def test_decode_validation(lib):

@@ -233,6 +233,83 @@ def test_forward_varlen_prologue():
     assert worst <= 2e-2
 
 
+# (name, base workload, overrides, theta_max)
+PHASE = [
+    ("f32_kda_d32_c32_T67", 0, dict(B=1, H=3, T=67, D=32, chunk=32), 3.0),
+    ("f32_ckda_d64_c16_T130_s0", 1, dict(B=2, H=1, T=130, D=64, chunk=16, s0_std=0.3), 1.0),
+    ("bf16_kda_d128_c64_T300_s0", 2, dict(B=1, H=2, T=300, chunk=64, s0_std=0.1), 3.0),
+    ("bf16_ckda_d128_c64_T200", 3, dict(B=1, H=2, T=200, chunk=64), 0.5),
+    ("bf16_kda_d64_c32_T96", 2, dict(B=2, H=2, T=96, D=64, chunk=32), 0.1),
+]
+
+
+@pytest.mark.parametrize("name,base,ov,tmax", PHASE, ids=[c[0] for c in PHASE])
+def test_forward_phase(name, base, ov, tmax):
+    """kda_chunk_forward_phase against the oracle's phase-variant recurrence
+    (gates and phases per channel pair; CKDA cases include exact 0 and -1
+    gates, so zero-segment columns and the exact kernel are exercised)."""
+    w = workloads.workload(base, **ov)
+    say(f"[forward phase] {name}: {w} theta_max {tmax}")
+    inp = workloads.make_prefill_phase(w, theta_max=tmax)
+    o_ref, s_ref = oracle.forward_phase(
+        np32(inp["q"]), np32(inp["k"]), np32(inp["v"]), np32(inp["alpha"]), np32(inp["theta"]),
+        np32(inp["beta"]), None if inp["S0"] is None else np32(inp["S0"]), nthreads=oracle_threads())
+    d = to_dev(inp)
+    out, st = kda.chunk_forward_phase(d["q"], d["k"], d["v"], d["alpha"], d["theta"], d["beta"],
+                                      d["S0"], chunk=w.chunk, mode=w.mode)
+    torch.cuda.synchronize()
+    eo, es = slice_err_out(np32(out), o_ref), slice_err_state(np32(st), s_ref)
+    say(f"  err out {eo:.3e} state {es:.3e}")
+    assert eo <= TOL[w.dtype] and es <= TOL[w.dtype]
+
+
+def test_forward_phase_zero_is_kda_bitwise():
+    """theta = 0 makes every rotation the identity (sin 0 = 0, cos 0 = 1
+    exactly), so the phase path gives bit for bit the plain path with each
+    pair's gate on both of its channels."""
+    w = workloads.workload(2, B=1, H=2, T=150, chunk=64, s0_std=0.2)
+    say(f"[forward phase] theta = 0 vs plain {w}")
+    d = to_dev(workloads.make_prefill_phase(w))
+    zero = torch.zeros_like(d["theta"])
+    out1, st1 = kda.chunk_forward_phase(d["q"], d["k"], d["v"], d["alpha"], zero, d["beta"],
+                                        d["S0"], chunk=64, mode=w.mode)
+    out2, st2 = run_gpu(dict(d, alpha=d["alpha"].repeat_interleave(2, dim=-1).contiguous()), 64, w.mode)
+    torch.cuda.synchronize()
+    assert torch.equal(out1, out2) and torch.equal(st1, st2)
+
+
+@pytest.mark.parametrize("dtype,Dk,Dv", [(torch.float32, 32, 48), (torch.bfloat16, 128, 128),
+                                         (torch.bfloat16, 16, 80)])
+def test_decode_phase(dtype, Dk, Dv):
+    """kda_decode_step_phase: three steps against the oracle's phase-variant
+    recurrence on the same tokens."""
+    say(f"[decode phase] {dtype} Dk={Dk} Dv={Dv}")
+    g = torch.Generator().manual_seed(Dk + Dv)
+    B, H, N = 3, 2, 3
+    q = torch.randn(N, B, H, Dk, generator=g).to(dtype)
+    k = (torch.randn(N, B, H, Dk, generator=g) * 0.3).to(dtype)
+    v = torch.randn(N, B, H, Dv, generator=g).to(dtype)
+    a = torch.rand(N, B, H, Dk // 2, generator=g) * 0.5 + 0.5
+    th = (torch.rand(N, B, H, Dk // 2, generator=g) - 0.5) * 6.0
+    b = torch.rand(N, B, H, generator=g)
+    S0 = torch.randn(B, H, Dk, Dv, generator=g) * 0.2
+    S = S0.to(DEV).contiguous()
+    outs = []
+    for t in range(N):
+        outs.append(kda.decode_step_phase(q[t].to(DEV).contiguous(), k[t].to(DEV).contiguous(),
+                                          v[t].to(DEV).contiguous(), a[t].to(DEV).contiguous(),
+                                          th[t].to(DEV).contiguous(), b[t].to(DEV).contiguous(), S,
+                                          mode=workloads.CKDA))
+    torch.cuda.synchronize()
+    perm = lambda x: np32(x.permute(1, 0, *range(2, x.dim())))        # [N,B,...] -> [B,N,...]
+    o_ref, s_ref = oracle.forward_phase(perm(q), perm(k), perm(v), perm(a), perm(th), perm(b),
+                                        np32(S0))
+    o_gpu = np.stack([np32(o) for o in outs], axis=1)
+    eo, es = slice_err_out(o_gpu, o_ref), slice_err_state(np32(S), s_ref)
+    say(f"  err out {eo:.3e} state {es:.3e}")
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
 def test_forward_cfg2_full():
     """KDA bf16 prefill, B=1 H=32 T=8192 d=128 chunk=64, every head."""
     w = workloads.workload(2)

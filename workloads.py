@@ -170,6 +170,19 @@ def make_varlen(w: Workload, lengths, device="cpu", seed: int | None = None):
     return inp
 
 
+def make_prefill_phase(w: Workload, theta_max: float = 3.0, device="cpu", seed: int | None = None):
+    """Inputs of the phase variant: those of make_prefill, except alpha, now
+    one gate per channel pair [B,T,H,D/2] (drawn like make_prefill's gates),
+    plus phases theta = theta_max * tanh(x), x ~ N(0,1), [B,T,H,D/2] fp32."""
+    inp = make_prefill(w, device=device, seed=seed)
+    g = _gen((w.seed if seed is None else seed) + 2000, device)
+    B, T, H, D = w.B, w.T, w.H, w.D
+    inp["alpha"] = _gates((B, T, H, D // 2), w.mode, g, device)
+    inp["theta"] = (theta_max * torch.tanh(torch.randn((B, T, H, D // 2), generator=g,
+                                                       device=device, dtype=torch.float32))).contiguous()
+    return inp
+
+
 def make_decode(w: Workload, steps: int | None = None, device="cpu", seed: int | None = None):
     """Inputs for stacked decode steps: S0 [B,H,D,D] fp32, then per step
     q, k, v [N,B,H,D] (w.dtype), alpha [N,B,H,D] fp32, beta [N,B,H] fp32."""
