@@ -84,7 +84,7 @@ def chunk_flops(w):
     return w.B * w.T * w.H * per_tok
 
 
-def time_forward(kda, torch, w, inp, steps, warmup):
+def time_forward(kda, torch, w, inp, steps, warmup, extra_flags=0):
     stream = torch.cuda.current_stream()
     ws = torch.empty(kda.workspace_size(w.B, w.T, w.H, w.Dk, w.Dv, w.chunk, w.dtype),
                      dtype=torch.uint8, device="cuda")
@@ -94,7 +94,7 @@ def time_forward(kda, torch, w, inp, steps, warmup):
     def call(flags=0):
         kda.chunk_forward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["S0"],
                           chunk=w.chunk, mode=w.mode, out=out, final_state=st, workspace=ws,
-                          stream=stream, flags=flags)
+                          stream=stream, flags=flags | extra_flags)
 
     for _ in range(warmup):
         call()
@@ -174,8 +174,8 @@ def decode_bench(kda, torch, workloads, steps_cap=None):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-others", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-probe", action="store_true",
@@ -238,6 +238,14 @@ def main():
                                "path_hbm_frac": abo["path"] / (mso / 1e3) / 1e9 / HBM_PEAK_GBS,
                                "kernels_ms": pero}
             del io
+        # few heads, long context: sequence segments against one chain per head
+        wo = workloads.workload(3, H=2)
+        io = workloads.make_prefill(wo, device="cuda")
+        for tag, fl in (("segments", 0), ("no_segments", kda.NO_SEGMENTS)):
+            mso, pero, _, _ = time_forward(kda, torch, wo, io, 20, 2, fl)
+            others[f"ckda_bf16_long_ctx_H2_{tag}"] = {"ms": mso, "tokens_per_s": wo.B * wo.T / (mso / 1e3),
+                                                     "kernels_ms": pero}
+        del io
         others["ckda_bf16_decode"] = decode_bench(kda, torch, workloads)
         line["others"] = others
     if args.copy_probe:

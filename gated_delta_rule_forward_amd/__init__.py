@@ -21,11 +21,12 @@ __all__ = [
     "KDA", "CKDA", "KdaError", "library_path", "load", "abi_version", "workspace_size",
     "chunk_forward", "chunk_forward_prologue", "chunk_forward_varlen", "chunk_forward_phase",
     "decode_step", "decode_step_phase", "gate_prep", "last_stage_times",
-    "STAGE_EVENTS",
+    "STAGE_EVENTS", "NO_SEGMENTS",
 ]
 
 KDA, CKDA = 0, 1
 STAGE_EVENTS = 2
+NO_SEGMENTS = 4        # KDA_FLAG_NO_SEGMENTS
 _DT = {torch.float32: 0, torch.bfloat16: 1}
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkda.so")

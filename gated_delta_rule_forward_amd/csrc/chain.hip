@@ -255,13 +255,25 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
 
     const int Dv = a.Dv, H = a.H;
     const int NS = Dv / 16;
+    const bool summary = a.summ != nullptr;
+    const int nseg = a.nseg > 1 ? a.nseg : 1;
+    const int NSX = summary ? DK / 16 + NS : NS;           // column slices per chain
     const int g = blockIdx.x, xcd = g % kXcds, jx = g / kXcds;
-    const int bh = (jx / NS) * kXcds + xcd, slice = jx % NS;
-    if (bh >= a.B * H) return;
+    const int vb = (jx / NSX) * kXcds + xcd, xslice = jx % NSX;
+    if (vb >= a.B * H * nseg) return;
+    const int bh = vb / nseg, sg = vb % nseg;
+    if (summary && sg == nseg - 1) return;        // the last segment's map is never used
     const int h = bh % H;
-    // this (sequence, head): chunk count, first token row, length, first unit
+    // summary pass: slices below DK / 16 carry the homogeneous part (columns of
+    // the identity, U taken as zero), the others the particular part
+    const bool xpart = summary && xslice < DK / 16;
+    const int slice = summary ? (xpart ? 0 : xslice - DK / 16) : xslice;   // U / column slice
+    // this (sequence, head): chunk count, first token row, length, first unit;
+    // a segment is chunks [c0, c0 + NC) of it
     const SeqPos sp = locate_seq(bh, H, a.T, a.NC, a.cu, a.cs);
-    const int NC = sp.nc, T_ = sp.len;
+    const int c0 = nseg > 1 ? sg * a.seg : 0;
+    const int NC = nseg > 1 ? min(a.seg, sp.nc - c0) : sp.nc;
+    const int T_ = sp.len - c0 * C;
     const int tid = threadIdx.x, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = slice * 16 + ln;
@@ -274,7 +286,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
     // of step c - 1, and stage c & 1 is free again after barrier 2 of step
     // c - 1.  Past the last chunk the last one is re-read, so every step
     // issues the same NDMA loads per loader.
-    const size_t u0 = sp.ubase;
+    const size_t u0 = sp.ubase + c0;
     const int last = NC - 1;
     if (NC == 0) {
         // an empty sequence of a packed batch: the state passes through
@@ -326,12 +338,19 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
     }
 
     f32x4 S[G::SPW];
+    // initial state: S0 (or the segment's start state), the identity columns of
+    // a homogeneous summary slice, or zero
+    const float* sinit = summary ? nullptr
+                       : (sg > 0 ? a.Sseg + (size_t)(bh * nseg + sg) * DK * Dv : (a.S0 ? a.S0 + (size_t)bh * DK * Dv : nullptr));
 #pragma unroll
     for (int u = 0; u < G::SPW; ++u) {
         const int t = wave + 4 * u;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            S[u][i] = (a.S0 && t < G::NT) ? a.S0[((size_t)bh * DK + 16 * t + 4 * lg + i) * Dv + col] : 0.f;
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * t + 4 * lg + i;
+            S[u][i] = xpart ? (row == 16 * xslice + ln ? 1.f : 0.f)
+                            : ((sinit && t < G::NT) ? sinit[(size_t)row * Dv + col] : 0.f);
+        }
         if (t < G::NT) put_tile<T, G::KB>(sSf, t, lane, S[u]);
     }
 
@@ -342,12 +361,12 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
 
     T* out = static_cast<T*>(a.out);
     const size_t ostride = (size_t)H * Dv;                      // one token
-    T* obase = out + (((size_t)sp.row0 + 16 * wave + 4 * lg) * H + h) * Dv + col;
+    T* obase = out + (((size_t)sp.row0 + (size_t)c0 * C + 16 * wave + 4 * lg) * H + h) * Dv + col;
     // outputs of chunk n: O = (Q * Gamma) S_n + P Delta_n (off the state's
     // critical path, so computed during the next chunk's first phase)
     F pqg[G::NKD], pp[G::NKC], psf[G::NKD], pdf[G::NKC];
     auto emit = [&](int n) {
-        if (G::NM == 4 || wave < G::NM) {
+        if (!summary && (G::NM == 4 || wave < G::NM)) {
             f32x4 acc = zero4();
 #pragma unroll
             for (int s = 0; s < G::NKD; ++s) acc = mma(pqg[s], psf[s], acc);
@@ -368,7 +387,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
     for (int nc = 0; nc < NC; ++nc) {
         if (a.CS) {
             // the state entering chunk nc (this wave's tiles, rounded to T)
-            T* cs = static_cast<T*>(a.CS) + ((size_t)bh * NC + nc) * DK * Dv + col;
+            T* cs = static_cast<T*>(a.CS) + ((size_t)bh * sp.nc + c0 + nc) * DK * Dv + col;
 #pragma unroll
             for (int u = 0; u < G::SPW; ++u) {
                 const int t = wave + 4 * u;
@@ -390,7 +409,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
             for (int s = 0; s < G::NKD; ++s) acc = mma(cur.w[s], sf[s], acc);
             f32x4 dl;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dl[i] = cur.u[i] - acc[i];
+            for (int i = 0; i < 4; ++i) dl[i] = (xpart ? 0.f : cur.u[i]) - acc[i];
             put_tile<T, G::KB>(sDf, wave, lane, dl);
         }
         lds_barrier();
@@ -432,7 +451,18 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
     }
     emit(NC - 1);
 
-    if (a.ST) {
+    if (summary) {
+        // this slice's columns of [X_g | Y_g]
+        float* dst = a.summ + (size_t)(bh * nseg + sg) * DK * (DK + Dv) + 16 * xslice + ln;
+#pragma unroll
+        for (int u = 0; u < G::SPW; ++u) {
+            const int t = wave + 4 * u;
+            if (t < G::NT) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[(size_t)(16 * t + 4 * lg + i) * (DK + Dv)] = S[u][i];
+            }
+        }
+    } else if (a.ST && sg == nseg - 1) {
 #pragma unroll
         for (int u = 0; u < G::SPW; ++u) {
             const int t = wave + 4 * u;
@@ -445,6 +475,86 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
     }
 }
 
+// Segment start states: S_0 = S0 (or zero), S_{g+1} = X_g S_g + Y_g in fp32
+// ("Semidirect Fourier Delta Attention", §2.2 eq. (10): affine maps compose).
+// One workgroup per (b, h, 16-column slice).  The slice of S_g stays in LDS,
+// transposed, as the B operand of fp32 MFMA tiles (16 x 16 x 4); wavefront w
+// takes row tiles w, w + 4, .. of X_g S_g, reading X_g straight from memory as
+// the A operand (each element once per step) and starting from Y_g.
+template <int DK>
+__global__ __launch_bounds__(256) void segment_combine_kernel(const float* __restrict__ S0,
+                                                              const float* __restrict__ summ,
+                                                              float* __restrict__ Sseg, int BH,
+                                                              int nseg, int Dv)
+{
+    constexpr int LD = DK + 4;
+    __shared__ __attribute__((aligned(16))) float sT[16 * LD];     // S_g^T: [column][row]
+    const int NS = Dv / 16;
+    const int bh = blockIdx.x / NS, slice = blockIdx.x % NS;
+    if (bh >= BH) return;
+    const int tid = threadIdx.x, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    const int wave = tid >> 6;
+    for (int idx = tid; idx < DK * 16; idx += 256) {
+        const int r = idx / 16, j = idx % 16;
+        sT[j * LD + r] = S0 ? S0[((size_t)bh * DK + r) * Dv + slice * 16 + j] : 0.f;
+    }
+    __syncthreads();
+    constexpr int NT = DK / 16, TPW = (NT + 3) / 4;     // row tiles, per wavefront
+    constexpr int NK = DK / 16;                          // k16 blocks
+    // the operands of map gi: X_g rows of this wavefront's tiles (A fragments)
+    // and Y_g's tile entries; the next map's are loaded during this product
+    Vec4<float> xa[TPW][NK];
+    f32x4 ya[TPW];
+    auto load_ops = [&](int gi) {
+        const float* xg = summ + (size_t)(bh * nseg + gi) * DK * (DK + Dv);
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            const int mt = min(wave + 4 * u, NT - 1);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                ya[u][i] = xg[(size_t)(16 * mt + 4 * lg + i) * (DK + Dv) + DK + slice * 16 + ln];
+            const float* xr = xg + (size_t)(16 * mt + ln) * (DK + Dv) + 4 * lg;
+#pragma unroll
+            for (int kb = 0; kb < NK; ++kb) xa[u][kb] = Vec4<float>::load(xr + 16 * kb);
+        }
+    };
+    if (nseg > 1) load_ops(0);
+    for (int gi = 0; gi + 1 < nseg; ++gi) {
+        f32x4 acc[TPW];
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            acc[u] = ya[u];
+#pragma unroll
+            for (int kb = 0; kb < NK; ++kb)
+                acc[u] = mma_k16(xa[u][kb], Vec4<float>::load(sT + ln * LD + 16 * kb + 4 * lg), acc[u]);
+        }
+        if (gi + 2 < nseg) load_ops(gi + 1);
+        __syncthreads();
+        float* dst = Sseg + (size_t)(bh * nseg + gi + 1) * DK * Dv + slice * 16 + ln;
+#pragma unroll
+        for (int u = 0; u < TPW; ++u) {
+            const int mt = wave + 4 * u;
+            if (mt < NT) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * mt + 4 * lg + i;
+                    sT[ln * LD + r] = acc[u][i];
+                    dst[(size_t)r * Dv] = acc[u][i];
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+template <int DK>
+hipError_t launch_combine_t(int BH, int Dv, int nseg, const float* S0, const float* summ,
+                            float* Sseg, hipStream_t stream)
+{
+    return launch_kernel(segment_combine_kernel<DK>, dim3((unsigned)(BH * (Dv / 16))), dim3(256),
+                         0, stream, S0, summ, Sseg, BH, nseg, Dv);
+}
+
 template <typename T, int C, int DK>
 hipError_t launch_chain_t(const ChunkShape& s, const ChainArgs& a, hipStream_t stream)
 {
@@ -453,8 +563,8 @@ hipError_t launch_chain_t(const ChunkShape& s, const ChainArgs& a, hipStream_t s
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)G::LDS_TOTAL);
     if (e != hipSuccess) return e;
-    const int NS = s.Dv / 16;
-    const int bh = s.B * s.H;
+    const int NS = a.summ ? DK / 16 + s.Dv / 16 : s.Dv / 16;
+    const int bh = s.B * s.H * (a.nseg > 1 ? a.nseg : 1);
     const unsigned grid = (unsigned)(kXcds * NS * ((bh + kXcds - 1) / kXcds));
     return launch_kernel(kern, dim3(grid), dim3(kChainThreads), (uint32_t)G::LDS_TOTAL, stream, a);
 }
@@ -485,6 +595,18 @@ hipError_t dispatch_c(const ChunkShape& s, const ChainArgs& a, hipStream_t st)
 }
 
 }  // namespace
+
+hipError_t launch_segment_combine(int BH, int Dk, int Dv, int nseg, const float* S0,
+                                  const float* summ, float* Sseg, hipStream_t stream)
+{
+    switch (Dk) {
+    case 16: return launch_combine_t<16>(BH, Dv, nseg, S0, summ, Sseg, stream);
+    case 32: return launch_combine_t<32>(BH, Dv, nseg, S0, summ, Sseg, stream);
+    case 64: return launch_combine_t<64>(BH, Dv, nseg, S0, summ, Sseg, stream);
+    case 128: return launch_combine_t<128>(BH, Dv, nseg, S0, summ, Sseg, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
 
 hipError_t launch_chain(IoType io, const ChunkShape& s, const ChainArgs& a, hipStream_t stream)
 {

@@ -21,7 +21,7 @@ using kda::ChunkShape;
 using kda::ChunkWorkspace;
 using kda::IoType;
 
-constexpr unsigned kKnownFlags = KDA_FLAG_STAGE_EVENTS;
+constexpr unsigned kKnownFlags = KDA_FLAG_STAGE_EVENTS | KDA_FLAG_NO_SEGMENTS;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 bool aligned16(const void* p) { return aligned(p, 16); }
@@ -107,6 +107,44 @@ kda_status_t check_forward_shape(int B, int T, int H, int Dk, int Dv, int chunk,
 ChunkShape make_shape(int B, int T, int H, int Dk, int Dv, int chunk)
 {
     return ChunkShape{B, T, H, Dk, Dv, chunk, (T + chunk - 1) / chunk};
+}
+
+// Sequence segments for a dense forward whose chains leave most of the GPU
+// idle: with few (b, h, column slice) chains and many chunks, each (b, h) is
+// cut into nseg segments that run side by side (a summary pass computes each
+// segment's affine map, a short fp32 pass chains the segment start states,
+// then every segment runs the normal chain from its own start).  nseg <= 1:
+// no segments.  The summary pass must fit one round of workgroups.
+struct Segments { int nseg, seg; };
+Segments segments_for(int B, int H, int Dk, int Dv, int NC)
+{
+    const long long chains = (long long)B * H * (Dv / 16);
+    if (chains > 64 || NC < 128) return {1, NC};
+    const long long per = (long long)B * H * ((Dk + Dv) / 16);   // summary workgroups per segment
+    long long g = 256 / per;
+    if (g > NC / 32) g = NC / 32;
+    if (g < 2) return {1, NC};
+    const int seg = (int)((NC + g - 1) / g);
+    return {(NC + seg - 1) / seg, seg};
+}
+
+// workspace of a dense forward: the per-unit regions, then (with segments)
+// the segment maps [B H][nseg][Dk][Dk + Dv] and start states [B H][nseg][Dk][Dv]
+size_t dense_layout(int B, int T, int H, int Dk, int Dv, int chunk, IoType io,
+                    size_t off[kda::kWorkspaceRegions], size_t* summ_off, size_t* sseg_off)
+{
+    const ChunkShape sh = make_shape(B, T, H, Dk, Dv, chunk);
+    size_t n = kda::chunk_workspace_layout(sh, io, off);
+    const Segments sgm = segments_for(B, H, Dk, Dv, sh.NC);
+    *summ_off = *sseg_off = 0;
+    if (sgm.nseg > 1) {
+        const size_t bhs = (size_t)B * H * sgm.nseg;
+        *summ_off = n;
+        n += (bhs * Dk * (Dk + Dv) * 4 + 255) & ~size_t(255);
+        *sseg_off = n;
+        n += (bhs * Dk * Dv * 4 + 255) & ~size_t(255);
+    }
+    return n;
 }
 
 // prologue parameters inside the mode's ranges (KDA: gates in [0, 1], beta in
@@ -222,9 +260,18 @@ kda_status_t chunk_forward(const void* q, const void* k, const void* v, const fl
                            pro ? pro->eps : 0.f,
                            pro ? pro->normalize_q : 0,
                            nullptr, nullptr, 0, theta};
+    const Segments sgm = (flags & KDA_FLAG_NO_SEGMENTS) ? Segments{1, sh.NC}
+                                                          : segments_for(B, H, Dk, Dv, sh.NC);
+    size_t so = 0, ss = 0;
+    if (sgm.nseg > 1) {
+        size_t off2[kda::kWorkspaceRegions];
+        dense_layout(B, T, H, Dk, Dv, chunk, io, off2, &so, &ss);
+    }
+    float* summ = sgm.nseg > 1 ? reinterpret_cast<float*>(w + so) : nullptr;
+    float* sseg = sgm.nseg > 1 ? reinterpret_cast<float*>(w + ss) : nullptr;
     const kda::ChainArgs ca{ws.W, ws.U, ws.Kt, ws.QG, ws.P, ws.GC, initial_state, out,
                             final_state, chunk_states, B, T, H, Dv, sh.NC, nullptr, nullptr,
-                            theta ? 1 : 0};
+                            theta ? 1 : 0, sgm.seg, sgm.nseg, nullptr, sseg};
 
     if (rec.mark("prep_fast") != hipSuccess) return KDA_ERR_HIP;
     if (kda::launch_prep_fast(io, sh, pa, s) != hipSuccess) return KDA_ERR_HIP;
@@ -232,6 +279,23 @@ kda_status_t chunk_forward(const void* q, const void* k, const void* v, const fl
     if (rec.mark("prep_exact") != hipSuccess) return KDA_ERR_HIP;
     if (kda::launch_prep_exact(io, sh, pa, s) != hipSuccess) return KDA_ERR_HIP;
     if (rec.done() != hipSuccess) return KDA_ERR_HIP;
+    if (sgm.nseg > 1) {
+        // segment maps, then the segment start states, then every segment
+        kda::ChainArgs cs = ca;
+        cs.S0 = nullptr;
+        cs.out = nullptr;
+        cs.ST = nullptr;
+        cs.CS = nullptr;
+        cs.summ = summ;
+        if (rec.mark("chain_summary") != hipSuccess) return KDA_ERR_HIP;
+        if (kda::launch_chain(io, sh, cs, s) != hipSuccess) return KDA_ERR_HIP;
+        if (rec.done() != hipSuccess) return KDA_ERR_HIP;
+        if (rec.mark("segment_combine") != hipSuccess) return KDA_ERR_HIP;
+        if (kda::launch_segment_combine(B * H, Dk, Dv, sgm.nseg, initial_state, summ, sseg, s) !=
+            hipSuccess)
+            return KDA_ERR_HIP;
+        if (rec.done() != hipSuccess) return KDA_ERR_HIP;
+    }
     if (rec.mark("chain") != hipSuccess) return KDA_ERR_HIP;
     if (kda::launch_chain(io, sh, ca, s) != hipSuccess) return KDA_ERR_HIP;
     if (rec.done() != hipSuccess) return KDA_ERR_HIP;
@@ -338,10 +402,10 @@ kda_status_t kda_chunk_forward_workspace_size(int B, int T, int H, int Dk, int D
     if (!bytes) return KDA_ERR_NULL_POINTER;
     const kda_status_t st = check_forward_shape(B, T, H, Dk, Dv, chunk, dtype);
     if (st != KDA_OK) return st;
-    size_t off[kda::kWorkspaceRegions];
+    size_t off[kda::kWorkspaceRegions], so, ss;
     *bytes = T == 0 ? 0
-                    : kda::chunk_workspace_layout(make_shape(B, T, H, Dk, Dv, chunk),
-                                                  dtype == KDA_DTYPE_F32 ? IoType::F32 : IoType::BF16, off);
+                    : dense_layout(B, T, H, Dk, Dv, chunk,
+                                   dtype == KDA_DTYPE_F32 ? IoType::F32 : IoType::BF16, off, &so, &ss);
     return KDA_OK;
 }
 
@@ -498,7 +562,8 @@ kda_status_t kda_chunk_forward_varlen(const void* q, const void* k, const void* 
                            prologue ? prologue->normalize_q : 0,
                            cu_s, cs, N, nullptr};
     const kda::ChainArgs ca{ws.W, ws.U, ws.Kt, ws.QG, ws.P, ws.GC, initial_state, out,
-                            final_state, nullptr, N, total_T, H, Dv, umax, cu_s, cs, 0};
+                            final_state, nullptr, N, total_T, H, Dv, umax, cu_s, cs, 0,
+                            0, 1, nullptr, nullptr};
     if (rec.mark("prep_fast") != hipSuccess) return KDA_ERR_HIP;
     if (kda::launch_prep_fast(io, shp, pa, s) != hipSuccess) return KDA_ERR_HIP;
     if (rec.done() != hipSuccess) return KDA_ERR_HIP;

@@ -206,6 +206,15 @@ struct ChainArgs {
     const int* cu;     // packed batches (B = number of sequences): see PrepArgs
     const int* cs;
     int ph;            // GC holds (magnitude cos, magnitude sin) per channel pair
+    // sequence segments (dense batches): nseg segments of seg chunks per (b, h).
+    // summ != null: summary pass, segment g's affine map S -> X_g S + Y_g into
+    // summ [B H][nseg][Dk][Dk + Dv] (column slices 0 .. Dk/16 - 1 carry X from
+    // the identity with U = 0, the rest carry Y from zero), no outputs.
+    // Otherwise with nseg > 1: segment g starts from Sseg [B H][nseg][Dk][Dv]
+    // (g = 0: S0) and only the last segment writes ST.
+    int seg, nseg;
+    float* summ;
+    const float* Sseg;
 };
 
 // Where one unit (one chunk of one sequence and head) lives.  Dense batches:

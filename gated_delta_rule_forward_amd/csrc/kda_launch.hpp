@@ -59,6 +59,8 @@ size_t prep_fast_lds_bytes(IoType io, int C, int Dk, int zx);
 hipError_t launch_prep_fast(IoType io, const ChunkShape& s, const PrepArgs& a, hipStream_t stream);
 hipError_t launch_prep_exact(IoType io, const ChunkShape& s, const PrepArgs& a, hipStream_t stream);
 hipError_t launch_chain(IoType io, const ChunkShape& s, const ChainArgs& a, hipStream_t stream);
+hipError_t launch_segment_combine(int BH, int Dk, int Dv, int nseg, const float* S0,
+                                  const float* summ, float* Sseg, hipStream_t stream);
 
 hipError_t launch_state_copy(const float* S0, float* ST, size_t n, hipStream_t stream);
 hipError_t launch_varlen_table(const int* cu, int N, int total_T, int C, int umax, int* cu_s,

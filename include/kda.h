@@ -73,6 +73,14 @@ typedef enum { KDA_MODE_KDA = 0, KDA_MODE_CKDA = 1 } kda_mode_t;
  * and end) so that kda_last_stage_times() can report per-kernel durations;
  * performs no extra work on the data. */
 #define KDA_FLAG_STAGE_EVENTS 2u
+/* flags: never cut a sequence into segments.  By default a dense forward whose
+ * (b, h, 16-column) chains would leave most of the GPU idle (at most 64 of
+ * them) and that has at least 128 chunks runs each (b, h) as several segments
+ * side by side: each segment's affine map is computed ("Semidirect Fourier
+ * Delta Attention" §2.2 eq. (10): affine maps compose), the segment start
+ * states are chained in fp32, and every segment then runs from its own start.
+ * The results agree with the unsegmented path up to rounding. */
+#define KDA_FLAG_NO_SEGMENTS 4u
 
 /* ABI version of the loaded library (KDA_ABI_VERSION it was built with). */
 int kda_abi_version(void);

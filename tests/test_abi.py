@@ -95,6 +95,19 @@ def fwd(lib, **kw):
                                  None)
 
 
+def test_workspace_includes_segments(lib):
+    """Few chains and many chunks: the workspace also holds the segment maps
+    and start states (here 4 segments of Dk x (Dk + Dv) and Dk x Dv fp32)."""
+    st, n = ws_size(lib, 1, 2500, 1, 32, 32, 16, F32)
+    assert st == OK
+    nu = 157
+    per_unit = 3 * 16 * 32 * 4 + 16 * 32 * 4 + 16 * 16 * 4 + 32 * 4 + 1
+    seg = 4 * 32 * 64 * 4 + 4 * 32 * 32 * 4
+    assert n >= nu * per_unit + seg
+    st2, n2 = ws_size(lib, 1, 2500, 64, 32, 32, 16, F32)          # 128 chains: no segments
+    assert n2 < 64 * nu * per_unit + 7 * 256 + 1
+
+
 def test_forward_validation(lib):
     assert fwd(lib, q=None) == NULLP
     assert fwd(lib, out=None) == NULLP

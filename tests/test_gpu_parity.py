@@ -310,6 +310,70 @@ def test_decode_phase(dtype, Dk, Dv):
     assert eo <= TOL[dtype] and es <= TOL[dtype]
 
 
+# (name, base workload, overrides, expected segments) — few chains and many
+# chunks, so the forward cuts every (b, h) into segments
+SEGMENTED = [
+    ("f32_kda_d32_c16_T2500", 0, dict(B=1, H=1, T=2500, D=32, chunk=16), 4),
+    ("bf16_ckda_d128_c64_T9000_s0", 3, dict(B=1, H=2, T=9000, chunk=64, s0_std=0.2), 4),
+]
+
+
+def _stage_names():
+    names = [n for n, _ in kda.last_stage_times()]
+    return names
+
+
+@pytest.mark.parametrize("name,base,ov,nseg", SEGMENTED, ids=[c[0] for c in SEGMENTED])
+def test_forward_segmented(name, base, ov, nseg):
+    """Sequence segments (segment maps, fp32 chaining of the segment start
+    states, then all segments side by side) against the oracle's sequential
+    recurrence; the stage list shows that the segmented path ran."""
+    w = workloads.workload(base, **ov)
+    say(f"[forward segmented] {name}: {w}")
+    inp = workloads.make_prefill(w, device="cpu")
+    o_ref, s_ref = run_oracle(inp)
+    out, st = run_gpu(to_dev(inp), w.chunk, w.mode, flags=kda.STAGE_EVENTS)
+    names = _stage_names()
+    say(f"  stages {names}")
+    assert "chain_summary" in names and "segment_combine" in names
+    eo, es = slice_err_out(np32(out), o_ref), slice_err_state(np32(st), s_ref)
+    say(f"  err out {eo:.3e} state {es:.3e}")
+    assert eo <= TOL[w.dtype] and es <= TOL[w.dtype]
+
+
+def test_forward_segmented_chunk_states_and_phase():
+    """Segments together with the chunk-start states output and with the
+    phase variant."""
+    w = workloads.workload(2, B=1, H=1, T=5000, D=64, chunk=32, s0_std=0.3)
+    say(f"[forward segmented] chunk states {w}")
+    inp = workloads.make_prefill(w, device="cpu")
+    q, k, v, a = (np32(inp[x]) for x in ("q", "k", "v", "alpha"))
+    o_ref, s_ref, cs_ref = oracle.forward(q, k, v, a, np32(inp["beta"]), np32(inp["S0"]),
+                                          nthreads=oracle_threads(), chunk=32)
+    nc = (w.T + 31) // 32
+    cs = torch.empty((1, 1, nc, 64, 64), dtype=w.dtype, device=DEV)
+    out, st = run_gpu(to_dev(inp), 32, w.mode, chunk_states=cs, flags=kda.STAGE_EVENTS)
+    assert "chain_summary" in _stage_names()
+    ec = slice_err_state(np32(cs).reshape(1, nc, 64, 64), cs_ref.reshape(1, nc, 64, 64))
+    eo, es = slice_err_out(np32(out), o_ref), slice_err_state(np32(st), s_ref)
+    say(f"  err out {eo:.3e} state {es:.3e} chunk states {ec:.3e}")
+    assert eo <= 2e-2 and es <= 2e-2 and ec <= 2e-2
+    wp = workloads.workload(1, B=1, H=1, T=3000, D=64, chunk=16, s0_std=0.3)
+    say(f"[forward segmented] phase {wp}")
+    ip = workloads.make_prefill_phase(wp, theta_max=2.0)
+    o_ref, s_ref = oracle.forward_phase(np32(ip["q"]), np32(ip["k"]), np32(ip["v"]),
+                                        np32(ip["alpha"]), np32(ip["theta"]), np32(ip["beta"]),
+                                        np32(ip["S0"]), nthreads=oracle_threads())
+    d = to_dev(ip)
+    out, st = kda.chunk_forward_phase(d["q"], d["k"], d["v"], d["alpha"], d["theta"], d["beta"],
+                                      d["S0"], chunk=16, mode=wp.mode, flags=kda.STAGE_EVENTS)
+    torch.cuda.synchronize()
+    assert "chain_summary" in _stage_names()
+    eo, es = slice_err_out(np32(out), o_ref), slice_err_state(np32(st), s_ref)
+    say(f"  err out {eo:.3e} state {es:.3e}")
+    assert eo <= 1e-4 and es <= 1e-4
+
+
 def test_forward_cfg2_full():
     """KDA bf16 prefill, B=1 H=32 T=8192 d=128 chunk=64, every head."""
     w = workloads.workload(2)
