@@ -59,6 +59,9 @@ def _load():
         lib.kda_oracle_forward_phase.argtypes = [fp, fp, fp, fp, fp, fp, fp, dp, dp,
                                                  i, i, i, i, i, i]
         lib.kda_oracle_forward_phase.restype = i
+        lib.kda_oracle_backward.argtypes = [fp, fp, fp, fp, fp, fp, fp, fp, dp, dp, dp, dp, dp,
+                                            dp, i, i, i, i, i, i]
+        lib.kda_oracle_backward.restype = i
         lib.kda_oracle_decode.argtypes = [fp, fp, fp, fp, fp, dp, dp,
                                           i, i, i, i, i, i]
         lib.kda_oracle_decode.restype = i
@@ -166,6 +169,37 @@ def forward_phase(q, k, v, alpha, theta, beta, S0=None, nthreads: int | None = N
     if rc != 0:
         raise RuntimeError("kda_oracle_forward_phase failed")
     return out, ST
+
+
+def backward(q, k, v, alpha, beta, dO, S0=None, dST=None, nthreads: int | None = None):
+    """Gradients of L = sum <out, dO> + <ST, dST> (dST None = zero) with respect
+    to q, k, v, alpha, beta and S0, by the chain rule through each token of
+    the recurrence, last token first.  Layouts as forward(); dO like out.
+    Returns a dict of float64 arrays dq, dk, dv, dalpha, dbeta, dS0."""
+    lib = _load()
+    q, k, v, alpha, beta, dO = (_f32(x) for x in (q, k, v, alpha, beta, dO))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    assert k.shape == (B, T, H, Dk) and alpha.shape == (B, T, H, Dk)
+    assert v.shape == (B, T, H, Dv) and beta.shape == (B, T, H) and dO.shape == v.shape
+    s0 = None if S0 is None else _f32(S0)
+    ds = None if dST is None else _f32(dST)
+    for x in (s0, ds):
+        if x is not None:
+            assert x.shape == (B, H, Dk, Dv)
+    r = {"dq": np.empty((B, T, H, Dk)), "dk": np.empty((B, T, H, Dk)),
+         "dv": np.empty((B, T, H, Dv)), "dalpha": np.empty((B, T, H, Dk)),
+         "dbeta": np.empty((B, T, H)), "dS0": np.empty((B, H, Dk, Dv))}
+    dp = ctypes.c_double
+    rc = lib.kda_oracle_backward(
+        _ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float),
+        _ptr(alpha, ctypes.c_float), _ptr(beta, ctypes.c_float), _ptr(s0, ctypes.c_float),
+        _ptr(dO, ctypes.c_float), _ptr(ds, ctypes.c_float),
+        _ptr(r["dq"], dp), _ptr(r["dk"], dp), _ptr(r["dv"], dp), _ptr(r["dalpha"], dp),
+        _ptr(r["dbeta"], dp), _ptr(r["dS0"], dp), B, T, H, Dk, Dv, nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError("kda_oracle_backward failed")
+    return r
 
 
 def decode(q, k, v, alpha, beta, S, nthreads: int | None = None):

@@ -225,6 +225,165 @@ int kda_oracle_forward_phase(const float* q, const float* k, const float* v,
                         Dv, nthreads);
 }
 
+/*
+ * Reverse-mode derivative of the forward above (inputs taken as given, no
+ * prologue, no phase), for the scalar loss
+ *   L = sum_t <o_t, dO_t> + <S_T, dST>
+ * so dO and dST are the loss gradients of the outputs and the final state.
+ * It is the chain rule applied to one token of eq. (1) + eq. (14) at a time,
+ * from the last token back to the first, with G the gradient of the state the
+ * token leaves behind (from later tokens and dST):
+ *   o_t = S_t^T q_t            ->  dq_t = S_t dO_t,   G += q_t dO_t^T
+ *   S_t = St + k_t delta^T,  St = diag(alpha_t) S_{t-1},
+ *         delta = beta_t u,  u = v_t - St^T k_t
+ *        y = G^T k_t          ->  dv_t = beta_t y,   dbeta_t = <u, y>
+ *                                 dk_t = G delta - beta_t St y
+ *                                 dSt  = G - beta_t k_t y^T
+ *   St = diag(alpha_t) S_{t-1} -> dalpha_t[c] = <dSt[c,:], S_{t-1}[c,:]>,
+ *                                 G_{t-1} = diag(alpha_t) dSt
+ * and dS0 is the last G.  The states S_{t-1} are recomputed forward from
+ * checkpoints taken every 64 tokens (the same forward arithmetic).
+ */
+static int backward_impl(const float* q, const float* k, const float* v, const float* alpha,
+                         const float* beta, const float* S0, const float* dO, const float* dST,
+                         double* dq, double* dk, double* dv, double* dalpha, double* dbeta,
+                         double* dS0, int B, int T, int H, int Dk, int Dv, int nthreads)
+{
+    if (!q || !k || !v || !alpha || !beta || !dO || !dq || !dk || !dv || !dalpha || !dbeta)
+        return -1;
+    if (B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return -1;
+    const int K = 64;
+    const long nseg = (T + K - 1) / K;
+    const size_t SZ = (size_t)Dk * Dv;
+    set_threads(nthreads);
+    const long nbh = (long)B * H;
+    int failed = 0;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long bh = 0; bh < nbh; ++bh) {
+        const int b = (int)(bh / H), h = (int)(bh % H);
+        /* checkpoints [nseg][SZ], states of one segment [K + 1][SZ], G, dSt,
+         * and per-token vectors */
+        const size_t nd = (size_t)(nseg > 0 ? nseg : 1) * SZ + (size_t)(K + 1) * SZ + 2 * SZ +
+                          5 * (size_t)Dv + 3 * (size_t)Dk;
+        double* ck = (double*)malloc(sizeof(double) * nd);
+        if (!ck) {
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
+        double* buf = ck + (size_t)(nseg > 0 ? nseg : 1) * SZ;
+        double* G = buf + (size_t)(K + 1) * SZ;
+        double* dSt = G + SZ;
+        double* pred = dSt + SZ;
+        double* vd = pred + Dv;
+        double* u = vd + Dv;
+        double* y = u + Dv;
+        double* dod = y + Dv;
+        double* qd = dod + Dv;
+        double* kd = qd + Dk;
+        double* ad = kd + Dk;
+
+        /* forward: checkpoint the state before tokens 0, K, 2K, ... */
+        double* S = buf;
+        if (S0) {
+            const float* s0 = S0 + (size_t)bh * SZ;
+            for (size_t e = 0; e < SZ; ++e) S[e] = (double)s0[e];
+        } else {
+            memset(S, 0, sizeof(double) * SZ);
+        }
+        for (int t = 0; t < T; ++t) {
+            const size_t tok = ((size_t)b * T + t) * H + h;
+            if (t % K == 0) memcpy(ck + (size_t)(t / K) * SZ, S, sizeof(double) * SZ);
+            const double bt = load_token(NULL, q + tok * Dk, k + tok * Dk, v + tok * Dv,
+                                         alpha + tok * Dk, beta[tok], qd, kd, vd, ad, Dk, Dv, Dk);
+            token_update(S, qd, kd, vd, ad, NULL, bt, NULL, Dk, Dv, pred);
+        }
+
+        /* backward */
+        if (dST) {
+            const float* g = dST + (size_t)bh * SZ;
+            for (size_t e = 0; e < SZ; ++e) G[e] = (double)g[e];
+        } else {
+            memset(G, 0, sizeof(double) * SZ);
+        }
+        for (long sgi = nseg - 1; sgi >= 0; --sgi) {
+            const int a = (int)(sgi * K), e_ = (a + K < T) ? a + K : T;
+            /* buf[i] = state before token a + i, i = 0 .. e_ - a */
+            memcpy(buf, ck + (size_t)sgi * SZ, sizeof(double) * SZ);
+            for (int t = a; t < e_; ++t) {
+                const size_t tok = ((size_t)b * T + t) * H + h;
+                double* nx = buf + (size_t)(t - a + 1) * SZ;
+                memcpy(nx, buf + (size_t)(t - a) * SZ, sizeof(double) * SZ);
+                const double bt = load_token(NULL, q + tok * Dk, k + tok * Dk, v + tok * Dv,
+                                             alpha + tok * Dk, beta[tok], qd, kd, vd, ad, Dk, Dv, Dk);
+                token_update(nx, qd, kd, vd, ad, NULL, bt, NULL, Dk, Dv, pred);
+            }
+            for (int t = e_ - 1; t >= a; --t) {
+                const size_t tok = ((size_t)b * T + t) * H + h;
+                const double* Sp = buf + (size_t)(t - a) * SZ;       /* S_{t-1} */
+                const double* Sn = Sp + SZ;                          /* S_t */
+                const double bt = load_token(NULL, q + tok * Dk, k + tok * Dk, v + tok * Dv,
+                                             alpha + tok * Dk, beta[tok], qd, kd, vd, ad, Dk, Dv, Dk);
+                for (int j = 0; j < Dv; ++j) dod[j] = (double)dO[tok * Dv + j];
+                /* read-out o_t = S_t^T q_t */
+                for (int c = 0; c < Dk; ++c) {
+                    double s = 0.0;
+                    for (int j = 0; j < Dv; ++j) s += Sn[(size_t)c * Dv + j] * dod[j];
+                    dq[tok * Dk + c] = s;
+                    for (int j = 0; j < Dv; ++j) G[(size_t)c * Dv + j] += qd[c] * dod[j];
+                }
+                /* delta correction of St = diag(alpha) S_{t-1} */
+                for (int j = 0; j < Dv; ++j) {
+                    double p = 0.0, yy = 0.0;
+                    for (int c = 0; c < Dk; ++c) {
+                        p += kd[c] * ad[c] * Sp[(size_t)c * Dv + j];
+                        yy += G[(size_t)c * Dv + j] * kd[c];
+                    }
+                    u[j] = vd[j] - p;
+                    y[j] = yy;
+                }
+                double db = 0.0;
+                for (int j = 0; j < Dv; ++j) {
+                    dv[tok * Dv + j] = bt * y[j];
+                    db += u[j] * y[j];
+                }
+                dbeta[tok] = db;
+                for (int c = 0; c < Dk; ++c) {
+                    double s1 = 0.0, s2 = 0.0;
+                    for (int j = 0; j < Dv; ++j) {
+                        s1 += G[(size_t)c * Dv + j] * bt * u[j];
+                        s2 += ad[c] * Sp[(size_t)c * Dv + j] * y[j];
+                    }
+                    dk[tok * Dk + c] = s1 - bt * s2;
+                }
+                for (int c = 0; c < Dk; ++c)
+                    for (int j = 0; j < Dv; ++j)
+                        dSt[(size_t)c * Dv + j] = G[(size_t)c * Dv + j] - bt * kd[c] * y[j];
+                /* decay: St = diag(alpha) S_{t-1} */
+                for (int c = 0; c < Dk; ++c) {
+                    double s = 0.0;
+                    for (int j = 0; j < Dv; ++j) s += dSt[(size_t)c * Dv + j] * Sp[(size_t)c * Dv + j];
+                    dalpha[tok * Dk + c] = s;
+                    for (int j = 0; j < Dv; ++j) G[(size_t)c * Dv + j] = ad[c] * dSt[(size_t)c * Dv + j];
+                }
+            }
+        }
+        if (dS0) memcpy(dS0 + (size_t)bh * SZ, G, sizeof(double) * SZ);
+        free(ck);
+    }
+    return failed ? -1 : 0;
+}
+
+int kda_oracle_backward(const float* q, const float* k, const float* v, const float* alpha,
+                        const float* beta, const float* S0, const float* dO, const float* dST,
+                        double* dq, double* dk, double* dv, double* dalpha, double* dbeta,
+                        double* dS0, int B, int T, int H, int Dk, int Dv, int nthreads)
+{
+    return backward_impl(q, k, v, alpha, beta, S0, dO, dST, dq, dk, dv, dalpha, dbeta, dS0,
+                         B, T, H, Dk, Dv, nthreads);
+}
+
 int kda_oracle_decode(const float* q, const float* k, const float* v,
                       const float* alpha, const float* beta, double* S,
                       double* out, int nsteps, int B, int H, int Dk, int Dv,

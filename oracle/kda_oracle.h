@@ -68,6 +68,17 @@ int kda_oracle_forward_phase(const float* q, const float* k, const float* v,
                              const float* S0, double* out, double* ST,
                              int B, int T, int H, int Dk, int Dv, int nthreads);
 
+/* Gradients of the scalar loss L = sum_t <o_t, dO_t> + <S_T, dST> with
+ * respect to every input of kda_oracle_forward (reverse-mode chain rule
+ * through each token of eq. (1) and eq. (14), last token first; dST may be
+ * NULL = zero).  dO has out's layout; dq, dk, dalpha [B, T, H, Dk],
+ * dv [B, T, H, Dv], dbeta [B, T, H], dS0 [B, H, Dk, Dv] (may be NULL).
+ * The states are recomputed from checkpoints every 64 tokens. */
+int kda_oracle_backward(const float* q, const float* k, const float* v, const float* alpha,
+                        const float* beta, const float* S0, const float* dO, const float* dST,
+                        double* dq, double* dk, double* dv, double* dalpha, double* dbeta,
+                        double* dS0, int B, int T, int H, int Dk, int Dv, int nthreads);
+
 /* nsteps single-token updates applied to a resident double state in place.
  * Per-step inputs are stacked: q, k, alpha [nsteps, B, H, Dk],
  * v [nsteps, B, H, Dv], beta [nsteps, B, H]; out [nsteps, B, H, Dv];
