@@ -117,6 +117,52 @@ def time_forward(kda, torch, w, inp, steps, warmup, extra_flags=0):
     return ms, per, out, st
 
 
+def time_backward(kda, torch, w, inp, steps, warmup):
+    """kda_chunk_backward on workload w (loss gradients from workloads.make_backward_seeds):
+    ms per call and per-kernel durations, plus the algorithmic bytes of the call
+    (the inputs q, k, v, alpha, beta, dO, S0, dST read once; dq, dk, dv, dalpha,
+    dbeta, dS0 written once)."""
+    import workloads
+    stream = torch.cuda.current_stream()
+    dO, dST = workloads.make_backward_seeds(w, device="cuda")
+    ws = torch.empty(kda.backward_workspace_size(w.B, w.T, w.H, w.Dk, w.Dv, w.chunk, w.dtype),
+                     dtype=torch.uint8, device="cuda")
+    grads = {"dq": torch.empty_like(inp["q"]), "dk": torch.empty_like(inp["k"]),
+             "dv": torch.empty_like(inp["v"]), "d_alpha": torch.empty_like(inp["alpha"]),
+             "d_beta": torch.empty_like(inp["beta"]),
+             "d_initial_state": torch.empty((w.B, w.H, w.Dk, w.Dv), dtype=torch.float32,
+                                            device="cuda")}
+
+    def call(flags=0):
+        kda.chunk_backward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], dO, inp["S0"],
+                           dST, chunk=w.chunk, mode=w.mode, grads=grads, workspace=ws,
+                           stream=stream, flags=flags)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    per = {}
+    for _ in range(steps):
+        call(kda.STAGE_EVENTS)
+        for name, t in kda.last_stage_times():
+            per.setdefault(name, []).append(t)
+    torch.cuda.synchronize()
+    per = {k: sum(v) / len(v) for k, v in per.items()}
+    e = 2 if w.dtype == torch.bfloat16 else 4
+    ntok = w.B * w.T * w.H
+    state = w.B * w.H * w.Dk * w.Dv * 4
+    nbytes = (ntok * (2 * (2 * w.Dk + 2 * w.Dv) * e + 2 * (4 * w.Dk + 4))
+              + state * (3 if inp["S0"] is not None else 2))
+    return ms, per, nbytes
+
+
 def cpu_baseline(oracle, w, inp, max_heads=None, min_seconds=10.0):
     import numpy as np
     heads = list(range(w.H if max_heads is None else min(w.H, max_heads)))
@@ -178,6 +224,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-others", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward on the headline workload even with --no-others")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -248,6 +296,12 @@ def main():
         del io
         others["ckda_bf16_decode"] = decode_bench(kda, torch, workloads)
         line["others"] = others
+    if not args.no_others or args.backward:
+        # the backward (kda_chunk_backward) on the headline workload
+        msb, perb, nbb = time_backward(kda, torch, w, inp, max(3, args.steps // 4), 3)
+        line.setdefault("others", {})["kda_bf16_prefill_backward"] = {
+            "ms": msb, "tokens_per_s": tokens / (msb / 1e3), "algorithmic_bytes": nbb,
+            "path_hbm_frac": nbb / (msb / 1e3) / 1e9 / HBM_PEAK_GBS, "kernels_ms": perb}
     if args.copy_probe:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)

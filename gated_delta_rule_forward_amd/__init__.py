@@ -86,6 +86,10 @@ def load():
     lib.kda_chunk_forward_varlen.restype = i
     lib.kda_decode_step.argtypes = [vp] * 7 + [i] * 6 + [u, vp]
     lib.kda_decode_step.restype = i
+    lib.kda_chunk_backward_workspace_size.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(sz)]
+    lib.kda_chunk_backward_workspace_size.restype = i
+    lib.kda_chunk_backward.argtypes = [vp] * 14 + [i] * 8 + [u, vp, sz, vp]
+    lib.kda_chunk_backward.restype = i
     lib.kda_gate_prep.argtypes = [vp] * 4 + [i] * 5 + [vp]
     lib.kda_gate_prep.restype = i
     lib.kda_last_stage_times.argtypes = [ctypes.POINTER(ctypes.c_float),
@@ -310,6 +314,55 @@ def decode_step(q, k, v, alpha, beta, state, *, out=None, mode: int = CKDA, stre
                              _ptr(out), B, H, Dk, Dv, _DT[q.dtype], mode, flags, _stream(stream))
     _check("kda_decode_step", st)
     return out
+
+
+def backward_workspace_size(B: int, T: int, H: int, Dk: int, Dv: int, chunk: int,
+                            dtype: torch.dtype) -> int:
+    lib = load()
+    n = ctypes.c_size_t(0)
+    st = lib.kda_chunk_backward_workspace_size(B, T, H, Dk, Dv, chunk, _DT[dtype], ctypes.byref(n))
+    _check("kda_chunk_backward_workspace_size", st)
+    return n.value
+
+
+def chunk_backward(q, k, v, alpha, beta, d_out, initial_state=None, d_final_state=None, *,
+                   chunk: int = 64, mode: int = CKDA, want_d_initial_state: bool = True,
+                   grads=None, workspace=None, stream=None, flags: int = 0):
+    """Backward of chunk_forward (kda_chunk_backward): gradients of
+    sum <out, d_out> + <final_state, d_final_state> with respect to q, k, v,
+    alpha, beta and initial_state.  Layouts as chunk_forward; d_out like out,
+    d_final_state [B,H,Dk,Dv] fp32 or None.  grads: optional dict of output
+    tensors.  Returns a dict dq, dk, dv (q's dtype), d_alpha, d_beta,
+    d_initial_state (fp32; None unless wanted)."""
+    lib = load()
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    g = dict(grads or {})
+    g.setdefault("dq", torch.empty((B, T, H, Dk), dtype=q.dtype, device=dev))
+    g.setdefault("dk", torch.empty((B, T, H, Dk), dtype=q.dtype, device=dev))
+    g.setdefault("dv", torch.empty((B, T, H, Dv), dtype=q.dtype, device=dev))
+    g.setdefault("d_alpha", torch.empty((B, T, H, Dk), dtype=torch.float32, device=dev))
+    g.setdefault("d_beta", torch.empty((B, T, H), dtype=torch.float32, device=dev))
+    if want_d_initial_state:
+        g.setdefault("d_initial_state", torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev))
+    else:
+        g["d_initial_state"] = None
+    if workspace is None:
+        nbytes = backward_workspace_size(B, T, H, Dk, Dv, chunk, q.dtype)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _dev(q, k, v, alpha, beta, d_out, initial_state, d_final_state, workspace, *g.values())
+    if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype or d_out.dtype != q.dtype:
+        raise ValueError("q, k, v and d_out must share one dtype (float32 or bfloat16)")
+    wsb = workspace.numel() * workspace.element_size()
+    st = lib.kda_chunk_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                _ptr(initial_state), _ptr(d_out), _ptr(d_final_state),
+                                _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["d_alpha"]),
+                                _ptr(g["d_beta"]), _ptr(g["d_initial_state"]),
+                                B, T, H, Dk, Dv, chunk, _DT[q.dtype], mode, flags,
+                                _ptr(workspace), wsb, _stream(stream))
+    _check("kda_chunk_backward", st)
+    return g
 
 
 def gate_prep(alpha, chunk: int, *, stream=None):

@@ -1,0 +1,787 @@
+// bwd.hip — the chunkwise backward: gradients of L = sum_t <o_t, dO_t> +
+// <S_T, dST> with respect to q, k, v, alpha, beta and S0, for the recurrence
+// of "Semidirect Fourier Delta Attention" §1 eq. (1) read out by §3 eq. (14).
+//
+// Per chunk (C tokens, S the state entering it, dSn the loss gradient of the
+// state leaving it through later chunks and dST), differentiating the
+// chunkwise forward  Delta = U - W S,  O = (Q * Gamma) S + P Delta,
+// S_next = diag(Gamma_{C-1}) S + Ktil^T Delta  gives the reverse chain
+//   X  = P^T dO + Ktil dSn                          (gradient of Delta)
+//   dS = diag(Gamma_{C-1}) dSn + (Q * Gamma)^T dO - W^T X
+// (columns of dS are independent, as the forward's columns of S are), and
+// per chunk, with y = Tinv^T X (y_r = G_r^T k_r, G_r the gradient of the
+// state after token r), B1 = dO Delta^T, B3 = Y Delta^T, F1 = dO S^T,
+// F2 = Y S^T, F3 = Delta dSn^T and the decay-weighted sums
+//   LQ1_r = sum_{i<r} B1[r,i] rho(r,i) k_i     LK3_r = sum_{i<r} B3[r,i] rho(r,i) k_i
+//   UQ1_r = sum_{j>r} B1[j,r] rho(j,r) q_j     UK2_r = sum_{j>r} beta_j B3[j,r] rho(j,r) k_j
+// (rho(r,i) = prod_{l=i+1..r} alpha_l per channel):
+//   dv = diag(beta) y
+//   dq = Gamma F1 + LQ1 + diag(B1) k
+//   dk = rho(C-1,.) F3 + UQ1 + diag(B1) q - UK2 - beta (Gamma F2 + LK3)
+//   dbeta_r = v_r.y_r - (k_r Gamma_r).F2_r - k_r.LK3_r
+//   alpha_r dalpha_r = Gamma_{C-1} sigma + sum_{i<r} (Ktil F3)_i
+//                      + sum_{j>=r} [Gamma (q F1 - beta k F2) + q LQ1 - beta k LK3
+//                                    - k (UQ1 - UK2)]_j,   sigma_c = <dSn[c], S[c]>
+// the last term read off the reverse-mode derivative of the gates through
+// every product rho that contains alpha_r.  Where |alpha_r| < 2^-6 (zero
+// gates included) the quotient is replaced by the direct form
+//   dalpha_r[c] = <H_r[c,:], S_{r-1}[c,:]>,  H_r = G_r - k_r dv_r^T,
+// from a per-channel sweep over the chunk (bwd_tiny_kernel).
+//
+// Kernels, after the forward's prep (which also stores Tinv) and its chain
+// (which also stores the fp32 chunk states and Delta):
+//   relayout_kernel    W, Q*Gamma, Ktil^T, P -> W^T, (Q*Gamma)^T, Ktil, P^T in
+//                      the fragment-major A-operand layout, in place
+//   bwd_chain_kernel   the reverse chain, one workgroup per (b, h, 16 columns)
+//   bwd_local_kernel   every chunk's gradients, one workgroup per chunk
+//   bwd_tiny_kernel    the direct dalpha of small gates, flagged chunks only
+#include "kda_chunk.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+
+namespace {
+
+constexpr int kBwdThreads = 256;
+constexpr int kXcds = 8;
+constexpr float kTinyGate = 0x1p-6f;
+
+// ---- relayout ---------------------------------------------------------------
+// (row, column) of the element at offset o of an A-operand matrix with K
+// columns (the inverse of frag_off)
+template <int KB>
+__device__ __forceinline__ void frag_pos(int o, int K, int& r, int& k)
+{
+    constexpr int NV = KB / 4;
+    const int j = o % NV, x = o / NV;
+    const int lane = x & 63, blk = x >> 6;
+    const int nkb = K / KB;
+    const int g = lane >> 4;
+    int kk;
+    if constexpr (KB == 32) kk = 16 * (j >> 2) + 4 * g + (j & 3);
+    else kk = 4 * g + j;
+    r = 16 * (blk / nkb) + (lane & 15);
+    k = (blk % nkb) * KB + kk;
+}
+
+template <typename T, int C, int DK>
+struct RelayoutLds {
+    static constexpr size_t W = 0, Q = W + (size_t)C * DK, K = Q + (size_t)C * DK, P = K + (size_t)C * DK;
+    static constexpr size_t BYTES = (P + (size_t)C * C) * sizeof(T);
+};
+
+template <typename T, int C, int DK>
+__global__ __launch_bounds__(kBwdThreads) void relayout_kernel(T* __restrict__ W, T* __restrict__ QG,
+                                                               T* __restrict__ Kt, T* __restrict__ P)
+{
+    constexpr int KB = KBlock<T, C, DK>::value;
+    using L = RelayoutLds<T, C, DK>;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    T* s = reinterpret_cast<T*>(lds);
+    const size_t unit = blockIdx.x;
+    T* gW = W + unit * C * DK;
+    T* gQ = QG + unit * C * DK;
+    T* gK = Kt + unit * DK * C;
+    T* gP = P + unit * C * C;
+    const int tid = threadIdx.x;
+    int r, k;
+    for (int o = tid; o < C * DK; o += kBwdThreads) {
+        frag_pos<KB>(o, DK, r, k);                 // W, Q*Gamma: [C][DK]
+        s[L::W + r * DK + k] = gW[o];
+        s[L::Q + r * DK + k] = gQ[o];
+        frag_pos<KB>(o, C, r, k);                  // Ktil^T: [DK][C]
+        s[L::K + r * C + k] = gK[o];
+    }
+    for (int o = tid; o < C * C; o += kBwdThreads) {
+        frag_pos<KB>(o, C, r, k);
+        s[L::P + r * C + k] = gP[o];
+    }
+    __syncthreads();
+    for (int o = tid; o < C * DK; o += kBwdThreads) {
+        frag_pos<KB>(o, C, r, k);                  // W^T, (Q*Gamma)^T: rows DK, K = C
+        gW[o] = s[L::W + k * DK + r];
+        gQ[o] = s[L::Q + k * DK + r];
+        frag_pos<KB>(o, DK, r, k);                 // Ktil: rows C, K = DK
+        gK[o] = s[L::K + k * C + r];
+    }
+    for (int o = tid; o < C * C; o += kBwdThreads) {
+        frag_pos<KB>(o, C, r, k);
+        gP[o] = s[L::P + k * C + r];
+    }
+}
+
+// ---- reverse chain ----------------------------------------------------------
+template <typename T, int C, int DK>
+struct RevGeom {
+    static constexpr int KB = KBlock<T, C, DK>::value;
+    static constexpr int NV = KB / 4;
+    static constexpr int NT = DK / 16, NM = C / 16, NKD = DK / KB, NKC = C / KB;
+    static constexpr int SPW = (NT + 3) / 4;
+};
+
+template <typename T, int C, int DK>
+__global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
+{
+    using G = RevGeom<T, C, DK>;
+    using F = Frag<T, G::KB>;
+    __shared__ F sSf[G::NKD * 64];      // dS as B fragments, k = channels
+    __shared__ F sXf[G::NKC * 64];      // -X as B fragments, k = tokens
+
+    const int Dv = a.Dv, H = a.H, NS = Dv / 16, NC = a.NC;
+    const int gid = blockIdx.x, xcd = gid % kXcds, jx = gid / kXcds;
+    const int bh = (jx / NS) * kXcds + xcd, slice = jx % NS;
+    if (bh >= a.B * H) return;
+    const int b = bh / H, h = bh % H;
+    const int tid = threadIdx.x, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = slice * 16 + ln;
+    const T* dO = static_cast<const T*>(a.dO);
+
+    f32x4 dS[G::SPW];
+#pragma unroll
+    for (int u = 0; u < G::SPW; ++u) {
+        const int t = wave + 4 * u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            dS[u][i] = (a.dST && t < G::NT) ? a.dST[((size_t)bh * DK + 16 * t + 4 * lg + i) * Dv + col] : 0.f;
+        if (t < G::NT) put_tile<T, G::KB>(sSf, t, lane, dS[u]);
+    }
+    __syncthreads();
+
+    for (int n = NC - 1; n >= 0; --n) {
+        const size_t unit = (size_t)bh * NC + n;
+        // the gradient of the state leaving chunk n
+#pragma unroll
+        for (int u = 0; u < G::SPW; ++u) {
+            const int t = wave + 4 * u;
+            if (t < G::NT) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    a.DSN[(unit * DK + 16 * t + 4 * lg + i) * Dv + col] = dS[u][i];
+            }
+        }
+        // dO of this chunk's column slice as B fragments over tokens
+        F dof[G::NKC];
+#pragma unroll
+        for (int s = 0; s < G::NKC; ++s) {
+            float f[G::NV];
+#pragma unroll
+            for (int j = 0; j < G::NV; ++j) {
+                const int kk = G::KB == 32 ? 16 * (j >> 2) + 4 * lg + (j & 3) : 4 * lg + j;
+                const int row = n * C + s * G::KB + kk;
+                f[j] = row < a.T ? to_f32(dO[(((size_t)b * a.T + row) * H + h) * Dv + col]) : 0.f;
+            }
+            dof[s] = F::from(f);
+        }
+        F sf[G::NKD];
+#pragma unroll
+        for (int s = 0; s < G::NKD; ++s) sf[s] = sSf[s * 64 + lane];
+        // X for token tile `wave`
+        if (G::NM == 4 || wave < G::NM) {
+            const T* pt = static_cast<const T*>(a.PT) + unit * C * C + (size_t)wave * G::NKC * 64 * G::NV;
+            const T* kt = static_cast<const T*>(a.Ktil) + unit * C * DK + (size_t)wave * G::NKD * 64 * G::NV;
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int s = 0; s < G::NKC; ++s) acc = mma(F::load(pt + (s * 64 + lane) * G::NV), dof[s], acc);
+#pragma unroll
+            for (int s = 0; s < G::NKD; ++s) acc = mma(F::load(kt + (s * 64 + lane) * G::NV), sf[s], acc);
+            float* xb = a.XB + (unit * C + 16 * wave + 4 * lg) * Dv + col;
+            f32x4 neg;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                xb[(size_t)i * Dv] = acc[i];
+                neg[i] = -acc[i];
+            }
+            put_tile<T, G::KB>(sXf, wave, lane, neg);
+        }
+        __syncthreads();
+        F xf[G::NKC];
+#pragma unroll
+        for (int s = 0; s < G::NKC; ++s) xf[s] = sXf[s * 64 + lane];
+        // dS <- diag(Gamma_{C-1}) dS + (Q*Gamma)^T dO - W^T X for this wave's state tiles
+#pragma unroll
+        for (int u = 0; u < G::SPW; ++u) {
+            const int t = wave + 4 * u;
+            if (G::NT % 4 == 0 || t < G::NT) {
+                const f32x4 gc = *reinterpret_cast<const f32x4*>(a.GC + unit * DK + 16 * t + 4 * lg);
+                f32x4 acc;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[i] = gc[i] * dS[u][i];
+                const T* qt = static_cast<const T*>(a.QGT) + unit * DK * C + (size_t)t * G::NKC * 64 * G::NV;
+                const T* wt = static_cast<const T*>(a.WT) + unit * DK * C + (size_t)t * G::NKC * 64 * G::NV;
+#pragma unroll
+                for (int s = 0; s < G::NKC; ++s) acc = mma(F::load(qt + (s * 64 + lane) * G::NV), dof[s], acc);
+#pragma unroll
+                for (int s = 0; s < G::NKC; ++s) acc = mma(F::load(wt + (s * 64 + lane) * G::NV), xf[s], acc);
+                dS[u] = acc;
+                put_tile<T, G::KB>(sSf, t, lane, acc);
+            }
+        }
+        __syncthreads();
+    }
+    if (a.dS0) {
+#pragma unroll
+        for (int u = 0; u < G::SPW; ++u) {
+            const int t = wave + 4 * u;
+            if (t < G::NT) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    a.dS0[((size_t)bh * DK + 16 * t + 4 * lg + i) * Dv + col] = dS[u][i];
+            }
+        }
+    }
+}
+
+// ---- per-chunk gradients ----------------------------------------------------
+template <typename T, int C, int DK>
+struct LocalGeom {
+    static constexpr int NM = C / 16, NCT = DK / 16, CTW = (NCT + 3) / 4;
+    static constexpr int DVMAX = sizeof(T) == 4 ? 64 : 128;
+    static constexpr int LDV = DVMAX + 4;      // row stride of the [C][Dv] fp32 arrays
+    static constexpr int LDT = C + 4;          // row stride of the [C][C] fp32 arrays
+    static constexpr size_t al16(size_t x) { return (x + 15) & ~size_t(15); }
+    // R0: Tinv (y phase), then B1, B3
+    static constexpr size_t B1 = 0, B3 = B1 + 4 * (size_t)C * LDT, R0 = B3 + 4 * (size_t)C * LDT;
+    static constexpr size_t TI = 0;
+    // R1, GEMM phase: dO, Delta, Y
+    static constexpr size_t DO = R0, DL = DO + 4 * (size_t)C * LDV, YY = DL + 4 * (size_t)C * LDV;
+    static constexpr size_t R1A = YY + 4 * (size_t)C * LDV;
+    // R1, weight phase: alpha (fp32), k, q (io type), B1^T, B3^T; then Za, Zb over k, q, ...
+    static constexpr size_t AL = R0, KK = AL + 4 * (size_t)C * DK, QQ = al16(KK + sizeof(T) * C * DK);
+    static constexpr size_t B1T = al16(QQ + sizeof(T) * C * DK), B3T = B1T + 4 * (size_t)C * LDT;
+    static constexpr size_t R1B = B3T + 4 * (size_t)C * LDT;
+    static constexpr size_t ZA = KK, ZB = ZA + 4 * (size_t)C * DK, R1C = ZB + 4 * (size_t)C * DK;
+    // small arrays
+    static constexpr size_t R1 = R1A > R1B ? (R1A > R1C ? R1A : R1C) : (R1B > R1C ? R1B : R1C);
+    static constexpr size_t BETA = R1, DB = BETA + 4 * C, DBW = DB + 4 * C, SIG = DBW + 16 * C;
+    static constexpr size_t BYTES = SIG + 4 * DK + 16;
+    static_assert(BYTES <= 160 * 1024, "LDS");
+};
+
+template <typename T, int C, int DK>
+__global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(BwdLocalArgs a)
+{
+    using G = LocalGeom<T, C, DK>;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    float* sT = reinterpret_cast<float*>(lds + G::TI);
+    float* sB1 = reinterpret_cast<float*>(lds + G::B1);
+    float* sB3 = reinterpret_cast<float*>(lds + G::B3);
+    float* sDO = reinterpret_cast<float*>(lds + G::DO);
+    float* sDL = reinterpret_cast<float*>(lds + G::DL);
+    float* sY = reinterpret_cast<float*>(lds + G::YY);
+    float* sAl = reinterpret_cast<float*>(lds + G::AL);
+    T* sK = reinterpret_cast<T*>(lds + G::KK);
+    T* sQ = reinterpret_cast<T*>(lds + G::QQ);
+    float* sB1T = reinterpret_cast<float*>(lds + G::B1T);
+    float* sB3T = reinterpret_cast<float*>(lds + G::B3T);
+    float* sZa = reinterpret_cast<float*>(lds + G::ZA);
+    float* sZb = reinterpret_cast<float*>(lds + G::ZB);
+    float* sBeta = reinterpret_cast<float*>(lds + G::BETA);
+    float* sDB = reinterpret_cast<float*>(lds + G::DB);
+    float* sDBw = reinterpret_cast<float*>(lds + G::DBW);      // [4 waves][C]
+    float* sSig = reinterpret_cast<float*>(lds + G::SIG);
+    constexpr int LDV = G::LDV, LDT = G::LDT, NM = G::NM;
+
+    const int Dv = a.Dv, H = a.H, NC = a.NC, NVT = Dv / 16;
+    const size_t unit = blockIdx.x;
+    const int bh = (int)(unit / NC), n = (int)(unit % NC);
+    const int b = bh / H, h = bh % H;
+    const int nvalid = min(C, a.T - n * C);
+    const size_t row0 = (size_t)b * a.T + (size_t)n * C;       // first token row
+    const int tid = threadIdx.x, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    auto tok = [&](int r) { return (row0 + r) * H + h; };       // token index of local row r
+
+    // ---- load -------------------------------------------------------------------
+    bool tiny = false;
+    for (int idx = tid; idx < nvalid * DK; idx += kBwdThreads)
+        tiny |= fabsf(a.alpha[tok(idx / DK) * DK + idx % DK]) < kTinyGate;
+    const int any_tiny = __syncthreads_or(tiny);
+    if (tid < C) {
+        sBeta[tid] = tid < nvalid ? a.beta[tok(tid)] : 0.f;
+        sDB[tid] = 0.f;
+    }
+    for (int idx = tid; idx < C * C; idx += kBwdThreads)
+        sT[(idx / C) * LDT + idx % C] = a.Tm[unit * C * C + idx];
+    const T* dO = static_cast<const T*>(a.dO);
+    for (int idx = tid; idx < C * (Dv / 4); idx += kBwdThreads) {
+        const int r = idx / (Dv / 4), c4 = 4 * (idx % (Dv / 4));
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f), d = o;
+        if (r < nvalid) {
+            const Vec4<T> x = Vec4<T>::load(dO + tok(r) * Dv + c4);
+            o = make_float4(x.get(0), x.get(1), x.get(2), x.get(3));
+            d = *reinterpret_cast<const float4*>(a.DL + (unit * C + r) * Dv + c4);
+        }
+        *reinterpret_cast<float4*>(sDO + r * LDV + c4) = o;
+        *reinterpret_cast<float4*>(sDL + r * LDV + c4) = d;
+    }
+    __syncthreads();
+
+    // ---- y = Tinv^T X, dv = diag(beta) y ------------------------------------------
+    T* dv = static_cast<T*>(a.dv);
+    for (int job = wave; job < NM * NVT; job += 4) {
+        const int mt = job / NVT, vt = job % NVT;
+        f32x4 acc = zero4();
+        for (int s = mt; s < NM; ++s) {          // Tinv[k][m] = 0 for k < m
+            float fa[4], fb[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int kk = 16 * s + 4 * lg + j;
+                fa[j] = sT[kk * LDT + 16 * mt + ln];
+                fb[j] = a.XB[(unit * C + kk) * Dv + 16 * vt + ln];
+            }
+            acc = mma_k16(Vec4<float>::from(fa), Vec4<float>::from(fb), acc);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * mt + 4 * lg + i, c = 16 * vt + ln;
+            sY[r * LDV + c] = acc[i];
+            if (r < nvalid) dv[tok(r) * Dv + c] = from_f32<T>(sBeta[r] * acc[i]);
+        }
+    }
+    __syncthreads();
+
+    // ---- dbeta, first term: v_r . y_r ---------------------------------------------
+    {
+        constexpr int TPR = kBwdThreads / C;       // threads per row
+        const int r = tid / TPR, part = tid % TPR;
+        const T* v = static_cast<const T*>(a.v);
+        float sacc = 0.f;
+        if (r < nvalid)
+            for (int c = part; c < Dv; c += TPR) sacc += to_f32(v[tok(r) * Dv + c]) * sY[r * LDV + c];
+#pragma unroll
+        for (int o = TPR / 2; o > 0; o >>= 1) sacc += __shfl_xor(sacc, o);
+        if (part == 0) sDB[r] = sacc;
+    }
+
+    // ---- B1 = dO Delta^T (i <= r), B3 = Y Delta^T (i < r): lower tiles --------------
+    {
+        constexpr int NP = NM * (NM + 1) / 2;
+        for (int job = wave; job < 2 * NP; job += 4) {
+            const int which = job / NP;
+            int p = job % NP, mt = 0;
+            while (p > mt) { p -= mt + 1; ++mt; }
+            const int it = p;                          // it <= mt
+            const float* src = which == 0 ? sDO : sY;
+            const f32x4 acc = tile_tn<float>(src + 16 * mt * LDV, LDV, sDL + 16 * it * LDV, LDV, Dv, zero4());
+            float* dst = which == 0 ? sB1 : sB3;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * mt + 4 * lg + i, ic = 16 * it + ln;
+                dst[r * LDT + ic] = (which == 0 ? ic <= r : ic < r) ? acc[i] : 0.f;
+            }
+        }
+    }
+
+    // ---- F1 = dO S^T, F2 = Y S^T, F3 = Delta dSn^T; sigma = rowdot(dSn, S) ----------
+    f32x4 F1[G::CTW][NM], F2[G::CTW][NM], F3[G::CTW][NM];
+#pragma unroll
+    for (int cw = 0; cw < G::CTW; ++cw) {
+        const int ct = wave + 4 * cw;
+#pragma unroll
+        for (int mt = 0; mt < NM; ++mt) F1[cw][mt] = F2[cw][mt] = F3[cw][mt] = zero4();
+        if (G::NCT % 4 == 0 || ct < G::NCT) {
+            const float* ps = a.CS32 + (unit * DK + 16 * ct + ln) * Dv + 4 * lg;
+            const float* pn = a.DSN + (unit * DK + 16 * ct + ln) * Dv + 4 * lg;
+            float sig = 0.f;
+            for (int s = 0; s < NVT; ++s) {
+                const Vec4<float> bS = Vec4<float>::load(ps + 16 * s);
+                const Vec4<float> bN = Vec4<float>::load(pn + 16 * s);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sig += bS.v[j] * bN.v[j];
+#pragma unroll
+                for (int mt = 0; mt < NM; ++mt) {
+                    const int off = (16 * mt + ln) * LDV + 16 * s + 4 * lg;
+                    F1[cw][mt] = mma_k16(Vec4<float>::load(sDO + off), bS, F1[cw][mt]);
+                    F2[cw][mt] = mma_k16(Vec4<float>::load(sY + off), bS, F2[cw][mt]);
+                    F3[cw][mt] = mma_k16(Vec4<float>::load(sDL + off), bN, F3[cw][mt]);
+                }
+            }
+            sig += __shfl_xor(sig, 16);
+            sig += __shfl_xor(sig, 32);
+            if (lg == 0) sSig[16 * ct + ln] = sig;
+        }
+    }
+    // the small-gate kernel needs y: it replaces X in place (every read of X is done)
+    if (any_tiny) {
+        for (int idx = tid; idx < C * Dv; idx += kBwdThreads)
+            a.XB[unit * C * Dv + idx] = sY[(idx / Dv) * LDV + idx % Dv];
+    }
+    __syncthreads();
+
+    // ---- weight phase: alpha, k, q, B1^T, B3^T ----------------------------------------
+    {
+        const T* kg = static_cast<const T*>(a.k);
+        const T* qg = static_cast<const T*>(a.q);
+        for (int idx = tid; idx < C * (DK / 4); idx += kBwdThreads) {
+            const int r = idx / (DK / 4), c4 = 4 * (idx % (DK / 4));
+            float4 al = make_float4(1.f, 1.f, 1.f, 1.f);
+            Vec4<T> kv = Vec4<T>::zero(), qv = Vec4<T>::zero();
+            if (r < nvalid) {
+                al = *reinterpret_cast<const float4*>(a.alpha + tok(r) * DK + c4);
+                kv = Vec4<T>::load(kg + tok(r) * DK + c4);
+                qv = Vec4<T>::load(qg + tok(r) * DK + c4);
+            }
+            *reinterpret_cast<float4*>(sAl + r * DK + c4) = al;
+            *reinterpret_cast<Vec4<T>*>(sK + r * DK + c4) = kv;
+            *reinterpret_cast<Vec4<T>*>(sQ + r * DK + c4) = qv;
+        }
+        for (int idx = tid; idx < C * C; idx += kBwdThreads) {
+            const int r = idx / C, i = idx % C;
+            sB1T[i * LDT + r] = sB1[r * LDT + i];
+            sB3T[i * LDT + r] = sB3[r * LDT + i];
+        }
+    }
+    __syncthreads();
+
+    float Za[G::CTW][NM][4], Zb[G::CTW][NM][4];
+    float dbp[NM][4];
+#pragma unroll
+    for (int mt = 0; mt < NM; ++mt)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) dbp[mt][m] = 0.f;
+    T* dqg = static_cast<T*>(a.dq);
+    T* dkg = static_cast<T*>(a.dk);
+#pragma unroll
+    for (int cw = 0; cw < G::CTW; ++cw) {
+        const int ct = wave + 4 * cw;
+        if (!(G::NCT % 4 == 0 || ct < G::NCT)) continue;
+        const int c = 16 * ct + ln;
+        auto al = [&](int t) { return sAl[t * DK + c]; };
+        auto kf = [&](int t) { return to_f32(sK[t * DK + c]); };
+        auto qf = [&](int t) { return to_f32(sQ[t * DK + c]); };
+        // Gamma_r (inclusive prefix products) and rho(C-1, r) of the lane's rows
+        float gam[NM][4], gend[NM][4];
+        {
+            float p = 1.f;
+            int t = 0;
+#pragma unroll
+            for (int mt = 0; mt < NM; ++mt)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int r = 16 * mt + 4 * lg + m;
+                    for (; t <= r; ++t) p *= al(t);
+                    gam[mt][m] = p;
+                }
+            p = 1.f;
+            t = C - 1;
+#pragma unroll
+            for (int mt = NM - 1; mt >= 0; --mt)
+#pragma unroll
+                for (int m = 3; m >= 0; --m) {
+                    const int r = 16 * mt + 4 * lg + m;
+                    for (; t > r; --t) p *= al(t);
+                    gend[mt][m] = p;
+                }
+        }
+#pragma unroll
+        for (int mt = 0; mt < NM; ++mt) {
+            const int r0 = 16 * mt + 4 * lg, r3 = r0 + 3;
+            // L sums over i < r0 with w = rho(r0, i), then rho(r0 + m, r0)
+            float lq[4] = {0.f, 0.f, 0.f, 0.f}, lk[4] = {0.f, 0.f, 0.f, 0.f};
+            {
+                float w = 1.f;
+                for (int i = r0 - 1; i >= 0; --i) {
+                    w *= al(i + 1);
+                    const float wk = w * kf(i);
+                    const float4 b1 = *reinterpret_cast<const float4*>(sB1T + i * LDT + r0);
+                    const float4 b3 = *reinterpret_cast<const float4*>(sB3T + i * LDT + r0);
+                    lq[0] += b1.x * wk; lq[1] += b1.y * wk; lq[2] += b1.z * wk; lq[3] += b1.w * wk;
+                    lk[0] += b3.x * wk; lk[1] += b3.y * wk; lk[2] += b3.z * wk; lk[3] += b3.w * wk;
+                }
+                float f = 1.f;
+#pragma unroll
+                for (int m = 1; m < 4; ++m) {
+                    f *= al(r0 + m);
+                    lq[m] *= f;
+                    lk[m] *= f;
+                    // pairs inside the group: r0 <= i < r0 + m
+                    float wi = 1.f;
+                    for (int i = r0 + m - 1; i >= r0; --i) {
+                        wi *= al(i + 1);
+                        const float wk = wi * kf(i);
+                        lq[m] += sB1[(r0 + m) * LDT + i] * wk;
+                        lk[m] += sB3[(r0 + m) * LDT + i] * wk;
+                    }
+                }
+            }
+            // U sums over j > r3 with w = rho(j, r3), then rho(r3, r0 + m)
+            float uq[4] = {0.f, 0.f, 0.f, 0.f}, uk[4] = {0.f, 0.f, 0.f, 0.f};
+            {
+                float w = 1.f;
+                for (int j = r3 + 1; j < C; ++j) {
+                    w *= al(j);
+                    const float wq = w * qf(j), wk = w * sBeta[j] * kf(j);
+                    const float4 b1 = *reinterpret_cast<const float4*>(sB1 + j * LDT + r0);
+                    const float4 b3 = *reinterpret_cast<const float4*>(sB3 + j * LDT + r0);
+                    uq[0] += b1.x * wq; uq[1] += b1.y * wq; uq[2] += b1.z * wq; uq[3] += b1.w * wq;
+                    uk[0] += b3.x * wk; uk[1] += b3.y * wk; uk[2] += b3.z * wk; uk[3] += b3.w * wk;
+                }
+                float f = 1.f;
+#pragma unroll
+                for (int m = 2; m >= 0; --m) {
+                    f *= al(r0 + m + 1);
+                    uq[m] *= f;
+                    uk[m] *= f;
+                    // pairs inside the group: r0 + m < j <= r3
+                    float wj = 1.f;
+                    for (int j = r0 + m + 1; j <= r3; ++j) {
+                        wj *= al(j);
+                        uq[m] += sB1[j * LDT + r0 + m] * wj * qf(j);
+                        uk[m] += sB3[j * LDT + r0 + m] * wj * sBeta[j] * kf(j);
+                    }
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int r = r0 + m;
+                const float kr = kf(r), qr = qf(r), br = sBeta[r];
+                const float b1d = sB1[r * LDT + r];
+                const float g = gam[mt][m], ge = gend[mt][m];
+                const float f1 = F1[cw][mt][m], f2 = F2[cw][mt][m], f3 = F3[cw][mt][m];
+                const float dqv = g * f1 + lq[m] + b1d * kr;
+                const float dkv = ge * f3 + uq[m] + b1d * qr - uk[m] - br * (g * f2 + lk[m]);
+                dbp[mt][m] -= kr * (g * f2 + lk[m]);
+                Za[cw][mt][m] = ge * kr * f3;
+                Zb[cw][mt][m] = g * (qr * f1 - br * kr * f2) + qr * lq[m] - br * kr * lk[m] - kr * (uq[m] - uk[m]);
+                if (r < nvalid) {
+                    dqg[tok(r) * DK + c] = from_f32<T>(dqv);
+                    dkg[tok(r) * DK + c] = from_f32<T>(dkv);
+                }
+            }
+        }
+    }
+    // dbeta: sum over the lane's channels, then over the 16 lanes of a row
+    // group; each wave covers every row once, and the waves' sums are added in
+    // a fixed order below (the result does not depend on scheduling)
+#pragma unroll
+    for (int mt = 0; mt < NM; ++mt)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const float sacc = row16_sum(dbp[mt][m]);
+            if (ln == 0) sDBw[wave * C + 16 * mt + 4 * lg + m] = sacc;
+        }
+    __syncthreads();     // k, q, B1^T, B3^T dead: Za, Zb take their place
+#pragma unroll
+    for (int cw = 0; cw < G::CTW; ++cw) {
+        const int ct = wave + 4 * cw;
+        if (!(G::NCT % 4 == 0 || ct < G::NCT)) continue;
+#pragma unroll
+        for (int mt = 0; mt < NM; ++mt)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int r = 16 * mt + 4 * lg + m;
+                sZa[r * DK + 16 * ct + ln] = Za[cw][mt][m];
+                sZb[r * DK + 16 * ct + ln] = Zb[cw][mt][m];
+            }
+    }
+    __syncthreads();
+    // per channel: Z_r = Gamma_{C-1} sigma + (prefix of Za, r excluded) + (suffix of Zb)
+    if (tid < DK) {
+        const int c = tid;
+        float gc = 1.f;
+        for (int t = 0; t < C; ++t) gc *= sAl[t * DK + c];
+        float pre = 0.f;
+        for (int r = 0; r < C; ++r) {
+            const float z = sZa[r * DK + c];
+            sZa[r * DK + c] = pre;
+            pre += z;
+        }
+        const float base = gc * sSig[c];
+        float suf = 0.f;
+        for (int r = C - 1; r >= 0; --r) {
+            suf += sZb[r * DK + c];
+            sZb[r * DK + c] = base + sZa[r * DK + c] + suf;
+        }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < nvalid * DK; idx += kBwdThreads) {
+        const int r = idx / DK, c = idx % DK;
+        const float av = sAl[r * DK + c];
+        a.dalpha[tok(r) * DK + c] = fabsf(av) >= kTinyGate ? sZb[r * DK + c] / av : 0.f;
+    }
+    if (tid < nvalid)
+        a.dbeta[tok(tid)] = sDB[tid] + ((sDBw[tid] + sDBw[C + tid]) + (sDBw[2 * C + tid] + sDBw[3 * C + tid]));
+    if (tid == 0) a.FLB[unit] = any_tiny ? 1 : 0;
+}
+
+// ---- direct dalpha of small gates ---------------------------------------------
+template <typename T, int C, int DK>
+struct TinyLds {
+    static constexpr int DVMAX = sizeof(T) == 4 ? 64 : 128;
+    static constexpr size_t DL = 0, DO = DL + 4 * (size_t)C * DVMAX, E = DO + 4 * (size_t)C * DVMAX;
+    static constexpr size_t LIST = E + 4 * (size_t)C * DVMAX, CNT = LIST + 4 * (size_t)C * DK;
+    static constexpr size_t BYTES = CNT + 16;
+};
+
+template <typename T, int C, int DK>
+__global__ __launch_bounds__(kBwdThreads) void bwd_tiny_kernel(BwdLocalArgs a)
+{
+    using L = TinyLds<T, C, DK>;
+    const size_t unit = blockIdx.x;
+    if (!a.FLB[unit]) return;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    float* sDL = reinterpret_cast<float*>(lds + L::DL);
+    float* sDO = reinterpret_cast<float*>(lds + L::DO);
+    float* sE = reinterpret_cast<float*>(lds + L::E);
+    int* sList = reinterpret_cast<int*>(lds + L::LIST);
+    int* sCnt = reinterpret_cast<int*>(lds + L::CNT);
+    const int Dv = a.Dv, H = a.H, NC = a.NC;
+    const int bh = (int)(unit / NC), n = (int)(unit % NC);
+    const int b = bh / H, h = bh % H;
+    const int nvalid = min(C, a.T - n * C);
+    const size_t row0 = (size_t)b * a.T + (size_t)n * C;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    auto tok = [&](int r) { return (row0 + r) * H + h; };
+    const T* dO = static_cast<const T*>(a.dO);
+    const T* kg = static_cast<const T*>(a.k);
+    const T* qg = static_cast<const T*>(a.q);
+
+    if (tid == 0) *sCnt = 0;
+    for (int idx = tid; idx < nvalid * Dv; idx += kBwdThreads) {
+        const int r = idx / Dv, c = idx % Dv;
+        sDL[idx] = a.DL[(unit * C + r) * Dv + c];
+        sDO[idx] = to_f32(dO[tok(r) * Dv + c]);
+        sE[idx] = a.beta[tok(r)] * a.XB[(unit * C + r) * Dv + c];
+    }
+    __syncthreads();
+    for (int idx = tid; idx < nvalid * DK; idx += kBwdThreads) {
+        const int r = idx / DK, c = idx % DK;
+        if (fabsf(a.alpha[tok(r) * DK + c]) < kTinyGate) sList[atomicAdd(sCnt, 1)] = idx;
+    }
+    __syncthreads();
+    const int cnt = *sCnt;
+    constexpr int JPL = L::DVMAX / 64;           // columns per lane (at most)
+    for (int e = wave; e < cnt; e += 4) {
+        const int r = sList[e] / DK, c = sList[e] % DK;
+        // S_{r-1}[c, :] forward from the chunk start
+        float s[JPL], hh[JPL], g[JPL];
+#pragma unroll
+        for (int x = 0; x < JPL; ++x) {
+            const int j = lane + 64 * x;
+            s[x] = j < Dv ? a.CS32[(unit * DK + c) * Dv + j] : 0.f;
+        }
+        for (int t = 0; t < r; ++t) {
+            const float at = a.alpha[tok(t) * DK + c], kt = to_f32(kg[tok(t) * DK + c]);
+#pragma unroll
+            for (int x = 0; x < JPL; ++x) {
+                const int j = lane + 64 * x;
+                if (j < Dv) s[x] = at * s[x] + kt * sDL[t * Dv + j];
+            }
+        }
+        // H_r[c, :] backward from the chunk end: G_{last} = dSn + q dO, then
+        // H_t = G_t - k_t dv_t,  G_{t-1} = alpha_t H_t + q_{t-1} dO_{t-1}
+        const int tl = nvalid - 1;
+        const float ql = to_f32(qg[tok(tl) * DK + c]);
+#pragma unroll
+        for (int x = 0; x < JPL; ++x) {
+            const int j = lane + 64 * x;
+            g[x] = j < Dv ? a.DSN[(unit * DK + c) * Dv + j] + ql * sDO[tl * Dv + j] : 0.f;
+        }
+        for (int t = tl; t >= r; --t) {
+            const float kt = to_f32(kg[tok(t) * DK + c]);
+#pragma unroll
+            for (int x = 0; x < JPL; ++x) {
+                const int j = lane + 64 * x;
+                hh[x] = j < Dv ? g[x] - kt * sE[t * Dv + j] : 0.f;
+            }
+            if (t > r) {
+                const float at = a.alpha[tok(t) * DK + c], qp = to_f32(qg[tok(t - 1) * DK + c]);
+#pragma unroll
+                for (int x = 0; x < JPL; ++x) {
+                    const int j = lane + 64 * x;
+                    g[x] = j < Dv ? at * hh[x] + qp * sDO[(t - 1) * Dv + j] : 0.f;
+                }
+            }
+        }
+        float d = 0.f;
+#pragma unroll
+        for (int x = 0; x < JPL; ++x) d += hh[x] * s[x];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) d += __shfl_xor(d, o);
+        if (lane == 0) a.dalpha[tok(r) * DK + c] = d;
+    }
+}
+
+// ---- launchers ------------------------------------------------------------------
+template <typename K>
+hipError_t set_lds(K kern, size_t bytes)
+{
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+template <typename T, int C, int DK>
+hipError_t launch_bwd_t(int stage, const ChunkShape& s, const ChunkWorkspace& ws,
+                        const BwdChainArgs& ca, const BwdLocalArgs& la, hipStream_t stream)
+{
+    const unsigned nu = (unsigned)((size_t)s.B * s.H * s.NC);
+    switch (stage) {
+    case 0: {
+        using L = RelayoutLds<T, C, DK>;
+        auto kern = relayout_kernel<T, C, DK>;
+        const hipError_t e = set_lds(kern, L::BYTES);
+        if (e != hipSuccess) return e;
+        return launch_kernel(kern, dim3(nu), dim3(kBwdThreads), (uint32_t)L::BYTES, stream,
+                             static_cast<T*>(ws.W), static_cast<T*>(ws.QG), static_cast<T*>(ws.Kt),
+                             static_cast<T*>(ws.P));
+    }
+    case 1: {
+        const int bh = s.B * s.H;
+        const unsigned grid = (unsigned)(kXcds * (s.Dv / 16) * ((bh + kXcds - 1) / kXcds));
+        return launch_kernel(bwd_chain_kernel<T, C, DK>, dim3(grid), dim3(kBwdThreads), 0, stream, ca);
+    }
+    case 2: {
+        using G = LocalGeom<T, C, DK>;
+        auto kern = bwd_local_kernel<T, C, DK>;
+        const hipError_t e = set_lds(kern, G::BYTES);
+        if (e != hipSuccess) return e;
+        return launch_kernel(kern, dim3(nu), dim3(kBwdThreads), (uint32_t)G::BYTES, stream, la);
+    }
+    case 3: {
+        using L = TinyLds<T, C, DK>;
+        auto kern = bwd_tiny_kernel<T, C, DK>;
+        const hipError_t e = set_lds(kern, L::BYTES);
+        if (e != hipSuccess) return e;
+        return launch_kernel(kern, dim3(nu), dim3(kBwdThreads), (uint32_t)L::BYTES, stream, la);
+    }
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T, int C>
+hipError_t bwd_dk(int stage, const ChunkShape& s, const ChunkWorkspace& ws, const BwdChainArgs& ca,
+                  const BwdLocalArgs& la, hipStream_t st)
+{
+    switch (s.Dk) {
+    case 32: return launch_bwd_t<T, C, 32>(stage, s, ws, ca, la, st);
+    case 64: return launch_bwd_t<T, C, 64>(stage, s, ws, ca, la, st);
+    case 128:
+        if constexpr (sizeof(T) == 2) return launch_bwd_t<T, C, 128>(stage, s, ws, ca, la, st);
+        else return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename T>
+hipError_t bwd_c(int stage, const ChunkShape& s, const ChunkWorkspace& ws, const BwdChainArgs& ca,
+                 const BwdLocalArgs& la, hipStream_t st)
+{
+    switch (s.C) {
+    case 32: return bwd_dk<T, 32>(stage, s, ws, ca, la, st);
+    case 64: return bwd_dk<T, 64>(stage, s, ws, ca, la, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_backward_stage(int stage, IoType io, const ChunkShape& s, const ChunkWorkspace& ws,
+                                 const BwdChainArgs& ca, const BwdLocalArgs& la, hipStream_t stream)
+{
+    if (io == IoType::F32) return bwd_c<float>(stage, s, ws, ca, la, stream);
+    return bwd_c<bf16_t>(stage, s, ws, ca, la, stream);
+}
+
+}  // namespace kda

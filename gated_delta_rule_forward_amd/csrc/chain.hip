@@ -233,17 +233,6 @@ __device__ __forceinline__ void read_ops(ChainOps<T, C, DK>& o, const unsigned c
     }
 }
 
-// write a C-layout tile (4 values per lane) into slot base (tile % TPB) * 4 of
-// the lane's fragment of k block tile / TPB
-template <typename T, int KB>
-__device__ __forceinline__ void put_tile(Frag<T, KB>* frags, int tile, int lane, const f32x4& v)
-{
-    constexpr int TPB = KB / 16;
-    T* p = reinterpret_cast<T*>(&frags[(tile / TPB) * 64 + lane]) + 4 * (tile % TPB);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = from_f32<T>(v[i]);
-}
-
 template <typename T, int C, int DK>
 __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
 {
@@ -366,7 +355,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
     // critical path, so computed during the next chunk's first phase)
     F pqg[G::NKD], pp[G::NKC], psf[G::NKD], pdf[G::NKC];
     auto emit = [&](int n) {
-        if (!summary && (G::NM == 4 || wave < G::NM)) {
+        if (a.out && (G::NM == 4 || wave < G::NM)) {
             f32x4 acc = zero4();
 #pragma unroll
             for (int s = 0; s < G::NKD; ++s) acc = mma(pqg[s], psf[s], acc);
@@ -397,6 +386,18 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
                 }
             }
         }
+        if (a.CS32) {
+            // the same state in fp32, by unit
+            float* cs = a.CS32 + (u0 + nc) * DK * Dv + col;
+#pragma unroll
+            for (int u = 0; u < G::SPW; ++u) {
+                const int t = wave + 4 * u;
+                if (t < G::NT) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) cs[(size_t)(16 * t + 4 * lg + i) * Dv] = S[u][i];
+                }
+            }
+        }
         F sf[G::NKD];
 #pragma unroll
         for (int s = 0; s < G::NKD; ++s) sf[s] = sSf[s * 64 + lane];
@@ -411,6 +412,11 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
 #pragma unroll
             for (int i = 0; i < 4; ++i) dl[i] = (xpart ? 0.f : cur.u[i]) - acc[i];
             put_tile<T, G::KB>(sDf, wave, lane, dl);
+            if (a.DL) {
+                float* d = a.DL + ((u0 + nc) * C + 16 * wave + 4 * lg) * Dv + col;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) d[(size_t)i * Dv] = dl[i];
+            }
         }
         lds_barrier();
         F df[G::NKC];

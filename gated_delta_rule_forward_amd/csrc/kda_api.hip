@@ -375,6 +375,153 @@ kda_status_t decode_step(const void* q, const void* k, const void* v, const floa
     return rec.done() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+// ---- backward ----------------------------------------------------------------
+// workspace: the forward's per-unit regions, then Tinv [NU][C][C], the fp32
+// chunk states [NU][Dk][Dv], Delta [NU][C][Dv], the state gradients
+// [NU][Dk][Dv], X / y [NU][C][Dv] (all fp32) and the small-gate flags [NU]
+constexpr int kBwdRegions = 6;
+size_t backward_layout(int B, int T, int H, int Dk, int Dv, int chunk, IoType io,
+                       size_t off[kda::kWorkspaceRegions], size_t boff[kBwdRegions])
+{
+    const ChunkShape sh = make_shape(B, T, H, Dk, Dv, chunk);
+    size_t n = kda::chunk_workspace_layout(sh, io, off);
+    const size_t nu = (size_t)B * H * sh.NC;
+    const size_t sz[kBwdRegions] = {nu * chunk * chunk * 4, nu * Dk * Dv * 4, nu * chunk * Dv * 4,
+                                    nu * Dk * Dv * 4, nu * chunk * Dv * 4, nu};
+    for (int i = 0; i < kBwdRegions; ++i) {
+        boff[i] = n;
+        n += (sz[i] + 255) & ~size_t(255);
+    }
+    return n;
+}
+
+kda_status_t check_backward_shape(int B, int T, int H, int Dk, int Dv, int chunk,
+                                  kda_dtype_t dtype)
+{
+    const kda_status_t st = check_forward_shape(B, T, H, Dk, Dv, chunk, dtype);
+    if (st != KDA_OK) return st;
+    if (chunk != 32 && chunk != 64) return KDA_ERR_UNSUPPORTED;
+    if (Dk != 32 && Dk != 64 && Dk != 128) return KDA_ERR_UNSUPPORTED;
+    return KDA_OK;
+}
+
+kda_status_t chunk_backward(const void* q, const void* k, const void* v, const float* alpha,
+                            const float* beta, const float* initial_state, const void* d_out,
+                            const float* d_final_state, void* dq, void* dk, void* dv,
+                            float* d_alpha, float* d_beta, float* d_initial_state, int B, int T,
+                            int H, int Dk, int Dv, int chunk, kda_dtype_t dtype, kda_mode_t mode,
+                            unsigned flags, void* workspace, size_t workspace_bytes, void* stream)
+{
+    kda_status_t st = check_backward_shape(B, T, H, Dk, Dv, chunk, dtype);
+    if (st != KDA_OK) return st;
+    if (mode != KDA_MODE_KDA && mode != KDA_MODE_CKDA) return KDA_ERR_UNSUPPORTED;
+    if (flags & ~KDA_FLAG_STAGE_EVENTS) return KDA_ERR_UNSUPPORTED;
+    if (T > 0 && (!q || !k || !v || !alpha || !beta || !d_out || !dq || !dk || !dv || !d_alpha ||
+                  !d_beta))
+        return KDA_ERR_NULL_POINTER;
+    size_t ws_need = 0;
+    kda_chunk_backward_workspace_size(B, T, H, Dk, Dv, chunk, dtype, &ws_need);
+    if (T > 0 && !workspace) return KDA_ERR_NULL_POINTER;
+    if (workspace_bytes < ws_need) return KDA_ERR_WORKSPACE_TOO_SMALL;
+
+    const size_t e = elem_size(dtype);
+    const size_t ntok = (size_t)B * T * H;
+    const size_t nstate = (size_t)B * H * Dk * Dv * 4;
+    const void* vec[] = {q, k, d_out, alpha, workspace};
+    for (const void* p : vec)
+        if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
+    const void* elt[] = {v, beta, initial_state, d_final_state, dq, dk, dv, d_alpha, d_beta,
+                         d_initial_state};
+    const uintptr_t ea[] = {e, 4, 4, 4, e, e, e, 4, 4, 4};
+    for (int i = 0; i < 10; ++i)
+        if (elt[i] && !aligned(elt[i], ea[i])) return KDA_ERR_MISALIGNED;
+    struct R { const void* p; size_t n; };
+    const R in[] = {{q, ntok * Dk * e}, {k, ntok * Dk * e}, {v, ntok * Dv * e},
+                    {alpha, ntok * Dk * 4}, {beta, ntok * 4},
+                    {initial_state, initial_state ? nstate : 0}, {d_out, ntok * Dv * e},
+                    {d_final_state, d_final_state ? nstate : 0}};
+    const R outs[] = {{dq, ntok * Dk * e}, {dk, ntok * Dk * e}, {dv, ntok * Dv * e},
+                      {d_alpha, ntok * Dk * 4}, {d_beta, ntok * 4},
+                      {d_initial_state, d_initial_state ? nstate : 0}, {workspace, ws_need}};
+    constexpr int NO = sizeof(outs) / sizeof(outs[0]);
+    for (const R& o : outs)
+        for (const R& i : in)
+            if (overlaps(o.p, o.n, i.p, i.n)) return KDA_ERR_ALIAS;
+    for (int x = 0; x < NO; ++x)
+        for (int y = x + 1; y < NO; ++y)
+            if (overlaps(outs[x].p, outs[x].n, outs[y].p, outs[y].n)) return KDA_ERR_ALIAS;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    std::unique_lock<std::mutex> lock(g_stage.mu, std::defer_lock);
+    Recorder rec{(flags & KDA_FLAG_STAGE_EVENTS) != 0, s};
+    if (rec.on) {
+        lock.lock();
+        if (stage_begin() != hipSuccess) return KDA_ERR_HIP;
+    }
+    if (T == 0) {
+        // no tokens: the loss is <S0, dST>, so dS0 = dST
+        if (!d_initial_state) return KDA_OK;
+        if (rec.mark("state_copy") != hipSuccess) return KDA_ERR_HIP;
+        if (d_final_state) {
+            if (kda::launch_state_copy(d_final_state, d_initial_state, nstate / 4, s) != hipSuccess)
+                return KDA_ERR_HIP;
+        } else if (kda::launch_state_copy(nullptr, d_initial_state, nstate / 4, s) != hipSuccess) {
+            return KDA_ERR_HIP;
+        }
+        return rec.done() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    }
+
+    const ChunkShape sh = make_shape(B, T, H, Dk, Dv, chunk);
+    const IoType io = dtype == KDA_DTYPE_F32 ? IoType::F32 : IoType::BF16;
+    size_t off[kda::kWorkspaceRegions], boff[kBwdRegions];
+    backward_layout(B, T, H, Dk, Dv, chunk, io, off, boff);
+    unsigned char* w = static_cast<unsigned char*>(workspace);
+    const ChunkWorkspace ws{w + off[0], w + off[1], w + off[2],
+                            w + off[3], w + off[4], reinterpret_cast<float*>(w + off[5]),
+                            w + off[6]};
+    float* Tm = reinterpret_cast<float*>(w + boff[0]);
+    float* CS32 = reinterpret_cast<float*>(w + boff[1]);
+    float* DL = reinterpret_cast<float*>(w + boff[2]);
+    float* DSN = reinterpret_cast<float*>(w + boff[3]);
+    float* XB = reinterpret_cast<float*>(w + boff[4]);
+    uint8_t* FLB = w + boff[5];
+    int zx = 0;
+    if (mode == KDA_MODE_CKDA) {
+        zx = 128;
+        while (zx > 0 && kda::prep_fast_lds_bytes(io, chunk, Dk, zx) > 160 * 1024) zx -= 16;
+    }
+    kda::PrepArgs pa{q, k, v, alpha, beta, ws.W, ws.U, ws.Kt, ws.QG, ws.P, ws.GC, ws.FL,
+                     T, H, Dv, sh.NC, zx, 0, 0.f, 0.f, 0.f, 0.f, 0,
+                     nullptr, nullptr, 0, nullptr};
+    pa.Tm = Tm;
+    kda::ChainArgs ca{ws.W, ws.U, ws.Kt, ws.QG, ws.P, ws.GC, initial_state, nullptr,
+                      nullptr, nullptr, B, T, H, Dv, sh.NC, nullptr, nullptr,
+                      0, sh.NC, 1, nullptr, nullptr};
+    ca.CS32 = CS32;
+    ca.DL = DL;
+    const kda::BwdChainArgs ra{ws.Kt, ws.P, ws.QG, ws.W, ws.GC, d_out, d_final_state,
+                               d_initial_state, DSN, XB, B, T, H, Dv, sh.NC};
+    const kda::BwdLocalArgs la{q, k, v, alpha, beta, d_out, Tm, CS32, DL, DSN, XB,
+                               dq, dk, dv, d_alpha, d_beta, FLB, T, H, Dv, sh.NC};
+
+    if (rec.mark("prep_fast") != hipSuccess) return KDA_ERR_HIP;
+    if (kda::launch_prep_fast(io, sh, pa, s) != hipSuccess) return KDA_ERR_HIP;
+    if (rec.done() != hipSuccess) return KDA_ERR_HIP;
+    if (rec.mark("prep_exact") != hipSuccess) return KDA_ERR_HIP;
+    if (kda::launch_prep_exact(io, sh, pa, s) != hipSuccess) return KDA_ERR_HIP;
+    if (rec.done() != hipSuccess) return KDA_ERR_HIP;
+    if (rec.mark("chain_states") != hipSuccess) return KDA_ERR_HIP;
+    if (kda::launch_chain(io, sh, ca, s) != hipSuccess) return KDA_ERR_HIP;
+    if (rec.done() != hipSuccess) return KDA_ERR_HIP;
+    static const char* const names[4] = {"relayout", "chain_reverse", "chunk_grads", "small_gates"};
+    for (int stage = 0; stage < 4; ++stage) {
+        if (rec.mark(names[stage]) != hipSuccess) return KDA_ERR_HIP;
+        if (kda::launch_backward_stage(stage, io, sh, ws, ra, la, s) != hipSuccess) return KDA_ERR_HIP;
+        if (rec.done() != hipSuccess) return KDA_ERR_HIP;
+    }
+    return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -617,6 +764,32 @@ kda_status_t kda_gate_prep(const float* alpha, float* L, unsigned char* meta, fl
                               static_cast<hipStream_t>(stream)) != hipSuccess)
         return KDA_ERR_HIP;
     return KDA_OK;
+}
+
+kda_status_t kda_chunk_backward_workspace_size(int B, int T, int H, int Dk, int Dv, int chunk,
+                                               kda_dtype_t dtype, size_t* bytes)
+{
+    if (!bytes) return KDA_ERR_NULL_POINTER;
+    const kda_status_t st = check_backward_shape(B, T, H, Dk, Dv, chunk, dtype);
+    if (st != KDA_OK) return st;
+    size_t off[kda::kWorkspaceRegions], boff[kBwdRegions];
+    *bytes = T == 0 ? 0
+                    : backward_layout(B, T, H, Dk, Dv, chunk,
+                                      dtype == KDA_DTYPE_F32 ? IoType::F32 : IoType::BF16, off, boff);
+    return KDA_OK;
+}
+
+kda_status_t kda_chunk_backward(const void* q, const void* k, const void* v, const float* alpha,
+                                const float* beta, const float* initial_state, const void* d_out,
+                                const float* d_final_state, void* dq, void* dk, void* dv,
+                                float* d_alpha, float* d_beta, float* d_initial_state, int B,
+                                int T, int H, int Dk, int Dv, int chunk, kda_dtype_t dtype,
+                                kda_mode_t mode, unsigned flags, void* workspace,
+                                size_t workspace_bytes, void* stream)
+{
+    return chunk_backward(q, k, v, alpha, beta, initial_state, d_out, d_final_state, dq, dk, dv,
+                          d_alpha, d_beta, d_initial_state, B, T, H, Dk, Dv, chunk, dtype, mode,
+                          flags, workspace, workspace_bytes, stream);
 }
 
 kda_status_t kda_last_stage_times(float* ms, const char** names, int max, int* count)

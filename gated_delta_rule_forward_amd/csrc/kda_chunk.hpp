@@ -107,6 +107,17 @@ __device__ __forceinline__ f32x4 mma(const Frag<float, 16>& a, const Frag<float,
     return acc;
 }
 
+// write a C-layout tile (4 values per lane) into slot base (tile % TPB) * 4 of
+// the lane's fragment of k block tile / TPB (B fragments kept in LDS)
+template <typename T, int KB>
+__device__ __forceinline__ void put_tile(Frag<T, KB>* frags, int tile, int lane, const f32x4& v)
+{
+    constexpr int TPB = KB / 16;
+    T* p = reinterpret_cast<T*>(&frags[(tile / TPB) * 64 + lane]) + 4 * (tile % TPB);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = from_f32<T>(v[i]);
+}
+
 // B fragment of k block s built from C-layout accumulator tiles (rows 4g+i of
 // column n in lane l = 16g + n): a k32 block spans tiles 2s and 2s+1 (slot j =
 // tile 2s + j/4, register j%4), a k16 block is tile s.
@@ -183,6 +194,9 @@ struct PrepArgs {
     // phase variant ("Semidirect Fourier Delta Attention" eq. (13)): theta
     // [..., Dk/2] per channel pair and alpha then also per pair; null = KDA
     const float* theta;
+    // backward support: Tinv = (I + A)^{-1} of every unit, fp32 [NU][C][C]
+    // row-major (zero above the diagonal), or null
+    float* Tm;
 };
 
 // logistic function in fp32 (exp2 of the scaled argument; saturates to 0 / 1)
@@ -215,6 +229,56 @@ struct ChainArgs {
     int seg, nseg;
     float* summ;
     const float* Sseg;
+    // backward support (dense batches): the fp32 state entering every chunk,
+    // CS32 [NU][Dk][Dv], and every chunk's deltas Delta, DL [NU][C][Dv]
+    // (rows past the sequence end hold zeros); either may be null.  out may
+    // be null when only these are wanted.
+    float* CS32;
+    float* DL;
+};
+
+// Backward (dense batches).  The reverse chain reads the forward's operands
+// after relayout_kernel turned them into W^T, (Q * Gamma)^T, Ktil and P^T
+// (fragment-major A operands: rows channels / tokens / tokens, k tokens /
+// channels / tokens) and writes, per unit, the gradient of the state leaving
+// the chunk (DSN [NU][Dk][Dv] fp32) and X = P^T dO + Ktil dSn (XB [NU][C][Dv]
+// fp32); dS0 [B,H,Dk,Dv] may be null, dST (may be null = zero) seeds it.
+struct BwdChainArgs {
+    const void* Ktil;
+    const void* PT;
+    const void* QGT;
+    const void* WT;
+    const float* GC;
+    const void* dO;
+    const float* dST;
+    float* dS0;
+    float* DSN;
+    float* XB;
+    int B, T, H, Dv, NC;
+};
+// The per-chunk gradient kernels: inputs, Tinv (Tm), the fp32 chunk states
+// (CS32), Delta (DL), DSN and XB (replaced by y in flagged units); outputs
+// dq, dk, dv (io type), dalpha, dbeta (fp32) and FLB [NU] (1 = the unit has a
+// gate with |alpha| < 2^-6, whose dalpha the small-gate kernel writes).
+struct BwdLocalArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* alpha;
+    const float* beta;
+    const void* dO;
+    const float* Tm;
+    const float* CS32;
+    const float* DL;
+    const float* DSN;
+    float* XB;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dalpha;
+    float* dbeta;
+    uint8_t* FLB;
+    int T, H, Dv, NC;
 };
 
 // Where one unit (one chunk of one sequence and head) lives.  Dense batches:

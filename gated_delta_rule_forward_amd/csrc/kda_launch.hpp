@@ -71,6 +71,13 @@ hipError_t launch_decode(IoType io, int B, int H, int Dk, int Dv, const void* q,
                          const float* beta, float* state, void* out, hipStream_t stream,
                          const float* theta = nullptr);
 
+struct BwdChainArgs;
+struct BwdLocalArgs;
+// backward stages: 0 relayout, 1 reverse chain, 2 per-chunk gradients,
+// 3 small-gate dalpha (kda_chunk.hpp describes the arguments)
+hipError_t launch_backward_stage(int stage, IoType io, const ChunkShape& s, const ChunkWorkspace& ws,
+                                 const BwdChainArgs& ca, const BwdLocalArgs& la, hipStream_t stream);
+
 hipError_t launch_gate_prep(const float* alpha, float* L, uint8_t* meta, float* gend, int B,
                             int T, int H, int Dk, int C, hipStream_t stream);
 

@@ -340,6 +340,11 @@ __global__ __launch_bounds__(kPrepThreads) void prep_exact_kernel(PrepArgs args,
             }
 #pragma unroll
             for (int r = 0; r < C; ++r) sTi[r * C + j] = from_f32<T>(t[r]);
+            if (args.Tm) {
+                float* tg = args.Tm + (size_t)unit * C * C;
+#pragma unroll
+                for (int r = 0; r < C; ++r) tg[r * C + j] = t[r];
+            }
         }
     } else {
         const int VPR = Dv / 4;    // groups of 4 elements

@@ -611,6 +611,10 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
         }
         __syncthreads();
     }
+    if (args.Tm) {
+        float* tg = args.Tm + (size_t)unit * C * C;
+        for (int idx = tid; idx < C * C; idx += kThreads) tg[idx] = sT[(idx / C) * LDF + idx % C];
+    }
 
     // ---- W = Tinv X_W and U = Tinv (diag(beta) V): wave w takes token tile
     //      mt = w; its Tinv rows serve as the A operand of U and the B operand

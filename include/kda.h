@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 5
+#define KDA_ABI_VERSION 6
 
 typedef enum {
     KDA_OK = 0,
@@ -269,6 +269,40 @@ kda_status_t kda_decode_step_phase(const void* q, const void* k, const void* v,
                                    int B, int H, int Dk, int Dv,
                                    kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
                                    void* stream);
+
+/*
+ * Backward of kda_chunk_forward (dense batches, gates and beta as given):
+ * the gradients of the scalar loss
+ *   L = sum_t <o_t, d_out_t> + <S_T, d_final_state>
+ * with respect to q, k, v, alpha, beta and initial_state, for the recurrence
+ * of "Semidirect Fourier Delta Attention" §1 eq. (1) read out by §3 eq. (14)
+ * (reverse-mode differentiation of the chunkwise form of "Kimi Delta
+ * Attention: a bounded case study", Exercise 2).  The forward is recomputed
+ * inside the call; nothing from a previous forward call is needed.
+ *   inputs : q, k, v, alpha, beta, initial_state as for kda_chunk_forward
+ *            (initial_state NULL = zero); d_out [B,T,H,Dv] in dtype;
+ *            d_final_state [B,H,Dk,Dv] fp32 or NULL (= zero)
+ *   outputs: dq, dk [B,T,H,Dk] and dv [B,T,H,Dv] in dtype; d_alpha
+ *            [B,T,H,Dk] and d_beta [B,T,H] fp32; d_initial_state [B,H,Dk,Dv]
+ *            fp32 or NULL (not wanted)
+ * Supported: chunk in {32, 64}; Dk in {32, 64, 128} (fp32: Dk, Dv <= 64);
+ * Dv a multiple of 16 up to 128.  q, k, d_out, alpha and the workspace are
+ * 16-byte aligned, the rest element-aligned.  No output may overlap an input,
+ * another output or the workspace.  The workspace (caller-owned, contents
+ * undefined after the call) is at least
+ * kda_chunk_backward_workspace_size bytes.  Status codes as for the forward;
+ * the call only enqueues kernels on `stream`.
+ */
+kda_status_t kda_chunk_backward_workspace_size(int B, int T, int H, int Dk, int Dv, int chunk,
+                                               kda_dtype_t dtype, size_t* bytes);
+kda_status_t kda_chunk_backward(const void* q, const void* k, const void* v,
+                                const float* alpha, const float* beta,
+                                const float* initial_state, const void* d_out,
+                                const float* d_final_state, void* dq, void* dk, void* dv,
+                                float* d_alpha, float* d_beta, float* d_initial_state,
+                                int B, int T, int H, int Dk, int Dv, int chunk,
+                                kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Chunk-local gate summary (log-magnitude, sign and zero form of the

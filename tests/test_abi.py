@@ -34,13 +34,14 @@ def test_exports_every_declared_symbol(lib):
     syms = declared_symbols()
     assert {"kda_chunk_forward", "kda_chunk_forward_states", "kda_chunk_forward_prologue",
             "kda_chunk_forward_phase", "kda_decode_step_phase", "kda_chunk_forward_varlen", "kda_decode_step", "kda_chunk_forward_workspace_size",
+            "kda_chunk_backward", "kda_chunk_backward_workspace_size",
             "kda_gate_prep", "kda_status_string", "kda_abi_version"} <= set(syms)
     for s in syms:
         assert hasattr(lib, s), s
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 5
+    assert lib.kda_abi_version() == 6
     for s in range(8):
         assert lib.kda_status_string(s)
     assert lib.kda_status_string(99) == b"unknown status"
@@ -253,3 +254,54 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 4, 1, 16)
     with pytest.raises(ValueError):
         kda.chunk_forward(x, x, x, x, torch.zeros(1, 4, 1), chunk=16, workspace=torch.zeros(1))
+
+
+def test_backward_workspace_size(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.kda_chunk_backward_workspace_size(1, 8192, 32, 128, 128, 64, BF16, ctypes.byref(n)) == OK
+    nu = 32 * 128
+    fwd = nu * (3 * 64 * 128 * 2 + 64 * 128 * 2 + 64 * 64 * 2 + 128 * 4 + 1)
+    # plus Tinv, chunk states, Delta, state gradients, X (fp32) and one flag byte per unit
+    extra = nu * (64 * 64 * 4 + 128 * 128 * 4 + 64 * 128 * 4 + 128 * 128 * 4 + 64 * 128 * 4) + nu
+    assert n.value == fwd + extra
+    assert lib.kda_chunk_backward_workspace_size(1, 100, 2, 16, 16, 64, BF16, ctypes.byref(n)) == UNSUP
+    assert lib.kda_chunk_backward_workspace_size(1, 100, 2, 64, 64, 16, BF16, ctypes.byref(n)) == UNSUP
+    assert lib.kda_chunk_backward_workspace_size(1, 100, 2, 128, 64, 64, F32, ctypes.byref(n)) == UNSUP
+    assert lib.kda_chunk_backward_workspace_size(1, 0, 2, 64, 64, 64, F32, ctypes.byref(n)) == OK
+    assert n.value == 0
+    assert lib.kda_chunk_backward_workspace_size(1, 10, 2, 64, 64, 64, F32, None) == NULLP
+
+
+def test_backward_validation(lib):
+    f = Fake()
+    n = ctypes.c_size_t(0)
+    assert lib.kda_chunk_backward_workspace_size(1, 64, 2, 64, 64, 64, F32, ctypes.byref(n)) == OK
+    need = n.value
+
+    def bw(ptrs=None, T=64, Dk=64, chunk=64, dt=F32, mode=1, flags=0, ws=True, wsb=None):
+        p = ptrs if ptrs is not None else [f() for _ in range(14)]
+        return lib.kda_chunk_backward(*p, 1, T, 2, Dk, 64, chunk, dt, mode, flags,
+                                      f(need + 4096) if ws else None,
+                                      need if wsb is None else wsb, None)
+
+    base = [f() for _ in range(14)]
+    assert bw(ptrs=[None] + base[1:]) == NULLP                    # q
+    assert bw(ptrs=base[:6] + [None] + base[7:]) == NULLP         # d_out
+    assert bw(ws=False) == NULLP
+    assert bw(wsb=need - 1) == WS
+    assert bw(chunk=16) == UNSUP
+    assert bw(Dk=16) == UNSUP
+    assert bw(mode=5) == UNSUP
+    assert bw(flags=4) == UNSUP                                    # segments are forward-only
+    mis = list(base)
+    mis[6] = ctypes.c_void_p(base[6].value + 4)                   # d_out: 16-byte rule
+    assert bw(ptrs=mis) == MISAL
+    al = list(base)
+    al[8] = base[0]                                               # dq == q
+    assert bw(ptrs=al) == ALIAS
+    al = list(base)
+    al[9] = base[8]                                               # dk == dq
+    assert bw(ptrs=al) == ALIAS
+    opt = list(base)
+    opt[5] = opt[7] = opt[13] = None                              # S0, dST, dS0 optional
+    assert bw(ptrs=opt, T=0) == OK                                # nothing to do, no HIP call

@@ -1,0 +1,129 @@
+"""GPU parity of the chunkwise backward (kda_chunk_backward) against the
+oracle's token-by-token gradients.
+
+Each case prints its name before touching the GPU.  Inputs come from
+workloads.py; expected values only from oracle/.  Error measure as for the
+forward (tests/parity.py): per (b, h) slice, max |gpu - oracle| / max |oracle|,
+for every gradient separately; fp32 within 1e-4, bf16 within 2e-2.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_forward_amd as kda
+import oracle
+import workloads
+from parity import TOL, np32, oracle_threads, say, slice_err_out, slice_err_state
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+# (name, base workload, overrides, with S0, with dST)
+CASES = [
+    ("f32_kda_d64_c64_T200", 0, dict(B=1, H=2, T=200, D=64, chunk=64), True, True),
+    ("f32_ckda_d64_c64_T130", 1, dict(B=2, H=2, T=130, D=64, chunk=64), False, True),
+    ("f32_ckda_d32_c32_T77", 1, dict(B=1, H=3, T=77, D=32, chunk=32), True, False),
+    ("f32_kda_d64_c32_T1", 0, dict(B=2, H=1, T=1, D=64, chunk=32), True, True),
+    ("bf16_kda_d128_c64_T300", 2, dict(B=1, H=2, T=300, chunk=64), True, True),
+    ("bf16_ckda_d128_c64_T257", 3, dict(B=1, H=2, T=257, chunk=64), True, False),
+    ("bf16_ckda_d64_c64_T192", 3, dict(B=2, H=1, T=192, D=64, chunk=64), False, True),
+    ("bf16_ckda_d128_c32_T100", 3, dict(B=1, H=2, T=100, chunk=32), True, True),
+    ("bf16_kda_d32_c32_T65", 2, dict(B=1, H=2, T=65, D=32, chunk=32), False, False),
+]
+
+GRADS = [("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("d_alpha", "dalpha"), ("d_beta", "dbeta")]
+
+
+def _inputs(base, ov, s0, dst):
+    w = workloads.workload(base, **ov)
+    if s0 and w.s0_std is None:
+        w = workloads.workload(base, **ov, s0_std=0.5)
+    if not s0:
+        w = workloads.workload(base, **{**ov, "s0_std": None})
+    inp = workloads.make_prefill(w)
+    dO, dST = workloads.make_backward_seeds(w, dst=dst)
+    return w, inp, dO, dST
+
+
+def _oracle(inp, dO, dST):
+    s0 = None if inp["S0"] is None else np32(inp["S0"])
+    return oracle.backward(np32(inp["q"]), np32(inp["k"]), np32(inp["v"]), np32(inp["alpha"]),
+                           np32(inp["beta"]), np32(dO), s0, None if dST is None else np32(dST),
+                           nthreads=oracle_threads())
+
+
+def _gpu(w, inp, dO, dST, **kw):
+    d = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
+    g = kda.chunk_backward(d["q"], d["k"], d["v"], d["alpha"], d["beta"], dO.to(DEV), d["S0"],
+                           None if dST is None else dST.to(DEV), chunk=w.chunk, mode=w.mode, **kw)
+    torch.cuda.synchronize()
+    return g
+
+
+def _errors(g, ref):
+    errs = {}
+    for gn, rn in GRADS:
+        a, b = np32(g[gn]), ref[rn]
+        if a.ndim == 3:
+            a, b = a[..., None], b[..., None]
+        errs[gn] = slice_err_out(a, b)
+    errs["d_initial_state"] = slice_err_state(np32(g["d_initial_state"]), ref["dS0"])
+    return errs
+
+
+@pytest.mark.parametrize("name,base,ov,s0,dst", CASES, ids=[c[0] for c in CASES])
+def test_backward_matches_oracle(name, base, ov, s0, dst):
+    w, inp, dO, dST = _inputs(base, ov, s0, dst)
+    say(f"[backward] {name}: {w} S0={s0} dST={dst}")
+    ref = _oracle(inp, dO, dST)
+    g = _gpu(w, inp, dO, dST)
+    errs = _errors(g, ref)
+    say("  " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= TOL[w.dtype], (k, v)
+
+
+def test_backward_empty_sequence_passes_dst_through():
+    """T = 0: the loss is <S0, dST>, so dS0 = dST and nothing else is written."""
+    say("[backward] T=0")
+    B, H, D = 1, 2, 64
+    z = torch.empty((B, 0, H, D), device=DEV)
+    dST = torch.randn((B, H, D, D), device=DEV)
+    g = kda.chunk_backward(z, z, z, z, torch.empty((B, 0, H), device=DEV), z, None, dST,
+                           chunk=64, mode=workloads.CKDA)
+    torch.cuda.synchronize()
+    assert torch.equal(g["d_initial_state"], dST)
+
+
+def test_backward_small_gates_take_the_direct_form():
+    """Gates at exactly 0 and just below 2^-6 in magnitude (the quotient form's
+    limit) in every chunk: d_alpha there comes from the direct per-channel
+    form and must still match the oracle."""
+    w = workloads.workload(1, B=1, H=2, T=150, D=64, chunk=64, s0_std=0.5)
+    inp = workloads.make_prefill(w)
+    a = inp["alpha"]
+    gen = torch.Generator().manual_seed(5)
+    m = torch.rand(a.shape, generator=gen)
+    a[m < 0.02] = 0.0
+    a[(m >= 0.02) & (m < 0.04)] = 0.0151
+    a[(m >= 0.04) & (m < 0.06)] = -0.003
+    dO, dST = workloads.make_backward_seeds(w)
+    say("[backward] small gates f32 d64 T150")
+    ref = _oracle(inp, dO, dST)
+    g = _gpu(w, inp, dO, dST)
+    errs = _errors(g, ref)
+    say("  " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= TOL[w.dtype], (k, v)
+
+
+def test_backward_without_initial_state_gradient():
+    """d_initial_state = NULL is allowed and changes nothing else."""
+    w, inp, dO, dST = _inputs(1, dict(B=1, H=2, T=100, D=32, chunk=32), True, True)
+    say("[backward] no d_initial_state")
+    g1 = _gpu(w, inp, dO, dST)
+    g2 = _gpu(w, inp, dO, dST, want_d_initial_state=False)
+    assert g2["d_initial_state"] is None
+    for gn, _ in GRADS:
+        assert torch.equal(g1[gn], g2[gn]), gn

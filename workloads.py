@@ -183,6 +183,20 @@ def make_prefill_phase(w: Workload, theta_max: float = 3.0, device="cpu", seed: 
     return inp
 
 
+def make_backward_seeds(w: Workload, device="cpu", seed: int | None = None, dst: bool = True):
+    """Loss gradients for a backward pass: dO [B,T,H,D] ~ N(0,1) in w.dtype and
+    dST [B,H,D,D] ~ N(0,1) fp32 (None unless dst), from seed w.seed + 1000 (so
+    the forward inputs of the same workload are unchanged).  Draw order: dO,
+    dST."""
+    g = _gen((w.seed if seed is None else seed) + 1000, device)
+    B, T, H, D = w.B, w.T, w.H, w.D
+    dO = torch.randn((B, T, H, D), generator=g, device=device, dtype=torch.float32).to(w.dtype)
+    dST = None
+    if dst:
+        dST = torch.randn((B, H, D, D), generator=g, device=device, dtype=torch.float32)
+    return dO.contiguous(), dST
+
+
 def make_decode(w: Workload, steps: int | None = None, device="cpu", seed: int | None = None):
     """Inputs for stacked decode steps: S0 [B,H,D,D] fp32, then per step
     q, k, v [N,B,H,D] (w.dtype), alpha [N,B,H,D] fp32, beta [N,B,H] fp32."""
