@@ -35,6 +35,8 @@
 //   bwd_chain_kernel   the reverse chain, one workgroup per (b, h, 16 columns)
 //   bwd_local_kernel   every chunk's gradients, one workgroup per chunk
 //   bwd_tiny_kernel    the direct dalpha of small gates, flagged chunks only
+#include <type_traits>
+
 #include "kda_chunk.hpp"
 #include "kda_launch.hpp"
 
@@ -70,12 +72,24 @@ struct RelayoutLds {
     static constexpr size_t BYTES = (P + (size_t)C * C) * sizeof(T);
 };
 
+// copy NV consecutive elements (one lane's fragment slots, NV * sizeof(T)
+// bytes: 8 or 16, aligned to that size)
+template <typename T, int NV>
+struct FragVec {
+    static constexpr int BYTES = NV * (int)sizeof(T);
+    using V = typename std::conditional<BYTES == 16, uint4, uint2>::type;
+    __attribute__((aligned(16))) T e[NV];
+    __device__ __forceinline__ void load(const T* p) { *reinterpret_cast<V*>(e) = *reinterpret_cast<const V*>(p); }
+    __device__ __forceinline__ void store(T* p) const { *reinterpret_cast<V*>(p) = *reinterpret_cast<const V*>(e); }
+};
+
 template <typename T, int C, int DK>
 __global__ __launch_bounds__(kBwdThreads) void relayout_kernel(T* __restrict__ W, T* __restrict__ QG,
                                                                T* __restrict__ Kt, T* __restrict__ P)
 {
-    constexpr int KB = KBlock<T, C, DK>::value;
+    constexpr int KB = KBlock<T, C, DK>::value, NV = KB / 4;
     using L = RelayoutLds<T, C, DK>;
+    using FV = FragVec<T, NV>;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     T* s = reinterpret_cast<T*>(lds);
     const size_t unit = blockIdx.x;
@@ -85,28 +99,54 @@ __global__ __launch_bounds__(kBwdThreads) void relayout_kernel(T* __restrict__ W
     T* gP = P + unit * C * C;
     const int tid = threadIdx.x;
     int r, k;
-    for (int o = tid; o < C * DK; o += kBwdThreads) {
-        frag_pos<KB>(o, DK, r, k);                 // W, Q*Gamma: [C][DK]
-        s[L::W + r * DK + k] = gW[o];
-        s[L::Q + r * DK + k] = gQ[o];
-        frag_pos<KB>(o, C, r, k);                  // Ktil^T: [DK][C]
-        s[L::K + r * C + k] = gK[o];
+    // read: one lane fragment (NV slots) per step, scattered to row-major LDS
+    for (int f = tid; f < C * DK / NV; f += kBwdThreads) {
+        FV w, q, kt;
+        w.load(gW + f * NV);
+        q.load(gQ + f * NV);
+        kt.load(gK + f * NV);
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            frag_pos<KB>(f * NV + j, DK, r, k);        // W, Q*Gamma: [C][DK]
+            s[L::W + r * DK + k] = w.e[j];
+            s[L::Q + r * DK + k] = q.e[j];
+            frag_pos<KB>(f * NV + j, C, r, k);         // Ktil^T: [DK][C]
+            s[L::K + r * C + k] = kt.e[j];
+        }
     }
-    for (int o = tid; o < C * C; o += kBwdThreads) {
-        frag_pos<KB>(o, C, r, k);
-        s[L::P + r * C + k] = gP[o];
+    for (int f = tid; f < C * C / NV; f += kBwdThreads) {
+        FV p;
+        p.load(gP + f * NV);
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            frag_pos<KB>(f * NV + j, C, r, k);
+            s[L::P + r * C + k] = p.e[j];
+        }
     }
     __syncthreads();
-    for (int o = tid; o < C * DK; o += kBwdThreads) {
-        frag_pos<KB>(o, C, r, k);                  // W^T, (Q*Gamma)^T: rows DK, K = C
-        gW[o] = s[L::W + k * DK + r];
-        gQ[o] = s[L::Q + k * DK + r];
-        frag_pos<KB>(o, DK, r, k);                 // Ktil: rows C, K = DK
-        gK[o] = s[L::K + k * C + r];
+    // write the transposes, one lane fragment per step
+    for (int f = tid; f < C * DK / NV; f += kBwdThreads) {
+        FV w, q, kt;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            frag_pos<KB>(f * NV + j, C, r, k);         // W^T, (Q*Gamma)^T: rows DK, K = C
+            w.e[j] = s[L::W + k * DK + r];
+            q.e[j] = s[L::Q + k * DK + r];
+            frag_pos<KB>(f * NV + j, DK, r, k);        // Ktil: rows C, K = DK
+            kt.e[j] = s[L::K + k * C + r];
+        }
+        w.store(gW + f * NV);
+        q.store(gQ + f * NV);
+        kt.store(gK + f * NV);
     }
-    for (int o = tid; o < C * C; o += kBwdThreads) {
-        frag_pos<KB>(o, C, r, k);
-        gP[o] = s[L::P + k * C + r];
+    for (int f = tid; f < C * C / NV; f += kBwdThreads) {
+        FV p;
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            frag_pos<KB>(f * NV + j, C, r, k);
+            p.e[j] = s[L::P + k * C + r];
+        }
+        p.store(gP + f * NV);
     }
 }
 
@@ -148,8 +188,53 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
     }
     __syncthreads();
 
+    // one chunk's operands in registers; chunk n - 1's are loaded while
+    // chunk n is processed
+    struct Ops {
+        F pt[G::NKC], kt[G::NKD], qt[G::SPW][G::NKC], wt[G::SPW][G::NKC], dof[G::NKC];
+        f32x4 gc[G::SPW];
+    };
+    auto load_ops = [&](Ops& o, int n) {
+        const size_t unit = (size_t)bh * NC + n;
+        const int mt = wave < G::NM ? wave : G::NM - 1;
+        const T* pt = static_cast<const T*>(a.PT) + unit * C * C + (size_t)mt * G::NKC * 64 * G::NV;
+        const T* kt = static_cast<const T*>(a.Ktil) + unit * C * DK + (size_t)mt * G::NKD * 64 * G::NV;
+#pragma unroll
+        for (int s = 0; s < G::NKC; ++s) o.pt[s] = F::load(pt + (s * 64 + lane) * G::NV);
+#pragma unroll
+        for (int s = 0; s < G::NKD; ++s) o.kt[s] = F::load(kt + (s * 64 + lane) * G::NV);
+#pragma unroll
+        for (int u = 0; u < G::SPW; ++u) {
+            const int t = min(wave + 4 * u, G::NT - 1);
+            const T* qt = static_cast<const T*>(a.QGT) + unit * DK * C + (size_t)t * G::NKC * 64 * G::NV;
+            const T* wt = static_cast<const T*>(a.WT) + unit * DK * C + (size_t)t * G::NKC * 64 * G::NV;
+#pragma unroll
+            for (int s = 0; s < G::NKC; ++s) {
+                o.qt[u][s] = F::load(qt + (s * 64 + lane) * G::NV);
+                o.wt[u][s] = F::load(wt + (s * 64 + lane) * G::NV);
+            }
+            o.gc[u] = *reinterpret_cast<const f32x4*>(a.GC + unit * DK + 16 * t + 4 * lg);
+        }
+        // dO of this chunk's column slice as B fragments over tokens
+#pragma unroll
+        for (int s = 0; s < G::NKC; ++s) {
+            float f[G::NV];
+#pragma unroll
+            for (int j = 0; j < G::NV; ++j) {
+                const int kk = G::KB == 32 ? 16 * (j >> 2) + 4 * lg + (j & 3) : 4 * lg + j;
+                const int row = n * C + s * G::KB + kk;
+                f[j] = row < a.T ? to_f32(dO[(((size_t)b * a.T + row) * H + h) * Dv + col]) : 0.f;
+            }
+            o.dof[s] = F::from(f);
+        }
+    };
+
+    Ops cur;
+    load_ops(cur, NC - 1);
     for (int n = NC - 1; n >= 0; --n) {
         const size_t unit = (size_t)bh * NC + n;
+        Ops nxt;
+        if (n > 0) load_ops(nxt, n - 1);
         // the gradient of the state leaving chunk n
 #pragma unroll
         for (int u = 0; u < G::SPW; ++u) {
@@ -160,31 +245,16 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
                     a.DSN[(unit * DK + 16 * t + 4 * lg + i) * Dv + col] = dS[u][i];
             }
         }
-        // dO of this chunk's column slice as B fragments over tokens
-        F dof[G::NKC];
-#pragma unroll
-        for (int s = 0; s < G::NKC; ++s) {
-            float f[G::NV];
-#pragma unroll
-            for (int j = 0; j < G::NV; ++j) {
-                const int kk = G::KB == 32 ? 16 * (j >> 2) + 4 * lg + (j & 3) : 4 * lg + j;
-                const int row = n * C + s * G::KB + kk;
-                f[j] = row < a.T ? to_f32(dO[(((size_t)b * a.T + row) * H + h) * Dv + col]) : 0.f;
-            }
-            dof[s] = F::from(f);
-        }
         F sf[G::NKD];
 #pragma unroll
         for (int s = 0; s < G::NKD; ++s) sf[s] = sSf[s * 64 + lane];
         // X for token tile `wave`
         if (G::NM == 4 || wave < G::NM) {
-            const T* pt = static_cast<const T*>(a.PT) + unit * C * C + (size_t)wave * G::NKC * 64 * G::NV;
-            const T* kt = static_cast<const T*>(a.Ktil) + unit * C * DK + (size_t)wave * G::NKD * 64 * G::NV;
             f32x4 acc = zero4();
 #pragma unroll
-            for (int s = 0; s < G::NKC; ++s) acc = mma(F::load(pt + (s * 64 + lane) * G::NV), dof[s], acc);
+            for (int s = 0; s < G::NKC; ++s) acc = mma(cur.pt[s], cur.dof[s], acc);
 #pragma unroll
-            for (int s = 0; s < G::NKD; ++s) acc = mma(F::load(kt + (s * 64 + lane) * G::NV), sf[s], acc);
+            for (int s = 0; s < G::NKD; ++s) acc = mma(cur.kt[s], sf[s], acc);
             float* xb = a.XB + (unit * C + 16 * wave + 4 * lg) * Dv + col;
             f32x4 neg;
 #pragma unroll
@@ -203,21 +273,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
         for (int u = 0; u < G::SPW; ++u) {
             const int t = wave + 4 * u;
             if (G::NT % 4 == 0 || t < G::NT) {
-                const f32x4 gc = *reinterpret_cast<const f32x4*>(a.GC + unit * DK + 16 * t + 4 * lg);
                 f32x4 acc;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = gc[i] * dS[u][i];
-                const T* qt = static_cast<const T*>(a.QGT) + unit * DK * C + (size_t)t * G::NKC * 64 * G::NV;
-                const T* wt = static_cast<const T*>(a.WT) + unit * DK * C + (size_t)t * G::NKC * 64 * G::NV;
+                for (int i = 0; i < 4; ++i) acc[i] = cur.gc[u][i] * dS[u][i];
 #pragma unroll
-                for (int s = 0; s < G::NKC; ++s) acc = mma(F::load(qt + (s * 64 + lane) * G::NV), dof[s], acc);
+                for (int s = 0; s < G::NKC; ++s) acc = mma(cur.qt[u][s], cur.dof[s], acc);
 #pragma unroll
-                for (int s = 0; s < G::NKC; ++s) acc = mma(F::load(wt + (s * 64 + lane) * G::NV), xf[s], acc);
+                for (int s = 0; s < G::NKC; ++s) acc = mma(cur.wt[u][s], xf[s], acc);
                 dS[u] = acc;
                 put_tile<T, G::KB>(sSf, t, lane, acc);
             }
         }
         __syncthreads();
+        if (n > 0) cur = nxt;
     }
     if (a.dS0) {
 #pragma unroll
@@ -233,9 +301,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
 }
 
 // ---- per-chunk gradients ----------------------------------------------------
+// One workgroup of 8 wavefronts per chunk.  Wave w owns the channel tiles
+// ct = w, w + 8, ..; its lane (n, g) owns, for each such tile, the rows
+// 16 mt + 4 g + m (every token tile mt, m = 0..3) of channel 16 ct + n: the
+// C-layout of the F1 / F2 / F3 accumulator tiles, so every per-(row, channel)
+// quantity stays in that lane, and the 64 rows of one channel sit in the four
+// lanes n, n + 16, n + 32, n + 48 of one wavefront (the prefix and suffix
+// sums of dalpha are shuffles among them).
+constexpr int kLocalThreads = 512;
+constexpr int kLocalWaves = kLocalThreads / 64;
+
 template <typename T, int C, int DK>
 struct LocalGeom {
-    static constexpr int NM = C / 16, NCT = DK / 16, CTW = (NCT + 3) / 4;
+    static constexpr int NM = C / 16, NCT = DK / 16, CTW = (NCT + kLocalWaves - 1) / kLocalWaves;
     static constexpr int DVMAX = sizeof(T) == 4 ? 64 : 128;
     static constexpr int LDV = DVMAX + 4;      // row stride of the [C][Dv] fp32 arrays
     static constexpr int LDT = C + 4;          // row stride of the [C][C] fp32 arrays
@@ -246,20 +324,19 @@ struct LocalGeom {
     // R1, GEMM phase: dO, Delta, Y
     static constexpr size_t DO = R0, DL = DO + 4 * (size_t)C * LDV, YY = DL + 4 * (size_t)C * LDV;
     static constexpr size_t R1A = YY + 4 * (size_t)C * LDV;
-    // R1, weight phase: alpha (fp32), k, q (io type), B1^T, B3^T; then Za, Zb over k, q, ...
+    // R1, weight phase: alpha (fp32), k, q (io type), B1^T, B3^T
     static constexpr size_t AL = R0, KK = AL + 4 * (size_t)C * DK, QQ = al16(KK + sizeof(T) * C * DK);
     static constexpr size_t B1T = al16(QQ + sizeof(T) * C * DK), B3T = B1T + 4 * (size_t)C * LDT;
     static constexpr size_t R1B = B3T + 4 * (size_t)C * LDT;
-    static constexpr size_t ZA = KK, ZB = ZA + 4 * (size_t)C * DK, R1C = ZB + 4 * (size_t)C * DK;
     // small arrays
-    static constexpr size_t R1 = R1A > R1B ? (R1A > R1C ? R1A : R1C) : (R1B > R1C ? R1B : R1C);
-    static constexpr size_t BETA = R1, DB = BETA + 4 * C, DBW = DB + 4 * C, SIG = DBW + 16 * C;
-    static constexpr size_t BYTES = SIG + 4 * DK + 16;
+    static constexpr size_t R1 = R1A > R1B ? R1A : R1B;
+    static constexpr size_t BETA = R1, DB = BETA + 4 * C, DBW = DB + 4 * C;
+    static constexpr size_t BYTES = DBW + 4 * (size_t)kLocalWaves * C;
     static_assert(BYTES <= 160 * 1024, "LDS");
 };
 
 template <typename T, int C, int DK>
-__global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(BwdLocalArgs a)
+__global__ __launch_bounds__(kLocalThreads) void bwd_local_kernel(BwdLocalArgs a)
 {
     using G = LocalGeom<T, C, DK>;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -274,13 +351,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(BwdLocalArgs a)
     T* sQ = reinterpret_cast<T*>(lds + G::QQ);
     float* sB1T = reinterpret_cast<float*>(lds + G::B1T);
     float* sB3T = reinterpret_cast<float*>(lds + G::B3T);
-    float* sZa = reinterpret_cast<float*>(lds + G::ZA);
-    float* sZb = reinterpret_cast<float*>(lds + G::ZB);
     float* sBeta = reinterpret_cast<float*>(lds + G::BETA);
     float* sDB = reinterpret_cast<float*>(lds + G::DB);
-    float* sDBw = reinterpret_cast<float*>(lds + G::DBW);      // [4 waves][C]
-    float* sSig = reinterpret_cast<float*>(lds + G::SIG);
-    constexpr int LDV = G::LDV, LDT = G::LDT, NM = G::NM;
+    float* sDBw = reinterpret_cast<float*>(lds + G::DBW);     // [waves][C]
+    constexpr int LDV = G::LDV, LDT = G::LDT, NM = G::NM, NW = kLocalWaves, NTH = kLocalThreads;
 
     const int Dv = a.Dv, H = a.H, NC = a.NC, NVT = Dv / 16;
     const size_t unit = blockIdx.x;
@@ -294,17 +368,17 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(BwdLocalArgs a)
 
     // ---- load -------------------------------------------------------------------
     bool tiny = false;
-    for (int idx = tid; idx < nvalid * DK; idx += kBwdThreads)
+    for (int idx = tid; idx < nvalid * DK; idx += NTH)
         tiny |= fabsf(a.alpha[tok(idx / DK) * DK + idx % DK]) < kTinyGate;
     const int any_tiny = __syncthreads_or(tiny);
     if (tid < C) {
         sBeta[tid] = tid < nvalid ? a.beta[tok(tid)] : 0.f;
         sDB[tid] = 0.f;
     }
-    for (int idx = tid; idx < C * C; idx += kBwdThreads)
+    for (int idx = tid; idx < C * C; idx += NTH)
         sT[(idx / C) * LDT + idx % C] = a.Tm[unit * C * C + idx];
     const T* dO = static_cast<const T*>(a.dO);
-    for (int idx = tid; idx < C * (Dv / 4); idx += kBwdThreads) {
+    for (int idx = tid; idx < C * (Dv / 4); idx += NTH) {
         const int r = idx / (Dv / 4), c4 = 4 * (idx % (Dv / 4));
         float4 o = make_float4(0.f, 0.f, 0.f, 0.f), d = o;
         if (r < nvalid) {
@@ -319,7 +393,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(BwdLocalArgs a)
 
     // ---- y = Tinv^T X, dv = diag(beta) y ------------------------------------------
     T* dv = static_cast<T*>(a.dv);
-    for (int job = wave; job < NM * NVT; job += 4) {
+    for (int job = wave; job < NM * NVT; job += NW) {
         const int mt = job / NVT, vt = job % NVT;
         f32x4 acc = zero4();
         for (int s = mt; s < NM; ++s) {          // Tinv[k][m] = 0 for k < m
@@ -343,7 +417,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(BwdLocalArgs a)
 
     // ---- dbeta, first term: v_r . y_r ---------------------------------------------
     {
-        constexpr int TPR = kBwdThreads / C;       // threads per row
+        constexpr int TPR = NTH / C;               // threads per row
         const int r = tid / TPR, part = tid % TPR;
         const T* v = static_cast<const T*>(a.v);
         float sacc = 0.f;
@@ -357,7 +431,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(BwdLocalArgs a)
     // ---- B1 = dO Delta^T (i <= r), B3 = Y Delta^T (i < r): lower tiles --------------
     {
         constexpr int NP = NM * (NM + 1) / 2;
-        for (int job = wave; job < 2 * NP; job += 4) {
+        for (int job = wave; job < 2 * NP; job += NW) {
             const int which = job / NP;
             int p = job % NP, mt = 0;
             while (p > mt) { p -= mt + 1; ++mt; }
@@ -375,12 +449,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(BwdLocalArgs a)
 
     // ---- F1 = dO S^T, F2 = Y S^T, F3 = Delta dSn^T; sigma = rowdot(dSn, S) ----------
     f32x4 F1[G::CTW][NM], F2[G::CTW][NM], F3[G::CTW][NM];
+    float sigv[G::CTW];
 #pragma unroll
     for (int cw = 0; cw < G::CTW; ++cw) {
-        const int ct = wave + 4 * cw;
+        const int ct = wave + NW * cw;
+        sigv[cw] = 0.f;
 #pragma unroll
         for (int mt = 0; mt < NM; ++mt) F1[cw][mt] = F2[cw][mt] = F3[cw][mt] = zero4();
-        if (G::NCT % 4 == 0 || ct < G::NCT) {
+        if (ct < G::NCT) {
             const float* ps = a.CS32 + (unit * DK + 16 * ct + ln) * Dv + 4 * lg;
             const float* pn = a.DSN + (unit * DK + 16 * ct + ln) * Dv + 4 * lg;
             float sig = 0.f;
@@ -399,12 +475,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(BwdLocalArgs a)
             }
             sig += __shfl_xor(sig, 16);
             sig += __shfl_xor(sig, 32);
-            if (lg == 0) sSig[16 * ct + ln] = sig;
+            sigv[cw] = sig;
         }
     }
     // the small-gate kernel needs y: it replaces X in place (every read of X is done)
     if (any_tiny) {
-        for (int idx = tid; idx < C * Dv; idx += kBwdThreads)
+        for (int idx = tid; idx < C * Dv; idx += NTH)
             a.XB[unit * C * Dv + idx] = sY[(idx / Dv) * LDV + idx % Dv];
     }
     __syncthreads();
@@ -413,7 +489,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(BwdLocalArgs a)
     {
         const T* kg = static_cast<const T*>(a.k);
         const T* qg = static_cast<const T*>(a.q);
-        for (int idx = tid; idx < C * (DK / 4); idx += kBwdThreads) {
+        for (int idx = tid; idx < C * (DK / 4); idx += NTH) {
             const int r = idx / (DK / 4), c4 = 4 * (idx % (DK / 4));
             float4 al = make_float4(1.f, 1.f, 1.f, 1.f);
             Vec4<T> kv = Vec4<T>::zero(), qv = Vec4<T>::zero();
@@ -426,7 +502,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(BwdLocalArgs a)
             *reinterpret_cast<Vec4<T>*>(sK + r * DK + c4) = kv;
             *reinterpret_cast<Vec4<T>*>(sQ + r * DK + c4) = qv;
         }
-        for (int idx = tid; idx < C * C; idx += kBwdThreads) {
+        for (int idx = tid; idx < C * C; idx += NTH) {
             const int r = idx / C, i = idx % C;
             sB1T[i * LDT + r] = sB1[r * LDT + i];
             sB3T[i * LDT + r] = sB3[r * LDT + i];
@@ -434,7 +510,6 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(BwdLocalArgs a)
     }
     __syncthreads();
 
-    float Za[G::CTW][NM][4], Zb[G::CTW][NM][4];
     float dbp[NM][4];
 #pragma unroll
     for (int mt = 0; mt < NM; ++mt)
@@ -444,46 +519,27 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(BwdLocalArgs a)
     T* dkg = static_cast<T*>(a.dk);
 #pragma unroll
     for (int cw = 0; cw < G::CTW; ++cw) {
-        const int ct = wave + 4 * cw;
-        if (!(G::NCT % 4 == 0 || ct < G::NCT)) continue;
+        const int ct = wave + NW * cw;
+        if (ct >= G::NCT) continue;
         const int c = 16 * ct + ln;
         auto al = [&](int t) { return sAl[t * DK + c]; };
         auto kf = [&](int t) { return to_f32(sK[t * DK + c]); };
         auto qf = [&](int t) { return to_f32(sQ[t * DK + c]); };
-        // Gamma_r (inclusive prefix products) and rho(C-1, r) of the lane's rows
-        float gam[NM][4], gend[NM][4];
-        {
-            float p = 1.f;
-            int t = 0;
-#pragma unroll
-            for (int mt = 0; mt < NM; ++mt)
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const int r = 16 * mt + 4 * lg + m;
-                    for (; t <= r; ++t) p *= al(t);
-                    gam[mt][m] = p;
-                }
-            p = 1.f;
-            t = C - 1;
-#pragma unroll
-            for (int mt = NM - 1; mt >= 0; --mt)
-#pragma unroll
-                for (int m = 3; m >= 0; --m) {
-                    const int r = 16 * mt + 4 * lg + m;
-                    for (; t > r; --t) p *= al(t);
-                    gend[mt][m] = p;
-                }
-        }
+        float Za[NM][4], Zb[NM][4];
+        float gcl = 1.f;                   // Gamma of the lane's last row (row C - 1 in lanes lg = 3)
+        const float a0 = al(0);
 #pragma unroll
         for (int mt = 0; mt < NM; ++mt) {
             const int r0 = 16 * mt + 4 * lg, r3 = r0 + 3;
-            // L sums over i < r0 with w = rho(r0, i), then rho(r0 + m, r0)
+            // L sums over i < r0 with w = rho(r0, i), then rho(r0 + m, r0); the
+            // final w is rho(r0, 0), so Gamma_{r0+m} = alpha_0 w rho(r0 + m, r0)
             float lq[4] = {0.f, 0.f, 0.f, 0.f}, lk[4] = {0.f, 0.f, 0.f, 0.f};
+            float fL[4] = {1.f, 1.f, 1.f, 1.f}, wL = 1.f;
             {
-                float w = 1.f;
+#pragma unroll 4
                 for (int i = r0 - 1; i >= 0; --i) {
-                    w *= al(i + 1);
-                    const float wk = w * kf(i);
+                    wL *= al(i + 1);
+                    const float wk = wL * kf(i);
                     const float4 b1 = *reinterpret_cast<const float4*>(sB1T + i * LDT + r0);
                     const float4 b3 = *reinterpret_cast<const float4*>(sB3T + i * LDT + r0);
                     lq[0] += b1.x * wk; lq[1] += b1.y * wk; lq[2] += b1.z * wk; lq[3] += b1.w * wk;
@@ -493,11 +549,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(BwdLocalArgs a)
 #pragma unroll
                 for (int m = 1; m < 4; ++m) {
                     f *= al(r0 + m);
+                    fL[m] = f;
                     lq[m] *= f;
                     lk[m] *= f;
                     // pairs inside the group: r0 <= i < r0 + m
                     float wi = 1.f;
-                    for (int i = r0 + m - 1; i >= r0; --i) {
+#pragma unroll
+                    for (int d = 1; d <= m; ++d) {
+                        const int i = r0 + m - d;
                         wi *= al(i + 1);
                         const float wk = wi * kf(i);
                         lq[m] += sB1[(r0 + m) * LDT + i] * wk;
@@ -505,13 +564,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(BwdLocalArgs a)
                     }
                 }
             }
-            // U sums over j > r3 with w = rho(j, r3), then rho(r3, r0 + m)
+            // U sums over j > r3 with w = rho(j, r3), then rho(r3, r0 + m); the
+            // final w is rho(C - 1, r3), so rho(C - 1, r0 + m) = w rho(r3, r0 + m)
             float uq[4] = {0.f, 0.f, 0.f, 0.f}, uk[4] = {0.f, 0.f, 0.f, 0.f};
+            float hU[4] = {1.f, 1.f, 1.f, 1.f}, wU = 1.f;
             {
-                float w = 1.f;
+#pragma unroll 4
                 for (int j = r3 + 1; j < C; ++j) {
-                    w *= al(j);
-                    const float wq = w * qf(j), wk = w * sBeta[j] * kf(j);
+                    wU *= al(j);
+                    const float wq = wU * qf(j), wk = wU * sBeta[j] * kf(j);
                     const float4 b1 = *reinterpret_cast<const float4*>(sB1 + j * LDT + r0);
                     const float4 b3 = *reinterpret_cast<const float4*>(sB3 + j * LDT + r0);
                     uq[0] += b1.x * wq; uq[1] += b1.y * wq; uq[2] += b1.z * wq; uq[3] += b1.w * wq;
@@ -521,10 +582,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(BwdLocalArgs a)
 #pragma unroll
                 for (int m = 2; m >= 0; --m) {
                     f *= al(r0 + m + 1);
+                    hU[m] = f;
                     uq[m] *= f;
                     uk[m] *= f;
                     // pairs inside the group: r0 + m < j <= r3
                     float wj = 1.f;
+#pragma unroll
                     for (int j = r0 + m + 1; j <= r3; ++j) {
                         wj *= al(j);
                         uq[m] += sB1[j * LDT + r0 + m] * wj * qf(j);
@@ -537,18 +600,68 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(BwdLocalArgs a)
                 const int r = r0 + m;
                 const float kr = kf(r), qr = qf(r), br = sBeta[r];
                 const float b1d = sB1[r * LDT + r];
-                const float g = gam[mt][m], ge = gend[mt][m];
+                const float g = a0 * wL * fL[m], ge = wU * hU[m];
                 const float f1 = F1[cw][mt][m], f2 = F2[cw][mt][m], f3 = F3[cw][mt][m];
                 const float dqv = g * f1 + lq[m] + b1d * kr;
                 const float dkv = ge * f3 + uq[m] + b1d * qr - uk[m] - br * (g * f2 + lk[m]);
                 dbp[mt][m] -= kr * (g * f2 + lk[m]);
-                Za[cw][mt][m] = ge * kr * f3;
-                Zb[cw][mt][m] = g * (qr * f1 - br * kr * f2) + qr * lq[m] - br * kr * lk[m] - kr * (uq[m] - uk[m]);
+                Za[mt][m] = ge * kr * f3;
+                Zb[mt][m] = g * (qr * f1 - br * kr * f2) + qr * lq[m] - br * kr * lk[m] - kr * (uq[m] - uk[m]);
+                if (m == 3) gcl = g;
                 if (r < nvalid) {
                     dqg[tok(r) * DK + c] = from_f32<T>(dqv);
                     dkg[tok(r) * DK + c] = from_f32<T>(dkv);
                 }
             }
+        }
+        // alpha_r dalpha_r = Gamma_{C-1} sigma + (sum of Za over rows before r)
+        // + (sum of Zb over rows from r on); the channel's rows are the lanes
+        // ln + 16 j, j = 0..3 (row 16 mt + 4 j + m).  Za is replaced by its
+        // exclusive prefix, then the suffix of Zb completes dalpha.
+        const float gcs = __shfl(gcl, ln + 48) * sigv[cw];
+        float run = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < NM; ++mt) {
+            const float sa = (Za[mt][0] + Za[mt][1]) + (Za[mt][2] + Za[mt][3]);
+            float tot = 0.f, before = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float x = __shfl(sa, ln + 16 * j);
+                tot += x;
+                before += j < lg ? x : 0.f;
+            }
+            float in = run + before;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const float z = Za[mt][m];
+                Za[mt][m] = in;
+                in += z;
+            }
+            run += tot;
+        }
+        run = 0.f;
+#pragma unroll
+        for (int mt = NM - 1; mt >= 0; --mt) {
+            const float sb = (Zb[mt][0] + Zb[mt][1]) + (Zb[mt][2] + Zb[mt][3]);
+            float tot = 0.f, after = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float x = __shfl(sb, ln + 16 * j);
+                tot += x;
+                after += j > lg ? x : 0.f;
+            }
+            float in = run + after;
+#pragma unroll
+            for (int m = 3; m >= 0; --m) {
+                in += Zb[mt][m];
+                const int r = 16 * mt + 4 * lg + m;
+                if (r < nvalid) {
+                    const float av = al(r);
+                    const float z = gcs + Za[mt][m] + in;
+                    a.dalpha[tok(r) * DK + c] = fabsf(av) >= kTinyGate ? z / av : 0.f;
+                }
+            }
+            run += tot;
         }
     }
     // dbeta: sum over the lane's channels, then over the 16 lanes of a row
@@ -561,47 +674,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_local_kernel(BwdLocalArgs a)
             const float sacc = row16_sum(dbp[mt][m]);
             if (ln == 0) sDBw[wave * C + 16 * mt + 4 * lg + m] = sacc;
         }
-    __syncthreads();     // k, q, B1^T, B3^T dead: Za, Zb take their place
-#pragma unroll
-    for (int cw = 0; cw < G::CTW; ++cw) {
-        const int ct = wave + 4 * cw;
-        if (!(G::NCT % 4 == 0 || ct < G::NCT)) continue;
-#pragma unroll
-        for (int mt = 0; mt < NM; ++mt)
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int r = 16 * mt + 4 * lg + m;
-                sZa[r * DK + 16 * ct + ln] = Za[cw][mt][m];
-                sZb[r * DK + 16 * ct + ln] = Zb[cw][mt][m];
-            }
-    }
     __syncthreads();
-    // per channel: Z_r = Gamma_{C-1} sigma + (prefix of Za, r excluded) + (suffix of Zb)
-    if (tid < DK) {
-        const int c = tid;
-        float gc = 1.f;
-        for (int t = 0; t < C; ++t) gc *= sAl[t * DK + c];
-        float pre = 0.f;
-        for (int r = 0; r < C; ++r) {
-            const float z = sZa[r * DK + c];
-            sZa[r * DK + c] = pre;
-            pre += z;
-        }
-        const float base = gc * sSig[c];
-        float suf = 0.f;
-        for (int r = C - 1; r >= 0; --r) {
-            suf += sZb[r * DK + c];
-            sZb[r * DK + c] = base + sZa[r * DK + c] + suf;
-        }
+    if (tid < nvalid) {
+        float sacc = sDB[tid];
+#pragma unroll
+        for (int w = 0; w < NW; ++w) sacc += sDBw[w * C + tid];
+        a.dbeta[tok(tid)] = sacc;
     }
-    __syncthreads();
-    for (int idx = tid; idx < nvalid * DK; idx += kBwdThreads) {
-        const int r = idx / DK, c = idx % DK;
-        const float av = sAl[r * DK + c];
-        a.dalpha[tok(r) * DK + c] = fabsf(av) >= kTinyGate ? sZb[r * DK + c] / av : 0.f;
-    }
-    if (tid < nvalid)
-        a.dbeta[tok(tid)] = sDB[tid] + ((sDBw[tid] + sDBw[C + tid]) + (sDBw[2 * C + tid] + sDBw[3 * C + tid]));
     if (tid == 0) a.FLB[unit] = any_tiny ? 1 : 0;
 }
 
@@ -618,6 +697,7 @@ template <typename T, int C, int DK>
 __global__ __launch_bounds__(kBwdThreads) void bwd_tiny_kernel(BwdLocalArgs a)
 {
     using L = TinyLds<T, C, DK>;
+    static_assert(C <= 64, "one token per lane");
     const size_t unit = blockIdx.x;
     if (!a.FLB[unit]) return;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -655,6 +735,17 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_tiny_kernel(BwdLocalArgs a)
     constexpr int JPL = L::DVMAX / 64;           // columns per lane (at most)
     for (int e = wave; e < cnt; e += 4) {
         const int r = sList[e] / DK, c = sList[e] % DK;
+        // the channel's gates, keys and queries, token t in lane t, broadcast
+        // to the whole wavefront by readlane in the sweeps
+        float at = 1.f, kt = 0.f, qt = 0.f;
+        if (lane < nvalid) {
+            at = a.alpha[tok(lane) * DK + c];
+            kt = to_f32(kg[tok(lane) * DK + c]);
+            qt = to_f32(qg[tok(lane) * DK + c]);
+        }
+        auto bc = [](float x, int t) {
+            return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), t));
+        };
         // S_{r-1}[c, :] forward from the chunk start
         float s[JPL], hh[JPL], g[JPL];
 #pragma unroll
@@ -663,35 +754,35 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_tiny_kernel(BwdLocalArgs a)
             s[x] = j < Dv ? a.CS32[(unit * DK + c) * Dv + j] : 0.f;
         }
         for (int t = 0; t < r; ++t) {
-            const float at = a.alpha[tok(t) * DK + c], kt = to_f32(kg[tok(t) * DK + c]);
+            const float a_t = bc(at, t), k_t = bc(kt, t);
 #pragma unroll
             for (int x = 0; x < JPL; ++x) {
                 const int j = lane + 64 * x;
-                if (j < Dv) s[x] = at * s[x] + kt * sDL[t * Dv + j];
+                if (j < Dv) s[x] = a_t * s[x] + k_t * sDL[t * Dv + j];
             }
         }
         // H_r[c, :] backward from the chunk end: G_{last} = dSn + q dO, then
         // H_t = G_t - k_t dv_t,  G_{t-1} = alpha_t H_t + q_{t-1} dO_{t-1}
         const int tl = nvalid - 1;
-        const float ql = to_f32(qg[tok(tl) * DK + c]);
+        const float ql = bc(qt, tl);
 #pragma unroll
         for (int x = 0; x < JPL; ++x) {
             const int j = lane + 64 * x;
             g[x] = j < Dv ? a.DSN[(unit * DK + c) * Dv + j] + ql * sDO[tl * Dv + j] : 0.f;
         }
         for (int t = tl; t >= r; --t) {
-            const float kt = to_f32(kg[tok(t) * DK + c]);
+            const float k_t = bc(kt, t);
 #pragma unroll
             for (int x = 0; x < JPL; ++x) {
                 const int j = lane + 64 * x;
-                hh[x] = j < Dv ? g[x] - kt * sE[t * Dv + j] : 0.f;
+                hh[x] = j < Dv ? g[x] - k_t * sE[t * Dv + j] : 0.f;
             }
             if (t > r) {
-                const float at = a.alpha[tok(t) * DK + c], qp = to_f32(qg[tok(t - 1) * DK + c]);
+                const float a_t = bc(at, t), q_p = bc(qt, t - 1);
 #pragma unroll
                 for (int x = 0; x < JPL; ++x) {
                     const int j = lane + 64 * x;
-                    g[x] = j < Dv ? at * hh[x] + qp * sDO[(t - 1) * Dv + j] : 0.f;
+                    g[x] = j < Dv ? a_t * hh[x] + q_p * sDO[(t - 1) * Dv + j] : 0.f;
                 }
             }
         }
@@ -737,7 +828,7 @@ hipError_t launch_bwd_t(int stage, const ChunkShape& s, const ChunkWorkspace& ws
         auto kern = bwd_local_kernel<T, C, DK>;
         const hipError_t e = set_lds(kern, G::BYTES);
         if (e != hipSuccess) return e;
-        return launch_kernel(kern, dim3(nu), dim3(kBwdThreads), (uint32_t)G::BYTES, stream, la);
+        return launch_kernel(kern, dim3(nu), dim3(kLocalThreads), (uint32_t)G::BYTES, stream, la);
     }
     case 3: {
         using L = TinyLds<T, C, DK>;
