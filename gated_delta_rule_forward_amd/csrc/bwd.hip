@@ -229,10 +229,45 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
         }
     };
 
+    // L2 prefetch of chunk n - 3: the column slices of one (b, h) share one
+    // XCD's L2, so each workgroup loads every NS-th kilobyte of that chunk's
+    // P^T, Ktil, (Q*Gamma)^T, W^T (one 16-byte piece per lane and kilobyte).
+    // Ordinary loads, consumed into pf one step later (a dependence the
+    // compiler keeps; the value is only stored if T < 0, which never holds).
+    constexpr int PBYTES = (C * C + 3 * C * DK) * (int)sizeof(T);
+    constexpr int NPIECE = PBYTES / 1024;
+    const int per_wg = (NPIECE + NS - 1) / NS;
+    unsigned pf = 0;
+    uint4 pfv[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
+    auto prefetch = [&](int n) {
+        const size_t unit = (size_t)bh * NC + n;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int q = wave + 4 * i;
+            int p = slice + NS * q;
+            if (q >= per_wg || p >= NPIECE) p = slice % NPIECE;
+            const unsigned char* base;
+            int off = p * 1024;
+            if (off < C * C * (int)sizeof(T)) {
+                base = static_cast<const unsigned char*>(a.PT) + unit * C * C * sizeof(T);
+            } else {
+                off -= C * C * (int)sizeof(T);
+                const int blk = C * DK * (int)sizeof(T);
+                const void* arr = off < blk ? a.Ktil : (off < 2 * blk ? a.QGT : a.WT);
+                off %= blk;
+                base = static_cast<const unsigned char*>(arr) + unit * C * DK * sizeof(T);
+            }
+            pfv[i] = *reinterpret_cast<const uint4*>(base + off + 16 * lane);
+        }
+    };
+    auto consume = [&]() { pf ^= pfv[0].x ^ pfv[1].y; };
+
     Ops cur;
     load_ops(cur, NC - 1);
     for (int n = NC - 1; n >= 0; --n) {
         const size_t unit = (size_t)bh * NC + n;
+        consume();
+        if (n >= 3) prefetch(n - 3);
         Ops nxt;
         if (n > 0) load_ops(nxt, n - 1);
         // the gradient of the state leaving chunk n
@@ -287,6 +322,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
         __syncthreads();
         if (n > 0) cur = nxt;
     }
+    consume();
+    if (a.T < 0) a.XB[lane] = __uint_as_float(pf);
     if (a.dS0) {
 #pragma unroll
         for (int u = 0; u < G::SPW; ++u) {
@@ -460,17 +497,21 @@ __global__ __launch_bounds__(kLocalThreads) void bwd_local_kernel(BwdLocalArgs a
             const float* ps = a.CS32 + (unit * DK + 16 * ct + ln) * Dv + 4 * lg;
             const float* pn = a.DSN + (unit * DK + 16 * ct + ln) * Dv + 4 * lg;
             float sig = 0.f;
+            // bf16 inputs: the products run as bf16 MFMAs (operands rounded
+            // from fp32, fp32 accumulation), fp32 inputs stay in fp32
+            using V = Vec4<T>;
             for (int s = 0; s < NVT; ++s) {
-                const Vec4<float> bS = Vec4<float>::load(ps + 16 * s);
-                const Vec4<float> bN = Vec4<float>::load(pn + 16 * s);
+                const Vec4<float> fS = Vec4<float>::load(ps + 16 * s);
+                const Vec4<float> fN = Vec4<float>::load(pn + 16 * s);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) sig += bS.v[j] * bN.v[j];
+                for (int j = 0; j < 4; ++j) sig += fS.v[j] * fN.v[j];
+                const V bS = V::from(fS.v), bN = V::from(fN.v);
 #pragma unroll
                 for (int mt = 0; mt < NM; ++mt) {
                     const int off = (16 * mt + ln) * LDV + 16 * s + 4 * lg;
-                    F1[cw][mt] = mma_k16(Vec4<float>::load(sDO + off), bS, F1[cw][mt]);
-                    F2[cw][mt] = mma_k16(Vec4<float>::load(sY + off), bS, F2[cw][mt]);
-                    F3[cw][mt] = mma_k16(Vec4<float>::load(sDL + off), bN, F3[cw][mt]);
+                    F1[cw][mt] = mma_k16(V::from(Vec4<float>::load(sDO + off).v), bS, F1[cw][mt]);
+                    F2[cw][mt] = mma_k16(V::from(Vec4<float>::load(sY + off).v), bS, F2[cw][mt]);
+                    F3[cw][mt] = mma_k16(V::from(Vec4<float>::load(sDL + off).v), bN, F3[cw][mt]);
                 }
             }
             sig += __shfl_xor(sig, 16);
