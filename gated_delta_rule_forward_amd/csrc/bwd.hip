@@ -368,7 +368,8 @@ struct LocalGeom {
     // small arrays
     static constexpr size_t R1 = R1A > R1B ? R1A : R1B;
     static constexpr size_t BETA = R1, DB = BETA + 4 * C, DBW = DB + 4 * C;
-    static constexpr size_t BYTES = DBW + 4 * (size_t)kLocalWaves * C;
+    static constexpr size_t DBV = DBW + 4 * (size_t)kLocalWaves * C;
+    static constexpr size_t BYTES = DBV + 4 * (size_t)kLocalWaves * C;
     static_assert(BYTES <= 160 * 1024, "LDS");
 };
 
@@ -389,8 +390,8 @@ __global__ __launch_bounds__(kLocalThreads) void bwd_local_kernel(BwdLocalArgs a
     float* sB1T = reinterpret_cast<float*>(lds + G::B1T);
     float* sB3T = reinterpret_cast<float*>(lds + G::B3T);
     float* sBeta = reinterpret_cast<float*>(lds + G::BETA);
-    float* sDB = reinterpret_cast<float*>(lds + G::DB);
     float* sDBw = reinterpret_cast<float*>(lds + G::DBW);     // [waves][C]
+    float* sDBv = reinterpret_cast<float*>(lds + G::DBV);     // [waves][C]: v . y partials
     constexpr int LDV = G::LDV, LDT = G::LDT, NM = G::NM, NW = kLocalWaves, NTH = kLocalThreads;
 
     const int Dv = a.Dv, H = a.H, NC = a.NC, NVT = Dv / 16;
@@ -403,67 +404,131 @@ __global__ __launch_bounds__(kLocalThreads) void bwd_local_kernel(BwdLocalArgs a
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     auto tok = [&](int r) { return (row0 + r) * H + h; };       // token index of local row r
 
-    // ---- load -------------------------------------------------------------------
+    // ---- load (every loop has a compile-time trip count, so the loads of a
+    //      thread are issued together) ---------------------------------------------
     bool tiny = false;
-    for (int idx = tid; idx < nvalid * DK; idx += NTH)
-        tiny |= fabsf(a.alpha[tok(idx / DK) * DK + idx % DK]) < kTinyGate;
-    const int any_tiny = __syncthreads_or(tiny);
+    {
+        constexpr int NA = C * DK / 4 / NTH > 0 ? C * DK / 4 / NTH : 1;
+#pragma unroll
+        for (int x = 0; x < NA; ++x) {
+            const int idx = tid + NTH * x;
+            const int r = idx / (DK / 4), c4 = 4 * (idx % (DK / 4));
+            if (idx < C * DK / 4 && r < nvalid) {
+                const float4 al = *reinterpret_cast<const float4*>(a.alpha + tok(r) * DK + c4);
+                tiny |= fabsf(al.x) < kTinyGate || fabsf(al.y) < kTinyGate ||
+                        fabsf(al.z) < kTinyGate || fabsf(al.w) < kTinyGate;
+            }
+        }
+    }
     if (tid < C) {
         sBeta[tid] = tid < nvalid ? a.beta[tok(tid)] : 0.f;
-        sDB[tid] = 0.f;
-    }
-    for (int idx = tid; idx < C * C; idx += NTH)
-        sT[(idx / C) * LDT + idx % C] = a.Tm[unit * C * C + idx];
-    const T* dO = static_cast<const T*>(a.dO);
-    for (int idx = tid; idx < C * (Dv / 4); idx += NTH) {
-        const int r = idx / (Dv / 4), c4 = 4 * (idx % (Dv / 4));
-        float4 o = make_float4(0.f, 0.f, 0.f, 0.f), d = o;
-        if (r < nvalid) {
-            const Vec4<T> x = Vec4<T>::load(dO + tok(r) * Dv + c4);
-            o = make_float4(x.get(0), x.get(1), x.get(2), x.get(3));
-            d = *reinterpret_cast<const float4*>(a.DL + (unit * C + r) * Dv + c4);
-        }
-        *reinterpret_cast<float4*>(sDO + r * LDV + c4) = o;
-        *reinterpret_cast<float4*>(sDL + r * LDV + c4) = d;
-    }
-    __syncthreads();
-
-    // ---- y = Tinv^T X, dv = diag(beta) y ------------------------------------------
-    T* dv = static_cast<T*>(a.dv);
-    for (int job = wave; job < NM * NVT; job += NW) {
-        const int mt = job / NVT, vt = job % NVT;
-        f32x4 acc = zero4();
-        for (int s = mt; s < NM; ++s) {          // Tinv[k][m] = 0 for k < m
-            float fa[4], fb[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int kk = 16 * s + 4 * lg + j;
-                fa[j] = sT[kk * LDT + 16 * mt + ln];
-                fb[j] = a.XB[(unit * C + kk) * Dv + 16 * vt + ln];
-            }
-            acc = mma_k16(Vec4<float>::from(fa), Vec4<float>::from(fb), acc);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 16 * mt + 4 * lg + i, c = 16 * vt + ln;
-            sY[r * LDV + c] = acc[i];
-            if (r < nvalid) dv[tok(r) * Dv + c] = from_f32<T>(sBeta[r] * acc[i]);
-        }
+        for (int w = 0; w < NW; ++w) sDBv[w * C + tid] = 0.f;
     }
-    __syncthreads();
-
-    // ---- dbeta, first term: v_r . y_r ---------------------------------------------
     {
-        constexpr int TPR = NTH / C;               // threads per row
-        const int r = tid / TPR, part = tid % TPR;
-        const T* v = static_cast<const T*>(a.v);
-        float sacc = 0.f;
-        if (r < nvalid)
-            for (int c = part; c < Dv; c += TPR) sacc += to_f32(v[tok(r) * Dv + c]) * sY[r * LDV + c];
+        constexpr int NTL = (C * C / 4 + NTH - 1) / NTH;
 #pragma unroll
-        for (int o = TPR / 2; o > 0; o >>= 1) sacc += __shfl_xor(sacc, o);
-        if (part == 0) sDB[r] = sacc;
+        for (int x = 0; x < NTL; ++x) {
+            const int idx = tid + NTH * x;
+            if (idx < C * C / 4) {
+                const float4 t4 = *reinterpret_cast<const float4*>(a.Tm + unit * C * C + 4 * idx);
+                *reinterpret_cast<float4*>(sT + (4 * idx / C) * LDT + (4 * idx) % C) = t4;
+            }
+        }
     }
+    const T* dO = static_cast<const T*>(a.dO);
+    {
+        // dO, Delta, and X (into the Y buffer; y replaces it below)
+        constexpr int NL = (C * G::DVMAX / 4 + NTH - 1) / NTH;
+        const int DV4 = Dv / 4;
+#pragma unroll
+        for (int x = 0; x < NL; ++x) {
+            const int idx = tid + NTH * x;
+            if (idx < C * DV4) {
+                const int r = idx / DV4, c4 = 4 * (idx % DV4);
+                float4 o = make_float4(0.f, 0.f, 0.f, 0.f), d = o;
+                if (r < nvalid) {
+                    const Vec4<T> xo = Vec4<T>::load(dO + tok(r) * Dv + c4);
+                    o = make_float4(xo.get(0), xo.get(1), xo.get(2), xo.get(3));
+                    d = *reinterpret_cast<const float4*>(a.DL + (unit * C + r) * Dv + c4);
+                }
+                const float4 xb = *reinterpret_cast<const float4*>(a.XB + (unit * C + r) * Dv + c4);
+                *reinterpret_cast<float4*>(sDO + r * LDV + c4) = o;
+                *reinterpret_cast<float4*>(sDL + r * LDV + c4) = d;
+                *reinterpret_cast<float4*>(sY + r * LDV + c4) = xb;
+            }
+        }
+    }
+    // loads of later phases issued now, so that their latency overlaps the
+    // y and B products: v of this wave's y tiles, S and dSn of its channel tiles
+    T* dv = static_cast<T*>(a.dv);
+    const T* vg = static_cast<const T*>(a.v);
+    constexpr int MAXJ = (NM * (G::DVMAX / 16) + NW - 1) / NW;
+    constexpr int NKV = G::DVMAX / 16;
+    float vv[MAXJ][4];
+#pragma unroll
+    for (int jj = 0; jj < MAXJ; ++jj) {
+        const int job = min(wave + NW * jj, NM * NVT - 1);
+        const int mt = job / NVT, vt = job % NVT;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)        // rows past the end read the last row (weight 0 below)
+            vv[jj][i] = to_f32(vg[tok(min(16 * mt + 4 * lg + i, nvalid - 1)) * Dv + 16 * vt + ln]);
+    }
+    Vec4<float> pS[G::CTW][NKV], pN[G::CTW][NKV];
+#pragma unroll
+    for (int cw = 0; cw < G::CTW; ++cw) {
+        const int ct = min(wave + NW * cw, G::NCT - 1);
+        const float* ps = a.CS32 + (unit * DK + 16 * ct + ln) * Dv + 4 * lg;
+        const float* pn = a.DSN + (unit * DK + 16 * ct + ln) * Dv + 4 * lg;
+#pragma unroll
+        for (int s2 = 0; s2 < NKV; ++s2) {
+            const int so = 16 * min(s2, NVT - 1);
+            pS[cw][s2] = Vec4<float>::load(ps + so);
+            pN[cw][s2] = Vec4<float>::load(pn + so);
+        }
+    }
+    const int any_tiny = __syncthreads_or(tiny);
+
+    // ---- y = Tinv^T X, dv = diag(beta) y, and v . y -----------------------------------
+    f32x4 yt[MAXJ];
+#pragma unroll
+    for (int jj = 0; jj < MAXJ; ++jj) {
+        const int job = wave + NW * jj;
+        yt[jj] = zero4();
+        if (job < NM * NVT) {
+            const int mt = job / NVT, vt = job % NVT;
+#pragma unroll
+            for (int s2 = 0; s2 < NM; ++s2) {        // Tinv[k][m] = 0 for k < m
+                if (s2 < mt) continue;
+                float fa[4], fb[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int kk = 16 * s2 + 4 * lg + j;
+                    fa[j] = sT[kk * LDT + 16 * mt + ln];
+                    fb[j] = sY[kk * LDV + 16 * vt + ln];
+                }
+                yt[jj] = mma_k16(Vec4<float>::from(fa), Vec4<float>::from(fb), yt[jj]);
+            }
+        }
+    }
+    __syncthreads();     // every read of X is done: y takes its place
+#pragma unroll
+    for (int jj = 0; jj < MAXJ; ++jj) {
+        const int job = wave + NW * jj;
+        if (job < NM * NVT) {
+            const int mt = job / NVT, vt = job % NVT;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * mt + 4 * lg + i, c = 16 * vt + ln;
+                const float yv = yt[jj][i];
+                sY[r * LDV + c] = yv;
+                if (r < nvalid) dv[tok(r) * Dv + c] = from_f32<T>(sBeta[r] * yv);
+                const float vy = row16_sum(r < nvalid ? vv[jj][i] * yv : 0.f);
+                if (ln == 0) sDBv[wave * C + r] += vy;
+            }
+        }
+    }
+    __syncthreads();
 
     // ---- B1 = dO Delta^T (i <= r), B3 = Y Delta^T (i < r): lower tiles --------------
     {
@@ -485,6 +550,21 @@ __global__ __launch_bounds__(kLocalThreads) void bwd_local_kernel(BwdLocalArgs a
     }
 
     // ---- F1 = dO S^T, F2 = Y S^T, F3 = Delta dSn^T; sigma = rowdot(dSn, S) ----------
+    // the weight phase's gates, keys and queries, loaded now (rows past the end
+    // read the last row and are replaced by alpha = 1, k = q = 0 when stored)
+    const T* kg = static_cast<const T*>(a.k);
+    const T* qg = static_cast<const T*>(a.q);
+    constexpr int NA = (C * DK / 4 + NTH - 1) / NTH;
+    float4 wal[NA];
+    Vec4<T> wk4[NA], wq4[NA];
+#pragma unroll
+    for (int x = 0; x < NA; ++x) {
+        const int idx = min(tid + NTH * x, C * DK / 4 - 1);
+        const int r = min(idx / (DK / 4), nvalid - 1), c4 = 4 * (idx % (DK / 4));
+        wal[x] = *reinterpret_cast<const float4*>(a.alpha + tok(r) * DK + c4);
+        wk4[x] = Vec4<T>::load(kg + tok(r) * DK + c4);
+        wq4[x] = Vec4<T>::load(qg + tok(r) * DK + c4);
+    }
     f32x4 F1[G::CTW][NM], F2[G::CTW][NM], F3[G::CTW][NM];
     float sigv[G::CTW];
 #pragma unroll
@@ -494,15 +574,15 @@ __global__ __launch_bounds__(kLocalThreads) void bwd_local_kernel(BwdLocalArgs a
 #pragma unroll
         for (int mt = 0; mt < NM; ++mt) F1[cw][mt] = F2[cw][mt] = F3[cw][mt] = zero4();
         if (ct < G::NCT) {
-            const float* ps = a.CS32 + (unit * DK + 16 * ct + ln) * Dv + 4 * lg;
-            const float* pn = a.DSN + (unit * DK + 16 * ct + ln) * Dv + 4 * lg;
             float sig = 0.f;
             // bf16 inputs: the products run as bf16 MFMAs (operands rounded
             // from fp32, fp32 accumulation), fp32 inputs stay in fp32
             using V = Vec4<T>;
-            for (int s = 0; s < NVT; ++s) {
-                const Vec4<float> fS = Vec4<float>::load(ps + 16 * s);
-                const Vec4<float> fN = Vec4<float>::load(pn + 16 * s);
+#pragma unroll
+            for (int s = 0; s < G::DVMAX / 16; ++s) {
+                if (s >= NVT) break;
+                const Vec4<float> fS = pS[cw][s];
+                const Vec4<float> fN = pN[cw][s];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) sig += fS.v[j] * fN.v[j];
                 const V bS = V::from(fS.v), bN = V::from(fN.v);
@@ -528,20 +608,15 @@ __global__ __launch_bounds__(kLocalThreads) void bwd_local_kernel(BwdLocalArgs a
 
     // ---- weight phase: alpha, k, q, B1^T, B3^T ----------------------------------------
     {
-        const T* kg = static_cast<const T*>(a.k);
-        const T* qg = static_cast<const T*>(a.q);
-        for (int idx = tid; idx < C * (DK / 4); idx += NTH) {
+#pragma unroll
+        for (int x = 0; x < NA; ++x) {
+            const int idx = tid + NTH * x;
+            if (idx >= C * DK / 4) break;
             const int r = idx / (DK / 4), c4 = 4 * (idx % (DK / 4));
-            float4 al = make_float4(1.f, 1.f, 1.f, 1.f);
-            Vec4<T> kv = Vec4<T>::zero(), qv = Vec4<T>::zero();
-            if (r < nvalid) {
-                al = *reinterpret_cast<const float4*>(a.alpha + tok(r) * DK + c4);
-                kv = Vec4<T>::load(kg + tok(r) * DK + c4);
-                qv = Vec4<T>::load(qg + tok(r) * DK + c4);
-            }
-            *reinterpret_cast<float4*>(sAl + r * DK + c4) = al;
-            *reinterpret_cast<Vec4<T>*>(sK + r * DK + c4) = kv;
-            *reinterpret_cast<Vec4<T>*>(sQ + r * DK + c4) = qv;
+            const bool ok = r < nvalid;
+            *reinterpret_cast<float4*>(sAl + r * DK + c4) = ok ? wal[x] : make_float4(1.f, 1.f, 1.f, 1.f);
+            *reinterpret_cast<Vec4<T>*>(sK + r * DK + c4) = ok ? wk4[x] : Vec4<T>::zero();
+            *reinterpret_cast<Vec4<T>*>(sQ + r * DK + c4) = ok ? wq4[x] : Vec4<T>::zero();
         }
         for (int idx = tid; idx < C * C; idx += NTH) {
             const int r = idx / C, i = idx % C;
@@ -717,10 +792,13 @@ __global__ __launch_bounds__(kLocalThreads) void bwd_local_kernel(BwdLocalArgs a
         }
     __syncthreads();
     if (tid < nvalid) {
-        float sacc = sDB[tid];
+        float sv = 0.f, sw = 0.f;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) sacc += sDBw[w * C + tid];
-        a.dbeta[tok(tid)] = sacc;
+        for (int w = 0; w < NW; ++w) {
+            sv += sDBv[w * C + tid];
+            sw += sDBw[w * C + tid];
+        }
+        a.dbeta[tok(tid)] = sv + sw;
     }
     if (tid == 0) a.FLB[unit] = any_tiny ? 1 : 0;
 }
@@ -760,16 +838,41 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_tiny_kernel(BwdLocalArgs a)
     const T* qg = static_cast<const T*>(a.q);
 
     if (tid == 0) *sCnt = 0;
-    for (int idx = tid; idx < nvalid * Dv; idx += kBwdThreads) {
-        const int r = idx / Dv, c = idx % Dv;
-        sDL[idx] = a.DL[(unit * C + r) * Dv + c];
-        sDO[idx] = to_f32(dO[tok(r) * Dv + c]);
-        sE[idx] = a.beta[tok(r)] * a.XB[(unit * C + r) * Dv + c];
+    {
+        // Delta, dO and dv = beta y of the chunk (compile-time trip counts so
+        // a thread's loads are issued together)
+        constexpr int NL = (C * L::DVMAX / 4 + kBwdThreads - 1) / kBwdThreads;
+        const int DV4 = Dv / 4;
+#pragma unroll
+        for (int x = 0; x < NL; ++x) {
+            const int idx = tid + kBwdThreads * x;
+            if (idx < nvalid * DV4) {
+                const int r = idx / DV4, c4 = 4 * (idx % DV4);
+                const float4 d = *reinterpret_cast<const float4*>(a.DL + (unit * C + r) * Dv + c4);
+                const Vec4<T> o = Vec4<T>::load(dO + tok(r) * Dv + c4);
+                const float4 y = *reinterpret_cast<const float4*>(a.XB + (unit * C + r) * Dv + c4);
+                const float bt = a.beta[tok(r)];
+                *reinterpret_cast<float4*>(sDL + r * Dv + c4) = d;
+                *reinterpret_cast<float4*>(sDO + r * Dv + c4) = make_float4(o.get(0), o.get(1), o.get(2), o.get(3));
+                *reinterpret_cast<float4*>(sE + r * Dv + c4) = make_float4(bt * y.x, bt * y.y, bt * y.z, bt * y.w);
+            }
+        }
     }
     __syncthreads();
-    for (int idx = tid; idx < nvalid * DK; idx += kBwdThreads) {
-        const int r = idx / DK, c = idx % DK;
-        if (fabsf(a.alpha[tok(r) * DK + c]) < kTinyGate) sList[atomicAdd(sCnt, 1)] = idx;
+    {
+        constexpr int NA = (C * DK / 4 + kBwdThreads - 1) / kBwdThreads;
+#pragma unroll
+        for (int x = 0; x < NA; ++x) {
+            const int idx = tid + kBwdThreads * x;
+            if (idx < nvalid * (DK / 4)) {
+                const int r = idx / (DK / 4), c4 = 4 * (idx % (DK / 4));
+                const float4 al = *reinterpret_cast<const float4*>(a.alpha + tok(r) * DK + c4);
+                const float v4[4] = {al.x, al.y, al.z, al.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (fabsf(v4[j]) < kTinyGate) sList[atomicAdd(sCnt, 1)] = r * DK + c4 + j;
+            }
+        }
     }
     __syncthreads();
     const int cnt = *sCnt;
