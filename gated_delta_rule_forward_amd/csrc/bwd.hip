@@ -361,16 +361,22 @@ struct LocalGeom {
     // R1, GEMM phase: dO, Delta, Y
     static constexpr size_t DO = R0, DL = DO + 4 * (size_t)C * LDV, YY = DL + 4 * (size_t)C * LDV;
     static constexpr size_t R1A = YY + 4 * (size_t)C * LDV;
-    // R1, weight phase: alpha (fp32), k, q (io type), B1^T, B3^T
+    // R1, weight phase: alpha (fp32), k, q (io type), one decayed operand
+    // (fp32 [NDR][DKP]: k, q or beta k decayed to the 16-token block edges)
+    // and the per-channel block-edge products GB (Gamma_{16 b - 1}) and GE
+    // (rho(C - 1, 16 b + 15)), [NM][DK] each
+    static constexpr int NDR = 8 * NM * (NM - 1), DKP = DK + 4;
     static constexpr size_t AL = R0, KK = AL + 4 * (size_t)C * DK, QQ = al16(KK + sizeof(T) * C * DK);
-    static constexpr size_t B1T = al16(QQ + sizeof(T) * C * DK), B3T = B1T + 4 * (size_t)C * LDT;
-    static constexpr size_t R1B = B3T + 4 * (size_t)C * LDT;
+    static constexpr size_t DEC = al16(QQ + sizeof(T) * C * DK), GB = DEC + 4 * (size_t)NDR * DKP;
+    static constexpr size_t GE = GB + 4 * (size_t)NM * DK;
+    static constexpr size_t R1B = GE + 4 * (size_t)NM * DK;
     // small arrays
     static constexpr size_t R1 = R1A > R1B ? R1A : R1B;
     static constexpr size_t BETA = R1, DB = BETA + 4 * C, DBW = DB + 4 * C;
     static constexpr size_t DBV = DBW + 4 * (size_t)kLocalWaves * C;
     static constexpr size_t BYTES = DBV + 4 * (size_t)kLocalWaves * C;
     static_assert(BYTES <= 160 * 1024, "LDS");
+    static_assert(CTW == 1, "one channel tile per wavefront");
 };
 
 template <typename T, int C, int DK>
@@ -387,8 +393,9 @@ __global__ __launch_bounds__(kLocalThreads) void bwd_local_kernel(BwdLocalArgs a
     float* sAl = reinterpret_cast<float*>(lds + G::AL);
     T* sK = reinterpret_cast<T*>(lds + G::KK);
     T* sQ = reinterpret_cast<T*>(lds + G::QQ);
-    float* sB1T = reinterpret_cast<float*>(lds + G::B1T);
-    float* sB3T = reinterpret_cast<float*>(lds + G::B3T);
+    float* sDec = reinterpret_cast<float*>(lds + G::DEC);
+    float* sGB = reinterpret_cast<float*>(lds + G::GB);
+    float* sGE = reinterpret_cast<float*>(lds + G::GE);
     float* sBeta = reinterpret_cast<float*>(lds + G::BETA);
     float* sDBw = reinterpret_cast<float*>(lds + G::DBW);     // [waves][C]
     float* sDBv = reinterpret_cast<float*>(lds + G::DBV);     // [waves][C]: v . y partials
@@ -618,13 +625,132 @@ __global__ __launch_bounds__(kLocalThreads) void bwd_local_kernel(BwdLocalArgs a
             *reinterpret_cast<Vec4<T>*>(sK + r * DK + c4) = ok ? wk4[x] : Vec4<T>::zero();
             *reinterpret_cast<Vec4<T>*>(sQ + r * DK + c4) = ok ? wq4[x] : Vec4<T>::zero();
         }
-        for (int idx = tid; idx < C * C; idx += NTH) {
-            const int r = idx / C, i = idx % C;
-            sB1T[i * LDT + r] = sB1[r * LDT + i];
-            sB3T[i * LDT + r] = sB3[r * LDT + i];
+    }
+    __syncthreads();
+
+    // ---- the off-diagonal parts of the decay-weighted sums, per 16-token block
+    // b (rows 16 b .. 16 b + 15), as fp32 MFMA products: with e = 16 b - 1,
+    //   sum_{i <= e} B[r,i] rho(r,i) k_i = rho(r, e) sum_i B[r,i] (k_i rho(e, i))
+    // and with e' = 16 b + 15,
+    //   sum_{j > e'} B[j,r] rho(j,r) x_j = rho(e', r) sum_j B[j,r] (x_j rho(j, e'))
+    // (x = q with B1, x = beta k with B3).  The decayed operands are exact
+    // running products of the gates (|factor| <= 1), built per channel.
+    constexpr int NDR = G::NDR, DKP = G::DKP;
+    auto offL = [](int b) { return 8 * b * (b - 1); };                 // rows of blocks before b
+    auto offU = [](int b) { return 16 * (b * (NM - 1) - b * (b - 1) / 2); };
+    f32x4 mL1[NM], mL3[NM], mU1[NM], mU2[NM];
+#pragma unroll
+    for (int b = 0; b < NM; ++b) mL1[b] = mL3[b] = mU1[b] = mU2[b] = zero4();
+    const int ctw = wave;                       // this wave's channel tile (DK <= 128: one)
+    // k decayed forward to each block edge; Gamma at the block edges
+    // (each 16-token piece of the channel is read into registers before any
+    // of its results is written, so the reads are issued together)
+    if (tid < DK) {
+        const int c = tid;
+        sGB[c] = 1.f;
+#pragma unroll
+        for (int b = 1; b < NM; ++b) {
+            float w = 1.f;
+#pragma unroll
+            for (int blk = b - 1; blk >= 0; --blk) {
+                float av[16], kv[16];
+#pragma unroll
+                for (int x = 0; x < 16; ++x) {
+                    av[x] = sAl[(16 * blk + x) * DK + c];
+                    kv[x] = to_f32(sK[(16 * blk + x) * DK + c]);
+                }
+#pragma unroll
+                for (int x = 15; x >= 0; --x) {
+                    sDec[(offL(b) + 16 * blk + x) * DKP + c] = kv[x] * w;
+                    w *= av[x];
+                }
+            }
+            sGB[b * DK + c] = w;
         }
     }
     __syncthreads();
+    if (ctw < G::NCT) {
+#pragma unroll
+        for (int b = 1; b < NM; ++b) {
+#pragma unroll
+            for (int k0 = 0; k0 < 16 * b; k0 += 4) {
+                const float bb = sDec[(offL(b) + k0 + lg) * DKP + 16 * ctw + ln];
+                mL1[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(sB1[(16 * b + ln) * LDT + k0 + lg], bb, mL1[b], 0, 0, 0);
+                mL3[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(sB3[(16 * b + ln) * LDT + k0 + lg], bb, mL3[b], 0, 0, 0);
+            }
+        }
+    }
+    __syncthreads();
+    // q decayed backward to each block's end; rho(C - 1, block end)
+    if (tid < DK) {
+        const int c = tid;
+        sGE[(NM - 1) * DK + c] = 1.f;
+#pragma unroll
+        for (int b = 0; b + 1 < NM; ++b) {
+            float w = 1.f;
+#pragma unroll
+            for (int blk = b + 1; blk < NM; ++blk) {
+                float av[16], qv[16];
+#pragma unroll
+                for (int x = 0; x < 16; ++x) {
+                    av[x] = sAl[(16 * blk + x) * DK + c];
+                    qv[x] = to_f32(sQ[(16 * blk + x) * DK + c]);
+                }
+#pragma unroll
+                for (int x = 0; x < 16; ++x) {
+                    w *= av[x];
+                    sDec[(offU(b) + 16 * (blk - b - 1) + x) * DKP + c] = qv[x] * w;
+                }
+            }
+            sGE[b * DK + c] = w;
+        }
+    }
+    __syncthreads();
+    if (ctw < G::NCT) {
+#pragma unroll
+        for (int b = 0; b + 1 < NM; ++b) {
+#pragma unroll
+            for (int k0 = 16 * b + 16; k0 < C; k0 += 4) {
+                const float bb = sDec[(offU(b) + k0 - 16 * b - 16 + lg) * DKP + 16 * ctw + ln];
+                mU1[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(sB1[(k0 + lg) * LDT + 16 * b + ln], bb, mU1[b], 0, 0, 0);
+            }
+        }
+    }
+    __syncthreads();
+    // beta k decayed backward to each block's end
+    if (tid < DK) {
+        const int c = tid;
+#pragma unroll
+        for (int b = 0; b + 1 < NM; ++b) {
+            float w = 1.f;
+#pragma unroll
+            for (int blk = b + 1; blk < NM; ++blk) {
+                float av[16], kv[16];
+#pragma unroll
+                for (int x = 0; x < 16; ++x) {
+                    av[x] = sAl[(16 * blk + x) * DK + c];
+                    kv[x] = sBeta[16 * blk + x] * to_f32(sK[(16 * blk + x) * DK + c]);
+                }
+#pragma unroll
+                for (int x = 0; x < 16; ++x) {
+                    w *= av[x];
+                    sDec[(offU(b) + 16 * (blk - b - 1) + x) * DKP + c] = kv[x] * w;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    if (ctw < G::NCT) {
+#pragma unroll
+        for (int b = 0; b + 1 < NM; ++b) {
+#pragma unroll
+            for (int k0 = 16 * b + 16; k0 < C; k0 += 4) {
+                const float bb = sDec[(offU(b) + k0 - 16 * b - 16 + lg) * DKP + 16 * ctw + ln];
+                mU2[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(sB3[(k0 + lg) * LDT + 16 * b + ln], bb, mU2[b], 0, 0, 0);
+            }
+        }
+    }
+    (void)NDR;
 
     float dbp[NM][4];
 #pragma unroll
@@ -643,23 +769,30 @@ __global__ __launch_bounds__(kLocalThreads) void bwd_local_kernel(BwdLocalArgs a
         auto qf = [&](int t) { return to_f32(sQ[t * DK + c]); };
         float Za[NM][4], Zb[NM][4];
         float gcl = 1.f;                   // Gamma of the lane's last row (row C - 1 in lanes lg = 3)
-        const float a0 = al(0);
 #pragma unroll
         for (int mt = 0; mt < NM; ++mt) {
             const int r0 = 16 * mt + 4 * lg, r3 = r0 + 3;
-            // L sums over i < r0 with w = rho(r0, i), then rho(r0 + m, r0); the
-            // final w is rho(r0, 0), so Gamma_{r0+m} = alpha_0 w rho(r0 + m, r0)
+            // L sums inside block mt (16 mt <= i < r0) with w = rho(r0, i), then
+            // the block product (rho(r0, 16 mt - 1) = w alpha_{16 mt}) and
+            // rho(r0 + m, r0); Gamma_{r0+m} = GB rho(r0, 16 mt - 1) rho(r0 + m, r0)
             float lq[4] = {0.f, 0.f, 0.f, 0.f}, lk[4] = {0.f, 0.f, 0.f, 0.f};
             float fL[4] = {1.f, 1.f, 1.f, 1.f}, wL = 1.f;
             {
-#pragma unroll 4
-                for (int i = r0 - 1; i >= 0; --i) {
+                for (int i = r0 - 1; i >= 16 * mt; --i) {
                     wL *= al(i + 1);
                     const float wk = wL * kf(i);
-                    const float4 b1 = *reinterpret_cast<const float4*>(sB1T + i * LDT + r0);
-                    const float4 b3 = *reinterpret_cast<const float4*>(sB3T + i * LDT + r0);
-                    lq[0] += b1.x * wk; lq[1] += b1.y * wk; lq[2] += b1.z * wk; lq[3] += b1.w * wk;
-                    lk[0] += b3.x * wk; lk[1] += b3.y * wk; lk[2] += b3.z * wk; lk[3] += b3.w * wk;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        lq[m] += sB1[(r0 + m) * LDT + i] * wk;
+                        lk[m] += sB3[(r0 + m) * LDT + i] * wk;
+                    }
+                }
+                const float pe = wL * al(16 * mt);          // rho(r0, 16 mt - 1)
+                wL = pe;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    lq[m] += pe * mL1[mt][m];
+                    lk[m] += pe * mL3[mt][m];
                 }
                 float f = 1.f;
 #pragma unroll
@@ -680,19 +813,24 @@ __global__ __launch_bounds__(kLocalThreads) void bwd_local_kernel(BwdLocalArgs a
                     }
                 }
             }
-            // U sums over j > r3 with w = rho(j, r3), then rho(r3, r0 + m); the
-            // final w is rho(C - 1, r3), so rho(C - 1, r0 + m) = w rho(r3, r0 + m)
+            // U sums inside block mt (r3 < j <= 16 mt + 15) with w = rho(j, r3),
+            // then the block product (w = rho(16 mt + 15, r3)) and rho(r3, r0 + m);
+            // rho(C - 1, r0 + m) = GE w rho(r3, r0 + m)
             float uq[4] = {0.f, 0.f, 0.f, 0.f}, uk[4] = {0.f, 0.f, 0.f, 0.f};
             float hU[4] = {1.f, 1.f, 1.f, 1.f}, wU = 1.f;
             {
-#pragma unroll 4
-                for (int j = r3 + 1; j < C; ++j) {
+                for (int j = r3 + 1; j <= 16 * mt + 15; ++j) {
                     wU *= al(j);
                     const float wq = wU * qf(j), wk = wU * sBeta[j] * kf(j);
                     const float4 b1 = *reinterpret_cast<const float4*>(sB1 + j * LDT + r0);
                     const float4 b3 = *reinterpret_cast<const float4*>(sB3 + j * LDT + r0);
                     uq[0] += b1.x * wq; uq[1] += b1.y * wq; uq[2] += b1.z * wq; uq[3] += b1.w * wq;
                     uk[0] += b3.x * wk; uk[1] += b3.y * wk; uk[2] += b3.z * wk; uk[3] += b3.w * wk;
+                }
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    uq[m] += wU * mU1[mt][m];
+                    uk[m] += wU * mU2[mt][m];
                 }
                 float f = 1.f;
 #pragma unroll
@@ -711,12 +849,13 @@ __global__ __launch_bounds__(kLocalThreads) void bwd_local_kernel(BwdLocalArgs a
                     }
                 }
             }
+            const float gbm = sGB[mt * DK + c], gem = sGE[mt * DK + c];
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const int r = r0 + m;
                 const float kr = kf(r), qr = qf(r), br = sBeta[r];
                 const float b1d = sB1[r * LDT + r];
-                const float g = a0 * wL * fL[m], ge = wU * hU[m];
+                const float g = gbm * wL * fL[m], ge = gem * wU * hU[m];
                 const float f1 = F1[cw][mt][m], f2 = F2[cw][mt][m], f3 = F3[cw][mt][m];
                 const float dqv = g * f1 + lq[m] + b1d * kr;
                 const float dkv = ge * f3 + uq[m] + b1d * qr - uk[m] - br * (g * f2 + lk[m]);
