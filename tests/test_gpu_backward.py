@@ -127,3 +127,25 @@ def test_backward_without_initial_state_gradient():
     assert g2["d_initial_state"] is None
     for gn, _ in GRADS:
         assert torch.equal(g1[gn], g2[gn]), gn
+
+
+def test_backward_full_headline_shape_sampled_heads():
+    """The headline shape (B=1, H=32, T=8192, d=128, bf16 KDA, chunk 64) in the
+    launch configuration the benchmark times: every head on the GPU, the
+    oracle's gradients for three sampled heads."""
+    w = workloads.workload(2)
+    inp = workloads.make_prefill(w)
+    dO, dST = workloads.make_backward_seeds(w)
+    say(f"[backward] full {w.name}")
+    g = _gpu(w, inp, dO, dST)
+    heads = [0, 13, 31]
+    sel = lambda t: None if t is None else t[:, :, heads].contiguous()
+    sub = {k: sel(v) for k, v in inp.items() if k != "S0"}
+    sub["S0"] = None if inp["S0"] is None else inp["S0"][:, heads].contiguous()
+    ref = _oracle(sub, sel(dO), dST[:, heads].contiguous())
+    gs = {k: (None if v is None else (v[:, :, heads] if k != "d_initial_state" else v[:, heads]))
+          for k, v in g.items()}
+    errs = _errors(gs, ref)
+    say("  " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= TOL[w.dtype], (k, v)
