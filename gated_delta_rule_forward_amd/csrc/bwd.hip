@@ -166,6 +166,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
     using F = Frag<T, G::KB>;
     __shared__ F sSf[G::NKD * 64];      // dS as B fragments, k = channels
     __shared__ F sXf[G::NKC * 64];      // -X as B fragments, k = tokens
+    // dO of this column slice, two chunks, transposed ([buffer][column][token]),
+    // so a lane's fragment slots (runs of 4 consecutive tokens) are 8 bytes
+    __shared__ __attribute__((aligned(16))) T sDOt[2][16][C];
 
     const int Dv = a.Dv, H = a.H, NS = Dv / 16, NC = a.NC;
     const int gid = blockIdx.x, xcd = gid % kXcds, jx = gid / kXcds;
@@ -176,6 +179,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = slice * 16 + ln;
     const T* dO = static_cast<const T*>(a.dO);
+    // the dO piece this thread stages: row tid / 4, columns 4 (tid % 4) .. + 3
+    const int drow = tid >> 2, dcol = 4 * (tid & 3);
 
     f32x4 dS[G::SPW];
 #pragma unroll
@@ -186,13 +191,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
             dS[u][i] = (a.dST && t < G::NT) ? a.dST[((size_t)bh * DK + 16 * t + 4 * lg + i) * Dv + col] : 0.f;
         if (t < G::NT) put_tile<T, G::KB>(sSf, t, lane, dS[u]);
     }
-    __syncthreads();
 
-    // one chunk's operands in registers; chunk n - 1's are loaded while
-    // chunk n is processed
+    // one chunk's operands in registers
     struct Ops {
-        F pt[G::NKC], kt[G::NKD], qt[G::SPW][G::NKC], wt[G::SPW][G::NKC], dof[G::NKC];
+        F pt[G::NKC], kt[G::NKD], qt[G::SPW][G::NKC], wt[G::SPW][G::NKC];
         f32x4 gc[G::SPW];
+        Vec4<T> dov;                     // this thread's staged dO piece
     };
     auto load_ops = [&](Ops& o, int n) {
         const size_t unit = (size_t)bh * NC + n;
@@ -215,17 +219,35 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
             }
             o.gc[u] = *reinterpret_cast<const f32x4*>(a.GC + unit * DK + 16 * t + 4 * lg);
         }
-        // dO of this chunk's column slice as B fragments over tokens
+        // rows past the end (and threads past the chunk) read row T - 1, zeroed when staged
+        const int row = min(n * C + min(drow, C - 1), a.T - 1);
+        o.dov = Vec4<T>::load(dO + (((size_t)b * a.T + row) * H + h) * Dv + slice * 16 + dcol);
+    };
+    auto stage_do = [&](const Ops& o, int n) {
+        if (drow < C) {
+            const bool ok = n * C + drow < a.T;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) sDOt[n & 1][dcol + x][drow] = ok ? o.dov.elem(x) : from_f32<T>(0.f);
+        }
+    };
+    // dO B fragments of chunk n from the staged copy
+    auto do_frags = [&](F* dof, int n) {
 #pragma unroll
         for (int s = 0; s < G::NKC; ++s) {
-            float f[G::NV];
+            const T* base = &sDOt[n & 1][ln][s * G::KB + 4 * lg];
+            if constexpr (G::KB == 32) {
+                const Vec4<T> lo = Vec4<T>::load(base), hi = Vec4<T>::load(base + 16);
+                float f[8];
 #pragma unroll
-            for (int j = 0; j < G::NV; ++j) {
-                const int kk = G::KB == 32 ? 16 * (j >> 2) + 4 * lg + (j & 3) : 4 * lg + j;
-                const int row = n * C + s * G::KB + kk;
-                f[j] = row < a.T ? to_f32(dO[(((size_t)b * a.T + row) * H + h) * Dv + col]) : 0.f;
+                for (int x = 0; x < 4; ++x) { f[x] = lo.get(x); f[4 + x] = hi.get(x); }
+                dof[s] = F::from(f);
+            } else {
+                const Vec4<T> q4 = Vec4<T>::load(base);
+                float f[4];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) f[x] = q4.get(x);
+                dof[s] = F::from(f);
             }
-            o.dof[s] = F::from(f);
         }
     };
 
@@ -262,14 +284,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
     };
     auto consume = [&]() { pf ^= pfv[0].x ^ pfv[1].y; };
 
-    Ops cur;
-    load_ops(cur, NC - 1);
-    for (int n = NC - 1; n >= 0; --n) {
+    // one step of the reverse chain on chunk n with its operands o; the
+    // next chunk's dO piece (in nx, loaded during this step) is staged before
+    // the step's second barrier
+    auto step = [&](const Ops& o, int n, const Ops* nx) {
         const size_t unit = (size_t)bh * NC + n;
         consume();
         if (n >= 3) prefetch(n - 3);
-        Ops nxt;
-        if (n > 0) load_ops(nxt, n - 1);
         // the gradient of the state leaving chunk n
 #pragma unroll
         for (int u = 0; u < G::SPW; ++u) {
@@ -280,16 +301,17 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
                     a.DSN[(unit * DK + 16 * t + 4 * lg + i) * Dv + col] = dS[u][i];
             }
         }
-        F sf[G::NKD];
+        F sf[G::NKD], dof[G::NKC];
 #pragma unroll
         for (int s = 0; s < G::NKD; ++s) sf[s] = sSf[s * 64 + lane];
+        do_frags(dof, n);
         // X for token tile `wave`
         if (G::NM == 4 || wave < G::NM) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int s = 0; s < G::NKC; ++s) acc = mma(cur.pt[s], cur.dof[s], acc);
+            for (int s = 0; s < G::NKC; ++s) acc = mma(o.pt[s], dof[s], acc);
 #pragma unroll
-            for (int s = 0; s < G::NKD; ++s) acc = mma(cur.kt[s], sf[s], acc);
+            for (int s = 0; s < G::NKD; ++s) acc = mma(o.kt[s], sf[s], acc);
             float* xb = a.XB + (unit * C + 16 * wave + 4 * lg) * Dv + col;
             f32x4 neg;
 #pragma unroll
@@ -310,17 +332,30 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
             if (G::NT % 4 == 0 || t < G::NT) {
                 f32x4 acc;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = cur.gc[u][i] * dS[u][i];
+                for (int i = 0; i < 4; ++i) acc[i] = o.gc[u][i] * dS[u][i];
 #pragma unroll
-                for (int s = 0; s < G::NKC; ++s) acc = mma(cur.qt[u][s], cur.dof[s], acc);
+                for (int s = 0; s < G::NKC; ++s) acc = mma(o.qt[u][s], dof[s], acc);
 #pragma unroll
-                for (int s = 0; s < G::NKC; ++s) acc = mma(cur.wt[u][s], xf[s], acc);
+                for (int s = 0; s < G::NKC; ++s) acc = mma(o.wt[u][s], xf[s], acc);
                 dS[u] = acc;
                 put_tile<T, G::KB>(sSf, t, lane, acc);
             }
         }
+        if (nx) stage_do(*nx, n - 1);
         __syncthreads();
-        if (n > 0) cur = nxt;
+    };
+
+    // two operand sets used in turn (no register copies between steps)
+    Ops A, B;
+    load_ops(A, NC - 1);
+    stage_do(A, NC - 1);
+    __syncthreads();
+    for (int n = NC - 1; n >= 0; n -= 2) {
+        if (n >= 1) load_ops(B, n - 1);
+        step(A, n, n >= 1 ? &B : nullptr);
+        if (n < 1) break;
+        if (n >= 2) load_ops(A, n - 2);
+        step(B, n - 1, n >= 2 ? &A : nullptr);
     }
     consume();
     if (a.T < 0) a.XB[lane] = __uint_as_float(pf);
