@@ -169,6 +169,9 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
     // dO of this column slice, two chunks, transposed ([buffer][column][token]),
     // so a lane's fragment slots (runs of 4 consecutive tokens) are 8 bytes
     __shared__ __attribute__((aligned(16))) T sDOt[2][16][C];
+    // this step's dSn and X slices in fp32, written through LDS so the
+    // global stores are 16-byte and coalesced
+    __shared__ __attribute__((aligned(16))) float sOut[(DK + C) * 16];
 
     const int Dv = a.Dv, H = a.H, NS = Dv / 16, NC = a.NC;
     const int gid = blockIdx.x, xcd = gid % kXcds, jx = gid / kXcds;
@@ -291,14 +294,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
         const size_t unit = (size_t)bh * NC + n;
         consume();
         if (n >= 3) prefetch(n - 3);
-        // the gradient of the state leaving chunk n
+        // the gradient of the state leaving chunk n (rows 0 .. DK-1 of sOut)
 #pragma unroll
         for (int u = 0; u < G::SPW; ++u) {
             const int t = wave + 4 * u;
             if (t < G::NT) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    a.DSN[(unit * DK + 16 * t + 4 * lg + i) * Dv + col] = dS[u][i];
+                for (int i = 0; i < 4; ++i) sOut[(16 * t + 4 * lg + i) * 16 + ln] = dS[u][i];
             }
         }
         F sf[G::NKD], dof[G::NKC];
@@ -312,16 +314,23 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
             for (int s = 0; s < G::NKC; ++s) acc = mma(o.pt[s], dof[s], acc);
 #pragma unroll
             for (int s = 0; s < G::NKD; ++s) acc = mma(o.kt[s], sf[s], acc);
-            float* xb = a.XB + (unit * C + 16 * wave + 4 * lg) * Dv + col;
             f32x4 neg;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                xb[(size_t)i * Dv] = acc[i];
+                sOut[(DK + 16 * wave + 4 * lg + i) * 16 + ln] = acc[i];
                 neg[i] = -acc[i];
             }
             put_tile<T, G::KB>(sXf, wave, lane, neg);
         }
         __syncthreads();
+        // dSn [DK][16] and X [C][16] of this column slice to memory
+        for (int e = tid; e < (DK + C) * 4; e += kBwdThreads) {
+            const int r = e >> 2, c4 = 4 * (e & 3);
+            const float4 v = *reinterpret_cast<const float4*>(&sOut[r * 16 + c4]);
+            float* dst = r < DK ? a.DSN + (unit * DK + r) * Dv + slice * 16 + c4
+                                : a.XB + (unit * C + r - DK) * Dv + slice * 16 + c4;
+            *reinterpret_cast<float4*>(dst) = v;
+        }
         F xf[G::NKC];
 #pragma unroll
         for (int s = 0; s < G::NKC; ++s) xf[s] = sXf[s * 64 + lane];
