@@ -679,7 +679,7 @@ __global__ __launch_bounds__(kLocalThreads) void bwd_local_kernel(BwdLocalArgs a
     //   sum_{j > e'} B[j,r] rho(j,r) x_j = rho(e', r) sum_j B[j,r] (x_j rho(j, e'))
     // (x = q with B1, x = beta k with B3).  The decayed operands are exact
     // running products of the gates (|factor| <= 1), built per channel.
-    constexpr int NDR = G::NDR, DKP = G::DKP;
+    constexpr int DKP = G::DKP;
     auto offL = [](int b) { return 8 * b * (b - 1); };                 // rows of blocks before b
     auto offU = [](int b) { return 16 * (b * (NM - 1) - b * (b - 1) / 2); };
     f32x4 mL1[NM], mL3[NM], mU1[NM], mU2[NM];
@@ -794,7 +794,6 @@ __global__ __launch_bounds__(kLocalThreads) void bwd_local_kernel(BwdLocalArgs a
             }
         }
     }
-    (void)NDR;
 
     float dbp[NM][4];
 #pragma unroll

@@ -149,3 +149,39 @@ def test_backward_full_headline_shape_sampled_heads():
     say("  " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
     for k, v in errs.items():
         assert v <= TOL[w.dtype], (k, v)
+
+
+@pytest.mark.parametrize("name,base,ov,dv", [
+    ("f32_ckda_dk64_dv32_c64_T150", 1, dict(B=1, H=2, T=150, D=64, chunk=64), 32),
+    ("bf16_ckda_dk128_dv64_c64_T200", 3, dict(B=1, H=2, T=200, chunk=64), 64),
+    ("bf16_kda_dk64_dv112_c32_T90", 2, dict(B=1, H=1, T=90, D=64, chunk=32), None),
+])
+def test_backward_dk_ne_dv(name, base, ov, dv):
+    """Dk != Dv: rows and columns of the state and its gradient must not be
+    swapped anywhere (v, dO and dS_T keep their first Dv columns; for Dv >
+    Dk the inputs are drawn at width Dv and q, k, alpha cut to Dk)."""
+    w, inp, dO, dST = _inputs(base, ov, True, True)
+    if dv is None:
+        # Dv = 112 > Dk = 64: draw at D = 112 and cut the key side
+        w = workloads.workload(base, **{**ov, "D": 112, "s0_std": 0.5})
+        inp = workloads.make_prefill(w)
+        dO, dST = workloads.make_backward_seeds(w)
+        for k_ in ("q", "k", "alpha"):
+            inp[k_] = inp[k_][..., :64].contiguous()
+        # keys back to unit length after the cut (the recipe's normalisation)
+        inp["k"] = (inp["k"].float() / inp["k"].float().norm(dim=-1, keepdim=True)).to(w.dtype).contiguous()
+        inp["S0"] = inp["S0"][:, :, :64, :].contiguous()
+        dST = dST[:, :, :64, :].contiguous()
+    else:
+        inp["v"] = inp["v"][..., :dv].contiguous()
+        dO = dO[..., :dv].contiguous()
+        if inp["S0"] is not None:
+            inp["S0"] = inp["S0"][..., :dv].contiguous()
+        dST = dST[..., :dv].contiguous()
+    say(f"[backward] {name}: q {tuple(inp['q'].shape)} v {tuple(inp['v'].shape)}")
+    ref = _oracle(inp, dO, dST)
+    g = _gpu(w, inp, dO, dST)
+    errs = _errors(g, ref)
+    say("  " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= TOL[w.dtype], (k, v)
