@@ -62,6 +62,9 @@ def _load():
         lib.kda_oracle_backward.argtypes = [fp, fp, fp, fp, fp, fp, fp, fp, dp, dp, dp, dp, dp,
                                             dp, i, i, i, i, i, i]
         lib.kda_oracle_backward.restype = i
+        lib.kda_oracle_backward_prologue.argtypes = [fp, fp, fp, fp, fp, fp, fp, fp, d, d, d, d, i,
+                                                     dp, dp, dp, dp, dp, dp, i, i, i, i, i, i]
+        lib.kda_oracle_backward_prologue.restype = i
         lib.kda_oracle_decode.argtypes = [fp, fp, fp, fp, fp, dp, dp,
                                           i, i, i, i, i, i]
         lib.kda_oracle_decode.restype = i
@@ -199,6 +202,38 @@ def backward(q, k, v, alpha, beta, dO, S0=None, dST=None, nthreads: int | None =
         _ptr(r["dbeta"], dp), _ptr(r["dS0"], dp), B, T, H, Dk, Dv, nthreads or default_threads())
     if rc != 0:
         raise RuntimeError("kda_oracle_backward failed")
+    return r
+
+
+def backward_prologue(q_raw, k_raw, v, gate, beta_logit, dO, S0=None, dST=None, *,
+                      alpha_min: float, alpha_max: float, beta_max: float, eps: float,
+                      normalize_q: bool, nthreads: int | None = None):
+    """Gradients of L = sum <out, dO> + <ST, dST> for the forward from raw
+    inputs (forward_prologue) with respect to q_raw, k_raw, v, the gate logits,
+    the beta logits and S0.  Returns a dict of float64 arrays dq, dk, dv,
+    dgate, dbeta_logit, dS0."""
+    lib = _load()
+    q, k, v, g, c, dO = (_f32(x) for x in (q_raw, k_raw, v, gate, beta_logit, dO))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    assert k.shape == (B, T, H, Dk) and g.shape == (B, T, H, Dk) and c.shape == (B, T, H)
+    assert v.shape == (B, T, H, Dv) and dO.shape == v.shape
+    s0 = None if S0 is None else _f32(S0)
+    ds = None if dST is None else _f32(dST)
+    r = {"dq": np.empty((B, T, H, Dk)), "dk": np.empty((B, T, H, Dk)),
+         "dv": np.empty((B, T, H, Dv)), "dgate": np.empty((B, T, H, Dk)),
+         "dbeta_logit": np.empty((B, T, H)), "dS0": np.empty((B, H, Dk, Dv))}
+    dp = ctypes.c_double
+    rc = lib.kda_oracle_backward_prologue(
+        _ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float),
+        _ptr(g, ctypes.c_float), _ptr(c, ctypes.c_float), _ptr(s0, ctypes.c_float),
+        _ptr(dO, ctypes.c_float), _ptr(ds, ctypes.c_float),
+        float(alpha_min), float(alpha_max), float(beta_max), float(eps), int(bool(normalize_q)),
+        _ptr(r["dq"], dp), _ptr(r["dk"], dp), _ptr(r["dv"], dp), _ptr(r["dgate"], dp),
+        _ptr(r["dbeta_logit"], dp), _ptr(r["dS0"], dp), B, T, H, Dk, Dv,
+        nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError("kda_oracle_backward_prologue failed")
     return r
 
 

@@ -226,6 +226,65 @@ int kda_oracle_forward_phase(const float* q, const float* k, const float* v,
 }
 
 /*
+ * One token's gradients with respect to the inputs as the recurrence uses
+ * them (dqt, dkt, dat, db for q, k, alpha, beta) stored as gradients of the
+ * given inputs: unchanged without a prologue; with one, by the chain rule
+ * through eqs. (15), (17), (18):
+ *   d gate_c       = dalpha_c (amax - amin) s_c (1 - s_c),  s_c = sigmoid(gate_c)
+ *   d beta_logit   = dbeta bmax s (1 - s),                   s = sigmoid(beta_logit)
+ *   d k_raw        = dk / (n + eps) - k_raw <k_raw, dk> / (n (n + eps)^2),  n = ||k_raw||
+ *                    (the second term absent for n = 0; zero when n + eps = 0)
+ *   d q_raw        likewise when q is normalised, else dq.
+ */
+static void store_token_grads(const struct prologue* pro, const float* q, const float* k,
+                              const float* alpha, float beta, const double* qd,
+                              const double* kd, const double* dqt, const double* dkt,
+                              const double* dat, double db, double* dq, double* dk,
+                              double* dalpha, double* dbeta, int Dk)
+{
+    (void)qd;
+    (void)kd;
+    if (!pro) {
+        for (int c = 0; c < Dk; ++c) {
+            dq[c] = dqt[c];
+            dk[c] = dkt[c];
+            dalpha[c] = dat[c];
+        }
+        *dbeta = db;
+        return;
+    }
+    for (int c = 0; c < Dk; ++c) {
+        const double sg = sigmoid((double)alpha[c]);
+        dalpha[c] = dat[c] * (pro->amax - pro->amin) * sg * (1.0 - sg);
+    }
+    const double sb = sigmoid((double)beta);
+    *dbeta = db * pro->bmax * sb * (1.0 - sb);
+    for (int pass = 0; pass < 2; ++pass) {
+        const float* raw = pass == 0 ? k : q;
+        const double* g = pass == 0 ? dkt : dqt;
+        double* out = pass == 0 ? dk : dq;
+        if (pass == 1 && !pro->normalize_q) {
+            for (int c = 0; c < Dk; ++c) out[c] = g[c];
+            continue;
+        }
+        double n = 0.0, dot = 0.0;
+        for (int c = 0; c < Dk; ++c) {
+            n += (double)raw[c] * (double)raw[c];
+            dot += (double)raw[c] * g[c];
+        }
+        n = sqrt(n);
+        const double den = n + pro->eps;
+        for (int c = 0; c < Dk; ++c) {
+            if (den <= 0.0) {
+                out[c] = 0.0;
+            } else {
+                out[c] = g[c] / den - (n > 0.0 ? (double)raw[c] * dot / (n * den * den) : 0.0);
+            }
+        }
+    }
+}
+
+/*
  * Reverse-mode derivative of the forward above (inputs taken as given, no
  * prologue, no phase), for the scalar loss
  *   L = sum_t <o_t, dO_t> + <S_T, dST>
@@ -244,10 +303,11 @@ int kda_oracle_forward_phase(const float* q, const float* k, const float* v,
  * and dS0 is the last G.  The states S_{t-1} are recomputed forward from
  * checkpoints taken every 64 tokens (the same forward arithmetic).
  */
-static int backward_impl(const float* q, const float* k, const float* v, const float* alpha,
-                         const float* beta, const float* S0, const float* dO, const float* dST,
-                         double* dq, double* dk, double* dv, double* dalpha, double* dbeta,
-                         double* dS0, int B, int T, int H, int Dk, int Dv, int nthreads)
+static int backward_impl(const struct prologue* pro, const float* q, const float* k,
+                         const float* v, const float* alpha, const float* beta, const float* S0,
+                         const float* dO, const float* dST, double* dq, double* dk, double* dv,
+                         double* dalpha, double* dbeta, double* dS0, int B, int T, int H, int Dk,
+                         int Dv, int nthreads)
 {
     if (!q || !k || !v || !alpha || !beta || !dO || !dq || !dk || !dv || !dalpha || !dbeta)
         return -1;
@@ -265,7 +325,7 @@ static int backward_impl(const float* q, const float* k, const float* v, const f
         /* checkpoints [nseg][SZ], states of one segment [K + 1][SZ], G, dSt,
          * and per-token vectors */
         const size_t nd = (size_t)(nseg > 0 ? nseg : 1) * SZ + (size_t)(K + 1) * SZ + 2 * SZ +
-                          5 * (size_t)Dv + 3 * (size_t)Dk;
+                          5 * (size_t)Dv + 6 * (size_t)Dk;
         double* ck = (double*)malloc(sizeof(double) * nd);
         if (!ck) {
 #pragma omp atomic write
@@ -283,6 +343,9 @@ static int backward_impl(const float* q, const float* k, const float* v, const f
         double* qd = dod + Dv;
         double* kd = qd + Dk;
         double* ad = kd + Dk;
+        double* dqt = ad + Dk;      /* this token's gradients of q, k, alpha as used */
+        double* dkt = dqt + Dk;
+        double* dat = dkt + Dk;
 
         /* forward: checkpoint the state before tokens 0, K, 2K, ... */
         double* S = buf;
@@ -295,7 +358,7 @@ static int backward_impl(const float* q, const float* k, const float* v, const f
         for (int t = 0; t < T; ++t) {
             const size_t tok = ((size_t)b * T + t) * H + h;
             if (t % K == 0) memcpy(ck + (size_t)(t / K) * SZ, S, sizeof(double) * SZ);
-            const double bt = load_token(NULL, q + tok * Dk, k + tok * Dk, v + tok * Dv,
+            const double bt = load_token(pro, q + tok * Dk, k + tok * Dk, v + tok * Dv,
                                          alpha + tok * Dk, beta[tok], qd, kd, vd, ad, Dk, Dv, Dk);
             token_update(S, qd, kd, vd, ad, NULL, bt, NULL, Dk, Dv, pred);
         }
@@ -315,7 +378,7 @@ static int backward_impl(const float* q, const float* k, const float* v, const f
                 const size_t tok = ((size_t)b * T + t) * H + h;
                 double* nx = buf + (size_t)(t - a + 1) * SZ;
                 memcpy(nx, buf + (size_t)(t - a) * SZ, sizeof(double) * SZ);
-                const double bt = load_token(NULL, q + tok * Dk, k + tok * Dk, v + tok * Dv,
+                const double bt = load_token(pro, q + tok * Dk, k + tok * Dk, v + tok * Dv,
                                              alpha + tok * Dk, beta[tok], qd, kd, vd, ad, Dk, Dv, Dk);
                 token_update(nx, qd, kd, vd, ad, NULL, bt, NULL, Dk, Dv, pred);
             }
@@ -323,14 +386,14 @@ static int backward_impl(const float* q, const float* k, const float* v, const f
                 const size_t tok = ((size_t)b * T + t) * H + h;
                 const double* Sp = buf + (size_t)(t - a) * SZ;       /* S_{t-1} */
                 const double* Sn = Sp + SZ;                          /* S_t */
-                const double bt = load_token(NULL, q + tok * Dk, k + tok * Dk, v + tok * Dv,
+                const double bt = load_token(pro, q + tok * Dk, k + tok * Dk, v + tok * Dv,
                                              alpha + tok * Dk, beta[tok], qd, kd, vd, ad, Dk, Dv, Dk);
                 for (int j = 0; j < Dv; ++j) dod[j] = (double)dO[tok * Dv + j];
                 /* read-out o_t = S_t^T q_t */
                 for (int c = 0; c < Dk; ++c) {
                     double s = 0.0;
                     for (int j = 0; j < Dv; ++j) s += Sn[(size_t)c * Dv + j] * dod[j];
-                    dq[tok * Dk + c] = s;
+                    dqt[c] = s;
                     for (int j = 0; j < Dv; ++j) G[(size_t)c * Dv + j] += qd[c] * dod[j];
                 }
                 /* delta correction of St = diag(alpha) S_{t-1} */
@@ -348,14 +411,13 @@ static int backward_impl(const float* q, const float* k, const float* v, const f
                     dv[tok * Dv + j] = bt * y[j];
                     db += u[j] * y[j];
                 }
-                dbeta[tok] = db;
                 for (int c = 0; c < Dk; ++c) {
                     double s1 = 0.0, s2 = 0.0;
                     for (int j = 0; j < Dv; ++j) {
                         s1 += G[(size_t)c * Dv + j] * bt * u[j];
                         s2 += ad[c] * Sp[(size_t)c * Dv + j] * y[j];
                     }
-                    dk[tok * Dk + c] = s1 - bt * s2;
+                    dkt[c] = s1 - bt * s2;
                 }
                 for (int c = 0; c < Dk; ++c)
                     for (int j = 0; j < Dv; ++j)
@@ -364,9 +426,12 @@ static int backward_impl(const float* q, const float* k, const float* v, const f
                 for (int c = 0; c < Dk; ++c) {
                     double s = 0.0;
                     for (int j = 0; j < Dv; ++j) s += dSt[(size_t)c * Dv + j] * Sp[(size_t)c * Dv + j];
-                    dalpha[tok * Dk + c] = s;
+                    dat[c] = s;
                     for (int j = 0; j < Dv; ++j) G[(size_t)c * Dv + j] = ad[c] * dSt[(size_t)c * Dv + j];
                 }
+                store_token_grads(pro, q + tok * Dk, k + tok * Dk, alpha + tok * Dk, beta[tok],
+                                  qd, kd, dqt, dkt, dat, db, dq + tok * Dk, dk + tok * Dk,
+                                  dalpha + tok * Dk, dbeta + tok, Dk);
             }
         }
         if (dS0) memcpy(dS0 + (size_t)bh * SZ, G, sizeof(double) * SZ);
@@ -380,8 +445,21 @@ int kda_oracle_backward(const float* q, const float* k, const float* v, const fl
                         double* dq, double* dk, double* dv, double* dalpha, double* dbeta,
                         double* dS0, int B, int T, int H, int Dk, int Dv, int nthreads)
 {
-    return backward_impl(q, k, v, alpha, beta, S0, dO, dST, dq, dk, dv, dalpha, dbeta, dS0,
+    return backward_impl(NULL, q, k, v, alpha, beta, S0, dO, dST, dq, dk, dv, dalpha, dbeta, dS0,
                          B, T, H, Dk, Dv, nthreads);
+}
+
+int kda_oracle_backward_prologue(const float* q_raw, const float* k_raw, const float* v,
+                                 const float* gate, const float* beta_logit, const float* S0,
+                                 const float* dO, const float* dST, double amin, double amax,
+                                 double bmax, double eps, int normalize_q, double* dq_raw,
+                                 double* dk_raw, double* dv, double* dgate, double* dbeta_logit,
+                                 double* dS0, int B, int T, int H, int Dk, int Dv, int nthreads)
+{
+    if (!(eps >= 0.0)) return -1;
+    const struct prologue pro = {amin, amax, bmax, eps, normalize_q};
+    return backward_impl(&pro, q_raw, k_raw, v, gate, beta_logit, S0, dO, dST, dq_raw, dk_raw, dv,
+                         dgate, dbeta_logit, dS0, B, T, H, Dk, Dv, nthreads);
 }
 
 int kda_oracle_decode(const float* q, const float* k, const float* v,

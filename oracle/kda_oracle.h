@@ -79,6 +79,17 @@ int kda_oracle_backward(const float* q, const float* k, const float* v, const fl
                         double* dq, double* dk, double* dv, double* dalpha, double* dbeta,
                         double* dS0, int B, int T, int H, int Dk, int Dv, int nthreads);
 
+/* The same gradients for the forward from raw inputs
+ * (kda_oracle_forward_prologue): with respect to q_raw, k_raw, v, the gate
+ * logits, the beta logits and S0, by the chain rule through eqs. (15), (17)
+ * and (18) after the reverse pass.  Layouts as the forward's. */
+int kda_oracle_backward_prologue(const float* q_raw, const float* k_raw, const float* v,
+                                 const float* gate, const float* beta_logit, const float* S0,
+                                 const float* dO, const float* dST, double amin, double amax,
+                                 double bmax, double eps, int normalize_q, double* dq_raw,
+                                 double* dk_raw, double* dv, double* dgate, double* dbeta_logit,
+                                 double* dS0, int B, int T, int H, int Dk, int Dv, int nthreads);
+
 /* nsteps single-token updates applied to a resident double state in place.
  * Per-step inputs are stacked: q, k, alpha [nsteps, B, H, Dk],
  * v [nsteps, B, H, Dv], beta [nsteps, B, H]; out [nsteps, B, H, Dv];

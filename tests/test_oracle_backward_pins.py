@@ -157,3 +157,55 @@ def test_chunked_backward_equals_sequential(oracle_lib, chunk, T, ckda):
     for name in g:
         scale = max(1.0, float(np.abs(g[name]).max()))
         np.testing.assert_allclose(m[name], g[name], rtol=0, atol=1e-9 * scale, err_msg=name)
+
+
+# ---- backward through the input prologue ("Semidirect Fourier Delta
+# Attention" §3, eqs. (15), (17), (18)) ------------------------------------------
+
+PRO = dict(alpha_min=-1.0, alpha_max=1.0, beta_max=2.0, eps=0.0, normalize_q=True)
+
+
+def _raw(seed, T=5, H=2, Dk=4, Dv=3):
+    rng = np.random.default_rng(seed)
+    g = lambda *s: _grid(rng.uniform(-1.5, 1.5, s))
+    return dict(q=g(1, T, H, Dk), k=g(1, T, H, Dk), v=g(1, T, H, Dv), gate=g(1, T, H, Dk),
+                beta=g(1, T, H), S0=g(1, H, Dk, Dv)), g(1, T, H, Dv), g(1, H, Dk, Dv)
+
+
+def _loss_pro(oracle_lib, x, dO, dST, pro):
+    out, ST = oracle_lib.forward_prologue(x["q"], x["k"], x["v"], x["gate"], x["beta"], x["S0"],
+                                          nthreads=1, **pro)
+    return float(np.sum(out * dO) + np.sum(ST * dST))
+
+
+@pytest.mark.parametrize("pro", [PRO, dict(alpha_min=0.05, alpha_max=0.95, beta_max=1.0,
+                                                eps=0.125, normalize_q=False)])
+def test_backward_prologue_matches_differences(oracle_lib, pro):
+    """Every gradient of the raw inputs against a 4-point central difference
+    (error O(h^4); the raw inputs lie on a 2^-12 grid, the step is 2^-7)."""
+    x, dO, dST = _raw(3)
+    g = oracle_lib.backward_prologue(x["q"], x["k"], x["v"], x["gate"], x["beta"], dO, x["S0"],
+                                     dST, nthreads=1, **pro)
+    names = {"q": "dq", "k": "dk", "v": "dv", "gate": "dgate", "beta": "dbeta_logit", "S0": "dS0"}
+    h = 2.0 ** -7
+    for name, gname in names.items():
+        for idx in np.ndindex(x[name].shape):
+            vals = []
+            for m in (2, 1, -1, -2):
+                xp = {n: a.copy() for n, a in x.items()}
+                xp[name][idx] += m * h
+                vals.append(_loss_pro(oracle_lib, xp, dO, dST, pro))
+            fd = (-vals[0] + 8 * vals[1] - 8 * vals[2] + vals[3]) / (12 * h)
+            assert abs(fd - g[gname][idx]) <= 2e-6 * (1 + abs(fd)), (name, idx, fd, g[gname][idx])
+
+
+def test_backward_prologue_key_gradient_is_tangent(oracle_lib):
+    """With eps = 0, k = k_raw / |k_raw| is invariant under scaling k_raw, so
+    the gradient of k_raw is orthogonal to k_raw (likewise q_raw)."""
+    x, dO, dST = _raw(8, T=7, Dk=6, Dv=5)
+    g = oracle_lib.backward_prologue(x["q"], x["k"], x["v"], x["gate"], x["beta"], dO, x["S0"],
+                                     dST, **PRO)
+    for raw, gr in (("k", "dk"), ("q", "dq")):
+        dots = np.sum(g[gr] * x[raw], axis=-1)
+        scale = np.abs(g[gr]).max() * np.abs(x[raw]).max()
+        assert np.abs(dots).max() <= 1e-12 * scale * x[raw].shape[-1]
