@@ -90,6 +90,12 @@ def load():
     lib.kda_chunk_backward_workspace_size.restype = i
     lib.kda_chunk_backward.argtypes = [vp] * 14 + [i] * 8 + [u, vp, sz, vp]
     lib.kda_chunk_backward.restype = i
+    lib.kda_chunk_backward_prologue_workspace_size.argtypes = [i, i, i, i, i, i, i,
+                                                               ctypes.POINTER(sz)]
+    lib.kda_chunk_backward_prologue_workspace_size.restype = i
+    lib.kda_chunk_backward_prologue.argtypes = [vp] * 8 + [ctypes.POINTER(Prologue)] + [vp] * 6 + \
+        [i] * 8 + [u, vp, sz, vp]
+    lib.kda_chunk_backward_prologue.restype = i
     lib.kda_gate_prep.argtypes = [vp] * 4 + [i] * 5 + [vp]
     lib.kda_gate_prep.restype = i
     lib.kda_last_stage_times.argtypes = [ctypes.POINTER(ctypes.c_float),
@@ -362,6 +368,49 @@ def chunk_backward(q, k, v, alpha, beta, d_out, initial_state=None, d_final_stat
                                 B, T, H, Dk, Dv, chunk, _DT[q.dtype], mode, flags,
                                 _ptr(workspace), wsb, _stream(stream))
     _check("kda_chunk_backward", st)
+    return g
+
+
+def chunk_backward_prologue(q_raw, k_raw, v, gate, beta_logit, d_out, initial_state=None,
+                            d_final_state=None, *, alpha_min: float, alpha_max: float,
+                            beta_max: float, eps: float = 1e-6, normalize_q: bool = True,
+                            chunk: int = 64, mode: int = CKDA, want_d_initial_state: bool = True,
+                            workspace=None, stream=None, flags: int = 0):
+    """Backward of chunk_forward_prologue (kda_chunk_backward_prologue):
+    gradients with respect to q_raw, k_raw, v, the gate logits, the beta logits
+    and initial_state.  Returns a dict dq, dk, dv (q_raw's dtype), d_gate,
+    d_beta_logit, d_initial_state (fp32; None unless wanted)."""
+    lib = load()
+    B, T, H, Dk = q_raw.shape
+    Dv = v.shape[-1]
+    dev = q_raw.device
+    g = {"dq": torch.empty((B, T, H, Dk), dtype=q_raw.dtype, device=dev),
+         "dk": torch.empty((B, T, H, Dk), dtype=q_raw.dtype, device=dev),
+         "dv": torch.empty((B, T, H, Dv), dtype=q_raw.dtype, device=dev),
+         "d_gate": torch.empty((B, T, H, Dk), dtype=torch.float32, device=dev),
+         "d_beta_logit": torch.empty((B, T, H), dtype=torch.float32, device=dev),
+         "d_initial_state": (torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
+                             if want_d_initial_state else None)}
+    if workspace is None:
+        n = ctypes.c_size_t(0)
+        _check("kda_chunk_backward_prologue_workspace_size",
+               lib.kda_chunk_backward_prologue_workspace_size(B, T, H, Dk, Dv, chunk,
+                                                               _DT[q_raw.dtype], ctypes.byref(n)))
+        workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=dev)
+    _dev(q_raw, k_raw, v, gate, beta_logit, d_out, initial_state, d_final_state, workspace,
+         *g.values())
+    if (q_raw.dtype not in _DT or k_raw.dtype != q_raw.dtype or v.dtype != q_raw.dtype
+            or d_out.dtype != q_raw.dtype):
+        raise ValueError("q_raw, k_raw, v and d_out must share one dtype (float32 or bfloat16)")
+    pro = Prologue(alpha_min, alpha_max, beta_max, eps, int(bool(normalize_q)))
+    wsb = workspace.numel() * workspace.element_size()
+    st = lib.kda_chunk_backward_prologue(
+        _ptr(q_raw), _ptr(k_raw), _ptr(v), _ptr(gate), _ptr(beta_logit), _ptr(initial_state),
+        _ptr(d_out), _ptr(d_final_state), ctypes.byref(pro), _ptr(g["dq"]), _ptr(g["dk"]),
+        _ptr(g["dv"]), _ptr(g["d_gate"]), _ptr(g["d_beta_logit"]), _ptr(g["d_initial_state"]),
+        B, T, H, Dk, Dv, chunk, _DT[q_raw.dtype], mode, flags, _ptr(workspace), wsb,
+        _stream(stream))
+    _check("kda_chunk_backward_prologue", st)
     return g
 
 

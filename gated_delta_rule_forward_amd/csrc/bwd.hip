@@ -1121,6 +1121,107 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_tiny_kernel(BwdLocalArgs a)
     }
 }
 
+// ---- the input prologue around the backward ("Semidirect Fourier Delta
+// Attention" §3, eqs. (15), (17), (18)) --------------------------------------
+// One token of one head per NQ = DK / 4 consecutive lanes, four channels per
+// lane (the same grouping and fp32 arithmetic as the prep kernels' prologue).
+template <typename T, int DK>
+__global__ __launch_bounds__(256) void prologue_in_kernel(ProArgs a)
+{
+    constexpr int NQ = DK / 4, TPB = 256 / NQ;
+    const size_t tokn = (size_t)blockIdx.x * TPB + threadIdx.x / NQ;
+    const int c0 = 4 * (threadIdx.x % NQ);
+    const bool ok = tokn < a.ntok;
+    const size_t t = ok ? tokn : a.ntok - 1;          // idle lanes repeat the last token
+    const size_t e = t * DK + c0;
+    Vec4<T> k = Vec4<T>::load(static_cast<const T*>(a.k_raw) + e);
+    Vec4<T> q = Vec4<T>::load(static_cast<const T*>(a.q_raw) + e);
+    k = l2_normalised<T, NQ>(k, a.eps);
+    if (a.normq) q = l2_normalised<T, NQ>(q, a.eps);
+    const float4 g = *reinterpret_cast<const float4*>(a.gate + e);
+    if (ok) {
+        *reinterpret_cast<Vec4<T>*>(static_cast<T*>(a.kh) + e) = k;
+        *reinterpret_cast<Vec4<T>*>(static_cast<T*>(a.qh) + e) = q;
+        *reinterpret_cast<float4*>(a.al + e) =
+            make_float4(a.amin + a.arange * sigmoid_f32(g.x), a.amin + a.arange * sigmoid_f32(g.y),
+                        a.amin + a.arange * sigmoid_f32(g.z), a.amin + a.arange * sigmoid_f32(g.w));
+        if (c0 == 0) a.be[t] = a.bmax * sigmoid_f32(a.blogit[t]);
+    }
+}
+
+// gradients of the raw inputs from those of the transformed ones:
+//   d gate = d alpha (amax - amin) s (1 - s),  d beta_logit = d beta bmax s (1 - s)
+//   d x_raw = d x / (n + eps) - x_raw <x_raw, d x> / (n (n + eps)^2),  n = |x_raw|
+// (x = k, and q when normalised; the second term absent for n = 0, zero
+// when n + eps = 0).  d gate and d beta_logit are updated in place.
+template <typename T, int DK>
+__global__ __launch_bounds__(256) void prologue_out_kernel(ProArgs a)
+{
+    constexpr int NQ = DK / 4, TPB = 256 / NQ;
+    const size_t tokn = (size_t)blockIdx.x * TPB + threadIdx.x / NQ;
+    const int c0 = 4 * (threadIdx.x % NQ);
+    const bool ok = tokn < a.ntok;
+    const size_t t = ok ? tokn : a.ntok - 1;
+    const size_t e = t * DK + c0;
+    auto raw_grad = [&](const void* rawp, const void* gp, void* outp, bool norm) {
+        const Vec4<T> x = Vec4<T>::load(static_cast<const T*>(rawp) + e);
+        const Vec4<T> g = Vec4<T>::load(static_cast<const T*>(gp) + e);
+        float f[4];
+        if (!norm) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) f[i] = g.get(i);
+        } else {
+            float ss = 0.f, dot = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ss += x.get(i) * x.get(i);
+                dot += x.get(i) * g.get(i);
+            }
+            const float n = __builtin_sqrtf(quad_group_sum<NQ>(ss));
+            dot = quad_group_sum<NQ>(dot);
+            const float den = n + a.eps;
+            const float inv = den > 0.f ? 1.f / den : 0.f;
+            const float c2 = (den > 0.f && n > 0.f) ? dot / (n * den * den) : 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) f[i] = g.get(i) * inv - x.get(i) * c2;
+        }
+        if (ok) *reinterpret_cast<Vec4<T>*>(static_cast<T*>(outp) + e) = Vec4<T>::from(f);
+    };
+    raw_grad(a.k_raw, a.dkh, a.dk_raw, true);
+    raw_grad(a.q_raw, a.dqh, a.dq_raw, a.normq != 0);
+    if (ok) {
+        const float4 g = *reinterpret_cast<const float4*>(a.gate + e);
+        float4 d = *reinterpret_cast<const float4*>(a.dgate + e);
+        auto ds = [&](float x) { const float s = sigmoid_f32(x); return a.arange * s * (1.f - s); };
+        d.x *= ds(g.x); d.y *= ds(g.y); d.z *= ds(g.z); d.w *= ds(g.w);
+        *reinterpret_cast<float4*>(a.dgate + e) = d;
+        if (c0 == 0) {
+            const float s = sigmoid_f32(a.blogit[t]);
+            a.dblogit[t] *= a.bmax * s * (1.f - s);
+        }
+    }
+}
+
+template <typename T, int DK>
+hipError_t launch_pro_t(bool out, const ProArgs& a, hipStream_t stream)
+{
+    constexpr int TPB = 256 / (DK / 4);
+    const unsigned grid = (unsigned)((a.ntok + TPB - 1) / TPB);
+    if (out) return launch_kernel(prologue_out_kernel<T, DK>, dim3(grid), dim3(256), 0, stream, a);
+    return launch_kernel(prologue_in_kernel<T, DK>, dim3(grid), dim3(256), 0, stream, a);
+}
+
+template <typename T>
+hipError_t launch_pro_dk(bool out, int Dk, const ProArgs& a, hipStream_t stream)
+{
+    switch (Dk) {
+    case 32: return launch_pro_t<T, 32>(out, a, stream);
+    case 64: return launch_pro_t<T, 64>(out, a, stream);
+    case 128: return launch_pro_t<T, 128>(out, a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 // ---- launchers ------------------------------------------------------------------
 template <typename K>
 hipError_t set_lds(K kern, size_t bytes)
@@ -1193,6 +1294,13 @@ hipError_t bwd_c(int stage, const ChunkShape& s, const ChunkWorkspace& ws, const
 }
 
 }  // namespace
+
+hipError_t launch_backward_prologue(bool out, IoType io, int Dk, const ProArgs& a, hipStream_t stream)
+{
+    if (a.ntok == 0) return hipSuccess;
+    if (io == IoType::F32) return launch_pro_dk<float>(out, Dk, a, stream);
+    return launch_pro_dk<bf16_t>(out, Dk, a, stream);
+}
 
 hipError_t launch_backward_stage(int stage, IoType io, const ChunkShape& s, const ChunkWorkspace& ws,
                                  const BwdChainArgs& ca, const BwdLocalArgs& la, hipStream_t stream)

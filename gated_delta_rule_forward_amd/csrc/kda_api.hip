@@ -43,7 +43,7 @@ bool overlaps(const void* p, size_t n, const void* q, size_t m)
 // ---- per-kernel events (opt-in) ---------------------------------------------
 // Stage i owns events 2i and 2i+1, attached to its kernel launch: the elapsed
 // time between them is that kernel's own duration.
-constexpr int kMaxStages = 8;
+constexpr int kMaxStages = 12;
 struct StageEvents {
     std::mutex mu;
     hipEvent_t ev[2 * kMaxStages] = {};
@@ -395,6 +395,13 @@ size_t backward_layout(int B, int T, int H, int Dk, int Dv, int chunk, IoType io
     return n;
 }
 
+kda_status_t backward_enqueue(const void* q, const void* k, const void* v, const float* alpha,
+                              const float* beta, const float* initial_state, const void* d_out,
+                              const float* d_final_state, void* dq, void* dk, void* dv,
+                              float* d_alpha, float* d_beta, float* d_initial_state, int B, int T,
+                              int H, int Dk, int Dv, int chunk, kda_dtype_t dtype, kda_mode_t mode,
+                              void* workspace, Recorder& rec, hipStream_t s);
+
 kda_status_t check_backward_shape(int B, int T, int H, int Dk, int Dv, int chunk,
                                   kda_dtype_t dtype)
 {
@@ -458,6 +465,21 @@ kda_status_t chunk_backward(const void* q, const void* k, const void* v, const f
         lock.lock();
         if (stage_begin() != hipSuccess) return KDA_ERR_HIP;
     }
+    return backward_enqueue(q, k, v, alpha, beta, initial_state, d_out, d_final_state, dq, dk, dv,
+                            d_alpha, d_beta, d_initial_state, B, T, H, Dk, Dv, chunk, dtype, mode,
+                            workspace, rec, s);
+}
+
+// the backward's launches (arguments validated by the caller, stage events
+// through rec)
+kda_status_t backward_enqueue(const void* q, const void* k, const void* v, const float* alpha,
+                              const float* beta, const float* initial_state, const void* d_out,
+                              const float* d_final_state, void* dq, void* dk, void* dv,
+                              float* d_alpha, float* d_beta, float* d_initial_state, int B, int T,
+                              int H, int Dk, int Dv, int chunk, kda_dtype_t dtype, kda_mode_t mode,
+                              void* workspace, Recorder& rec, hipStream_t s)
+{
+    const size_t nstate = (size_t)B * H * Dk * Dv * 4;
     if (T == 0) {
         // no tokens: the loss is <S0, dST>, so dS0 = dST
         if (!d_initial_state) return KDA_OK;
@@ -520,6 +542,111 @@ kda_status_t chunk_backward(const void* q, const void* k, const void* v, const f
         if (rec.done() != hipSuccess) return KDA_ERR_HIP;
     }
     return KDA_OK;
+}
+
+// the backward from raw inputs: workspace = the backward's, then the
+// transformed inputs q^, k^ (io type), alpha, beta (fp32) and the gradients
+// dq^, dk^ (io type) of the transformed q, k
+size_t backward_prologue_layout(int B, int T, int H, int Dk, int Dv, int chunk, IoType io,
+                                size_t xo[6])
+{
+    size_t off[kda::kWorkspaceRegions], boff[kBwdRegions];
+    size_t n = backward_layout(B, T, H, Dk, Dv, chunk, io, off, boff);
+    const size_t ntok = (size_t)B * T * H, e = io == IoType::F32 ? 4 : 2;
+    const size_t sz[6] = {ntok * Dk * e, ntok * Dk * e, ntok * Dk * 4, ntok * 4, ntok * Dk * e,
+                          ntok * Dk * e};
+    for (int i = 0; i < 6; ++i) {
+        xo[i] = n;
+        n += (sz[i] + 255) & ~size_t(255);
+    }
+    return n;
+}
+
+kda_status_t chunk_backward_prologue(const void* q_raw, const void* k_raw, const void* v,
+                                     const float* gate, const float* beta_logit,
+                                     const float* initial_state, const void* d_out,
+                                     const float* d_final_state, const kda_prologue_t* pro,
+                                     void* dq_raw, void* dk_raw, void* dv, float* d_gate,
+                                     float* d_beta_logit, float* d_initial_state, int B, int T,
+                                     int H, int Dk, int Dv, int chunk, kda_dtype_t dtype,
+                                     kda_mode_t mode, unsigned flags, void* workspace,
+                                     size_t workspace_bytes, void* stream)
+{
+    kda_status_t st = check_backward_shape(B, T, H, Dk, Dv, chunk, dtype);
+    if (st != KDA_OK) return st;
+    if (mode != KDA_MODE_KDA && mode != KDA_MODE_CKDA) return KDA_ERR_UNSUPPORTED;
+    if (flags & ~KDA_FLAG_STAGE_EVENTS) return KDA_ERR_UNSUPPORTED;
+    if (!pro) return KDA_ERR_NULL_POINTER;
+    if (!prologue_ok(*pro, mode)) return KDA_ERR_UNSUPPORTED;
+    if (T > 0 && (!q_raw || !k_raw || !v || !gate || !beta_logit || !d_out || !dq_raw || !dk_raw ||
+                  !dv || !d_gate || !d_beta_logit))
+        return KDA_ERR_NULL_POINTER;
+    const IoType io = dtype == KDA_DTYPE_F32 ? IoType::F32 : IoType::BF16;
+    size_t xo[6];
+    const size_t ws_need = T == 0 ? 0 : backward_prologue_layout(B, T, H, Dk, Dv, chunk, io, xo);
+    if (T > 0 && !workspace) return KDA_ERR_NULL_POINTER;
+    if (workspace_bytes < ws_need) return KDA_ERR_WORKSPACE_TOO_SMALL;
+
+    const size_t e = elem_size(dtype);
+    const size_t ntok = (size_t)B * T * H;
+    const size_t nstate = (size_t)B * H * Dk * Dv * 4;
+    const void* vec[] = {q_raw, k_raw, d_out, gate, workspace, dq_raw, dk_raw, d_gate};
+    for (const void* p : vec)
+        if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
+    const void* elt[] = {v, beta_logit, initial_state, d_final_state, dv, d_beta_logit,
+                         d_initial_state};
+    const uintptr_t ea[] = {e, 4, 4, 4, e, 4, 4};
+    for (int i = 0; i < 7; ++i)
+        if (elt[i] && !aligned(elt[i], ea[i])) return KDA_ERR_MISALIGNED;
+    struct R { const void* p; size_t n; };
+    const R in[] = {{q_raw, ntok * Dk * e}, {k_raw, ntok * Dk * e}, {v, ntok * Dv * e},
+                    {gate, ntok * Dk * 4}, {beta_logit, ntok * 4},
+                    {initial_state, initial_state ? nstate : 0}, {d_out, ntok * Dv * e},
+                    {d_final_state, d_final_state ? nstate : 0}};
+    const R outs[] = {{dq_raw, ntok * Dk * e}, {dk_raw, ntok * Dk * e}, {dv, ntok * Dv * e},
+                      {d_gate, ntok * Dk * 4}, {d_beta_logit, ntok * 4},
+                      {d_initial_state, d_initial_state ? nstate : 0}, {workspace, ws_need}};
+    constexpr int NO = sizeof(outs) / sizeof(outs[0]);
+    for (const R& o : outs)
+        for (const R& i : in)
+            if (overlaps(o.p, o.n, i.p, i.n)) return KDA_ERR_ALIAS;
+    for (int x = 0; x < NO; ++x)
+        for (int y = x + 1; y < NO; ++y)
+            if (overlaps(outs[x].p, outs[x].n, outs[y].p, outs[y].n)) return KDA_ERR_ALIAS;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    std::unique_lock<std::mutex> lock(g_stage.mu, std::defer_lock);
+    Recorder rec{(flags & KDA_FLAG_STAGE_EVENTS) != 0, s};
+    if (rec.on) {
+        lock.lock();
+        if (stage_begin() != hipSuccess) return KDA_ERR_HIP;
+    }
+    if (T == 0)
+        return backward_enqueue(nullptr, nullptr, nullptr, nullptr, nullptr, initial_state, nullptr,
+                                d_final_state, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                d_initial_state, B, T, H, Dk, Dv, chunk, dtype, mode, workspace,
+                                rec, s);
+    unsigned char* w = static_cast<unsigned char*>(workspace);
+    void* qh = w + xo[0];
+    void* kh = w + xo[1];
+    float* al = reinterpret_cast<float*>(w + xo[2]);
+    float* be = reinterpret_cast<float*>(w + xo[3]);
+    void* dqh = w + xo[4];
+    void* dkh = w + xo[5];
+    const kda::ProArgs pa{q_raw, k_raw, gate, beta_logit, qh, kh, al, be, dqh, dkh, dq_raw, dk_raw,
+                          d_gate, d_beta_logit, ntok, pro->alpha_min,
+                          pro->alpha_max - pro->alpha_min, pro->beta_max, pro->eps,
+                          pro->normalize_q};
+    if (rec.mark("prologue_in") != hipSuccess) return KDA_ERR_HIP;
+    if (kda::launch_backward_prologue(false, io, Dk, pa, s) != hipSuccess) return KDA_ERR_HIP;
+    if (rec.done() != hipSuccess) return KDA_ERR_HIP;
+    st = backward_enqueue(qh, kh, v, al, be, initial_state, d_out, d_final_state, dqh, dkh, dv,
+                          d_gate, d_beta_logit, d_initial_state, B, T, H, Dk, Dv, chunk, dtype,
+                          mode, workspace, rec, s);
+    if (st != KDA_OK) return st;
+    if (rec.mark("prologue_out") != hipSuccess) return KDA_ERR_HIP;
+    if (kda::launch_backward_prologue(true, io, Dk, pa, s) != hipSuccess) return KDA_ERR_HIP;
+    return rec.done() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 }  // namespace
@@ -790,6 +917,35 @@ kda_status_t kda_chunk_backward(const void* q, const void* k, const void* v, con
     return chunk_backward(q, k, v, alpha, beta, initial_state, d_out, d_final_state, dq, dk, dv,
                           d_alpha, d_beta, d_initial_state, B, T, H, Dk, Dv, chunk, dtype, mode,
                           flags, workspace, workspace_bytes, stream);
+}
+
+kda_status_t kda_chunk_backward_prologue_workspace_size(int B, int T, int H, int Dk, int Dv,
+                                                        int chunk, kda_dtype_t dtype, size_t* bytes)
+{
+    if (!bytes) return KDA_ERR_NULL_POINTER;
+    const kda_status_t st = check_backward_shape(B, T, H, Dk, Dv, chunk, dtype);
+    if (st != KDA_OK) return st;
+    size_t xo[6];
+    *bytes = T == 0 ? 0
+                    : backward_prologue_layout(B, T, H, Dk, Dv, chunk,
+                                               dtype == KDA_DTYPE_F32 ? IoType::F32 : IoType::BF16, xo);
+    return KDA_OK;
+}
+
+kda_status_t kda_chunk_backward_prologue(const void* q_raw, const void* k_raw, const void* v,
+                                         const float* gate, const float* beta_logit,
+                                         const float* initial_state, const void* d_out,
+                                         const float* d_final_state, const kda_prologue_t* prologue,
+                                         void* dq_raw, void* dk_raw, void* dv, float* d_gate,
+                                         float* d_beta_logit, float* d_initial_state, int B, int T,
+                                         int H, int Dk, int Dv, int chunk, kda_dtype_t dtype,
+                                         kda_mode_t mode, unsigned flags, void* workspace,
+                                         size_t workspace_bytes, void* stream)
+{
+    return chunk_backward_prologue(q_raw, k_raw, v, gate, beta_logit, initial_state, d_out,
+                                   d_final_state, prologue, dq_raw, dk_raw, dv, d_gate, d_beta_logit,
+                                   d_initial_state, B, T, H, Dk, Dv, chunk, dtype, mode, flags,
+                                   workspace, workspace_bytes, stream);
 }
 
 kda_status_t kda_last_stage_times(float* ms, const char** names, int max, int* count)

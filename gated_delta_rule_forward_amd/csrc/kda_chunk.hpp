@@ -199,6 +199,30 @@ struct PrepArgs {
     float* Tm;
 };
 
+// sum over the NQ consecutive lanes of a group (every lane receives the sum)
+template <int NQ>
+__device__ __forceinline__ float quad_group_sum(float x)
+{
+#pragma unroll
+    for (int off = NQ / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, NQ);
+    return x;
+}
+
+// x / (|x|_2 + eps) for one token whose Dk channels are spread as quads over NQ
+// consecutive lanes (a zero vector stays zero)
+template <typename T, int NQ>
+__device__ __forceinline__ Vec4<T> l2_normalised(const Vec4<T>& v, float eps)
+{
+    float f[4], ss = 0.f;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) { f[x] = v.get(x); ss += f[x] * f[x]; }
+    const float nrm = __builtin_sqrtf(quad_group_sum<NQ>(ss)) + eps;
+    const float inv = nrm > 0.f ? 1.f / nrm : 0.f;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) f[x] *= inv;
+    return Vec4<T>::from(f);
+}
+
 // logistic function in fp32 (exp2 of the scaled argument; saturates to 0 / 1)
 __device__ __forceinline__ float sigmoid_f32(float x)
 {
@@ -279,6 +303,30 @@ struct BwdLocalArgs {
     float* dbeta;
     uint8_t* FLB;
     int T, H, Dv, NC;
+};
+
+// The input prologue around the backward: raw q, k (io type), gate and beta
+// logits (fp32) -> qh, kh (io type), al, be (fp32), and afterwards the raw
+// gradients dq_raw, dk_raw (io type) from dqh, dkh, with dgate / dblogit
+// (holding d alpha / d beta on entry) turned into the logits' gradients.
+struct ProArgs {
+    const void* q_raw;
+    const void* k_raw;
+    const float* gate;
+    const float* blogit;
+    void* qh;
+    void* kh;
+    float* al;
+    float* be;
+    const void* dqh;
+    const void* dkh;
+    void* dq_raw;
+    void* dk_raw;
+    float* dgate;
+    float* dblogit;
+    size_t ntok;
+    float amin, arange, bmax, eps;
+    int normq;
 };
 
 // Where one unit (one chunk of one sequence and head) lives.  Dense batches:

@@ -73,6 +73,10 @@ hipError_t launch_decode(IoType io, int B, int H, int Dk, int Dv, const void* q,
 
 struct BwdChainArgs;
 struct BwdLocalArgs;
+struct ProArgs;
+// the input prologue before the backward (out = false) and the raw-input
+// gradients after it (out = true)
+hipError_t launch_backward_prologue(bool out, IoType io, int Dk, const ProArgs& a, hipStream_t stream);
 // backward stages: 0 relayout, 1 reverse chain, 2 per-chunk gradients,
 // 3 small-gate dalpha (kda_chunk.hpp describes the arguments)
 hipError_t launch_backward_stage(int stage, IoType io, const ChunkShape& s, const ChunkWorkspace& ws,

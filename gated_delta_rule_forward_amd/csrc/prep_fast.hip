@@ -100,30 +100,6 @@ __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(
 __device__ __forceinline__ float flog2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float frcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// sum over the NQ consecutive lanes that hold one token's channel quads
-template <int NQ>
-__device__ __forceinline__ float quad_group_sum(float x)
-{
-#pragma unroll
-    for (int off = NQ / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, NQ);
-    return x;
-}
-
-// x / (|x|_2 + eps) for one token whose Dk channels are spread as quads over NQ
-// consecutive lanes (a zero vector stays zero)
-template <typename T, int NQ>
-__device__ __forceinline__ Vec4<T> l2_normalised(const Vec4<T>& v, float eps)
-{
-    float f[4], ss = 0.f;
-#pragma unroll
-    for (int x = 0; x < 4; ++x) { f[x] = v.get(x); ss += f[x] * f[x]; }
-    const float nrm = __builtin_sqrtf(quad_group_sum<NQ>(ss)) + eps;
-    const float inv = nrm > 0.f ? 1.f / nrm : 0.f;
-#pragma unroll
-    for (int x = 0; x < 4; ++x) f[x] *= inv;
-    return Vec4<T>::from(f);
-}
-
 // ZS: the chunk may hold zero gates, placed in extra contraction columns (the
 // launch passes ZS = true exactly when extra columns are allotted); without
 // them a zero gate makes a part product vanish and flags the chunk.

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 6
+#define KDA_ABI_VERSION 7
 
 typedef enum {
     KDA_OK = 0,
@@ -303,6 +303,36 @@ kda_status_t kda_chunk_backward(const void* q, const void* k, const void* v,
                                 int B, int T, int H, int Dk, int Dv, int chunk,
                                 kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of kda_chunk_forward_prologue: the same loss gradients with respect
+ * to the raw inputs q_raw, k_raw, v, the gate logits (`gate`, alpha's layout),
+ * the beta logits ([B,T,H]) and initial_state, through the stable
+ * parameterisation of "Semidirect Fourier Delta Attention" §3 (eqs. (15),
+ * (17), (18); `prologue` as for the forward).  The transformed inputs are
+ * formed first (as the forward forms them), the backward runs on them, and
+ * the chain rule through the parameterisation maps the gradients back:
+ *   d gate = d alpha (alpha_max - alpha_min) s (1 - s),  d beta_logit = d beta
+ *   beta_max s (1 - s) (s the logistic of the logit), d k_raw = d k / (n + eps)
+ *   - k_raw <k_raw, d k> / (n (n + eps)^2) with n = |k_raw| (q_raw likewise
+ *   when normalize_q, else d q_raw = d q).
+ * Outputs dq_raw, dk_raw, dv in dtype; d_gate, d_beta_logit, d_initial_state
+ * fp32 (d_initial_state may be NULL).  Shapes, alignment (gate, dq_raw,
+ * dk_raw and d_gate 16-byte aligned too), aliasing and status rules as for
+ * kda_chunk_backward; the workspace is at least
+ * kda_chunk_backward_prologue_workspace_size bytes.
+ */
+kda_status_t kda_chunk_backward_prologue_workspace_size(int B, int T, int H, int Dk, int Dv,
+                                                        int chunk, kda_dtype_t dtype, size_t* bytes);
+kda_status_t kda_chunk_backward_prologue(const void* q_raw, const void* k_raw, const void* v,
+                                         const float* gate, const float* beta_logit,
+                                         const float* initial_state, const void* d_out,
+                                         const float* d_final_state, const kda_prologue_t* prologue,
+                                         void* dq_raw, void* dk_raw, void* dv, float* d_gate,
+                                         float* d_beta_logit, float* d_initial_state,
+                                         int B, int T, int H, int Dk, int Dv, int chunk,
+                                         kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
+                                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Chunk-local gate summary (log-magnitude, sign and zero form of the

@@ -35,13 +35,14 @@ def test_exports_every_declared_symbol(lib):
     assert {"kda_chunk_forward", "kda_chunk_forward_states", "kda_chunk_forward_prologue",
             "kda_chunk_forward_phase", "kda_decode_step_phase", "kda_chunk_forward_varlen", "kda_decode_step", "kda_chunk_forward_workspace_size",
             "kda_chunk_backward", "kda_chunk_backward_workspace_size",
+            "kda_chunk_backward_prologue", "kda_chunk_backward_prologue_workspace_size",
             "kda_gate_prep", "kda_status_string", "kda_abi_version"} <= set(syms)
     for s in syms:
         assert hasattr(lib, s), s
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 6
+    assert lib.kda_abi_version() == 7
     for s in range(8):
         assert lib.kda_status_string(s)
     assert lib.kda_status_string(99) == b"unknown status"
@@ -305,3 +306,31 @@ def test_backward_validation(lib):
     opt = list(base)
     opt[5] = opt[7] = opt[13] = None                              # S0, dST, dS0 optional
     assert bw(ptrs=opt, T=0) == OK                                # nothing to do, no HIP call
+
+
+def test_backward_prologue_validation(lib):
+    f = Fake()
+    n = ctypes.c_size_t(0)
+    assert lib.kda_chunk_backward_prologue_workspace_size(1, 64, 2, 64, 64, 64, F32, ctypes.byref(n)) == OK
+    need = n.value
+    m = ctypes.c_size_t(0)
+    lib.kda_chunk_backward_workspace_size(1, 64, 2, 64, 64, 64, F32, ctypes.byref(m))
+    assert need > m.value                       # the transformed inputs and their gradients
+
+    def bw(ptrs=None, pro=kda.Prologue(-1.0, 1.0, 2.0, 1e-6, 1), mode=1, T=64):
+        p = ptrs if ptrs is not None else [f() for _ in range(14)]
+        return lib.kda_chunk_backward_prologue(*p[:8], ctypes.byref(pro) if pro else None, *p[8:],
+                                               1, T, 2, 64, 64, 64, F32, mode, 0, f(need + 4096),
+                                               need, None)
+
+    base = [f() for _ in range(14)]
+    assert bw(pro=None) == NULLP
+    assert bw(pro=kda.Prologue(-1.0, 1.0, 2.0, 1e-6, 1), mode=0) == UNSUP   # CKDA range in KDA mode
+    assert bw(pro=kda.Prologue(0.5, 0.2, 1.0, 0.0, 1), mode=1) == UNSUP      # alpha_min > alpha_max
+    assert bw(ptrs=[None] + base[1:]) == NULLP
+    mis = list(base)
+    mis[3] = ctypes.c_void_p(base[3].value + 4)                               # gate: 16-byte rule
+    assert bw(ptrs=mis) == MISAL
+    al = list(base)
+    al[11] = base[3]                                                          # d_gate == gate
+    assert bw(ptrs=al) == ALIAS

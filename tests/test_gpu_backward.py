@@ -185,3 +185,44 @@ def test_backward_dk_ne_dv(name, base, ov, dv):
     say("  " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
     for k, v in errs.items():
         assert v <= TOL[w.dtype], (k, v)
+
+
+# ---- backward from raw inputs (kda_chunk_backward_prologue) ---------------------
+PRO_CASES = [
+    ("f32_ckda_d64_c64_T150", 1, dict(B=1, H=2, T=150, D=64, chunk=64, s0_std=0.5),
+     dict(alpha_min=-1.0, alpha_max=1.0, beta_max=2.0, eps=1e-6, normalize_q=True)),
+    ("f32_kda_d32_c32_T70_noqnorm", 0, dict(B=2, H=1, T=70, D=32, chunk=32),
+     dict(alpha_min=0.0, alpha_max=1.0, beta_max=1.0, eps=0.25, normalize_q=False)),
+    ("bf16_ckda_d128_c64_T200", 3, dict(B=1, H=2, T=200, chunk=64),
+     dict(alpha_min=-1.0, alpha_max=1.0, beta_max=2.0, eps=1e-6, normalize_q=True)),
+    ("bf16_kda_d64_c64_T129", 2, dict(B=1, H=2, T=129, D=64, chunk=64, s0_std=0.3),
+     dict(alpha_min=0.2, alpha_max=0.99, beta_max=1.0, eps=0.0, normalize_q=True)),
+]
+
+
+@pytest.mark.parametrize("name,base,ov,pro", PRO_CASES, ids=[c[0] for c in PRO_CASES])
+def test_backward_prologue_matches_oracle(name, base, ov, pro):
+    w = workloads.workload(base, **ov)
+    raw = workloads.make_prefill_raw(w)
+    dO, dST = workloads.make_backward_seeds(w)
+    say(f"[backward prologue] {name}: {pro}")
+    s0 = None if raw["S0"] is None else np32(raw["S0"])
+    ref = oracle.backward_prologue(np32(raw["q"]), np32(raw["k"]), np32(raw["v"]), np32(raw["gate"]),
+                                   np32(raw["beta_logit"]), np32(dO), s0, np32(dST),
+                                   nthreads=oracle_threads(), **pro)
+    d = {k: (None if v is None else v.to(DEV)) for k, v in raw.items()}
+    g = kda.chunk_backward_prologue(d["q"], d["k"], d["v"], d["gate"], d["beta_logit"], dO.to(DEV),
+                                    d["S0"], dST.to(DEV), chunk=w.chunk, mode=w.mode, **pro)
+    torch.cuda.synchronize()
+    pairs = (("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("d_gate", "dgate"),
+             ("d_beta_logit", "dbeta_logit"))
+    errs = {}
+    for gn, rn in pairs:
+        a_, b_ = np32(g[gn]), ref[rn]
+        if a_.ndim == 3:
+            a_, b_ = a_[..., None], b_[..., None]
+        errs[gn] = slice_err_out(a_, b_)
+    errs["d_initial_state"] = slice_err_state(np32(g["d_initial_state"]), ref["dS0"])
+    say("  " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= TOL[w.dtype], (k, v)
