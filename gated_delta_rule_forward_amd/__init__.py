@@ -96,6 +96,11 @@ def load():
     lib.kda_chunk_backward_prologue.argtypes = [vp] * 8 + [ctypes.POINTER(Prologue)] + [vp] * 6 + \
         [i] * 8 + [u, vp, sz, vp]
     lib.kda_chunk_backward_prologue.restype = i
+    lib.kda_chunk_backward_varlen_workspace_size.argtypes = [i, i, i, i, i, i, i,
+                                                             ctypes.POINTER(sz)]
+    lib.kda_chunk_backward_varlen_workspace_size.restype = i
+    lib.kda_chunk_backward_varlen.argtypes = [vp] * 6 + [i] + [vp] * 9 + [i] * 7 + [u, vp, sz, vp]
+    lib.kda_chunk_backward_varlen.restype = i
     lib.kda_gate_prep.argtypes = [vp] * 4 + [i] * 5 + [vp]
     lib.kda_gate_prep.restype = i
     lib.kda_last_stage_times.argtypes = [ctypes.POINTER(ctypes.c_float),
@@ -411,6 +416,49 @@ def chunk_backward_prologue(q_raw, k_raw, v, gate, beta_logit, d_out, initial_st
         B, T, H, Dk, Dv, chunk, _DT[q_raw.dtype], mode, flags, _ptr(workspace), wsb,
         _stream(stream))
     _check("kda_chunk_backward_prologue", st)
+    return g
+
+
+def chunk_backward_varlen(q, k, v, alpha, beta, cu_seqlens, d_out, initial_state=None,
+                          d_final_state=None, *, chunk: int = 64, mode: int = CKDA,
+                          want_d_initial_state: bool = True, workspace=None, stream=None,
+                          flags: int = 0):
+    """Backward of chunk_forward_varlen (kda_chunk_backward_varlen): layouts as
+    chunk_forward_varlen, d_out like v, d_final_state [N,H,Dk,Dv] fp32 or None.
+    Returns a dict dq, dk, dv (q's dtype, q's / v's shape), d_alpha, d_beta
+    (fp32) and d_initial_state ([N,H,Dk,Dv] fp32; None unless wanted)."""
+    lib = load()
+    H, Dk = q.shape[-2], q.shape[-1]
+    total_T = q.shape[-3]
+    Dv = v.shape[-1]
+    N = cu_seqlens.numel() - 1
+    if cu_seqlens.dtype != torch.int32 or N < 1:
+        raise ValueError("cu_seqlens must be an int32 tensor of N + 1 offsets, N >= 1")
+    dev = q.device
+    g = {"dq": torch.empty(q.shape, dtype=q.dtype, device=dev),
+         "dk": torch.empty(k.shape, dtype=q.dtype, device=dev),
+         "dv": torch.empty(v.shape, dtype=q.dtype, device=dev),
+         "d_alpha": torch.empty(alpha.shape, dtype=torch.float32, device=dev),
+         "d_beta": torch.empty(beta.shape, dtype=torch.float32, device=dev),
+         "d_initial_state": (torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev)
+                             if want_d_initial_state else None)}
+    if workspace is None:
+        n = ctypes.c_size_t(0)
+        _check("kda_chunk_backward_varlen_workspace_size",
+               lib.kda_chunk_backward_varlen_workspace_size(N, total_T, H, Dk, Dv, chunk,
+                                                             _DT[q.dtype], ctypes.byref(n)))
+        workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=dev)
+    _dev(q, k, v, alpha, beta, cu_seqlens, d_out, initial_state, d_final_state, workspace,
+         *g.values())
+    if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype or d_out.dtype != q.dtype:
+        raise ValueError("q, k, v and d_out must share one dtype (float32 or bfloat16)")
+    st = lib.kda_chunk_backward_varlen(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(cu_seqlens), N,
+        _ptr(initial_state), _ptr(d_out), _ptr(d_final_state), _ptr(g["dq"]), _ptr(g["dk"]),
+        _ptr(g["dv"]), _ptr(g["d_alpha"]), _ptr(g["d_beta"]), _ptr(g["d_initial_state"]),
+        total_T, H, Dk, Dv, chunk, _DT[q.dtype], mode, flags, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("kda_chunk_backward_varlen", st)
     return g
 
 

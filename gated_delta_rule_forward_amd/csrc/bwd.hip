@@ -173,17 +173,37 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
     // global stores are 16-byte and coalesced
     __shared__ __attribute__((aligned(16))) float sOut[(DK + C) * 16];
 
-    const int Dv = a.Dv, H = a.H, NS = Dv / 16, NC = a.NC;
+    const int Dv = a.Dv, H = a.H, NS = Dv / 16;
     const int gid = blockIdx.x, xcd = gid % kXcds, jx = gid / kXcds;
     const int bh = (jx / NS) * kXcds + xcd, slice = jx % NS;
     if (bh >= a.B * H) return;
-    const int b = bh / H, h = bh % H;
+    const int h = bh % H;
     const int tid = threadIdx.x, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = slice * 16 + ln;
     const T* dO = static_cast<const T*>(a.dO);
     // the dO piece this thread stages: row tid / 4, columns 4 (tid % 4) .. + 3
     const int drow = tid >> 2, dcol = 4 * (tid & 3);
+    // this (sequence, head): chunk count, first token row, length, first unit
+    const SeqPos sp = locate_seq(bh, H, a.T, a.NC, a.cu, a.cs);
+    const int NCs = sp.nc;
+    if (NCs == 0) {
+        // an empty sequence of a packed batch: dS0 = dST
+        if (a.dS0 && wave < 4) {
+#pragma unroll
+            for (int u = 0; u < G::SPW; ++u) {
+                const int t = wave + 4 * u;
+                if (t < G::NT) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const size_t e = ((size_t)bh * DK + 16 * t + 4 * lg + i) * Dv + col;
+                        a.dS0[e] = a.dST ? a.dST[e] : 0.f;
+                    }
+                }
+            }
+        }
+        return;
+    }
 
     f32x4 dS[G::SPW];
 #pragma unroll
@@ -202,7 +222,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
         Vec4<T> dov;                     // this thread's staged dO piece
     };
     auto load_ops = [&](Ops& o, int n) {
-        const size_t unit = (size_t)bh * NC + n;
+        const size_t unit = sp.ubase + n;
         const int mt = wave < G::NM ? wave : G::NM - 1;
         const T* pt = static_cast<const T*>(a.PT) + unit * C * C + (size_t)mt * G::NKC * 64 * G::NV;
         const T* kt = static_cast<const T*>(a.Ktil) + unit * C * DK + (size_t)mt * G::NKD * 64 * G::NV;
@@ -222,13 +242,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
             }
             o.gc[u] = *reinterpret_cast<const f32x4*>(a.GC + unit * DK + 16 * t + 4 * lg);
         }
-        // rows past the end (and threads past the chunk) read row T - 1, zeroed when staged
-        const int row = min(n * C + min(drow, C - 1), a.T - 1);
-        o.dov = Vec4<T>::load(dO + (((size_t)b * a.T + row) * H + h) * Dv + slice * 16 + dcol);
+        // rows past the end (and threads past the chunk) read the sequence's
+        // last row, zeroed when staged
+        const int row = min(n * C + min(drow, C - 1), sp.len - 1);
+        o.dov = Vec4<T>::load(dO + (((size_t)sp.row0 + row) * H + h) * Dv + slice * 16 + dcol);
     };
     auto stage_do = [&](const Ops& o, int n) {
         if (drow < C) {
-            const bool ok = n * C + drow < a.T;
+            const bool ok = n * C + drow < sp.len;
 #pragma unroll
             for (int x = 0; x < 4; ++x) sDOt[n & 1][dcol + x][drow] = ok ? o.dov.elem(x) : from_f32<T>(0.f);
         }
@@ -265,7 +286,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
     unsigned pf = 0;
     uint4 pfv[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
     auto prefetch = [&](int n) {
-        const size_t unit = (size_t)bh * NC + n;
+        const size_t unit = sp.ubase + n;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int q = wave + 4 * i;
@@ -291,7 +312,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
     // next chunk's dO piece (in nx, loaded during this step) is staged before
     // the step's second barrier
     auto step = [&](const Ops& o, int n, const Ops* nx) {
-        const size_t unit = (size_t)bh * NC + n;
+        const size_t unit = sp.ubase + n;
         consume();
         if (n >= 3) prefetch(n - 3);
         // the gradient of the state leaving chunk n (rows 0 .. DK-1 of sOut)
@@ -356,10 +377,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
 
     // two operand sets used in turn (no register copies between steps)
     Ops A, B;
-    load_ops(A, NC - 1);
-    stage_do(A, NC - 1);
+    load_ops(A, NCs - 1);
+    stage_do(A, NCs - 1);
     __syncthreads();
-    for (int n = NC - 1; n >= 0; n -= 2) {
+    for (int n = NCs - 1; n >= 0; n -= 2) {
         if (n >= 1) load_ops(B, n - 1);
         step(A, n, n >= 1 ? &B : nullptr);
         if (n < 1) break;
@@ -445,12 +466,16 @@ __global__ __launch_bounds__(kLocalThreads) void bwd_local_kernel(BwdLocalArgs a
     float* sDBv = reinterpret_cast<float*>(lds + G::DBV);     // [waves][C]: v . y partials
     constexpr int LDV = G::LDV, LDT = G::LDT, NM = G::NM, NW = kLocalWaves, NTH = kLocalThreads;
 
-    const int Dv = a.Dv, H = a.H, NC = a.NC, NVT = Dv / 16;
+    const int Dv = a.Dv, H = a.H, NVT = Dv / 16;
     const size_t unit = blockIdx.x;
-    const int bh = (int)(unit / NC), n = (int)(unit % NC);
-    const int b = bh / H, h = bh % H;
-    const int nvalid = min(C, a.T - n * C);
-    const size_t row0 = (size_t)b * a.T + (size_t)n * C;       // first token row
+    const UnitPos up = locate_unit((int)unit, H, a.T, a.NC, C, a.cu, a.cs, a.N);
+    if (!up.valid) {                  // past the last sequence of a packed batch
+        if (threadIdx.x == 0) a.FLB[unit] = 0;
+        return;
+    }
+    const int h = up.h;
+    const int nvalid = up.nvalid;
+    const size_t row0 = (size_t)up.row0;                        // first token row
     const int tid = threadIdx.x, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     auto tok = [&](int r) { return (row0 + r) * H + h; };       // token index of local row r
@@ -1007,11 +1032,12 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_tiny_kernel(BwdLocalArgs a)
     float* sE = reinterpret_cast<float*>(lds + L::E);
     int* sList = reinterpret_cast<int*>(lds + L::LIST);
     int* sCnt = reinterpret_cast<int*>(lds + L::CNT);
-    const int Dv = a.Dv, H = a.H, NC = a.NC;
-    const int bh = (int)(unit / NC), n = (int)(unit % NC);
-    const int b = bh / H, h = bh % H;
-    const int nvalid = min(C, a.T - n * C);
-    const size_t row0 = (size_t)b * a.T + (size_t)n * C;
+    const int Dv = a.Dv, H = a.H;
+    const UnitPos up = locate_unit((int)unit, H, a.T, a.NC, C, a.cu, a.cs, a.N);
+    if (!up.valid) return;
+    const int h = up.h;
+    const int nvalid = up.nvalid;
+    const size_t row0 = (size_t)up.row0;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     auto tok = [&](int r) { return (row0 + r) * H + h; };

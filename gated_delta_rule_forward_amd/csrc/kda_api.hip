@@ -380,12 +380,12 @@ kda_status_t decode_step(const void* q, const void* k, const void* v, const floa
 // chunk states [NU][Dk][Dv], Delta [NU][C][Dv], the state gradients
 // [NU][Dk][Dv], X / y [NU][C][Dv] (all fp32) and the small-gate flags [NU]
 constexpr int kBwdRegions = 6;
-size_t backward_layout(int B, int T, int H, int Dk, int Dv, int chunk, IoType io,
-                       size_t off[kda::kWorkspaceRegions], size_t boff[kBwdRegions])
+size_t backward_layout_sh(const ChunkShape& sh, IoType io, size_t off[kda::kWorkspaceRegions],
+                          size_t boff[kBwdRegions])
 {
-    const ChunkShape sh = make_shape(B, T, H, Dk, Dv, chunk);
+    const size_t chunk = sh.C, Dk = sh.Dk, Dv = sh.Dv;
     size_t n = kda::chunk_workspace_layout(sh, io, off);
-    const size_t nu = (size_t)B * H * sh.NC;
+    const size_t nu = (size_t)sh.B * sh.H * sh.NC;
     const size_t sz[kBwdRegions] = {nu * chunk * chunk * 4, nu * Dk * Dv * 4, nu * chunk * Dv * 4,
                                     nu * Dk * Dv * 4, nu * chunk * Dv * 4, nu};
     for (int i = 0; i < kBwdRegions; ++i) {
@@ -395,12 +395,31 @@ size_t backward_layout(int B, int T, int H, int Dk, int Dv, int chunk, IoType io
     return n;
 }
 
+size_t backward_layout(int B, int T, int H, int Dk, int Dv, int chunk, IoType io,
+                       size_t off[kda::kWorkspaceRegions], size_t boff[kBwdRegions])
+{
+    return backward_layout_sh(make_shape(B, T, H, Dk, Dv, chunk), io, off, boff);
+}
+
+// packed batches: the per-unit regions for the chunk-count bound, then the
+// sanitised tables (cu_s, cs: 2 (N + 1) ints)
+size_t backward_varlen_layout(int N, int total_T, int H, int Dk, int Dv, int chunk, IoType io,
+                              size_t off[kda::kWorkspaceRegions], size_t boff[kBwdRegions],
+                              size_t* table_off)
+{
+    const int umax = (int)varlen_max_chunks(N, total_T, chunk);
+    const size_t n = backward_layout_sh(ChunkShape{1, total_T, H, Dk, Dv, chunk, umax}, io, off, boff);
+    *table_off = n;
+    return n + ((2 * ((size_t)N + 1) * sizeof(int) + 255) & ~size_t(255));
+}
+
 kda_status_t backward_enqueue(const void* q, const void* k, const void* v, const float* alpha,
                               const float* beta, const float* initial_state, const void* d_out,
                               const float* d_final_state, void* dq, void* dk, void* dv,
                               float* d_alpha, float* d_beta, float* d_initial_state, int B, int T,
                               int H, int Dk, int Dv, int chunk, kda_dtype_t dtype, kda_mode_t mode,
-                              void* workspace, Recorder& rec, hipStream_t s);
+                              void* workspace, Recorder& rec, hipStream_t s,
+                              const int* cu_seqlens = nullptr);
 
 kda_status_t check_backward_shape(int B, int T, int H, int Dk, int Dv, int chunk,
                                   kda_dtype_t dtype)
@@ -471,13 +490,14 @@ kda_status_t chunk_backward(const void* q, const void* k, const void* v, const f
 }
 
 // the backward's launches (arguments validated by the caller, stage events
-// through rec)
+// through rec); with cu_seqlens (device, B + 1 offsets) the batch is packed:
+// B sequences over T tokens in total
 kda_status_t backward_enqueue(const void* q, const void* k, const void* v, const float* alpha,
                               const float* beta, const float* initial_state, const void* d_out,
                               const float* d_final_state, void* dq, void* dk, void* dv,
                               float* d_alpha, float* d_beta, float* d_initial_state, int B, int T,
                               int H, int Dk, int Dv, int chunk, kda_dtype_t dtype, kda_mode_t mode,
-                              void* workspace, Recorder& rec, hipStream_t s)
+                              void* workspace, Recorder& rec, hipStream_t s, const int* cu_seqlens)
 {
     const size_t nstate = (size_t)B * H * Dk * Dv * 4;
     if (T == 0) {
@@ -493,11 +513,30 @@ kda_status_t backward_enqueue(const void* q, const void* k, const void* v, const
         return rec.done() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
     }
 
-    const ChunkShape sh = make_shape(B, T, H, Dk, Dv, chunk);
     const IoType io = dtype == KDA_DTYPE_F32 ? IoType::F32 : IoType::BF16;
     size_t off[kda::kWorkspaceRegions], boff[kBwdRegions];
-    backward_layout(B, T, H, Dk, Dv, chunk, io, off, boff);
     unsigned char* w = static_cast<unsigned char*>(workspace);
+    // dense: units and chains from (B, T); packed: all units of the chunk-count
+    // bound (shp) and B x H chains (shc), located through the tables
+    ChunkShape shp = make_shape(B, T, H, Dk, Dv, chunk), shc = shp;
+    int* cu_s = nullptr;
+    int* cs = nullptr;
+    if (cu_seqlens) {
+        size_t toff = 0;
+        backward_varlen_layout(B, T, H, Dk, Dv, chunk, io, off, boff, &toff);
+        const int umax = (int)varlen_max_chunks(B, T, chunk);
+        shp = ChunkShape{1, T, H, Dk, Dv, chunk, umax};
+        shc = ChunkShape{B, T, H, Dk, Dv, chunk, umax};
+        cu_s = reinterpret_cast<int*>(w + toff);
+        cs = cu_s + (B + 1);
+        if (rec.mark("varlen_table") != hipSuccess) return KDA_ERR_HIP;
+        if (kda::launch_varlen_table(cu_seqlens, B, T, chunk, umax, cu_s, cs, s) != hipSuccess)
+            return KDA_ERR_HIP;
+        if (rec.done() != hipSuccess) return KDA_ERR_HIP;
+    } else {
+        backward_layout(B, T, H, Dk, Dv, chunk, io, off, boff);
+    }
+    const ChunkShape& sh = shp;
     const ChunkWorkspace ws{w + off[0], w + off[1], w + off[2],
                             w + off[3], w + off[4], reinterpret_cast<float*>(w + off[5]),
                             w + off[6]};
@@ -514,17 +553,18 @@ kda_status_t backward_enqueue(const void* q, const void* k, const void* v, const
     }
     kda::PrepArgs pa{q, k, v, alpha, beta, ws.W, ws.U, ws.Kt, ws.QG, ws.P, ws.GC, ws.FL,
                      T, H, Dv, sh.NC, zx, 0, 0.f, 0.f, 0.f, 0.f, 0,
-                     nullptr, nullptr, 0, nullptr};
+                     cu_s, cs, cu_seqlens ? B : 0, nullptr};
     pa.Tm = Tm;
     kda::ChainArgs ca{ws.W, ws.U, ws.Kt, ws.QG, ws.P, ws.GC, initial_state, nullptr,
-                      nullptr, nullptr, B, T, H, Dv, sh.NC, nullptr, nullptr,
+                      nullptr, nullptr, B, T, H, Dv, sh.NC, cu_s, cs,
                       0, sh.NC, 1, nullptr, nullptr};
     ca.CS32 = CS32;
     ca.DL = DL;
     const kda::BwdChainArgs ra{ws.Kt, ws.P, ws.QG, ws.W, ws.GC, d_out, d_final_state,
-                               d_initial_state, DSN, XB, B, T, H, Dv, sh.NC};
+                               d_initial_state, DSN, XB, B, T, H, Dv, sh.NC, cu_s, cs};
     const kda::BwdLocalArgs la{q, k, v, alpha, beta, d_out, Tm, CS32, DL, DSN, XB,
-                               dq, dk, dv, d_alpha, d_beta, FLB, T, H, Dv, sh.NC};
+                               dq, dk, dv, d_alpha, d_beta, FLB, T, H, Dv, sh.NC,
+                               cu_s, cs, cu_seqlens ? B : 0};
 
     if (rec.mark("prep_fast") != hipSuccess) return KDA_ERR_HIP;
     if (kda::launch_prep_fast(io, sh, pa, s) != hipSuccess) return KDA_ERR_HIP;
@@ -533,12 +573,13 @@ kda_status_t backward_enqueue(const void* q, const void* k, const void* v, const
     if (kda::launch_prep_exact(io, sh, pa, s) != hipSuccess) return KDA_ERR_HIP;
     if (rec.done() != hipSuccess) return KDA_ERR_HIP;
     if (rec.mark("chain_states") != hipSuccess) return KDA_ERR_HIP;
-    if (kda::launch_chain(io, sh, ca, s) != hipSuccess) return KDA_ERR_HIP;
+    if (kda::launch_chain(io, shc, ca, s) != hipSuccess) return KDA_ERR_HIP;
     if (rec.done() != hipSuccess) return KDA_ERR_HIP;
     static const char* const names[4] = {"relayout", "chain_reverse", "chunk_grads", "small_gates"};
     for (int stage = 0; stage < 4; ++stage) {
         if (rec.mark(names[stage]) != hipSuccess) return KDA_ERR_HIP;
-        if (kda::launch_backward_stage(stage, io, sh, ws, ra, la, s) != hipSuccess) return KDA_ERR_HIP;
+        if (kda::launch_backward_stage(stage, io, stage == 1 ? shc : shp, ws, ra, la, s) != hipSuccess)
+            return KDA_ERR_HIP;
         if (rec.done() != hipSuccess) return KDA_ERR_HIP;
     }
     return KDA_OK;
@@ -647,6 +688,73 @@ kda_status_t chunk_backward_prologue(const void* q_raw, const void* k_raw, const
     if (rec.mark("prologue_out") != hipSuccess) return KDA_ERR_HIP;
     if (kda::launch_backward_prologue(true, io, Dk, pa, s) != hipSuccess) return KDA_ERR_HIP;
     return rec.done() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+// the backward of a packed batch (kda_chunk_backward_varlen)
+kda_status_t chunk_backward_varlen(const void* q, const void* k, const void* v, const float* alpha,
+                                   const float* beta, const int* cu_seqlens, int N,
+                                   const float* initial_state, const void* d_out,
+                                   const float* d_final_state, void* dq, void* dk, void* dv,
+                                   float* d_alpha, float* d_beta, float* d_initial_state,
+                                   int total_T, int H, int Dk, int Dv, int chunk,
+                                   kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
+                                   void* workspace, size_t workspace_bytes, void* stream)
+{
+    kda_status_t st = check_varlen_shape(N, total_T, H, Dk, Dv, chunk, dtype);
+    if (st != KDA_OK) return st;
+    st = check_backward_shape(1, total_T, H, Dk, Dv, chunk, dtype);
+    if (st != KDA_OK) return st;
+    if (mode != KDA_MODE_KDA && mode != KDA_MODE_CKDA) return KDA_ERR_UNSUPPORTED;
+    if (flags & ~KDA_FLAG_STAGE_EVENTS) return KDA_ERR_UNSUPPORTED;
+    if (!cu_seqlens) return KDA_ERR_NULL_POINTER;
+    if (total_T > 0 && (!q || !k || !v || !alpha || !beta || !d_out || !dq || !dk || !dv ||
+                        !d_alpha || !d_beta))
+        return KDA_ERR_NULL_POINTER;
+    const IoType io = dtype == KDA_DTYPE_F32 ? IoType::F32 : IoType::BF16;
+    size_t off[kda::kWorkspaceRegions], boff[kBwdRegions], toff = 0;
+    const size_t ws_need =
+        total_T == 0 ? 0 : backward_varlen_layout(N, total_T, H, Dk, Dv, chunk, io, off, boff, &toff);
+    if (total_T > 0 && !workspace) return KDA_ERR_NULL_POINTER;
+    if (workspace_bytes < ws_need) return KDA_ERR_WORKSPACE_TOO_SMALL;
+
+    const size_t e = elem_size(dtype);
+    const size_t ntok = (size_t)total_T * H;
+    const size_t nstate = (size_t)N * H * Dk * Dv * 4;
+    const void* vec[] = {q, k, d_out, alpha, workspace};
+    for (const void* p : vec)
+        if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
+    const void* elt[] = {v, beta, initial_state, d_final_state, dq, dk, dv, d_alpha, d_beta,
+                         d_initial_state, cu_seqlens};
+    const uintptr_t ea[] = {e, 4, 4, 4, e, e, e, 4, 4, 4, 4};
+    for (int i = 0; i < 11; ++i)
+        if (elt[i] && !aligned(elt[i], ea[i])) return KDA_ERR_MISALIGNED;
+    struct R { const void* p; size_t n; };
+    const R in[] = {{q, ntok * Dk * e}, {k, ntok * Dk * e}, {v, ntok * Dv * e},
+                    {alpha, ntok * Dk * 4}, {beta, ntok * 4},
+                    {initial_state, initial_state ? nstate : 0}, {d_out, ntok * Dv * e},
+                    {d_final_state, d_final_state ? nstate : 0},
+                    {cu_seqlens, ((size_t)N + 1) * 4}};
+    const R outs[] = {{dq, ntok * Dk * e}, {dk, ntok * Dk * e}, {dv, ntok * Dv * e},
+                      {d_alpha, ntok * Dk * 4}, {d_beta, ntok * 4},
+                      {d_initial_state, d_initial_state ? nstate : 0}, {workspace, ws_need}};
+    constexpr int NO = sizeof(outs) / sizeof(outs[0]);
+    for (const R& o : outs)
+        for (const R& i : in)
+            if (overlaps(o.p, o.n, i.p, i.n)) return KDA_ERR_ALIAS;
+    for (int x = 0; x < NO; ++x)
+        for (int y = x + 1; y < NO; ++y)
+            if (overlaps(outs[x].p, outs[x].n, outs[y].p, outs[y].n)) return KDA_ERR_ALIAS;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    std::unique_lock<std::mutex> lock(g_stage.mu, std::defer_lock);
+    Recorder rec{(flags & KDA_FLAG_STAGE_EVENTS) != 0, s};
+    if (rec.on) {
+        lock.lock();
+        if (stage_begin() != hipSuccess) return KDA_ERR_HIP;
+    }
+    return backward_enqueue(q, k, v, alpha, beta, initial_state, d_out, d_final_state, dq, dk, dv,
+                            d_alpha, d_beta, d_initial_state, N, total_T, H, Dk, Dv, chunk, dtype,
+                            mode, workspace, rec, s, total_T > 0 ? cu_seqlens : nullptr);
 }
 
 }  // namespace
@@ -946,6 +1054,38 @@ kda_status_t kda_chunk_backward_prologue(const void* q_raw, const void* k_raw, c
                                    d_final_state, prologue, dq_raw, dk_raw, dv, d_gate, d_beta_logit,
                                    d_initial_state, B, T, H, Dk, Dv, chunk, dtype, mode, flags,
                                    workspace, workspace_bytes, stream);
+}
+
+kda_status_t kda_chunk_backward_varlen_workspace_size(int N, int total_T, int H, int Dk, int Dv,
+                                                      int chunk, kda_dtype_t dtype, size_t* bytes)
+{
+    if (!bytes) return KDA_ERR_NULL_POINTER;
+    kda_status_t st = check_varlen_shape(N, total_T, H, Dk, Dv, chunk, dtype);
+    if (st != KDA_OK) return st;
+    st = check_backward_shape(1, total_T, H, Dk, Dv, chunk, dtype);
+    if (st != KDA_OK) return st;
+    size_t off[kda::kWorkspaceRegions], boff[kBwdRegions], toff;
+    *bytes = total_T == 0 ? 0
+                          : backward_varlen_layout(N, total_T, H, Dk, Dv, chunk,
+                                                   dtype == KDA_DTYPE_F32 ? IoType::F32 : IoType::BF16,
+                                                   off, boff, &toff);
+    return KDA_OK;
+}
+
+kda_status_t kda_chunk_backward_varlen(const void* q, const void* k, const void* v,
+                                       const float* alpha, const float* beta,
+                                       const int* cu_seqlens, int N, const float* initial_state,
+                                       const void* d_out, const float* d_final_state, void* dq,
+                                       void* dk, void* dv, float* d_alpha, float* d_beta,
+                                       float* d_initial_state, int total_T, int H, int Dk, int Dv,
+                                       int chunk, kda_dtype_t dtype, kda_mode_t mode,
+                                       unsigned flags, void* workspace, size_t workspace_bytes,
+                                       void* stream)
+{
+    return chunk_backward_varlen(q, k, v, alpha, beta, cu_seqlens, N, initial_state, d_out,
+                                 d_final_state, dq, dk, dv, d_alpha, d_beta, d_initial_state,
+                                 total_T, H, Dk, Dv, chunk, dtype, mode, flags, workspace,
+                                 workspace_bytes, stream);
 }
 
 kda_status_t kda_last_stage_times(float* ms, const char** names, int max, int* count)

@@ -279,6 +279,8 @@ struct BwdChainArgs {
     float* DSN;
     float* XB;
     int B, T, H, Dv, NC;
+    const int* cu;     // packed batches (B = number of sequences): see PrepArgs
+    const int* cs;
 };
 // The per-chunk gradient kernels: inputs, Tinv (Tm), the fp32 chunk states
 // (CS32), Delta (DL), DSN and XB (replaced by y in flagged units); outputs
@@ -303,6 +305,9 @@ struct BwdLocalArgs {
     float* dbeta;
     uint8_t* FLB;
     int T, H, Dv, NC;
+    const int* cu;     // packed batches: see PrepArgs (null for dense)
+    const int* cs;
+    int N;
 };
 
 // The input prologue around the backward: raw q, k (io type), gate and beta

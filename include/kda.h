@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 7
+#define KDA_ABI_VERSION 8
 
 typedef enum {
     KDA_OK = 0,
@@ -333,6 +333,29 @@ kda_status_t kda_chunk_backward_prologue(const void* q_raw, const void* k_raw, c
                                          int B, int T, int H, int Dk, int Dv, int chunk,
                                          kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
                                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of kda_chunk_forward_varlen (packed batch of N sequences, device
+ * cu_seqlens [N + 1], the same sanitising rules as the forward): the gradients
+ * of sum_t <o_t, d_out_t> + sum_i <S_T,i, d_final_state_i> with respect to q,
+ * k, v, alpha, beta ([total_T, H, .] as for the forward) and the per-sequence
+ * initial states ([N, H, Dk, Dv]; NULL = zero).  d_final_state and
+ * d_initial_state are [N, H, Dk, Dv] fp32 or NULL; an empty sequence has
+ * d_initial_state = d_final_state.  Shape support, alignment, aliasing and
+ * status rules as for kda_chunk_backward (cu_seqlens 4-byte aligned); the
+ * workspace is at least kda_chunk_backward_varlen_workspace_size bytes.
+ */
+kda_status_t kda_chunk_backward_varlen_workspace_size(int N, int total_T, int H, int Dk, int Dv,
+                                                      int chunk, kda_dtype_t dtype, size_t* bytes);
+kda_status_t kda_chunk_backward_varlen(const void* q, const void* k, const void* v,
+                                       const float* alpha, const float* beta,
+                                       const int* cu_seqlens, int N, const float* initial_state,
+                                       const void* d_out, const float* d_final_state, void* dq,
+                                       void* dk, void* dv, float* d_alpha, float* d_beta,
+                                       float* d_initial_state, int total_T, int H, int Dk, int Dv,
+                                       int chunk, kda_dtype_t dtype, kda_mode_t mode,
+                                       unsigned flags, void* workspace, size_t workspace_bytes,
+                                       void* stream);
 
 /*
  * Chunk-local gate summary (log-magnitude, sign and zero form of the

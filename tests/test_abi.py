@@ -36,13 +36,14 @@ def test_exports_every_declared_symbol(lib):
             "kda_chunk_forward_phase", "kda_decode_step_phase", "kda_chunk_forward_varlen", "kda_decode_step", "kda_chunk_forward_workspace_size",
             "kda_chunk_backward", "kda_chunk_backward_workspace_size",
             "kda_chunk_backward_prologue", "kda_chunk_backward_prologue_workspace_size",
+            "kda_chunk_backward_varlen", "kda_chunk_backward_varlen_workspace_size",
             "kda_gate_prep", "kda_status_string", "kda_abi_version"} <= set(syms)
     for s in syms:
         assert hasattr(lib, s), s
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 7
+    assert lib.kda_abi_version() == 8
     for s in range(8):
         assert lib.kda_status_string(s)
     assert lib.kda_status_string(99) == b"unknown status"
@@ -333,4 +334,31 @@ def test_backward_prologue_validation(lib):
     assert bw(ptrs=mis) == MISAL
     al = list(base)
     al[11] = base[3]                                                          # d_gate == gate
+    assert bw(ptrs=al) == ALIAS
+
+
+def test_backward_varlen_validation(lib):
+    f = Fake()
+    n = ctypes.c_size_t(0)
+    assert lib.kda_chunk_backward_varlen_workspace_size(3, 200, 2, 64, 64, 64, F32, ctypes.byref(n)) == OK
+    need = n.value
+    m = ctypes.c_size_t(0)
+    lib.kda_chunk_backward_workspace_size(1, 200, 2, 64, 64, 64, F32, ctypes.byref(m))
+    assert need > m.value                       # one more chunk per sequence, plus the tables
+    assert lib.kda_chunk_backward_varlen_workspace_size(0, 200, 2, 64, 64, 64, F32, ctypes.byref(n)) == SHAPE
+    assert lib.kda_chunk_backward_varlen_workspace_size(3, 200, 2, 64, 64, 16, F32, ctypes.byref(n)) == UNSUP
+
+    def bw(ptrs=None, N=3, total=200):
+        p = ptrs if ptrs is not None else [f() for _ in range(15)]
+        return lib.kda_chunk_backward_varlen(*p[:6], N, *p[6:], total, 2, 64, 64, 64, F32, 1, 0,
+                                             f(need + 4096), need, None)
+
+    base = [f() for _ in range(15)]
+    assert bw(ptrs=base[:5] + [None] + base[6:]) == NULLP             # cu_seqlens
+    assert bw(ptrs=[None] + base[1:]) == NULLP                         # q
+    mis = list(base)
+    mis[5] = ctypes.c_void_p(base[5].value + 2)                        # cu_seqlens: 4-byte rule
+    assert bw(ptrs=mis) == MISAL
+    al = list(base)
+    al[9] = base[5]                                                    # dq == cu_seqlens
     assert bw(ptrs=al) == ALIAS

@@ -226,3 +226,69 @@ def test_backward_prologue_matches_oracle(name, base, ov, pro):
     say("  " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
     for k, v in errs.items():
         assert v <= TOL[w.dtype], (k, v)
+
+
+# ---- packed batches (kda_chunk_backward_varlen) ---------------------------------
+VL_CASES = [
+    ("f32_ckda_d64_c64", 1, dict(H=2, D=64, chunk=64, s0_std=0.5), [70, 0, 1, 130, 64]),
+    ("bf16_ckda_d128_c64", 3, dict(H=2, chunk=64), [200, 33, 0, 64]),
+    ("bf16_kda_d64_c32", 2, dict(H=1, D=64, chunk=32, s0_std=0.3), [5, 97, 32]),
+]
+
+
+@pytest.mark.parametrize("name,base,ov,lengths", VL_CASES, ids=[c[0] for c in VL_CASES])
+def test_backward_varlen_matches_oracle(name, base, ov, lengths):
+    """Every sequence of the packed batch against the oracle's gradients of
+    that sequence alone (its own initial state and final-state gradient)."""
+    w = workloads.workload(base, **ov)
+    inp = workloads.make_varlen(w, lengths)
+    N, total = len(lengths), sum(lengths)
+    gen = torch.Generator().manual_seed(77)
+    dO = torch.randn((1, total, w.H, w.D), generator=gen).to(w.dtype)
+    dST = torch.randn((N, w.H, w.D, w.D), generator=gen)
+    say(f"[backward varlen] {name}: lengths {lengths}")
+    d = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
+    g = kda.chunk_backward_varlen(d["q"][0], d["k"][0], d["v"][0], d["alpha"][0], d["beta"][0],
+                                  d["cu_seqlens"], dO[0].to(DEV), d["S0"], dST.to(DEV),
+                                  chunk=w.chunk, mode=w.mode)
+    torch.cuda.synchronize()
+    cu = inp["cu_seqlens"].tolist()
+    worst = {}
+    for i, L in enumerate(lengths):
+        sl = slice(cu[i], cu[i + 1])
+        sub = {x: inp[x][:, sl] for x in ("q", "k", "v", "alpha", "beta")}
+        sub["S0"] = None if inp["S0"] is None else inp["S0"][i:i + 1]
+        ref = _oracle(sub, dO[:, sl], dST[i:i + 1])
+        e = {"d_initial_state": slice_err_state(np32(g["d_initial_state"][i:i + 1]), ref["dS0"])}
+        if L > 0:
+            for gn, rn in GRADS:
+                a_, b_ = np32(g[gn][sl])[None], ref[rn]
+                if a_.ndim == 3:
+                    a_, b_ = a_[..., None], b_[..., None]
+                e[gn] = slice_err_out(a_, b_)
+        for k_, v_ in e.items():
+            worst[k_] = max(worst.get(k_, 0.0), v_)
+    say("  " + " ".join(f"{k} {v:.2e}" for k, v in worst.items()))
+    for k_, v_ in worst.items():
+        assert v_ <= TOL[w.dtype], (k_, v_)
+
+
+def test_backward_varlen_uniform_equals_dense():
+    """Equal lengths: the packed batch numbers its chunks like the dense batch,
+    so every gradient is bit-identical to kda_chunk_backward's."""
+    w = workloads.workload(2, B=3, H=2, T=100, chunk=64, s0_std=0.2)
+    say(f"[backward varlen] uniform vs dense {w}")
+    inp = workloads.make_prefill(w)
+    dO, dST = workloads.make_backward_seeds(w)
+    d = {k: (None if v is None else v.to(DEV)) for k, v in inp.items()}
+    gd = kda.chunk_backward(d["q"], d["k"], d["v"], d["alpha"], d["beta"], dO.to(DEV), d["S0"],
+                            dST.to(DEV), chunk=64, mode=w.mode)
+    flat = lambda t: t.reshape(w.B * w.T, *t.shape[2:]).contiguous()
+    cu = torch.arange(0, (w.B + 1) * w.T, w.T, dtype=torch.int32, device=DEV)
+    gv = kda.chunk_backward_varlen(flat(d["q"]), flat(d["k"]), flat(d["v"]), flat(d["alpha"]),
+                                   flat(d["beta"]), cu, flat(dO.to(DEV)), d["S0"], dST.to(DEV),
+                                   chunk=64, mode=w.mode)
+    torch.cuda.synchronize()
+    for gn in ("dq", "dk", "dv", "d_alpha", "d_beta"):
+        assert torch.equal(flat(gd[gn]), gv[gn]), gn
+    assert torch.equal(gd["d_initial_state"], gv["d_initial_state"])
