@@ -35,6 +35,9 @@
 //   bwd_chain_kernel   the reverse chain, one workgroup per (b, h, 16 columns)
 //   bwd_local_kernel   every chunk's gradients, one workgroup per chunk
 //   bwd_tiny_kernel    the direct dalpha of small gates, flagged chunks only
+// Packed batches locate chunks and sequences through the forward's tables.
+// With raw inputs, prologue_in_kernel forms the transformed inputs first and
+// prologue_out_kernel maps the gradients back (eqs. (15), (17), (18)).
 #include <type_traits>
 
 #include "kda_chunk.hpp"
@@ -682,7 +685,7 @@ __global__ __launch_bounds__(kLocalThreads) void bwd_local_kernel(BwdLocalArgs a
     }
     __syncthreads();
 
-    // ---- weight phase: alpha, k, q, B1^T, B3^T ----------------------------------------
+    // ---- weight phase: alpha, k, q ----------------------------------------------------
     {
 #pragma unroll
         for (int x = 0; x < NA; ++x) {
