@@ -32,6 +32,12 @@ bool chunk_ok(int c) { return c == 16 || c == 32 || c == 64; }
 
 size_t elem_size(kda_dtype_t t) { return t == KDA_DTYPE_F32 ? 4 : 2; }
 
+// Extra zero-segment columns the fast prep kernel may take per chunk: none in
+// KDA mode (gates in (0, 1] have no zeros; a chunk that holds one goes to the
+// exact kernel), 4 Dk in CKDA mode (contracted Dk per pass, so at most four
+// extra passes); a chunk with more zero gates goes to the exact kernel.
+int fast_zero_columns(int mode, int Dk) { return mode == KDA_MODE_CKDA ? 4 * Dk : 0; }
+
 // [p, p + n) and [q, q + m) intersect (n, m in bytes; empty ranges never do)
 bool overlaps(const void* p, size_t n, const void* q, size_t m)
 {
@@ -243,14 +249,7 @@ kda_status_t chunk_forward(const void* q, const void* k, const void* v, const fl
     const ChunkWorkspace ws{w + off[0], w + off[1], w + off[2],
                             w + off[3], w + off[4], reinterpret_cast<float*>(w + off[5]),
                             w + off[6]};
-    // Extra zero-segment columns of the fast prep kernel: none in KDA mode
-    // (gates in (0, 1] have no zeros; a chunk that has one goes to the exact
-    // kernel), in CKDA mode as many as fit in 160 KB of LDS (at most 128).
-    int zx = 0;
-    if (mode == KDA_MODE_CKDA) {
-        zx = 128;
-        while (zx > 0 && kda::prep_fast_lds_bytes(io, chunk, Dk, zx) > 160 * 1024) zx -= 16;
-    }
+    const int zx = fast_zero_columns(mode, Dk);
     const kda::PrepArgs pa{q, k, v, alpha, beta, ws.W, ws.U, ws.Kt, ws.QG, ws.P, ws.GC, ws.FL,
                            T, H, Dv, sh.NC, zx,
                            pro ? 1 : 0,
@@ -546,11 +545,7 @@ kda_status_t backward_enqueue(const void* q, const void* k, const void* v, const
     float* DSN = reinterpret_cast<float*>(w + boff[3]);
     float* XB = reinterpret_cast<float*>(w + boff[4]);
     uint8_t* FLB = w + boff[5];
-    int zx = 0;
-    if (mode == KDA_MODE_CKDA) {
-        zx = 128;
-        while (zx > 0 && kda::prep_fast_lds_bytes(io, chunk, Dk, zx) > 160 * 1024) zx -= 16;
-    }
+    const int zx = fast_zero_columns(mode, Dk);
     kda::PrepArgs pa{q, k, v, alpha, beta, ws.W, ws.U, ws.Kt, ws.QG, ws.P, ws.GC, ws.FL,
                      T, H, Dv, sh.NC, zx, 0, 0.f, 0.f, 0.f, 0.f, 0,
                      cu_s, cs, cu_seqlens ? B : 0, nullptr};
@@ -929,11 +924,7 @@ kda_status_t kda_chunk_forward_varlen(const void* q, const void* k, const void* 
     const ChunkWorkspace ws{w + off[0], w + off[1], w + off[2],
                             w + off[3], w + off[4], reinterpret_cast<float*>(w + off[5]),
                             w + off[6]};
-    int zx = 0;
-    if (mode == KDA_MODE_CKDA) {
-        zx = 128;
-        while (zx > 0 && kda::prep_fast_lds_bytes(io, chunk, Dk, zx) > 160 * 1024) zx -= 16;
-    }
+    const int zx = fast_zero_columns(mode, Dk);
     const kda::PrepArgs pa{q, k, v, alpha, beta, ws.W, ws.U, ws.Kt, ws.QG, ws.P, ws.GC, ws.FL,
                            total_T, H, Dv, umax, zx,
                            prologue ? 1 : 0,

@@ -178,7 +178,8 @@ struct PrepArgs {
     float* GC;
     uint8_t* FL;
     int T, H, Dv, NC;
-    int zx;   // extra (zero-segment) columns available to the fast prep kernel
+    int zx;   // most zero gates per chunk the fast prep kernel takes (each one
+              // adds a contraction column; 0: a chunk with a zero gate is flagged)
     // input parameterisation ("Semidirect Fourier Delta Attention" §3, eqs.
     // (15), (17), (18)); when pro != 0, alpha holds gate logits, beta holds
     // beta logits and q, k are raw:  alpha = amin + arange * sigmoid(gate),

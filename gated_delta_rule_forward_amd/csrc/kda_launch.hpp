@@ -53,8 +53,9 @@ constexpr int kWorkspaceRegions = 7;
 // Byte offset of each workspace region and the total (regions 256-byte aligned).
 size_t chunk_workspace_layout(const ChunkShape& s, IoType io, size_t offsets[kWorkspaceRegions]);
 
-// LDS bytes the fast prep kernel needs with zx extra zero-segment columns.
-size_t prep_fast_lds_bytes(IoType io, int C, int Dk, int zx);
+// LDS bytes of one workgroup of the fast prep kernel (the same for any number
+// of zero-segment columns: those are contracted Dk columns per pass).
+size_t prep_fast_lds_bytes(IoType io, int C, int Dk);
 
 hipError_t launch_prep_fast(IoType io, const ChunkShape& s, const PrepArgs& a, hipStream_t stream);
 hipError_t launch_prep_exact(IoType io, const ChunkShape& s, const PrepArgs& a, hipStream_t stream);

@@ -20,10 +20,12 @@
 // segment of a channel becomes its own contraction column ("virtual channel":
 // segment 0 stays in column c, later segments get extra columns), so pairs
 // across a zero gate meet only zeros and stay exactly zero.  A and P are then
-// one MFMA product each over Dk + (#zeros) columns.  A chunk whose half span
-// max|L_r - M| exceeds 96 (factors could leave the normal range) or whose zero
-// count exceeds the extra columns is flagged for the exact kernel
-// (prep_exact.hip) instead.
+// one MFMA product each over Dk + (#zeros) columns, contracted Dk columns at a
+// time: the Dk main columns first, then the extra columns in passes of Dk
+// that reuse the same operand region, so the LDS size does not depend on the
+// zero count.  A chunk whose half span max|L_r - M| exceeds 96 (factors could
+// leave the normal range) or whose zero count exceeds the allowed extra
+// columns is flagged for the exact kernel (prep_exact.hip) instead.
 //
 // Tinv is a blocked inverse over 16x16 diagonal blocks (fp32 MFMA):
 //   T_aa = (I + A_aa)^{-1} by forward substitution,
@@ -70,17 +72,15 @@ struct FastGeom {
 
 template <typename T, int C, int DK>
 struct FastLayout {
-    int KS;                 // operand row stride (elements)
+    static constexpr int KS = DK + FastGeom<T, C, DK>::PADE;   // operand row stride (elements)
     size_t scr, total;
     // one region reused phase by phase (offsets from 0):
     //   gate summary: partL, partPZ [PARTS][DK] fp32 / int
-    //   A / P:        XA, XP, Y [C][KS] io type
+    //   A / P:        XA, XP, Y [C][KS] io type (one contraction pass of DK columns)
     //   Tinv:         A, Tinv [C][LDF] fp32
     //   W / U:        X_W^T [DK][XTS], (beta V)^T [DVMAX][XTS] io type
-    __host__ __device__ FastLayout(int zx) {
+    __host__ __device__ FastLayout() {
         using G = FastGeom<T, C, DK>;
-        const int kp_max = ((DK + zx + G::KB - 1) / G::KB) * G::KB;
-        KS = kp_max + G::PADE;
         const size_t e = sizeof(T);
         const size_t r1 = (size_t)2 * G::PARTS * DK * 4 + (size_t)G::PARTS * (DK / 2) * 4;
         const size_t r2 = 3 * (size_t)C * KS * e;
@@ -120,8 +120,8 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
     constexpr int NB = G::NB, LDF = G::LDF, XTS = G::XTS, TV = G::TV;
     constexpr int NKD = DK / KB, NKC = C / KB;
     const int Dv = args.Dv;
-    const FastLayout<T, C, DK> LY(args.zx);
-    const int KS = LY.KS;
+    const FastLayout<T, C, DK> LY;
+    constexpr int KS = FastLayout<T, C, DK>::KS;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     float* partL = reinterpret_cast<float*>(lds);                           // gate summary
     int* partPZ = reinterpret_cast<int*>(partL + PARTS * DK);               // nz << 1 | parity
@@ -359,16 +359,14 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
     }
 
     // ---- factored operands (LDS), Q*Gamma (staged), Ktil (direct) ---------------
-    const int KP = ((DK + Ztot + KB - 1) / KB) * KB;     // contraction length
-    if (KP > DK) {
-        const int ext = KP - DK;
-        for (int idx = tid; idx < 3 * C * ext; idx += kThreads) {
-            const int m = idx / (C * ext), rem = idx % (C * ext);
-            const int r = rem / ext, col = DK + rem % ext;
-            XA[m * C * KS + r * KS + col] = from_f32<T>(0.f);
-        }
-        __syncthreads();
-    }
+    // A operand beta k F, P operand q F, shared operand k G of token j, channel x
+    auto factors = [&](int j, int x, float& fa, float& fp, float& fy) {
+        const float kx = kv[j].get(x);
+        const float Fv = F0[x] * pr[j][x];
+        fa = bt[j] * kx * Fv;
+        fp = qv[j].get(x) * Fv;
+        fy = kx * (G0[x] * frcp(pr[j][x]));
+    };
     Vec4<T> xw[TOK];
     float kt[TOK][4];
 #pragma unroll
@@ -378,13 +376,7 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
         int segs[4];
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-            const float kx = kv[j].get(x), qx = qv[j].get(x);
-            const float Fv = F0[x] * pr[j][x];
-            const float Gv = G0[x] * frcp(pr[j][x]);
-            const float bk = bt[j] * kx;
-            fa[x] = bk * Fv;
-            fp[x] = qx * Fv;
-            fy[x] = kx * Gv;
+            factors(j, x, fa[x], fp[x], fy[x]);
             // Gamma_r = F_r E in the first zero segment; rho(C-1, r) = stot E G_r
             // in the last one (stot: sign of the whole chunk's product)
             const float stot = (totPZ[x] & 1) ? -1.f : 1.f;
@@ -403,25 +395,16 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
         xw[j] = Vec4<T>::from(fw);
         if (own) {
             *reinterpret_cast<Vec4<T>*>(QGg + frag_off<KB>(r, c0, DK)) = Vec4<T>::from(fq);
-            if (!ZS || Ztot == 0) {
-                *reinterpret_cast<Vec4<T>*>(XA + r * KS + c0) = Vec4<T>::from(fa);
-                *reinterpret_cast<Vec4<T>*>(XP + r * KS + c0) = Vec4<T>::from(fp);
-                *reinterpret_cast<Vec4<T>*>(Y + r * KS + c0) = Vec4<T>::from(fy);
-            } else {
+            // main columns hold zero segment 0 only; later segments wait for
+            // their extra-column pass
+            if constexpr (ZS) {
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const int c = c0 + x;
-                    const int col = segs[x] == 0 ? c : DK + sBase[c] + segs[x] - 1;
-                    XA[r * KS + col] = from_f32<T>(fa[x]);
-                    XP[r * KS + col] = from_f32<T>(fp[x]);
-                    Y[r * KS + col] = from_f32<T>(fy[x]);
-                    if (col != c) {
-                        XA[r * KS + c] = from_f32<T>(0.f);
-                        XP[r * KS + c] = from_f32<T>(0.f);
-                        Y[r * KS + c] = from_f32<T>(0.f);
-                    }
-                }
+                for (int x = 0; x < 4; ++x)
+                    if (segs[x] != 0) { fa[x] = 0.f; fp[x] = 0.f; fy[x] = 0.f; }
             }
+            *reinterpret_cast<Vec4<T>*>(XA + r * KS + c0) = Vec4<T>::from(fa);
+            *reinterpret_cast<Vec4<T>*>(XP + r * KS + c0) = Vec4<T>::from(fp);
+            *reinterpret_cast<Vec4<T>*>(Y + r * KS + c0) = Vec4<T>::from(fy);
         }
     }
     if (own) {
@@ -496,25 +479,62 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
     // registers until the operands are dead and the region becomes A, Tinv)
     static_assert(NB <= 4, "one row tile per wavefront");
     const int ta = wave;
-    f32x4 accA[NB];
+    f32x4 accA[NB], accP[NB];
 #pragma unroll
-    for (int tb = 0; tb < NB; ++tb) accA[tb] = zero4();
-    if (ta < NB) {
-        f32x4 accP[NB];
+    for (int tb = 0; tb < NB; ++tb) { accA[tb] = zero4(); accP[tb] = zero4(); }
+    // one pass: the first kw columns of the operand region
+    auto contract = [&](int kw) {
+        if (ta < NB) {
+            for (int k0 = 0; k0 < kw; k0 += KB) {
+                const F xa = frag_row<T, KB>(XA + (16 * ta + ln) * KS, k0);
+                const F xp = frag_row<T, KB>(XP + (16 * ta + ln) * KS, k0);
 #pragma unroll
-        for (int tb = 0; tb < NB; ++tb) accP[tb] = zero4();
-        for (int k0 = 0; k0 < KP; k0 += KB) {
-            const F xa = frag_row<T, KB>(XA + (16 * ta + ln) * KS, k0);
-            const F xp = frag_row<T, KB>(XP + (16 * ta + ln) * KS, k0);
-#pragma unroll
-            for (int tb = 0; tb < NB; ++tb) {
-                if (tb <= ta) {
-                    const F y = frag_row<T, KB>(Y + (16 * tb + ln) * KS, k0);
-                    accA[tb] = mma(xa, y, accA[tb]);    // A[16ta + 4g + i][16tb + n]
-                    accP[tb] = mma(y, xp, accP[tb]);    // P[16ta + n][16tb + 4g + i]
+                for (int tb = 0; tb < NB; ++tb) {
+                    if (tb <= ta) {
+                        const F y = frag_row<T, KB>(Y + (16 * tb + ln) * KS, k0);
+                        accA[tb] = mma(xa, y, accA[tb]);    // A[16ta + 4g + i][16tb + n]
+                        accP[tb] = mma(y, xp, accP[tb]);    // P[16ta + n][16tb + 4g + i]
+                    }
                 }
             }
         }
+    };
+    contract(DK);
+    if constexpr (ZS) {
+        // extra columns e = 0 .. Ztot-1, DK per pass: (channel c, segment s >= 1)
+        // is column e = sBase[c] + s - 1
+        for (int e0 = 0; e0 < Ztot; e0 += DK) {
+            __syncthreads();                              // previous pass read
+            constexpr int RV = DK * (int)sizeof(T) / 16;  // 16-byte runs per operand row
+            for (int idx = tid; idx < 3 * C * RV; idx += kThreads) {
+                const int row = idx / RV, run = idx % RV;
+                *reinterpret_cast<uint4*>(XA + row * KS + run * (16 / (int)sizeof(T))) =
+                    make_uint4(0u, 0u, 0u, 0u);
+            }
+            __syncthreads();
+            if (own) {
+#pragma unroll
+                for (int j = 0; j < TOK; ++j) {
+                    const int r = part * TOK + j;
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        const int seg = (offPZ[x] >> 1) + (int)((zc[j] >> (8 * x)) & 0xffu);
+                        const int col = sBase[c0 + x] + seg - 1 - e0;
+                        if (seg > 0 && col >= 0 && col < DK) {
+                            float fa, fp, fy;
+                            factors(j, x, fa, fp, fy);
+                            XA[r * KS + col] = from_f32<T>(fa);
+                            XP[r * KS + col] = from_f32<T>(fp);
+                            Y[r * KS + col] = from_f32<T>(fy);
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+            contract(min(DK, ((Ztot - e0 + KB - 1) / KB) * KB));
+        }
+    }
+    if (ta < NB) {
 #pragma unroll
         for (int s = 0; s < NKC; ++s) {
             float f[NV];
@@ -675,7 +695,7 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
 template <typename T, int C, int DK>
 hipError_t launch_fast_t(const ChunkShape& s, const PrepArgs& a, hipStream_t stream)
 {
-    const FastLayout<T, C, DK> LY(a.zx);
+    const FastLayout<T, C, DK> LY;
     // (the input parameterisation and the phase variant are not combined)
     auto kern = a.theta ? (a.zx > 0 ? prep_fast_kernel<T, C, DK, true, false, true>
                                     : prep_fast_kernel<T, C, DK, false, false, true>)
@@ -692,7 +712,7 @@ hipError_t launch_fast_t(const ChunkShape& s, const PrepArgs& a, hipStream_t str
 }
 
 template <typename T, int C, int DK>
-size_t fast_lds_t(int zx) { return FastLayout<T, C, DK>(zx).total; }
+size_t fast_lds_t() { return FastLayout<T, C, DK>().total; }
 
 template <typename T, int C>
 hipError_t dispatch_dk(const ChunkShape& s, const PrepArgs& a, hipStream_t st)
@@ -720,27 +740,27 @@ hipError_t dispatch_c(const ChunkShape& s, const PrepArgs& a, hipStream_t st)
 }
 
 template <typename T, int C>
-size_t lds_dk(int Dk, int zx)
+size_t lds_dk(int Dk)
 {
     switch (Dk) {
-    case 16: return fast_lds_t<T, C, 16>(zx);
-    case 32: return fast_lds_t<T, C, 32>(zx);
-    case 64: return fast_lds_t<T, C, 64>(zx);
-    default: return fast_lds_t<T, C, 128>(zx);
+    case 16: return fast_lds_t<T, C, 16>();
+    case 32: return fast_lds_t<T, C, 32>();
+    case 64: return fast_lds_t<T, C, 64>();
+    default: return fast_lds_t<T, C, 128>();
     }
 }
 
 }  // namespace
 
-size_t prep_fast_lds_bytes(IoType io, int C, int Dk, int zx)
+size_t prep_fast_lds_bytes(IoType io, int C, int Dk)
 {
     if (io == IoType::F32) {
         if (Dk > 64) return ~size_t(0);
-        return C == 16 ? lds_dk<float, 16>(Dk, zx) : C == 32 ? lds_dk<float, 32>(Dk, zx)
-                                                              : lds_dk<float, 64>(Dk, zx);
+        return C == 16 ? lds_dk<float, 16>(Dk) : C == 32 ? lds_dk<float, 32>(Dk)
+                                                          : lds_dk<float, 64>(Dk);
     }
-    return C == 16 ? lds_dk<bf16_t, 16>(Dk, zx) : C == 32 ? lds_dk<bf16_t, 32>(Dk, zx)
-                                                           : lds_dk<bf16_t, 64>(Dk, zx);
+    return C == 16 ? lds_dk<bf16_t, 16>(Dk) : C == 32 ? lds_dk<bf16_t, 32>(Dk)
+                                                       : lds_dk<bf16_t, 64>(Dk);
 }
 
 hipError_t launch_prep_fast(IoType io, const ChunkShape& s, const PrepArgs& a, hipStream_t stream)

@@ -586,3 +586,40 @@ def test_exact_fallback_chunks(dt):
         eo, es = slice_err_out(np32(out), o_ref), slice_err_state(np32(st), s_ref)
         say(f"  mode {mode}: err out {eo:.3e} state {es:.3e}")
         assert eo <= TOL[dt] and es <= TOL[dt]
+
+
+# zero-gate rate per head: about 1, 2, 3 and 4 extra contraction passes of the
+# fast prep kernel (Dk zero-segment columns each), then more zeros than the
+# CKDA column budget (4 Dk per chunk) so that chunk goes to the exact kernel
+DENSE_ZERO_RATES = (0.012, 0.024, 0.04, 0.056, 0.09)
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_forward_dense_zero_gates(dt):
+    """CKDA gates with many exact zeros: every later zero segment of a channel
+    is its own contraction column, contracted Dk columns per pass.  Heads with
+    rising zero rates take one to four extra passes or the exact kernel; one
+    more head puts a zero on every other token of channels 0 and Dk - 1
+    (32 segments in one channel) and at the first and last token of every
+    chunk.  Results must match the oracle."""
+    D = 64 if dt == torch.float32 else 128
+    H = len(DENSE_ZERO_RATES) + 1
+    w = workloads.workload(1, B=1, H=H, T=256 + 37, D=D, chunk=64, dtype=dt, s0_std=0.3)
+    say(f"[dense zeros] {dt} {w}")
+    inp = workloads.make_prefill(w)
+    a = inp["alpha"]
+    g = torch.Generator().manual_seed(77)
+    for h, rate in enumerate(DENSE_ZERO_RATES):
+        mask = torch.rand(a[:, :, h].shape, generator=g) < rate
+        a[:, :, h][mask] = 0.0
+    hz = H - 1
+    a[0, 1::2, hz, 0] = 0.0
+    a[0, ::2, hz, D - 1] = 0.0
+    a[0, ::64, hz, :] = 0.0
+    a[0, 63::64, hz, 5:9] = 0.0
+    o_ref, s_ref = run_oracle(inp)
+    d = to_dev(inp)
+    out, st = run_gpu(d, 64, workloads.CKDA)
+    eo, es = slice_err_out(np32(out), o_ref), slice_err_state(np32(st), s_ref)
+    say(f"  err out {eo:.3e} state {es:.3e}")
+    assert eo <= TOL[dt] and es <= TOL[dt]
