@@ -110,7 +110,10 @@ def time_forward(kda, torch, w, inp, steps, warmup, extra_flags=0):
     per = {}
     for _ in range(steps):
         call(kda.STAGE_EVENTS)
-        for name, t in kda.last_stage_times():
+        tot = {}
+        for name, t in kda.last_stage_times():      # a kernel may run once per part
+            tot[name] = tot.get(name, 0.0) + t
+        for name, t in tot.items():
             per.setdefault(name, []).append(t)
     torch.cuda.synchronize()
     per = {k: sum(v) / len(v) for k, v in per.items()}

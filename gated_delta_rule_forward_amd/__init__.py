@@ -21,12 +21,13 @@ __all__ = [
     "KDA", "CKDA", "KdaError", "library_path", "load", "abi_version", "workspace_size",
     "chunk_forward", "chunk_forward_prologue", "chunk_forward_varlen", "chunk_forward_phase",
     "decode_step", "decode_step_phase", "gate_prep", "last_stage_times",
-    "STAGE_EVENTS", "NO_SEGMENTS",
+    "STAGE_EVENTS", "NO_SEGMENTS", "SINGLE_STREAM",
 ]
 
 KDA, CKDA = 0, 1
 STAGE_EVENTS = 2
 NO_SEGMENTS = 4        # KDA_FLAG_NO_SEGMENTS
+SINGLE_STREAM = 8      # KDA_FLAG_SINGLE_STREAM
 _DT = {torch.float32: 0, torch.bfloat16: 1}
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkda.so")
@@ -478,10 +479,13 @@ def gate_prep(alpha, chunk: int, *, stream=None):
 
 
 def last_stage_times():
-    """[(kernel name, ms)] of the last call made with flags=STAGE_EVENTS."""
+    """[(kernel name, ms)] of the last call made with flags=STAGE_EVENTS, one
+    entry per kernel launch in launch order (a name repeats when a call
+    launches that kernel more than once)."""
     lib = load()
-    ms = (ctypes.c_float * 8)()
-    names = (ctypes.c_char_p * 8)()
+    cap = 32
+    ms = (ctypes.c_float * cap)()
+    names = (ctypes.c_char_p * cap)()
     n = ctypes.c_int(0)
-    _check("kda_last_stage_times", lib.kda_last_stage_times(ms, names, 8, ctypes.byref(n)))
-    return [(names[i].decode(), float(ms[i])) for i in range(min(n.value, 8))]
+    _check("kda_last_stage_times", lib.kda_last_stage_times(ms, names, cap, ctypes.byref(n)))
+    return [(names[i].decode(), float(ms[i])) for i in range(min(n.value, cap))]

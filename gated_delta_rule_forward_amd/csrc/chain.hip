@@ -260,8 +260,8 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
     // this (sequence, head): chunk count, first token row, length, first unit;
     // a segment is chunks [c0, c0 + NC) of it
     const SeqPos sp = locate_seq(bh, H, a.T, a.NC, a.cu, a.cs);
-    const int c0 = nseg > 1 ? sg * a.seg : 0;
-    const int NC = nseg > 1 ? min(a.seg, sp.nc - c0) : sp.nc;
+    const int c0 = nseg > 1 ? sg * a.seg : (a.pcn > 0 ? a.pc0 : 0);
+    const int NC = nseg > 1 ? min(a.seg, sp.nc - c0) : (a.pcn > 0 ? min(a.pcn, sp.nc - c0) : sp.nc);
     const int T_ = sp.len - c0 * C;
     const int tid = threadIdx.x, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

@@ -9,6 +9,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <map>
+#include <algorithm>
 #include <mutex>
 
 #include "../../include/kda.h"
@@ -21,7 +23,7 @@ using kda::ChunkShape;
 using kda::ChunkWorkspace;
 using kda::IoType;
 
-constexpr unsigned kKnownFlags = KDA_FLAG_STAGE_EVENTS | KDA_FLAG_NO_SEGMENTS;
+constexpr unsigned kKnownFlags = KDA_FLAG_STAGE_EVENTS | KDA_FLAG_NO_SEGMENTS | KDA_FLAG_SINGLE_STREAM;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 bool aligned16(const void* p) { return aligned(p, 16); }
@@ -49,7 +51,8 @@ bool overlaps(const void* p, size_t n, const void* q, size_t m)
 // ---- per-kernel events (opt-in) ---------------------------------------------
 // Stage i owns events 2i and 2i+1, attached to its kernel launch: the elapsed
 // time between them is that kernel's own duration.
-constexpr int kMaxStages = 12;
+constexpr int kMaxParts = 8;
+constexpr int kMaxStages = 3 * kMaxParts;
 struct StageEvents {
     std::mutex mu;
     hipEvent_t ev[2 * kMaxStages] = {};
@@ -134,10 +137,31 @@ Segments segments_for(int B, int H, int Dk, int Dv, int NC)
     return {(NC + seg - 1) / seg, seg};
 }
 
+// Prep / chain overlap for a dense forward whose chains leave half the GPU or
+// more idle: the chunks of every (b, h) are cut into `parts` consecutive
+// ranges of `len` chunks, and the prep kernels of range p + 1 run on a second
+// stream, on the idle compute units, while the chain runs range p.  Measured
+// (B=1, H=16, T=65536, d=128, CKDA bf16: 128 chains, 1024 chunks): 2.09 ms in
+// one pass, 1.87 ms in 8 parts.  With 256 chains (H=32, T=8192) the prep
+// slows the chain more than it saves (0.340 -> 0.375 ms in 2 parts), and
+// short chunk axes lose to the extra launches.  parts <= 1: one prep pass,
+// then one chain pass.
+struct Parts { int parts, len; };
+Parts parts_for(int B, int H, int Dk, int Dv, int NC)
+{
+    (void)Dk;
+    const long long chains = (long long)B * H * (Dv / 16);
+    if (chains > 128 || NC < 256) return {1, NC};
+    const int len = (NC + kMaxParts - 1) / kMaxParts;
+    return {(NC + len - 1) / len, len};
+}
+
 // workspace of a dense forward: the per-unit regions, then (with segments)
-// the segment maps [B H][nseg][Dk][Dk + Dv] and start states [B H][nseg][Dk][Dv]
+// the segment maps [B H][nseg][Dk][Dk + Dv] and start states [B H][nseg][Dk][Dv],
+// then (with parts) the state between parts [B H][Dk][Dv] fp32
 size_t dense_layout(int B, int T, int H, int Dk, int Dv, int chunk, IoType io,
-                    size_t off[kda::kWorkspaceRegions], size_t* summ_off, size_t* sseg_off)
+                    size_t off[kda::kWorkspaceRegions], size_t* summ_off, size_t* sseg_off,
+                    size_t* spart_off = nullptr)
 {
     const ChunkShape sh = make_shape(B, T, H, Dk, Dv, chunk);
     size_t n = kda::chunk_workspace_layout(sh, io, off);
@@ -150,7 +174,42 @@ size_t dense_layout(int B, int T, int H, int Dk, int Dv, int chunk, IoType io,
         *sseg_off = n;
         n += (bhs * Dk * Dv * 4 + 255) & ~size_t(255);
     }
+    if (spart_off) *spart_off = 0;
+    if (parts_for(B, H, Dk, Dv, sh.NC).parts > 1) {
+        if (spart_off) *spart_off = n;
+        n += ((size_t)B * H * Dk * Dv * 4 + 255) & ~size_t(255);
+    }
     return n;
+}
+
+// per device: the second stream of the prep / chain overlap and its events
+// (event 0: the caller's stream reached the call; event p + 1: prep of part p
+// done).  Created on first use, kept until the process ends; g_side_mu is
+// held while a call enqueues, so calls from several host threads do not
+// share events in flight.
+struct SideStream {
+    hipStream_t st = nullptr;
+    hipEvent_t ev[kMaxParts + 1] = {};
+};
+std::mutex g_side_mu;
+std::map<int, SideStream> g_side;
+
+hipError_t side_stream(SideStream** out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    SideStream& ss = g_side[dev];
+    if (!ss.st) {
+        for (int i = 0; i <= kMaxParts; ++i) {
+            if (!ss.ev[i]) e = hipEventCreateWithFlags(&ss.ev[i], hipEventDisableTiming);
+            if (e != hipSuccess) return e;
+        }
+        e = hipStreamCreateWithFlags(&ss.st, hipStreamNonBlocking);
+        if (e != hipSuccess) return e;
+    }
+    *out = &ss;
+    return hipSuccess;
 }
 
 // prologue parameters inside the mode's ranges (KDA: gates in [0, 1], beta in
@@ -261,16 +320,55 @@ kda_status_t chunk_forward(const void* q, const void* k, const void* v, const fl
                            nullptr, nullptr, 0, theta};
     const Segments sgm = (flags & KDA_FLAG_NO_SEGMENTS) ? Segments{1, sh.NC}
                                                           : segments_for(B, H, Dk, Dv, sh.NC);
-    size_t so = 0, ss = 0;
-    if (sgm.nseg > 1) {
+    const Parts prt = (sgm.nseg > 1 || (flags & KDA_FLAG_SINGLE_STREAM)) ? Parts{1, sh.NC}
+                                                                       : parts_for(B, H, Dk, Dv, sh.NC);
+    size_t so = 0, ss = 0, sp = 0;
+    if (sgm.nseg > 1 || prt.parts > 1) {
         size_t off2[kda::kWorkspaceRegions];
-        dense_layout(B, T, H, Dk, Dv, chunk, io, off2, &so, &ss);
+        dense_layout(B, T, H, Dk, Dv, chunk, io, off2, &so, &ss, &sp);
     }
     float* summ = sgm.nseg > 1 ? reinterpret_cast<float*>(w + so) : nullptr;
     float* sseg = sgm.nseg > 1 ? reinterpret_cast<float*>(w + ss) : nullptr;
     const kda::ChainArgs ca{ws.W, ws.U, ws.Kt, ws.QG, ws.P, ws.GC, initial_state, out,
                             final_state, chunk_states, B, T, H, Dv, sh.NC, nullptr, nullptr,
                             theta ? 1 : 0, sgm.seg, sgm.nseg, nullptr, sseg};
+
+    if (prt.parts > 1) {
+        // prep of every part on the side stream, chain of part p on the
+        // caller's stream after the prep of part p; the state between parts
+        // lives in the workspace (each chain workgroup reads its slice before
+        // writing it back)
+        float* spart = reinterpret_cast<float*>(w + sp);
+        std::lock_guard<std::mutex> side_lock(g_side_mu);
+        SideStream* side = nullptr;
+        if (side_stream(&side) != hipSuccess) return KDA_ERR_HIP;
+        if (hipEventRecord(side->ev[0], s) != hipSuccess) return KDA_ERR_HIP;
+        if (hipStreamWaitEvent(side->st, side->ev[0], 0) != hipSuccess) return KDA_ERR_HIP;
+        for (int p = 0; p < prt.parts; ++p) {
+            kda::PrepArgs pp = pa;
+            pp.pc0 = p * prt.len;
+            pp.pcn = std::min(prt.len, sh.NC - pp.pc0);
+            if (rec.mark("prep_fast") != hipSuccess) return KDA_ERR_HIP;
+            if (kda::launch_prep_fast(io, sh, pp, side->st) != hipSuccess) return KDA_ERR_HIP;
+            if (rec.done() != hipSuccess) return KDA_ERR_HIP;
+            if (rec.mark("prep_exact") != hipSuccess) return KDA_ERR_HIP;
+            if (kda::launch_prep_exact(io, sh, pp, side->st) != hipSuccess) return KDA_ERR_HIP;
+            if (rec.done() != hipSuccess) return KDA_ERR_HIP;
+            if (hipEventRecord(side->ev[p + 1], side->st) != hipSuccess) return KDA_ERR_HIP;
+        }
+        for (int p = 0; p < prt.parts; ++p) {
+            kda::ChainArgs cp = ca;
+            cp.pc0 = p * prt.len;
+            cp.pcn = std::min(prt.len, sh.NC - cp.pc0);
+            cp.S0 = p == 0 ? initial_state : spart;
+            cp.ST = p == prt.parts - 1 ? final_state : spart;
+            if (hipStreamWaitEvent(s, side->ev[p + 1], 0) != hipSuccess) return KDA_ERR_HIP;
+            if (rec.mark("chain") != hipSuccess) return KDA_ERR_HIP;
+            if (kda::launch_chain(io, sh, cp, s) != hipSuccess) return KDA_ERR_HIP;
+            if (rec.done() != hipSuccess) return KDA_ERR_HIP;
+        }
+        return KDA_OK;
+    }
 
     if (rec.mark("prep_fast") != hipSuccess) return KDA_ERR_HIP;
     if (kda::launch_prep_fast(io, sh, pa, s) != hipSuccess) return KDA_ERR_HIP;

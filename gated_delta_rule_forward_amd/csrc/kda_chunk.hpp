@@ -198,7 +198,17 @@ struct PrepArgs {
     // backward support: Tinv = (I + A)^{-1} of every unit, fp32 [NU][C][C]
     // row-major (zero above the diagonal), or null
     float* Tm;
+    // dense batches: pcn > 0 restricts a launch to chunks [pc0, pc0 + pcn) of
+    // every (b, h) (launch index v -> unit part_unit(v, ...)); 0: all units
+    int pc0, pcn;
 };
+
+// unit of launch index v when a launch covers chunks [pc0, pc0 + pcn) of every
+// (b, h) of a dense batch with NC chunks per (b, h); pcn = 0: v itself
+__host__ __device__ __forceinline__ int part_unit(int v, int pc0, int pcn, int NC)
+{
+    return pcn > 0 ? (v / pcn) * NC + pc0 + v % pcn : v;
+}
 
 // sum over the NQ consecutive lanes of a group (every lane receives the sum)
 template <int NQ>
@@ -260,6 +270,11 @@ struct ChainArgs {
     // be null when only these are wanted.
     float* CS32;
     float* DL;
+    // dense batches without segments: pcn > 0 runs chunks [pc0, pc0 + pcn) of
+    // every (b, h) only, from S0 (the state entering chunk pc0) to ST (the
+    // state leaving the range; may be S0: each workgroup reads its slice of S0
+    // before it writes that slice of ST)
+    int pc0, pcn;
 };
 
 // Backward (dense batches).  The reverse chain reads the forward's operands

@@ -96,7 +96,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_exact_kernel(PrepArgs args,
     if (tid == 0) sCount = 0;
     __syncthreads();
     if (base + tid < nper) {
-        const int u = (int)blockIdx.x + (base + tid) * (int)gridDim.x;
+        const int u = part_unit((int)blockIdx.x + (base + tid) * (int)gridDim.x,
+                                args.pc0, args.pcn, NC);
         if (args.FL[u] != 0) sList[atomicAdd(&sCount, 1)] = u;
     }
     __syncthreads();
@@ -398,7 +399,7 @@ hipError_t launch_exact_t(const ChunkShape& s, const PrepArgs& a, hipStream_t st
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              (int)L::TOTAL);
     if (e != hipSuccess) return e;
-    const int nu = (int)((size_t)s.B * s.H * s.NC);
+    const int nu = (int)((size_t)s.B * s.H * (a.pcn > 0 ? a.pcn : s.NC));
     const int grid = nu < 256 ? nu : 256;   // one workgroup per CU (LDS-bound)
     return launch_kernel(kern, dim3(grid), dim3(kPrepThreads), (uint32_t)L::TOTAL, stream, a, nu);
 }

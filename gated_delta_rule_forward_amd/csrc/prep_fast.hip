@@ -144,7 +144,7 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
     const int q4 = tid % G::NQ, part = own ? tid / G::NQ : PARTS - 1;
     const int c0 = 4 * q4;                                    // my channels c0 .. c0+3
     const int T_ = args.T, H = args.H, NC = args.NC;
-    const int unit = blockIdx.x;
+    const int unit = part_unit(blockIdx.x, args.pc0, args.pcn, NC);
     const UnitPos up = locate_unit(unit, H, T_, NC, C, args.cu, args.cs, args.N);
     if (!up.valid) {                  // past the last sequence of a packed batch
         if (tid == 0) args.FL[unit] = 0;
@@ -707,7 +707,7 @@ hipError_t launch_fast_t(const ChunkShape& s, const PrepArgs& a, hipStream_t str
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              (int)LY.total);
     if (e != hipSuccess) return e;
-    const unsigned nunits = (unsigned)((size_t)s.B * s.H * s.NC);
+    const unsigned nunits = (unsigned)((size_t)s.B * s.H * (a.pcn > 0 ? a.pcn : s.NC));
     return launch_kernel(kern, dim3(nunits), dim3(kThreads), (uint32_t)LY.total, stream, a);
 }
 

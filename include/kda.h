@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 8
+#define KDA_ABI_VERSION 9
 
 typedef enum {
     KDA_OK = 0,
@@ -81,6 +81,15 @@ typedef enum { KDA_MODE_KDA = 0, KDA_MODE_CKDA = 1 } kda_mode_t;
  * states are chained in fp32, and every segment then runs from its own start.
  * The results agree with the unsegmented path up to rounding. */
 #define KDA_FLAG_NO_SEGMENTS 4u
+/* flags: run every kernel on the caller's stream.  By default a dense forward
+ * whose chains would leave half the GPU or more idle (at most 128 of them, and
+ * no segments) and that has at least 256 chunks runs its chunks in consecutive
+ * parts: the per-chunk factors of part p + 1 are formed on a second stream of
+ * the library's own (one per device, default priority, kept until the
+ * process ends) while the chain runs part p on the caller's stream, joined
+ * by events, so the call still ends on the caller's stream.  The results are
+ * bitwise those of the single-stream path. */
+#define KDA_FLAG_SINGLE_STREAM 8u
 
 /* ABI version of the loaded library (KDA_ABI_VERSION it was built with). */
 int kda_abi_version(void);

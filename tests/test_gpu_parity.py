@@ -623,3 +623,58 @@ def test_forward_dense_zero_gates(dt):
     eo, es = slice_err_out(np32(out), o_ref), slice_err_state(np32(st), s_ref)
     say(f"  err out {eo:.3e} state {es:.3e}")
     assert eo <= TOL[dt] and es <= TOL[dt]
+
+
+# (name, base workload, overrides, flags) — at most 128 (b, h, 16-column)
+# chains and at least 256 chunks, so the forward runs in parts: chunk factors
+# of part p + 1 on the library's second stream while the chain runs part p
+PARTS = [
+    ("bf16_ckda_d128_c16_H9_T4133_s0", 3, dict(B=1, H=9, T=4133, chunk=16, s0_std=0.2), 0),
+    ("f32_kda_d32_c16_B2_T4100_nosegments", 0, dict(B=2, H=1, T=4100, D=32, chunk=16),
+     kda.NO_SEGMENTS),
+]
+
+
+@pytest.mark.parametrize("name,base,ov,flags", PARTS, ids=[c[0] for c in PARTS])
+def test_forward_parts(name, base, ov, flags):
+    """Prep / chain overlap in parts: the oracle's sequential recurrence, and
+    bitwise the single-stream path (KDA_FLAG_SINGLE_STREAM) for the outputs,
+    the final state and the chunk-start states; the stage list shows one
+    chain launch per part."""
+    w = workloads.workload(base, **ov)
+    say(f"[forward parts] {name}: {w}")
+    inp = workloads.make_prefill(w, device="cpu")
+    o_ref, s_ref = run_oracle(inp)
+    d = to_dev(inp)
+    out, st = run_gpu(d, w.chunk, w.mode, flags=flags | kda.STAGE_EVENTS)
+    names = _stage_names()
+    say(f"  stages {names}")
+    assert names.count("chain") == 8 and names.count("prep_fast") == 8
+    eo, es = slice_err_out(np32(out), o_ref), slice_err_state(np32(st), s_ref)
+    say(f"  err out {eo:.3e} state {es:.3e}")
+    assert eo <= TOL[w.dtype] and es <= TOL[w.dtype]
+    out1, st1 = run_gpu(d, w.chunk, w.mode, flags=flags | kda.SINGLE_STREAM | kda.STAGE_EVENTS)
+    assert _stage_names().count("chain") == 1
+    assert torch.equal(out, out1) and torch.equal(st, st1)
+    nc = (w.T + w.chunk - 1) // w.chunk
+    cs = [torch.full((w.B, w.H, nc, w.Dk, w.Dv), float("nan"), dtype=w.dtype, device=DEV)
+          for _ in range(2)]
+    for c, fl in zip(cs, (flags, flags | kda.SINGLE_STREAM)):
+        o2, s2 = run_gpu(d, w.chunk, w.mode, flags=fl, chunk_states=c)
+        assert torch.equal(o2, out) and torch.equal(s2, st)
+    assert torch.equal(cs[0], cs[1])
+
+
+def test_forward_prologue_parts_bitwise():
+    """The raw-input forward in parts equals its single-stream path bitwise."""
+    w = workloads.workload(3, B=1, H=9, T=4133, chunk=16, s0_std=0.2)
+    say(f"[forward prologue parts] {w}")
+    r = to_dev(workloads.make_prefill_raw(w, forget_frac=0.01))
+    res = []
+    for fl in (0, kda.SINGLE_STREAM):
+        res.append(kda.chunk_forward_prologue(r["q"], r["k"], r["v"], r["gate"], r["beta_logit"],
+                                              r["S0"], alpha_min=-1.0, alpha_max=1.0,
+                                              beta_max=2.0, chunk=w.chunk, mode=w.mode,
+                                              flags=fl))
+    torch.cuda.synchronize()
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
