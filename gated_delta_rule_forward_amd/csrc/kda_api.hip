@@ -194,13 +194,21 @@ struct SideStream {
 std::mutex g_side_mu;
 std::map<int, SideStream> g_side;
 
-hipError_t side_stream(SideStream** out)
+// The side stream of the current device in *out, created on first use; while
+// `caller` is being captured into a graph nothing is created (*out = null if
+// it does not exist yet: the call then keeps to the caller's stream).
+hipError_t side_stream(hipStream_t caller, SideStream** out)
 {
+    *out = nullptr;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     SideStream& ss = g_side[dev];
     if (!ss.st) {
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        e = hipStreamIsCapturing(caller, &cap);
+        if (e != hipSuccess) return e;
+        if (cap != hipStreamCaptureStatusNone) return hipSuccess;
         for (int i = 0; i <= kMaxParts; ++i) {
             if (!ss.ev[i]) e = hipEventCreateWithFlags(&ss.ev[i], hipEventDisableTiming);
             if (e != hipSuccess) return e;
@@ -333,15 +341,18 @@ kda_status_t chunk_forward(const void* q, const void* k, const void* v, const fl
                             final_state, chunk_states, B, T, H, Dv, sh.NC, nullptr, nullptr,
                             theta ? 1 : 0, sgm.seg, sgm.nseg, nullptr, sseg};
 
+    std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
+    SideStream* side = nullptr;
     if (prt.parts > 1) {
+        side_lock.lock();
+        if (side_stream(s, &side) != hipSuccess) return KDA_ERR_HIP;
+    }
+    if (side) {
         // prep of every part on the side stream, chain of part p on the
         // caller's stream after the prep of part p; the state between parts
         // lives in the workspace (each chain workgroup reads its slice before
         // writing it back)
         float* spart = reinterpret_cast<float*>(w + sp);
-        std::lock_guard<std::mutex> side_lock(g_side_mu);
-        SideStream* side = nullptr;
-        if (side_stream(&side) != hipSuccess) return KDA_ERR_HIP;
         if (hipEventRecord(side->ev[0], s) != hipSuccess) return KDA_ERR_HIP;
         if (hipStreamWaitEvent(side->st, side->ev[0], 0) != hipSuccess) return KDA_ERR_HIP;
         for (int p = 0; p < prt.parts; ++p) {

@@ -87,8 +87,11 @@ typedef enum { KDA_MODE_KDA = 0, KDA_MODE_CKDA = 1 } kda_mode_t;
  * parts: the per-chunk factors of part p + 1 are formed on a second stream of
  * the library's own (one per device, default priority, kept until the
  * process ends) while the chain runs part p on the caller's stream, joined
- * by events, so the call still ends on the caller's stream.  The results are
- * bitwise those of the single-stream path. */
+ * by events, so the call still ends on the caller's stream (a graph captured
+ * from the caller's stream takes in both; the second stream is never created
+ * during a capture, so a call captured before any uncaptured call of that
+ * shape on the device keeps to one stream).  The results are bitwise those
+ * of the single-stream path. */
 #define KDA_FLAG_SINGLE_STREAM 8u
 
 /* ABI version of the loaded library (KDA_ABI_VERSION it was built with). */

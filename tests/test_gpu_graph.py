@@ -1,0 +1,70 @@
+"""HIP graph capture of the chunked forward (through the C ABI): a call
+captured once from torch's capture stream and replayed several times, with
+the program's own eager work and synchronisations between the replays; every
+replay must equal the eager call bitwise.  Covers the single-pass launch
+sequence and the parts path, whose second stream the capture takes in through
+its events."""
+import pytest
+import torch
+
+import gated_delta_rule_forward_amd as kda
+import workloads
+from parity import say
+
+pytestmark = pytest.mark.gpu
+
+# (name, base workload, overrides, parts expected)
+GRAPH_CASES = [
+    ("bf16_kda_d128_c64_H4_T700", 2, dict(B=1, H=4, T=700), False),
+    ("bf16_ckda_d128_c16_H9_T4133_parts", 3, dict(B=1, H=9, T=4133, chunk=16, s0_std=0.2), True),
+]
+
+
+@pytest.mark.parametrize("name,base,ov,parts", GRAPH_CASES, ids=[c[0] for c in GRAPH_CASES])
+def test_forward_graph_replay(name, base, ov, parts):
+    w = workloads.workload(base, **ov)
+    say(f"[graph] {name}: {w}")
+    d = {k: (None if v is None else v.to("cuda")) for k, v in workloads.make_prefill(w).items()}
+    ws = torch.empty(kda.workspace_size(w.B, w.T, w.H, w.Dk, w.Dv, w.chunk, w.dtype),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.B, w.T, w.H, w.Dv), dtype=w.dtype, device="cuda")
+    st = torch.empty((w.B, w.H, w.Dk, w.Dv), dtype=torch.float32, device="cuda")
+
+    def call(o, s, flags=0):
+        kda.chunk_forward(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], chunk=w.chunk,
+                          mode=w.mode, out=o, final_state=s, workspace=ws, flags=flags)
+
+    # eager reference (also creates the side stream when the shape runs in parts)
+    call(out, st, kda.STAGE_EVENTS)
+    torch.cuda.synchronize()
+    names = [n for n, _ in kda.last_stage_times()]
+    say(f"  stages {names}")
+    assert names.count("chain") == (8 if parts else 1)
+    ref_out, ref_st = out.clone(), st.clone()
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(out, st)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(out, st)
+    torch.cuda.synchronize()
+
+    o2 = torch.empty_like(out)
+    s2 = torch.empty_like(st)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        st.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ok = torch.equal(out, ref_out) and torch.equal(st, ref_st)
+        say(f"  replay {rep}: bitwise {ok}")
+        assert ok
+        call(o2, s2)                         # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(o2, ref_out) and torch.equal(s2, ref_st)
