@@ -15,15 +15,18 @@
  *
  * Conventions shared by every entry point:
  *  - Every tensor pointer is a DEVICE pointer owned by the caller; the library
- *    never allocates, frees or synchronises (except where a flag says so) and
- *    never keeps a pointer after the call returns.
+ *    never allocates or frees memory, never synchronises (except where a flag
+ *    says so) and never keeps a pointer after the call returns.  It creates
+ *    one stream and a few events per device, on first use, for the parts
+ *    path of the chunked forward (KDA_FLAG_SINGLE_STREAM).
  *  - Layouts are row-major and contiguous:
  *      q, k, alpha : [B, T, H, Dk]     v, out : [B, T, H, Dv]    beta : [B, T, H]
  *      state       : [B, H, Dk, Dv]
  *    (decode uses the same layouts with T = 1).
  *  - q, k, v and out share `dtype`; alpha, beta and every state are fp32.
- *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
- *    is asynchronous: argument errors are reported synchronously, before any
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream),
+ *    part of it on the library's second stream where KDA_FLAG_SINGLE_STREAM
+ *    says so, joined back to `stream` by events, and is asynchronous: argument errors are reported synchronously, before any
  *    HIP call is made; launch failures come back as KDA_ERR_HIP; faults during
  *    execution surface at the caller's next synchronisation.
  *  - The library does not normalise q or k, applies no gate parameterisation
