@@ -11,14 +11,24 @@
 // The step is bound by HBM bandwidth on the state (Dk*Dv*4 bytes read and
 // written per (b, h)); the arithmetic is fp32 VALU.
 //
-// One 256-thread workgroup per (b, h).  Thread (rg, cg): columns 4cg..4cg+3
-// (one 16-byte load per row, 32 column groups cover a 128-wide row with fully
-// coalesced 512-byte rows), rows rg, rg + NRG, ... .  Partial sums meet in LDS.
+// Columns of S update independently (pred_j, r_j and e_j use column j only),
+// so one workgroup owns NCOL columns of one (b, h), all Dk rows: thread
+// (row group rg, column quad cq) holds RPT consecutive rows x 4 columns in
+// registers from the read to the write (16-byte accesses; NCOL / 4
+// consecutive lanes cover one row's NCOL columns).  The sums over rows go
+// through lane shuffles within a wavefront, then LDS across wavefronts.
+// Each thread holds one row pair, so a workgroup has NCOL * Dk / 8 threads
+// (1024 at 64 columns and Dk = 128: 32 KB of state); slices of 64 columns
+// (256-byte row segments) keep more of HBM busy than one workgroup per (b, h)
+// (launch_decode_cols gives the measurements).  The state is read and written
+// with non-temporal accesses (it is touched once per step and does not fit
+// the caches).  The column slices of one (b, h) are numbered onto one XCD
+// (consecutive workgroups go to consecutive XCDs).
 //
 // PH (phase variant, "Semidirect Fourier Delta Attention" eq. (13)): the decay
 // is the 2x2 block Lambda_p = alpha_p R(theta_p) on rows 2p, 2p+1, so the reads
-// use Lambda^T k and Lambda^T q, and a thread owns whole row pairs (rows
-// 2(rg + j NRG) and the next) to apply Lambda to its own registers.
+// use Lambda^T k and Lambda^T q, and each thread's rows come in pairs
+// (RPT even) so that it applies Lambda to its own registers.
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -26,31 +36,52 @@ namespace kda {
 
 namespace {
 
-constexpr int kDecodeThreads = 256;
+constexpr int kDecodeXcds = 8;
 
-template <typename T, int DK, bool PH>
-__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
+// threads of a workgroup with NCOL columns: one row pair per thread, at most 1024
+constexpr int decode_threads(int DK, int NCOL)
+{
+    return NCOL * DK / 8 > 1024 ? 1024 : (NCOL * DK / 8 < 64 ? 64 : NCOL * DK / 8);
+}
+
+template <int DK, int NCOL, int NTHR>
+struct DecodeGeom {
+    static constexpr int NCQ = NCOL / 4;                                    // column quads
+    static constexpr int NRG = (NTHR / NCQ) < DK / 2 ? NTHR / NCQ : DK / 2;
+    static constexpr int RPT = DK / NRG;                                    // rows per thread (even)
+    static constexpr int ACTIVE = NRG * NCQ;                                // threads holding state
+    static constexpr int WAVES = (ACTIVE + 63) / 64;
+    static_assert(RPT % 2 == 0 && RPT * NRG == DK, "row pairs");
+};
+
+template <typename T, int DK, int NCOL, int NTHR, bool PH>
+__global__ __launch_bounds__(NTHR) void decode_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ theta,
-    const float* __restrict__ beta, float* __restrict__ state, T* __restrict__ out, int Dv)
+    const float* __restrict__ beta, float* __restrict__ state, T* __restrict__ out, int BH, int Dv)
 {
-    constexpr int RMAX = DK / 8 > 0 ? DK / 8 : 1;   // rows per thread when Dv = 128
-    static_assert(!PH || RMAX % 2 == 0, "row pairs");
-    __shared__ float sKa[DK], sQa[DK], sK[DK], sAl[DK], sQK[DK];
+    using G = DecodeGeom<DK, NCOL, NTHR>;
+    constexpr int NCQ = G::NCQ, RPT = G::RPT;
+    __shared__ float sKa[DK], sQa[DK], sK[DK], sAl[DK];
     __shared__ float sLc[DK / 2], sLs[DK / 2];      // (PH) alpha cos, alpha sin per pair
-    __shared__ float sV[128], sE[128];
-    __shared__ float sPk[kDecodeThreads * 4], sPq[kDecodeThreads * 4];
-    __shared__ float sQKsum;
+    __shared__ float sPk[G::WAVES][NCOL], sPq[G::WAVES][NCOL], sE[NCOL];
+    __shared__ float sQKw[NTHR / 64];
 
-    const int bh = blockIdx.x;
-    const int tid = threadIdx.x;
+    // workgroup -> (b h, column slice): the NS slices of one (b, h) share g % 8
+    const int NS = Dv / NCOL;
+    const int g = blockIdx.x, xcd = g % kDecodeXcds, jx = g / kDecodeXcds;
+    const int slice = jx % NS, bh = (jx / NS) * kDecodeXcds + xcd;
+    if (bh >= BH) return;
+    const int c0 = slice * NCOL;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float b = beta[bh];
 
+    float qk = 0.f;
     if (tid < DK) {
         const float kc = to_f32(k[(size_t)bh * DK + tid]);
         const float qc = to_f32(q[(size_t)bh * DK + tid]);
         sK[tid] = kc;
-        sQK[tid] = qc * kc;
+        qk = qc * kc;
         if constexpr (PH) {
             const int p = tid >> 1;
             float sn, cs;
@@ -71,110 +102,123 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
             sQa[tid] = ac * qc;
         }
     }
-    if (tid < Dv) sV[tid] = to_f32(v[(size_t)bh * Dv + tid]);
+    // q . k over the Dk channels: per wavefront, then across them after the barrier
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) qk += __shfl_xor(qk, off);
+    if (lane == 0) sQKw[wave] = qk;
+
+    const int cq = tid % NCQ, rg = tid / NCQ;
+    const bool active = tid < G::ACTIVE;
+    float* Sc = state + (size_t)bh * DK * Dv + c0 + 4 * cq;     // column quad cq of the slice
+    f32x4 s[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int row = rg * RPT + i;
+        s[i] = active ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sc + (size_t)row * Dv))
+                      : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     __syncthreads();
-    if (tid < 64) {
-        float s = 0.f;
-        for (int c = tid; c < DK; c += 64) s += sQK[c];
-        for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-        if (tid == 0) sQKsum = s;
-    }
-
-    const int ncg = Dv >> 2;               // column groups of 4
-    const int nrg = kDecodeThreads / ncg;  // row groups
-    const int cg = tid % ncg, rg = tid / ncg;
-    const bool active = rg < nrg;          // 256 % ncg != 0 leaves a few idle threads
-    float* Sbh = state + (size_t)bh * DK * Dv;
-
-    float4 s[RMAX];
-    float pk[4] = {0.f, 0.f, 0.f, 0.f}, pq[4] = {0.f, 0.f, 0.f, 0.f};
-    auto row_of = [&](int i) { return PH ? 2 * (rg + (i >> 1) * nrg) + (i & 1) : rg + i * nrg; };
-#pragma unroll
-    for (int i = 0; i < RMAX; ++i) {
-        const int row = row_of(i);
-        if (active && row < DK) s[i] = *reinterpret_cast<const float4*>(Sbh + (size_t)row * Dv + 4 * cg);
-    }
-#pragma unroll
-    for (int i = 0; i < RMAX; ++i) {
-        const int row = row_of(i);
-        if (active && row < DK) {
-            const float ka = sKa[row], qa = sQa[row];
-            pk[0] += ka * s[i].x; pk[1] += ka * s[i].y; pk[2] += ka * s[i].z; pk[3] += ka * s[i].w;
-            pq[0] += qa * s[i].x; pq[1] += qa * s[i].y; pq[2] += qa * s[i].z; pq[3] += qa * s[i].w;
-        }
-    }
+    f32x4 pk = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
     if (active) {
 #pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int row = rg * RPT + i;
+            pk += sKa[row] * s[i];
+            pq += sQa[row] * s[i];
+        }
+    }
+    // sum over the row groups of this wavefront (lanes NCQ apart)
+#pragma unroll
+    for (int off = NCQ; off < 64; off <<= 1) {
+#pragma unroll
         for (int j = 0; j < 4; ++j) {
-            sPk[rg * Dv + 4 * cg + j] = pk[j];
-            sPq[rg * Dv + 4 * cg + j] = pq[j];
+            pk[j] += __shfl_xor(pk[j], off);
+            pq[j] += __shfl_xor(pq[j], off);
+        }
+    }
+    if (lane < NCQ && wave < G::WAVES) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            sPk[wave][4 * lane + j] = pk[j];
+            sPq[wave][4 * lane + j] = pq[j];
         }
     }
     __syncthreads();
-    if (tid < Dv) {
-        float pred = 0.f, r = 0.f;
-        for (int g = 0; g < nrg; ++g) {
-            pred += sPk[g * Dv + tid];
-            r += sPq[g * Dv + tid];
-        }
-        const float e = sV[tid] - pred;
+    if (tid < NCOL) {
+        float pred = 0.f, r = 0.f, qks = 0.f;
+#pragma unroll
+        for (int w = 0; w < G::WAVES; ++w) { pred += sPk[w][tid]; r += sPq[w][tid]; }
+#pragma unroll
+        for (int w = 0; w < (DK + 63) / 64; ++w) qks += sQKw[w];
+        const float e = to_f32(v[(size_t)bh * Dv + c0 + tid]) - pred;
         sE[tid] = e;
-        out[(size_t)bh * Dv + tid] = from_f32<T>(r + b * sQKsum * e);
+        out[(size_t)bh * Dv + c0 + tid] = from_f32<T>(r + b * qks * e);
     }
     __syncthreads();
-    const float e0 = sE[4 * cg], e1 = sE[4 * cg + 1], e2 = sE[4 * cg + 2], e3 = sE[4 * cg + 3];
+    if (!active) return;
+    const f32x4 e4 = {sE[4 * cq], sE[4 * cq + 1], sE[4 * cq + 2], sE[4 * cq + 3]};
     if constexpr (PH) {
         // rows (2p, 2p+1) sit in s[i], s[i + 1]: Lambda S, then the correction
 #pragma unroll
-        for (int i = 0; i < RMAX; i += 2) {
-            const int row = row_of(i);
-            if (active && row < DK) {
-                const float lc = sLc[row >> 1], ls = sLs[row >> 1];
-                const float b0 = b * sK[row], b1 = b * sK[row + 1];
-                const float4 x = s[i], y = s[i + 1];
-                float4 o0, o1;
-                o0.x = lc * x.x - ls * y.x + b0 * e0; o1.x = ls * x.x + lc * y.x + b1 * e0;
-                o0.y = lc * x.y - ls * y.y + b0 * e1; o1.y = ls * x.y + lc * y.y + b1 * e1;
-                o0.z = lc * x.z - ls * y.z + b0 * e2; o1.z = ls * x.z + lc * y.z + b1 * e2;
-                o0.w = lc * x.w - ls * y.w + b0 * e3; o1.w = ls * x.w + lc * y.w + b1 * e3;
-                *reinterpret_cast<float4*>(Sbh + (size_t)row * Dv + 4 * cg) = o0;
-                *reinterpret_cast<float4*>(Sbh + (size_t)(row + 1) * Dv + 4 * cg) = o1;
-            }
+        for (int i = 0; i < RPT; i += 2) {
+            const int row = rg * RPT + i;
+            const float lc = sLc[row >> 1], ls = sLs[row >> 1];
+            const f32x4 o0 = lc * s[i] - ls * s[i + 1] + (b * sK[row]) * e4;
+            const f32x4 o1 = ls * s[i] + lc * s[i + 1] + (b * sK[row + 1]) * e4;
+            __builtin_nontemporal_store(o0, reinterpret_cast<f32x4*>(Sc + (size_t)row * Dv));
+            __builtin_nontemporal_store(o1, reinterpret_cast<f32x4*>(Sc + (size_t)(row + 1) * Dv));
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < RMAX; ++i) {
-            const int row = row_of(i);
-            if (active && row < DK) {
-                const float a = sAl[row], bk = b * sK[row];
-                float4 o;
-                o.x = a * s[i].x + bk * e0;
-                o.y = a * s[i].y + bk * e1;
-                o.z = a * s[i].z + bk * e2;
-                o.w = a * s[i].w + bk * e3;
-                *reinterpret_cast<float4*>(Sbh + (size_t)row * Dv + 4 * cg) = o;
-            }
+        for (int i = 0; i < RPT; ++i) {
+            const int row = rg * RPT + i;
+            const f32x4 o = sAl[row] * s[i] + (b * sK[row]) * e4;
+            __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(Sc + (size_t)row * Dv));
         }
     }
 }
 
-template <typename T, bool PH>
+template <typename T, bool PH, int NCOL>
 hipError_t launch_decode_t(int B, int H, int Dk, int Dv, const void* q, const void* k,
                            const void* v, const float* alpha, const float* theta,
                            const float* beta, float* state, void* out, hipStream_t stream)
 {
-    const dim3 grid((unsigned)(B * H)), block(kDecodeThreads);
+    const int BH = B * H;
+    // (b h) rounded up to whole XCD rounds, times the column slices
+    const unsigned nblk = (unsigned)(((BH + kDecodeXcds - 1) / kDecodeXcds) * kDecodeXcds * (Dv / NCOL));
+    const dim3 grid(nblk);
     const T* qq = static_cast<const T*>(q);
     const T* kk = static_cast<const T*>(k);
     const T* vv = static_cast<const T*>(v);
     T* oo = static_cast<T*>(out);
     switch (Dk) {
-    case 16: return launch_kernel(decode_kernel<T, 16, PH>, grid, block, 0, stream, qq, kk, vv, alpha, theta, beta, state, oo, Dv);
-    case 32: return launch_kernel(decode_kernel<T, 32, PH>, grid, block, 0, stream, qq, kk, vv, alpha, theta, beta, state, oo, Dv);
-    case 64: return launch_kernel(decode_kernel<T, 64, PH>, grid, block, 0, stream, qq, kk, vv, alpha, theta, beta, state, oo, Dv);
-    case 128: return launch_kernel(decode_kernel<T, 128, PH>, grid, block, 0, stream, qq, kk, vv, alpha, theta, beta, state, oo, Dv);
+    case 16: return launch_kernel(decode_kernel<T, 16, NCOL, decode_threads(16, NCOL), PH>, grid,
+                                   dim3(decode_threads(16, NCOL)), 0, stream, qq, kk, vv, alpha, theta, beta, state, oo, BH, Dv);
+    case 32: return launch_kernel(decode_kernel<T, 32, NCOL, decode_threads(32, NCOL), PH>, grid,
+                                   dim3(decode_threads(32, NCOL)), 0, stream, qq, kk, vv, alpha, theta, beta, state, oo, BH, Dv);
+    case 64: return launch_kernel(decode_kernel<T, 64, NCOL, decode_threads(64, NCOL), PH>, grid,
+                                   dim3(decode_threads(64, NCOL)), 0, stream, qq, kk, vv, alpha, theta, beta, state, oo, BH, Dv);
+    case 128: return launch_kernel(decode_kernel<T, 128, NCOL, decode_threads(128, NCOL), PH>, grid,
+                                   dim3(decode_threads(128, NCOL)), 0, stream, qq, kk, vv, alpha, theta, beta, state, oo, BH, Dv);
     default: return hipErrorInvalidValue;
     }
+}
+
+template <typename T, bool PH>
+hipError_t launch_decode_cols(int B, int H, int Dk, int Dv, const void* q, const void* k,
+                              const void* v, const float* alpha, const float* theta,
+                              const float* beta, float* state, void* out, hipStream_t stream)
+{
+    // 64 columns (256-byte row segments) where Dv allows, else 32, else 16.
+    // Measured (B=256, H=32, d=128, in-place fp32 state, 1.086 GB per step):
+    // 212 us with one workgroup per (b, h); 175 us at 64 columns / 1024
+    // threads, 181 us at 32 / 256, 185 us at 128 / 1024, 217 us at 16 / 256
+    // (half-line row segments), 429 us at 8 / 128.
+    if (Dv % 64 == 0)
+        return launch_decode_t<T, PH, 64>(B, H, Dk, Dv, q, k, v, alpha, theta, beta, state, out, stream);
+    if (Dv % 32 == 0)
+        return launch_decode_t<T, PH, 32>(B, H, Dk, Dv, q, k, v, alpha, theta, beta, state, out, stream);
+    return launch_decode_t<T, PH, 16>(B, H, Dk, Dv, q, k, v, alpha, theta, beta, state, out, stream);
 }
 
 }  // namespace
@@ -185,12 +229,12 @@ hipError_t launch_decode(IoType io, int B, int H, int Dk, int Dv, const void* q,
 {
     if (theta) {
         if (io == IoType::F32)
-            return launch_decode_t<float, true>(B, H, Dk, Dv, q, k, v, alpha, theta, beta, state, out, stream);
-        return launch_decode_t<bf16_t, true>(B, H, Dk, Dv, q, k, v, alpha, theta, beta, state, out, stream);
+            return launch_decode_cols<float, true>(B, H, Dk, Dv, q, k, v, alpha, theta, beta, state, out, stream);
+        return launch_decode_cols<bf16_t, true>(B, H, Dk, Dv, q, k, v, alpha, theta, beta, state, out, stream);
     }
     if (io == IoType::F32)
-        return launch_decode_t<float, false>(B, H, Dk, Dv, q, k, v, alpha, nullptr, beta, state, out, stream);
-    return launch_decode_t<bf16_t, false>(B, H, Dk, Dv, q, k, v, alpha, nullptr, beta, state, out, stream);
+        return launch_decode_cols<float, false>(B, H, Dk, Dv, q, k, v, alpha, nullptr, beta, state, out, stream);
+    return launch_decode_cols<bf16_t, false>(B, H, Dk, Dv, q, k, v, alpha, nullptr, beta, state, out, stream);
 }
 
 }  // namespace kda

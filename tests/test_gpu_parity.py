@@ -279,7 +279,8 @@ def test_forward_phase_zero_is_kda_bitwise():
 
 
 @pytest.mark.parametrize("dtype,Dk,Dv", [(torch.float32, 32, 48), (torch.bfloat16, 128, 128),
-                                         (torch.bfloat16, 16, 80)])
+                                         (torch.bfloat16, 16, 80), (torch.bfloat16, 64, 96),
+                                         (torch.float32, 64, 64)])
 def test_decode_phase(dtype, Dk, Dv):
     """kda_decode_step_phase: three steps against the oracle's phase-variant
     recurrence on the same tokens."""
@@ -406,6 +407,9 @@ DECODE = [
     ("f32_d64_dv48", torch.float32, 1, 2, 64, 48, 5),
     ("bf16_d128_dv128", torch.bfloat16, 4, 4, 128, 128, 9),
     ("bf16_d32_dv80", torch.bfloat16, 3, 2, 32, 80, 4),
+    ("bf16_d64_dv96", torch.bfloat16, 3, 3, 64, 96, 6),
+    ("bf16_d128_dv32", torch.bfloat16, 2, 5, 128, 32, 5),
+    ("f32_d64_dv64", torch.float32, 1, 3, 64, 64, 6),
 ]
 
 
