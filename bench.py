@@ -6,7 +6,7 @@ kda_chunk_forward call over the whole batch (gate summary, intra-chunk WY,
 state propagation and outputs).  Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-others] [--no-cpu]
-                  [--copy-probe]
+                  [--backward] [--decode] [--gate-prep] [--copy-probe]
 
 The roofline object describes the kernel with the largest average duration,
 timed live with HIP events recorded by the library on the launch stream
@@ -220,6 +220,30 @@ def decode_bench(kda, torch, workloads, steps_cap=None):
             "hbm_frac": bytes_step / (per_step / 1e3) / 1e9 / HBM_PEAK_GBS}
 
 
+def gate_prep_bench(kda, torch, w, inp, steps):
+    """kda_gate_prep (the standalone gate summary, row a1) on workload w: us per
+    call and the HBM fraction of its algorithmic bytes (alpha read once; L,
+    the meta byte and Gamma_C written once)."""
+    alpha = inp["alpha"]
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        kda.gate_prep(alpha, w.chunk, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        kda.gate_prep(alpha, w.chunk, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = 1e3 * e0.elapsed_time(e1) / steps
+    nc = (w.T + w.chunk - 1) // w.chunk
+    nbytes = (w.B * w.T * w.H * w.Dk * 4 + w.B * w.H * nc * w.chunk * w.Dk * (4 + 1)
+              + w.B * w.H * nc * w.Dk * 4)
+    return {"workload": w.name, "us": us, "algorithmic_bytes": nbytes,
+            "achieved_GBps": nbytes / (us / 1e6) / 1e9,
+            "hbm_frac": nbytes / (us / 1e6) / 1e9 / HBM_PEAK_GBS}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -229,6 +253,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward on the headline workload even with --no-others")
+    ap.add_argument("--decode", action="store_true",
+                    help="time the decode workload even with --no-others")
+    ap.add_argument("--gate-prep", action="store_true",
+                    help="time the standalone gate summary even with --no-others")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -297,8 +325,12 @@ def main():
             others[f"ckda_bf16_long_ctx_H2_{tag}"] = {"ms": mso, "tokens_per_s": wo.B * wo.T / (mso / 1e3),
                                                      "kernels_ms": pero}
         del io
-        others["ckda_bf16_decode"] = decode_bench(kda, torch, workloads)
         line["others"] = others
+    if not args.no_others or args.decode:
+        line.setdefault("others", {})["ckda_bf16_decode"] = decode_bench(kda, torch, workloads)
+    if not args.no_others or args.gate_prep:
+        line.setdefault("others", {})["kda_gate_prep"] = gate_prep_bench(kda, torch, w, inp,
+                                                                         max(10, args.steps // 4))
     if not args.no_others or args.backward:
         # the backward (kda_chunk_backward) on the headline workload
         msb, perb, nbb = time_backward(kda, torch, w, inp, max(3, args.steps // 4), 3)

@@ -1087,7 +1087,8 @@ kda_status_t kda_gate_prep(const float* alpha, float* L, unsigned char* meta, fl
     if ((long long)B * H * NC > 0x7fffffffLL) return KDA_ERR_BAD_SHAPE;
     if (T == 0) return KDA_OK;
     if (!alpha || !L || !meta || !gend) return KDA_ERR_NULL_POINTER;
-    if (!aligned(alpha, 4) || !aligned(L, 4) || !aligned(gend, 4)) return KDA_ERR_MISALIGNED;
+    if (!aligned16(alpha) || !aligned16(L) || !aligned16(gend) || !aligned(meta, 4))
+        return KDA_ERR_MISALIGNED;
     const size_t nel = (size_t)B * H * NC * chunk * Dk;
     const size_t na = (size_t)B * T * H * Dk * 4;
     struct R { const void* p; size_t n; } rs[] = {

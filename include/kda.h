@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 9
+#define KDA_ABI_VERSION 10
 
 typedef enum {
     KDA_OK = 0,
@@ -388,7 +388,9 @@ kda_status_t kda_chunk_backward_varlen(const void* q, const void* k, const void*
  * 2^(L_r - L_i).  alpha : [B,T,H,Dk] fp32.  L : [B,H,NC,chunk,Dk] fp32,
  * meta : [B,H,NC,chunk,Dk] uint8, gend : [B,H,NC,Dk] fp32; entries of a short
  * last chunk past T are written as L = 0, meta = 0.  Same shape rules as the
- * forward (Dk in {16,32,64,128}, chunk in {16,32,64}).
+ * forward (Dk in {16,32,64,128}, chunk in {16,32,64}).  alpha, L and gend are
+ * accessed 16 bytes at a time and must be 16-byte aligned, meta 4-byte
+ * aligned (KDA_ERR_MISALIGNED otherwise).
  */
 kda_status_t kda_gate_prep(const float* alpha, float* L, unsigned char* meta,
                            float* gend, int B, int T, int H, int Dk, int chunk,

@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 9
+    assert lib.kda_abi_version() == 10
     for s in range(8):
         assert lib.kda_status_string(s)
     assert lib.kda_status_string(99) == b"unknown status"
@@ -249,6 +249,11 @@ def test_gate_prep_validation(lib):
     assert lib.kda_gate_prep(*a, 1, 10, 1, 16, 20, None) == UNSUP
     assert lib.kda_gate_prep(*a, 1, -1, 1, 16, 16, None) == SHAPE
     assert lib.kda_gate_prep(*a, 1, 0, 1, 16, 16, None) == OK       # nothing to do
+    off = lambda i, d: a[:i] + [ctypes.c_void_p(a[i].value + d)] + a[i + 1:]
+    assert lib.kda_gate_prep(*off(0, 4), 1, 10, 1, 16, 16, None) == MISAL   # alpha: 16 B
+    assert lib.kda_gate_prep(*off(1, 8), 1, 10, 1, 16, 16, None) == MISAL   # L: 16 B
+    assert lib.kda_gate_prep(*off(2, 2), 1, 10, 1, 16, 16, None) == MISAL   # meta: 4 B
+    assert lib.kda_gate_prep(*off(3, 4), 1, 10, 1, 16, 16, None) == MISAL   # gend: 16 B
 
 
 def test_binding_refuses_cpu_tensors():
