@@ -40,6 +40,11 @@ template <> struct Vec4<float> {
         const float4 x = *reinterpret_cast<const float4*>(p);
         return Vec4{{x.x, x.y, x.z, x.w}};
     }
+    // non-temporal: for inputs read once (streamed past the caches)
+    __device__ __forceinline__ static Vec4 load_nt(const float* p) {
+        const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+        return Vec4{{x[0], x[1], x[2], x[3]}};
+    }
     __device__ __forceinline__ static Vec4 from(const float* f) { return Vec4{{f[0], f[1], f[2], f[3]}}; }
     __device__ __forceinline__ static Vec4 zero() { return Vec4{{0.f, 0.f, 0.f, 0.f}}; }
     __device__ __forceinline__ float get(int i) const { return v[i]; }
@@ -49,6 +54,9 @@ template <> struct Vec4<bf16_t> {
     i16x4 v;   // raw bf16 bits
     __device__ __forceinline__ static Vec4 load(const bf16_t* p) {
         return Vec4{*reinterpret_cast<const i16x4*>(p)};
+    }
+    __device__ __forceinline__ static Vec4 load_nt(const bf16_t* p) {
+        return Vec4{__builtin_nontemporal_load(reinterpret_cast<const i16x4*>(p))};
     }
     __device__ __forceinline__ static Vec4 from(const float* f) {
         i16x4 r;

@@ -166,7 +166,8 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
     T* Pg = static_cast<T*>(args.P) + (size_t)unit * C * C;
 
     // ---- loads: my 4 channels over my TOK tokens (k, q kept in io precision) ----
-    // (rows past the end re-read the last valid row and become no-op tokens)
+    // (rows past the end re-read the last valid row and become no-op tokens;
+    // the inputs are read once, so the loads are non-temporal)
     float al[TOK][4], bt[TOK];
     float th[TOK][2];                  // (PH) the phases of my two channel pairs
     Vec4<T> kv[TOK], qv[TOK];
@@ -181,11 +182,11 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
             th[j][0] = t2.x;
             th[j][1] = t2.y;
         } else {
-            const float4 a4 = *reinterpret_cast<const float4*>(ga + r * rs + c0);
-            al[j][0] = a4.x; al[j][1] = a4.y; al[j][2] = a4.z; al[j][3] = a4.w;
+            const f32x4 a4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ga + r * rs + c0));
+            al[j][0] = a4[0]; al[j][1] = a4[1]; al[j][2] = a4[2]; al[j][3] = a4[3];
         }
-        kv[j] = Vec4<T>::load(gk + r * rs + c0);
-        qv[j] = Vec4<T>::load(gq + r * rs + c0);
+        kv[j] = Vec4<T>::load_nt(gk + r * rs + c0);
+        qv[j] = Vec4<T>::load_nt(gq + r * rs + c0);
         bt[j] = gb[r * H];
     }
     if constexpr (PRO) {
@@ -469,7 +470,7 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
         const int vq = it % nvq, tg = it / nvq;
 #pragma unroll
         for (int z = 0; z < TV; ++z)
-            vreg[x][z] = Vec4<T>::load(gv + min(tg * TV + z, nvalid - 1) * rsv + 4 * vq);
+            vreg[x][z] = Vec4<T>::load_nt(gv + min(tg * TV + z, nvalid - 1) * rsv + 4 * vq);
     }
 
     // ---- A (strictly lower, LDS) and P^T tiles (global, fragment-major) --------
