@@ -682,3 +682,28 @@ def test_forward_prologue_parts_bitwise():
                                               flags=fl))
     torch.cuda.synchronize()
     assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+
+
+def test_forward_phase_parts():
+    """The phase variant in parts: the oracle's phase recurrence, and bitwise
+    its single-stream path (outputs and final state); one chain launch per
+    part."""
+    w = workloads.workload(3, B=1, H=9, T=4133, chunk=16, s0_std=0.2)
+    say(f"[forward phase parts] {w}")
+    inp = workloads.make_prefill_phase(w, theta_max=2.0)
+    o_ref, s_ref = oracle.forward_phase(np32(inp["q"]), np32(inp["k"]), np32(inp["v"]),
+                                        np32(inp["alpha"]), np32(inp["theta"]), np32(inp["beta"]),
+                                        np32(inp["S0"]), nthreads=oracle_threads())
+    d = to_dev(inp)
+    res = []
+    for fl in (kda.STAGE_EVENTS, kda.SINGLE_STREAM | kda.STAGE_EVENTS):
+        res.append(kda.chunk_forward_phase(d["q"], d["k"], d["v"], d["alpha"], d["theta"], d["beta"],
+                                           d["S0"], chunk=w.chunk, mode=w.mode, flags=fl))
+        torch.cuda.synchronize()
+        names = [n for n, _ in kda.last_stage_times()]
+        assert names.count("chain") == (8 if fl == kda.STAGE_EVENTS else 1)
+    (out, st), (out1, st1) = res
+    eo, es = slice_err_out(np32(out), o_ref), slice_err_state(np32(st), s_ref)
+    say(f"  err out {eo:.3e} state {es:.3e}")
+    assert eo <= TOL[w.dtype] and es <= TOL[w.dtype]
+    assert torch.equal(out, out1) and torch.equal(st, st1)
