@@ -222,7 +222,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
     struct Ops {
         F pt[G::NKC], kt[G::NKD], qt[G::SPW][G::NKC], wt[G::SPW][G::NKC];
         f32x4 gc[G::SPW];
-        Vec4<T> dov;                     // this thread's staged dO piece
+        Vec4<T> dov;                     // this thread's dO piece of chunk n - 1
+    };
+    // this thread's dO piece of chunk m (rows past the end, and threads past
+    // the chunk, read the sequence's last row; they are zeroed when staged)
+    auto load_do = [&](int m) {
+        const int row = min(m * C + min(drow, C - 1), sp.len - 1);
+        return Vec4<T>::load(dO + (((size_t)sp.row0 + row) * H + h) * Dv + slice * 16 + dcol);
     };
     auto load_ops = [&](Ops& o, int n) {
         const size_t unit = sp.ubase + n;
@@ -245,16 +251,15 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
             }
             o.gc[u] = *reinterpret_cast<const f32x4*>(a.GC + unit * DK + 16 * t + 4 * lg);
         }
-        // rows past the end (and threads past the chunk) read the sequence's
-        // last row, zeroed when staged
-        const int row = min(n * C + min(drow, C - 1), sp.len - 1);
-        o.dov = Vec4<T>::load(dO + (((size_t)sp.row0 + row) * H + h) * Dv + slice * 16 + dcol);
+        // one chunk ahead of the operands: staged during the step on chunk n,
+        // a step after it was loaded
+        o.dov = load_do(n > 0 ? n - 1 : 0);
     };
-    auto stage_do = [&](const Ops& o, int n) {
+    auto stage_do = [&](const Vec4<T>& dv, int n) {
         if (drow < C) {
             const bool ok = n * C + drow < sp.len;
 #pragma unroll
-            for (int x = 0; x < 4; ++x) sDOt[n & 1][dcol + x][drow] = ok ? o.dov.elem(x) : from_f32<T>(0.f);
+            for (int x = 0; x < 4; ++x) sDOt[n & 1][dcol + x][drow] = ok ? dv.elem(x) : from_f32<T>(0.f);
         }
     };
     // dO B fragments of chunk n from the staged copy
@@ -311,10 +316,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
     };
     auto consume = [&]() { pf ^= pfv[0].x ^ pfv[1].y; };
 
-    // one step of the reverse chain on chunk n with its operands o; the
-    // next chunk's dO piece (in nx, loaded during this step) is staged before
-    // the step's second barrier
-    auto step = [&](const Ops& o, int n, const Ops* nx) {
+    // one step of the reverse chain on chunk n with its operands o; the next
+    // chunk's dO piece (o.dov, loaded with these operands a step earlier) is
+    // staged before the step's second barrier
+    auto step = [&](const Ops& o, int n) {
         const size_t unit = sp.ubase + n;
         consume();
         if (n >= 3) prefetch(n - 3);
@@ -374,21 +379,21 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
                 put_tile<T, G::KB>(sSf, t, lane, acc);
             }
         }
-        if (nx) stage_do(*nx, n - 1);
+        if (n >= 1) stage_do(o.dov, n - 1);
         __syncthreads();
     };
 
     // two operand sets used in turn (no register copies between steps)
     Ops A, B;
     load_ops(A, NCs - 1);
-    stage_do(A, NCs - 1);
+    stage_do(load_do(NCs - 1), NCs - 1);
     __syncthreads();
     for (int n = NCs - 1; n >= 0; n -= 2) {
         if (n >= 1) load_ops(B, n - 1);
-        step(A, n, n >= 1 ? &B : nullptr);
+        step(A, n);
         if (n < 1) break;
         if (n >= 2) load_ops(A, n - 2);
-        step(B, n - 1, n >= 2 ? &A : nullptr);
+        step(B, n - 1);
     }
     consume();
     if (a.T < 0) a.XB[lane] = __uint_as_float(pf);
