@@ -194,15 +194,22 @@ struct SideStream {
 std::mutex g_side_mu;
 std::map<int, SideStream> g_side;
 
-// The side stream of the current device in *out, created on first use; while
-// `caller` is being captured into a graph nothing is created (*out = null if
-// it does not exist yet: the call then keeps to the caller's stream).
+// The side stream of the current device in *out, created on first use.
+// *out stays null (the call keeps to the caller's stream) when `caller`
+// belongs to another device, or when it is being captured into a graph and
+// the side stream does not exist yet (nothing is created during a capture).
 hipError_t side_stream(hipStream_t caller, SideStream** out)
 {
     *out = nullptr;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
+    if (caller) {
+        hipDevice_t sdev = 0;
+        e = hipStreamGetDevice(caller, &sdev);
+        if (e != hipSuccess) return e;
+        if (sdev != dev) return hipSuccess;
+    }
     SideStream& ss = g_side[dev];
     if (!ss.st) {
         hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;

@@ -93,8 +93,9 @@ typedef enum { KDA_MODE_KDA = 0, KDA_MODE_CKDA = 1 } kda_mode_t;
  * by events, so the call still ends on the caller's stream (a graph captured
  * from the caller's stream takes in both; the second stream is never created
  * during a capture, so a call captured before any uncaptured call of that
- * shape on the device keeps to one stream).  The results are bitwise those
- * of the single-stream path. */
+ * shape on the device keeps to one stream; a caller stream of another device
+ * than the current one also keeps to one stream).  The results are bitwise
+ * those of the single-stream path. */
 #define KDA_FLAG_SINGLE_STREAM 8u
 
 /* ABI version of the loaded library (KDA_ABI_VERSION it was built with). */

@@ -660,6 +660,12 @@ def test_forward_parts(name, base, ov, flags):
     out1, st1 = run_gpu(d, w.chunk, w.mode, flags=flags | kda.SINGLE_STREAM | kda.STAGE_EVENTS)
     assert _stage_names().count("chain") == 1
     assert torch.equal(out, out1) and torch.equal(st, st1)
+    # an explicit (non-default) caller stream takes the parts path too
+    cs_ = torch.cuda.Stream()
+    cs_.wait_stream(torch.cuda.current_stream())
+    out2, st2 = run_gpu(d, w.chunk, w.mode, flags=flags | kda.STAGE_EVENTS, stream=cs_)
+    assert _stage_names().count("chain") == 8
+    assert torch.equal(out, out2) and torch.equal(st, st2)
     nc = (w.T + w.chunk - 1) // w.chunk
     cs = [torch.full((w.B, w.H, nc, w.Dk, w.Dv), float("nan"), dtype=w.dtype, device=DEV)
           for _ in range(2)]
