@@ -20,7 +20,7 @@ import torch
 __all__ = [
     "KDA", "CKDA", "KdaError", "library_path", "load", "abi_version", "workspace_size",
     "chunk_forward", "chunk_forward_prologue", "chunk_forward_varlen", "chunk_forward_phase",
-    "decode_step", "decode_step_phase", "gate_prep", "last_stage_times",
+    "decode_step", "decode_step_phase", "decode_step_prologue", "gate_prep", "last_stage_times",
     "STAGE_EVENTS", "NO_SEGMENTS", "SINGLE_STREAM",
 ]
 
@@ -87,6 +87,9 @@ def load():
     lib.kda_chunk_forward_varlen.restype = i
     lib.kda_decode_step.argtypes = [vp] * 7 + [i] * 6 + [u, vp]
     lib.kda_decode_step.restype = i
+    lib.kda_decode_step_prologue.argtypes = [vp] * 5 + [ctypes.POINTER(Prologue)] + [vp] * 2 + \
+        [i] * 6 + [u, vp]
+    lib.kda_decode_step_prologue.restype = i
     lib.kda_chunk_backward_workspace_size.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(sz)]
     lib.kda_chunk_backward_workspace_size.restype = i
     lib.kda_chunk_backward.argtypes = [vp] * 14 + [i] * 8 + [u, vp, sz, vp]
@@ -325,6 +328,28 @@ def decode_step(q, k, v, alpha, beta, state, *, out=None, mode: int = CKDA, stre
     st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state),
                              _ptr(out), B, H, Dk, Dv, _DT[q.dtype], mode, flags, _stream(stream))
     _check("kda_decode_step", st)
+    return out
+
+
+def decode_step_prologue(q_raw, k_raw, v, gate, beta_logit, state, *, alpha_min: float,
+                         alpha_max: float, beta_max: float, eps: float = 1e-6,
+                         normalize_q: bool = True, out=None, mode: int = CKDA, stream=None,
+                         flags: int = 0):
+    """One token for every (b, h) from raw inputs (kda_decode_step_prologue):
+    gate [B,H,Dk] and beta_logit [B,H] fp32 logits, q_raw / k_raw
+    unnormalised; the transforms of chunk_forward_prologue.  state [B,H,Dk,Dv]
+    fp32 is updated in place.  Returns out [B,H,Dv]."""
+    lib = load()
+    B, H, Dk = q_raw.shape
+    Dv = v.shape[-1]
+    if out is None:
+        out = torch.empty((B, H, Dv), dtype=q_raw.dtype, device=q_raw.device)
+    _dev(q_raw, k_raw, v, gate, beta_logit, state, out)
+    pro = Prologue(alpha_min, alpha_max, beta_max, eps, 1 if normalize_q else 0)
+    st = lib.kda_decode_step_prologue(_ptr(q_raw), _ptr(k_raw), _ptr(v), _ptr(gate),
+                                      _ptr(beta_logit), ctypes.byref(pro), _ptr(state), _ptr(out),
+                                      B, H, Dk, Dv, _DT[q_raw.dtype], mode, flags, _stream(stream))
+    _check("kda_decode_step_prologue", st)
     return out
 
 

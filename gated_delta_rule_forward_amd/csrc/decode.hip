@@ -25,11 +25,18 @@
 // the caches).  The column slices of one (b, h) are numbered onto one XCD
 // (consecutive workgroups go to consecutive XCDs).
 //
+// PRO (input parameterisation, same page §3 eqs. (15), (17), (18)): alpha and
+// beta arrive as logits and q, k raw; the loads apply alpha = amin + arange
+// sigmoid(gate), beta = bmax sigmoid(logit) and k / (|k| + eps) (q likewise
+// when normq), with the norms summed over the Dk channels across the
+// workgroup and the normalised q, k rounded to the io type once, as in the
+// chunked forward.
+//
 // PH (phase variant, "Semidirect Fourier Delta Attention" eq. (13)): the decay
 // is the 2x2 block Lambda_p = alpha_p R(theta_p) on rows 2p, 2p+1, so the reads
 // use Lambda^T k and Lambda^T q, and each thread's rows come in pairs
 // (RPT even) so that it applies Lambda to its own registers.
-#include "kda_device.hpp"
+#include "kda_chunk.hpp"
 #include "kda_launch.hpp"
 
 namespace kda {
@@ -54,12 +61,14 @@ struct DecodeGeom {
     static_assert(RPT % 2 == 0 && RPT * NRG == DK, "row pairs");
 };
 
-template <typename T, int DK, int NCOL, int NTHR, bool PH>
+template <typename T, int DK, int NCOL, int NTHR, bool PH, bool PRO>
 __global__ __launch_bounds__(NTHR) void decode_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ theta,
-    const float* __restrict__ beta, float* __restrict__ state, T* __restrict__ out, int BH, int Dv)
+    const float* __restrict__ beta, float* __restrict__ state, T* __restrict__ out, int BH, int Dv,
+    DecodePro pro)
 {
+    static_assert(!(PH && PRO), "the parameterisation and the phase variant are not combined");
     using G = DecodeGeom<DK, NCOL, NTHR>;
     constexpr int NCQ = G::NCQ, RPT = G::RPT;
     __shared__ float sKa[DK], sQa[DK], sK[DK], sAl[DK];
@@ -74,12 +83,31 @@ __global__ __launch_bounds__(NTHR) void decode_kernel(
     if (bh >= BH) return;
     const int c0 = slice * NCOL;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const float b = beta[bh];
+    const float b = PRO ? pro.bmax * sigmoid_f32(beta[bh]) : beta[bh];
 
     float qk = 0.f;
+    float kc = tid < DK ? to_f32(k[(size_t)bh * DK + tid]) : 0.f;
+    float qc = tid < DK ? to_f32(q[(size_t)bh * DK + tid]) : 0.f;
+    if constexpr (PRO) {
+        // |k| and |q| over the Dk channels: per wavefront, then across them
+        __shared__ float sNrm[NTHR / 64][2];
+        float kk = kc * kc, qq = qc * qc;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            kk += __shfl_xor(kk, off);
+            qq += __shfl_xor(qq, off);
+        }
+        if (lane == 0) { sNrm[wave][0] = kk; sNrm[wave][1] = qq; }
+        __syncthreads();
+        kk = 0.f;
+        qq = 0.f;
+#pragma unroll
+        for (int w = 0; w < (DK + 63) / 64; ++w) { kk += sNrm[w][0]; qq += sNrm[w][1]; }
+        const float nk = __builtin_sqrtf(kk) + pro.eps, nq = __builtin_sqrtf(qq) + pro.eps;
+        kc = to_f32(from_f32<T>(kc * (nk > 0.f ? 1.f / nk : 0.f)));
+        if (pro.normq) qc = to_f32(from_f32<T>(qc * (nq > 0.f ? 1.f / nq : 0.f)));
+    }
     if (tid < DK) {
-        const float kc = to_f32(k[(size_t)bh * DK + tid]);
-        const float qc = to_f32(q[(size_t)bh * DK + tid]);
         sK[tid] = kc;
         qk = qc * kc;
         if constexpr (PH) {
@@ -96,7 +124,8 @@ __global__ __launch_bounds__(NTHR) void decode_kernel(
             sQa[tid] = lc * qc + sg * ls * qo;
             if ((tid & 1) == 0) { sLc[p] = lc; sLs[p] = ls; }
         } else {
-            const float ac = alpha[(size_t)bh * DK + tid];
+            const float ac = PRO ? pro.amin + pro.arange * sigmoid_f32(alpha[(size_t)bh * DK + tid])
+                                 : alpha[(size_t)bh * DK + tid];
             sAl[tid] = ac;
             sKa[tid] = ac * kc;
             sQa[tid] = ac * qc;
@@ -178,10 +207,11 @@ __global__ __launch_bounds__(NTHR) void decode_kernel(
     }
 }
 
-template <typename T, bool PH, int NCOL>
+template <typename T, bool PH, bool PRO, int NCOL>
 hipError_t launch_decode_t(int B, int H, int Dk, int Dv, const void* q, const void* k,
                            const void* v, const float* alpha, const float* theta,
-                           const float* beta, float* state, void* out, hipStream_t stream)
+                           const float* beta, float* state, void* out, hipStream_t stream,
+                           const DecodePro& pro)
 {
     const int BH = B * H;
     // (b h) rounded up to whole XCD rounds, times the column slices
@@ -192,22 +222,23 @@ hipError_t launch_decode_t(int B, int H, int Dk, int Dv, const void* q, const vo
     const T* vv = static_cast<const T*>(v);
     T* oo = static_cast<T*>(out);
     switch (Dk) {
-    case 16: return launch_kernel(decode_kernel<T, 16, NCOL, decode_threads(16, NCOL), PH>, grid,
-                                   dim3(decode_threads(16, NCOL)), 0, stream, qq, kk, vv, alpha, theta, beta, state, oo, BH, Dv);
-    case 32: return launch_kernel(decode_kernel<T, 32, NCOL, decode_threads(32, NCOL), PH>, grid,
-                                   dim3(decode_threads(32, NCOL)), 0, stream, qq, kk, vv, alpha, theta, beta, state, oo, BH, Dv);
-    case 64: return launch_kernel(decode_kernel<T, 64, NCOL, decode_threads(64, NCOL), PH>, grid,
-                                   dim3(decode_threads(64, NCOL)), 0, stream, qq, kk, vv, alpha, theta, beta, state, oo, BH, Dv);
-    case 128: return launch_kernel(decode_kernel<T, 128, NCOL, decode_threads(128, NCOL), PH>, grid,
-                                   dim3(decode_threads(128, NCOL)), 0, stream, qq, kk, vv, alpha, theta, beta, state, oo, BH, Dv);
+    case 16: return launch_kernel(decode_kernel<T, 16, NCOL, decode_threads(16, NCOL), PH, PRO>, grid,
+                                   dim3(decode_threads(16, NCOL)), 0, stream, qq, kk, vv, alpha, theta, beta, state, oo, BH, Dv, pro);
+    case 32: return launch_kernel(decode_kernel<T, 32, NCOL, decode_threads(32, NCOL), PH, PRO>, grid,
+                                   dim3(decode_threads(32, NCOL)), 0, stream, qq, kk, vv, alpha, theta, beta, state, oo, BH, Dv, pro);
+    case 64: return launch_kernel(decode_kernel<T, 64, NCOL, decode_threads(64, NCOL), PH, PRO>, grid,
+                                   dim3(decode_threads(64, NCOL)), 0, stream, qq, kk, vv, alpha, theta, beta, state, oo, BH, Dv, pro);
+    case 128: return launch_kernel(decode_kernel<T, 128, NCOL, decode_threads(128, NCOL), PH, PRO>, grid,
+                                   dim3(decode_threads(128, NCOL)), 0, stream, qq, kk, vv, alpha, theta, beta, state, oo, BH, Dv, pro);
     default: return hipErrorInvalidValue;
     }
 }
 
-template <typename T, bool PH>
+template <typename T, bool PH, bool PRO>
 hipError_t launch_decode_cols(int B, int H, int Dk, int Dv, const void* q, const void* k,
                               const void* v, const float* alpha, const float* theta,
-                              const float* beta, float* state, void* out, hipStream_t stream)
+                              const float* beta, float* state, void* out, hipStream_t stream,
+                              const DecodePro& pro)
 {
     // 64 columns (256-byte row segments) where Dv allows, else 32, else 16.
     // Measured (B=256, H=32, d=128, in-place fp32 state, 1.086 GB per step):
@@ -215,26 +246,33 @@ hipError_t launch_decode_cols(int B, int H, int Dk, int Dv, const void* q, const
     // threads, 181 us at 32 / 256, 185 us at 128 / 1024, 217 us at 16 / 256
     // (half-line row segments), 429 us at 8 / 128.
     if (Dv % 64 == 0)
-        return launch_decode_t<T, PH, 64>(B, H, Dk, Dv, q, k, v, alpha, theta, beta, state, out, stream);
+        return launch_decode_t<T, PH, PRO, 64>(B, H, Dk, Dv, q, k, v, alpha, theta, beta, state, out, stream, pro);
     if (Dv % 32 == 0)
-        return launch_decode_t<T, PH, 32>(B, H, Dk, Dv, q, k, v, alpha, theta, beta, state, out, stream);
-    return launch_decode_t<T, PH, 16>(B, H, Dk, Dv, q, k, v, alpha, theta, beta, state, out, stream);
+        return launch_decode_t<T, PH, PRO, 32>(B, H, Dk, Dv, q, k, v, alpha, theta, beta, state, out, stream, pro);
+    return launch_decode_t<T, PH, PRO, 16>(B, H, Dk, Dv, q, k, v, alpha, theta, beta, state, out, stream, pro);
 }
 
 }  // namespace
 
 hipError_t launch_decode(IoType io, int B, int H, int Dk, int Dv, const void* q, const void* k,
                          const void* v, const float* alpha, const float* beta, float* state,
-                         void* out, hipStream_t stream, const float* theta)
+                         void* out, hipStream_t stream, const float* theta, const DecodePro* pro)
 {
+    const DecodePro none{};
+    if (pro) {
+        if (theta) return hipErrorInvalidValue;
+        if (io == IoType::F32)
+            return launch_decode_cols<float, false, true>(B, H, Dk, Dv, q, k, v, alpha, nullptr, beta, state, out, stream, *pro);
+        return launch_decode_cols<bf16_t, false, true>(B, H, Dk, Dv, q, k, v, alpha, nullptr, beta, state, out, stream, *pro);
+    }
     if (theta) {
         if (io == IoType::F32)
-            return launch_decode_cols<float, true>(B, H, Dk, Dv, q, k, v, alpha, theta, beta, state, out, stream);
-        return launch_decode_cols<bf16_t, true>(B, H, Dk, Dv, q, k, v, alpha, theta, beta, state, out, stream);
+            return launch_decode_cols<float, true, false>(B, H, Dk, Dv, q, k, v, alpha, theta, beta, state, out, stream, none);
+        return launch_decode_cols<bf16_t, true, false>(B, H, Dk, Dv, q, k, v, alpha, theta, beta, state, out, stream, none);
     }
     if (io == IoType::F32)
-        return launch_decode_cols<float, false>(B, H, Dk, Dv, q, k, v, alpha, nullptr, beta, state, out, stream);
-    return launch_decode_cols<bf16_t, false>(B, H, Dk, Dv, q, k, v, alpha, nullptr, beta, state, out, stream);
+        return launch_decode_cols<float, false, false>(B, H, Dk, Dv, q, k, v, alpha, nullptr, beta, state, out, stream, none);
+    return launch_decode_cols<bf16_t, false, false>(B, H, Dk, Dv, q, k, v, alpha, nullptr, beta, state, out, stream, none);
 }
 
 }  // namespace kda

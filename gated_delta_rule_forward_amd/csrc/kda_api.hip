@@ -451,7 +451,7 @@ size_t varlen_layout(int N, int total_T, int H, int Dk, int Dv, int chunk, IoTyp
 kda_status_t decode_step(const void* q, const void* k, const void* v, const float* alpha,
                          const float* theta, const float* beta, float* state, void* out, int B,
                          int H, int Dk, int Dv, kda_dtype_t dtype, kda_mode_t mode,
-                         unsigned flags, void* stream)
+                         unsigned flags, void* stream, const kda_prologue_t* pro = nullptr)
 {
     if (B < 1 || H < 1) return KDA_ERR_BAD_SHAPE;
     if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERR_UNSUPPORTED;
@@ -460,6 +460,7 @@ kda_status_t decode_step(const void* q, const void* k, const void* v, const floa
     if (flags & ~kKnownFlags) return KDA_ERR_UNSUPPORTED;
     if ((long long)B * H > 0x7fffffffLL) return KDA_ERR_BAD_SHAPE;
     if (!q || !k || !v || !alpha || !beta || !state || !out) return KDA_ERR_NULL_POINTER;
+    if (pro && !prologue_ok(*pro, mode)) return KDA_ERR_UNSUPPORTED;
     const size_t e = elem_size(dtype), nbh = (size_t)B * H;
     // the state is streamed with 16-byte vectors; everything else element-wise
     if (!aligned16(state)) return KDA_ERR_MISALIGNED;
@@ -484,8 +485,12 @@ kda_status_t decode_step(const void* q, const void* k, const void* v, const floa
         if (stage_begin() != hipSuccess) return KDA_ERR_HIP;
     }
     if (rec.mark("decode") != hipSuccess) return KDA_ERR_HIP;
+    kda::DecodePro dp{};
+    if (pro)
+        dp = kda::DecodePro{pro->alpha_min, pro->alpha_max - pro->alpha_min, pro->beta_max, pro->eps,
+                            pro->normalize_q};
     if (kda::launch_decode(dtype == KDA_DTYPE_F32 ? IoType::F32 : IoType::BF16, B, H, Dk, Dv, q, k,
-                           v, alpha, beta, state, out, s, theta) != hipSuccess)
+                           v, alpha, beta, state, out, s, theta, pro ? &dp : nullptr) != hipSuccess)
         return KDA_ERR_HIP;
     return rec.done() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
@@ -1083,6 +1088,17 @@ kda_status_t kda_decode_step_phase(const void* q, const void* k, const void* v,
     if (!theta) return KDA_ERR_NULL_POINTER;
     return decode_step(q, k, v, alpha, theta, beta, state, out, B, H, Dk, Dv, dtype, mode, flags,
                        stream);
+}
+
+kda_status_t kda_decode_step_prologue(const void* q_raw, const void* k_raw, const void* v,
+                                      const float* gate, const float* beta_logit,
+                                      const kda_prologue_t* prologue, float* state, void* out,
+                                      int B, int H, int Dk, int Dv, kda_dtype_t dtype,
+                                      kda_mode_t mode, unsigned flags, void* stream)
+{
+    if (!prologue) return KDA_ERR_NULL_POINTER;
+    return decode_step(q_raw, k_raw, v, gate, nullptr, beta_logit, state, out, B, H, Dk, Dv, dtype,
+                       mode, flags, stream, prologue);
 }
 
 kda_status_t kda_gate_prep(const float* alpha, float* L, unsigned char* meta, float* gend, int B,

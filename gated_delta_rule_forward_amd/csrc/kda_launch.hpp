@@ -67,10 +67,18 @@ hipError_t launch_state_copy(const float* S0, float* ST, size_t n, hipStream_t s
 hipError_t launch_varlen_table(const int* cu, int N, int total_T, int C, int umax, int* cu_s,
                                int* cs, hipStream_t stream);
 
+// decode from raw inputs: alpha and beta hold logits, q and k are normalised
+// in the kernel (alpha = amin + arange sigmoid, beta = bmax sigmoid,
+// x / (|x| + eps), q only when normq)
+struct DecodePro {
+    float amin, arange, bmax, eps;
+    int normq;
+};
+
 hipError_t launch_decode(IoType io, int B, int H, int Dk, int Dv, const void* q,
                          const void* k, const void* v, const float* alpha,
                          const float* beta, float* state, void* out, hipStream_t stream,
-                         const float* theta = nullptr);
+                         const float* theta = nullptr, const DecodePro* pro = nullptr);
 
 struct BwdChainArgs;
 struct BwdLocalArgs;

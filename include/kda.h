@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 10
+#define KDA_ABI_VERSION 11
 
 typedef enum {
     KDA_OK = 0,
@@ -273,6 +273,26 @@ kda_status_t kda_decode_step(const void* q, const void* k, const void* v,
                              int B, int H, int Dk, int Dv,
                              kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
                              void* stream);
+
+/*
+ * kda_decode_step from raw inputs through the parameterisation of
+ * kda_prologue_t ("Semidirect Fourier Delta Attention" §3 eqs. (15), (17),
+ * (18)): gate takes alpha's place ([B,H,Dk] fp32 logits), beta_logit beta's
+ * ([B,H] fp32), q_raw and k_raw those of q and k, so that
+ *   alpha = alpha_min + (alpha_max - alpha_min) sigmoid(gate),
+ *   beta = beta_max sigmoid(beta_logit),  k = k_raw / (|k_raw| + eps)
+ * (q likewise when normalize_q; a zero vector with eps = 0 stays zero), with
+ * the normalised q, k rounded to dtype once, as kda_chunk_forward_prologue
+ * does.  Every other argument, rule and error is that of kda_decode_step;
+ * prologue == NULL is KDA_ERR_NULL_POINTER and parameters outside the
+ * mode's ranges are KDA_ERR_UNSUPPORTED.  Same single read and write of the
+ * state: the transforms run where the kernel loads the inputs.
+ */
+kda_status_t kda_decode_step_prologue(const void* q_raw, const void* k_raw, const void* v,
+                                      const float* gate, const float* beta_logit,
+                                      const kda_prologue_t* prologue, float* state, void* out,
+                                      int B, int H, int Dk, int Dv, kda_dtype_t dtype,
+                                      kda_mode_t mode, unsigned flags, void* stream);
 
 /*
  * kda_decode_step for the phase variant (see kda_chunk_forward_phase):

@@ -33,7 +33,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     syms = declared_symbols()
     assert {"kda_chunk_forward", "kda_chunk_forward_states", "kda_chunk_forward_prologue",
-            "kda_chunk_forward_phase", "kda_decode_step_phase", "kda_chunk_forward_varlen", "kda_decode_step", "kda_chunk_forward_workspace_size",
+            "kda_chunk_forward_phase", "kda_decode_step_phase", "kda_chunk_forward_varlen", "kda_decode_step",
+            "kda_decode_step_prologue", "kda_chunk_forward_workspace_size",
             "kda_chunk_backward", "kda_chunk_backward_workspace_size",
             "kda_chunk_backward_prologue", "kda_chunk_backward_prologue_workspace_size",
             "kda_chunk_backward_varlen", "kda_chunk_backward_varlen_workspace_size",
@@ -43,7 +44,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 10
+    assert lib.kda_abi_version() == 11
     for s in range(8):
         assert lib.kda_status_string(s)
     assert lib.kda_status_string(99) == b"unknown status"
@@ -240,6 +241,25 @@ def test_decode_validation(lib):
     assert dec(ptrs=a[:5] + [ctypes.c_void_p(a[5].value + 4)] + a[6:]) == MISAL   # state
     assert dec(ptrs=a[:4] + [ctypes.c_void_p(a[4].value + 2)] + a[5:]) == MISAL   # beta
     assert dec(ptrs=a[:6] + [a[5]]) == ALIAS          # out == state
+
+
+def test_decode_prologue_validation(lib):
+    f = Fake()
+    a = [f() for _ in range(7)]      # q_raw, k_raw, v, gate, beta_logit, state, out
+
+    def dec(ptrs=a, pro=kda.Prologue(-1.0, 1.0, 2.0, 1e-6, 1), mode=1, Dk=16):
+        p = None if pro is None else ctypes.byref(pro)
+        return lib.kda_decode_step_prologue(*ptrs[:5], p, *ptrs[5:], 2, 2, Dk, 16, BF16, mode, 0,
+                                            None)
+
+    assert dec(pro=None) == NULLP
+    assert dec(ptrs=[None] + a[1:]) == NULLP
+    assert dec(Dk=48) == UNSUP
+    assert dec(mode=0) == UNSUP                                             # CKDA range in KDA mode
+    assert dec(pro=kda.Prologue(0.5, 0.2, 1.0, 0.0, 1), mode=1) == UNSUP    # alpha_min > alpha_max
+    assert dec(pro=kda.Prologue(-1.0, 1.0, 2.0, -1.0, 1)) == UNSUP         # eps < 0
+    assert dec(ptrs=a[:5] + [ctypes.c_void_p(a[5].value + 4)] + a[6:]) == MISAL   # state
+    assert dec(ptrs=a[:6] + [a[5]]) == ALIAS                                # out == state
 
 
 def test_gate_prep_validation(lib):

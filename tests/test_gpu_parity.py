@@ -713,3 +713,41 @@ def test_forward_phase_parts():
     say(f"  err out {eo:.3e} state {es:.3e}")
     assert eo <= TOL[w.dtype] and es <= TOL[w.dtype]
     assert torch.equal(out, out1) and torch.equal(st, st1)
+
+
+@pytest.mark.parametrize("dt,Dk,Dv,mode,pro", [
+    (torch.bfloat16, 128, 128, workloads.CKDA, (-1.0, 1.0, 2.0, 1e-6, True)),
+    (torch.float32, 64, 48, workloads.KDA, (0.0, 1.0, 1.0, 1e-6, False)),
+    (torch.bfloat16, 32, 80, workloads.CKDA, (-1.0, 1.0, 2.0, 0.0, True)),
+])
+def test_decode_prologue(dt, Dk, Dv, mode, pro):
+    """kda_decode_step_prologue: six steps from raw inputs (gate and beta
+    logits, unnormalised q, k; some gates at -200, i.e. alpha = alpha_min)
+    against the oracle's prologue recurrence over the same tokens."""
+    amin, amax, bmax, eps, normq = pro
+    say(f"[decode prologue] {dt} Dk={Dk} Dv={Dv} mode={mode} pro={pro}")
+    g = torch.Generator().manual_seed(Dk * 7 + Dv)
+    B, H, N = 3, 2, 6
+    q = torch.randn(N, B, H, Dk, generator=g).to(dt)
+    k = torch.randn(N, B, H, Dk, generator=g).to(dt)
+    v = torch.randn(N, B, H, Dv, generator=g).to(dt)
+    gate = 2.0 * torch.randn(N, B, H, Dk, generator=g)
+    gate[torch.rand(N, B, H, Dk, generator=g) < 0.05] = -200.0
+    blog = torch.randn(N, B, H, generator=g)
+    S0 = 0.3 * torch.randn(B, H, Dk, Dv, generator=g)
+    S = S0.to(DEV).contiguous()
+    outs = []
+    for t in range(N):
+        outs.append(kda.decode_step_prologue(q[t].to(DEV), k[t].to(DEV), v[t].to(DEV),
+                                             gate[t].to(DEV), blog[t].to(DEV).contiguous(), S,
+                                             alpha_min=amin, alpha_max=amax, beta_max=bmax,
+                                             eps=eps, normalize_q=normq, mode=mode))
+    torch.cuda.synchronize()
+    perm = lambda x: np32(x.permute(1, 0, *range(2, x.dim())))
+    o_ref, s_ref = oracle.forward_prologue(perm(q), perm(k), perm(v), perm(gate), perm(blog),
+                                           np32(S0), alpha_min=amin, alpha_max=amax,
+                                           beta_max=bmax, eps=eps, normalize_q=normq)
+    o_gpu = np.stack([np32(o) for o in outs], axis=1)
+    eo, es = slice_err_out(o_gpu, o_ref), slice_err_state(np32(S), s_ref)
+    say(f"  err out {eo:.3e} state {es:.3e}")
+    assert eo <= TOL[dt] and es <= TOL[dt]
