@@ -261,8 +261,8 @@ def main():
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(heads shard with no communication; see the design notes).", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(heads would shard across GPUs with no communication).", file=sys.stderr)
         sys.exit(2)
 
     import torch
