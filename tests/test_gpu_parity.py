@@ -41,8 +41,8 @@ def run_gpu(inp, chunk, mode, **kw):
 
 # (name, base workload, overrides)
 SMALL = [
-    ("cfg0_kda_fp32_tiny", 0, {}),
-    ("cfg1_ckda_fp32", 1, {}),
+    ("kda_fp32_tiny_T64", 0, {}),
+    ("ckda_fp32_B2_H4_T1024", 1, {}),
     ("f32_ckda_dk32_dv48_c32_T67_s0", 1, dict(B=1, H=3, T=67, D=32, chunk=32, s0_std=0.5)),
     ("f32_kda_d64_c64_T5", 0, dict(B=2, H=2, T=5, D=64, chunk=64)),
     ("f32_ckda_d16_c16_T1", 1, dict(B=1, H=1, T=1, D=16, chunk=16)),
@@ -375,10 +375,10 @@ def test_forward_segmented_chunk_states_and_phase():
     assert eo <= 1e-4 and es <= 1e-4
 
 
-def test_forward_cfg2_full():
+def test_forward_kda_bf16_prefill_full():
     """KDA bf16 prefill, B=1 H=32 T=8192 d=128 chunk=64, every head."""
     w = workloads.workload(2)
-    say(f"[forward] cfg2 full {w}")
+    say(f"[forward] kda_bf16_prefill full {w}")
     inp = workloads.make_prefill(w, device=DEV)
     out, st = run_gpu(inp, w.chunk, w.mode)
     o_ref, s_ref = run_oracle(inp)
@@ -387,11 +387,11 @@ def test_forward_cfg2_full():
     assert eo <= 2e-2 and es <= 2e-2
 
 
-def test_forward_cfg3_sampled_heads():
+def test_forward_ckda_long_ctx_sampled_heads():
     """CKDA bf16 long context, B=1 H=16 T=65536 d=128, S0 ~ N(0, 0.02^2): the GPU
     runs all heads; the oracle checks a sample of heads (heads are independent)."""
     w = workloads.workload(3)
-    say(f"[forward] cfg3 full, sampled heads {w}")
+    say(f"[forward] ckda_bf16_long_ctx full, sampled heads {w}")
     inp = workloads.make_prefill(w, device=DEV)
     out, st = run_gpu(inp, w.chunk, w.mode)
     heads = [0, 7, 15]
@@ -435,11 +435,11 @@ def test_decode_small(name, dt, B, H, Dk, Dv, N):
     assert eo <= TOL[dt] and es <= TOL[dt]
 
 
-def test_decode_cfg4_sampled():
+def test_decode_ckda_bf16_decode_sampled():
     """CKDA decode, B=256 H=32 d=128, state [256,32,128,128] resident and updated
     in place for 1000 steps; the oracle follows a sample of (b, h) pairs."""
     w = workloads.workload(4)
-    say(f"[decode] cfg4 full, 1000 steps, sampled pairs")
+    say(f"[decode] ckda_bf16_decode full, 1000 steps, sampled pairs")
     inp = workloads.make_decode(w, device=DEV)
     S = inp["S0"].clone()
     N = w.steps
