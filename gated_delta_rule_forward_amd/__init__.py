@@ -21,6 +21,8 @@ __all__ = [
     "KDA", "CKDA", "KdaError", "library_path", "load", "abi_version", "workspace_size",
     "chunk_forward", "chunk_forward_prologue", "chunk_forward_varlen", "chunk_forward_phase",
     "decode_step", "decode_step_phase", "decode_step_prologue", "gate_prep", "last_stage_times",
+    "chunk_backward", "chunk_backward_prologue", "chunk_backward_varlen",
+    "chunk_backward_varlen_prologue", "backward_workspace_size",
     "STAGE_EVENTS", "NO_SEGMENTS", "SINGLE_STREAM",
 ]
 
@@ -105,6 +107,12 @@ def load():
     lib.kda_chunk_backward_varlen_workspace_size.restype = i
     lib.kda_chunk_backward_varlen.argtypes = [vp] * 6 + [i] + [vp] * 9 + [i] * 7 + [u, vp, sz, vp]
     lib.kda_chunk_backward_varlen.restype = i
+    lib.kda_chunk_backward_varlen_prologue_workspace_size.argtypes = [i, i, i, i, i, i, i,
+                                                                      ctypes.POINTER(sz)]
+    lib.kda_chunk_backward_varlen_prologue_workspace_size.restype = i
+    lib.kda_chunk_backward_varlen_prologue.argtypes = [vp] * 6 + [i] + [vp] * 3 + \
+        [ctypes.POINTER(Prologue)] + [vp] * 6 + [i] * 7 + [u, vp, sz, vp]
+    lib.kda_chunk_backward_varlen_prologue.restype = i
     lib.kda_gate_prep.argtypes = [vp] * 4 + [i] * 5 + [vp]
     lib.kda_gate_prep.restype = i
     lib.kda_last_stage_times.argtypes = [ctypes.POINTER(ctypes.c_float),
@@ -485,6 +493,53 @@ def chunk_backward_varlen(q, k, v, alpha, beta, cu_seqlens, d_out, initial_state
         total_T, H, Dk, Dv, chunk, _DT[q.dtype], mode, flags, _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream))
     _check("kda_chunk_backward_varlen", st)
+    return g
+
+
+def chunk_backward_varlen_prologue(q_raw, k_raw, v, gate, beta_logit, cu_seqlens, d_out,
+                                   initial_state=None, d_final_state=None, *, alpha_min: float,
+                                   alpha_max: float, beta_max: float, eps: float = 1e-6,
+                                   normalize_q: bool = True, chunk: int = 64, mode: int = CKDA,
+                                   want_d_initial_state: bool = True, workspace=None,
+                                   stream=None, flags: int = 0):
+    """Raw-input backward of a packed batch (kda_chunk_backward_varlen_prologue):
+    layouts as chunk_backward_varlen, inputs and parameterisation as
+    chunk_backward_prologue.  Returns a dict dq, dk, dv (q_raw's dtype), d_gate,
+    d_beta_logit and d_initial_state ([N,H,Dk,Dv] fp32; None unless wanted)."""
+    lib = load()
+    H, Dk = q_raw.shape[-2], q_raw.shape[-1]
+    total_T = q_raw.shape[-3]
+    Dv = v.shape[-1]
+    N = cu_seqlens.numel() - 1
+    if cu_seqlens.dtype != torch.int32 or N < 1:
+        raise ValueError("cu_seqlens must be an int32 tensor of N + 1 offsets, N >= 1")
+    dev = q_raw.device
+    g = {"dq": torch.empty(q_raw.shape, dtype=q_raw.dtype, device=dev),
+         "dk": torch.empty(k_raw.shape, dtype=q_raw.dtype, device=dev),
+         "dv": torch.empty(v.shape, dtype=q_raw.dtype, device=dev),
+         "d_gate": torch.empty(gate.shape, dtype=torch.float32, device=dev),
+         "d_beta_logit": torch.empty(beta_logit.shape, dtype=torch.float32, device=dev),
+         "d_initial_state": (torch.empty((N, H, Dk, Dv), dtype=torch.float32, device=dev)
+                             if want_d_initial_state else None)}
+    if workspace is None:
+        n = ctypes.c_size_t(0)
+        _check("kda_chunk_backward_varlen_prologue_workspace_size",
+               lib.kda_chunk_backward_varlen_prologue_workspace_size(
+                   N, total_T, H, Dk, Dv, chunk, _DT[q_raw.dtype], ctypes.byref(n)))
+        workspace = torch.empty(max(n.value, 1), dtype=torch.uint8, device=dev)
+    _dev(q_raw, k_raw, v, gate, beta_logit, cu_seqlens, d_out, initial_state, d_final_state,
+         workspace, *g.values())
+    if (q_raw.dtype not in _DT or k_raw.dtype != q_raw.dtype or v.dtype != q_raw.dtype
+            or d_out.dtype != q_raw.dtype):
+        raise ValueError("q_raw, k_raw, v and d_out must share one dtype (float32 or bfloat16)")
+    pro = Prologue(alpha_min, alpha_max, beta_max, eps, int(bool(normalize_q)))
+    st = lib.kda_chunk_backward_varlen_prologue(
+        _ptr(q_raw), _ptr(k_raw), _ptr(v), _ptr(gate), _ptr(beta_logit), _ptr(cu_seqlens), N,
+        _ptr(initial_state), _ptr(d_out), _ptr(d_final_state), ctypes.byref(pro), _ptr(g["dq"]),
+        _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["d_gate"]), _ptr(g["d_beta_logit"]),
+        _ptr(g["d_initial_state"]), total_T, H, Dk, Dv, chunk, _DT[q_raw.dtype], mode, flags,
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("kda_chunk_backward_varlen_prologue", st)
     return g
 
 

@@ -719,6 +719,25 @@ size_t backward_prologue_layout(int B, int T, int H, int Dk, int Dv, int chunk, 
     return n;
 }
 
+// the same six regions after a packed batch's backward workspace
+size_t backward_varlen_prologue_layout(int N, int total_T, int H, int Dk, int Dv, int chunk,
+                                       IoType io, size_t xo[6])
+{
+    size_t off[kda::kWorkspaceRegions], boff[kBwdRegions], toff = 0;
+    size_t n = backward_varlen_layout(N, total_T, H, Dk, Dv, chunk, io, off, boff, &toff);
+    const size_t ntok = (size_t)total_T * H, e = io == IoType::F32 ? 4 : 2;
+    const size_t sz[6] = {ntok * Dk * e, ntok * Dk * e, ntok * Dk * 4, ntok * 4, ntok * Dk * e,
+                          ntok * Dk * e};
+    for (int i = 0; i < 6; ++i) {
+        xo[i] = n;
+        n += (sz[i] + 255) & ~size_t(255);
+    }
+    return n;
+}
+
+// raw-input backward of a dense batch, or of a packed batch when cu_seqlens
+// is given (then B is ignored, N sequences share the T = total_T rows and the
+// states are per sequence)
 kda_status_t chunk_backward_prologue(const void* q_raw, const void* k_raw, const void* v,
                                      const float* gate, const float* beta_logit,
                                      const float* initial_state, const void* d_out,
@@ -727,9 +746,14 @@ kda_status_t chunk_backward_prologue(const void* q_raw, const void* k_raw, const
                                      float* d_beta_logit, float* d_initial_state, int B, int T,
                                      int H, int Dk, int Dv, int chunk, kda_dtype_t dtype,
                                      kda_mode_t mode, unsigned flags, void* workspace,
-                                     size_t workspace_bytes, void* stream)
+                                     size_t workspace_bytes, void* stream,
+                                     const int* cu_seqlens = nullptr, int N = 0)
 {
-    kda_status_t st = check_backward_shape(B, T, H, Dk, Dv, chunk, dtype);
+    const bool packed = cu_seqlens != nullptr;
+    kda_status_t st = packed ? check_varlen_shape(N, T, H, Dk, Dv, chunk, dtype) : KDA_OK;
+    if (st != KDA_OK) return st;
+    if (packed) B = 1;
+    st = check_backward_shape(B, T, H, Dk, Dv, chunk, dtype);
     if (st != KDA_OK) return st;
     if (mode != KDA_MODE_KDA && mode != KDA_MODE_CKDA) return KDA_ERR_UNSUPPORTED;
     if (flags & ~KDA_FLAG_STAGE_EVENTS) return KDA_ERR_UNSUPPORTED;
@@ -740,13 +764,16 @@ kda_status_t chunk_backward_prologue(const void* q_raw, const void* k_raw, const
         return KDA_ERR_NULL_POINTER;
     const IoType io = dtype == KDA_DTYPE_F32 ? IoType::F32 : IoType::BF16;
     size_t xo[6];
-    const size_t ws_need = T == 0 ? 0 : backward_prologue_layout(B, T, H, Dk, Dv, chunk, io, xo);
+    const size_t ws_need = T == 0 ? 0
+                         : packed ? backward_varlen_prologue_layout(N, T, H, Dk, Dv, chunk, io, xo)
+                                  : backward_prologue_layout(B, T, H, Dk, Dv, chunk, io, xo);
     if (T > 0 && !workspace) return KDA_ERR_NULL_POINTER;
     if (workspace_bytes < ws_need) return KDA_ERR_WORKSPACE_TOO_SMALL;
 
     const size_t e = elem_size(dtype);
     const size_t ntok = (size_t)B * T * H;
-    const size_t nstate = (size_t)B * H * Dk * Dv * 4;
+    const size_t nstate = (size_t)(packed ? N : B) * H * Dk * Dv * 4;
+    if (packed && !aligned(cu_seqlens, 4)) return KDA_ERR_MISALIGNED;
     const void* vec[] = {q_raw, k_raw, d_out, gate, workspace, dq_raw, dk_raw, d_gate};
     for (const void* p : vec)
         if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
@@ -759,7 +786,8 @@ kda_status_t chunk_backward_prologue(const void* q_raw, const void* k_raw, const
     const R in[] = {{q_raw, ntok * Dk * e}, {k_raw, ntok * Dk * e}, {v, ntok * Dv * e},
                     {gate, ntok * Dk * 4}, {beta_logit, ntok * 4},
                     {initial_state, initial_state ? nstate : 0}, {d_out, ntok * Dv * e},
-                    {d_final_state, d_final_state ? nstate : 0}};
+                    {d_final_state, d_final_state ? nstate : 0},
+                    {cu_seqlens, packed ? ((size_t)N + 1) * 4 : 0}};
     const R outs[] = {{dq_raw, ntok * Dk * e}, {dk_raw, ntok * Dk * e}, {dv, ntok * Dv * e},
                       {d_gate, ntok * Dk * 4}, {d_beta_logit, ntok * 4},
                       {d_initial_state, d_initial_state ? nstate : 0}, {workspace, ws_need}};
@@ -778,10 +806,11 @@ kda_status_t chunk_backward_prologue(const void* q_raw, const void* k_raw, const
         lock.lock();
         if (stage_begin() != hipSuccess) return KDA_ERR_HIP;
     }
+    const int Bs = packed ? N : B;      // batch entries of the states
     if (T == 0)
         return backward_enqueue(nullptr, nullptr, nullptr, nullptr, nullptr, initial_state, nullptr,
                                 d_final_state, nullptr, nullptr, nullptr, nullptr, nullptr,
-                                d_initial_state, B, T, H, Dk, Dv, chunk, dtype, mode, workspace,
+                                d_initial_state, Bs, T, H, Dk, Dv, chunk, dtype, mode, workspace,
                                 rec, s);
     unsigned char* w = static_cast<unsigned char*>(workspace);
     void* qh = w + xo[0];
@@ -798,8 +827,8 @@ kda_status_t chunk_backward_prologue(const void* q_raw, const void* k_raw, const
     if (kda::launch_backward_prologue(false, io, Dk, pa, s) != hipSuccess) return KDA_ERR_HIP;
     if (rec.done() != hipSuccess) return KDA_ERR_HIP;
     st = backward_enqueue(qh, kh, v, al, be, initial_state, d_out, d_final_state, dqh, dkh, dv,
-                          d_gate, d_beta_logit, d_initial_state, B, T, H, Dk, Dv, chunk, dtype,
-                          mode, workspace, rec, s);
+                          d_gate, d_beta_logit, d_initial_state, Bs, T, H, Dk, Dv, chunk, dtype,
+                          mode, workspace, rec, s, cu_seqlens);
     if (st != KDA_OK) return st;
     if (rec.mark("prologue_out") != hipSuccess) return KDA_ERR_HIP;
     if (kda::launch_backward_prologue(true, io, Dk, pa, s) != hipSuccess) return KDA_ERR_HIP;
@@ -1162,6 +1191,39 @@ kda_status_t kda_chunk_backward_prologue_workspace_size(int B, int T, int H, int
                     : backward_prologue_layout(B, T, H, Dk, Dv, chunk,
                                                dtype == KDA_DTYPE_F32 ? IoType::F32 : IoType::BF16, xo);
     return KDA_OK;
+}
+
+kda_status_t kda_chunk_backward_varlen_prologue_workspace_size(int N, int total_T, int H, int Dk,
+                                                               int Dv, int chunk,
+                                                               kda_dtype_t dtype, size_t* bytes)
+{
+    if (!bytes) return KDA_ERR_NULL_POINTER;
+    kda_status_t st = check_varlen_shape(N, total_T, H, Dk, Dv, chunk, dtype);
+    if (st != KDA_OK) return st;
+    st = check_backward_shape(1, total_T, H, Dk, Dv, chunk, dtype);
+    if (st != KDA_OK) return st;
+    size_t xo[6];
+    *bytes = total_T == 0 ? 0
+                          : backward_varlen_prologue_layout(N, total_T, H, Dk, Dv, chunk,
+                                                            dtype == KDA_DTYPE_F32 ? IoType::F32
+                                                                                   : IoType::BF16,
+                                                            xo);
+    return KDA_OK;
+}
+
+kda_status_t kda_chunk_backward_varlen_prologue(
+    const void* q_raw, const void* k_raw, const void* v, const float* gate,
+    const float* beta_logit, const int* cu_seqlens, int N, const float* initial_state,
+    const void* d_out, const float* d_final_state, const kda_prologue_t* prologue, void* dq_raw,
+    void* dk_raw, void* dv, float* d_gate, float* d_beta_logit, float* d_initial_state,
+    int total_T, int H, int Dk, int Dv, int chunk, kda_dtype_t dtype, kda_mode_t mode,
+    unsigned flags, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!cu_seqlens) return KDA_ERR_NULL_POINTER;
+    return chunk_backward_prologue(q_raw, k_raw, v, gate, beta_logit, initial_state, d_out,
+                                   d_final_state, prologue, dq_raw, dk_raw, dv, d_gate, d_beta_logit,
+                                   d_initial_state, 1, total_T, H, Dk, Dv, chunk, dtype, mode, flags,
+                                   workspace, workspace_bytes, stream, cu_seqlens, N);
 }
 
 kda_status_t kda_chunk_backward_prologue(const void* q_raw, const void* k_raw, const void* v,

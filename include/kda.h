@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 11
+#define KDA_ABI_VERSION 12
 
 typedef enum {
     KDA_OK = 0,
@@ -392,6 +392,25 @@ kda_status_t kda_chunk_backward_varlen(const void* q, const void* k, const void*
                                        int chunk, kda_dtype_t dtype, kda_mode_t mode,
                                        unsigned flags, void* workspace, size_t workspace_bytes,
                                        void* stream);
+
+/*
+ * The raw-input backward (kda_chunk_backward_prologue) of a packed batch
+ * (kda_chunk_backward_varlen): gate, beta_logit, q_raw, k_raw, v, d_out and
+ * their gradients are [1, total_T, H, *] with the N sequences' rows given by
+ * the device table cu_seqlens [N+1]; initial_state, d_final_state and
+ * d_initial_state are per sequence [N,H,Dk,Dv].  Every other argument, rule
+ * and error is that of the two; cu_seqlens == NULL is KDA_ERR_NULL_POINTER.
+ */
+kda_status_t kda_chunk_backward_varlen_prologue_workspace_size(int N, int total_T, int H, int Dk,
+                                                               int Dv, int chunk,
+                                                               kda_dtype_t dtype, size_t* bytes);
+kda_status_t kda_chunk_backward_varlen_prologue(
+    const void* q_raw, const void* k_raw, const void* v, const float* gate,
+    const float* beta_logit, const int* cu_seqlens, int N, const float* initial_state,
+    const void* d_out, const float* d_final_state, const kda_prologue_t* prologue, void* dq_raw,
+    void* dk_raw, void* dv, float* d_gate, float* d_beta_logit, float* d_initial_state,
+    int total_T, int H, int Dk, int Dv, int chunk, kda_dtype_t dtype, kda_mode_t mode,
+    unsigned flags, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Chunk-local gate summary (log-magnitude, sign and zero form of the

@@ -38,13 +38,14 @@ def test_exports_every_declared_symbol(lib):
             "kda_chunk_backward", "kda_chunk_backward_workspace_size",
             "kda_chunk_backward_prologue", "kda_chunk_backward_prologue_workspace_size",
             "kda_chunk_backward_varlen", "kda_chunk_backward_varlen_workspace_size",
+            "kda_chunk_backward_varlen_prologue", "kda_chunk_backward_varlen_prologue_workspace_size",
             "kda_gate_prep", "kda_status_string", "kda_abi_version"} <= set(syms)
     for s in syms:
         assert hasattr(lib, s), s
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 11
+    assert lib.kda_abi_version() == 12
     for s in range(8):
         assert lib.kda_status_string(s)
     assert lib.kda_status_string(99) == b"unknown status"
@@ -359,6 +360,38 @@ def test_backward_prologue_validation(lib):
     assert bw(ptrs=mis) == MISAL
     al = list(base)
     al[11] = base[3]                                                          # d_gate == gate
+    assert bw(ptrs=al) == ALIAS
+
+
+def test_backward_varlen_prologue_validation(lib):
+    f = Fake()
+    n, m = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert lib.kda_chunk_backward_varlen_prologue_workspace_size(3, 200, 2, 64, 64, 64, F32,
+                                                                  ctypes.byref(n)) == OK
+    lib.kda_chunk_backward_varlen_workspace_size(3, 200, 2, 64, 64, 64, F32, ctypes.byref(m))
+    assert n.value > m.value                     # plus the transformed inputs and their gradients
+    assert lib.kda_chunk_backward_varlen_prologue_workspace_size(0, 200, 2, 64, 64, 64, F32,
+                                                                  ctypes.byref(n)) == SHAPE
+    need = n.value if n.value else 1 << 20
+    lib.kda_chunk_backward_varlen_prologue_workspace_size(3, 200, 2, 64, 64, 64, F32, ctypes.byref(n))
+    need = n.value
+
+    def bw(ptrs=None, pro=kda.Prologue(-1.0, 1.0, 2.0, 1e-6, 1), mode=1):
+        p = ptrs if ptrs is not None else [f() for _ in range(15)]
+        pp = None if pro is None else ctypes.byref(pro)
+        return lib.kda_chunk_backward_varlen_prologue(*p[:6], 3, *p[6:9], pp, *p[9:], 200, 2, 64,
+                                                      64, 64, F32, mode, 0, f(need + 4096), need,
+                                                      None)
+
+    base = [f() for _ in range(15)]
+    assert bw(ptrs=base[:5] + [None] + base[6:]) == NULLP             # cu_seqlens
+    assert bw(ptrs=base, pro=None) == NULLP                            # prologue
+    assert bw(ptrs=base, mode=0) == UNSUP                              # CKDA range in KDA mode
+    mis = list(base)
+    mis[5] = ctypes.c_void_p(base[5].value + 2)                        # cu_seqlens: 4-byte rule
+    assert bw(ptrs=mis) == MISAL
+    al = list(base)
+    al[9] = base[5]                                                    # dq_raw == cu_seqlens
     assert bw(ptrs=al) == ALIAS
 
 

@@ -292,3 +292,78 @@ def test_backward_varlen_uniform_equals_dense():
     for gn in ("dq", "dk", "dv", "d_alpha", "d_beta"):
         assert torch.equal(flat(gd[gn]), gv[gn]), gn
     assert torch.equal(gd["d_initial_state"], gv["d_initial_state"])
+
+
+# ---- packed batches from raw inputs (kda_chunk_backward_varlen_prologue) ---------
+VLP_CASES = [
+    ("f32_ckda_d64_c64", 1, dict(H=2, D=64, chunk=64), [70, 0, 1, 130],
+     dict(alpha_min=-1.0, alpha_max=1.0, beta_max=2.0, eps=1e-6, normalize_q=True)),
+    ("bf16_kda_d128_c32", 2, dict(H=1, chunk=32), [97, 33, 64],
+     dict(alpha_min=0.0, alpha_max=1.0, beta_max=1.0, eps=1e-6, normalize_q=False)),
+]
+
+
+@pytest.mark.parametrize("name,base,ov,lengths,pro", VLP_CASES, ids=[c[0] for c in VLP_CASES])
+def test_backward_varlen_prologue_matches_oracle(name, base, ov, lengths, pro):
+    """Every sequence of a packed batch from raw inputs against the oracle's
+    raw-input gradients of that sequence alone."""
+    N, total = len(lengths), sum(lengths)
+    w = workloads.workload(base, B=1, T=total, s0_std=None, **ov)
+    raw = workloads.make_prefill_raw(w, forget_frac=0.01)
+    gen = torch.Generator().manual_seed(91)
+    S0 = 0.3 * torch.randn((N, w.H, w.D, w.D), generator=gen)
+    dO = torch.randn((1, total, w.H, w.D), generator=gen).to(w.dtype)
+    dST = torch.randn((N, w.H, w.D, w.D), generator=gen)
+    cu = torch.tensor([0] + list(np.cumsum(lengths)), dtype=torch.int32)
+    say(f"[backward varlen prologue] {name}: lengths {lengths} {pro}")
+    d = {k: (None if v is None else v.to(DEV)) for k, v in raw.items()}
+    g = kda.chunk_backward_varlen_prologue(d["q"][0], d["k"][0], d["v"][0], d["gate"][0],
+                                           d["beta_logit"][0], cu.to(DEV), dO[0].to(DEV),
+                                           S0.to(DEV), dST.to(DEV), chunk=w.chunk, mode=w.mode,
+                                           **pro)
+    torch.cuda.synchronize()
+    c = cu.tolist()
+    worst = {}
+    pairs = (("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("d_gate", "dgate"),
+             ("d_beta_logit", "dbeta_logit"))
+    for i, L in enumerate(lengths):
+        sl = slice(c[i], c[i + 1])
+        ref = oracle.backward_prologue(np32(raw["q"][:, sl]), np32(raw["k"][:, sl]),
+                                       np32(raw["v"][:, sl]), np32(raw["gate"][:, sl]),
+                                       np32(raw["beta_logit"][:, sl]), np32(dO[:, sl]),
+                                       np32(S0[i:i + 1]), np32(dST[i:i + 1]),
+                                       nthreads=oracle_threads(), **pro)
+        e = {"d_initial_state": slice_err_state(np32(g["d_initial_state"][i:i + 1]), ref["dS0"])}
+        if L > 0:
+            for gn, rn in pairs:
+                a_, b_ = np32(g[gn][sl])[None], ref[rn]
+                if a_.ndim == 3:
+                    a_, b_ = a_[..., None], b_[..., None]
+                e[gn] = slice_err_out(a_, b_)
+        for k_, v_ in e.items():
+            worst[k_] = max(worst.get(k_, 0.0), v_)
+    say("  " + " ".join(f"{k} {v:.2e}" for k, v in worst.items()))
+    for k_, v_ in worst.items():
+        assert v_ <= TOL[w.dtype], (k_, v_)
+
+
+def test_backward_varlen_prologue_uniform_equals_dense():
+    """Equal lengths: bit-identical to kda_chunk_backward_prologue."""
+    w = workloads.workload(3, B=3, H=2, T=100, chunk=64, s0_std=0.2)
+    say(f"[backward varlen prologue] uniform vs dense {w}")
+    raw = workloads.make_prefill_raw(w, forget_frac=0.01)
+    dO, dST = workloads.make_backward_seeds(w)
+    pro = dict(alpha_min=-1.0, alpha_max=1.0, beta_max=2.0, eps=1e-6, normalize_q=True)
+    d = {k: (None if v is None else v.to(DEV)) for k, v in raw.items()}
+    gd = kda.chunk_backward_prologue(d["q"], d["k"], d["v"], d["gate"], d["beta_logit"],
+                                     dO.to(DEV), d["S0"], dST.to(DEV), chunk=64, mode=w.mode, **pro)
+    flat = lambda t: t.reshape(w.B * w.T, *t.shape[2:]).contiguous()
+    cu = torch.arange(0, (w.B + 1) * w.T, w.T, dtype=torch.int32, device=DEV)
+    gv = kda.chunk_backward_varlen_prologue(flat(d["q"]), flat(d["k"]), flat(d["v"]),
+                                            flat(d["gate"]), flat(d["beta_logit"]), cu,
+                                            flat(dO.to(DEV)), d["S0"], dST.to(DEV), chunk=64,
+                                            mode=w.mode, **pro)
+    torch.cuda.synchronize()
+    for gn in ("dq", "dk", "dv", "d_gate", "d_beta_logit"):
+        assert torch.equal(flat(gd[gn]), gv[gn]), gn
+    assert torch.equal(gd["d_initial_state"], gv["d_initial_state"])
