@@ -77,13 +77,22 @@ struct RelayoutLds {
 
 // copy NV consecutive elements (one lane's fragment slots, NV * sizeof(T)
 // bytes: 8 or 16, aligned to that size)
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+
 template <typename T, int NV>
 struct FragVec {
     static constexpr int BYTES = NV * (int)sizeof(T);
     using V = typename std::conditional<BYTES == 16, uint4, uint2>::type;
+    using NV_t = typename std::conditional<BYTES == 16, u32x4_t, u32x2_t>::type;
     __attribute__((aligned(16))) T e[NV];
-    __device__ __forceinline__ void load(const T* p) { *reinterpret_cast<V*>(e) = *reinterpret_cast<const V*>(p); }
-    __device__ __forceinline__ void store(T* p) const { *reinterpret_cast<V*>(p) = *reinterpret_cast<const V*>(e); }
+    // non-temporal: each fragment is read once and written once
+    __device__ __forceinline__ void load(const T* p) {
+        *reinterpret_cast<NV_t*>(e) = __builtin_nontemporal_load(reinterpret_cast<const NV_t*>(p));
+    }
+    __device__ __forceinline__ void store(T* p) const {
+        __builtin_nontemporal_store(*reinterpret_cast<const NV_t*>(e), reinterpret_cast<NV_t*>(p));
+    }
 };
 
 template <typename T, int C, int DK>
