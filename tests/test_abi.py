@@ -420,3 +420,22 @@ def test_backward_varlen_validation(lib):
     al = list(base)
     al[9] = base[5]                                                    # dq == cu_seqlens
     assert bw(ptrs=al) == ALIAS
+
+
+def test_forward_workspace_reserves_the_parts_state(lib):
+    """At most 128 (b, h, 16-column) chains (and more than 64, so no
+    segments) with at least 256 chunks select the parts path, whose state
+    between parts ([B H][Dk][Dv] fp32) lives in the workspace; 255 chunks do
+    not.  The query must differ by the per-chunk regions plus that buffer."""
+    def ws(T, H=9, D=128, chunk=64):
+        n = ctypes.c_size_t(0)
+        assert lib.kda_chunk_forward_workspace_size(1, T, H, D, D, chunk, BF16,
+                                                    ctypes.byref(n)) == OK
+        return n.value
+    per_chunk = ws(64 * 2) - ws(64 * 1)            # the per-unit regions of one more chunk per head
+    with_parts, without = ws(64 * 256), ws(64 * 255)
+    state = (9 * 128 * 128 * 4 + 255) // 256 * 256
+    assert with_parts - without == per_chunk + state
+    # 256 chains (H = 32): no parts, so no state buffer
+    big = lambda T: ws(T, H=32)
+    assert big(64 * 256) - big(64 * 255) == big(64 * 2) - big(64 * 1)
