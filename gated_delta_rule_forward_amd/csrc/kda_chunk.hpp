@@ -201,6 +201,10 @@ struct PrepArgs {
     // dense batches: pcn > 0 restricts a launch to chunks [pc0, pc0 + pcn) of
     // every (b, h) (launch index v -> unit part_unit(v, ...)); 0: all units
     int pc0, pcn;
+    // nonzero: the fast prep kernel writes the whole-fragment workspace blocks
+    // (P, W, U) with non-temporal stores (worth it when many chains stream the
+    // workspace; plain inputs only, not the prologue or phase variants)
+    int ntst;
 };
 
 // unit of launch index v when a launch covers chunks [pc0, pc0 + pcn) of every

@@ -48,6 +48,28 @@ namespace kda {
 namespace {
 
 constexpr int kThreads = 256;
+
+// Store of a workspace block written as whole fragments (P, W: 1 KB per
+// wavefront; U: 512 B), non-temporal in the NT kernel variant (PrepArgs ntst:
+// many chains stream the workspace; a compile-time choice, since a run-time
+// branch between two equal stores is merged into one plain store).  Measured at H=32, T=8192, d=128
+// (256 chains): prep 140 -> 144 us but chain 158 -> 145 us; with 16 chains
+// (H=2, T=65536) the chain was 4-10 % slower, so few chains keep ordinary
+// stores.  Never for the 8-byte Q*Gamma / Ktil pieces: those rely on write
+// combining in L2 (prep 140 -> 398 us as non-temporal stores).
+typedef unsigned nt_u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned nt_u32x2 __attribute__((ext_vector_type(2)));
+template <bool NT, typename V>
+__device__ __forceinline__ void store_ws(void* p, const V& v)
+{
+    static_assert(sizeof(V) == 16 || sizeof(V) == 8, "16 or 8 bytes");
+    if constexpr (!NT)
+        *reinterpret_cast<V*>(p) = v;
+    else if constexpr (sizeof(V) == 16)
+        __builtin_nontemporal_store(__builtin_bit_cast(nt_u32x4, v), reinterpret_cast<nt_u32x4*>(p));
+    else
+        __builtin_nontemporal_store(__builtin_bit_cast(nt_u32x2, v), reinterpret_cast<nt_u32x2*>(p));
+}
 constexpr float kHalfSpanMax = 96.f;
 constexpr float kMinPart = 0x1p-120f;   // smallest product of one token range's gates
 
@@ -111,7 +133,7 @@ __device__ __forceinline__ float frcp(float x) { return __builtin_amdgcn_rcpf(x)
 // -phi_r turns every decay-weighted product into the real one of the plain
 // kernel on the rotated vectors; Ktil is rotated back by phi_{C-1} and
 // Gamma_{C-1} is stored as (|Gamma| cos phi_{C-1}, |Gamma| sin phi_{C-1}).
-template <typename T, int C, int DK, bool ZS, bool PRO, bool PH>
+template <typename T, int C, int DK, bool ZS, bool PRO, bool PH, bool NT = false>
 __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
 {
     using G = FastGeom<T, C, DK>;
@@ -546,7 +568,7 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
                 for (int i = 0; i < 4; ++i)
                     f[4 * u + i] = (tb <= ta && 16 * tb + 4 * lg + i <= 16 * ta + ln) ? accP[tb][i] : 0.f;
             }
-            *reinterpret_cast<F*>(Pg + ((size_t)(ta * NKC + s) * 64 + lane) * NV) = F::from(f);
+            store_ws<NT>(Pg + ((size_t)(ta * NKC + s) * 64 + lane) * NV, F::from(f));
         }
     }
     __syncthreads();   // operands dead: the region now holds A and Tinv
@@ -677,7 +699,7 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) f[4 * u + i] = acc[i];
                 }
-                *reinterpret_cast<F*>(Wg + ((size_t)(mt * NKD + s) * 64 + lane) * NV) = F::from(f);
+                store_ws<NT>(Wg + ((size_t)(mt * NKD + s) * 64 + lane) * NV, F::from(f));
             }
             for (int nt = 0; nt < NUt; ++nt) {
                 f32x4 acc = zero4();
@@ -686,7 +708,7 @@ __global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
                     if (kb < nkb) acc = mma(tf[kb], frag_row<T, KB>(sVt + (16 * nt + ln) * XTS, kb * KB), acc);
                 {
                     const float u4[4] = {acc[0], acc[1], acc[2], acc[3]};
-                    *reinterpret_cast<Vec4<T>*>(Ug + ((size_t)(mt * NUt + nt) * 64 + lane) * 4) = Vec4<T>::from(u4);
+                    store_ws<NT>(Ug + ((size_t)(mt * NUt + nt) * 64 + lane) * 4, Vec4<T>::from(u4));
                 }
             }
         }
@@ -697,13 +719,16 @@ template <typename T, int C, int DK>
 hipError_t launch_fast_t(const ChunkShape& s, const PrepArgs& a, hipStream_t stream)
 {
     const FastLayout<T, C, DK> LY;
-    // (the input parameterisation and the phase variant are not combined)
+    // (the input parameterisation and the phase variant are not combined; the
+    // non-temporal workspace stores exist for the plain variants)
     auto kern = a.theta ? (a.zx > 0 ? prep_fast_kernel<T, C, DK, true, false, true>
                                     : prep_fast_kernel<T, C, DK, false, false, true>)
               : a.zx > 0 ? (a.pro ? prep_fast_kernel<T, C, DK, true, true, false>
-                                  : prep_fast_kernel<T, C, DK, true, false, false>)
+                                  : a.ntst ? prep_fast_kernel<T, C, DK, true, false, false, true>
+                                           : prep_fast_kernel<T, C, DK, true, false, false>)
                          : (a.pro ? prep_fast_kernel<T, C, DK, false, true, false>
-                                  : prep_fast_kernel<T, C, DK, false, false, false>);
+                                  : a.ntst ? prep_fast_kernel<T, C, DK, false, false, false, true>
+                                           : prep_fast_kernel<T, C, DK, false, false, false>);
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              (int)LY.total);
