@@ -23,11 +23,12 @@ __all__ = [
     "decode_step", "decode_step_phase", "decode_step_prologue", "gate_prep", "last_stage_times",
     "chunk_backward", "chunk_backward_prologue", "chunk_backward_varlen",
     "chunk_backward_varlen_prologue", "backward_workspace_size",
-    "STAGE_EVENTS", "NO_SEGMENTS", "SINGLE_STREAM",
+    "VALIDATE_RANGES", "STAGE_EVENTS", "NO_SEGMENTS", "SINGLE_STREAM",
 ]
 
 KDA, CKDA = 0, 1
 STAGE_EVENTS = 2
+VALIDATE_RANGES = 1    # KDA_FLAG_VALIDATE_RANGES
 NO_SEGMENTS = 4        # KDA_FLAG_NO_SEGMENTS
 SINGLE_STREAM = 8      # KDA_FLAG_SINGLE_STREAM
 _DT = {torch.float32: 0, torch.bfloat16: 1}
@@ -36,7 +37,8 @@ _LIB_PATH = os.path.join(_HERE, "libkda.so")
 _lib = None
 
 _STATUS = {0: "ok", 1: "null pointer", 2: "bad shape", 3: "unsupported", 4: "misaligned",
-           5: "workspace too small", 6: "alias", 7: "hip error"}
+           5: "workspace too small", 6: "alias", 7: "hip error",
+           8: "input out of range"}
 
 
 class KdaError(RuntimeError):

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkda.so")
 SOURCES = ["decode.hip", "gate_prep.hip", "prep_fast.hip", "prep_exact.hip", "chain.hip",
-           "chunk_util.hip", "bwd.hip", "kda_api.hip"]
+           "chunk_util.hip", "bwd.hip", "range_check.hip", "kda_api.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops off: packed fp32 VALU forms are not emitted (the host pass

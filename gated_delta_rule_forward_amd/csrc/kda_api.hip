@@ -16,6 +16,7 @@
 #include "../../include/kda.h"
 #include "kda_chunk.hpp"
 #include "kda_launch.hpp"
+#include "range_check.hpp"
 
 namespace {
 
@@ -23,7 +24,8 @@ using kda::ChunkShape;
 using kda::ChunkWorkspace;
 using kda::IoType;
 
-constexpr unsigned kKnownFlags = KDA_FLAG_STAGE_EVENTS | KDA_FLAG_NO_SEGMENTS | KDA_FLAG_SINGLE_STREAM;
+constexpr unsigned kKnownFlags = KDA_FLAG_VALIDATE_RANGES | KDA_FLAG_STAGE_EVENTS |
+                                  KDA_FLAG_NO_SEGMENTS | KDA_FLAG_SINGLE_STREAM;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 bool aligned16(const void* p) { return aligned(p, 16); }
@@ -243,6 +245,21 @@ bool prologue_ok(const kda_prologue_t& p, kda_mode_t mode)
            (p.normalize_q == 0 || p.normalize_q == 1);
 }
 
+// KDA_FLAG_VALIDATE_RANGES: the device range check (synchronises the stream),
+// run once the arguments are validated and before any work is enqueued
+kda_status_t validate_ranges(unsigned flags, kda_mode_t mode, const float* alpha, size_t na,
+                             const float* beta, size_t nb, const float* theta, size_t nt,
+                             hipStream_t s)
+{
+    if (!(flags & KDA_FLAG_VALIDATE_RANGES)) return KDA_OK;
+    switch (kda::check_ranges(alpha, na, beta, nb, theta, nt, mode == KDA_MODE_CKDA, s)) {
+    case kda::RangeResult::InRange: return KDA_OK;
+    case kda::RangeResult::OutOfRange: return KDA_ERR_RANGE;
+    case kda::RangeResult::Capturing: return KDA_ERR_UNSUPPORTED;
+    default: return KDA_ERR_HIP;
+    }
+}
+
 // the chunked forward; chunk_states (may be null) receives the state entering
 // every chunk; pro (may be null) makes alpha / beta logits and q, k raw
 kda_status_t chunk_forward(const void* q, const void* k, const void* v, const float* alpha,
@@ -307,6 +324,11 @@ kda_status_t chunk_forward(const void* q, const void* k, const void* v, const fl
 
     // ---- validated: enqueue ------------------------------------------------------
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!pro && T > 0) {    // (with a prologue the ranges hold by construction)
+        st = validate_ranges(flags, mode, alpha, ntok * na, beta, ntok, theta,
+                             theta ? ntok * na : 0, s);
+        if (st != KDA_OK) return st;
+    }
     std::unique_lock<std::mutex> lock(g_stage.mu, std::defer_lock);
     Recorder rec{(flags & KDA_FLAG_STAGE_EVENTS) != 0, s};
     if (rec.on) {
@@ -485,6 +507,11 @@ kda_status_t decode_step(const void* q, const void* k, const void* v, const floa
     if (overlaps(st.p, st.n, o.p, o.n)) return KDA_ERR_ALIAS;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!pro) {
+        const kda_status_t vr = validate_ranges(flags, mode, alpha, nbh * na, beta, nbh, theta,
+                                                theta ? nbh * na : 0, s);
+        if (vr != KDA_OK) return vr;
+    }
     std::unique_lock<std::mutex> lock(g_stage.mu, std::defer_lock);
     Recorder rec{(flags & KDA_FLAG_STAGE_EVENTS) != 0, s};
     if (rec.on) {
@@ -927,6 +954,7 @@ const char* kda_status_string(int s)
     case KDA_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than kda_chunk_forward_workspace_size";
     case KDA_ERR_ALIAS: return "an output overlaps an input";
     case KDA_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+    case KDA_ERR_RANGE: return "an input lies outside the mode's ranges";
     default: return "unknown status";
     }
 }
@@ -1062,6 +1090,10 @@ kda_status_t kda_chunk_forward_varlen(const void* q, const void* k, const void* 
     }
 
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!prologue && total_T > 0) {
+        st = validate_ranges(flags, mode, alpha, ntok * Dk, beta, ntok, nullptr, 0, s);
+        if (st != KDA_OK) return st;
+    }
     std::unique_lock<std::mutex> lock(g_stage.mu, std::defer_lock);
     Recorder rec{(flags & KDA_FLAG_STAGE_EVENTS) != 0, s};
     if (rec.on) {

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 12
+#define KDA_ABI_VERSION 13
 
 typedef enum {
     KDA_OK = 0,
@@ -59,7 +59,8 @@ typedef enum {
     KDA_ERR_MISALIGNED = 4,          /* a pointer breaks the alignment rule below */
     KDA_ERR_WORKSPACE_TOO_SMALL = 5, /* workspace_bytes below the queried size */
     KDA_ERR_ALIAS = 6,               /* an output overlaps an input it must not */
-    KDA_ERR_HIP = 7                  /* a HIP runtime call or launch failed */
+    KDA_ERR_HIP = 7,                 /* a HIP runtime call or launch failed */
+    KDA_ERR_RANGE = 8                /* KDA_FLAG_VALIDATE_RANGES found an input out of range */
 } kda_status_t;
 
 typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype_t;
@@ -70,6 +71,20 @@ typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype_t;
  * stated range give results of the same formula but carry no accuracy
  * guarantee. */
 typedef enum { KDA_MODE_KDA = 0, KDA_MODE_CKDA = 1 } kda_mode_t;
+
+/* flags: check the inputs against the mode's ranges on the device before any
+ * work is enqueued: every alpha in (0,1] (KDA) or [-1,1] (CKDA), every beta in
+ * [0,1] (KDA) or [0,2] (CKDA), every theta of the phase variant finite; NaN is
+ * out of range.  One extra read of alpha, beta (and theta); the call then
+ * synchronises `stream` and returns KDA_ERR_RANGE, with nothing enqueued and
+ * no output written, if any element is out of range.  Accepted by
+ * kda_chunk_forward, its _states, _phase and _varlen forms and every
+ * kda_decode_step form; the _prologue forms check nothing (their gates are
+ * in range by construction); the backward entry points refuse the flag
+ * (KDA_ERR_UNSUPPORTED).  Under graph capture of `stream` the call returns
+ * KDA_ERR_UNSUPPORTED (the check must synchronise).  A debugging aid, not
+ * for the timed path. */
+#define KDA_FLAG_VALIDATE_RANGES 1u
 
 /* flags: attach a pair of HIP events to every kernel launch of this call
  * (hipExtLaunchKernelGGL start/stop events, stamped by the kernel's own start

@@ -45,9 +45,9 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 12
-    for s in range(8):
-        assert lib.kda_status_string(s)
+    assert lib.kda_abi_version() == 13
+    for s in range(9):
+        assert lib.kda_status_string(s) != b"unknown status"
     assert lib.kda_status_string(99) == b"unknown status"
 
 
@@ -124,6 +124,11 @@ def test_forward_validation(lib):
     assert fwd(lib, C=128) == UNSUP
     assert fwd(lib, mode=2) == UNSUP
     assert fwd(lib, flags=1 << 5) == UNSUP
+    # the range-check flag is known; argument errors still come first, before
+    # the device check makes any HIP call
+    assert fwd(lib, flags=1, q=None) == NULLP
+    assert fwd(lib, flags=1, Dk=20) == UNSUP
+    assert fwd(lib, flags=1, wsb=0) == WS
     assert fwd(lib, dt=5) == UNSUP
     assert fwd(lib, q=ctypes.c_void_p(0x7f0000000008)) == MISAL
     assert fwd(lib, beta=ctypes.c_void_p(0x7f0000000002)) == MISAL
@@ -321,6 +326,7 @@ def test_backward_validation(lib):
     assert bw(Dk=16) == UNSUP
     assert bw(mode=5) == UNSUP
     assert bw(flags=4) == UNSUP                                    # segments are forward-only
+    assert bw(flags=1) == UNSUP                                    # range check: forward only
     mis = list(base)
     mis[6] = ctypes.c_void_p(base[6].value + 4)                   # d_out: 16-byte rule
     assert bw(ptrs=mis) == MISAL
