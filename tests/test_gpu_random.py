@@ -13,7 +13,7 @@ import torch
 import gated_delta_rule_forward_amd as kda
 import oracle
 import workloads
-from parity import TOL, np32, oracle_threads, say, slice_err_out, slice_err_state
+from parity import TOL, np32, oracle_threads, say, slice_err_out, slice_err_state, elem_note
 
 pytestmark = pytest.mark.gpu
 
@@ -74,7 +74,7 @@ def test_forward_random_shape(name, dt, B, H, T, Dk, Dv, chunk, mode, s0, seed):
                                 chunk=chunk, mode=mode)
     torch.cuda.synchronize()
     eo, es = slice_err_out(np32(out), o_ref), slice_err_state(np32(st), s_ref)
-    say(f"  err out {eo:.3e} state {es:.3e}")
+    say(f"  err out {eo:.3e} state {es:.3e}{elem_note()}")
     assert eo <= TOL[DT[dt]] and es <= TOL[DT[dt]]
 
 

@@ -567,3 +567,38 @@ def test_phase_rotation_preserves_norm(oracle_lib):
         n0 = np.sqrt((S0.astype(np.float64) ** 2).sum(axis=(-2, -1)))
         n1 = np.sqrt((s ** 2).sum(axis=(-2, -1)))
         assert np.abs(n1 - n0).max() < 1e-12 * n0.max()
+
+
+def test_prologue_eps_sits_outside_the_norm(oracle_lib):
+    """Eq. (18) ("Semidirect Fourier Delta Attention", §3) adds eps to the norm
+    itself: k = k_raw / (|k_raw|_2 + eps).  One token with the gate range
+    collapsed to {0} (eq. (15) with alpha_min = alpha_max = 0: the state is
+    forgotten) and beta = 2 sigmoid(0) = 1 (eq. (17)) leaves S_1 = k v^T, so
+    the normalised key is read off the state.  k_raw = (3, 4, 0, ...) has norm
+    5; with eps = 1 the key is k_raw / 6 exactly, while eps under the root
+    (sqrt(25 + 1)) or squared (sqrt(25) + 1 with eps^2, the same here) is told
+    apart by a second eps = 2 case: k_raw / 7, not k_raw / sqrt(29) or / 9.
+    With q normalised the same way, q_raw = (6, 8, 0, ...) (norm 10) gives
+    o_1 = (q.k) v with q.k = (3 6 + 4 8) / (6 11) = 50 / 66."""
+    Dk, Dv = 8, 3
+    q = np.zeros((1, 1, 1, Dk), np.float32)
+    k = np.zeros((1, 1, 1, Dk), np.float32)
+    q[..., 0], q[..., 1] = 6.0, 8.0
+    k[..., 0], k[..., 1] = 3.0, 4.0
+    v = np.array([1.5, -2.0, 0.25], np.float32).reshape(1, 1, 1, Dv)
+    g = np.full((1, 1, 1, Dk), 0.7, np.float32)          # any logit: the range is {0}
+    c = np.zeros((1, 1, 1), np.float32)
+    S0 = np.full((1, 1, Dk, Dv), 3.0, np.float32)        # forgotten by alpha = 0
+    v64 = v.reshape(Dv).astype(np.float64)
+    for eps, kden, qden in ((1.0, 6.0, 11.0), (2.0, 7.0, 12.0), (0.5, 5.5, 10.5)):
+        o, s = oracle_lib.forward_prologue(q, k, v, g, c, S0, alpha_min=0.0, alpha_max=0.0,
+                                           beta_max=2.0, eps=eps, normalize_q=True)
+        kn = np.zeros(Dk)
+        kn[0], kn[1] = 3.0 / kden, 4.0 / kden
+        assert np.abs(s[0, 0] - np.outer(kn, v64)).max() < 1e-15, eps
+        qk = (3.0 * 6.0 + 4.0 * 8.0) / (kden * qden)
+        assert np.abs(o[0, 0, 0] - qk * v64).max() < 1e-15, eps
+        # without q normalisation the raw q reads the same state
+        o2, _ = oracle_lib.forward_prologue(q, k, v, g, c, S0, alpha_min=0.0, alpha_max=0.0,
+                                            beta_max=2.0, eps=eps, normalize_q=False)
+        assert np.abs(o2[0, 0, 0] - (50.0 / kden) * v64).max() < 1e-14, eps
