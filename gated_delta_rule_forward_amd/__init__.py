@@ -19,6 +19,7 @@ import torch
 
 __all__ = [
     "KDA", "CKDA", "KdaError", "library_path", "load", "abi_version", "workspace_size",
+    "chunk_forward_noalloc", "NOALLOC_SCRATCH_BYTES",
     "chunk_forward", "chunk_forward_prologue", "chunk_forward_varlen", "chunk_forward_phase",
     "decode_step", "decode_step_phase", "decode_step_prologue", "gate_prep", "last_stage_times",
     "chunk_backward", "chunk_backward_prologue", "chunk_backward_varlen",
@@ -38,7 +39,8 @@ _lib = None
 
 _STATUS = {0: "ok", 1: "null pointer", 2: "bad shape", 3: "unsupported", 4: "misaligned",
            5: "workspace too small", 6: "alias", 7: "hip error",
-           8: "input out of range"}
+           8: "input out of range", 9: "workspace above the built-in scratch"}
+NOALLOC_SCRATCH_BYTES = 32 << 20     # KDA_NOALLOC_SCRATCH_BYTES
 
 
 class KdaError(RuntimeError):
@@ -75,6 +77,8 @@ def load():
     lib.kda_chunk_forward_workspace_size.restype = i
     lib.kda_chunk_forward.argtypes = [vp] * 8 + [i] * 8 + [u, vp, sz, vp]
     lib.kda_chunk_forward.restype = i
+    lib.kda_chunk_forward_noalloc.argtypes = [vp] * 8 + [i] * 8 + [u, vp]
+    lib.kda_chunk_forward_noalloc.restype = i
     lib.kda_chunk_forward_states.argtypes = [vp] * 9 + [i] * 8 + [u, vp, sz, vp]
     lib.kda_chunk_forward_states.restype = i
     lib.kda_chunk_forward_prologue.argtypes = [vp] * 5 + [ctypes.POINTER(Prologue)] + [vp] * 3 + \
@@ -198,6 +202,26 @@ def chunk_forward(q, k, v, alpha, beta, initial_state=None, *, chunk: int = 64, 
                                           _DT[q.dtype], mode, flags, _ptr(workspace), wsb,
                                           _stream(stream))
         _check("kda_chunk_forward_states", st)
+    return out, final_state
+
+
+def chunk_forward_noalloc(q, k, v, alpha, beta, initial_state, out, final_state=None, *,
+                          chunk: int = 64, mode: int = CKDA, stream=None, flags: int = 0):
+    """kda_chunk_forward_noalloc: the chunked forward with the library's built-in
+    scratch in place of a workspace.  The caller passes every tensor (out, and
+    final_state or None); nothing is allocated here or in the library.  Returns
+    (out, final_state)."""
+    lib = load()
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    _dev(q, k, v, alpha, beta, initial_state, out, final_state)
+    if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype or out.dtype != q.dtype:
+        raise ValueError("q, k, v and out must share one dtype (float32 or bfloat16)")
+    st = lib.kda_chunk_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                       _ptr(initial_state), _ptr(out), _ptr(final_state),
+                                       B, T, H, Dk, Dv, chunk, _DT[q.dtype], mode, flags,
+                                       _stream(stream))
+    _check("kda_chunk_forward_noalloc", st)
     return out, final_state
 
 

@@ -937,6 +937,43 @@ kda_status_t chunk_backward_varlen(const void* q, const void* k, const void* v, 
                             mode, workspace, rec, s, total_T > 0 ? cu_seqlens : nullptr);
 }
 
+// ---- scratch of kda_chunk_forward_noalloc -------------------------------------
+// A fixed array per device in place of the caller's workspace, for callers that
+// cannot allocate.  The runtime sets it aside when the library's code object is
+// loaded on a device, and it stays until the process ends.  On the host the
+// name `scratch` is only a stand-in for the symbol, not a device address: the
+// address is taken per device with hipGetSymbolAddress, once, with that device
+// current, and only that address is ever handed to kernels.  The forward writes
+// every workspace byte it reads later in the same call (the per-unit factors,
+// flags and, with segments, the maps and start states), so nothing is cleared
+// between calls.
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// the address of `scratch` on `dev`, looked up on first use with dev current
+hipError_t scratch_address(int dev, void** out)
+{
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> guard(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = 0;
+        hipError_t e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        const hipError_t eg = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur && (e = hipSetDevice(cur)) != hipSuccess) return e;
+        if (eg != hipSuccess) return eg;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -955,6 +992,8 @@ const char* kda_status_string(int s)
     case KDA_ERR_ALIAS: return "an output overlaps an input";
     case KDA_ERR_HIP: return "a HIP runtime call or kernel launch failed";
     case KDA_ERR_RANGE: return "an input lies outside the mode's ranges";
+    case KDA_ERR_SCRATCH_LIMIT:
+        return "the shape's workspace exceeds the built-in scratch of kda_chunk_forward_noalloc";
     default: return "unknown status";
     }
 }
@@ -981,6 +1020,36 @@ kda_status_t kda_chunk_forward(const void* q, const void* k, const void* v, cons
     return chunk_forward(q, k, v, alpha, beta, initial_state, out, final_state, nullptr, nullptr,
                          B, T, H, Dk, Dv, chunk, dtype, mode, flags, workspace, workspace_bytes,
                          stream);
+}
+
+kda_status_t kda_chunk_forward_noalloc(const void* q, const void* k, const void* v,
+                                       const float* alpha, const float* beta,
+                                       const float* initial_state, void* out, float* final_state,
+                                       int B, int T, int H, int Dk, int Dv, int chunk,
+                                       kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
+                                       void* stream)
+{
+    // every check that needs no HIP call first (shape, flags, the scratch limit)
+    const kda_status_t st = check_forward_shape(B, T, H, Dk, Dv, chunk, dtype);
+    if (st != KDA_OK) return st;
+    if (flags & (KDA_FLAG_STAGE_EVENTS | KDA_FLAG_VALIDATE_RANGES)) return KDA_ERR_UNSUPPORTED;
+    if (flags & ~kKnownFlags) return KDA_ERR_UNSUPPORTED;
+    size_t need = 0;
+    kda_chunk_forward_workspace_size(B, T, H, Dk, Dv, chunk, dtype, &need);
+    if (need > (size_t)KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_SCRATCH_LIMIT;
+    if (T == 0 || need == 0)
+        return chunk_forward(q, k, v, alpha, beta, initial_state, out, final_state, nullptr,
+                             nullptr, B, T, H, Dk, Dv, chunk, dtype, mode,
+                             flags | KDA_FLAG_SINGLE_STREAM, nullptr, 0, stream);
+    // the scratch of the device `stream` belongs to
+    int dev = 0;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev)) != hipSuccess) return KDA_ERR_HIP;
+    void* ws = nullptr;
+    if (scratch_address(dev, &ws) != hipSuccess) return KDA_ERR_HIP;
+    return chunk_forward(q, k, v, alpha, beta, initial_state, out, final_state, nullptr, nullptr,
+                         B, T, H, Dk, Dv, chunk, dtype, mode, flags | KDA_FLAG_SINGLE_STREAM, ws,
+                         (size_t)KDA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 kda_status_t kda_chunk_forward_prologue(const void* q_raw, const void* k_raw, const void* v,

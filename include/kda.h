@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 13
+#define KDA_ABI_VERSION 14
 
 typedef enum {
     KDA_OK = 0,
@@ -60,7 +60,8 @@ typedef enum {
     KDA_ERR_WORKSPACE_TOO_SMALL = 5, /* workspace_bytes below the queried size */
     KDA_ERR_ALIAS = 6,               /* an output overlaps an input it must not */
     KDA_ERR_HIP = 7,                 /* a HIP runtime call or launch failed */
-    KDA_ERR_RANGE = 8                /* KDA_FLAG_VALIDATE_RANGES found an input out of range */
+    KDA_ERR_RANGE = 8,               /* KDA_FLAG_VALIDATE_RANGES found an input out of range */
+    KDA_ERR_SCRATCH_LIMIT = 9        /* kda_chunk_forward_noalloc: workspace above its scratch */
 } kda_status_t;
 
 typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype_t;
@@ -201,6 +202,39 @@ typedef struct {
     float eps;
     int normalize_q;
 } kda_prologue_t;
+
+/* Size of the built-in scratch of kda_chunk_forward_noalloc (bytes per device). */
+#define KDA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * kda_chunk_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * The same computation and kernels as kda_chunk_forward, with the workspace
+ * taken from an array of KDA_NOALLOC_SCRATCH_BYTES inside the library instead
+ * of the caller's (one array per device, set aside when the library is loaded
+ * on that device and held until the process ends).  The caller still passes
+ * inputs and outputs; every argument, rule and result is that of
+ * kda_chunk_forward, with these differences:
+ *  - shapes whose kda_chunk_forward_workspace_size() exceeds
+ *    KDA_NOALLOC_SCRATCH_BYTES return KDA_ERR_SCRATCH_LIMIT (checked before any
+ *    HIP call);
+ *  - all work runs on `stream` (as with KDA_FLAG_SINGLE_STREAM), and the flags
+ *    KDA_FLAG_STAGE_EVENTS and KDA_FLAG_VALIDATE_RANGES are refused
+ *    (KDA_ERR_UNSUPPORTED): the call creates no stream or event and makes no
+ *    allocating call;
+ *  - the array used is that of the device `stream` belongs to (the current
+ *    device for the null stream); its address is looked up once per device.
+ * Every call on a device shares that device's array: calls whose work
+ * overlaps in time on one device (different streams, or several host threads
+ * without ordering) race on it and give unspecified results.  Calls ordered
+ * on one stream are safe; nothing needs clearing between them.
+ */
+kda_status_t kda_chunk_forward_noalloc(const void* q, const void* k, const void* v,
+                                       const float* alpha, const float* beta,
+                                       const float* initial_state, void* out, float* final_state,
+                                       int B, int T, int H, int Dk, int Dv, int chunk,
+                                       kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
+                                       void* stream);
 
 /*
  * kda_chunk_forward from raw inputs through the parameterisation above: gate

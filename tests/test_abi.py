@@ -39,14 +39,15 @@ def test_exports_every_declared_symbol(lib):
             "kda_chunk_backward_prologue", "kda_chunk_backward_prologue_workspace_size",
             "kda_chunk_backward_varlen", "kda_chunk_backward_varlen_workspace_size",
             "kda_chunk_backward_varlen_prologue", "kda_chunk_backward_varlen_prologue_workspace_size",
-            "kda_gate_prep", "kda_status_string", "kda_abi_version"} <= set(syms)
+            "kda_gate_prep", "kda_status_string", "kda_abi_version",
+            "kda_chunk_forward_noalloc"} <= set(syms)
     for s in syms:
         assert hasattr(lib, s), s
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 13
-    for s in range(9):
+    assert lib.kda_abi_version() == 14
+    for s in range(10):
         assert lib.kda_status_string(s) != b"unknown status"
     assert lib.kda_status_string(99) == b"unknown status"
 
@@ -445,3 +446,39 @@ def test_forward_workspace_reserves_the_parts_state(lib):
     # 256 chains (H = 32): no parts, so no state buffer
     big = lambda T: ws(T, H=32)
     assert big(64 * 256) - big(64 * 255) == big(64 * 2) - big(64 * 1)
+
+
+def test_noalloc_refusals_before_any_hip_call(lib):
+    """kda_chunk_forward_noalloc checks shape, flags and its scratch limit
+    before it touches the GPU: a shape whose workspace exceeds the built-in
+    scratch (KDA_NOALLOC_SCRATCH_BYTES, 32 MiB) is KDA_ERR_SCRATCH_LIMIT, the
+    event and range-check flags are refused, and a bad shape keeps its own
+    status."""
+    SCRATCH_LIMIT = 9
+    f = Fake()
+    q, k, v, a, b, s0, o, st = (f() for _ in range(8))
+    lib.kda_chunk_forward_noalloc.argtypes = [ctypes.c_void_p] * 8 + [ctypes.c_int] * 8 + \
+        [ctypes.c_uint, ctypes.c_void_p]
+    call = lambda B, T, H, D, C, dt, fl: lib.kda_chunk_forward_noalloc(
+        q, k, v, a, b, s0, o, st, B, T, H, D, D, C, dt, 1, fl, None)
+    # the headline prefill needs ~297 MB of workspace
+    assert call(1, 8192, 32, 128, 64, BF16, 0) == SCRATCH_LIMIT
+    n_big = ws_size(lib, 1, 8192, 32, 128, 128, 64, BF16)[1]
+    assert n_big > 32 << 20
+    # the longest single-head bf16 d = 128 sequence that fits, found by
+    # bisection on the workspace query; one token more is refused
+    lo, hi = 1, 1 << 20
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        if ws_size(lib, 1, mid, 1, 128, 128, 64, BF16)[1] <= 32 << 20:
+            lo = mid
+        else:
+            hi = mid
+    assert ws_size(lib, 1, hi, 1, 128, 128, 64, BF16)[1] > 32 << 20
+    assert call(1, hi, 1, 128, 64, BF16, 0) == SCRATCH_LIMIT
+    assert call(1, 64, 1, 128, 64, BF16, 2) == UNSUP          # KDA_FLAG_STAGE_EVENTS
+    assert call(1, 64, 1, 128, 64, BF16, 1) == UNSUP          # KDA_FLAG_VALIDATE_RANGES
+    assert call(1, 64, 1, 128, 64, BF16, 64) == UNSUP         # unknown flag
+    assert call(0, 64, 1, 128, 64, BF16, 0) == SHAPE
+    assert call(1, 64, 1, 24, 64, BF16, 0) == UNSUP
+    assert lib.kda_status_string(SCRATCH_LIMIT) != b"unknown status"
