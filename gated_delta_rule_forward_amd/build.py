@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkda.so")
-SOURCES = ["decode.hip", "gate_prep.hip", "prep_fast.hip", "prep_exact.hip", "chain.hip",
+SOURCES = ["decode.hip", "gate_prep.hip", "prep_fast.hip", "prep_exact.hip", "chain.hip", "chain_wide.hip",
            "chunk_util.hip", "bwd.hip", "range_check.hip", "kda_api.hip"]
 ARCH = "gfx950"
 

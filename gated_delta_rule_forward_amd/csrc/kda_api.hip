@@ -104,6 +104,18 @@ struct Recorder {
     ~Recorder() { if (on) kda::g_launch_timer = {}; }
 };
 
+// The chain of a forward: the wide-slice kernel (chain_wide.hip) where it
+// covers the shape and the call (outputs wanted; no summary pass, segment
+// starts or backward side outputs), else the 16-column kernel (chain.hip).
+hipError_t launch_forward_chain(IoType io, const ChunkShape& sh, const kda::ChainArgs& a,
+                                hipStream_t s)
+{
+    const int ct = kda::wide_chain_tiles(io, sh);
+    if (ct > 0 && a.out && !a.summ && a.nseg <= 1 && !a.CS32 && !a.DL)
+        return kda::launch_chain_wide(io, sh, a, ct, s);
+    return kda::launch_chain(io, sh, a, s);
+}
+
 // fields shared by the forward and its workspace query
 kda_status_t check_forward_shape(int B, int T, int H, int Dk, int Dv, int chunk,
                                  kda_dtype_t dtype)
@@ -411,7 +423,7 @@ kda_status_t chunk_forward(const void* q, const void* k, const void* v, const fl
             cp.ST = p == prt.parts - 1 ? final_state : spart;
             if (hipStreamWaitEvent(s, side->ev[p + 1], 0) != hipSuccess) return KDA_ERR_HIP;
             if (rec.mark("chain") != hipSuccess) return KDA_ERR_HIP;
-            if (kda::launch_chain(io, sh, cp, s) != hipSuccess) return KDA_ERR_HIP;
+            if (launch_forward_chain(io, sh, cp, s) != hipSuccess) return KDA_ERR_HIP;
             if (rec.done() != hipSuccess) return KDA_ERR_HIP;
         }
         return KDA_OK;
@@ -441,7 +453,7 @@ kda_status_t chunk_forward(const void* q, const void* k, const void* v, const fl
         if (rec.done() != hipSuccess) return KDA_ERR_HIP;
     }
     if (rec.mark("chain") != hipSuccess) return KDA_ERR_HIP;
-    if (kda::launch_chain(io, sh, ca, s) != hipSuccess) return KDA_ERR_HIP;
+    if (launch_forward_chain(io, sh, ca, s) != hipSuccess) return KDA_ERR_HIP;
     if (rec.done() != hipSuccess) return KDA_ERR_HIP;
     return KDA_OK;
 }
@@ -1204,7 +1216,7 @@ kda_status_t kda_chunk_forward_varlen(const void* q, const void* k, const void* 
     if (kda::launch_prep_exact(io, shp, pa, s) != hipSuccess) return KDA_ERR_HIP;
     if (rec.done() != hipSuccess) return KDA_ERR_HIP;
     if (rec.mark("chain") != hipSuccess) return KDA_ERR_HIP;
-    if (kda::launch_chain(io, shc, ca, s) != hipSuccess) return KDA_ERR_HIP;
+    if (launch_forward_chain(io, shc, ca, s) != hipSuccess) return KDA_ERR_HIP;
     if (rec.done() != hipSuccess) return KDA_ERR_HIP;
     return KDA_OK;
 }

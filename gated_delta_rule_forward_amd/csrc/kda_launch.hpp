@@ -60,6 +60,11 @@ size_t prep_fast_lds_bytes(IoType io, int C, int Dk);
 hipError_t launch_prep_fast(IoType io, const ChunkShape& s, const PrepArgs& a, hipStream_t stream);
 hipError_t launch_prep_exact(IoType io, const ChunkShape& s, const PrepArgs& a, hipStream_t stream);
 hipError_t launch_chain(IoType io, const ChunkShape& s, const ChainArgs& a, hipStream_t stream);
+// the wide-slice chain (16 ct columns per workgroup, operands in registers);
+// wide_chain_tiles: the ct to use for a shape, 0 when the kernel does not cover it
+int wide_chain_tiles(IoType io, const ChunkShape& s);
+hipError_t launch_chain_wide(IoType io, const ChunkShape& s, const ChainArgs& a, int ct,
+                             hipStream_t stream);
 hipError_t launch_segment_combine(int BH, int Dk, int Dv, int nseg, const float* S0,
                                   const float* summ, float* Sseg, hipStream_t stream);
 
