@@ -19,7 +19,7 @@ import torch
 
 __all__ = [
     "KDA", "CKDA", "KdaError", "library_path", "load", "abi_version", "workspace_size",
-    "chunk_forward_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "chunk_forward_noalloc", "NOALLOC_SCRATCH_BYTES", "SideStream", "SIDE_EVENTS",
     "chunk_forward", "chunk_forward_prologue", "chunk_forward_varlen", "chunk_forward_phase",
     "decode_step", "decode_step_phase", "decode_step_prologue", "gate_prep", "last_stage_times",
     "chunk_backward", "chunk_backward_prologue", "chunk_backward_varlen",
@@ -47,6 +47,31 @@ class KdaError(RuntimeError):
     def __init__(self, fn: str, status: int):
         self.status = status
         super().__init__(f"{fn} failed: status {status} ({_STATUS.get(status, 'unknown')})")
+
+
+SIDE_EVENTS = 9    # KDA_SIDE_EVENTS
+
+
+class _Side(ctypes.Structure):
+    """kda_side_t (include/kda.h)."""
+    _fields_ = [("stream", ctypes.c_void_p), ("events", ctypes.c_void_p * SIDE_EVENTS)]
+
+
+class SideStream:
+    """A second stream and its events, owned here and lent to
+    kda_chunk_forward_side (chunk_forward(..., side=...)): the chunk factors of
+    later parts are formed on it while the chain runs earlier parts."""
+
+    def __init__(self, device=None):
+        self.stream = torch.cuda.Stream(device=device)
+        self.events = [torch.cuda.Event(enable_timing=False) for _ in range(SIDE_EVENTS)]
+        for e in self.events:              # torch creates the event at its first record
+            e.record(self.stream)
+        self._c = _Side(self.stream.cuda_stream,
+                        (ctypes.c_void_p * SIDE_EVENTS)(*[e.cuda_event for e in self.events]))
+
+    def _as_arg(self):
+        return ctypes.byref(self._c)
 
 
 class Prologue(ctypes.Structure):
@@ -77,6 +102,8 @@ def load():
     lib.kda_chunk_forward_workspace_size.restype = i
     lib.kda_chunk_forward.argtypes = [vp] * 8 + [i] * 8 + [u, vp, sz, vp]
     lib.kda_chunk_forward.restype = i
+    lib.kda_chunk_forward_side.argtypes = [vp] * 8 + [i] * 8 + [u, vp, sz, vp, ctypes.POINTER(_Side)]
+    lib.kda_chunk_forward_side.restype = i
     lib.kda_chunk_forward_noalloc.argtypes = [vp] * 8 + [i] * 8 + [u, vp]
     lib.kda_chunk_forward_noalloc.restype = i
     lib.kda_chunk_forward_states.argtypes = [vp] * 9 + [i] * 8 + [u, vp, sz, vp]
@@ -166,12 +193,13 @@ def workspace_size(B: int, T: int, H: int, Dk: int, Dv: int, chunk: int, dtype: 
 
 def chunk_forward(q, k, v, alpha, beta, initial_state=None, *, chunk: int = 64, mode: int = CKDA,
                   out=None, final_state=None, output_final_state: bool = True, workspace=None,
-                  chunk_states=None, stream=None, flags: int = 0):
+                  chunk_states=None, stream=None, flags: int = 0, side=None):
     """Chunked forward.  q, k: [B,T,H,Dk]; v: [B,T,H,Dv] (fp32 or bf16, same dtype);
     alpha: [B,T,H,Dk] fp32; beta: [B,T,H] fp32; initial_state: [B,H,Dk,Dv] fp32 or None.
     chunk_states: None, or a [B,H,ceil(T/chunk),Dk,Dv] tensor of q's dtype that
     receives the state entering every chunk (kda_chunk_forward_states).
-    Returns (out [B,T,H,Dv], final_state [B,H,Dk,Dv] fp32 or None)."""
+    side: None, or a SideStream lent to kda_chunk_forward_side (not with
+    chunk_states).  Returns (out [B,T,H,Dv], final_state [B,H,Dk,Dv] fp32 or None)."""
     lib = load()
     B, T, H, Dk = q.shape
     Dv = v.shape[-1]
@@ -186,7 +214,15 @@ def chunk_forward(q, k, v, alpha, beta, initial_state=None, *, chunk: int = 64, 
     if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype or out.dtype != q.dtype:
         raise ValueError("q, k, v and out must share one dtype (float32 or bfloat16)")
     wsb = workspace.numel() * workspace.element_size()
-    if chunk_states is None:
+    if side is not None and chunk_states is not None:
+        raise ValueError("chunk_states and side cannot be combined")
+    if side is not None:
+        st = lib.kda_chunk_forward_side(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                        _ptr(initial_state), _ptr(out), _ptr(final_state),
+                                        B, T, H, Dk, Dv, chunk, _DT[q.dtype], mode, flags,
+                                        _ptr(workspace), wsb, _stream(stream), side._as_arg())
+        _check("kda_chunk_forward_side", st)
+    elif chunk_states is None:
         st = lib.kda_chunk_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
                                    _ptr(initial_state), _ptr(out), _ptr(final_state),
                                    B, T, H, Dk, Dv, chunk, _DT[q.dtype], mode, flags,

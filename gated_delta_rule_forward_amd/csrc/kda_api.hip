@@ -37,8 +37,8 @@ bool chunk_ok(int c) { return c == 16 || c == 32 || c == 64; }
 size_t elem_size(kda_dtype_t t) { return t == KDA_DTYPE_F32 ? 4 : 2; }
 
 // Extra zero-segment columns the fast prep kernel may take per chunk: none in
-// KDA mode (gates in (0, 1] have no zeros; a chunk that holds one goes to the
-// exact kernel), 4 Dk in CKDA mode (contracted Dk per pass, so at most four
+// KDA mode (a zero gate is in range but rare there; a chunk that holds one goes
+// to the exact kernel), 4 Dk in CKDA mode (contracted Dk per pass, so at most four
 // extra passes); a chunk with more zero gates goes to the exact kernel.
 int fast_zero_columns(int mode, int Dk) { return mode == KDA_MODE_CKDA ? 4 * Dk : 0; }
 
@@ -157,6 +157,8 @@ Segments segments_for(int B, int H, int Dk, int Dv, int NC)
     return {(NC + seg - 1) / seg, seg};
 }
 
+static_assert(KDA_SIDE_EVENTS == 1 + kMaxParts, "one event for the call's start, one per part");
+
 // Prep / chain overlap for a dense forward whose chains leave half the GPU or
 // more idle: the chunks of every (b, h) are cut into `parts` consecutive
 // ranges of `len` chunks, and the prep kernels of range p + 1 run on a second
@@ -202,51 +204,6 @@ size_t dense_layout(int B, int T, int H, int Dk, int Dv, int chunk, IoType io,
     return n;
 }
 
-// per device: the second stream of the prep / chain overlap and its events
-// (event 0: the caller's stream reached the call; event p + 1: prep of part p
-// done).  Created on first use, kept until the process ends; g_side_mu is
-// held while a call enqueues, so calls from several host threads do not
-// share events in flight.
-struct SideStream {
-    hipStream_t st = nullptr;
-    hipEvent_t ev[kMaxParts + 1] = {};
-};
-std::mutex g_side_mu;
-std::map<int, SideStream> g_side;
-
-// The side stream of the current device in *out, created on first use.
-// *out stays null (the call keeps to the caller's stream) when `caller`
-// belongs to another device, or when it is being captured into a graph and
-// the side stream does not exist yet (nothing is created during a capture).
-hipError_t side_stream(hipStream_t caller, SideStream** out)
-{
-    *out = nullptr;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (caller) {
-        hipDevice_t sdev = 0;
-        e = hipStreamGetDevice(caller, &sdev);
-        if (e != hipSuccess) return e;
-        if (sdev != dev) return hipSuccess;
-    }
-    SideStream& ss = g_side[dev];
-    if (!ss.st) {
-        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-        e = hipStreamIsCapturing(caller, &cap);
-        if (e != hipSuccess) return e;
-        if (cap != hipStreamCaptureStatusNone) return hipSuccess;
-        for (int i = 0; i <= kMaxParts; ++i) {
-            if (!ss.ev[i]) e = hipEventCreateWithFlags(&ss.ev[i], hipEventDisableTiming);
-            if (e != hipSuccess) return e;
-        }
-        e = hipStreamCreateWithFlags(&ss.st, hipStreamNonBlocking);
-        if (e != hipSuccess) return e;
-    }
-    *out = &ss;
-    return hipSuccess;
-}
-
 // prologue parameters inside the mode's ranges (KDA: gates in [0, 1], beta in
 // [0, 1]; CKDA: gates in [-1, 1], beta in [0, 2]), finite, eps >= 0
 bool prologue_ok(const kda_prologue_t& p, kda_mode_t mode)
@@ -279,7 +236,8 @@ kda_status_t chunk_forward(const void* q, const void* k, const void* v, const fl
                            float* final_state, void* chunk_states, const kda_prologue_t* pro,
                            int B, int T, int H, int Dk, int Dv, int chunk, kda_dtype_t dtype,
                            kda_mode_t mode, unsigned flags, void* workspace,
-                           size_t workspace_bytes, void* stream, const float* theta = nullptr)
+                           size_t workspace_bytes, void* stream, const float* theta = nullptr,
+                           const kda_side_t* side = nullptr)
 {
     kda_status_t st = check_forward_shape(B, T, H, Dk, Dv, chunk, dtype);
     if (st != KDA_OK) return st;
@@ -288,6 +246,11 @@ kda_status_t chunk_forward(const void* q, const void* k, const void* v, const fl
     if (T > 0 && (!q || !k || !v || !alpha || !beta || !out)) return KDA_ERR_NULL_POINTER;
     if (pro && !prologue_ok(*pro, mode)) return KDA_ERR_UNSUPPORTED;
     if (pro && theta) return KDA_ERR_UNSUPPORTED;
+    if (side) {
+        if (!side->stream) return KDA_ERR_NULL_POINTER;
+        for (int i = 0; i < KDA_SIDE_EVENTS; ++i)
+            if (!side->events[i]) return KDA_ERR_NULL_POINTER;
+    }
 
     const size_t e = elem_size(dtype);
     const size_t ntok = (size_t)B * T * H;
@@ -376,8 +339,8 @@ kda_status_t chunk_forward(const void* q, const void* k, const void* v, const fl
     pa.ntst = workspace_nt((long long)B * H * (Dv / 16));
     const Segments sgm = (flags & KDA_FLAG_NO_SEGMENTS) ? Segments{1, sh.NC}
                                                           : segments_for(B, H, Dk, Dv, sh.NC);
-    const Parts prt = (sgm.nseg > 1 || (flags & KDA_FLAG_SINGLE_STREAM)) ? Parts{1, sh.NC}
-                                                                       : parts_for(B, H, Dk, Dv, sh.NC);
+    const Parts prt = (!side || sgm.nseg > 1 || (flags & KDA_FLAG_SINGLE_STREAM))
+                          ? Parts{1, sh.NC} : parts_for(B, H, Dk, Dv, sh.NC);
     size_t so = 0, ss = 0, sp = 0;
     if (sgm.nseg > 1 || prt.parts > 1) {
         size_t off2[kda::kWorkspaceRegions];
@@ -389,31 +352,44 @@ kda_status_t chunk_forward(const void* q, const void* k, const void* v, const fl
                             final_state, chunk_states, B, T, H, Dv, sh.NC, nullptr, nullptr,
                             theta ? 1 : 0, sgm.seg, sgm.nseg, nullptr, sseg};
 
-    std::unique_lock<std::mutex> side_lock(g_side_mu, std::defer_lock);
-    SideStream* side = nullptr;
-    if (prt.parts > 1) {
-        side_lock.lock();
-        if (side_stream(s, &side) != hipSuccess) return KDA_ERR_HIP;
+    // the caller's second stream takes part in the call only when it belongs to
+    // the same device as `stream` (else the call keeps to `stream`)
+    bool use_side = prt.parts > 1;
+    if (use_side) {
+        hipDevice_t d0 = 0, d1 = 0;
+        if (s) {
+            if (hipStreamGetDevice(s, &d0) != hipSuccess) return KDA_ERR_HIP;
+        } else {
+            int cur = 0;
+            if (hipGetDevice(&cur) != hipSuccess) return KDA_ERR_HIP;
+            d0 = cur;
+        }
+        if (hipStreamGetDevice(static_cast<hipStream_t>(side->stream), &d1) != hipSuccess)
+            return KDA_ERR_HIP;
+        use_side = d0 == d1;
     }
-    if (side) {
+    if (use_side) {
         // prep of every part on the side stream, chain of part p on the
         // caller's stream after the prep of part p; the state between parts
         // lives in the workspace (each chain workgroup reads its slice before
         // writing it back)
+        hipStream_t ss = static_cast<hipStream_t>(side->stream);
+        hipEvent_t ev[KDA_SIDE_EVENTS];
+        for (int i = 0; i < KDA_SIDE_EVENTS; ++i) ev[i] = static_cast<hipEvent_t>(side->events[i]);
         float* spart = reinterpret_cast<float*>(w + sp);
-        if (hipEventRecord(side->ev[0], s) != hipSuccess) return KDA_ERR_HIP;
-        if (hipStreamWaitEvent(side->st, side->ev[0], 0) != hipSuccess) return KDA_ERR_HIP;
+        if (hipEventRecord(ev[0], s) != hipSuccess) return KDA_ERR_HIP;
+        if (hipStreamWaitEvent(ss, ev[0], 0) != hipSuccess) return KDA_ERR_HIP;
         for (int p = 0; p < prt.parts; ++p) {
             kda::PrepArgs pp = pa;
             pp.pc0 = p * prt.len;
             pp.pcn = std::min(prt.len, sh.NC - pp.pc0);
             if (rec.mark("prep_fast") != hipSuccess) return KDA_ERR_HIP;
-            if (kda::launch_prep_fast(io, sh, pp, side->st) != hipSuccess) return KDA_ERR_HIP;
+            if (kda::launch_prep_fast(io, sh, pp, ss) != hipSuccess) return KDA_ERR_HIP;
             if (rec.done() != hipSuccess) return KDA_ERR_HIP;
             if (rec.mark("prep_exact") != hipSuccess) return KDA_ERR_HIP;
-            if (kda::launch_prep_exact(io, sh, pp, side->st) != hipSuccess) return KDA_ERR_HIP;
+            if (kda::launch_prep_exact(io, sh, pp, ss) != hipSuccess) return KDA_ERR_HIP;
             if (rec.done() != hipSuccess) return KDA_ERR_HIP;
-            if (hipEventRecord(side->ev[p + 1], side->st) != hipSuccess) return KDA_ERR_HIP;
+            if (hipEventRecord(ev[p + 1], ss) != hipSuccess) return KDA_ERR_HIP;
         }
         for (int p = 0; p < prt.parts; ++p) {
             kda::ChainArgs cp = ca;
@@ -421,7 +397,7 @@ kda_status_t chunk_forward(const void* q, const void* k, const void* v, const fl
             cp.pcn = std::min(prt.len, sh.NC - cp.pc0);
             cp.S0 = p == 0 ? initial_state : spart;
             cp.ST = p == prt.parts - 1 ? final_state : spart;
-            if (hipStreamWaitEvent(s, side->ev[p + 1], 0) != hipSuccess) return KDA_ERR_HIP;
+            if (hipStreamWaitEvent(s, ev[p + 1], 0) != hipSuccess) return KDA_ERR_HIP;
             if (rec.mark("chain") != hipSuccess) return KDA_ERR_HIP;
             if (launch_forward_chain(io, sh, cp, s) != hipSuccess) return KDA_ERR_HIP;
             if (rec.done() != hipSuccess) return KDA_ERR_HIP;
@@ -1032,6 +1008,19 @@ kda_status_t kda_chunk_forward(const void* q, const void* k, const void* v, cons
     return chunk_forward(q, k, v, alpha, beta, initial_state, out, final_state, nullptr, nullptr,
                          B, T, H, Dk, Dv, chunk, dtype, mode, flags, workspace, workspace_bytes,
                          stream);
+}
+
+kda_status_t kda_chunk_forward_side(const void* q, const void* k, const void* v,
+                                    const float* alpha, const float* beta,
+                                    const float* initial_state, void* out, float* final_state,
+                                    int B, int T, int H, int Dk, int Dv, int chunk,
+                                    kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
+                                    void* workspace, size_t workspace_bytes, void* stream,
+                                    const kda_side_t* side)
+{
+    return chunk_forward(q, k, v, alpha, beta, initial_state, out, final_state, nullptr, nullptr,
+                         B, T, H, Dk, Dv, chunk, dtype, mode, flags, workspace, workspace_bytes,
+                         stream, nullptr, side);
 }
 
 kda_status_t kda_chunk_forward_noalloc(const void* q, const void* k, const void* v,

@@ -1,7 +1,9 @@
 // range_check.hip — the device range check behind KDA_FLAG_VALIDATE_RANGES.
-// Ranges: KDA gates in (0, 1] and write strengths in [0, 1] ("Semidirect
-// Fourier Delta Attention", §3); CKDA gates in [-1, 1] and write strengths in
-// [0, 2] ("Complex KDA", the abstract).
+// Ranges: KDA gates in [0, 1] and write strengths in [0, 1] (the layer of
+// "Semidirect Fourier Delta Attention", §3, draws its per-channel decays from
+// [0, 1]^d; a zero gate forgets the channel: "Kimi Delta Attention: a bounded
+// case study", §12.1); CKDA gates in [-1, 1] and write strengths in [0, 2]
+// ("Complex KDA", the abstract).
 #include "range_check.hpp"
 #include <map>
 #include <mutex>
@@ -14,8 +16,7 @@ namespace {
 __device__ unsigned g_range_flag;
 
 struct Bounds {
-    float alo, ahi, bhi;
-    int aopen;          // 1: alpha must exceed alo (KDA excludes 0)
+    float alo, ahi, bhi;    // alpha in [alo, ahi], beta in [0, bhi]
 };
 
 __global__ __launch_bounds__(64) void range_clear_kernel(unsigned* flag)
@@ -35,7 +36,7 @@ __global__ __launch_bounds__(256) void range_check_kernel(const float* __restric
     bool bad = false;
     for (size_t i = i0; i < na; i += stride) {
         const float x = a[i];
-        bad |= !((r.aopen ? x > r.alo : x >= r.alo) && x <= r.ahi);
+        bad |= !(x >= r.alo && x <= r.ahi);
     }
     for (size_t i = i0; i < nb; i += stride) {
         const float x = b[i];
@@ -76,7 +77,7 @@ RangeResult check_ranges(const float* alpha, size_t na, const float* beta, size_
         g_flag_ptr[dev] = flag;
     }
 
-    const Bounds r = ckda ? Bounds{-1.f, 1.f, 2.f, 0} : Bounds{0.f, 1.f, 1.f, 1};
+    const Bounds r = ckda ? Bounds{-1.f, 1.f, 2.f} : Bounds{0.f, 1.f, 1.f};
     hipLaunchKernelGGL(range_clear_kernel, dim3(1), dim3(64), 0, stream, flag);
     if (hipGetLastError() != hipSuccess) return RangeResult::HipError;
     const size_t n = na > nb ? (na > nt ? na : nt) : (nb > nt ? nb : nt);

@@ -7,7 +7,7 @@
  *   o_t = S_t^T q_t
  * Update: "Semidirect Fourier Delta Attention" (arXiv 2607.11897), §1 eq. (1)
  * and the affine form §2.2 eq. (9); read-out from the post-update state with no
- * scale factor: same page, §3 eq. (14).  Ranges: KDA has alpha in (0,1] and
+ * scale factor: same page, §3 eq. (14).  Ranges: KDA has alpha in [0,1] and
  * beta in [0,1] (same page, §3); CKDA allows alpha in [-1,1] and beta in [0,2]
  * ("Complex KDA: Understanding and Enhancing the Expressivity of Kimi Delta
  * Attention", the abstract).  The state S is d_k x d_v (§2.2), decayed along
@@ -17,16 +17,18 @@
  *  - Every tensor pointer is a DEVICE pointer owned by the caller; the library
  *    never allocates or frees memory, never synchronises (except where a flag
  *    says so) and never keeps a pointer after the call returns.  It creates
- *    one stream and a few events per device, on first use, for the parts
- *    path of the chunked forward (KDA_FLAG_SINGLE_STREAM).
+ *    no stream; events only for KDA_FLAG_STAGE_EVENTS (on first use).  The
+ *    second stream of the overlapped forward is the caller's
+ *    (kda_chunk_forward_side).
  *  - Layouts are row-major and contiguous:
  *      q, k, alpha : [B, T, H, Dk]     v, out : [B, T, H, Dv]    beta : [B, T, H]
  *      state       : [B, H, Dk, Dv]
  *    (decode uses the same layouts with T = 1).
  *  - q, k, v and out share `dtype`; alpha, beta and every state are fp32.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream),
- *    part of it on the library's second stream where KDA_FLAG_SINGLE_STREAM
- *    says so, joined back to `stream` by events, and is asynchronous: argument errors are reported synchronously, before any
+ *    part of it on the caller's second stream for kda_chunk_forward_side,
+ *    joined back to `stream` by the caller's events, and is asynchronous:
+ *    argument errors are reported synchronously, before any
  *    HIP call is made; launch failures come back as KDA_ERR_HIP; faults during
  *    execution surface at the caller's next synchronisation.
  *  - The library does not normalise q or k, applies no gate parameterisation
@@ -49,7 +51,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 14
+#define KDA_ABI_VERSION 15
 
 typedef enum {
     KDA_OK = 0,
@@ -67,14 +69,14 @@ typedef enum {
 typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype_t;
 
 /* Admissible input ranges.  The mathematics is identical for both; the mode
- * states the caller's contract (KDA: alpha in (0,1], beta in [0,1]; CKDA:
+ * states the caller's contract (KDA: alpha in [0,1], beta in [0,1]; CKDA:
  * alpha in [-1,1] incl. exact 0 and -1, beta in [0,2]).  Inputs outside the
  * stated range give results of the same formula but carry no accuracy
  * guarantee. */
 typedef enum { KDA_MODE_KDA = 0, KDA_MODE_CKDA = 1 } kda_mode_t;
 
 /* flags: check the inputs against the mode's ranges on the device before any
- * work is enqueued: every alpha in (0,1] (KDA) or [-1,1] (CKDA), every beta in
+ * work is enqueued: every alpha in [0,1] (KDA) or [-1,1] (CKDA), every beta in
  * [0,1] (KDA) or [0,2] (CKDA), every theta of the phase variant finite; NaN is
  * out of range.  One extra read of alpha, beta (and theta); the call then
  * synchronises `stream` and returns KDA_ERR_RANGE, with nothing enqueued and
@@ -100,18 +102,9 @@ typedef enum { KDA_MODE_KDA = 0, KDA_MODE_CKDA = 1 } kda_mode_t;
  * states are chained in fp32, and every segment then runs from its own start.
  * The results agree with the unsegmented path up to rounding. */
 #define KDA_FLAG_NO_SEGMENTS 4u
-/* flags: run every kernel on the caller's stream.  By default a dense forward
- * whose chains would leave half the GPU or more idle (at most 128 of them, and
- * no segments) and that has at least 256 chunks runs its chunks in consecutive
- * parts: the per-chunk factors of part p + 1 are formed on a second stream of
- * the library's own (one per device, default priority, kept until the
- * process ends) while the chain runs part p on the caller's stream, joined
- * by events, so the call still ends on the caller's stream (a graph captured
- * from the caller's stream takes in both; the second stream is never created
- * during a capture, so a call captured before any uncaptured call of that
- * shape on the device keeps to one stream; a caller stream of another device
- * than the current one also keeps to one stream).  The results are bitwise
- * those of the single-stream path. */
+/* flags: with kda_chunk_forward_side, run every kernel on `stream` anyway (the
+ * side stream and its events are not touched).  Calls without a side stream
+ * always run on `stream` alone. */
 #define KDA_FLAG_SINGLE_STREAM 8u
 
 /* ABI version of the loaded library (KDA_ABI_VERSION it was built with). */
@@ -203,6 +196,46 @@ typedef struct {
     int normalize_q;
 } kda_prologue_t;
 
+/* Events a kda_side_t carries: one marks the call's start on `stream`, one
+ * marks the end of each part's chunk factors on the side stream. */
+#define KDA_SIDE_EVENTS 9
+
+/* A second stream and events owned by the caller, lent to one call of
+ * kda_chunk_forward_side.  stream: a hipStream_t (default priority) of the same
+ * device as the call's stream (another device's stream is ignored: the call
+ * then keeps to its own stream); events: KDA_SIDE_EVENTS distinct hipEvent_t
+ * (timing may be disabled).  The library records and waits on them only
+ * during the call's enqueue; calls enqueued one after another may share one
+ * kda_side_t, calls enqueued concurrently from several host threads may not. */
+typedef struct {
+    void* stream;
+    void* events[KDA_SIDE_EVENTS];
+} kda_side_t;
+
+/*
+ * kda_chunk_forward with a second stream for the overlap of the chunk-factor
+ * kernels (intra-chunk WY, "Semidirect Fourier Delta Attention" §2.2) with the
+ * state chain: when the (b, h, 16-column) chains number at most 128 (half the
+ * GPU or less), no sequence segments are chosen and there are at least 256
+ * chunks, the chunks of every (b, h) run in 8 consecutive parts: the factors
+ * of part p + 1 are formed on side->stream while the chain runs part p on
+ * `stream`, joined by side->events, so the call still ends on `stream` (a graph
+ * captured from `stream` takes in the side stream through the events).  The
+ * state crosses part boundaries in fp32, so results are bitwise those of
+ * kda_chunk_forward.  Other shapes, side == NULL or KDA_FLAG_SINGLE_STREAM run
+ * as kda_chunk_forward.  The workspace query is kda_chunk_forward_workspace_size
+ * (it reserves the state between parts whenever the shape would run in
+ * parts).  Errors: those of kda_chunk_forward; a NULL side->stream or event
+ * is KDA_ERR_NULL_POINTER.
+ */
+kda_status_t kda_chunk_forward_side(const void* q, const void* k, const void* v,
+                                    const float* alpha, const float* beta,
+                                    const float* initial_state, void* out, float* final_state,
+                                    int B, int T, int H, int Dk, int Dv, int chunk,
+                                    kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
+                                    void* workspace, size_t workspace_bytes, void* stream,
+                                    const kda_side_t* side);
+
 /* Size of the built-in scratch of kda_chunk_forward_noalloc (bytes per device). */
 #define KDA_NOALLOC_SCRATCH_BYTES (32u << 20)
 
@@ -218,7 +251,7 @@ typedef struct {
  *  - shapes whose kda_chunk_forward_workspace_size() exceeds
  *    KDA_NOALLOC_SCRATCH_BYTES return KDA_ERR_SCRATCH_LIMIT (checked before any
  *    HIP call);
- *  - all work runs on `stream` (as with KDA_FLAG_SINGLE_STREAM), and the flags
+ *  - all work runs on `stream`, and the flags
  *    KDA_FLAG_STAGE_EVENTS and KDA_FLAG_VALIDATE_RANGES are refused
  *    (KDA_ERR_UNSUPPORTED): the call creates no stream or event and makes no
  *    allocating call;

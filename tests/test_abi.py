@@ -40,13 +40,13 @@ def test_exports_every_declared_symbol(lib):
             "kda_chunk_backward_varlen", "kda_chunk_backward_varlen_workspace_size",
             "kda_chunk_backward_varlen_prologue", "kda_chunk_backward_varlen_prologue_workspace_size",
             "kda_gate_prep", "kda_status_string", "kda_abi_version",
-            "kda_chunk_forward_noalloc"} <= set(syms)
+            "kda_chunk_forward_noalloc", "kda_chunk_forward_side"} <= set(syms)
     for s in syms:
         assert hasattr(lib, s), s
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 14
+    assert lib.kda_abi_version() == 15
     for s in range(10):
         assert lib.kda_status_string(s) != b"unknown status"
     assert lib.kda_status_string(99) == b"unknown status"
@@ -482,3 +482,23 @@ def test_noalloc_refusals_before_any_hip_call(lib):
     assert call(0, 64, 1, 128, 64, BF16, 0) == SHAPE
     assert call(1, 64, 1, 24, 64, BF16, 0) == UNSUP
     assert lib.kda_status_string(SCRATCH_LIMIT) != b"unknown status"
+
+
+def test_side_stream_refusals_before_any_hip_call(lib):
+    """kda_chunk_forward_side: a side argument with a NULL stream or a NULL
+    event is KDA_ERR_NULL_POINTER, found before any HIP call; shape errors keep
+    their own status."""
+    f = Fake()
+    q, k, v, a, b, o, st, ws = (f() for _ in range(8))
+    side = kda._Side(None, (ctypes.c_void_p * kda.SIDE_EVENTS)(*[f() for _ in range(kda.SIDE_EVENTS)]))
+    lib.kda_chunk_forward_side.argtypes = [ctypes.c_void_p] * 8 + [ctypes.c_int] * 8 + \
+        [ctypes.c_uint, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.POINTER(kda._Side)]
+    nws = ws_size(lib, 1, 4096, 1, 64, 64, 16, F32)[1]
+    call = lambda sd, D=64: lib.kda_chunk_forward_side(q, k, v, a, b, None, o, st, 1, 4096, 1, D, D,
+                                                       16, F32, 1, 0, ws, nws, None, ctypes.byref(sd))
+    assert call(side) == NULLP                     # no stream
+    side.stream = f()
+    side.events[3] = None
+    assert call(side) == NULLP                     # an event missing
+    side.events[3] = f()
+    assert call(side, D=24) == UNSUP               # the shape check still comes first

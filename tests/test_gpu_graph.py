@@ -2,8 +2,8 @@
 captured once from torch's capture stream and replayed several times, with
 the program's own eager work and synchronisations between the replays; every
 replay must equal the eager call bitwise.  Covers the single-pass launch
-sequence and the parts path, whose second stream the capture takes in through
-its events."""
+sequence and the parts path, whose second stream (the caller's, lent to
+kda_chunk_forward_side) the capture takes in through its events."""
 import pytest
 import torch
 
@@ -30,11 +30,13 @@ def test_forward_graph_replay(name, base, ov, parts):
     out = torch.empty((w.B, w.T, w.H, w.Dv), dtype=w.dtype, device="cuda")
     st = torch.empty((w.B, w.H, w.Dk, w.Dv), dtype=torch.float32, device="cuda")
 
+    side = kda.SideStream() if parts else None
+
     def call(o, s, flags=0):
         kda.chunk_forward(d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S0"], chunk=w.chunk,
-                          mode=w.mode, out=o, final_state=s, workspace=ws, flags=flags)
+                          mode=w.mode, out=o, final_state=s, workspace=ws, flags=flags, side=side)
 
-    # eager reference (also creates the side stream when the shape runs in parts)
+    # eager reference
     call(out, st, kda.STAGE_EVENTS)
     torch.cuda.synchronize()
     names = [n for n, _ in kda.last_stage_times()]
@@ -42,11 +44,11 @@ def test_forward_graph_replay(name, base, ov, parts):
     assert names.count("chain") == (8 if parts else 1)
     ref_out, ref_st = out.clone(), st.clone()
 
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
+    other = torch.cuda.Stream()
+    other.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(other):
         call(out, st)
-    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.current_stream().wait_stream(other)
     torch.cuda.synchronize()
 
     g = torch.cuda.CUDAGraph()

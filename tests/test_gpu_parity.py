@@ -395,11 +395,12 @@ def test_forward_kda_bf16_prefill_full():
 
 def test_forward_ckda_long_ctx_full():
     """CKDA bf16 long context, B=1 H=16 T=65536 d=128, S0 ~ N(0, 0.02^2), every
-    head against the oracle (the call the benchmark times: parts path)."""
+    head against the oracle (the call the benchmark times: parts path on a
+    side stream)."""
     w = workloads.workload(3)
     say(f"[forward] ckda_bf16_long_ctx full, all heads {w}")
     inp = workloads.make_prefill(w, device=DEV)
-    out, st = run_gpu(inp, w.chunk, w.mode)
+    out, st = run_gpu(inp, w.chunk, w.mode, side=kda.SideStream())
     o_ref, s_ref = run_oracle(inp)
     eo = slice_err_out(np32(out), o_ref)
     es = slice_err_state(np32(st), s_ref)
@@ -689,8 +690,9 @@ def test_forward_dense_zero_gates(dt):
 
 
 # (name, base workload, overrides, flags) — at most 128 (b, h, 16-column)
-# chains and at least 256 chunks, so the forward runs in parts: chunk factors
-# of part p + 1 on the library's second stream while the chain runs part p
+# chains and at least 256 chunks, so with a side stream the forward runs in
+# parts: chunk factors of part p + 1 on the caller's second stream while the
+# chain runs part p
 PARTS = [
     ("bf16_ckda_d128_c16_H9_T4133_s0", 3, dict(B=1, H=9, T=4133, chunk=16, s0_std=0.2), 0),
     ("f32_kda_d32_c16_B2_T4100_nosegments", 0, dict(B=2, H=1, T=4100, D=32, chunk=16),
@@ -700,78 +702,60 @@ PARTS = [
 
 @pytest.mark.parametrize("name,base,ov,flags", PARTS, ids=[c[0] for c in PARTS])
 def test_forward_parts(name, base, ov, flags):
-    """Prep / chain overlap in parts: the oracle's sequential recurrence, and
-    bitwise the single-stream path (KDA_FLAG_SINGLE_STREAM) for the outputs,
-    the final state and the chunk-start states; the stage list shows one
-    chain launch per part."""
+    """Prep / chain overlap in parts on a caller-owned side stream
+    (kda_chunk_forward_side): the oracle's sequential recurrence, and bitwise
+    the single-stream path for the outputs and the final state; the stage list
+    shows one chain launch per part.  Without a side stream, or with
+    KDA_FLAG_SINGLE_STREAM, the call keeps to one stream (one chain launch)."""
     w = workloads.workload(base, **ov)
     say(f"[forward parts] {name}: {w}")
     inp = workloads.make_prefill(w, device="cpu")
     o_ref, s_ref = run_oracle(inp)
     d = to_dev(inp)
-    out, st = run_gpu(d, w.chunk, w.mode, flags=flags | kda.STAGE_EVENTS)
+    side = kda.SideStream()
+    out, st = run_gpu(d, w.chunk, w.mode, flags=flags | kda.STAGE_EVENTS, side=side)
     names = _stage_names()
     say(f"  stages {names}")
     assert names.count("chain") == 8 and names.count("prep_fast") == 8
     eo, es = slice_err_out(np32(out), o_ref), slice_err_state(np32(st), s_ref)
     say(f"  err out {eo:.3e} state {es:.3e}{elem_note()}")
     assert eo <= TOL[w.dtype] and es <= TOL[w.dtype]
-    out1, st1 = run_gpu(d, w.chunk, w.mode, flags=flags | kda.SINGLE_STREAM | kda.STAGE_EVENTS)
-    assert _stage_names().count("chain") == 1
-    assert torch.equal(out, out1) and torch.equal(st, st1)
-    # an explicit (non-default) caller stream takes the parts path too
+    for kw in (dict(flags=flags | kda.STAGE_EVENTS),
+               dict(flags=flags | kda.SINGLE_STREAM | kda.STAGE_EVENTS, side=side)):
+        out1, st1 = run_gpu(d, w.chunk, w.mode, **kw)
+        assert _stage_names().count("chain") == 1
+        assert torch.equal(out, out1) and torch.equal(st, st1)
+    # an explicit (non-default) caller stream with the side stream
     cs_ = torch.cuda.Stream()
     cs_.wait_stream(torch.cuda.current_stream())
-    out2, st2 = run_gpu(d, w.chunk, w.mode, flags=flags | kda.STAGE_EVENTS, stream=cs_)
+    out2, st2 = run_gpu(d, w.chunk, w.mode, flags=flags | kda.STAGE_EVENTS, stream=cs_, side=side)
     assert _stage_names().count("chain") == 8
     assert torch.equal(out, out2) and torch.equal(st, st2)
-    nc = (w.T + w.chunk - 1) // w.chunk
-    cs = [torch.full((w.B, w.H, nc, w.Dk, w.Dv), float("nan"), dtype=w.dtype, device=DEV)
-          for _ in range(2)]
-    for c, fl in zip(cs, (flags, flags | kda.SINGLE_STREAM)):
-        o2, s2 = run_gpu(d, w.chunk, w.mode, flags=fl, chunk_states=c)
-        assert torch.equal(o2, out) and torch.equal(s2, st)
-    assert torch.equal(cs[0], cs[1])
+    # the same side stream lent to two calls enqueued back to back
+    outs = [run_gpu(d, w.chunk, w.mode, flags=flags, side=side) for _ in range(2)]
+    for o3, s3 in outs:
+        assert torch.equal(o3, out) and torch.equal(s3, st)
 
 
-def test_forward_prologue_parts_bitwise():
-    """The raw-input forward in parts equals its single-stream path bitwise."""
+def test_forward_phase_long_single_stream():
+    """The phase variant at a shape the plain forward would run in parts with a
+    side stream: one stream, one chain launch, against the oracle's phase
+    recurrence."""
     w = workloads.workload(3, B=1, H=9, T=4133, chunk=16, s0_std=0.2)
-    say(f"[forward prologue parts] {w}")
-    r = to_dev(workloads.make_prefill_raw(w, forget_frac=0.01))
-    res = []
-    for fl in (0, kda.SINGLE_STREAM):
-        res.append(kda.chunk_forward_prologue(r["q"], r["k"], r["v"], r["gate"], r["beta_logit"],
-                                              r["S0"], alpha_min=-1.0, alpha_max=1.0,
-                                              beta_max=2.0, chunk=w.chunk, mode=w.mode,
-                                              flags=fl))
-    torch.cuda.synchronize()
-    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
-
-
-def test_forward_phase_parts():
-    """The phase variant in parts: the oracle's phase recurrence, and bitwise
-    its single-stream path (outputs and final state); one chain launch per
-    part."""
-    w = workloads.workload(3, B=1, H=9, T=4133, chunk=16, s0_std=0.2)
-    say(f"[forward phase parts] {w}")
+    say(f"[forward phase long] {w}")
     inp = workloads.make_prefill_phase(w, theta_max=2.0)
     o_ref, s_ref = oracle.forward_phase(np32(inp["q"]), np32(inp["k"]), np32(inp["v"]),
                                         np32(inp["alpha"]), np32(inp["theta"]), np32(inp["beta"]),
                                         np32(inp["S0"]), nthreads=oracle_threads())
     d = to_dev(inp)
-    res = []
-    for fl in (kda.STAGE_EVENTS, kda.SINGLE_STREAM | kda.STAGE_EVENTS):
-        res.append(kda.chunk_forward_phase(d["q"], d["k"], d["v"], d["alpha"], d["theta"], d["beta"],
-                                           d["S0"], chunk=w.chunk, mode=w.mode, flags=fl))
-        torch.cuda.synchronize()
-        names = [n for n, _ in kda.last_stage_times()]
-        assert names.count("chain") == (8 if fl == kda.STAGE_EVENTS else 1)
-    (out, st), (out1, st1) = res
+    out, st = kda.chunk_forward_phase(d["q"], d["k"], d["v"], d["alpha"], d["theta"], d["beta"],
+                                      d["S0"], chunk=w.chunk, mode=w.mode, flags=kda.STAGE_EVENTS)
+    torch.cuda.synchronize()
+    names = [n for n, _ in kda.last_stage_times()]
+    assert names.count("chain") == 1
     eo, es = slice_err_out(np32(out), o_ref), slice_err_state(np32(st), s_ref)
     say(f"  err out {eo:.3e} state {es:.3e}{elem_note()}")
     assert eo <= TOL[w.dtype] and es <= TOL[w.dtype]
-    assert torch.equal(out, out1) and torch.equal(st, st1)
 
 
 @pytest.mark.parametrize("dt,Dk,Dv,mode,pro", [

@@ -1,8 +1,9 @@
 """KDA_FLAG_VALIDATE_RANGES through the C ABI: in-range inputs give results
 bitwise equal to an unchecked call; one element outside the mode's ranges
-(KDA: alpha in (0,1], beta in [0,1]; CKDA: alpha in [-1,1], beta in [0,2];
-NaN anywhere) gives status KDA_ERR_RANGE with the outputs untouched; under
-graph capture the flag is refused before anything is enqueued."""
+(KDA: alpha in [0,1], beta in [0,1]; CKDA: alpha in [-1,1], beta in [0,2];
+NaN anywhere; the phase variant's theta finite) gives status KDA_ERR_RANGE
+with the outputs untouched; under graph capture the flag is refused before
+anything is enqueued."""
 import pytest
 import torch
 
@@ -16,7 +17,10 @@ NAN = float("nan")
 
 # (name, mode, tensor, index, value, rejected)
 CASES = [
-    ("kda_alpha_zero", kda.KDA, "alpha", (0, 5, 1, 3), 0.0, True),
+    ("kda_alpha_zero", kda.KDA, "alpha", (0, 5, 1, 3), 0.0, False),
+    ("kda_alpha_below_zero", kda.KDA, "alpha", (0, 5, 1, 3), -1e-30, True),
+    ("kda_alpha_one", kda.KDA, "alpha", (0, 6, 0, 3), 1.0, False),
+    ("kda_alpha_above_one", kda.KDA, "alpha", (0, 6, 0, 3), 1.0000001, True),
     ("kda_alpha_negative", kda.KDA, "alpha", (0, 77, 0, 0), -0.5, True),
     ("ckda_alpha_negative", kda.CKDA, "alpha", (0, 77, 0, 0), -0.5, False),
     ("ckda_alpha_minus_one", kda.CKDA, "alpha", (0, 1, 1, 9), -1.0, False),
@@ -120,3 +124,43 @@ def test_refused_under_capture():
             status = e.status
     torch.cuda.synchronize()
     assert status == UNSUP
+
+
+INF = float("inf")
+
+
+@pytest.mark.parametrize("name,val,bad", [("theta_nan", NAN, True), ("theta_inf", INF, True),
+                                          ("theta_minus_inf", -INF, True),
+                                          ("theta_large_finite", 1.0e4, False)],
+                         ids=["theta_nan", "theta_inf", "theta_minus_inf", "theta_large_finite"])
+def test_phase_theta(name, val, bad):
+    """The phase variant (chunked forward and decode step) checks every theta
+    for finiteness: NaN or +-inf gives KDA_ERR_RANGE with nothing written; a
+    large finite phase is in range."""
+    w = workloads.workload(3, B=1, H=2, T=130, chunk=64, s0_std=0.1)
+    say(f"[ranges] phase {name}: {w}")
+    d = {k: (None if v is None else v.to("cuda"))
+         for k, v in workloads.make_prefill_phase(w, theta_max=2.0).items()}
+    d["theta"][0, 70, 1, 5] = val
+    out = torch.full((w.B, w.T, w.H, w.Dv), 7.0, dtype=w.dtype, device="cuda")
+    t = 70
+    sl = lambda x: x[:, t].contiguous()
+    S = torch.zeros((w.B, w.H, w.Dk, w.Dv), dtype=torch.float32, device="cuda")
+    args = (sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(d["alpha"]), sl(d["theta"]), sl(d["beta"]), S)
+    if bad:
+        with pytest.raises(kda.KdaError) as e:
+            kda.chunk_forward_phase(d["q"], d["k"], d["v"], d["alpha"], d["theta"], d["beta"],
+                                    d["S0"], chunk=w.chunk, mode=w.mode, out=out,
+                                    flags=kda.VALIDATE_RANGES)
+        assert e.value.status == RANGE
+        with pytest.raises(kda.KdaError) as e:
+            kda.decode_step_phase(*args, mode=w.mode, flags=kda.VALIDATE_RANGES)
+        assert e.value.status == RANGE
+        torch.cuda.synchronize()
+        assert bool((out == 7.0).all()) and bool((S == 0).all())
+    else:
+        kda.chunk_forward_phase(d["q"], d["k"], d["v"], d["alpha"], d["theta"], d["beta"],
+                                d["S0"], chunk=w.chunk, mode=w.mode, out=out,
+                                flags=kda.VALIDATE_RANGES)
+        kda.decode_step_phase(*args, mode=w.mode, flags=kda.VALIDATE_RANGES)
+        torch.cuda.synchronize()
