@@ -15,6 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkda.so")
+PROBE_LIB = os.path.join(HERE, "libkda_probe.so")
+PROBE_SOURCE = "probe.hip"
 SOURCES = ["decode.hip", "gate_prep.hip", "prep_fast.hip", "prep_exact.hip", "chain.hip", "chain_wide.hip",
            "chunk_util.hip", "bwd.hip", "range_check.hip", "kda_api.hip"]
 ARCH = "gfx950"
@@ -55,8 +57,15 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    # the peak-rate probes of the measurement leg: a library of their own
+    pobj = _compile(PROBE_SOURCE)
+    r = subprocess.run([_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o",
+                        PROBE_LIB + ".tmp", pobj], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"probe link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 
