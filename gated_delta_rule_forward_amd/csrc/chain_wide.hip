@@ -353,7 +353,9 @@ hipError_t launch_wide_t(const ChunkShape& s, const ChainArgs& a, hipStream_t st
 
 // Column tiles per workgroup of the wide chain for this shape, or 0 when the
 // 16-column chain of chain.hip should run instead.  Covered: chunk 64, Dk 128
-// or 64, one column tile (16 columns) per workgroup.  Chosen only when the
+// or 64, one column tile (16 columns) per workgroup.  Always used for fp32
+// with Dk = 128 (whose operands do not fit the 16-column kernel's LDS
+// staging), otherwise chosen only when the
 // (b, h, 16-column) chains number at most 64: there it measured faster
 // (B=1, H=2, T=65536, d=128, bf16: 0.75 ms against 0.96 ms; 0.72 against
 // 0.92 us per chunk step at H=8), while with 128 or 256 chains both kernels
@@ -364,8 +366,8 @@ hipError_t launch_wide_t(const ChunkShape& s, const ChainArgs& a, hipStream_t st
 // slower still (1.38 us per step at H=32).
 int wide_chain_tiles(IoType io, const ChunkShape& s)
 {
-    (void)io;
     if (s.C != 64 || (s.Dk != 128 && s.Dk != 64)) return 0;
+    if (io == IoType::F32 && s.Dk == 128) return 1;      // the only chain for this form
     if ((long long)s.B * s.H * (s.Dv / 16) > 64) return 0;
     return 1;
 }

@@ -123,7 +123,8 @@ kda_status_t check_forward_shape(int B, int T, int H, int Dk, int Dv, int chunk,
     if (B < 1 || H < 1 || T < 0) return KDA_ERR_BAD_SHAPE;
     if (dtype != KDA_DTYPE_F32 && dtype != KDA_DTYPE_BF16) return KDA_ERR_UNSUPPORTED;
     if (!dk_ok(Dk) || !dv_ok(Dv) || !chunk_ok(chunk)) return KDA_ERR_UNSUPPORTED;
-    if (dtype == KDA_DTYPE_F32 && (Dk > 64 || Dv > 64)) return KDA_ERR_UNSUPPORTED;
+    // fp32 with Dk = 128: the chain is the register-operand kernel, chunk 64 only
+    if (dtype == KDA_DTYPE_F32 && Dk == 128 && chunk != 64) return KDA_ERR_UNSUPPORTED;
     const long long NC = ((long long)T + chunk - 1) / chunk;
     const long long units = (long long)B * H * NC;
     if (units > 0x7fffffffLL || (long long)B * H * (Dv / 16) > 0x7fffffffLL)
@@ -145,8 +146,10 @@ ChunkShape make_shape(int B, int T, int H, int Dk, int Dv, int chunk)
 // then every segment runs the normal chain from its own start).  nseg <= 1:
 // no segments.  The summary pass must fit one round of workgroups.
 struct Segments { int nseg, seg; };
-Segments segments_for(int B, int H, int Dk, int Dv, int NC)
+Segments segments_for(int B, int H, int Dk, int Dv, int NC, kda_dtype_t dtype)
 {
+    // (the summary pass runs on the 16-column chain, which has no fp32 Dk = 128 form)
+    if (dtype == KDA_DTYPE_F32 && Dk == 128) return {1, NC};
     const long long chains = (long long)B * H * (Dv / 16);
     if (chains > 64 || NC < 128) return {1, NC};
     const long long per = (long long)B * H * ((Dk + Dv) / 16);   // summary workgroups per segment
@@ -187,7 +190,7 @@ size_t dense_layout(int B, int T, int H, int Dk, int Dv, int chunk, IoType io,
 {
     const ChunkShape sh = make_shape(B, T, H, Dk, Dv, chunk);
     size_t n = kda::chunk_workspace_layout(sh, io, off);
-    const Segments sgm = segments_for(B, H, Dk, Dv, sh.NC);
+    const Segments sgm = segments_for(B, H, Dk, Dv, sh.NC, io == IoType::F32 ? KDA_DTYPE_F32 : KDA_DTYPE_BF16);
     *summ_off = *sseg_off = 0;
     if (sgm.nseg > 1) {
         const size_t bhs = (size_t)B * H * sgm.nseg;
@@ -338,7 +341,7 @@ kda_status_t chunk_forward(const void* q, const void* k, const void* v, const fl
                            nullptr, nullptr, 0, theta};
     pa.ntst = workspace_nt((long long)B * H * (Dv / 16));
     const Segments sgm = (flags & KDA_FLAG_NO_SEGMENTS) ? Segments{1, sh.NC}
-                                                          : segments_for(B, H, Dk, Dv, sh.NC);
+                                                          : segments_for(B, H, Dk, Dv, sh.NC, dtype);
     const Parts prt = (!side || sgm.nseg > 1 || (flags & KDA_FLAG_SINGLE_STREAM))
                           ? Parts{1, sh.NC} : parts_for(B, H, Dk, Dv, sh.NC);
     size_t so = 0, ss = 0, sp = 0;
@@ -570,6 +573,7 @@ kda_status_t check_backward_shape(int B, int T, int H, int Dk, int Dv, int chunk
     if (st != KDA_OK) return st;
     if (chunk != 32 && chunk != 64) return KDA_ERR_UNSUPPORTED;
     if (Dk != 32 && Dk != 64 && Dk != 128) return KDA_ERR_UNSUPPORTED;
+    if (dtype == KDA_DTYPE_F32 && (Dk > 64 || Dv > 64)) return KDA_ERR_UNSUPPORTED;
     return KDA_OK;
 }
 

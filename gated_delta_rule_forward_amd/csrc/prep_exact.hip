@@ -26,26 +26,34 @@ constexpr int kPrepThreads = 256;
 template <typename T, int C, int DK>
 struct PrepLds {
     static constexpr int NB = C / 16;                      // 16-token blocks per chunk
-    static constexpr int DVMAX = sizeof(T) == 4 ? 64 : 128;
+    static constexpr int DVMAX = 128;
     static constexpr int KG_ROWS = 16 * NB * (NB - 1) / 2;  // sum over a of 16a
+    // fp32 with Dk = 128: the off-diagonal factor tables are built and
+    // contracted for half the channels at a time (CH passes of DKH channels),
+    // and beta K * Gamma (X) is written over the staged Q (each channel's
+    // column once its own tables are built), so the whole layout fits 160 KB
+    static constexpr bool BIG = sizeof(T) == 4 && DK == 128;
+    static constexpr int CH = BIG ? 2 : 1;
+    static constexpr int DKH = DK / CH;
     static constexpr size_t al16(size_t x) { return (x + 15) & ~size_t(15); }
     static constexpr size_t K = 0;                                   // T[C][DK]
     static constexpr size_t Q = al16(K + sizeof(T) * C * DK);        // T[C][DK]
     static constexpr size_t A = al16(Q + sizeof(T) * C * DK);        // float[C][C]
     static constexpr size_t BETA = al16(A + 4 * C * C);              // float[C]
-    static constexpr size_t X = al16(BETA + 4 * C);                  // T[C][DK]
-    static constexpr size_t TI = al16(X + sizeof(T) * C * DK);       // T[C][C]
+    static constexpr size_t X = BIG ? Q : al16(BETA + 4 * C);        // T[C][DK]
+    static constexpr size_t TI = BIG ? al16(BETA + 4 * C) : al16(X + sizeof(T) * C * DK);   // T[C][C]
     static constexpr size_t UNI = al16(TI + sizeof(T) * C * C);      // union
     // union members
     static constexpr size_t SZ_AL = 4 * C * DK;                                    // float[C][DK]
-    static constexpr size_t KF = 0;                                                // T[NB-1][16][DK]
-    static constexpr size_t QF = al16(KF + sizeof(T) * 16 * (NB > 1 ? NB - 1 : 0) * DK);
-    static constexpr size_t KG = al16(QF + sizeof(T) * 16 * (NB > 1 ? NB - 1 : 0) * DK);
-    static constexpr size_t SZ_FAC = al16(KG + sizeof(T) * KG_ROWS * DK);
+    static constexpr size_t KF = 0;                                                // T[NB-1][16][DKH]
+    static constexpr size_t QF = al16(KF + sizeof(T) * 16 * (NB > 1 ? NB - 1 : 0) * DKH);
+    static constexpr size_t KG = al16(QF + sizeof(T) * 16 * (NB > 1 ? NB - 1 : 0) * DKH);
+    static constexpr size_t SZ_FAC = al16(KG + sizeof(T) * KG_ROWS * DKH);
     static constexpr size_t SZ_Y = sizeof(T) * C * DVMAX;                          // T[C][DVMAX]
     static constexpr size_t SZ_UNI =
         SZ_AL > SZ_FAC ? (SZ_AL > SZ_Y ? SZ_AL : SZ_Y) : (SZ_FAC > SZ_Y ? SZ_FAC : SZ_Y);
     static constexpr size_t TOTAL = al16(UNI + SZ_UNI);
+    static_assert(TOTAL <= 160 * 1024, "LDS of one workgroup");
 };
 
 
@@ -240,14 +248,15 @@ __global__ __launch_bounds__(kPrepThreads) void prep_exact_kernel(PrepArgs args,
     __syncthreads();   // sAl is dead from here on (the union is reused)
     if (tid < DK) {
         const int c = tid;
-        // Gamma_r = rho(r, -1): Q*Gamma (global) and diag(beta) K*Gamma (LDS)
+        // Gamma_r = rho(r, -1): Q*Gamma (global) and diag(beta) K*Gamma (LDS;
+        // written in the table pass below when X shares Q's space)
         float gm = 1.f;
 #pragma unroll
         for (int r = 0; r < C; ++r) {
             gm *= a[r];
             const float kr = to_f32(sK[r * DK + c]), qr = to_f32(sQ[r * DK + c]);
             QGg[frag_off<KB>(r, c, DK)] = from_f32<T>(qr * gm);
-            sX[r * DK + c] = from_f32<T>(sBeta[r] * kr * gm);
+            if constexpr (!L::BIG) sX[r * DK + c] = from_f32<T>(sBeta[r] * kr * gm);
         }
         // Ktil_i = k_i rho(C-1, i), stored transposed (row c), 16-byte stores
         float kt[C];
@@ -273,42 +282,78 @@ __global__ __launch_bounds__(kPrepThreads) void prep_exact_kernel(PrepArgs args,
         GCg[c] = gm;
 #pragma unroll
         for (int i = 0; i < C; ++i) Ktg[frag_off<KB>(c, i, C)] = from_f32<T>(kt[i]);
-        // off-diagonal block a: rows r in block a scaled by rho(r, e_a), columns
-        // i < 16a by rho(e_a, i), e_a = 16a - 1
+    }
+
+    // ---- phase 3b / 4: off-diagonal blocks of A and P, CH channel passes -------
+    // pass hh: the channels [hh DKH, (hh + 1) DKH) write their factor tables
+    // (off-diagonal block a: rows r in block a scaled by rho(r, e_a), columns
+    // i < 16a by rho(e_a, i), e_a = 16a - 1), then every wave adds the pass's
+    // contraction to its tiles' accumulators
+    constexpr int NTILE = NB * (NB - 1);             // (a, b < a, A or P) tiles
+    constexpr int TPW = NTILE > 0 ? (NTILE + 3) / 4 : 1;
+    f32x4 acc4[TPW];
 #pragma unroll
-        for (int ab = 1; ab < NB; ++ab) {
-            float f = 1.f;
+    for (int j = 0; j < TPW; ++j) acc4[j] = zero4();
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-                const int r = 16 * ab + rr;
-                f *= a[r];
-                sKF[((ab - 1) * 16 + rr) * DK + c] = from_f32<T>(to_f32(sK[r * DK + c]) * f);
-                sQF[((ab - 1) * 16 + rr) * DK + c] = from_f32<T>(to_f32(sQ[r * DK + c]) * f);
+    for (int hh = 0; hh < L::CH; ++hh) {
+        __syncthreads();   // (hh = 0: sAl dead; hh > 0: the previous tables read)
+        if (tid >= hh * L::DKH && tid < (hh + 1) * L::DKH) {
+            const int c = tid, cc = c - hh * L::DKH;
+#pragma unroll
+            for (int ab = 1; ab < NB; ++ab) {
+                float f = 1.f;
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    const int r = 16 * ab + rr;
+                    f *= a[r];
+                    sKF[((ab - 1) * 16 + rr) * L::DKH + cc] = from_f32<T>(to_f32(sK[r * DK + c]) * f);
+                    sQF[((ab - 1) * 16 + rr) * L::DKH + cc] = from_f32<T>(to_f32(sQ[r * DK + c]) * f);
+                }
+                T* kg = sKG + 16 * (ab * (ab - 1) / 2) * L::DKH;
+                float gg = 1.f;
+#pragma unroll
+                for (int i = 16 * ab - 1; i >= 0; --i) {
+                    kg[i * L::DKH + cc] = from_f32<T>(to_f32(sK[i * DK + c]) * gg);
+                    gg *= a[i];
+                }
             }
-            T* kg = sKG + 16 * (ab * (ab - 1) / 2) * DK;
-            float gg = 1.f;
+            if constexpr (L::BIG) {
+                // this channel's Q column is no longer read: X takes its place
+                float gx = 1.f;
 #pragma unroll
-            for (int i = 16 * ab - 1; i >= 0; --i) {
-                kg[i * DK + c] = from_f32<T>(to_f32(sK[i * DK + c]) * gg);
-                gg *= a[i];
+                for (int r = 0; r < C; ++r) {
+                    gx *= a[r];
+                    sX[r * DK + c] = from_f32<T>(sBeta[r] * to_f32(sK[r * DK + c]) * gx);
+                }
             }
         }
-    }
-    __syncthreads();
-
-    // ---- phase 4: off-diagonal blocks by MFMA ---------------------------------
-    {
+        __syncthreads();
         int tile = 0;
 #pragma unroll
         for (int ab = 1; ab < NB; ++ab) {
-            const T* kg = sKG + 16 * (ab * (ab - 1) / 2) * DK;
+            const T* kg = sKG + 16 * (ab * (ab - 1) / 2) * L::DKH;
 #pragma unroll
             for (int bb = 0; bb < ab; ++bb) {
 #pragma unroll
                 for (int kind = 0; kind < 2; ++kind, ++tile) {
                     if ((tile & 3) != wave) continue;
-                    const T* op = (kind == 0 ? sKF : sQF) + (ab - 1) * 16 * DK;
-                    const f32x4 acc = tile_tn(op, DK, kg + 16 * bb * DK, DK, DK, zero4());
+                    const T* op = (kind == 0 ? sKF : sQF) + (ab - 1) * 16 * L::DKH;
+                    acc4[tile >> 2] = tile_tn(op, L::DKH, kg + 16 * bb * L::DKH, L::DKH, L::DKH,
+                                              acc4[tile >> 2]);
+                }
+            }
+        }
+    }
+    {
+        int tile = 0;
+#pragma unroll
+        for (int ab = 1; ab < NB; ++ab) {
+#pragma unroll
+            for (int bb = 0; bb < ab; ++bb) {
+#pragma unroll
+                for (int kind = 0; kind < 2; ++kind, ++tile) {
+                    if ((tile & 3) != wave) continue;
+                    const f32x4 acc = acc4[tile >> 2];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int r = 16 * ab + 4 * lg + i, col = 16 * bb + ln;
@@ -411,9 +456,7 @@ hipError_t dispatch_dk(const ChunkShape& s, const PrepArgs& a, hipStream_t st)
     case 16: return launch_exact_t<T, C, 16>(s, a, st);
     case 32: return launch_exact_t<T, C, 32>(s, a, st);
     case 64: return launch_exact_t<T, C, 64>(s, a, st);
-    case 128:
-        if constexpr (sizeof(T) == 2) return launch_exact_t<T, C, 128>(s, a, st);
-        else return hipErrorInvalidValue;
+    case 128: return launch_exact_t<T, C, 128>(s, a, st);
     default: return hipErrorInvalidValue;
     }
 }

@@ -85,7 +85,7 @@ struct FastGeom {
     static constexpr int PADE = 16 / (int)sizeof(T);          // 16-byte row pad
     static constexpr int LDF = C + 4;                         // row stride of fp32 A / Tinv
     static constexpr int NB = C / 16;
-    static constexpr int DVMAX = sizeof(T) == 4 ? 64 : 128;
+    static constexpr int DVMAX = 128;
     static constexpr int XTS = C + PADE;                      // row stride of X_W^T, (beta V)^T
     static constexpr int TV = 16 / (int)sizeof(T);            // tokens per 16-byte run of a V^T row
     // V items: (column quad, run of TV tokens); at most VIT per thread
@@ -134,7 +134,7 @@ __device__ __forceinline__ float frcp(float x) { return __builtin_amdgcn_rcpf(x)
 // kernel on the rotated vectors; Ktil is rotated back by phi_{C-1} and
 // Gamma_{C-1} is stored as (|Gamma| cos phi_{C-1}, |Gamma| sin phi_{C-1}).
 template <typename T, int C, int DK, bool ZS, bool PRO, bool PH, bool NT = false>
-__global__ __launch_bounds__(kThreads, 2) void prep_fast_kernel(PrepArgs args)
+__global__ __launch_bounds__(kThreads, (sizeof(T) == 4 && DK == 128) ? 1 : 2) void prep_fast_kernel(PrepArgs args)
 {
     using G = FastGeom<T, C, DK>;
     using F = Frag<T, G::KB>;
@@ -747,9 +747,7 @@ hipError_t dispatch_dk(const ChunkShape& s, const PrepArgs& a, hipStream_t st)
     case 16: return launch_fast_t<T, C, 16>(s, a, st);
     case 32: return launch_fast_t<T, C, 32>(s, a, st);
     case 64: return launch_fast_t<T, C, 64>(s, a, st);
-    case 128:
-        if constexpr (sizeof(T) == 2) return launch_fast_t<T, C, 128>(s, a, st);
-        else return hipErrorInvalidValue;
+    case 128: return launch_fast_t<T, C, 128>(s, a, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -781,7 +779,6 @@ size_t lds_dk(int Dk)
 size_t prep_fast_lds_bytes(IoType io, int C, int Dk)
 {
     if (io == IoType::F32) {
-        if (Dk > 64) return ~size_t(0);
         return C == 16 ? lds_dk<float, 16>(Dk) : C == 32 ? lds_dk<float, 32>(Dk)
                                                           : lds_dk<float, 64>(Dk);
     }

@@ -35,7 +35,7 @@
  *    and no output scale.
  *  - Supported shapes: Dk in {16, 32, 64, 128}; Dv a multiple of 16 in
  *    [16, 128]; chunk in {16, 32, 64}; B, H >= 1.  With dtype F32 the chunked
- *    forward additionally needs Dk <= 64 and Dv <= 64.
+ *    forward with Dk = 128 additionally needs chunk = 64.
  *  - Alignment: q, k and alpha of the chunked forward, its workspace and the
  *    decode state are read with 16-byte vector accesses and must be 16-byte
  *    aligned; every other pointer must be aligned to its element size
@@ -403,7 +403,8 @@ kda_status_t kda_decode_step_phase(const void* q, const void* k, const void* v,
  *   outputs: dq, dk [B,T,H,Dk] and dv [B,T,H,Dv] in dtype; d_alpha
  *            [B,T,H,Dk] and d_beta [B,T,H] fp32; d_initial_state [B,H,Dk,Dv]
  *            fp32 or NULL (not wanted)
- * Supported: chunk in {32, 64}; Dk in {32, 64, 128} (fp32: Dk, Dv <= 64);
+ * Supported: chunk in {32, 64}; Dk in {32, 64, 128} (fp32: Dk, Dv <= 64, else
+ * KDA_ERR_UNSUPPORTED);
  * Dv a multiple of 16 up to 128.  q, k, d_out, alpha and the workspace are
  * 16-byte aligned, the rest element-aligned.  No output may overlap an input,
  * another output or the workspace.  The workspace (caller-owned, contents

@@ -68,7 +68,10 @@ def test_workspace_size(lib):
     assert ws_size(lib, 1, 10, 1, 24, 16, 16, F32)[0] == UNSUP          # Dk not supported
     assert ws_size(lib, 1, 10, 1, 16, 24, 16, F32)[0] == UNSUP          # Dv not a multiple of 16
     assert ws_size(lib, 1, 10, 1, 16, 16, 48, F32)[0] == UNSUP          # chunk
-    assert ws_size(lib, 1, 10, 1, 128, 16, 16, F32)[0] == UNSUP         # fp32 needs Dk <= 64
+    assert ws_size(lib, 1, 10, 1, 128, 16, 16, F32)[0] == UNSUP         # fp32 Dk 128: chunk 64 only
+    assert ws_size(lib, 1, 10, 1, 128, 16, 32, F32)[0] == UNSUP
+    assert ws_size(lib, 1, 10, 1, 128, 128, 64, F32)[0] == OK
+    assert ws_size(lib, 1, 10, 1, 64, 128, 16, F32)[0] == OK           # fp32 Dv 128, any chunk
     assert ws_size(lib, 0, 10, 1, 16, 16, 16, F32)[0] == SHAPE
     assert ws_size(lib, 1, -1, 1, 16, 16, 16, F32)[0] == SHAPE
     assert ws_size(lib, 1, 10, 1, 16, 16, 16, 7)[0] == UNSUP

@@ -797,3 +797,74 @@ def test_decode_prologue(dt, Dk, Dv, mode, pro):
     eo, es = slice_err_out(o_gpu, o_ref), slice_err_state(np32(S), s_ref)
     say(f"  err out {eo:.3e} state {es:.3e}{elem_note()}")
     assert eo <= TOL[dt] and es <= TOL[dt]
+
+
+# fp32 with Dk or Dv = 128: cfg1-style CKDA inputs (signs, exact -1 and 0 gates,
+# beta up to exactly 2) at d = 128
+F32_128 = [
+    ("f32_ckda_d128_c64_B2_H4_T1024", 1, dict(B=2, H=4, T=1024, D=128, chunk=64), None),
+    ("f32_kda_d128_c64_T201_s0", 0, dict(B=1, H=3, T=201, D=128, chunk=64, s0_std=0.3), None),
+    ("f32_ckda_dk64_dv128_c32_T130", 1, dict(B=1, H=2, T=130, D=64, chunk=32), 128),
+    ("f32_ckda_dk64_dv128_c16_T77_s0", 1, dict(B=2, H=1, T=77, D=64, chunk=16, s0_std=0.2), 128),
+]
+
+
+@pytest.mark.parametrize("name,base,ov,dv", F32_128, ids=[c[0] for c in F32_128])
+def test_forward_f32_d128(name, base, ov, dv):
+    """The fp32 chunked forward at Dk = 128 (chunk 64) and at Dv = 128 (Dk = 64,
+    any chunk) against the oracle at the fp32 tolerance."""
+    w = workloads.workload(base, **ov)
+    say(f"[forward fp32 128] {name}: {w} Dv={dv or w.D}")
+    inp = workloads.make_prefill(w, device="cpu")
+    if dv is not None:
+        g = torch.Generator().manual_seed(77)
+        inp["v"] = torch.randn((w.B, w.T, w.H, dv), generator=g).contiguous()
+        if inp.get("S0") is not None:
+            inp["S0"] = (0.2 * torch.randn((w.B, w.H, w.D, dv), generator=g)).contiguous()
+    if base == 1:
+        a = inp["alpha"]
+        assert bool((a == -1.0).any()) and bool((a == 0.0).any())
+        assert bool((inp["beta"] == 2.0).any())
+    o_ref, s_ref = run_oracle(inp)
+    out, st = run_gpu(to_dev(inp), w.chunk, w.mode)
+    eo, es = slice_err_out(np32(out), o_ref), slice_err_state(np32(st), s_ref)
+    say(f"  err out {eo:.3e} state {es:.3e}{elem_note()}")
+    assert eo <= 1e-4 and es <= 1e-4
+
+
+def test_forward_f32_d128_exact_fallback_and_states():
+    """fp32 Dk = 128: chunks flagged for the exact kernel (a KDA-mode zero gate;
+    a span beyond the fast factorisation) through the half-channel factor
+    passes, the chunk-start states, and a packed batch."""
+    w = workloads.workload(1, B=1, H=3, T=200, D=128, chunk=64, dtype=torch.float32)
+    say(f"[fp32 d128 fallback] {w}")
+    inp = workloads.make_prefill(w)
+    a = inp["alpha"]
+    a.abs_()                                  # KDA-range gates ...
+    a[0, 70, 1, 5] = 0.0                      # ... with one exact zero (KDA mode: exact kernel)
+    a[0, 150:190, 2, 3] = 2.0 ** -30          # a span far beyond the midpoint factorisation
+    inp["beta"].clamp_(max=1.0)
+    q, k, v = (np32(inp[x]) for x in ("q", "k", "v"))
+    o_ref, s_ref, cs_ref = oracle.forward(q, k, v, np32(a), np32(inp["beta"]), None,
+                                          nthreads=oracle_threads(), chunk=64)
+    d = to_dev(inp)
+    nc = (w.T + 63) // 64
+    cs = torch.full((w.B, w.H, nc, w.D, w.D), float("nan"), dtype=torch.float32, device=DEV)
+    for mode in (workloads.KDA, workloads.CKDA):
+        out, st = run_gpu(d, 64, mode, chunk_states=cs)
+        eo, es = slice_err_out(np32(out), o_ref), slice_err_state(np32(st), s_ref)
+        ec = slice_err_state(np32(cs).reshape(w.B, w.H * nc, w.D, w.D),
+                             cs_ref.reshape(w.B, w.H * nc, w.D, w.D))
+        say(f"  mode {mode}: err out {eo:.3e} state {es:.3e} chunk states {ec:.3e}")
+        assert eo <= 1e-4 and es <= 1e-4 and ec <= 1e-4
+    # packed batch of the same tokens as sequences of 70 and 130
+    cu = torch.tensor([0, 70, 200], dtype=torch.int32, device=DEV)
+    outv, stv = kda.chunk_forward_varlen(d["q"][0], d["k"][0], d["v"][0], d["alpha"][0],
+                                         d["beta"][0], cu, None, chunk=64, mode=workloads.CKDA)
+    torch.cuda.synchronize()
+    for i, (lo, hi) in enumerate(((0, 70), (70, 200))):
+        sub = {x: inp[x][:, lo:hi] for x in ("q", "k", "v", "alpha", "beta")}
+        sub["S0"] = None
+        o_r, s_r = run_oracle(sub)
+        assert slice_err_out(np32(outv[lo:hi])[None], o_r) <= 1e-4
+        assert slice_err_state(np32(stv[i:i + 1]), s_r) <= 1e-4
