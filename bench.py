@@ -3,7 +3,8 @@
 Headline workload: KDA bf16 prefill, B=1 H=32 T=8192 d_k=d_v=128, chunk 64
 (seeded synthetic inputs resident in HBM before timing).  One step = one
 kda_chunk_forward call over the whole batch (gate summary, intra-chunk WY,
-state propagation and outputs).  Prints ONE JSON line.
+state propagation and outputs).  Every call is launched on a non-default
+stream of ours.  Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-others] [--no-cpu]
                   [--backward] [--decode] [--gate-prep] [--copy-probe] [--mfma-probe]
@@ -43,9 +44,12 @@ def algorithmic_bytes(w, io_bytes, with_s0: bool, with_st: bool):
     s0 = 4 * w.B * w.H * w.Dk * w.Dv if with_s0 else 0
     out = BTH * w.Dv * io_bytes
     st = 4 * w.B * w.H * w.Dk * w.Dv if with_st else 0
-    # prep_fast reads the inputs, chain writes the outputs and reads/writes the
-    # carried state; prep_exact only re-does chunks that prep_fast flagged
-    return {"prep_fast": read_in, "prep_exact": 0, "chain": s0 + out + st,
+    # prep_fast (prep_stream in the streamed call) reads the inputs, chain
+    # (chain_stream) writes the outputs and reads/writes the carried state;
+    # prep_exact only re-does chunks the fast prep flagged, and the streamed
+    # call's fallback chain only runs when the streamed chain gave up
+    return {"prep_fast": read_in, "prep_stream": read_in, "prep_exact": 0,
+            "chain": s0 + out + st, "chain_stream": s0 + out + st,
             "path": read_in + s0 + out + st}
 
 
@@ -54,6 +58,8 @@ KERNEL_SOURCES = {
     "prep_fast": ["prep_fast.hip", "kda_chunk.hpp", "kda_device.hpp", "kda_launch.hpp"],
     "chain": ["chain.hip", "kda_chunk.hpp", "kda_device.hpp", "kda_launch.hpp"],
     "prep_exact": ["prep_exact.hip", "kda_chunk.hpp", "kda_device.hpp", "kda_launch.hpp"],
+    "prep_stream": ["prep_fast.hip", "kda_chunk.hpp", "kda_device.hpp", "kda_launch.hpp"],
+    "chain_stream": ["chain_wide.hip", "kda_chunk.hpp", "kda_device.hpp", "kda_launch.hpp"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_kda_bf16_prefill.md")
 
@@ -91,6 +97,7 @@ def chunk_flops(w):
 
 
 def time_forward(kda, torch, w, inp, steps, warmup, extra_flags=0, side=None):
+    # (on the current stream: main() makes it a non-default one)
     """Median and mean ms per kda_chunk_forward call (each call bracketed by
     events on the launch stream) and the mean duration of every kernel (a
     separate pass with the library's per-launch events)."""
@@ -306,6 +313,10 @@ def main():
     w = workloads.workload(2)
     inp = workloads.make_prefill(w, device="cuda")
     torch.cuda.synchronize()
+    # every call on a stream of ours (the null stream would wait for the side
+    # stream's work: the overlapped forms need a non-default launch stream)
+    torch.cuda.set_stream(torch.cuda.Stream())
+    side = kda.SideStream()
     ms, mean_ms, per, out, st = time_forward(kda, torch, w, inp, args.steps, args.warmup)
     tokens = w.B * w.T
     io_bytes = 2
@@ -349,13 +360,19 @@ def main():
     }
     if not args.no_others:
         others = {}
+        # the same workload in the streamed form (KDA_FLAG_STREAMED: prep grid
+        # and chain at once on two streams; slower, kept for the record)
+        ms1, _, per1, _, _ = time_forward(kda, torch, w, inp, max(20, args.steps // 4), 3,
+                                          extra_flags=kda.STREAMED, side=side)
+        others["kda_bf16_prefill_streamed"] = {"ms": ms1, "tokens_per_s": tokens / (ms1 / 1e3),
+                                               "path_hbm_frac": ab["path"] / (ms1 / 1e3) / 1e9 / HBM_PEAK_GBS,
+                                               "kernels_ms": per1}
         for wid in (3, 1, 0):
             wo = workloads.workload(wid)
             io = workloads.make_prefill(wo, device="cuda")
             # the long-context workload runs in parts on a second stream of ours
-            side = kda.SideStream() if wid == 3 else None
             mso, _, pero, _, _ = time_forward(kda, torch, wo, io, max(20, args.steps // 4), 3,
-                                              side=side)
+                                              side=side if wid == 3 else None)
             abo = algorithmic_bytes(wo, 2 if wo.dtype == torch.bfloat16 else 4,
                                     io["S0"] is not None, True)
             others[wo.name] = {"ms": mso, "tokens_per_s": wo.B * wo.T / (mso / 1e3),

@@ -32,6 +32,7 @@ STAGE_EVENTS = 2
 VALIDATE_RANGES = 1    # KDA_FLAG_VALIDATE_RANGES
 NO_SEGMENTS = 4        # KDA_FLAG_NO_SEGMENTS
 SINGLE_STREAM = 8      # KDA_FLAG_SINGLE_STREAM
+STREAMED = 16          # KDA_FLAG_STREAMED
 _DT = {torch.float32: 0, torch.bfloat16: 1}
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libkda.so")
@@ -58,20 +59,29 @@ class _Side(ctypes.Structure):
 
 
 class SideStream:
-    """A second stream and its events, owned here and lent to
-    kda_chunk_forward_side (chunk_forward(..., side=...)): the chunk factors of
-    later parts are formed on it while the chain runs earlier parts."""
+    """A second stream and its events (kda_side_stream_create: a stream with a
+    hardware queue of its own), owned here and lent to kda_chunk_forward_side
+    (chunk_forward(..., side=...)).  `stream` wraps it for torch
+    (torch.cuda.ExternalStream).  The streamed form is not taken for calls
+    on the null stream (torch's default current stream): launch those calls
+    on a torch.cuda.Stream()."""
 
     def __init__(self, device=None):
-        self.stream = torch.cuda.Stream(device=device)
-        self.events = [torch.cuda.Event(enable_timing=False) for _ in range(SIDE_EVENTS)]
-        for e in self.events:              # torch creates the event at its first record
-            e.record(self.stream)
-        self._c = _Side(self.stream.cuda_stream,
-                        (ctypes.c_void_p * SIDE_EVENTS)(*[e.cuda_event for e in self.events]))
+        lib = load()
+        self._c = _Side()
+        with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
+            _check("kda_side_stream_create", lib.kda_side_stream_create(ctypes.byref(self._c)))
+        # (kept for __del__, which may run while the interpreter shuts down)
+        self._destroy, self._byref = lib.kda_side_stream_destroy, ctypes.byref
+        self.stream = torch.cuda.ExternalStream(self._c.stream, device=device)
 
     def _as_arg(self):
         return ctypes.byref(self._c)
+
+    def __del__(self):
+        c = getattr(self, "_c", None)
+        if c is not None and c.stream and getattr(self, "_destroy", None) is not None:
+            self._destroy(self._byref(c))
 
 
 class Prologue(ctypes.Structure):
@@ -104,6 +114,10 @@ def load():
     lib.kda_chunk_forward.restype = i
     lib.kda_chunk_forward_side.argtypes = [vp] * 8 + [i] * 8 + [u, vp, sz, vp, ctypes.POINTER(_Side)]
     lib.kda_chunk_forward_side.restype = i
+    lib.kda_side_stream_create.argtypes = [ctypes.POINTER(_Side)]
+    lib.kda_side_stream_create.restype = i
+    lib.kda_side_stream_destroy.argtypes = [ctypes.POINTER(_Side)]
+    lib.kda_side_stream_destroy.restype = i
     lib.kda_chunk_forward_noalloc.argtypes = [vp] * 8 + [i] * 8 + [u, vp]
     lib.kda_chunk_forward_noalloc.restype = i
     lib.kda_chunk_forward_states.argtypes = [vp] * 9 + [i] * 8 + [u, vp, sz, vp]

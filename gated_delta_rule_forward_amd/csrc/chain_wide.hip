@@ -125,10 +125,15 @@ struct WideCtx {
 // last one; only the last chunk's output store is masked), so the compiler's
 // wait counts are exact and chunk n + NSETS - 1 stays in flight during chunk n.
 // CS: also write the state entering every chunk.
-template <typename T, int C, int DK, int CT, int NSETS, bool ROLE_D, bool CS>
-__device__ __forceinline__ void wide_role(const ChainArgs& a, const WideCtx& x, f32x4 (&S)[CT],
+// STREAM: the operands are written by the prep kernel running at the same
+// time; before the loads of a chunk, wave NM (the first O wave) has seen its
+// ready word (polled during the previous step, answered through barrier B2 in
+// *status).  Returns false when the workgroup gave up (nothing more is
+// written; the call's fallback chain redoes the work).
+template <typename T, int C, int DK, int CT, int NSETS, bool ROLE_D, bool CS, bool STREAM>
+__device__ __forceinline__ bool wide_role(const ChainArgs& a, const WideCtx& x, f32x4 (&S)[CT],
                                           typename WideGeom<T, C, DK, CT>::F* Sf,
-                                          typename WideGeom<T, C, DK, CT>::F* Df)
+                                          typename WideGeom<T, C, DK, CT>::F* Df, int* status)
 {
     using G = WideGeom<T, C, DK, CT>;
     using F = typename G::F;
@@ -137,6 +142,21 @@ __device__ __forceinline__ void wide_role(const ChainArgs& a, const WideCtx& x, 
     const int NC = x.NC, lane = x.lane, lg = x.lg, mt = x.mt, t = x.t;
     const int Dv = a.Dv;
 
+    const bool poller = STREAM && !ROLE_D && mt == 0;     // wave NM
+    if constexpr (STREAM) {
+        if (poller) {
+            // the units of the first NSETS steps' loads: NSETS - 1 here, one
+            // more in step 0 (step n waits for the unit step n + 1 loads)
+            bool ok = true;
+            for (int j = 0; j < NSETS && ok; ++j) {
+                const size_t u = x.u0 + min(j, NC - 1);
+                ok = stream_wait_ready(a.ready, a.sctl, u, __hip_atomic_load(&a.ready[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+            }
+            *status = ok ? 0 : 1;                     // (every lane, the same word)
+        }
+        lds_barrier();
+        if (__builtin_amdgcn_readfirstlane(*status)) return false;
+    }
     Ops ops[NSETS];
 #pragma unroll
     for (int j = 0; j + 1 < NSETS; ++j)
@@ -170,7 +190,13 @@ __device__ __forceinline__ void wide_role(const ChainArgs& a, const WideCtx& x, 
         }
     };
 
-    auto step = [&](Ops& cur, Ops& prv, int n) {
+    auto step = [&](Ops& cur, Ops& prv, int n) -> bool {
+        // (streamed) the ready word of the unit the next step loads
+        const size_t unext = x.u0 + min(n + NSETS, NC - 1);
+        unsigned rnext = 1u;
+        if constexpr (STREAM) {
+            if (poller) rnext = __hip_atomic_load(&a.ready[unext], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         if constexpr (CS && has_t) {
             // the state entering chunk n (this wave's tiles, rounded to T)
             T* cs = static_cast<T*>(a.CS) + ((size_t)x.bh * x.nc_seq + x.c0 + n) * DK * Dv + x.col;
@@ -248,7 +274,20 @@ __device__ __forceinline__ void wide_role(const ChainArgs& a, const WideCtx& x, 
 #pragma unroll
                 for (int s = 0; s < G::NKC; ++s) pdf[c][s] = df[c][s];
         }
+        if constexpr (STREAM) {
+            if (poller) {
+                const bool ok = stream_wait_ready(a.ready, a.sctl, unext, rnext);
+                *status = ok ? 0 : 1;
+            }
+        }
         lds_barrier();                                // B2: S(n+1) visible
+        if constexpr (STREAM) {
+            if (__builtin_amdgcn_readfirstlane(*status)) {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                return false;
+            }
+        }
+        return true;
     };
 
     // the loop unrolled by NSETS (every register set keeps fixed registers);
@@ -256,18 +295,19 @@ __device__ __forceinline__ void wide_role(const ChainArgs& a, const WideCtx& x, 
     // step has issued the same memory operations
     int n = 0;
     for (;;) {
-        step(ops[0], ops[NSETS - 1], n);
+        if (!step(ops[0], ops[NSETS - 1], n)) return false;
         if (++n >= NC) { finish_o(ops[0], n - 1, std::false_type{}); break; }
-        step(ops[1], ops[0], n);
+        if (!step(ops[1], ops[0], n)) return false;
         if (++n >= NC) { finish_o(ops[1], n - 1, std::false_type{}); break; }
         if constexpr (NSETS == 3) {
-            step(ops[2], ops[1], n);
+            if (!step(ops[2], ops[1], n)) return false;
             if (++n >= NC) { finish_o(ops[2], n - 1, std::false_type{}); break; }
         }
     }
+    return true;
 }
 
-template <typename T, int C, int DK, int CT, int NSETS>
+template <typename T, int C, int DK, int CT, int NSETS, bool STREAM>
 __global__ __launch_bounds__(kWideThreads) void chain_wide_kernel(ChainArgs a)
 {
     using G = WideGeom<T, C, DK, CT>;
@@ -275,12 +315,35 @@ __global__ __launch_bounds__(kWideThreads) void chain_wide_kernel(ChainArgs a)
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     F* Sf = reinterpret_cast<F*>(lds + G::SF);     // [CT][NKD][64]
     F* Df = reinterpret_cast<F*>(lds + G::DF);     // [CT][NKC][64]
+    __shared__ int sStatus;
 
+    // the fallback launch of a streamed call runs only when the streamed chain
+    // gave up or left a (b, h) out
+    if (a.gate && !(a.gate->abort || a.gate->chains_done < a.gate->expect)) return;
     const int Dv = a.Dv, H = a.H;
     const int NSL = Dv / (16 * CT);                 // column slices per (b, h)
-    const int g = blockIdx.x, xcd = g % kXcds, jx = g / kXcds;
-    const int bh = (jx / NSL) * kXcds + xcd, slice = jx % NSL;
-    if (bh >= a.B * H) return;
+    int bh, slice;
+    if constexpr (STREAM) {
+        // a (b, h, column slice) of the heads on this workgroup's own XCD
+        // (b H + h = xcd + 8 j), so the units it reads were written there
+        if (threadIdx.x == 0) {
+            const int xcd = (int)xcc_id();
+            const int k = (int)atomicAdd(&a.sctl->chain_next[xcd], 1u);
+            const int bhx = xcd + kXcds * (k / NSL);
+            sStatus = bhx < a.B * H ? bhx * NSL + k % NSL : -1;
+        }
+        __syncthreads();
+        const int role = __builtin_amdgcn_readfirstlane(sStatus);
+        __syncthreads();
+        if (role < 0) return;
+        bh = role / NSL;
+        slice = role % NSL;
+    } else {
+        const int g = blockIdx.x, xcd = g % kXcds, jx = g / kXcds;
+        bh = (jx / NSL) * kXcds + xcd;
+        slice = jx % NSL;
+        if (bh >= a.B * H) return;
+    }
     const SeqPos sp = locate_seq(bh, H, a.T, a.NC, a.cu, a.cs);
     WideCtx x;
     x.bh = bh;
@@ -317,13 +380,18 @@ __global__ __launch_bounds__(kWideThreads) void chain_wide_kernel(ChainArgs a)
 #pragma unroll
             for (int c = 0; c < CT; ++c) put_tile<T, G::KB>(Sf + c * G::NKD * 64, t, x.lane, S[c]);
         }
-        if (a.CS) {
-            if (dwave) wide_role<T, C, DK, CT, NSETS, true, true>(a, x, S, Sf, Df);
-            else wide_role<T, C, DK, CT, NSETS, false, true>(a, x, S, Sf, Df);
+        bool done;
+        if constexpr (STREAM) {
+            done = dwave ? wide_role<T, C, DK, CT, NSETS, true, false, true>(a, x, S, Sf, Df, &sStatus)
+                         : wide_role<T, C, DK, CT, NSETS, false, false, true>(a, x, S, Sf, Df, &sStatus);
+        } else if (a.CS) {
+            done = dwave ? wide_role<T, C, DK, CT, NSETS, true, true, false>(a, x, S, Sf, Df, &sStatus)
+                         : wide_role<T, C, DK, CT, NSETS, false, true, false>(a, x, S, Sf, Df, &sStatus);
         } else {
-            if (dwave) wide_role<T, C, DK, CT, NSETS, true, false>(a, x, S, Sf, Df);
-            else wide_role<T, C, DK, CT, NSETS, false, false>(a, x, S, Sf, Df);
+            done = dwave ? wide_role<T, C, DK, CT, NSETS, true, false, false>(a, x, S, Sf, Df, &sStatus)
+                         : wide_role<T, C, DK, CT, NSETS, false, false, false>(a, x, S, Sf, Df, &sStatus);
         }
+        if (!done) return;                          // (streamed: gave up)
     }
     // (an empty sequence of a packed batch passes its state through)
     if (a.ST && has_t) {
@@ -333,13 +401,16 @@ __global__ __launch_bounds__(kWideThreads) void chain_wide_kernel(ChainArgs a)
             for (int i = 0; i < 4; ++i)
                 a.ST[((size_t)bh * DK + 16 * t + 4 * lg + i) * Dv + col + 16 * c] = S[c][i];
     }
+    if constexpr (STREAM) {
+        if (threadIdx.x == 0) atomicAdd(&a.sctl->chains_done, 1u);
+    }
 }
 
-template <typename T, int C, int DK, int CT, int NSETS>
+template <typename T, int C, int DK, int CT, int NSETS, bool STREAM = false>
 hipError_t launch_wide_t(const ChunkShape& s, const ChainArgs& a, hipStream_t stream)
 {
     using G = WideGeom<T, C, DK, CT>;
-    auto kern = chain_wide_kernel<T, C, DK, CT, NSETS>;
+    auto kern = chain_wide_kernel<T, C, DK, CT, NSETS, STREAM>;
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)G::LDS);
     if (e != hipSuccess) return e;
@@ -382,6 +453,24 @@ hipError_t launch_chain_wide(IoType io, const ChunkShape& s, const ChainArgs& a,
     }
     if (s.Dk == 128) return launch_wide_t<float, 64, 128, 1, 2>(s, a, stream);
     return launch_wide_t<float, 64, 64, 1, 3>(s, a, stream);
+}
+
+// The chain of the streamed forward: ct column tiles per workgroup, waiting on
+// the ready words of the prep kernel that runs beside it.
+hipError_t launch_chain_stream(IoType io, const ChunkShape& s, const ChainArgs& a, int ct,
+                               hipStream_t stream)
+{
+    if (io != IoType::BF16 || s.C != 64) return hipErrorInvalidValue;
+    if (s.Dk == 128) {
+        if (ct == 4) return launch_wide_t<bf16_t, 64, 128, 4, 2, true>(s, a, stream);
+        if (ct == 2) return launch_wide_t<bf16_t, 64, 128, 2, 2, true>(s, a, stream);
+        return launch_wide_t<bf16_t, 64, 128, 1, 3, true>(s, a, stream);
+    }
+    if (s.Dk == 64) {
+        if (ct == 2) return launch_wide_t<bf16_t, 64, 64, 2, 3, true>(s, a, stream);
+        return launch_wide_t<bf16_t, 64, 64, 1, 3, true>(s, a, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace kda

@@ -5,11 +5,13 @@
 // synchronisation).  Per-kernel HIP events are recorded only when the caller
 // passes KDA_FLAG_STAGE_EVENTS.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <stdint.h>
 #include <string.h>
 
 #include <map>
+#include <vector>
 #include <algorithm>
 #include <mutex>
 
@@ -25,7 +27,7 @@ using kda::ChunkWorkspace;
 using kda::IoType;
 
 constexpr unsigned kKnownFlags = KDA_FLAG_VALIDATE_RANGES | KDA_FLAG_STAGE_EVENTS |
-                                  KDA_FLAG_NO_SEGMENTS | KDA_FLAG_SINGLE_STREAM;
+                                  KDA_FLAG_NO_SEGMENTS | KDA_FLAG_SINGLE_STREAM | KDA_FLAG_STREAMED;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 bool aligned16(const void* p) { return aligned(p, 16); }
@@ -181,12 +183,35 @@ Parts parts_for(int B, int H, int Dk, int Dv, int NC)
     return {(NC + len - 1) / len, len};
 }
 
+// Streamed forward (kda_chunk_forward_side): the chunk factors are formed by a
+// persistent prep grid on the side stream while the chain consumes them on the
+// caller's stream, unit by unit, through the L2 of the XCD both run on.
+// Covered: bf16, chunk 64, Dk 128 or 64, at least 8 (b, h) (every XCD holds
+// heads, so every XCD's prep workgroups have units to form).
+bool stream_shape(int B, int H, int Dk, int chunk, kda_dtype_t dtype)
+{
+    return dtype == KDA_DTYPE_BF16 && chunk == 64 && (Dk == 128 || Dk == 64) &&
+           (long long)B * H >= 8;
+}
+// the streamed chain: the 16-column LDS-staged kernel while its workgroups
+// (one per (b, h, 16 columns), each the whole of a compute unit) leave half
+// the compute units to the prep grid, else the wide kernel
+bool stream_lds_chain(long long chains) { return chains <= 128; }
+// column tiles per workgroup of the streamed chain when it is the wide kernel
+int stream_tiles(int Dk, int Dv)
+{
+    if (Dk == 128 && Dv % 64 == 0) return 4;
+    if (Dv % 32 == 0) return 2;
+    return 1;
+}
+
 // workspace of a dense forward: the per-unit regions, then (with segments)
 // the segment maps [B H][nseg][Dk][Dk + Dv] and start states [B H][nseg][Dk][Dv],
 // then (with parts) the state between parts [B H][Dk][Dv] fp32
 size_t dense_layout(int B, int T, int H, int Dk, int Dv, int chunk, IoType io,
                     size_t off[kda::kWorkspaceRegions], size_t* summ_off, size_t* sseg_off,
-                    size_t* spart_off = nullptr)
+                    size_t* spart_off = nullptr, size_t* ready_off = nullptr,
+                    size_t* sctl_off = nullptr)
 {
     const ChunkShape sh = make_shape(B, T, H, Dk, Dv, chunk);
     size_t n = kda::chunk_workspace_layout(sh, io, off);
@@ -203,6 +228,15 @@ size_t dense_layout(int B, int T, int H, int Dk, int Dv, int chunk, IoType io,
     if (parts_for(B, H, Dk, Dv, sh.NC).parts > 1) {
         if (spart_off) *spart_off = n;
         n += ((size_t)B * H * Dk * Dv * 4 + 255) & ~size_t(255);
+    }
+    // (streamed forward) a ready word per unit, then the control words
+    if (ready_off) *ready_off = 0;
+    if (sctl_off) *sctl_off = 0;
+    if (stream_shape(B, H, Dk, chunk, io == IoType::F32 ? KDA_DTYPE_F32 : KDA_DTYPE_BF16)) {
+        if (ready_off) *ready_off = n;
+        n += ((size_t)B * H * sh.NC * 4 + 255) & ~size_t(255);
+        if (sctl_off) *sctl_off = n;
+        n += sizeof(kda::StreamCtl);
     }
     return n;
 }
@@ -357,9 +391,16 @@ kda_status_t chunk_forward(const void* q, const void* k, const void* v, const fl
 
     // the caller's second stream takes part in the call only when it belongs to
     // the same device as `stream` (else the call keeps to `stream`)
-    bool use_side = prt.parts > 1;
+    // (streamed: not from the null stream, which waits for the work of every
+    // blocking stream, a side stream made by kda_side_stream_create included)
+    const bool streamed = side && s && (flags & KDA_FLAG_STREAMED) &&
+                          !(flags & KDA_FLAG_SINGLE_STREAM) && !pro && !theta &&
+                          !chunk_states && !(final_state && final_state == initial_state) &&
+                          sgm.nseg == 1 && stream_shape(B, H, Dk, chunk, dtype);
+    bool use_side = prt.parts > 1 || streamed;
+    hipDevice_t d0 = 0;
     if (use_side) {
-        hipDevice_t d0 = 0, d1 = 0;
+        hipDevice_t d1 = 0;
         if (s) {
             if (hipStreamGetDevice(s, &d0) != hipSuccess) return KDA_ERR_HIP;
         } else {
@@ -370,6 +411,57 @@ kda_status_t chunk_forward(const void* q, const void* k, const void* v, const fl
         if (hipStreamGetDevice(static_cast<hipStream_t>(side->stream), &d1) != hipSuccess)
             return KDA_ERR_HIP;
         use_side = d0 == d1;
+    }
+    if (use_side && streamed) {
+        // prep grid on the side stream and the chain on `stream` at the same
+        // time; then, on `stream`, the exact kernel for flagged units and a
+        // fallback chain that runs only if the streamed one gave up
+        hipStream_t ss = static_cast<hipStream_t>(side->stream);
+        hipEvent_t ev0 = static_cast<hipEvent_t>(side->events[0]);
+        hipEvent_t ev1 = static_cast<hipEvent_t>(side->events[1]);
+        size_t offs[kda::kWorkspaceRegions], a0, a1, a2, roff = 0, coff = 0;
+        dense_layout(B, T, H, Dk, Dv, chunk, io, offs, &a0, &a1, &a2, &roff, &coff);
+        unsigned* ready = reinterpret_cast<unsigned*>(w + roff);
+        kda::StreamCtl* ctl = reinterpret_cast<kda::StreamCtl*>(w + coff);
+        // the chain: the 16-column LDS-staged kernel (ct = 0), or the wide one
+        // with ct column tiles per workgroup
+        const int ct = stream_lds_chain((long long)B * H * (Dv / 16)) ? 0 : stream_tiles(Dk, Dv);
+        const long long bhn = (long long)B * H;
+        const int nsl = Dv / (16 * (ct > 0 ? ct : 1));
+        kda::PrepArgs ps = pa;
+        ps.ntst = 0;
+        ps.nbh = (int)bhn;
+        ps.ready = ready;
+        ps.sctl = ctl;
+        kda::ChainArgs cst = ca;
+        cst.ready = ready;
+        cst.sctl = ctl;
+        if (rec.mark("stream_clear") != hipSuccess) return KDA_ERR_HIP;
+        if (kda::launch_stream_clear(ready, (size_t)bhn * sh.NC, ctl, (unsigned)(bhn * nsl), s) !=
+            hipSuccess)
+            return KDA_ERR_HIP;
+        if (rec.done() != hipSuccess) return KDA_ERR_HIP;
+        if (hipEventRecord(ev0, s) != hipSuccess) return KDA_ERR_HIP;
+        if (rec.mark("chain_stream") != hipSuccess) return KDA_ERR_HIP;
+        if ((ct > 0 ? kda::launch_chain_stream(io, sh, cst, ct, s)
+                    : kda::launch_chain_lds_stream(io, sh, cst, s)) != hipSuccess)
+            return KDA_ERR_HIP;
+        if (rec.done() != hipSuccess) return KDA_ERR_HIP;
+        if (hipStreamWaitEvent(ss, ev0, 0) != hipSuccess) return KDA_ERR_HIP;
+        if (rec.mark("prep_stream") != hipSuccess) return KDA_ERR_HIP;
+        if (kda::launch_prep_stream(io, sh, ps, ss) != hipSuccess) return KDA_ERR_HIP;
+        if (rec.done() != hipSuccess) return KDA_ERR_HIP;
+        if (hipEventRecord(ev1, ss) != hipSuccess) return KDA_ERR_HIP;
+        if (hipStreamWaitEvent(s, ev1, 0) != hipSuccess) return KDA_ERR_HIP;
+        if (rec.mark("prep_exact") != hipSuccess) return KDA_ERR_HIP;
+        if (kda::launch_prep_exact(io, sh, pa, s) != hipSuccess) return KDA_ERR_HIP;
+        if (rec.done() != hipSuccess) return KDA_ERR_HIP;
+        kda::ChainArgs cf = ca;
+        cf.gate = ctl;
+        if (rec.mark("chain") != hipSuccess) return KDA_ERR_HIP;
+        if (launch_forward_chain(io, sh, cf, s) != hipSuccess) return KDA_ERR_HIP;
+        if (rec.done() != hipSuccess) return KDA_ERR_HIP;
+        return KDA_OK;
     }
     if (use_side) {
         // prep of every part on the side stream, chain of part p on the
@@ -1025,6 +1117,45 @@ kda_status_t kda_chunk_forward_side(const void* q, const void* k, const void* v,
     return chunk_forward(q, k, v, alpha, beta, initial_state, out, final_state, nullptr, nullptr,
                          B, T, H, Dk, Dv, chunk, dtype, mode, flags, workspace, workspace_bytes,
                          stream, nullptr, side);
+}
+
+kda_status_t kda_side_stream_create(kda_side_t* side)
+{
+    if (!side) return KDA_ERR_NULL_POINTER;
+    memset(side, 0, sizeof(*side));
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        return KDA_ERR_HIP;
+    // every compute unit in the mask: the mask only buys the queue of its own
+    std::vector<uint32_t> mask((size_t)(cus + 31) / 32, 0u);
+    for (int i = 0; i < cus; ++i) mask[(size_t)i / 32] |= 1u << (i % 32);
+    hipStream_t st = nullptr;
+    if (hipExtStreamCreateWithCUMask(&st, (uint32_t)mask.size(), mask.data()) != hipSuccess)
+        return KDA_ERR_HIP;
+    side->stream = st;
+    for (int i = 0; i < KDA_SIDE_EVENTS; ++i) {
+        hipEvent_t e = nullptr;
+        if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
+            kda_side_stream_destroy(side);
+            return KDA_ERR_HIP;
+        }
+        side->events[i] = e;
+    }
+    return KDA_OK;
+}
+
+kda_status_t kda_side_stream_destroy(kda_side_t* side)
+{
+    if (!side) return KDA_ERR_NULL_POINTER;
+    bool ok = true;
+    if (side->stream) ok = hipStreamSynchronize(static_cast<hipStream_t>(side->stream)) == hipSuccess && ok;
+    for (int i = 0; i < KDA_SIDE_EVENTS; ++i)
+        if (side->events[i]) ok = hipEventDestroy(static_cast<hipEvent_t>(side->events[i])) == hipSuccess && ok;
+    if (side->stream) ok = hipStreamDestroy(static_cast<hipStream_t>(side->stream)) == hipSuccess && ok;
+    memset(side, 0, sizeof(*side));
+    return ok ? KDA_OK : KDA_ERR_HIP;
 }
 
 kda_status_t kda_chunk_forward_noalloc(const void* q, const void* k, const void* v,

@@ -164,6 +164,23 @@ __device__ __forceinline__ f32x4 tile_tn_nat(const T* A, int lda, const T* Bt, i
     return acc;
 }
 
+// Streamed forward: the prep and chain kernels run at the same time and hand
+// each unit over through the L2 of the XCD both run on; these control words
+// and a ready word per unit live in the workspace (cleared by the call).
+// (each group of words that workgroups poll or update often sits on a
+// 128-byte cache line of its own)
+struct StreamCtl {
+    unsigned prep_next[8];     // next unit index per XCD (prep workgroups)
+    unsigned pad0[24];
+    unsigned chain_next[8];    // next (head, column slice) index per XCD (chain workgroups)
+    unsigned chains_done;      // chain workgroups that ran their sequence to the end
+    unsigned expect;           // chain workgroups the call needs
+    unsigned pad1[22];
+    unsigned abort;            // a chain workgroup met a unit of the exact kernel or gave up waiting
+    unsigned pad2[31];
+};
+static_assert(sizeof(StreamCtl) == 384, "three 128-byte lines");
+
 struct PrepArgs {
     const void* q;
     const void* k;
@@ -205,6 +222,10 @@ struct PrepArgs {
     // (P, W, U) with non-temporal stores (worth it when many chains stream the
     // workspace; plain inputs only, not the prologue or phase variants)
     int ntst;
+    // streamed forward: B H, the ready word of every unit and the control words
+    int nbh;
+    unsigned* ready;
+    StreamCtl* sctl;
 };
 
 // unit of launch index v when a launch covers chunks [pc0, pc0 + pcn) of every
@@ -279,7 +300,48 @@ struct ChainArgs {
     // state leaving the range; may be S0: each workgroup reads its slice of S0
     // before it writes that slice of ST)
     int pc0, pcn;
+    // streamed forward: the ready words and control words the chain waits on
+    // (streamed kernel), or (gate) the control words that decide whether this
+    // launch runs at all: only when the streamed chain gave up or did not
+    // cover every (b, h)
+    const unsigned* ready;
+    StreamCtl* sctl;
+    const StreamCtl* gate;
 };
+
+// Streamed forward: how long a chain wavefront waits for one unit before it
+// gives up (s_memrealtime ticks, 100 MHz: 10 ms, far beyond the time the prep
+// grid takes per chunk index), and a cap on the polls of one wait that ends it
+// whatever the clock reads (about 0.2 us per poll); the call then recomputes
+// the chain after the prep grid has finished, so giving up costs time, never
+// correctness.  (The usual cause: the two streams share a hardware queue, so
+// the prep grid cannot start before the chain ends.)
+constexpr unsigned long long kStreamWaitTicks = 1000000ull;
+constexpr unsigned kStreamWaitPolls = 1u << 18;
+
+// Wait until unit u's ready word reads 1 (its factors are in the workspace,
+// written from this XCD).  Gives up, raising the abort word, when the unit
+// needs the exact kernel (2), when another workgroup gave up, or when the
+// bound expires.  `first` is a value of the ready word read earlier.  Every
+// lane of the wavefront takes part and gets the same answer.
+__device__ inline bool stream_wait_ready(const unsigned* ready, StreamCtl* ctl, size_t u,
+                                         unsigned first)
+{
+    if (first == 1u) return true;
+    unsigned r = first;
+    const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+    for (unsigned n = 0;; ++n) {
+        if (r == 2u ||
+            ((n & 15) == 15 && __hip_atomic_load(&ctl->abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) ||
+            __builtin_amdgcn_s_memrealtime() - t0 > kStreamWaitTicks || n >= kStreamWaitPolls)
+            break;
+        __builtin_amdgcn_s_sleep(2);
+        r = __hip_atomic_load(&ready[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (r == 1u) return true;
+    }
+    __hip_atomic_store(&ctl->abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return false;
+}
 
 // Backward (dense batches).  The reverse chain reads the forward's operands
 // after relayout_kernel turned them into W^T, (Q * Gamma)^T, Ktil and P^T

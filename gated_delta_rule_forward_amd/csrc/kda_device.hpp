@@ -112,4 +112,11 @@ __device__ __forceinline__ float row16_sum(float x) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// the XCD (accelerator complex die) this wavefront runs on, from the hardware
+// register XCC_ID (bits 3:0; the MI355X has 8)
+__device__ __forceinline__ unsigned xcc_id()
+{
+    return __builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11)) & 7u;
+}
+
 }  // namespace kda

@@ -58,6 +58,19 @@ size_t chunk_workspace_layout(const ChunkShape& s, IoType io, size_t offsets[kWo
 size_t prep_fast_lds_bytes(IoType io, int C, int Dk);
 
 hipError_t launch_prep_fast(IoType io, const ChunkShape& s, const PrepArgs& a, hipStream_t stream);
+// streamed forward: the prep grid that claims units per XCD, the chain that
+// waits on its ready words (ct column tiles per workgroup), and the clear of
+// the ready and control words that precedes both
+struct StreamCtl;
+hipError_t launch_prep_stream(IoType io, const ChunkShape& s, const PrepArgs& a,
+                              hipStream_t stream);
+hipError_t launch_chain_stream(IoType io, const ChunkShape& s, const ChainArgs& a, int ct,
+                               hipStream_t stream);
+// the 16-column LDS-staged chain (chain.hip) in the streamed form
+hipError_t launch_chain_lds_stream(IoType io, const ChunkShape& s, const ChainArgs& a,
+                                   hipStream_t stream);
+hipError_t launch_stream_clear(unsigned* ready, size_t nu, StreamCtl* ctl, unsigned expect,
+                               hipStream_t stream);
 hipError_t launch_prep_exact(IoType io, const ChunkShape& s, const PrepArgs& a, hipStream_t stream);
 hipError_t launch_chain(IoType io, const ChunkShape& s, const ChainArgs& a, hipStream_t stream);
 // the wide-slice chain (16 ct columns per workgroup, operands in registers);

@@ -133,8 +133,10 @@ __device__ __forceinline__ float frcp(float x) { return __builtin_amdgcn_rcpf(x)
 // -phi_r turns every decay-weighted product into the real one of the plain
 // kernel on the rotated vectors; Ktil is rotated back by phi_{C-1} and
 // Gamma_{C-1} is stored as (|Gamma| cos phi_{C-1}, |Gamma| sin phi_{C-1}).
-template <typename T, int C, int DK, bool ZS, bool PRO, bool PH, bool NT = false>
-__global__ __launch_bounds__(kThreads, (sizeof(T) == 4 && DK == 128) ? 1 : 2) void prep_fast_kernel(PrepArgs args)
+// One unit (one chunk of one (b, h)) by the whole workgroup.  Every thread
+// returns from it at the same point.
+template <typename T, int C, int DK, bool ZS, bool PRO, bool PH, bool NT>
+__device__ __forceinline__ bool prep_fast_unit(const PrepArgs& args, const int unit)
 {
     using G = FastGeom<T, C, DK>;
     using F = Frag<T, G::KB>;
@@ -159,18 +161,22 @@ __global__ __launch_bounds__(kThreads, (sizeof(T) == 4 && DK == 128) ? 1 : 2) vo
     int* misc = sBase + DK;
     float* sBeta = reinterpret_cast<float*>(misc + 8);
 
-    const int tid = threadIdx.x;
+    int tid_ = threadIdx.x;
+    // (opaque per unit: in the persistent grid this keeps the compiler from
+    // hoisting every per-thread index out of the unit loop and holding it live
+    // across the whole body, which spills)
+    asm volatile("" : "+v"(tid_));
+    const int tid = tid_;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, ln = lane & 15, lg = lane >> 4;
     const bool own = tid < G::ACTIVE;
     const int q4 = tid % G::NQ, part = own ? tid / G::NQ : PARTS - 1;
     const int c0 = 4 * q4;                                    // my channels c0 .. c0+3
     const int T_ = args.T, H = args.H, NC = args.NC;
-    const int unit = part_unit(blockIdx.x, args.pc0, args.pcn, NC);
     const UnitPos up = locate_unit(unit, H, T_, NC, C, args.cu, args.cs, args.N);
     if (!up.valid) {                  // past the last sequence of a packed batch
         if (tid == 0) args.FL[unit] = 0;
-        return;
+        return false;
     }
     const int h = up.h, nvalid = up.nvalid;
 
@@ -338,7 +344,7 @@ __global__ __launch_bounds__(kThreads, (sizeof(T) == 4 && DK == 128) ? 1 : 2) vo
             if (lane == 0) misc[0] = carry;
         }
         __syncthreads();
-        Ztot = misc[0];
+        Ztot = __builtin_amdgcn_readfirstlane(misc[0]);
         bad = Ztot > args.zx;
     }
     // midpoint M = L_total / 2;  F_r = F0 pr_r and G_r = G0 / pr_r, where F0, G0
@@ -353,9 +359,11 @@ __global__ __launch_bounds__(kThreads, (sizeof(T) == 4 && DK == 128) ? 1 : 2) vo
         F0[x] = so * fexp2(offL[x] - M[x]);
         G0[x] = so * fexp2(M[x] - offL[x]);
     }
-    if (__syncthreads_or(bad && own)) {
+    // (the workgroup-wide answer, made provably uniform for the compiler, so
+    // that every branch around a barrier here is a uniform one)
+    if (__builtin_amdgcn_readfirstlane((int)__syncthreads_or(bad && own))) {
         if (tid == 0) args.FL[unit] = 1;
-        return;
+        return true;
     }
     if (tid == 0) args.FL[unit] = 0;
 
@@ -713,6 +721,46 @@ __global__ __launch_bounds__(kThreads, (sizeof(T) == 4 && DK == 128) ? 1 : 2) vo
             }
         }
     }
+    return false;
+}
+
+template <typename T, int C, int DK, bool ZS, bool PRO, bool PH, bool NT = false>
+__global__ __launch_bounds__(kThreads, (sizeof(T) == 4 && DK == 128) ? 1 : 2) void prep_fast_kernel(PrepArgs args)
+{
+    prep_fast_unit<T, C, DK, ZS, PRO, PH, NT>(args, part_unit(blockIdx.x, args.pc0, args.pcn, args.NC));
+}
+
+// Streamed forward (dense batches): one unit per workgroup, but not the unit
+// of its index: each workgroup claims the next unit of the heads on its own
+// XCD (b H + h = xcd + 8 j, read from the hardware) from that XCD's counter,
+// in chunk-major order, so the chain workgroups of the same XCD read the unit
+// from the L2 they share, and chunk n of every head comes before chunk n + 1
+// of any.  After the unit, every wave waits for its stores, then the unit's
+// ready word is set (1: the factors are in the
+// workspace; 2: the unit needs the exact kernel, which runs after this grid).
+// The grid holds 8 x (the most units any XCD has) workgroups; those that find
+// no unit left exit.
+template <typename T, int C, int DK, bool ZS, bool NT>
+__global__ __launch_bounds__(kThreads, (sizeof(T) == 4 && DK == 128) ? 1 : 2) void prep_stream_kernel(PrepArgs args)
+{
+    __shared__ int sUnit;
+    const int xcd = (int)xcc_id();
+    const int BH = args.nbh, NC = args.NC;
+    const int hx = (BH - xcd + 7) / 8;               // heads of this XCD
+    const int total = hx > 0 ? hx * NC : 0;
+    if (threadIdx.x == 0) {
+        const int u = total > 0 ? (int)atomicAdd(&args.sctl->prep_next[xcd], 1u) : 0;
+        sUnit = u < total ? (xcd + 8 * (u % hx)) * NC + u / hx : -1;
+    }
+    __syncthreads();
+    const int unit = __builtin_amdgcn_readfirstlane(sUnit);
+    if (unit < 0) return;
+    const bool flagged = prep_fast_unit<T, C, DK, ZS, false, false, NT>(args, unit);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0)
+        __hip_atomic_store(&args.ready[unit], flagged ? 2u : 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <typename T, int C, int DK>
@@ -739,6 +787,21 @@ hipError_t launch_fast_t(const ChunkShape& s, const PrepArgs& a, hipStream_t str
 
 template <typename T, int C, int DK>
 size_t fast_lds_t() { return FastLayout<T, C, DK>().total; }
+
+template <typename T, int C, int DK>
+hipError_t launch_stream_t(const PrepArgs& a, hipStream_t stream)
+{
+    const FastLayout<T, C, DK> LY;
+    auto kern = a.zx > 0 ? prep_stream_kernel<T, C, DK, true, false>
+                         : prep_stream_kernel<T, C, DK, false, false>;
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)LY.total);
+    if (e != hipSuccess) return e;
+    constexpr int kXcd = 8;                              // XCDs of the MI355X
+    const unsigned grid = (unsigned)(kXcd * ((a.nbh + kXcd - 1) / kXcd) * a.NC);
+    return launch_kernel(kern, dim3(grid), dim3(kThreads), (uint32_t)LY.total, stream, a);
+}
 
 template <typename T, int C>
 hipError_t dispatch_dk(const ChunkShape& s, const PrepArgs& a, hipStream_t st)
@@ -784,6 +847,15 @@ size_t prep_fast_lds_bytes(IoType io, int C, int Dk)
     }
     return C == 16 ? lds_dk<bf16_t, 16>(Dk) : C == 32 ? lds_dk<bf16_t, 32>(Dk)
                                                        : lds_dk<bf16_t, 64>(Dk);
+}
+
+hipError_t launch_prep_stream(IoType io, const ChunkShape& s, const PrepArgs& a,
+                              hipStream_t stream)
+{
+    if (io != IoType::BF16 || s.C != 64) return hipErrorInvalidValue;
+    if (s.Dk == 128) return launch_stream_t<bf16_t, 64, 128>(a, stream);
+    if (s.Dk == 64) return launch_stream_t<bf16_t, 64, 64>(a, stream);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_prep_fast(IoType io, const ChunkShape& s, const PrepArgs& a, hipStream_t stream)

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 15
+#define KDA_ABI_VERSION 16
 
 typedef enum {
     KDA_OK = 0,
@@ -106,6 +106,10 @@ typedef enum { KDA_MODE_KDA = 0, KDA_MODE_CKDA = 1 } kda_mode_t;
  * side stream and its events are not touched).  Calls without a side stream
  * always run on `stream` alone. */
 #define KDA_FLAG_SINGLE_STREAM 8u
+/* flags: with kda_chunk_forward_side, take the streamed form where it applies
+ * (see kda_chunk_forward_side; it measured slower than the two-pass form on
+ * the MI355X for every workload tried, so it is opt-in). */
+#define KDA_FLAG_STREAMED 16u
 
 /* ABI version of the loaded library (KDA_ABI_VERSION it was built with). */
 int kda_abi_version(void);
@@ -215,18 +219,40 @@ typedef struct {
 /*
  * kda_chunk_forward with a second stream for the overlap of the chunk-factor
  * kernels (intra-chunk WY, "Semidirect Fourier Delta Attention" §2.2) with the
- * state chain: when the (b, h, 16-column) chains number at most 128 (half the
- * GPU or less), no sequence segments are chosen and there are at least 256
- * chunks, the chunks of every (b, h) run in 8 consecutive parts: the factors
- * of part p + 1 are formed on side->stream while the chain runs part p on
- * `stream`, joined by side->events, so the call still ends on `stream` (a graph
- * captured from `stream` takes in the side stream through the events).  The
- * state crosses part boundaries in fp32, so results are bitwise those of
- * kda_chunk_forward.  Other shapes, side == NULL or KDA_FLAG_SINGLE_STREAM run
- * as kda_chunk_forward.  The workspace query is kda_chunk_forward_workspace_size
- * (it reserves the state between parts whenever the shape would run in
- * parts).  Errors: those of kda_chunk_forward; a NULL side->stream or event
- * is KDA_ERR_NULL_POINTER.
+ * state chain (§2.3), in one of two forms; either way the side stream is
+ * joined to `stream` by side->events, so the call still ends on `stream` (a
+ * graph captured from `stream` takes in the side stream through the events).
+ *
+ * Streamed (only with KDA_FLAG_STREAMED): bf16, chunk 64, Dk 128 or 64,
+ * B H >= 8, no sequence segments, the final state not written over the
+ * initial one, and `stream` not the null stream.  The chunk factors are
+ * formed on side->stream while the chain,
+ * already running on `stream`, consumes them chunk by chunk (each chunk is
+ * published in the workspace with a ready word; the chain reads it from the
+ * L2 cache of the XCD that formed it).  A chunk that needs the exact factor
+ * kernel, or a wait past its bound (10 ms; typically because side->stream and
+ * `stream` share a hardware queue: use kda_side_stream_create), makes the
+ * chain give up; the call then forms the flagged chunks and reruns the chain
+ * after the factors are complete, so results never depend on the timing.
+ * The chain is the 16-column kernel of kda_chunk_forward while the
+ * (b, h, 16-column) chains number at most 128, else the wide-slice kernel
+ * with 2 or 4 column tiles per workgroup; results equal those of
+ * kda_chunk_forward within rounding, bitwise where both calls run the same
+ * products in the same order.
+ *
+ * In parts: otherwise (and without the flag), when the (b, h, 16-column)
+ * chains number at most 128
+ * (half the GPU or less), no sequence segments are chosen and there are at
+ * least 256 chunks, the chunks of every (b, h) run in 8 consecutive parts: the
+ * factors of part p + 1 are formed on side->stream while the chain runs part
+ * p on `stream`.  The state crosses part boundaries in fp32, so results are
+ * bitwise those of kda_chunk_forward.
+ *
+ * Other shapes, side == NULL or KDA_FLAG_SINGLE_STREAM run as
+ * kda_chunk_forward.  The workspace query is kda_chunk_forward_workspace_size
+ * (it reserves the ready words and control block of the streamed form, and the
+ * state between parts, for every shape that could take them).  Errors: those
+ * of kda_chunk_forward; a NULL side->stream or event is KDA_ERR_NULL_POINTER.
  */
 kda_status_t kda_chunk_forward_side(const void* q, const void* k, const void* v,
                                     const float* alpha, const float* beta,
@@ -235,6 +261,21 @@ kda_status_t kda_chunk_forward_side(const void* q, const void* k, const void* v,
                                     kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
                                     void* workspace, size_t workspace_bytes, void* stream,
                                     const kda_side_t* side);
+
+/*
+ * A kda_side_t for kda_chunk_forward_side on the current device: a stream
+ * with a hardware queue of its own (created with a compute-unit mask that
+ * holds every compute unit; HIP spreads ordinary streams over a few shared
+ * queues, and two streams on one queue cannot run kernels at the same time,
+ * which the streamed form needs) and KDA_SIDE_EVENTS events with timing
+ * disabled.  The stream is a blocking one: work on the null stream waits for
+ * it, so the streamed form is not taken for calls on the null stream.  The
+ * caller owns the result and releases it with kda_side_stream_destroy (which
+ * first waits for the stream's work).  Errors: KDA_ERR_NULL_POINTER,
+ * KDA_ERR_HIP (nothing is left allocated).
+ */
+kda_status_t kda_side_stream_create(kda_side_t* side);
+kda_status_t kda_side_stream_destroy(kda_side_t* side);
 
 /* Size of the built-in scratch of kda_chunk_forward_noalloc (bytes per device). */
 #define KDA_NOALLOC_SCRATCH_BYTES (32u << 20)

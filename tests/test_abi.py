@@ -40,13 +40,20 @@ def test_exports_every_declared_symbol(lib):
             "kda_chunk_backward_varlen", "kda_chunk_backward_varlen_workspace_size",
             "kda_chunk_backward_varlen_prologue", "kda_chunk_backward_varlen_prologue_workspace_size",
             "kda_gate_prep", "kda_status_string", "kda_abi_version",
-            "kda_chunk_forward_noalloc", "kda_chunk_forward_side"} <= set(syms)
+            "kda_chunk_forward_noalloc", "kda_chunk_forward_side", "kda_side_stream_create",
+            "kda_side_stream_destroy"} <= set(syms)
     for s in syms:
         assert hasattr(lib, s), s
 
 
+def test_side_stream_helpers_refuse_null(lib):
+    null = ctypes.POINTER(kda._Side)()
+    assert lib.kda_side_stream_create(null) == NULLP
+    assert lib.kda_side_stream_destroy(null) == NULLP
+
+
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 15
+    assert lib.kda_abi_version() == 16
     for s in range(10):
         assert lib.kda_status_string(s) != b"unknown status"
     assert lib.kda_status_string(99) == b"unknown status"
@@ -62,8 +69,13 @@ def test_workspace_size(lib):
     st, n = ws_size(lib, 1, 8192, 32, 128, 128, 64, BF16)
     assert st == OK
     nu = 32 * 128
-    # W, Kt, QG, U, P bf16 + chunk decay fp32 + one flag byte, per chunk
-    assert n == nu * (3 * 64 * 128 * 2 + 64 * 128 * 2 + 64 * 64 * 2 + 128 * 4 + 1)
+    # W, Kt, QG, U, P bf16 + chunk decay fp32 + one flag byte, per chunk; then
+    # (streamed forward) one ready word per chunk and a 384-byte control block
+    assert n == nu * (3 * 64 * 128 * 2 + 64 * 128 * 2 + 64 * 64 * 2 + 128 * 4 + 1) \
+        + nu * 4 + 384
+    # below 8 (b, h) there is no streamed form: the per-chunk regions only
+    st, n = ws_size(lib, 1, 4096, 4, 128, 128, 64, BF16)
+    assert n == 4 * 64 * (3 * 64 * 128 * 2 + 64 * 128 * 2 + 64 * 64 * 2 + 128 * 4 + 1)
     assert ws_size(lib, 1, 0, 1, 16, 16, 16, F32) == (OK, 0)
     assert ws_size(lib, 1, 10, 1, 24, 16, 16, F32)[0] == UNSUP          # Dk not supported
     assert ws_size(lib, 1, 10, 1, 16, 24, 16, F32)[0] == UNSUP          # Dv not a multiple of 16

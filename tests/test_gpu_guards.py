@@ -5,7 +5,7 @@ unchanged.  Covers the chunked forward with both workspace store variants
 (ordinary stores below 128 (b, h, 16-column) chains, non-temporal ones from
 128), the chunk-start states, packed batches (rows past cu[N] untouched), the
 parts path on a side stream, the allocation-free forward, decode and the
-backward.  The results themselves are checked elsewhere; here they are only
+backward, and the streamed path.  The results themselves are checked elsewhere; here they are only
 required to be finite where written."""
 import math
 
@@ -103,6 +103,22 @@ def test_forward_parts_and_noalloc_guards():
     torch.cuda.synchronize()
     assert [n for n, _ in kda.last_stage_times()].count("chain") == 8
     _check("chunk_forward_side (parts)", g)
+    # the streamed path: ready words and control words at the workspace's end
+    w3 = workloads.workload(2, B=1, H=9, T=333)
+    d3 = _dev(workloads.make_prefill(w3))
+    nws3 = kda.workspace_size(w3.B, w3.T, w3.H, w3.Dk, w3.Dv, w3.chunk, w3.dtype)
+    g3 = {"out": Guarded((w3.B, w3.T, w3.H, w3.Dv), w3.dtype),
+          "final_state": Guarded((w3.B, w3.H, w3.Dk, w3.Dv), torch.float32),
+          "workspace": Guarded((nws3,), torch.uint8)}
+    torch.cuda.synchronize()
+    kda.chunk_forward(d3["q"], d3["k"], d3["v"], d3["alpha"], d3["beta"], d3["S0"],
+                      chunk=w3.chunk, mode=w3.mode, out=g3["out"].t,
+                      final_state=g3["final_state"].t, workspace=g3["workspace"].t,
+                      side=kda.SideStream(), flags=kda.STAGE_EVENTS | kda.STREAMED,
+                      stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    assert "chain_stream" in [n for n, _ in kda.last_stage_times()]
+    _check("chunk_forward_side (streamed)", g3)
     w2 = workloads.workload(3, B=1, H=4, T=300, chunk=64)
     d2 = _dev(workloads.make_prefill(w2))
     g2 = {"out": Guarded((w2.B, w2.T, w2.H, w2.Dv), w2.dtype),

@@ -33,6 +33,8 @@ def run_oracle(inp, heads=None):
 
 
 def run_gpu(inp, chunk, mode, **kw):
+    if kw.get("stream") is not None:
+        torch.cuda.synchronize()         # (inputs were made on the current stream)
     out, st = kda.chunk_forward(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"],
                                 inp.get("S0"), chunk=chunk, mode=mode, **kw)
     torch.cuda.synchronize()
