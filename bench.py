@@ -2,9 +2,10 @@
 
 Headline workload: KDA bf16 prefill, B=1 H=32 T=8192 d_k=d_v=128, chunk 64
 (seeded synthetic inputs resident in HBM before timing).  One step = one
-kda_chunk_forward call over the whole batch (gate summary, intra-chunk WY,
-state propagation and outputs).  Every call is launched on a non-default
-stream of ours.  Prints ONE JSON line.
+kda_chunk_forward_side call over the whole batch in the streamed form
+(KDA_FLAG_STREAMED: gate summary and intra-chunk WY on a second stream while
+the state propagation and outputs consume each chunk as it is formed).  Every
+call is launched on a non-default stream of ours.  Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-others] [--no-cpu]
                   [--backward] [--decode] [--gate-prep] [--copy-probe] [--mfma-probe]
@@ -317,7 +318,8 @@ def main():
     # stream's work: the overlapped forms need a non-default launch stream)
     torch.cuda.set_stream(torch.cuda.Stream())
     side = kda.SideStream()
-    ms, mean_ms, per, out, st = time_forward(kda, torch, w, inp, args.steps, args.warmup)
+    ms, mean_ms, per, out, st = time_forward(kda, torch, w, inp, args.steps, args.warmup,
+                                             extra_flags=kda.STREAMED, side=side)
     tokens = w.B * w.T
     io_bytes = 2
     ab = algorithmic_bytes(w, io_bytes, inp["S0"] is not None, True)
@@ -354,24 +356,25 @@ def main():
                      "scope": "whole call", "algorithmic_bytes": ab["path"],
                      "traffic_ratio": (traffic_total / ab["path"]) if traffic_total else None,
                      "mfma_bf16_frac": chunk_flops(w) / (ms / 1e3) / 1e12 / MFMA_BF16_TFLOPS},
-        "timing": {"median_ms": ms, "mean_ms": mean_ms, "calls": args.steps},
+        "timing": {"median_ms": ms, "mean_ms": mean_ms, "calls": args.steps,
+                   "call": "kda_chunk_forward_side, KDA_FLAG_STREAMED"},
         "kernels": kernels,
         "kernels_ms": per,
     }
     if not args.no_others:
         others = {}
-        # the same workload in the streamed form (KDA_FLAG_STREAMED: prep grid
-        # and chain at once on two streams; slower, kept for the record)
-        ms1, _, per1, _, _ = time_forward(kda, torch, w, inp, max(20, args.steps // 4), 3,
-                                          extra_flags=kda.STREAMED, side=side)
-        others["kda_bf16_prefill_streamed"] = {"ms": ms1, "tokens_per_s": tokens / (ms1 / 1e3),
+        # the same workload in the two-pass form (kda_chunk_forward: the prep
+        # kernels, then the chain)
+        ms1, _, per1, _, _ = time_forward(kda, torch, w, inp, max(20, args.steps // 4), 3)
+        others["kda_bf16_prefill_two_pass"] = {"ms": ms1, "tokens_per_s": tokens / (ms1 / 1e3),
                                                "path_hbm_frac": ab["path"] / (ms1 / 1e3) / 1e9 / HBM_PEAK_GBS,
                                                "kernels_ms": per1}
         for wid in (3, 1, 0):
             wo = workloads.workload(wid)
             io = workloads.make_prefill(wo, device="cuda")
-            # the long-context workload runs in parts on a second stream of ours
+            # the long-context workload is streamed on a second stream of ours
             mso, _, pero, _, _ = time_forward(kda, torch, wo, io, max(20, args.steps // 4), 3,
+                                              extra_flags=kda.STREAMED if wid == 3 else 0,
                                               side=side if wid == 3 else None)
             abo = algorithmic_bytes(wo, 2 if wo.dtype == torch.bfloat16 else 4,
                                     io["S0"] is not None, True)
@@ -379,6 +382,14 @@ def main():
                                "path_hbm_frac": abo["path"] / (mso / 1e3) / 1e9 / HBM_PEAK_GBS,
                                "kernels_ms": pero}
             del io
+        # the long-context workload in parts (the prep of part p + 1 beside the
+        # chain of part p) instead of streamed
+        wo = workloads.workload(3)
+        io = workloads.make_prefill(wo, device="cuda")
+        mso, _, pero, _, _ = time_forward(kda, torch, wo, io, max(20, args.steps // 4), 3, side=side)
+        others["ckda_bf16_long_ctx_parts"] = {"ms": mso, "tokens_per_s": wo.B * wo.T / (mso / 1e3),
+                                              "kernels_ms": pero}
+        del io
         # few heads, long context: sequence segments against one chain per head
         wo = workloads.workload(3, H=2)
         io = workloads.make_prefill(wo, device="cuda")

@@ -233,15 +233,7 @@ __device__ __forceinline__ void read_ops(ChainOps<T, C, DK>& o, const unsigned c
     }
 }
 
-// STREAM: the streamed forward, run while the prep grid forms the units.  A
-// workgroup takes its (b, h, 16-column slice) from its own XCD's counter (so
-// it reads units formed on that XCD, from the L2 they share), and each loader
-// wavefront waits for a unit's ready word before it issues the unit's loads;
-// a loader that gives up (raising the abort word) issues the same loads
-// without waiting from then on, and the call's fallback chain redoes the
-// work.  The L2 prefetch then fetches the unit just waited for (the units
-// are in the L2 already; prefetching later ones could fetch them early).
-template <typename T, int C, int DK, bool STREAM = false>
+template <typename T, int C, int DK>
 __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
 {
     using G = ChainGeom<T, C, DK>;
@@ -258,18 +250,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
     const bool summary = a.summ != nullptr;
     const int nseg = a.nseg > 1 ? a.nseg : 1;
     const int NSX = summary ? DK / 16 + NS : NS;           // column slices per chain
-    int g = blockIdx.x;
-    if constexpr (STREAM) {
-        // the k-th claim on XCD x stands for launch index 8 k + x
-        __shared__ int sRole;
-        if (threadIdx.x == 0) {
-            const unsigned x = xcc_id();
-            sRole = (int)(atomicAdd(&a.sctl->chain_next[x], 1u) * kXcds + x);
-        }
-        __syncthreads();
-        g = __builtin_amdgcn_readfirstlane(sRole);
-    }
-    const int xcd = g % kXcds, jx = g / kXcds;
+    const int g = blockIdx.x, xcd = g % kXcds, jx = g / kXcds;
     const int vb = (jx / NSX) * kXcds + xcd, xslice = jx % NSX;
     if (vb >= a.B * H * nseg) return;
     const int bh = vb / nseg, sg = vb % nseg;
@@ -322,26 +303,11 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
         // chunk c is also prefetched into L2 at step c - 5 (KPF loads per
         // loader and step)
         unsigned char* sink = stages + G::SINK;
-        // (streamed) wait for unit u unless this loader gave up; `live` is
-        // uniform over the wavefront
-        bool live = true;
-        auto ready = [&](size_t u) {
-            if constexpr (STREAM) {
-                if (live)
-                    live = __builtin_amdgcn_readfirstlane(
-                        (int)stream_wait_ready(a.ready, a.sctl, u,
-                                               __hip_atomic_load(&a.ready[u], __ATOMIC_RELAXED,
-                                                                 __HIP_MEMORY_SCOPE_AGENT))) != 0;
-            }
-        };
-        auto pf = [&](int ahead, int now) { return u0 + min(STREAM ? now : ahead, last); };
-        ready(u0);
         issue_all<T, C, DK>(stg(0), a, u0, cw, lane, slice);
-        prefetch_chunk<T, C, DK>(a, pf(2, 0), slice, NS, cw, lane, sink);
-        prefetch_chunk<T, C, DK>(a, pf(3, 0), slice, NS, cw, lane, sink);
-        ready(u0 + min(1, last));
+        prefetch_chunk<T, C, DK>(a, u0 + min(2, last), slice, NS, cw, lane, sink);
+        prefetch_chunk<T, C, DK>(a, u0 + min(3, last), slice, NS, cw, lane, sink);
         issue_all<T, C, DK>(stg(1), a, u0 + min(1, last), cw, lane, slice);
-        prefetch_chunk<T, C, DK>(a, pf(4, 1), slice, NS, cw, lane, sink);
+        prefetch_chunk<T, C, DK>(a, u0 + min(4, last), slice, NS, cw, lane, sink);
         wait_vm<G::NDMA + 3 * G::KPF>();             // chunk 0 landed
         lds_barrier();                               // B0: compute reads chunk 0
         lds_barrier();                               // B1: stage 0 free
@@ -351,13 +317,12 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
             // issuing blocks while the load pipe is full, so the compute
             // wavefronts must not wait at barrier 1 for all of it.  Loads
             // issued after chunk nc + 1: the previous step's prefetch and part 0.
-            ready(u0 + min(nc + 2, last));
             issue_chunk<T, C, DK, 0>(stg(nc), a, u0 + min(nc + 2, last), cw, lane, slice);
             wait_vm<N0 + G::KPF>();                  // chunk nc + 1 landed
             lds_barrier();
             issue_chunk<T, C, DK, 1>(stg(nc), a, u0 + min(nc + 2, last), cw, lane, slice);
             issue_chunk<T, C, DK, 2>(stg(nc), a, u0 + min(nc + 2, last), cw, lane, slice);
-            prefetch_chunk<T, C, DK>(a, pf(nc + 5, nc + 2), slice, NS, cw, lane, sink);
+            prefetch_chunk<T, C, DK>(a, u0 + min(nc + 5, last), slice, NS, cw, lane, sink);
             lds_barrier();
         }
         wait_vm<0>();   // no load may land in LDS after the workgroup ends
@@ -517,9 +482,6 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
             }
         }
     }
-    if constexpr (STREAM) {
-        if (threadIdx.x == 0) atomicAdd(&a.sctl->chains_done, 1u);
-    }
 }
 
 // Segment start states: S_0 = S0 (or zero), S_{g+1} = X_g S_g + Y_g in fp32
@@ -602,11 +564,11 @@ hipError_t launch_combine_t(int BH, int Dv, int nseg, const float* S0, const flo
                          0, stream, S0, summ, Sseg, BH, nseg, Dv);
 }
 
-template <typename T, int C, int DK, bool STREAM = false>
+template <typename T, int C, int DK>
 hipError_t launch_chain_t(const ChunkShape& s, const ChainArgs& a, hipStream_t stream)
 {
     using G = ChainGeom<T, C, DK>;
-    auto kern = chain_kernel<T, C, DK, STREAM>;
+    auto kern = chain_kernel<T, C, DK>;
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)G::LDS_TOTAL);
     if (e != hipSuccess) return e;
@@ -659,15 +621,6 @@ hipError_t launch_chain(IoType io, const ChunkShape& s, const ChainArgs& a, hipS
 {
     if (io == IoType::F32) return dispatch_c<float>(s, a, stream);
     return dispatch_c<bf16_t>(s, a, stream);
-}
-
-hipError_t launch_chain_lds_stream(IoType io, const ChunkShape& s, const ChainArgs& a,
-                                   hipStream_t stream)
-{
-    if (io != IoType::BF16 || s.C != 64 || a.summ || a.nseg > 1) return hipErrorInvalidValue;
-    if (s.Dk == 128) return launch_chain_t<bf16_t, 64, 128, true>(s, a, stream);
-    if (s.Dk == 64) return launch_chain_t<bf16_t, 64, 64, true>(s, a, stream);
-    return hipErrorInvalidValue;
 }
 
 }  // namespace kda

@@ -463,7 +463,7 @@ hipError_t launch_chain_stream(IoType io, const ChunkShape& s, const ChainArgs& 
     if (io != IoType::BF16 || s.C != 64) return hipErrorInvalidValue;
     if (s.Dk == 128) {
         if (ct == 4) return launch_wide_t<bf16_t, 64, 128, 4, 2, true>(s, a, stream);
-        if (ct == 2) return launch_wide_t<bf16_t, 64, 128, 2, 2, true>(s, a, stream);
+        if (ct == 2) return launch_wide_t<bf16_t, 64, 128, 2, 3, true>(s, a, stream);
         return launch_wide_t<bf16_t, 64, 128, 1, 3, true>(s, a, stream);
     }
     if (s.Dk == 64) {

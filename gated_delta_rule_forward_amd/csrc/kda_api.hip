@@ -183,26 +183,56 @@ Parts parts_for(int B, int H, int Dk, int Dv, int NC)
     return {(NC + len - 1) / len, len};
 }
 
-// Streamed forward (kda_chunk_forward_side): the chunk factors are formed by a
-// persistent prep grid on the side stream while the chain consumes them on the
-// caller's stream, unit by unit, through the L2 of the XCD both run on.
-// Covered: bf16, chunk 64, Dk 128 or 64, at least 8 (b, h) (every XCD holds
-// heads, so every XCD's prep workgroups have units to form).
-bool stream_shape(int B, int H, int Dk, int chunk, kda_dtype_t dtype)
+// Streamed forward (kda_chunk_forward_side with KDA_FLAG_STREAMED): the chunk
+// factors are formed by a prep grid on the side stream while the chain
+// consumes them on the caller's stream, unit by unit, through the L2 of the
+// XCD both run on.  Covered: bf16, chunk 64, Dk 128 or 64, at least 8 (b, h)
+// (every XCD holds heads, so every XCD's prep workgroups have units to form),
+// and a chain width that leaves half the compute units to the prep grid.
+int stream_tiles(int B, int H, int Dk, int Dv);
+bool stream_shape(int B, int H, int Dk, int Dv, int chunk, kda_dtype_t dtype)
 {
     return dtype == KDA_DTYPE_BF16 && chunk == 64 && (Dk == 128 || Dk == 64) &&
-           (long long)B * H >= 8;
+           (long long)B * H >= 8 && stream_tiles(B, H, Dk, Dv) > 0;
 }
-// the streamed chain: the 16-column LDS-staged kernel while its workgroups
-// (one per (b, h, 16 columns), each the whole of a compute unit) leave half
-// the compute units to the prep grid, else the wide kernel
-bool stream_lds_chain(long long chains) { return chains <= 128; }
-// column tiles per workgroup of the streamed chain when it is the wide kernel
-int stream_tiles(int Dk, int Dv)
+// Column tiles per workgroup of the streamed chain (the wide kernel; each
+// workgroup holds a whole compute unit).  Allowed: the widths that keep the
+// chain within 128 workgroups (stream_tiles: the fewest such, 0 when none:
+// the call then takes the two-pass form).  Chosen (stream_pick_tiles): the
+// allowed width whose estimated call is shortest, the call being about the
+// longer of the chain (NC steps of 1.3, 1.6 or 2.9 us at 1, 2 or 4 tiles
+// beside the prep grid) and the prep grid on the compute units the chain
+// leaves (9.4 us of one compute unit per unit, 13.4 with zero-segment
+// columns).  Measured (bf16, d = 128; ms per call, two-pass against
+// streamed at 1 / 2 / 4 tiles): H=32, T=8192: 0.327 against gives up (the
+// chain fills every compute unit) / 0.318 / 0.395; H=16, T=8192: 0.237
+// against 0.187 / 0.225 / 0.289; H=16, T=65536 (CKDA): 1.84 in parts
+// against 1.79 / 1.675 / 2.41; H=24, T=8192: 0.272 against - / 0.230 /
+// 0.290; B=2, H=32, T=8192: 0.606 against - / - / 0.58.
+int stream_tiles(int B, int H, int Dk, int Dv)
 {
-    if (Dk == 128 && Dv % 64 == 0) return 4;
-    if (Dv % 32 == 0) return 2;
-    return 1;
+    const long long chains = (long long)B * H * (Dv / 16);
+    const int maxt = Dk == 128 ? 4 : 2;
+    for (int ct = 1; ct <= maxt; ct *= 2)
+        if (Dv % (16 * ct) == 0 && chains / ct <= 128) return ct;
+    return 0;
+}
+int stream_pick_tiles(int B, int H, int Dk, int Dv, int NC, bool zero_cols, int ncu)
+{
+    const long long chains = (long long)B * H * (Dv / 16);
+    const double units = (double)B * H * NC, unit_cu_us = zero_cols ? 13.4 : 9.4;
+    const int maxt = Dk == 128 ? 4 : 2;
+    int best = stream_tiles(B, H, Dk, Dv);
+    double best_t = 1e30;
+    for (int ct = best; ct >= 1 && ct <= maxt; ct *= 2) {
+        if (Dv % (16 * ct) != 0 || chains / ct > 128) continue;
+        const double wgs = (double)(chains / ct);
+        const double chain = NC * (ct == 1 ? 1.3 : ct == 2 ? 1.6 : 2.9);
+        const double prep = units * unit_cu_us / std::max(1.0, ncu - wgs);
+        const double t = std::max(chain, prep);
+        if (t < best_t) { best_t = t; best = ct; }
+    }
+    return best;
 }
 
 // workspace of a dense forward: the per-unit regions, then (with segments)
@@ -232,7 +262,7 @@ size_t dense_layout(int B, int T, int H, int Dk, int Dv, int chunk, IoType io,
     // (streamed forward) a ready word per unit, then the control words
     if (ready_off) *ready_off = 0;
     if (sctl_off) *sctl_off = 0;
-    if (stream_shape(B, H, Dk, chunk, io == IoType::F32 ? KDA_DTYPE_F32 : KDA_DTYPE_BF16)) {
+    if (stream_shape(B, H, Dk, Dv, chunk, io == IoType::F32 ? KDA_DTYPE_F32 : KDA_DTYPE_BF16)) {
         if (ready_off) *ready_off = n;
         n += ((size_t)B * H * sh.NC * 4 + 255) & ~size_t(255);
         if (sctl_off) *sctl_off = n;
@@ -396,7 +426,7 @@ kda_status_t chunk_forward(const void* q, const void* k, const void* v, const fl
     const bool streamed = side && s && (flags & KDA_FLAG_STREAMED) &&
                           !(flags & KDA_FLAG_SINGLE_STREAM) && !pro && !theta &&
                           !chunk_states && !(final_state && final_state == initial_state) &&
-                          sgm.nseg == 1 && stream_shape(B, H, Dk, chunk, dtype);
+                          sgm.nseg == 1 && stream_shape(B, H, Dk, Dv, chunk, dtype);
     bool use_side = prt.parts > 1 || streamed;
     hipDevice_t d0 = 0;
     if (use_side) {
@@ -423,11 +453,12 @@ kda_status_t chunk_forward(const void* q, const void* k, const void* v, const fl
         dense_layout(B, T, H, Dk, Dv, chunk, io, offs, &a0, &a1, &a2, &roff, &coff);
         unsigned* ready = reinterpret_cast<unsigned*>(w + roff);
         kda::StreamCtl* ctl = reinterpret_cast<kda::StreamCtl*>(w + coff);
-        // the chain: the 16-column LDS-staged kernel (ct = 0), or the wide one
-        // with ct column tiles per workgroup
-        const int ct = stream_lds_chain((long long)B * H * (Dv / 16)) ? 0 : stream_tiles(Dk, Dv);
+        int ncu = 0;
+        if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, d0) != hipSuccess)
+            return KDA_ERR_HIP;
+        const int ct = stream_pick_tiles(B, H, Dk, Dv, sh.NC, zx > 0, ncu);   // (>= 1: stream_shape)
         const long long bhn = (long long)B * H;
-        const int nsl = Dv / (16 * (ct > 0 ? ct : 1));
+        const int nsl = Dv / (16 * ct);
         kda::PrepArgs ps = pa;
         ps.ntst = 0;
         ps.nbh = (int)bhn;
@@ -443,9 +474,7 @@ kda_status_t chunk_forward(const void* q, const void* k, const void* v, const fl
         if (rec.done() != hipSuccess) return KDA_ERR_HIP;
         if (hipEventRecord(ev0, s) != hipSuccess) return KDA_ERR_HIP;
         if (rec.mark("chain_stream") != hipSuccess) return KDA_ERR_HIP;
-        if ((ct > 0 ? kda::launch_chain_stream(io, sh, cst, ct, s)
-                    : kda::launch_chain_lds_stream(io, sh, cst, s)) != hipSuccess)
-            return KDA_ERR_HIP;
+        if (kda::launch_chain_stream(io, sh, cst, ct, s) != hipSuccess) return KDA_ERR_HIP;
         if (rec.done() != hipSuccess) return KDA_ERR_HIP;
         if (hipStreamWaitEvent(ss, ev0, 0) != hipSuccess) return KDA_ERR_HIP;
         if (rec.mark("prep_stream") != hipSuccess) return KDA_ERR_HIP;
@@ -1135,9 +1164,11 @@ kda_status_t kda_side_stream_create(kda_side_t* side)
     if (hipExtStreamCreateWithCUMask(&st, (uint32_t)mask.size(), mask.data()) != hipSuccess)
         return KDA_ERR_HIP;
     side->stream = st;
+    // (the events only order work on this device: a device-scope release is
+    // enough, and it spares the system-scope cache write-back at each record)
     for (int i = 0; i < KDA_SIDE_EVENTS; ++i) {
         hipEvent_t e = nullptr;
-        if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
+        if (hipEventCreateWithFlags(&e, hipEventDisableTiming | hipEventReleaseToDevice) != hipSuccess) {
             kda_side_stream_destroy(side);
             return KDA_ERR_HIP;
         }

@@ -66,9 +66,6 @@ hipError_t launch_prep_stream(IoType io, const ChunkShape& s, const PrepArgs& a,
                               hipStream_t stream);
 hipError_t launch_chain_stream(IoType io, const ChunkShape& s, const ChainArgs& a, int ct,
                                hipStream_t stream);
-// the 16-column LDS-staged chain (chain.hip) in the streamed form
-hipError_t launch_chain_lds_stream(IoType io, const ChunkShape& s, const ChainArgs& a,
-                                   hipStream_t stream);
 hipError_t launch_stream_clear(unsigned* ready, size_t nu, StreamCtl* ctl, unsigned expect,
                                hipStream_t stream);
 hipError_t launch_prep_exact(IoType io, const ChunkShape& s, const PrepArgs& a, hipStream_t stream);

@@ -107,8 +107,9 @@ typedef enum { KDA_MODE_KDA = 0, KDA_MODE_CKDA = 1 } kda_mode_t;
  * always run on `stream` alone. */
 #define KDA_FLAG_SINGLE_STREAM 8u
 /* flags: with kda_chunk_forward_side, take the streamed form where it applies
- * (see kda_chunk_forward_side; it measured slower than the two-pass form on
- * the MI355X for every workload tried, so it is opt-in). */
+ * (see kda_chunk_forward_side).  Opt-in because it needs a side stream with
+ * a hardware queue of its own (kda_side_stream_create): on a shared queue
+ * every call waits out the chain's 10 ms bound before its fallback runs. */
 #define KDA_FLAG_STREAMED 16u
 
 /* ABI version of the loaded library (KDA_ABI_VERSION it was built with). */
@@ -225,8 +226,11 @@ typedef struct {
  *
  * Streamed (only with KDA_FLAG_STREAMED): bf16, chunk 64, Dk 128 or 64,
  * B H >= 8, no sequence segments, the final state not written over the
- * initial one, and `stream` not the null stream.  The chunk factors are
- * formed on side->stream while the chain,
+ * initial one, `stream` not the null stream, and at most 128 chain
+ * workgroups: the (b, h, 16-column) chains taken 1, 2 or 4 column tiles per
+ * workgroup (4 only at Dk = 128), the fewest tiles that leave half the
+ * compute units to the factor kernels.  The chunk factors are formed on
+ * side->stream while the chain,
  * already running on `stream`, consumes them chunk by chunk (each chunk is
  * published in the workspace with a ready word; the chain reads it from the
  * L2 cache of the XCD that formed it).  A chunk that needs the exact factor
@@ -234,11 +238,9 @@ typedef struct {
  * `stream` share a hardware queue: use kda_side_stream_create), makes the
  * chain give up; the call then forms the flagged chunks and reruns the chain
  * after the factors are complete, so results never depend on the timing.
- * The chain is the 16-column kernel of kda_chunk_forward while the
- * (b, h, 16-column) chains number at most 128, else the wide-slice kernel
- * with 2 or 4 column tiles per workgroup; results equal those of
- * kda_chunk_forward within rounding, bitwise where both calls run the same
- * products in the same order.
+ * The chain is the wide-slice kernel (operands straight into registers);
+ * results are bitwise those of kda_chunk_forward (the same products in the
+ * same order, whatever the column tiles per workgroup).
  *
  * In parts: otherwise (and without the flag), when the (b, h, 16-column)
  * chains number at most 128
@@ -268,7 +270,7 @@ kda_status_t kda_chunk_forward_side(const void* q, const void* k, const void* v,
  * holds every compute unit; HIP spreads ordinary streams over a few shared
  * queues, and two streams on one queue cannot run kernels at the same time,
  * which the streamed form needs) and KDA_SIDE_EVENTS events with timing
- * disabled.  The stream is a blocking one: work on the null stream waits for
+ * disabled and a device-scope release (they only order work on the device).  The stream is a blocking one: work on the null stream waits for
  * it, so the streamed form is not taken for calls on the null stream.  The
  * caller owns the result and releases it with kda_side_stream_destroy (which
  * first waits for the stream's work).  Errors: KDA_ERR_NULL_POINTER,

@@ -128,9 +128,10 @@ def test_streamed_flagged_chunks_give_up():
 
 def test_streamed_not_taken():
     """Forms outside the streamed path keep their launch sequence with a side
-    stream: fewer than 8 sequences, the final state written over the initial
-    one, KDA_FLAG_SINGLE_STREAM (all from a non-null stream; chunk-start states
-    have no side-stream entry point)."""
+    stream: fewer than 8 sequences, too many chains, the final state written
+    over the initial one, KDA_FLAG_SINGLE_STREAM, no KDA_FLAG_STREAMED (all
+    from a non-null stream; chunk-start states have no side-stream entry
+    point)."""
     w = workloads.workload(2, B=1, H=8, T=200)
     d = to_dev(workloads.make_prefill(w))
     side = kda.SideStream()
@@ -144,6 +145,12 @@ def test_streamed_not_taken():
     w7 = workloads.workload(2, B=1, H=7, T=200)
     d7 = to_dev(workloads.make_prefill(w7))
     run_gpu(d7, 64, w7.mode, side=side, flags=SF | kda.STAGE_EVENTS)
+    assert "chain_stream" not in _stage_names()
+    # 1024 (b, h, 16-column) chains: even 4 column tiles per workgroup would
+    # take every compute unit
+    wb = workloads.workload(2, B=4, H=32, T=64)
+    db = to_dev(workloads.make_prefill(wb))
+    run_gpu(db, 64, wb.mode, side=side, flags=SF | kda.STAGE_EVENTS)
     assert "chain_stream" not in _stage_names()
     S = torch.zeros((w.B, w.H, w.D, w.D), device=DEV)
     kda.chunk_forward(d["q"], d["k"], d["v"], d["alpha"], d["beta"], S, chunk=64, mode=w.mode,
