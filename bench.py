@@ -381,8 +381,12 @@ def main():
         # the same workload in the two-pass form (kda_chunk_forward: the prep
         # kernels, then the chain)
         ms1, _, per1, _, _ = time_forward(kda, torch, w, inp, max(20, args.steps // 4), 3)
+        tr1 = [measured_traffic(n) for n in per1 if n in KERNEL_SOURCES]
+        tr1 = None if (not tr1 or None in tr1) else sum(tr1)
         others["kda_bf16_prefill_two_pass"] = {"ms": ms1, "tokens_per_s": tokens / (ms1 / 1e3),
                                                "path_hbm_frac": ab["path"] / (ms1 / 1e3) / 1e9 / HBM_PEAK_GBS,
+                                               "traffic_bytes": tr1,
+                                               "traffic_ratio": tr1 / ab["path"] if tr1 else None,
                                                "kernels_ms": per1}
         for wid in (3, 1, 0):
             wo = workloads.workload(wid)

@@ -397,17 +397,26 @@ def test_forward_kda_bf16_prefill_full():
 
 def test_forward_ckda_long_ctx_full():
     """CKDA bf16 long context, B=1 H=16 T=65536 d=128, S0 ~ N(0, 0.02^2), every
-    head against the oracle (the call the benchmark times: parts path on a
-    side stream)."""
+    head against the oracle, through the call the benchmark times (streamed,
+    from a non-null stream); the parts form (the same side stream lent from
+    the null stream) and the two-pass call are bitwise equal to it."""
     w = workloads.workload(3)
     say(f"[forward] ckda_bf16_long_ctx full, all heads {w}")
     inp = workloads.make_prefill(w, device=DEV)
-    out, st = run_gpu(inp, w.chunk, w.mode, side=kda.SideStream())
+    side = kda.SideStream()
+    out, st = run_gpu(inp, w.chunk, w.mode, side=side, flags=kda.STREAMED | kda.STAGE_EVENTS,
+                      stream=torch.cuda.Stream())
+    assert "chain_stream" in [n for n, _ in kda.last_stage_times()]
     o_ref, s_ref = run_oracle(inp)
     eo = slice_err_out(np32(out), o_ref)
     es = slice_err_state(np32(st), s_ref)
     say(f"  err out {eo:.3e} state {es:.3e}{elem_note()}")
     assert eo <= 2e-2 and es <= 2e-2
+    out1, st1 = run_gpu(inp, w.chunk, w.mode, side=side, flags=kda.STAGE_EVENTS)
+    assert [n for n, _ in kda.last_stage_times()].count("chain") == 8
+    out2, st2 = run_gpu(inp, w.chunk, w.mode)
+    assert torch.equal(out, out1) and torch.equal(st, st1)
+    assert torch.equal(out, out2) and torch.equal(st, st2)
 
 
 DECODE = [
