@@ -71,25 +71,28 @@ __global__ __launch_bounds__(256) void varlen_table_kernel(const int* __restrict
 
 // streamed forward: every ready word 0, the control words 0, expect set
 __global__ __launch_bounds__(256) void stream_clear_kernel(unsigned* __restrict__ ready, size_t nu,
-                                                           StreamCtl* __restrict__ ctl, unsigned expect)
+                                                           StreamCtl* __restrict__ ctl, unsigned expect,
+                                                           unsigned tiles)
 {
     const size_t stride = (size_t)gridDim.x * blockDim.x;
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nu; i += stride) ready[i] = 0u;
     if (blockIdx.x == 0) {
         unsigned* w = reinterpret_cast<unsigned*>(ctl);
         for (unsigned i = threadIdx.x; i < sizeof(StreamCtl) / 4; i += blockDim.x)
-            w[i] = i == offsetof(StreamCtl, expect) / 4 ? expect : 0u;
+            w[i] = i == offsetof(StreamCtl, expect) / 4 ? expect
+                 : i == offsetof(StreamCtl, tiles) / 4  ? tiles : 0u;
     }
 }
 
 }  // namespace
 
 hipError_t launch_stream_clear(unsigned* ready, size_t nu, StreamCtl* ctl, unsigned expect,
-                               hipStream_t stream)
+                               unsigned tiles, hipStream_t stream)
 {
     const size_t blocks = (nu + 255) / 256;
     const unsigned grid = (unsigned)(blocks < 1 ? 1 : (blocks > 1024 ? 1024 : blocks));
-    return launch_kernel(stream_clear_kernel, dim3(grid), dim3(256), 0, stream, ready, nu, ctl, expect);
+    return launch_kernel(stream_clear_kernel, dim3(grid), dim3(256), 0, stream, ready, nu, ctl, expect,
+                         tiles);
 }
 
 hipError_t launch_varlen_table(const int* cu, int N, int total_T, int C, int umax, int* cu_s,

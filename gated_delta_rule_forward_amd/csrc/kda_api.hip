@@ -468,7 +468,8 @@ kda_status_t chunk_forward(const void* q, const void* k, const void* v, const fl
         cst.ready = ready;
         cst.sctl = ctl;
         if (rec.mark("stream_clear") != hipSuccess) return KDA_ERR_HIP;
-        if (kda::launch_stream_clear(ready, (size_t)bhn * sh.NC, ctl, (unsigned)(bhn * nsl), s) !=
+        if (kda::launch_stream_clear(ready, (size_t)bhn * sh.NC, ctl, (unsigned)(bhn * nsl),
+                                     (unsigned)ct, s) !=
             hipSuccess)
             return KDA_ERR_HIP;
         if (rec.done() != hipSuccess) return KDA_ERR_HIP;

@@ -175,7 +175,8 @@ struct StreamCtl {
     unsigned chain_next[8];    // next (head, column slice) index per XCD (chain workgroups)
     unsigned chains_done;      // chain workgroups that ran their sequence to the end
     unsigned expect;           // chain workgroups the call needs
-    unsigned pad1[22];
+    unsigned tiles;            // column tiles per chain workgroup (a record of the call's choice)
+    unsigned pad1[21];
     unsigned abort;            // a chain workgroup met a unit of the exact kernel or gave up waiting
     unsigned pad2[31];
 };

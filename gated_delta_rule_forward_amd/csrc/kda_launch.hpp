@@ -67,7 +67,7 @@ hipError_t launch_prep_stream(IoType io, const ChunkShape& s, const PrepArgs& a,
 hipError_t launch_chain_stream(IoType io, const ChunkShape& s, const ChainArgs& a, int ct,
                                hipStream_t stream);
 hipError_t launch_stream_clear(unsigned* ready, size_t nu, StreamCtl* ctl, unsigned expect,
-                               hipStream_t stream);
+                               unsigned tiles, hipStream_t stream);
 hipError_t launch_prep_exact(IoType io, const ChunkShape& s, const PrepArgs& a, hipStream_t stream);
 hipError_t launch_chain(IoType io, const ChunkShape& s, const ChainArgs& a, hipStream_t stream);
 // the wide-slice chain (16 ct columns per workgroup, operands in registers);

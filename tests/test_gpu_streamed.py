@@ -10,8 +10,8 @@ runs the exact kernel and a fallback chain after the prep grid has finished.
 
 White-box: the last 384 bytes of the workspace are the control words of the
 streamed call, as 32-bit words: prep counters [0:8], chain counters [32:40],
-chains done [40], chains expected [41], give-up word [64]; the tests read
-them to see which way the call went.
+chains done [40], chains expected [41], column tiles per chain workgroup
+[42], give-up word [64]; the tests read them to see which way the call went.
 
 Checks: the oracle's recurrence across column-tile widths (Dv 128, 96, 48 at
 Dk 128; 64, 48 at Dk 64), ragged tails, initial states, both modes and
@@ -41,6 +41,11 @@ def _ctl(ws):
     return int(w[64]), int(w[40]), int(w[41])
 
 
+def _tiles(ws):
+    """Column tiles per chain workgroup the call chose."""
+    return int(ws[-384:].cpu().view(torch.int32)[42])
+
+
 def _prefill(base, dv, **ov):
     w = workloads.workload(base, **ov)
     inp = workloads.make_prefill(w)
@@ -51,20 +56,24 @@ def _prefill(base, dv, **ov):
     return w, inp
 
 
-# (name, base workload, Dv, overrides)
+# (name, base workload, Dv, overrides, column tiles per chain workgroup)
 STREAMED = [
-    ("kda_d128_dv128_B1_H8_T1000", 2, 128, dict(B=1, H=8, T=1000)),
-    ("ckda_d128_dv128_B2_H4_T777_s0", 3, 128, dict(B=2, H=4, T=777, s0_std=0.3)),
-    ("ckda_d128_dv96_B1_H9_T300_s0", 3, 96, dict(B=1, H=9, T=300, s0_std=0.2)),
-    ("kda_d128_dv48_B3_H3_T129", 2, 48, dict(B=3, H=3, T=129)),
-    ("ckda_d64_dv64_B1_H12_T513_s0", 3, 64, dict(B=1, H=12, T=513, D=64, s0_std=0.3)),
-    ("kda_d64_dv48_B2_H5_T64", 2, 48, dict(B=2, H=5, T=64, D=64)),
-    ("kda_d128_dv128_B1_H24_T200", 2, 128, dict(B=1, H=24, T=200)),
+    ("kda_d128_dv128_B1_H8_T1000", 2, 128, dict(B=1, H=8, T=1000), 1),
+    ("ckda_d128_dv128_B2_H4_T777_s0", 3, 128, dict(B=2, H=4, T=777, s0_std=0.3), 1),
+    ("ckda_d128_dv96_B1_H9_T300_s0", 3, 96, dict(B=1, H=9, T=300, s0_std=0.2), 1),
+    ("kda_d128_dv48_B3_H3_T129", 2, 48, dict(B=3, H=3, T=129), 1),
+    ("ckda_d64_dv64_B1_H12_T513_s0", 3, 64, dict(B=1, H=12, T=513, D=64, s0_std=0.3), 1),
+    ("kda_d64_dv48_B2_H5_T64", 2, 48, dict(B=2, H=5, T=64, D=64), 1),
+    ("kda_d128_dv128_B1_H24_T200", 2, 128, dict(B=1, H=24, T=200), 2),
+    # 160 chains at Dk 64: more than 128 workgroups at one tile
+    ("ckda_d64_dv64_B1_H40_T130_s0", 3, 64, dict(B=1, H=40, T=130, D=64, s0_std=0.3), 2),
+    # 288 chains at Dk 128: more than 128 workgroups at two tiles
+    ("kda_d128_dv128_B3_H12_T100", 2, 128, dict(B=3, H=12, T=100), 4),
 ]
 
 
-@pytest.mark.parametrize("name,base,dv,ov", STREAMED, ids=[c[0] for c in STREAMED])
-def test_streamed_forward(name, base, dv, ov):
+@pytest.mark.parametrize("name,base,dv,ov,tiles", STREAMED, ids=[c[0] for c in STREAMED])
+def test_streamed_forward(name, base, dv, ov, tiles):
     w, inp = _prefill(base, dv, **ov)
     say(f"[streamed] {name}: {w} Dv={dv}")
     o_ref, s_ref = run_oracle(inp)
@@ -77,9 +86,10 @@ def test_streamed_forward(name, base, dv, ov):
                       stream=cs_)
     names = _stage_names()
     gave_up, done, expect = _ctl(ws)
-    say(f"  stages {names}; gave up {gave_up}, chains {done}/{expect}")
+    say(f"  stages {names}; gave up {gave_up}, chains {done}/{expect}, tiles {_tiles(ws)}")
     assert names == ["stream_clear", "chain_stream", "prep_stream", "prep_exact", "chain"]
     assert gave_up == 0 and done == expect > 0
+    assert _tiles(ws) == tiles
     eo, es = slice_err_out(np32(out), o_ref), slice_err_state(np32(st), s_ref)
     say(f"  err out {eo:.3e} state {es:.3e}{elem_note()}")
     assert eo <= TOL[w.dtype] and es <= TOL[w.dtype]
