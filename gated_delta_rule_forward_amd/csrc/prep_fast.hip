@@ -34,8 +34,10 @@
 // Outputs go out fragment-major (kda_chunk.hpp): P and W are produced as
 // transposed tiles (P^T = Y X_P^T, W^T = X_W^T Tinv^T), whose C-layout
 // accumulators are exactly the A fragments the chain kernel consumes, so each
-// lane stores one contiguous 16-byte fragment; the thread that owns
-// (channel quad, tokens) writes its Q*Gamma and Ktil fragment slots directly.
+// lane stores one contiguous 16-byte fragment.  Q*Gamma and (without zero
+// segments) Ktil are read back from the LDS operands (q F, k G) and scaled per
+// channel, one whole fragment per lane store; with zero segments the thread
+// that owns (channel quad, tokens) writes its Ktil fragment slots directly.
 //
 // LDS is one region reused phase by phase (gate summary, A/P operands, A and
 // Tinv, X_W^T and (beta V)^T), about 52 KB for bf16 C = 64, Dk = 128 without
@@ -112,8 +114,9 @@ struct FastLayout {
         r = r > r3 ? r : r3;
         r = r > r4 ? r : r4;
         scr = (r + 15) & ~size_t(15);
-        // base [DK], misc [8], beta [C]
-        total = scr + (DK + 8 + C) * 4;
+        // base [DK] (phase variant without zero segments: cos, sin of each
+        // pair's chunk phase), misc [8], beta [C], stot E [DK]
+        total = scr + (DK + 8 + C + DK) * 4;
         total = (total + 15) & ~size_t(15);
     }
 };
@@ -160,6 +163,8 @@ __device__ __forceinline__ bool prep_fast_unit(const PrepArgs& args, const int u
     int* sBase = reinterpret_cast<int*>(lds + LY.scr);
     int* misc = sBase + DK;
     float* sBeta = reinterpret_cast<float*>(misc + 8);
+    float* sRE = sBeta + C;            // per channel: the chunk product's sign times E = 2^M (> 0)
+    float* sRot = reinterpret_cast<float*>(sBase);   // (phase, no zero segments) cos, sin per pair
 
     int tid_ = threadIdx.x;
     // (opaque per unit: in the persistent grid this keeps the compiler from
@@ -389,7 +394,13 @@ __device__ __forceinline__ bool prep_fast_unit(const PrepArgs& args, const int u
         }
     }
 
-    // ---- factored operands (LDS), Q*Gamma (staged), Ktil (direct) ---------------
+    // ---- factored operands (LDS) ------------------------------------------------
+    // (Q*Gamma, and Ktil of the channels without a zero gate in the chunk, are
+    // written from the LDS operands after the build, one whole fragment per
+    // lane store: Q*Gamma = (q F) E and Ktil^T = (k G) stot E per channel, then
+    // turned by the chunk phase.  Ktil of a channel with zero gates, and every
+    // Ktil of the phase variant with zero segments, goes out directly here.)
+    constexpr bool KT_LDS = !(ZS && PH);
     // A operand beta k F, P operand q F, shared operand k G of token j, channel x
     auto factors = [&](int j, int x, float& fa, float& fp, float& fy) {
         const float kx = kv[j].get(x);
@@ -403,7 +414,7 @@ __device__ __forceinline__ bool prep_fast_unit(const PrepArgs& args, const int u
 #pragma unroll
     for (int j = 0; j < TOK; ++j) {
         const int r = part * TOK + j;
-        float fa[4], fp[4], fy[4], fq[4], fw[4];
+        float fa[4], fp[4], fy[4], fw[4];
         int segs[4];
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
@@ -418,14 +429,12 @@ __device__ __forceinline__ bool prep_fast_unit(const PrepArgs& args, const int u
                 ge = seg == 0 ? ge : 0.f;
                 re = seg == (totPZ[x] >> 1) ? re : 0.f;
             }
-            fq[x] = fp[x] * ge;
             fw[x] = fa[x] * ge;
             kt[j][x] = fy[x] * re;
             segs[x] = seg;
         }
         xw[j] = Vec4<T>::from(fw);
         if (own) {
-            *reinterpret_cast<Vec4<T>*>(QGg + frag_off<KB>(r, c0, DK)) = Vec4<T>::from(fq);
             // main columns hold zero segment 0 only; later segments wait for
             // their extra-column pass
             if constexpr (ZS) {
@@ -444,6 +453,13 @@ __device__ __forceinline__ bool prep_fast_unit(const PrepArgs& args, const int u
             // Ktil_i = |rho(C-1, i)| R(phi_{C-1}) R(-phi_i) k_i: rotate back
 #pragma unroll
             for (int pp = 0; pp < 2; ++pp) __sincosf(totPh[pp], &se[pp], &ce[pp]);
+            if (KT_LDS && part == 0) {
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp) {
+                    sRot[c0 + 2 * pp] = ce[pp];
+                    sRot[c0 + 2 * pp + 1] = se[pp];
+                }
+            }
 #pragma unroll
             for (int j = 0; j < TOK; ++j)
 #pragma unroll
@@ -455,23 +471,33 @@ __device__ __forceinline__ bool prep_fast_unit(const PrepArgs& args, const int u
         }
         // Ktil: A operand with rows = channels, k = tokens; 4 consecutive tokens
         // starting at a multiple of 4 are 4 consecutive slots of one fragment
-        if constexpr (TOK % 4 == 0) {
+        if constexpr (!KT_LDS || ZS) {
+            bool direct[4];
 #pragma unroll
-            for (int j0 = 0; j0 < TOK; j0 += 4)
+            for (int x = 0; x < 4; ++x) direct[x] = !KT_LDS || (totPZ[x] >> 1) != 0;
+            if constexpr (TOK % 4 == 0) {
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    const float f4[4] = {kt[j0][x], kt[j0 + 1][x], kt[j0 + 2][x], kt[j0 + 3][x]};
-                    *reinterpret_cast<Vec4<T>*>(Ktg + frag_off<KB>(c0 + x, part * TOK + j0, C)) =
-                        Vec4<T>::from(f4);
-                }
-        } else {
+                for (int j0 = 0; j0 < TOK; j0 += 4)
 #pragma unroll
-            for (int j = 0; j < TOK; ++j)
+                    for (int x = 0; x < 4; ++x) {
+                        const float f4[4] = {kt[j0][x], kt[j0 + 1][x], kt[j0 + 2][x], kt[j0 + 3][x]};
+                        if (direct[x])
+                            *reinterpret_cast<Vec4<T>*>(Ktg + frag_off<KB>(c0 + x, part * TOK + j0, C)) =
+                                Vec4<T>::from(f4);
+                    }
+            } else {
 #pragma unroll
-                for (int x = 0; x < 4; ++x)
-                    Ktg[frag_off<KB>(c0 + x, part * TOK + j, C)] = from_f32<T>(kt[j][x]);
+                for (int j = 0; j < TOK; ++j)
+#pragma unroll
+                    for (int x = 0; x < 4; ++x)
+                        if (direct[x]) Ktg[frag_off<KB>(c0 + x, part * TOK + j, C)] = from_f32<T>(kt[j][x]);
+            }
         }
         if (part == 0) {
+            // (written here, past the build's register peak)
+            *reinterpret_cast<float4*>(sRE + c0) =
+                make_float4((totPZ[0] & 1) ? -E[0] : E[0], (totPZ[1] & 1) ? -E[1] : E[1],
+                            (totPZ[2] & 1) ? -E[2] : E[2], (totPZ[3] & 1) ? -E[3] : E[3]);
             float g4[4];
 #pragma unroll
             for (int x = 0; x < 4; ++x)
@@ -489,6 +515,64 @@ __device__ __forceinline__ bool prep_fast_unit(const PrepArgs& args, const int u
         }
     }
     __syncthreads();
+    // Q*Gamma (rows = tokens, k = channels) and Ktil (rows = channels, k =
+    // tokens) from the main operand columns in LDS, before the V loads and the
+    // contraction, while few registers are live: lane (m, g) of fragment
+    // (tile, k block s) holds row m's columns kcol(s, g, j), j = 0 .. NV-1, in
+    // the workspace's slot order.  (With zero segments the main columns hold
+    // segment 0 only: that is all of Q*Gamma, and all of Ktil for a channel
+    // without zeros; the other channels' Ktil went out directly.)
+    {
+        auto kcol = [&](int s, int j) {
+            if constexpr (KB == 32) return 32 * s + 16 * (j >> 2) + 4 * lg + (j & 3);
+            else return 16 * s + 4 * lg + j;
+        };
+        if (wave < NB) {
+            const T* xrow = XP + (16 * wave + ln) * KS;
+#pragma unroll
+            for (int s = 0; s < NKD; ++s) {
+                float f[NV];
+#pragma unroll
+                for (int h4 = 0; h4 < NV / 4; ++h4) {       // runs of 4 consecutive columns
+                    const int c = kcol(s, 4 * h4);
+                    const Vec4<T> xv = Vec4<T>::load(xrow + c);
+                    const float4 ev = *reinterpret_cast<const float4*>(sRE + c);
+                    f[4 * h4 + 0] = xv.get(0) * fabsf(ev.x);
+                    f[4 * h4 + 1] = xv.get(1) * fabsf(ev.y);
+                    f[4 * h4 + 2] = xv.get(2) * fabsf(ev.z);
+                    f[4 * h4 + 3] = xv.get(3) * fabsf(ev.w);
+                }
+                store_ws<NT>(QGg + ((size_t)(wave * NKD + s) * 64 + lane) * NV, F::from(f));
+            }
+        }
+        if constexpr (KT_LDS) {
+            constexpr int NKT = (DK / 16) * NKC;            // Ktil fragments
+            for (int fi = wave; fi < NKT; fi += kThreads / 64) {
+                const int ct = fi / NKC, s = fi % NKC;
+                const int c = 16 * ct + ln;
+                const float re = sRE[c];
+                if constexpr (ZS) {
+                    if ((c + 1 < DK ? sBase[c + 1] : Ztot) != sBase[c]) continue;   // zeros: direct
+                }
+                float f[NV];
+                if constexpr (PH) {
+                    // rows 2p, 2p+1 turn by the pair's chunk phase (same gate, same re)
+                    const int c2 = c & ~1;
+                    const float cs = sRot[c2], sn = sRot[c2 + 1];
+#pragma unroll
+                    for (int j = 0; j < NV; ++j) {
+                        const float y0 = to_f32(Y[kcol(s, j) * KS + c2]);
+                        const float y1 = to_f32(Y[kcol(s, j) * KS + c2 + 1]);
+                        f[j] = re * ((c & 1) ? sn * y0 + cs * y1 : cs * y0 - sn * y1);
+                    }
+                } else {
+#pragma unroll
+                    for (int j = 0; j < NV; ++j) f[j] = to_f32(Y[kcol(s, j) * KS + c]) * re;
+                }
+                store_ws<NT>(Ktg + ((size_t)(ct * NKC + s) * 64 + lane) * NV, F::from(f));
+            }
+        }
+    }
     // V tile loads: in flight during the A / P tiles and Tinv
     // item (column quad vq, token run tg): 4 columns x TV tokens, stored later
     // as 4 rows of (beta V)^T; rows past the end re-read the last valid row
