@@ -183,6 +183,21 @@ Parts parts_for(int B, int H, int Dk, int Dv, int NC)
     return {(NC + len - 1) / len, len};
 }
 
+// Streamed forward: the prep's lead limit.  Left alone, the prep grid runs
+// far ahead of the chain on long sequences, and the factors of the chunks in
+// between (72.5 KB per unit at bf16, Dk = Dv = 128) no longer fit the
+// caches by the time the chain reads them; the limit keeps about 64 MiB of
+// units between the two, a quarter of the MI355X's 256 MB last-level cache
+// (at H = 16, T = 65536: 56 chunks, 1.80 -> 1.66 ms per call; 8 chunks starve
+// the chain, 2.6 ms).
+constexpr size_t kStreamLeadBytes = (size_t)64 << 20;
+static int stream_lead(long long bhn, int Dk, int Dv, int chunk, size_t e)
+{
+    const size_t unit = (size_t)chunk * (3 * (size_t)Dk + Dv + chunk) * e + (size_t)Dk * 4;
+    const size_t l = kStreamLeadBytes / ((size_t)bhn * unit);
+    return (int)(l < 16 ? 16 : (l > (1u << 20) ? (1u << 20) : l));
+}
+
 // Streamed forward (kda_chunk_forward_side with KDA_FLAG_STREAMED): the chunk
 // factors are formed by a prep grid on the side stream while the chain
 // consumes them on the caller's stream, unit by unit, through the L2 of the
@@ -464,6 +479,7 @@ kda_status_t chunk_forward(const void* q, const void* k, const void* v, const fl
         ps.nbh = (int)bhn;
         ps.ready = ready;
         ps.sctl = ctl;
+        ps.lead = stream_lead(bhn, Dk, Dv, chunk, 2);
         kda::ChainArgs cst = ca;
         cst.ready = ready;
         cst.sctl = ctl;

@@ -227,6 +227,10 @@ struct PrepArgs {
     int nbh;
     unsigned* ready;
     StreamCtl* sctl;
+    // streamed forward: a unit of chunk n >= lead first waits (a bounded,
+    // advisory wait) until the chain of its (b, h) has taken chunk n - lead;
+    // 0: no wait
+    int lead;
 };
 
 // unit of launch index v when a launch covers chunks [pc0, pc0 + pcn) of every
@@ -301,11 +305,11 @@ struct ChainArgs {
     // state leaving the range; may be S0: each workgroup reads its slice of S0
     // before it writes that slice of ST)
     int pc0, pcn;
-    // streamed forward: the ready words and control words the chain waits on
-    // (streamed kernel), or (gate) the control words that decide whether this
-    // launch runs at all: only when the streamed chain gave up or did not
-    // cover every (b, h)
-    const unsigned* ready;
+    // streamed forward: the ready words (the chain marks each unit it takes)
+    // and control words the chain waits on (streamed kernel), or (gate) the
+    // control words that decide whether this launch runs at all: only when
+    // the streamed chain gave up or did not cover every (b, h)
+    unsigned* ready;
     StreamCtl* sctl;
     const StreamCtl* gate;
 };
@@ -319,16 +323,26 @@ struct ChainArgs {
 // the prep grid cannot start before the chain ends.)
 constexpr unsigned long long kStreamWaitTicks = 1000000ull;
 constexpr unsigned kStreamWaitPolls = 1u << 18;
+// The prep's lead wait (advisory: past its bound the unit goes ahead): 1 ms,
+// and a poll cap likewise
+constexpr unsigned long long kLeadWaitTicks = 100000ull;
+constexpr unsigned kLeadWaitPolls = 1u << 15;
 
 // Wait until unit u's ready word reads 1 (its factors are in the workspace,
 // written from this XCD).  Gives up, raising the abort word, when the unit
 // needs the exact kernel (2), when another workgroup gave up, or when the
 // bound expires.  `first` is a value of the ready word read earlier.  Every
 // lane of the wavefront takes part and gets the same answer.
-__device__ inline bool stream_wait_ready(const unsigned* ready, StreamCtl* ctl, size_t u,
+__device__ inline bool stream_wait_ready(unsigned* ready, StreamCtl* ctl, size_t u,
                                          unsigned first)
 {
-    if (first == 1u) return true;
+    // ready: 1, or 3 once a chain workgroup of the (b, h) has taken the unit
+    // (the prep's lead limit reads that mark); 2: the exact kernel's unit
+    if (first == 3u) return true;
+    if (first == 1u) {
+        __hip_atomic_store(&ready[u], 3u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return true;
+    }
     unsigned r = first;
     const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
     for (unsigned n = 0;; ++n) {
@@ -338,7 +352,11 @@ __device__ inline bool stream_wait_ready(const unsigned* ready, StreamCtl* ctl, 
             break;
         __builtin_amdgcn_s_sleep(2);
         r = __hip_atomic_load(&ready[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (r == 1u) return true;
+        if (r == 3u) return true;
+        if (r == 1u) {
+            __hip_atomic_store(&ready[u], 3u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return true;
+        }
     }
     __hip_atomic_store(&ctl->abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return false;

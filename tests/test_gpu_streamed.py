@@ -12,6 +12,8 @@ White-box: the last 384 bytes of the workspace are the control words of the
 streamed call, as 32-bit words: prep counters [0:8], chain counters [32:40],
 chains done [40], chains expected [41], column tiles per chain workgroup
 [42], give-up word [64]; the tests read them to see which way the call went.
+Before them lie the units' ready words, padded to 256 bytes (3 once a chain
+workgroup took the unit: the prep grid keeps a bounded lead over that mark).
 
 Checks: the oracle's recurrence across column-tile widths (Dv 128, 96, 48 at
 Dk 128; 64, 48 at Dk 64), ragged tails, initial states, both modes and
@@ -44,6 +46,14 @@ def _ctl(ws):
 def _tiles(ws):
     """Column tiles per chain workgroup the call chose."""
     return int(ws[-384:].cpu().view(torch.int32)[42])
+
+
+def _ready(ws, nu):
+    """The units' ready words (a 256-byte padded block just before the control
+    words): 1 formed, 2 for the exact kernel, 3 formed and taken by a chain
+    workgroup."""
+    start = ws.numel() - 384 - ((4 * nu + 255) // 256) * 256
+    return ws[start:start + 4 * nu].cpu().view(torch.int32)
 
 
 def _prefill(base, dv, **ov):
@@ -90,6 +100,8 @@ def test_streamed_forward(name, base, dv, ov, tiles):
     assert names == ["stream_clear", "chain_stream", "prep_stream", "prep_exact", "chain"]
     assert gave_up == 0 and done == expect > 0
     assert _tiles(ws) == tiles
+    # every unit was taken by the chain (the mark the prep's lead limit reads)
+    assert bool((_ready(ws, w.B * w.H * -(-w.T // 64)) == 3).all())
     eo, es = slice_err_out(np32(out), o_ref), slice_err_state(np32(st), s_ref)
     say(f"  err out {eo:.3e} state {es:.3e}{elem_note()}")
     assert eo <= TOL[w.dtype] and es <= TOL[w.dtype]
@@ -129,6 +141,7 @@ def test_streamed_flagged_chunks_give_up():
     gave_up, done, expect = _ctl(ws)
     say(f"  gave up {gave_up}, chains {done}/{expect}")
     assert gave_up == 1
+    assert int((_ready(ws, w.B * w.H * -(-w.T // 64)) == 2).sum()) == 2   # the two flagged units
     eo, es = slice_err_out(np32(out), o_ref), slice_err_state(np32(st), s_ref)
     say(f"  err out {eo:.3e} state {es:.3e}{elem_note()}")
     assert eo <= TOL[w.dtype] and es <= TOL[w.dtype]
