@@ -438,7 +438,12 @@ struct LocalGeom {
     static constexpr int LDT = C + 4;          // row stride of the [C][C] fp32 arrays
     static constexpr size_t al16(size_t x) { return (x + 15) & ~size_t(15); }
     // R0: Tinv (y phase), then B1, B3
-    static constexpr size_t B1 = 0, B3 = B1 + 4 * (size_t)C * LDT, R0 = B3 + 4 * (size_t)C * LDT;
+    // (after the final phase's reads of B1 and B3, the region holds dalpha
+    // [C][DKA] fp32 for the coalesced write-out)
+    static constexpr int DKA = DK + 4;
+    static constexpr size_t DAB = 4 * (size_t)C * DKA;
+    static constexpr size_t B1 = 0, B3 = B1 + 4 * (size_t)C * LDT,
+                            R0 = al16(B3 + 4 * (size_t)C * LDT > DAB ? B3 + 4 * (size_t)C * LDT : DAB);
     static constexpr size_t TI = 0;
     // R1, GEMM phase: dO, Delta, Y
     static constexpr size_t DO = R0, DL = DO + 4 * (size_t)C * LDV, YY = DL + 4 * (size_t)C * LDV;
@@ -447,9 +452,14 @@ struct LocalGeom {
     // (fp32 [NDR][DKP]: k, q or beta k decayed to the 16-token block edges)
     // and the per-channel block-edge products GB (Gamma_{16 b - 1}) and GE
     // (rho(C - 1, 16 b + 15)), [NM][DK] each
+    // (row strides padded by 16 bytes: the final phase's lanes read one
+    // channel from rows 4 apart, which would otherwise share banks)
     static constexpr int NDR = 8 * NM * (NM - 1), DKP = DK + 4;
-    static constexpr size_t AL = R0, KK = AL + 4 * (size_t)C * DK, QQ = al16(KK + sizeof(T) * C * DK);
-    static constexpr size_t DEC = al16(QQ + sizeof(T) * C * DK), GB = DEC + 4 * (size_t)NDR * DKP;
+    static constexpr int DKT = DK + 16 / (int)sizeof(T);
+    static constexpr size_t AL = R0, KK = AL + 4 * (size_t)C * DKA, QQ = al16(KK + sizeof(T) * C * DKT);
+    // DEC: the decayed operands, then (final phase) dq and dk [C][DKT] io type
+    static constexpr size_t DECB = 4 * (size_t)NDR * DKP, DQB = 2 * sizeof(T) * (size_t)C * DKT;
+    static constexpr size_t DEC = al16(QQ + sizeof(T) * C * DKT), GB = DEC + al16(DECB > DQB ? DECB : DQB);
     static constexpr size_t GE = GB + 4 * (size_t)NM * DK;
     static constexpr size_t R1B = GE + 4 * (size_t)NM * DK;
     // small arrays
@@ -459,6 +469,7 @@ struct LocalGeom {
     static constexpr size_t BYTES = DBV + 4 * (size_t)kLocalWaves * C;
     static_assert(BYTES <= 160 * 1024, "LDS");
     static_assert(CTW == 1, "one channel tile per wavefront");
+    static_assert((NM - 1) * DK <= kLocalThreads, "one thread per (channel, block)");
 };
 
 template <typename T, int C, int DK>
@@ -482,6 +493,7 @@ __global__ __launch_bounds__(kLocalThreads) void bwd_local_kernel(BwdLocalArgs a
     float* sDBw = reinterpret_cast<float*>(lds + G::DBW);     // [waves][C]
     float* sDBv = reinterpret_cast<float*>(lds + G::DBV);     // [waves][C]: v . y partials
     constexpr int LDV = G::LDV, LDT = G::LDT, NM = G::NM, NW = kLocalWaves, NTH = kLocalThreads;
+    constexpr int DKA = G::DKA, DKT = G::DKT;
 
     const int Dv = a.Dv, H = a.H, NVT = Dv / 16;
     const size_t unit = blockIdx.x;
@@ -615,15 +627,32 @@ __global__ __launch_bounds__(kLocalThreads) void bwd_local_kernel(BwdLocalArgs a
                 const int r = 16 * mt + 4 * lg + i, c = 16 * vt + ln;
                 const float yv = yt[jj][i];
                 sY[r * LDV + c] = yv;
-                if (r < nvalid) dv[tok(r) * Dv + c] = from_f32<T>(sBeta[r] * yv);
                 const float vy = row16_sum(r < nvalid ? vv[jj][i] * yv : 0.f);
                 if (ln == 0) sDBv[wave * C + r] += vy;
             }
         }
     }
     __syncthreads();
+    // dv = diag(beta) y, written as whole 16-byte row pieces
+    {
+        constexpr int VQ = 16 / (int)sizeof(T);
+        const int NQV = Dv / VQ;
+        for (int idx = tid; idx < C * NQV; idx += NTH) {
+            const int r = idx / NQV, cq = VQ * (idx % NQV);
+            if (r < nvalid) {
+                const float br = sBeta[r];
+                __attribute__((aligned(16))) T o[VQ];
+#pragma unroll
+                for (int x = 0; x < VQ; ++x) o[x] = from_f32<T>(br * sY[r * LDV + cq + x]);
+                *reinterpret_cast<uint4*>(dv + tok(r) * Dv + cq) = *reinterpret_cast<const uint4*>(o);
+            }
+        }
+    }
 
     // ---- B1 = dO Delta^T (i <= r), B3 = Y Delta^T (i < r): lower tiles --------------
+    // (each strictly lower element also goes to its mirror place, which nothing
+    // else uses: the final phase reads B[r0 .. r0 + 3][i] as one 16-byte row
+    // piece B^T[i][r0 .. r0 + 3])
     {
         constexpr int NP = NM * (NM + 1) / 2;
         for (int job = wave; job < 2 * NP; job += NW) {
@@ -637,7 +666,12 @@ __global__ __launch_bounds__(kLocalThreads) void bwd_local_kernel(BwdLocalArgs a
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * mt + 4 * lg + i, ic = 16 * it + ln;
-                dst[r * LDT + ic] = (which == 0 ? ic <= r : ic < r) ? acc[i] : 0.f;
+                if (ic < r) {
+                    dst[r * LDT + ic] = acc[i];
+                    dst[ic * LDT + r] = acc[i];
+                } else if (ic == r) {
+                    dst[r * LDT + r] = which == 0 ? acc[i] : 0.f;
+                }
             }
         }
     }
@@ -707,9 +741,9 @@ __global__ __launch_bounds__(kLocalThreads) void bwd_local_kernel(BwdLocalArgs a
             if (idx >= C * DK / 4) break;
             const int r = idx / (DK / 4), c4 = 4 * (idx % (DK / 4));
             const bool ok = r < nvalid;
-            *reinterpret_cast<float4*>(sAl + r * DK + c4) = ok ? wal[x] : make_float4(1.f, 1.f, 1.f, 1.f);
-            *reinterpret_cast<Vec4<T>*>(sK + r * DK + c4) = ok ? wk4[x] : Vec4<T>::zero();
-            *reinterpret_cast<Vec4<T>*>(sQ + r * DK + c4) = ok ? wq4[x] : Vec4<T>::zero();
+            *reinterpret_cast<float4*>(sAl + r * DKA + c4) = ok ? wal[x] : make_float4(1.f, 1.f, 1.f, 1.f);
+            *reinterpret_cast<Vec4<T>*>(sK + r * DKT + c4) = ok ? wk4[x] : Vec4<T>::zero();
+            *reinterpret_cast<Vec4<T>*>(sQ + r * DKT + c4) = ok ? wq4[x] : Vec4<T>::zero();
         }
     }
     __syncthreads();
@@ -731,28 +765,28 @@ __global__ __launch_bounds__(kLocalThreads) void bwd_local_kernel(BwdLocalArgs a
     // k decayed forward to each block edge; Gamma at the block edges
     // (each 16-token piece of the channel is read into registers before any
     // of its results is written, so the reads are issued together)
+    // (one thread per (channel, block b): a channel's chains run side by side)
     if (tid < DK) {
-        const int c = tid;
-        sGB[c] = 1.f;
+        sGB[tid] = 1.f;
+        sGE[(NM - 1) * DK + tid] = 1.f;
+    }
+    if (tid < (NM - 1) * DK) {
+        const int c = tid % DK, b = 1 + tid / DK;
+        float w = 1.f;
+        for (int blk = b - 1; blk >= 0; --blk) {
+            float av[16], kv[16];
 #pragma unroll
-        for (int b = 1; b < NM; ++b) {
-            float w = 1.f;
-#pragma unroll
-            for (int blk = b - 1; blk >= 0; --blk) {
-                float av[16], kv[16];
-#pragma unroll
-                for (int x = 0; x < 16; ++x) {
-                    av[x] = sAl[(16 * blk + x) * DK + c];
-                    kv[x] = to_f32(sK[(16 * blk + x) * DK + c]);
-                }
-#pragma unroll
-                for (int x = 15; x >= 0; --x) {
-                    sDec[(offL(b) + 16 * blk + x) * DKP + c] = kv[x] * w;
-                    w *= av[x];
-                }
+            for (int x = 0; x < 16; ++x) {
+                av[x] = sAl[(16 * blk + x) * DKA + c];
+                kv[x] = to_f32(sK[(16 * blk + x) * DKT + c]);
             }
-            sGB[b * DK + c] = w;
+#pragma unroll
+            for (int x = 15; x >= 0; --x) {
+                sDec[(offL(b) + 16 * blk + x) * DKP + c] = kv[x] * w;
+                w *= av[x];
+            }
         }
+        sGB[b * DK + c] = w;
     }
     __syncthreads();
     if (ctw < G::NCT) {
@@ -768,28 +802,23 @@ __global__ __launch_bounds__(kLocalThreads) void bwd_local_kernel(BwdLocalArgs a
     }
     __syncthreads();
     // q decayed backward to each block's end; rho(C - 1, block end)
-    if (tid < DK) {
-        const int c = tid;
-        sGE[(NM - 1) * DK + c] = 1.f;
+    if (tid < (NM - 1) * DK) {
+        const int c = tid % DK, b = tid / DK;
+        float w = 1.f;
+        for (int blk = b + 1; blk < NM; ++blk) {
+            float av[16], qv[16];
 #pragma unroll
-        for (int b = 0; b + 1 < NM; ++b) {
-            float w = 1.f;
-#pragma unroll
-            for (int blk = b + 1; blk < NM; ++blk) {
-                float av[16], qv[16];
-#pragma unroll
-                for (int x = 0; x < 16; ++x) {
-                    av[x] = sAl[(16 * blk + x) * DK + c];
-                    qv[x] = to_f32(sQ[(16 * blk + x) * DK + c]);
-                }
-#pragma unroll
-                for (int x = 0; x < 16; ++x) {
-                    w *= av[x];
-                    sDec[(offU(b) + 16 * (blk - b - 1) + x) * DKP + c] = qv[x] * w;
-                }
+            for (int x = 0; x < 16; ++x) {
+                av[x] = sAl[(16 * blk + x) * DKA + c];
+                qv[x] = to_f32(sQ[(16 * blk + x) * DKT + c]);
             }
-            sGE[b * DK + c] = w;
+#pragma unroll
+            for (int x = 0; x < 16; ++x) {
+                w *= av[x];
+                sDec[(offU(b) + 16 * (blk - b - 1) + x) * DKP + c] = qv[x] * w;
+            }
         }
+        sGE[b * DK + c] = w;
     }
     __syncthreads();
     if (ctw < G::NCT) {
@@ -804,24 +833,20 @@ __global__ __launch_bounds__(kLocalThreads) void bwd_local_kernel(BwdLocalArgs a
     }
     __syncthreads();
     // beta k decayed backward to each block's end
-    if (tid < DK) {
-        const int c = tid;
+    if (tid < (NM - 1) * DK) {
+        const int c = tid % DK, b = tid / DK;
+        float w = 1.f;
+        for (int blk = b + 1; blk < NM; ++blk) {
+            float av[16], kv[16];
 #pragma unroll
-        for (int b = 0; b + 1 < NM; ++b) {
-            float w = 1.f;
+            for (int x = 0; x < 16; ++x) {
+                av[x] = sAl[(16 * blk + x) * DKA + c];
+                kv[x] = sBeta[16 * blk + x] * to_f32(sK[(16 * blk + x) * DKT + c]);
+            }
 #pragma unroll
-            for (int blk = b + 1; blk < NM; ++blk) {
-                float av[16], kv[16];
-#pragma unroll
-                for (int x = 0; x < 16; ++x) {
-                    av[x] = sAl[(16 * blk + x) * DK + c];
-                    kv[x] = sBeta[16 * blk + x] * to_f32(sK[(16 * blk + x) * DK + c]);
-                }
-#pragma unroll
-                for (int x = 0; x < 16; ++x) {
-                    w *= av[x];
-                    sDec[(offU(b) + 16 * (blk - b - 1) + x) * DKP + c] = kv[x] * w;
-                }
+            for (int x = 0; x < 16; ++x) {
+                w *= av[x];
+                sDec[(offU(b) + 16 * (blk - b - 1) + x) * DKP + c] = kv[x] * w;
             }
         }
     }
@@ -837,6 +862,7 @@ __global__ __launch_bounds__(kLocalThreads) void bwd_local_kernel(BwdLocalArgs a
         }
     }
 
+    __syncthreads();   // the decayed operands are read: their region takes dq, dk
     float dbp[NM][4];
 #pragma unroll
     for (int mt = 0; mt < NM; ++mt)
@@ -844,164 +870,170 @@ __global__ __launch_bounds__(kLocalThreads) void bwd_local_kernel(BwdLocalArgs a
         for (int m = 0; m < 4; ++m) dbp[mt][m] = 0.f;
     T* dqg = static_cast<T*>(a.dq);
     T* dkg = static_cast<T*>(a.dk);
-#pragma unroll
-    for (int cw = 0; cw < G::CTW; ++cw) {
-        const int ct = wave + NW * cw;
-        if (ct >= G::NCT) continue;
-        const int c = 16 * ct + ln;
-        auto al = [&](int t) { return sAl[t * DK + c]; };
-        auto kf = [&](int t) { return to_f32(sK[t * DK + c]); };
-        auto qf = [&](int t) { return to_f32(sQ[t * DK + c]); };
+    // dq, dk and dalpha are staged in LDS (dq, dk where the decayed operands
+    // were; dalpha where B1, B3 were, once every wave has read them) and
+    // written out at the end as whole 16-byte row pieces
+    T* sDQ = reinterpret_cast<T*>(lds + G::DEC);
+    T* sDK = sDQ + C * DKT;
+    float* sDA = reinterpret_cast<float*>(lds + G::B1);
+    {
+        constexpr int cw = 0;                  // (one channel tile per wavefront)
+        const int ct = wave;
+        const bool act = ct < G::NCT;
+        const int c = 16 * (act ? ct : G::NCT - 1) + ln;
+        auto al = [&](int t) { return sAl[t * DKA + c]; };
+        auto kf = [&](int t) { return to_f32(sK[t * DKT + c]); };
+        auto qf = [&](int t) { return to_f32(sQ[t * DKT + c]); };
         float Za[NM][4], Zb[NM][4];
         float gcl = 1.f;                   // Gamma of the lane's last row (row C - 1 in lanes lg = 3)
+        if (act) {
 #pragma unroll
-        for (int mt = 0; mt < NM; ++mt) {
-            const int r0 = 16 * mt + 4 * lg, r3 = r0 + 3;
-            // L sums inside block mt (16 mt <= i < r0) with w = rho(r0, i), then
-            // the block product (rho(r0, 16 mt - 1) = w alpha_{16 mt}) and
-            // rho(r0 + m, r0); Gamma_{r0+m} = GB rho(r0, 16 mt - 1) rho(r0 + m, r0)
-            float lq[4] = {0.f, 0.f, 0.f, 0.f}, lk[4] = {0.f, 0.f, 0.f, 0.f};
-            float fL[4] = {1.f, 1.f, 1.f, 1.f}, wL = 1.f;
-            {
-                for (int i = r0 - 1; i >= 16 * mt; --i) {
-                    wL *= al(i + 1);
-                    const float wk = wL * kf(i);
+            for (int mt = 0; mt < NM; ++mt) {
+                const int r0 = 16 * mt + 4 * lg, r3 = r0 + 3;
+                // L sums inside block mt (16 mt <= i < r0) with w = rho(r0, i), then
+                // the block product (rho(r0, 16 mt - 1) = w alpha_{16 mt}) and
+                // rho(r0 + m, r0); Gamma_{r0+m} = GB rho(r0, 16 mt - 1) rho(r0 + m, r0)
+                float lq[4] = {0.f, 0.f, 0.f, 0.f}, lk[4] = {0.f, 0.f, 0.f, 0.f};
+                float fL[4] = {1.f, 1.f, 1.f, 1.f}, wL = 1.f;
+                {
+                    for (int i = r0 - 1; i >= 16 * mt; --i) {
+                        wL *= al(i + 1);
+                        const float wk = wL * kf(i);
+                        const float4 b1 = *reinterpret_cast<const float4*>(sB1 + i * LDT + r0);   // B1[r0 + m][i]
+                        const float4 b3 = *reinterpret_cast<const float4*>(sB3 + i * LDT + r0);
+                        lq[0] += b1.x * wk; lq[1] += b1.y * wk; lq[2] += b1.z * wk; lq[3] += b1.w * wk;
+                        lk[0] += b3.x * wk; lk[1] += b3.y * wk; lk[2] += b3.z * wk; lk[3] += b3.w * wk;
+                    }
+                    const float pe = wL * al(16 * mt);          // rho(r0, 16 mt - 1)
+                    wL = pe;
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
-                        lq[m] += sB1[(r0 + m) * LDT + i] * wk;
-                        lk[m] += sB3[(r0 + m) * LDT + i] * wk;
+                        lq[m] += pe * mL1[mt][m];
+                        lk[m] += pe * mL3[mt][m];
+                    }
+                    float f = 1.f;
+#pragma unroll
+                    for (int m = 1; m < 4; ++m) {
+                        f *= al(r0 + m);
+                        fL[m] = f;
+                        lq[m] *= f;
+                        lk[m] *= f;
+                        // pairs inside the group: r0 <= i < r0 + m
+                        float wi = 1.f;
+#pragma unroll
+                        for (int d = 1; d <= m; ++d) {
+                            const int i = r0 + m - d;
+                            wi *= al(i + 1);
+                            const float wk = wi * kf(i);
+                            lq[m] += sB1[i * LDT + r0 + m] * wk;
+                            lk[m] += sB3[i * LDT + r0 + m] * wk;
+                        }
                     }
                 }
-                const float pe = wL * al(16 * mt);          // rho(r0, 16 mt - 1)
-                wL = pe;
+                // U sums inside block mt (r3 < j <= 16 mt + 15) with w = rho(j, r3),
+                // then the block product (w = rho(16 mt + 15, r3)) and rho(r3, r0 + m);
+                // rho(C - 1, r0 + m) = GE w rho(r3, r0 + m)
+                float uq[4] = {0.f, 0.f, 0.f, 0.f}, uk[4] = {0.f, 0.f, 0.f, 0.f};
+                float hU[4] = {1.f, 1.f, 1.f, 1.f}, wU = 1.f;
+                {
+                    for (int j = r3 + 1; j <= 16 * mt + 15; ++j) {
+                        wU *= al(j);
+                        const float wq = wU * qf(j), wk = wU * sBeta[j] * kf(j);
+                        const float4 b1 = *reinterpret_cast<const float4*>(sB1 + j * LDT + r0);
+                        const float4 b3 = *reinterpret_cast<const float4*>(sB3 + j * LDT + r0);
+                        uq[0] += b1.x * wq; uq[1] += b1.y * wq; uq[2] += b1.z * wq; uq[3] += b1.w * wq;
+                        uk[0] += b3.x * wk; uk[1] += b3.y * wk; uk[2] += b3.z * wk; uk[3] += b3.w * wk;
+                    }
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        uq[m] += wU * mU1[mt][m];
+                        uk[m] += wU * mU2[mt][m];
+                    }
+                    float f = 1.f;
+#pragma unroll
+                    for (int m = 2; m >= 0; --m) {
+                        f *= al(r0 + m + 1);
+                        hU[m] = f;
+                        uq[m] *= f;
+                        uk[m] *= f;
+                        // pairs inside the group: r0 + m < j <= r3
+                        float wj = 1.f;
+#pragma unroll
+                        for (int j = r0 + m + 1; j <= r3; ++j) {
+                            wj *= al(j);
+                            uq[m] += sB1[j * LDT + r0 + m] * wj * qf(j);
+                            uk[m] += sB3[j * LDT + r0 + m] * wj * sBeta[j] * kf(j);
+                        }
+                    }
+                }
+                const float gbm = sGB[mt * DK + c], gem = sGE[mt * DK + c];
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    lq[m] += pe * mL1[mt][m];
-                    lk[m] += pe * mL3[mt][m];
-                }
-                float f = 1.f;
-#pragma unroll
-                for (int m = 1; m < 4; ++m) {
-                    f *= al(r0 + m);
-                    fL[m] = f;
-                    lq[m] *= f;
-                    lk[m] *= f;
-                    // pairs inside the group: r0 <= i < r0 + m
-                    float wi = 1.f;
-#pragma unroll
-                    for (int d = 1; d <= m; ++d) {
-                        const int i = r0 + m - d;
-                        wi *= al(i + 1);
-                        const float wk = wi * kf(i);
-                        lq[m] += sB1[(r0 + m) * LDT + i] * wk;
-                        lk[m] += sB3[(r0 + m) * LDT + i] * wk;
-                    }
-                }
-            }
-            // U sums inside block mt (r3 < j <= 16 mt + 15) with w = rho(j, r3),
-            // then the block product (w = rho(16 mt + 15, r3)) and rho(r3, r0 + m);
-            // rho(C - 1, r0 + m) = GE w rho(r3, r0 + m)
-            float uq[4] = {0.f, 0.f, 0.f, 0.f}, uk[4] = {0.f, 0.f, 0.f, 0.f};
-            float hU[4] = {1.f, 1.f, 1.f, 1.f}, wU = 1.f;
-            {
-                for (int j = r3 + 1; j <= 16 * mt + 15; ++j) {
-                    wU *= al(j);
-                    const float wq = wU * qf(j), wk = wU * sBeta[j] * kf(j);
-                    const float4 b1 = *reinterpret_cast<const float4*>(sB1 + j * LDT + r0);
-                    const float4 b3 = *reinterpret_cast<const float4*>(sB3 + j * LDT + r0);
-                    uq[0] += b1.x * wq; uq[1] += b1.y * wq; uq[2] += b1.z * wq; uq[3] += b1.w * wq;
-                    uk[0] += b3.x * wk; uk[1] += b3.y * wk; uk[2] += b3.z * wk; uk[3] += b3.w * wk;
-                }
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    uq[m] += wU * mU1[mt][m];
-                    uk[m] += wU * mU2[mt][m];
-                }
-                float f = 1.f;
-#pragma unroll
-                for (int m = 2; m >= 0; --m) {
-                    f *= al(r0 + m + 1);
-                    hU[m] = f;
-                    uq[m] *= f;
-                    uk[m] *= f;
-                    // pairs inside the group: r0 + m < j <= r3
-                    float wj = 1.f;
-#pragma unroll
-                    for (int j = r0 + m + 1; j <= r3; ++j) {
-                        wj *= al(j);
-                        uq[m] += sB1[j * LDT + r0 + m] * wj * qf(j);
-                        uk[m] += sB3[j * LDT + r0 + m] * wj * sBeta[j] * kf(j);
-                    }
-                }
-            }
-            const float gbm = sGB[mt * DK + c], gem = sGE[mt * DK + c];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int r = r0 + m;
-                const float kr = kf(r), qr = qf(r), br = sBeta[r];
-                const float b1d = sB1[r * LDT + r];
-                const float g = gbm * wL * fL[m], ge = gem * wU * hU[m];
-                const float f1 = F1[cw][mt][m], f2 = F2[cw][mt][m], f3 = F3[cw][mt][m];
-                const float dqv = g * f1 + lq[m] + b1d * kr;
-                const float dkv = ge * f3 + uq[m] + b1d * qr - uk[m] - br * (g * f2 + lk[m]);
-                dbp[mt][m] -= kr * (g * f2 + lk[m]);
-                Za[mt][m] = ge * kr * f3;
-                Zb[mt][m] = g * (qr * f1 - br * kr * f2) + qr * lq[m] - br * kr * lk[m] - kr * (uq[m] - uk[m]);
-                if (m == 3) gcl = g;
-                if (r < nvalid) {
-                    dqg[tok(r) * DK + c] = from_f32<T>(dqv);
-                    dkg[tok(r) * DK + c] = from_f32<T>(dkv);
+                    const int r = r0 + m;
+                    const float kr = kf(r), qr = qf(r), br = sBeta[r];
+                    const float b1d = sB1[r * LDT + r];
+                    const float g = gbm * wL * fL[m], ge = gem * wU * hU[m];
+                    const float f1 = F1[cw][mt][m], f2 = F2[cw][mt][m], f3 = F3[cw][mt][m];
+                    const float dqv = g * f1 + lq[m] + b1d * kr;
+                    const float dkv = ge * f3 + uq[m] + b1d * qr - uk[m] - br * (g * f2 + lk[m]);
+                    dbp[mt][m] -= kr * (g * f2 + lk[m]);
+                    Za[mt][m] = ge * kr * f3;
+                    Zb[mt][m] = g * (qr * f1 - br * kr * f2) + qr * lq[m] - br * kr * lk[m] - kr * (uq[m] - uk[m]);
+                    if (m == 3) gcl = g;
+                    sDQ[r * DKT + c] = from_f32<T>(dqv);
+                    sDK[r * DKT + c] = from_f32<T>(dkv);
                 }
             }
         }
-        // alpha_r dalpha_r = Gamma_{C-1} sigma + (sum of Za over rows before r)
-        // + (sum of Zb over rows from r on); the channel's rows are the lanes
-        // ln + 16 j, j = 0..3 (row 16 mt + 4 j + m).  Za is replaced by its
-        // exclusive prefix, then the suffix of Zb completes dalpha.
-        const float gcs = __shfl(gcl, ln + 48) * sigv[cw];
-        float run = 0.f;
+        __syncthreads();   // every read of B1 and B3 is done: the region takes dalpha
+        if (act) {
+            // alpha_r dalpha_r = Gamma_{C-1} sigma + (sum of Za over rows before r)
+            // + (sum of Zb over rows from r on); the channel's rows are the lanes
+            // ln + 16 j, j = 0..3 (row 16 mt + 4 j + m).  Za is replaced by its
+            // exclusive prefix, then the suffix of Zb completes dalpha.
+            const float gcs = __shfl(gcl, ln + 48) * sigv[cw];
+            float run = 0.f;
 #pragma unroll
-        for (int mt = 0; mt < NM; ++mt) {
-            const float sa = (Za[mt][0] + Za[mt][1]) + (Za[mt][2] + Za[mt][3]);
-            float tot = 0.f, before = 0.f;
+            for (int mt = 0; mt < NM; ++mt) {
+                const float sa = (Za[mt][0] + Za[mt][1]) + (Za[mt][2] + Za[mt][3]);
+                float tot = 0.f, before = 0.f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float x = __shfl(sa, ln + 16 * j);
-                tot += x;
-                before += j < lg ? x : 0.f;
+                for (int j = 0; j < 4; ++j) {
+                    const float x = __shfl(sa, ln + 16 * j);
+                    tot += x;
+                    before += j < lg ? x : 0.f;
+                }
+                float in = run + before;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const float z = Za[mt][m];
+                    Za[mt][m] = in;
+                    in += z;
+                }
+                run += tot;
             }
-            float in = run + before;
+            run = 0.f;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const float z = Za[mt][m];
-                Za[mt][m] = in;
-                in += z;
-            }
-            run += tot;
-        }
-        run = 0.f;
+            for (int mt = NM - 1; mt >= 0; --mt) {
+                const float sb = (Zb[mt][0] + Zb[mt][1]) + (Zb[mt][2] + Zb[mt][3]);
+                float tot = 0.f, after = 0.f;
 #pragma unroll
-        for (int mt = NM - 1; mt >= 0; --mt) {
-            const float sb = (Zb[mt][0] + Zb[mt][1]) + (Zb[mt][2] + Zb[mt][3]);
-            float tot = 0.f, after = 0.f;
+                for (int j = 0; j < 4; ++j) {
+                    const float x = __shfl(sb, ln + 16 * j);
+                    tot += x;
+                    after += j > lg ? x : 0.f;
+                }
+                float in = run + after;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float x = __shfl(sb, ln + 16 * j);
-                tot += x;
-                after += j > lg ? x : 0.f;
-            }
-            float in = run + after;
-#pragma unroll
-            for (int m = 3; m >= 0; --m) {
-                in += Zb[mt][m];
-                const int r = 16 * mt + 4 * lg + m;
-                if (r < nvalid) {
+                for (int m = 3; m >= 0; --m) {
+                    in += Zb[mt][m];
+                    const int r = 16 * mt + 4 * lg + m;
                     const float av = al(r);
                     const float z = gcs + Za[mt][m] + in;
-                    a.dalpha[tok(r) * DK + c] = fabsf(av) >= kTinyGate ? z / av : 0.f;
+                    sDA[r * DKA + c] = fabsf(av) >= kTinyGate ? z / av : 0.f;
                 }
+                run += tot;
             }
-            run += tot;
         }
     }
     // dbeta: sum over the lane's channels, then over the 16 lanes of a row
@@ -1015,6 +1047,21 @@ __global__ __launch_bounds__(kLocalThreads) void bwd_local_kernel(BwdLocalArgs a
             if (ln == 0) sDBw[wave * C + 16 * mt + 4 * lg + m] = sacc;
         }
     __syncthreads();
+    {
+        constexpr int VQ = 16 / (int)sizeof(T);        // io elements per 16-byte piece
+        for (int idx = tid; idx < C * (DK / VQ); idx += NTH) {
+            const int r = idx / (DK / VQ), cq = VQ * (idx % (DK / VQ));
+            if (r < nvalid) {
+                *reinterpret_cast<uint4*>(dqg + tok(r) * DK + cq) = *reinterpret_cast<const uint4*>(sDQ + r * DKT + cq);
+                *reinterpret_cast<uint4*>(dkg + tok(r) * DK + cq) = *reinterpret_cast<const uint4*>(sDK + r * DKT + cq);
+            }
+        }
+        for (int idx = tid; idx < C * (DK / 4); idx += NTH) {
+            const int r = idx / (DK / 4), cq = 4 * (idx % (DK / 4));
+            if (r < nvalid)
+                *reinterpret_cast<float4*>(a.dalpha + tok(r) * DK + cq) = *reinterpret_cast<const float4*>(sDA + r * DKA + cq);
+        }
+    }
     if (tid < nvalid) {
         float sv = 0.f, sw = 0.f;
 #pragma unroll
