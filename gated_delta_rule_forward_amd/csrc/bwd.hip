@@ -511,57 +511,67 @@ __global__ __launch_bounds__(kLocalThreads) void bwd_local_kernel(BwdLocalArgs a
 
     // ---- load (every loop has a compile-time trip count, so the loads of a
     //      thread are issued together) ---------------------------------------------
-    bool tiny = false;
-    {
-        constexpr int NA = C * DK / 4 / NTH > 0 ? C * DK / 4 / NTH : 1;
+    // (every load of this phase is issued before its results are used: the
+    // addresses are clamped instead of guarded, and the gate test has no
+    // short-circuit, so no load waits for another)
+    constexpr int NA0 = (C * DK / 4 + NTH - 1) / NTH;
+    float4 al0[NA0];
 #pragma unroll
-        for (int x = 0; x < NA; ++x) {
-            const int idx = tid + NTH * x;
-            const int r = idx / (DK / 4), c4 = 4 * (idx % (DK / 4));
-            if (idx < C * DK / 4 && r < nvalid) {
-                const float4 al = *reinterpret_cast<const float4*>(a.alpha + tok(r) * DK + c4);
-                tiny |= fabsf(al.x) < kTinyGate || fabsf(al.y) < kTinyGate ||
-                        fabsf(al.z) < kTinyGate || fabsf(al.w) < kTinyGate;
-            }
-        }
+    for (int x = 0; x < NA0; ++x) {
+        const int idx = min(tid + NTH * x, C * DK / 4 - 1);
+        const int r = min(idx / (DK / 4), nvalid - 1), c4 = 4 * (idx % (DK / 4));
+        al0[x] = *reinterpret_cast<const float4*>(a.alpha + tok(r) * DK + c4);
+    }
+    const float bt0 = a.beta[tok(min(tid, nvalid - 1))];
+    constexpr int NTL = (C * C / 4 + NTH - 1) / NTH;
+    float4 t40[NTL];
+#pragma unroll
+    for (int x = 0; x < NTL; ++x)
+        t40[x] = *reinterpret_cast<const float4*>(a.Tm + unit * C * C + 4 * min(tid + NTH * x, C * C / 4 - 1));
+    const T* dO = static_cast<const T*>(a.dO);
+    // dO, Delta, and X (into the Y buffer; y replaces it below)
+    constexpr int NL = (C * G::DVMAX / 4 + NTH - 1) / NTH;
+    const int DV4 = Dv / 4;
+    Vec4<T> ro[NL];
+    float4 rd[NL], rx[NL];
+#pragma unroll
+    for (int x = 0; x < NL; ++x) {
+        const int idx = min(tid + NTH * x, C * DV4 - 1);
+        const int r = idx / DV4, c4 = 4 * (idx % DV4), rv = min(r, nvalid - 1);
+        ro[x] = Vec4<T>::load(dO + tok(rv) * Dv + c4);
+        rd[x] = *reinterpret_cast<const float4*>(a.DL + (unit * C + rv) * Dv + c4);
+        rx[x] = *reinterpret_cast<const float4*>(a.XB + (unit * C + r) * Dv + c4);
+    }
+    bool tiny = false;
+#pragma unroll
+    for (int x = 0; x < NA0; ++x) {
+        const int idx = tid + NTH * x;
+        const float4 al = al0[x];
+        const float m = fminf(fminf(fabsf(al.x), fabsf(al.y)), fminf(fabsf(al.z), fabsf(al.w)));
+        tiny = tiny | (idx < C * DK / 4 && idx / (DK / 4) < nvalid && m < kTinyGate);
     }
     if (tid < C) {
-        sBeta[tid] = tid < nvalid ? a.beta[tok(tid)] : 0.f;
+        sBeta[tid] = tid < nvalid ? bt0 : 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) sDBv[w * C + tid] = 0.f;
     }
-    {
-        constexpr int NTL = (C * C / 4 + NTH - 1) / NTH;
 #pragma unroll
-        for (int x = 0; x < NTL; ++x) {
-            const int idx = tid + NTH * x;
-            if (idx < C * C / 4) {
-                const float4 t4 = *reinterpret_cast<const float4*>(a.Tm + unit * C * C + 4 * idx);
-                *reinterpret_cast<float4*>(sT + (4 * idx / C) * LDT + (4 * idx) % C) = t4;
-            }
-        }
+    for (int x = 0; x < NTL; ++x) {
+        const int idx = tid + NTH * x;
+        if (idx < C * C / 4)
+            *reinterpret_cast<float4*>(sT + (4 * idx / C) * LDT + (4 * idx) % C) = t40[x];
     }
-    const T* dO = static_cast<const T*>(a.dO);
-    {
-        // dO, Delta, and X (into the Y buffer; y replaces it below)
-        constexpr int NL = (C * G::DVMAX / 4 + NTH - 1) / NTH;
-        const int DV4 = Dv / 4;
 #pragma unroll
-        for (int x = 0; x < NL; ++x) {
-            const int idx = tid + NTH * x;
-            if (idx < C * DV4) {
-                const int r = idx / DV4, c4 = 4 * (idx % DV4);
-                float4 o = make_float4(0.f, 0.f, 0.f, 0.f), d = o;
-                if (r < nvalid) {
-                    const Vec4<T> xo = Vec4<T>::load(dO + tok(r) * Dv + c4);
-                    o = make_float4(xo.get(0), xo.get(1), xo.get(2), xo.get(3));
-                    d = *reinterpret_cast<const float4*>(a.DL + (unit * C + r) * Dv + c4);
-                }
-                const float4 xb = *reinterpret_cast<const float4*>(a.XB + (unit * C + r) * Dv + c4);
-                *reinterpret_cast<float4*>(sDO + r * LDV + c4) = o;
-                *reinterpret_cast<float4*>(sDL + r * LDV + c4) = d;
-                *reinterpret_cast<float4*>(sY + r * LDV + c4) = xb;
-            }
+    for (int x = 0; x < NL; ++x) {
+        const int idx = tid + NTH * x;
+        if (idx < C * DV4) {
+            const int r = idx / DV4, c4 = 4 * (idx % DV4);
+            const float w = r < nvalid ? 1.f : 0.f;          // rows past the end: zero
+            const float4 dd = rd[x];
+            *reinterpret_cast<float4*>(sDO + r * LDV + c4) =
+                make_float4(w * ro[x].get(0), w * ro[x].get(1), w * ro[x].get(2), w * ro[x].get(3));
+            *reinterpret_cast<float4*>(sDL + r * LDV + c4) = make_float4(w * dd.x, w * dd.y, w * dd.z, w * dd.w);
+            *reinterpret_cast<float4*>(sY + r * LDV + c4) = rx[x];
         }
     }
     // loads of later phases issued now, so that their latency overlaps the
@@ -1111,35 +1121,49 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_tiny_kernel(BwdLocalArgs a)
 
     if (tid == 0) *sCnt = 0;
     {
-        // Delta, dO and dv = beta y of the chunk (compile-time trip counts so
-        // a thread's loads are issued together)
+        // Delta, dO and dv = beta y of the chunk, and the gates: every load is
+        // issued before any result is used (clamped addresses, no guards)
         constexpr int NL = (C * L::DVMAX / 4 + kBwdThreads - 1) / kBwdThreads;
-        const int DV4 = Dv / 4;
+        constexpr int NA = (C * DK / 4 + kBwdThreads - 1) / kBwdThreads;
+        const int DV4 = Dv / 4, nl = nvalid * DV4, na = nvalid * (DK / 4);
+        float4 rd[NL], ry[NL], ral[NA];
+        Vec4<T> ro[NL];
+        float rb[NL];
+#pragma unroll
+        for (int x = 0; x < NL; ++x) {
+            const int idx = min(tid + kBwdThreads * x, nl - 1);
+            const int r = idx / DV4, c4 = 4 * (idx % DV4);
+            rd[x] = *reinterpret_cast<const float4*>(a.DL + (unit * C + r) * Dv + c4);
+            ro[x] = Vec4<T>::load(dO + tok(r) * Dv + c4);
+            ry[x] = *reinterpret_cast<const float4*>(a.XB + (unit * C + r) * Dv + c4);
+            rb[x] = a.beta[tok(r)];
+        }
+#pragma unroll
+        for (int x = 0; x < NA; ++x) {
+            const int idx = min(tid + kBwdThreads * x, na - 1);
+            const int r = idx / (DK / 4), c4 = 4 * (idx % (DK / 4));
+            ral[x] = *reinterpret_cast<const float4*>(a.alpha + tok(r) * DK + c4);
+        }
 #pragma unroll
         for (int x = 0; x < NL; ++x) {
             const int idx = tid + kBwdThreads * x;
-            if (idx < nvalid * DV4) {
+            if (idx < nl) {
                 const int r = idx / DV4, c4 = 4 * (idx % DV4);
-                const float4 d = *reinterpret_cast<const float4*>(a.DL + (unit * C + r) * Dv + c4);
-                const Vec4<T> o = Vec4<T>::load(dO + tok(r) * Dv + c4);
-                const float4 y = *reinterpret_cast<const float4*>(a.XB + (unit * C + r) * Dv + c4);
-                const float bt = a.beta[tok(r)];
-                *reinterpret_cast<float4*>(sDL + r * Dv + c4) = d;
-                *reinterpret_cast<float4*>(sDO + r * Dv + c4) = make_float4(o.get(0), o.get(1), o.get(2), o.get(3));
+                const float bt = rb[x];
+                const float4 y = ry[x];
+                *reinterpret_cast<float4*>(sDL + r * Dv + c4) = rd[x];
+                *reinterpret_cast<float4*>(sDO + r * Dv + c4) =
+                    make_float4(ro[x].get(0), ro[x].get(1), ro[x].get(2), ro[x].get(3));
                 *reinterpret_cast<float4*>(sE + r * Dv + c4) = make_float4(bt * y.x, bt * y.y, bt * y.z, bt * y.w);
             }
         }
-    }
-    __syncthreads();
-    {
-        constexpr int NA = (C * DK / 4 + kBwdThreads - 1) / kBwdThreads;
+        __syncthreads();   // (the count is zero before any thread adds to it)
 #pragma unroll
         for (int x = 0; x < NA; ++x) {
             const int idx = tid + kBwdThreads * x;
-            if (idx < nvalid * (DK / 4)) {
+            if (idx < na) {
                 const int r = idx / (DK / 4), c4 = 4 * (idx % (DK / 4));
-                const float4 al = *reinterpret_cast<const float4*>(a.alpha + tok(r) * DK + c4);
-                const float v4[4] = {al.x, al.y, al.z, al.w};
+                const float v4[4] = {ral[x].x, ral[x].y, ral[x].z, ral[x].w};
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     if (fabsf(v4[j]) < kTinyGate) sList[atomicAdd(sCnt, 1)] = r * DK + c4 + j;
