@@ -850,13 +850,15 @@ __global__ __launch_bounds__(kThreads, (sizeof(T) == 4 && DK == 128) ? 1 : 2) vo
     if (unit < 0) return;
     // lead limit: chunk n waits until the chain of its (b, h) has taken chunk
     // n - lead (ready word 3), so the units between prep and chain stay in
-    // the caches; bounded, and only a matter of speed
+    // the caches; bounded, given up at once when a chain workgroup has given
+    // up (its marks stop), and only a matter of speed
     if (args.lead > 0 && unit % args.NC >= args.lead) {
         if (threadIdx.x == 0) {
             const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
             for (unsigned n = 0; n < kLeadWaitPolls; ++n) {
                 if (__hip_atomic_load(&args.ready[unit - args.lead], __ATOMIC_RELAXED,
                                       __HIP_MEMORY_SCOPE_AGENT) == 3u ||
+                    __hip_atomic_load(&args.sctl->abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ||
                     __builtin_amdgcn_s_memrealtime() - t0 > kLeadWaitTicks)
                     break;
                 __builtin_amdgcn_s_sleep(8);

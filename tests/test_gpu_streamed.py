@@ -149,6 +149,27 @@ def test_streamed_flagged_chunks_give_up():
     assert torch.equal(out, out1) and torch.equal(st, st1)
 
 
+def test_streamed_give_up_past_the_lead_limit():
+    """A give-up early in a sequence longer than the prep's lead limit
+    (H=32, T=2048: 32 chunks, a limit of 28): the prep units past the limit
+    stop waiting for marks that no longer come, and the result is bitwise the
+    single-stream call's."""
+    w = workloads.workload(2, B=1, H=32, T=2048)
+    inp = workloads.make_prefill(w)
+    inp["alpha"][0, 150:160, 3, :4] = 1e-30      # head 3, chunk 2: flagged for the exact kernel
+    say(f"[streamed give-up, long] {w}")
+    d = to_dev(inp)
+    ws = torch.empty(kda.workspace_size(w.B, w.T, w.H, w.D, w.D, 64, w.dtype), dtype=torch.uint8,
+                     device=DEV)
+    out, st = run_gpu(d, 64, w.mode, workspace=ws, side=kda.SideStream(),
+                      stream=torch.cuda.Stream(), flags=SF)
+    gave_up, done, expect = _ctl(ws)
+    say(f"  gave up {gave_up}, chains {done}/{expect}")
+    assert gave_up == 1
+    out1, st1 = run_gpu(d, 64, w.mode)
+    assert torch.equal(out, out1) and torch.equal(st, st1)
+
+
 def test_streamed_not_taken():
     """Forms outside the streamed path keep their launch sequence with a side
     stream: fewer than 8 sequences, too many chains, the final state written
