@@ -139,6 +139,49 @@ def time_forward(kda, torch, w, inp, steps, warmup, extra_flags=0, side=None):
     return med, mean, per, out, st
 
 
+def time_train_step(kda, torch, w, inp, steps, warmup):
+    """One training step split as kda_chunk_forward_save + kda_chunk_backward_saved
+    on workload w: ms per step (the pair), and per call ms of each half."""
+    import workloads
+    stream = torch.cuda.current_stream()
+    dO, dST = workloads.make_backward_seeds(w, device="cuda")
+    saved = torch.empty(kda.backward_workspace_size(w.B, w.T, w.H, w.Dk, w.Dv, w.chunk, w.dtype),
+                        dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(inp["v"])
+    st = torch.empty((w.B, w.H, w.Dk, w.Dv), dtype=torch.float32, device="cuda")
+    grads = {"dq": torch.empty_like(inp["q"]), "dk": torch.empty_like(inp["k"]),
+             "dv": torch.empty_like(inp["v"]), "d_alpha": torch.empty_like(inp["alpha"]),
+             "d_beta": torch.empty_like(inp["beta"]),
+             "d_initial_state": torch.empty((w.B, w.H, w.Dk, w.Dv), dtype=torch.float32,
+                                            device="cuda")}
+
+    def fwd():
+        kda.chunk_forward_save(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["S0"],
+                               chunk=w.chunk, mode=w.mode, out=out, final_state=st, saved=saved,
+                               stream=stream)
+
+    def bwd():
+        kda.chunk_backward_saved(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], dO, saved,
+                                 dST, chunk=w.chunk, mode=w.mode, grads=grads, stream=stream)
+
+    for _ in range(warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * steps)]
+    for i in range(steps):
+        ev[3 * i].record(stream)
+        fwd()
+        ev[3 * i + 1].record(stream)
+        bwd()
+        ev[3 * i + 2].record(stream)
+    torch.cuda.synchronize()
+    f = [ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(steps)]
+    b = [ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(steps)]
+    return (statistics.median([x + y for x, y in zip(f, b)]), statistics.median(f),
+            statistics.median(b))
+
+
 def time_backward(kda, torch, w, inp, steps, warmup):
     """kda_chunk_backward on workload w (loss gradients from workloads.make_backward_seeds):
     ms per call and per-kernel durations, plus the algorithmic bytes of the call
@@ -429,6 +472,12 @@ def main():
         line.setdefault("others", {})["kda_bf16_prefill_backward"] = {
             "ms": msb, "tokens_per_s": tokens / (msb / 1e3), "algorithmic_bytes": nbb,
             "path_hbm_frac": nbb / (msb / 1e3) / 1e9 / HBM_PEAK_GBS, "kernels_ms": perb}
+        # a training step without recomputation: the saving forward, then the
+        # gradients from its workspace
+        mst, msf, msbs = time_train_step(kda, torch, w, inp, max(3, args.steps // 4), 3)
+        line["others"]["kda_bf16_prefill_train_step_saved"] = {
+            "ms": mst, "forward_save_ms": msf, "backward_saved_ms": msbs,
+            "tokens_per_s": tokens / (mst / 1e3)}
     if args.mfma_probe:
         line["mfma_probe"] = mfma_probe(kda)
     if args.copy_probe:

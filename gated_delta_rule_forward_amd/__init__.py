@@ -19,6 +19,7 @@ import torch
 
 __all__ = [
     "KDA", "CKDA", "KdaError", "library_path", "load", "abi_version", "workspace_size",
+    "chunk_forward_save", "chunk_backward_saved",
     "chunk_forward_noalloc", "NOALLOC_SCRATCH_BYTES", "SideStream", "SIDE_EVENTS",
     "chunk_forward", "chunk_forward_prologue", "chunk_forward_varlen", "chunk_forward_phase",
     "decode_step", "decode_step_phase", "decode_step_prologue", "gate_prep", "last_stage_times",
@@ -143,6 +144,10 @@ def load():
     lib.kda_chunk_backward_workspace_size.restype = i
     lib.kda_chunk_backward.argtypes = [vp] * 14 + [i] * 8 + [u, vp, sz, vp]
     lib.kda_chunk_backward.restype = i
+    lib.kda_chunk_forward_save.argtypes = [vp] * 8 + [i] * 8 + [u, vp, sz, vp]
+    lib.kda_chunk_forward_save.restype = i
+    lib.kda_chunk_backward_saved.argtypes = [vp] * 13 + [i] * 8 + [u, vp, sz, vp]
+    lib.kda_chunk_backward_saved.restype = i
     lib.kda_chunk_backward_prologue_workspace_size.argtypes = [i, i, i, i, i, i, i,
                                                                ctypes.POINTER(sz)]
     lib.kda_chunk_backward_prologue_workspace_size.restype = i
@@ -483,6 +488,70 @@ def chunk_backward(q, k, v, alpha, beta, d_out, initial_state=None, d_final_stat
                                 B, T, H, Dk, Dv, chunk, _DT[q.dtype], mode, flags,
                                 _ptr(workspace), wsb, _stream(stream))
     _check("kda_chunk_backward", st)
+    return g
+
+
+def chunk_forward_save(q, k, v, alpha, beta, initial_state=None, *, chunk: int = 64,
+                       mode: int = CKDA, out=None, final_state=None, want_final_state: bool = True,
+                       saved=None, stream=None, flags: int = 0):
+    """kda_chunk_forward_save: the forward of chunk_forward that also leaves in
+    `saved` (uint8, backward_workspace_size bytes; allocated when None) what
+    chunk_backward_saved needs.  Returns (out, final_state, saved)."""
+    lib = load()
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, T, H, Dv), dtype=q.dtype, device=dev)
+    if final_state is None and want_final_state:
+        final_state = torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev)
+    if saved is None:
+        saved = torch.empty(max(backward_workspace_size(B, T, H, Dk, Dv, chunk, q.dtype), 1),
+                            dtype=torch.uint8, device=dev)
+    _dev(q, k, v, alpha, beta, initial_state, out, final_state, saved)
+    if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must share one dtype (float32 or bfloat16)")
+    st = lib.kda_chunk_forward_save(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                    _ptr(initial_state), _ptr(out), _ptr(final_state),
+                                    B, T, H, Dk, Dv, chunk, _DT[q.dtype], mode, flags,
+                                    _ptr(saved), saved.numel() * saved.element_size(),
+                                    _stream(stream))
+    _check("kda_chunk_forward_save", st)
+    return out, final_state, saved
+
+
+def chunk_backward_saved(q, k, v, alpha, beta, d_out, saved, d_final_state=None, *,
+                         chunk: int = 64, mode: int = CKDA, want_d_initial_state: bool = True,
+                         grads=None, stream=None, flags: int = 0):
+    """kda_chunk_backward_saved: chunk_backward's gradients from the workspace
+    a chunk_forward_save call on the same inputs filled (used up by this
+    call).  Returns the dict of chunk_backward."""
+    lib = load()
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    g = dict(grads or {})
+    g.setdefault("dq", torch.empty((B, T, H, Dk), dtype=q.dtype, device=dev))
+    g.setdefault("dk", torch.empty((B, T, H, Dk), dtype=q.dtype, device=dev))
+    g.setdefault("dv", torch.empty((B, T, H, Dv), dtype=q.dtype, device=dev))
+    g.setdefault("d_alpha", torch.empty((B, T, H, Dk), dtype=torch.float32, device=dev))
+    g.setdefault("d_beta", torch.empty((B, T, H), dtype=torch.float32, device=dev))
+    if want_d_initial_state:
+        g.setdefault("d_initial_state", torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev))
+    else:
+        g["d_initial_state"] = None
+    _dev(q, k, v, alpha, beta, d_out, d_final_state, saved, *g.values())
+    if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype or d_out.dtype != q.dtype:
+        raise ValueError("q, k, v and d_out must share one dtype (float32 or bfloat16)")
+    st = lib.kda_chunk_backward_saved(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+                                      _ptr(d_out), _ptr(d_final_state),
+                                      _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
+                                      _ptr(g["d_alpha"]), _ptr(g["d_beta"]),
+                                      _ptr(g["d_initial_state"]),
+                                      B, T, H, Dk, Dv, chunk, _DT[q.dtype], mode, flags,
+                                      _ptr(saved), saved.numel() * saved.element_size(),
+                                      _stream(stream))
+    _check("kda_chunk_backward_saved", st)
     return g
 
 

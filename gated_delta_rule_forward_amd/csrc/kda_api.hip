@@ -696,13 +696,19 @@ size_t backward_varlen_layout(int N, int total_T, int H, int Dk, int Dv, int chu
     return n + ((2 * ((size_t)N + 1) * sizeof(int) + 255) & ~size_t(255));
 }
 
+// which part of the backward's work a call enqueues: all of it; the forward
+// pass that leaves its saved state in the workspace (with the forward's
+// outputs); or the gradient pass from such a workspace
+enum class BwdPart { ALL, SAVE, FROM_SAVED };
+
 kda_status_t backward_enqueue(const void* q, const void* k, const void* v, const float* alpha,
                               const float* beta, const float* initial_state, const void* d_out,
                               const float* d_final_state, void* dq, void* dk, void* dv,
                               float* d_alpha, float* d_beta, float* d_initial_state, int B, int T,
                               int H, int Dk, int Dv, int chunk, kda_dtype_t dtype, kda_mode_t mode,
                               void* workspace, Recorder& rec, hipStream_t s,
-                              const int* cu_seqlens = nullptr);
+                              const int* cu_seqlens = nullptr, BwdPart part = BwdPart::ALL,
+                              void* out = nullptr, float* final_state = nullptr);
 
 kda_status_t check_backward_shape(int B, int T, int H, int Dk, int Dv, int chunk,
                                   kda_dtype_t dtype)
@@ -715,20 +721,28 @@ kda_status_t check_backward_shape(int B, int T, int H, int Dk, int Dv, int chunk
     return KDA_OK;
 }
 
-kda_status_t chunk_backward(const void* q, const void* k, const void* v, const float* alpha,
-                            const float* beta, const float* initial_state, const void* d_out,
-                            const float* d_final_state, void* dq, void* dk, void* dv,
-                            float* d_alpha, float* d_beta, float* d_initial_state, int B, int T,
-                            int H, int Dk, int Dv, int chunk, kda_dtype_t dtype, kda_mode_t mode,
-                            unsigned flags, void* workspace, size_t workspace_bytes, void* stream)
+// The backward, or one part of it (BwdPart): argument checks, then the enqueue.
+// SAVE takes no gradient arguments and writes out / final_state; FROM_SAVED
+// takes no initial_state (the saved chunk states hold it).
+kda_status_t chunk_backward_part(const void* q, const void* k, const void* v, const float* alpha,
+                                 const float* beta, const float* initial_state, const void* d_out,
+                                 const float* d_final_state, void* dq, void* dk, void* dv,
+                                 float* d_alpha, float* d_beta, float* d_initial_state, int B,
+                                 int T, int H, int Dk, int Dv, int chunk, kda_dtype_t dtype,
+                                 kda_mode_t mode, unsigned flags, void* workspace,
+                                 size_t workspace_bytes, void* stream, BwdPart part,
+                                 void* out = nullptr, float* final_state = nullptr)
 {
     kda_status_t st = check_backward_shape(B, T, H, Dk, Dv, chunk, dtype);
     if (st != KDA_OK) return st;
     if (mode != KDA_MODE_KDA && mode != KDA_MODE_CKDA) return KDA_ERR_UNSUPPORTED;
     if (flags & ~KDA_FLAG_STAGE_EVENTS) return KDA_ERR_UNSUPPORTED;
-    if (T > 0 && (!q || !k || !v || !alpha || !beta || !d_out || !dq || !dk || !dv || !d_alpha ||
-                  !d_beta))
+    const bool grads = part != BwdPart::SAVE;
+    if (T > 0 && (!q || !k || !v || !alpha || !beta))
         return KDA_ERR_NULL_POINTER;
+    if (T > 0 && grads && (!d_out || !dq || !dk || !dv || !d_alpha || !d_beta))
+        return KDA_ERR_NULL_POINTER;
+    if (T > 0 && !grads && !out) return KDA_ERR_NULL_POINTER;
     size_t ws_need = 0;
     kda_chunk_backward_workspace_size(B, T, H, Dk, Dv, chunk, dtype, &ws_need);
     if (T > 0 && !workspace) return KDA_ERR_NULL_POINTER;
@@ -741,18 +755,20 @@ kda_status_t chunk_backward(const void* q, const void* k, const void* v, const f
     for (const void* p : vec)
         if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
     const void* elt[] = {v, beta, initial_state, d_final_state, dq, dk, dv, d_alpha, d_beta,
-                         d_initial_state};
-    const uintptr_t ea[] = {e, 4, 4, 4, e, e, e, 4, 4, 4};
-    for (int i = 0; i < 10; ++i)
+                         d_initial_state, out, final_state};
+    const uintptr_t ea[] = {e, 4, 4, 4, e, e, e, 4, 4, 4, e, 4};
+    for (int i = 0; i < 12; ++i)
         if (elt[i] && !aligned(elt[i], ea[i])) return KDA_ERR_MISALIGNED;
     struct R { const void* p; size_t n; };
     const R in[] = {{q, ntok * Dk * e}, {k, ntok * Dk * e}, {v, ntok * Dv * e},
                     {alpha, ntok * Dk * 4}, {beta, ntok * 4},
-                    {initial_state, initial_state ? nstate : 0}, {d_out, ntok * Dv * e},
+                    {initial_state, initial_state ? nstate : 0}, {d_out, d_out ? ntok * Dv * e : 0},
                     {d_final_state, d_final_state ? nstate : 0}};
-    const R outs[] = {{dq, ntok * Dk * e}, {dk, ntok * Dk * e}, {dv, ntok * Dv * e},
-                      {d_alpha, ntok * Dk * 4}, {d_beta, ntok * 4},
-                      {d_initial_state, d_initial_state ? nstate : 0}, {workspace, ws_need}};
+    const R outs[] = {{dq, dq ? ntok * Dk * e : 0}, {dk, dk ? ntok * Dk * e : 0},
+                      {dv, dv ? ntok * Dv * e : 0}, {d_alpha, d_alpha ? ntok * Dk * 4 : 0},
+                      {d_beta, d_beta ? ntok * 4 : 0},
+                      {d_initial_state, d_initial_state ? nstate : 0}, {workspace, ws_need},
+                      {out, out ? ntok * Dv * e : 0}, {final_state, final_state ? nstate : 0}};
     constexpr int NO = sizeof(outs) / sizeof(outs[0]);
     for (const R& o : outs)
         for (const R& i : in)
@@ -768,9 +784,22 @@ kda_status_t chunk_backward(const void* q, const void* k, const void* v, const f
         lock.lock();
         if (stage_begin() != hipSuccess) return KDA_ERR_HIP;
     }
-    return backward_enqueue(q, k, v, alpha, beta, initial_state, d_out, d_final_state, dq, dk, dv,
-                            d_alpha, d_beta, d_initial_state, B, T, H, Dk, Dv, chunk, dtype, mode,
-                            workspace, rec, s);
+    return backward_enqueue(q, k, v, alpha, beta, part == BwdPart::FROM_SAVED ? nullptr : initial_state,
+                            d_out, d_final_state, dq, dk, dv, d_alpha, d_beta, d_initial_state, B,
+                            T, H, Dk, Dv, chunk, dtype, mode, workspace, rec, s, nullptr, part, out,
+                            final_state);
+}
+
+kda_status_t chunk_backward(const void* q, const void* k, const void* v, const float* alpha,
+                            const float* beta, const float* initial_state, const void* d_out,
+                            const float* d_final_state, void* dq, void* dk, void* dv,
+                            float* d_alpha, float* d_beta, float* d_initial_state, int B, int T,
+                            int H, int Dk, int Dv, int chunk, kda_dtype_t dtype, kda_mode_t mode,
+                            unsigned flags, void* workspace, size_t workspace_bytes, void* stream)
+{
+    return chunk_backward_part(q, k, v, alpha, beta, initial_state, d_out, d_final_state, dq, dk,
+                               dv, d_alpha, d_beta, d_initial_state, B, T, H, Dk, Dv, chunk, dtype,
+                               mode, flags, workspace, workspace_bytes, stream, BwdPart::ALL);
 }
 
 // the backward's launches (arguments validated by the caller, stage events
@@ -781,9 +810,18 @@ kda_status_t backward_enqueue(const void* q, const void* k, const void* v, const
                               const float* d_final_state, void* dq, void* dk, void* dv,
                               float* d_alpha, float* d_beta, float* d_initial_state, int B, int T,
                               int H, int Dk, int Dv, int chunk, kda_dtype_t dtype, kda_mode_t mode,
-                              void* workspace, Recorder& rec, hipStream_t s, const int* cu_seqlens)
+                              void* workspace, Recorder& rec, hipStream_t s, const int* cu_seqlens,
+                              BwdPart part, void* out, float* final_state)
 {
     const size_t nstate = (size_t)B * H * Dk * Dv * 4;
+    if (T == 0 && part == BwdPart::SAVE) {
+        // no tokens: the final state is the initial one
+        if (!final_state) return KDA_OK;
+        if (rec.mark("state_copy") != hipSuccess) return KDA_ERR_HIP;
+        if (kda::launch_state_copy(initial_state, final_state, nstate / 4, s) != hipSuccess)
+            return KDA_ERR_HIP;
+        return rec.done() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    }
     if (T == 0) {
         // no tokens: the loss is <S0, dST>, so dS0 = dST
         if (!d_initial_state) return KDA_OK;
@@ -841,21 +879,28 @@ kda_status_t backward_enqueue(const void* q, const void* k, const void* v, const
                       0, sh.NC, 1, nullptr, nullptr};
     ca.CS32 = CS32;
     ca.DL = DL;
+    if (part == BwdPart::SAVE) {
+        ca.out = out;
+        ca.ST = final_state;
+    }
     const kda::BwdChainArgs ra{ws.Kt, ws.P, ws.QG, ws.W, ws.GC, d_out, d_final_state,
                                d_initial_state, DSN, XB, B, T, H, Dv, sh.NC, cu_s, cs};
     const kda::BwdLocalArgs la{q, k, v, alpha, beta, d_out, Tm, CS32, DL, DSN, XB,
                                dq, dk, dv, d_alpha, d_beta, FLB, T, H, Dv, sh.NC,
                                cu_s, cs, cu_seqlens ? B : 0};
 
-    if (rec.mark("prep_fast") != hipSuccess) return KDA_ERR_HIP;
-    if (kda::launch_prep_fast(io, sh, pa, s) != hipSuccess) return KDA_ERR_HIP;
-    if (rec.done() != hipSuccess) return KDA_ERR_HIP;
-    if (rec.mark("prep_exact") != hipSuccess) return KDA_ERR_HIP;
-    if (kda::launch_prep_exact(io, sh, pa, s) != hipSuccess) return KDA_ERR_HIP;
-    if (rec.done() != hipSuccess) return KDA_ERR_HIP;
-    if (rec.mark("chain_states") != hipSuccess) return KDA_ERR_HIP;
-    if (kda::launch_chain(io, shc, ca, s) != hipSuccess) return KDA_ERR_HIP;
-    if (rec.done() != hipSuccess) return KDA_ERR_HIP;
+    if (part != BwdPart::FROM_SAVED) {
+        if (rec.mark("prep_fast") != hipSuccess) return KDA_ERR_HIP;
+        if (kda::launch_prep_fast(io, sh, pa, s) != hipSuccess) return KDA_ERR_HIP;
+        if (rec.done() != hipSuccess) return KDA_ERR_HIP;
+        if (rec.mark("prep_exact") != hipSuccess) return KDA_ERR_HIP;
+        if (kda::launch_prep_exact(io, sh, pa, s) != hipSuccess) return KDA_ERR_HIP;
+        if (rec.done() != hipSuccess) return KDA_ERR_HIP;
+        if (rec.mark("chain_states") != hipSuccess) return KDA_ERR_HIP;
+        if (kda::launch_chain(io, shc, ca, s) != hipSuccess) return KDA_ERR_HIP;
+        if (rec.done() != hipSuccess) return KDA_ERR_HIP;
+    }
+    if (part == BwdPart::SAVE) return KDA_OK;
     static const char* const names[4] = {"relayout", "chain_reverse", "chunk_grads", "small_gates"};
     for (int stage = 0; stage < 4; ++stage) {
         if (rec.mark(names[stage]) != hipSuccess) return KDA_ERR_HIP;
@@ -1472,6 +1517,32 @@ kda_status_t kda_chunk_backward(const void* q, const void* k, const void* v, con
     return chunk_backward(q, k, v, alpha, beta, initial_state, d_out, d_final_state, dq, dk, dv,
                           d_alpha, d_beta, d_initial_state, B, T, H, Dk, Dv, chunk, dtype, mode,
                           flags, workspace, workspace_bytes, stream);
+}
+
+kda_status_t kda_chunk_forward_save(const void* q, const void* k, const void* v,
+                                    const float* alpha, const float* beta,
+                                    const float* initial_state, void* out, float* final_state,
+                                    int B, int T, int H, int Dk, int Dv, int chunk,
+                                    kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
+                                    void* saved, size_t saved_bytes, void* stream)
+{
+    return chunk_backward_part(q, k, v, alpha, beta, initial_state, nullptr, nullptr, nullptr,
+                               nullptr, nullptr, nullptr, nullptr, nullptr, B, T, H, Dk, Dv, chunk,
+                               dtype, mode, flags, saved, saved_bytes, stream, BwdPart::SAVE, out,
+                               final_state);
+}
+
+kda_status_t kda_chunk_backward_saved(const void* q, const void* k, const void* v,
+                                      const float* alpha, const float* beta, const void* d_out,
+                                      const float* d_final_state, void* dq, void* dk, void* dv,
+                                      float* d_alpha, float* d_beta, float* d_initial_state,
+                                      int B, int T, int H, int Dk, int Dv, int chunk,
+                                      kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
+                                      void* saved, size_t saved_bytes, void* stream)
+{
+    return chunk_backward_part(q, k, v, alpha, beta, nullptr, d_out, d_final_state, dq, dk, dv,
+                               d_alpha, d_beta, d_initial_state, B, T, H, Dk, Dv, chunk, dtype,
+                               mode, flags, saved, saved_bytes, stream, BwdPart::FROM_SAVED);
 }
 
 kda_status_t kda_chunk_backward_prologue_workspace_size(int B, int T, int H, int Dk, int Dv,

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 16
+#define KDA_ABI_VERSION 17
 
 typedef enum {
     KDA_OK = 0,
@@ -465,6 +465,40 @@ kda_status_t kda_chunk_backward(const void* q, const void* k, const void* v,
                                 int B, int T, int H, int Dk, int Dv, int chunk,
                                 kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The forward and backward of one training step split into two calls, so the
+ * backward does not recompute the forward (the backward call above does).
+ * kda_chunk_forward_save is kda_chunk_forward (same inputs, outputs and
+ * supported set as kda_chunk_backward; out, final_state as for the forward,
+ * final_state may be NULL) that also leaves in `saved` what the gradient pass
+ * needs: the per-chunk factors, (I + A)^-1 in fp32, the fp32 chunk-start
+ * states and Delta of every chunk (the same chunkwise form, "Kimi Delta
+ * Attention: a bounded case study", Exercise 2).  `saved` is caller-owned,
+ * at least kda_chunk_backward_workspace_size bytes, 16-byte aligned.
+ * kda_chunk_backward_saved then gives the gradients of kda_chunk_backward
+ * (bit for bit the same) from that workspace and the same q, k, v, alpha,
+ * beta (initial_state is not passed again: the saved states hold it).  The
+ * saved workspace is used up by one kda_chunk_backward_saved call (the call
+ * rearranges its factors in place); a second gradient pass needs a new
+ * kda_chunk_forward_save.  Nothing checks that the inputs or the workspace
+ * are those of the save call: other data give undefined gradients (never an
+ * out-of-bounds access).  Status codes as for kda_chunk_backward; both calls
+ * only enqueue kernels on `stream`.
+ */
+kda_status_t kda_chunk_forward_save(const void* q, const void* k, const void* v,
+                                    const float* alpha, const float* beta,
+                                    const float* initial_state, void* out, float* final_state,
+                                    int B, int T, int H, int Dk, int Dv, int chunk,
+                                    kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
+                                    void* saved, size_t saved_bytes, void* stream);
+kda_status_t kda_chunk_backward_saved(const void* q, const void* k, const void* v,
+                                      const float* alpha, const float* beta, const void* d_out,
+                                      const float* d_final_state, void* dq, void* dk, void* dv,
+                                      float* d_alpha, float* d_beta, float* d_initial_state,
+                                      int B, int T, int H, int Dk, int Dv, int chunk,
+                                      kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
+                                      void* saved, size_t saved_bytes, void* stream);
 
 /*
  * Backward of kda_chunk_forward_prologue: the same loss gradients with respect

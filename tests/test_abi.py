@@ -53,7 +53,7 @@ def test_side_stream_helpers_refuse_null(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 16
+    assert lib.kda_abi_version() == 17
     for s in range(10):
         assert lib.kda_status_string(s) != b"unknown status"
     assert lib.kda_status_string(99) == b"unknown status"
@@ -355,6 +355,58 @@ def test_backward_validation(lib):
     opt = list(base)
     opt[5] = opt[7] = opt[13] = None                              # S0, dST, dS0 optional
     assert bw(ptrs=opt, T=0) == OK                                # nothing to do, no HIP call
+
+
+def test_save_and_saved_validation(lib):
+    """kda_chunk_forward_save / kda_chunk_backward_saved: the backward's
+    supported set and argument rules (checked before any HIP call)."""
+    f = Fake()
+    n = ctypes.c_size_t(0)
+    assert lib.kda_chunk_backward_workspace_size(1, 64, 2, 64, 64, 64, F32, ctypes.byref(n)) == OK
+    need = n.value
+
+    def fs(ptrs=None, T=64, Dk=64, chunk=64, dt=F32, mode=1, flags=0, ws=True, wsb=None):
+        p = ptrs if ptrs is not None else [f() for _ in range(8)]
+        return lib.kda_chunk_forward_save(*p, 1, T, 2, Dk, 64, chunk, dt, mode, flags,
+                                          f(need + 4096) if ws else None,
+                                          need if wsb is None else wsb, None)
+
+    base = [f() for _ in range(8)]                  # q k v alpha beta S0 out ST
+    assert fs(ptrs=[None] + base[1:]) == NULLP
+    assert fs(ptrs=base[:6] + [None] + base[7:]) == NULLP         # out
+    assert fs(ws=False) == NULLP
+    assert fs(wsb=need - 1) == WS
+    assert fs(chunk=16) == UNSUP
+    assert fs(Dk=16) == UNSUP
+    assert fs(flags=4) == UNSUP
+    al = list(base)
+    al[6] = base[2]                                               # out == v
+    assert fs(ptrs=al) == ALIAS
+    al = list(base)
+    al[7] = base[5]                                               # final state == S0
+    assert fs(ptrs=al) == ALIAS
+    opt = list(base)
+    opt[5] = opt[7] = None
+    assert fs(ptrs=opt, T=0) == OK                                # nothing to do, no HIP call
+
+    def bs(ptrs=None, T=64, chunk=64, flags=0, ws=True, wsb=None):
+        p = ptrs if ptrs is not None else [f() for _ in range(13)]
+        return lib.kda_chunk_backward_saved(*p, 1, T, 2, 64, 64, chunk, F32, 1, flags,
+                                            f(need + 4096) if ws else None,
+                                            need if wsb is None else wsb, None)
+
+    base = [f() for _ in range(13)]      # q k v alpha beta dO dST dq dk dv dalpha dbeta dS0
+    assert bs(ptrs=base[:5] + [None] + base[6:]) == NULLP         # d_out
+    assert bs(ptrs=base[:7] + [None] + base[8:]) == NULLP         # dq
+    assert bs(ws=False) == NULLP
+    assert bs(wsb=need - 1) == WS
+    assert bs(chunk=16) == UNSUP
+    al = list(base)
+    al[7] = base[0]                                               # dq == q
+    assert bs(ptrs=al) == ALIAS
+    opt = list(base)
+    opt[6] = opt[12] = None
+    assert bs(ptrs=opt, T=0) == OK
 
 
 def test_backward_prologue_validation(lib):
