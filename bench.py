@@ -58,7 +58,7 @@ def algorithmic_bytes(w, io_bytes, with_s0: bool, with_st: bool):
 KERNEL_SOURCES = {
     # files whose contents determine each kernel's code
     "prep_fast": ["prep_fast.hip", "kda_chunk.hpp", "kda_device.hpp", "kda_launch.hpp"],
-    "chain": ["chain.hip", "kda_chunk.hpp", "kda_device.hpp", "kda_launch.hpp"],
+    "chain": ["chain.hip", "kda_chunk.hpp", "kda_device.hpp", "kda_dma.hpp", "kda_launch.hpp"],
     "prep_exact": ["prep_exact.hip", "kda_chunk.hpp", "kda_device.hpp", "kda_launch.hpp"],
     "prep_stream": ["prep_fast.hip", "kda_chunk.hpp", "kda_device.hpp", "kda_launch.hpp"],
     "chain_stream": ["chain_wide.hip", "kda_chunk.hpp", "kda_device.hpp", "kda_launch.hpp"],

@@ -32,7 +32,8 @@
 // (which also stores the fp32 chunk states and Delta):
 //   relayout_kernel    W, Q*Gamma, Ktil^T, P -> W^T, (Q*Gamma)^T, Ktil, P^T in
 //                      the fragment-major A-operand layout, in place
-//   bwd_chain_kernel   the reverse chain, one workgroup per (b, h, 16 columns)
+//   bwd_chain_fifo_kernel  the reverse chain, one workgroup per (b, h, 16 columns)
+//                      (operands through an LDS FIFO fed by loader wavefronts)
 //   bwd_local_kernel   every chunk's gradients, one workgroup per chunk
 //   bwd_tiny_kernel    the direct dalpha of small gates, flagged chunks only
 // Packed batches locate chunks and sequences through the forward's tables.
@@ -41,6 +42,7 @@
 #include <type_traits>
 
 #include "kda_chunk.hpp"
+#include "kda_dma.hpp"
 #include "kda_launch.hpp"
 
 namespace kda {
@@ -171,19 +173,55 @@ struct RevGeom {
     static constexpr int SPW = (NT + 3) / 4;
 };
 
+// One workgroup per (b, h, 16-column slice), chunks in reverse: X = P^T dO +
+// Ktil dS for token tile w, then dS <- diag(Gamma_{C-1}) dS + (Q*Gamma)^T dO
+// - W^T X for the state tiles w, w + 4, ..; dS and -X are exchanged through
+// LDS as MFMA B fragments (two barriers per chunk), dO of the column slice is
+// staged transposed, and dSn and X go out through LDS as 16-byte stores.
+// Operands take the forward chain's route: four compute wavefronts and four
+// loader wavefronts.  Loader 4 + w moves compute wave w's operands of the chunk two
+// steps ahead into a two-stage FIFO with direct global-to-LDS loads (the P^T
+// and Ktil fragments of its token tile before the step's first barrier, the
+// (Q*Gamma)^T and W^T fragments and Gamma_C rows of its state tiles after it,
+// then L2 prefetches of the chunk five steps ahead into a sink); it waits for
+// the next chunk before the first barrier, and the compute wave moves that
+// chunk into registers before the second.  Every loader issues the same
+// loads each step, so its explicit wait counts are exact.
 template <typename T, int C, int DK>
-__global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
+struct RevFifo {
+    using G = RevGeom<T, C, DK>;
+    static constexpr int FB = 64 * G::NV * (int)sizeof(T);      // one 64-lane fragment
+    static constexpr int OPT = 0;                               // P^T, token tile     [NKC]
+    static constexpr int OKT = OPT + G::NKC * FB;               // Ktil, token tile    [NKD]
+    static constexpr int OQT = OKT + G::NKD * FB;               // (Q*Gamma)^T, state tiles [SPW][NKC]
+    static constexpr int OWT = OQT + G::SPW * G::NKC * FB;      // W^T, state tiles    [SPW][NKC]
+    static constexpr int OG = OWT + G::SPW * G::NKC * FB;       // Gamma_C rows        [SPW][4][16 B]
+    static constexpr int STAGE = OG + G::SPW * 64;
+    static constexpr size_t SINK = 2 * 4 * (size_t)STAGE;
+    static constexpr size_t BYTES = SINK + 1024;
+    static constexpr int runs(int bytes) { return (bytes + 1023) / 1024; }
+    static constexpr int NA = runs(G::NKC * FB) + runs(G::NKD * FB);         // loads before barrier 1
+    static constexpr int NDMA = NA + 2 * G::SPW * runs(G::NKC * FB) + 1;
+    static constexpr int KPF = 2;                                             // L2 prefetch loads
+    static constexpr size_t STATIC = (size_t)(G::NKD + G::NKC) * 64 * G::NV * sizeof(T) +
+                                     2 * 16 * (size_t)C * sizeof(T) + (size_t)(DK + C) * 16 * 4;
+    static_assert(NDMA + KPF <= 63, "vmcnt holds at most 63 outstanding loads");
+    static_assert(BYTES + STATIC <= 160 * 1024, "LDS of one workgroup");
+};
+
+constexpr int kRevThreads = 512;                 // four compute + four loader wavefronts
+
+template <typename T, int C, int DK>
+__global__ __launch_bounds__(kRevThreads) void bwd_chain_fifo_kernel(BwdChainArgs a)
 {
     using G = RevGeom<T, C, DK>;
+    using L = RevFifo<T, C, DK>;
     using F = Frag<T, G::KB>;
     __shared__ F sSf[G::NKD * 64];      // dS as B fragments, k = channels
     __shared__ F sXf[G::NKC * 64];      // -X as B fragments, k = tokens
-    // dO of this column slice, two chunks, transposed ([buffer][column][token]),
-    // so a lane's fragment slots (runs of 4 consecutive tokens) are 8 bytes
     __shared__ __attribute__((aligned(16))) T sDOt[2][16][C];
-    // this step's dSn and X slices in fp32, written through LDS so the
-    // global stores are 16-byte and coalesced
     __shared__ __attribute__((aligned(16))) float sOut[(DK + C) * 16];
+    extern __shared__ __attribute__((aligned(16))) unsigned char fifo[];
 
     const int Dv = a.Dv, H = a.H, NS = Dv / 16;
     const int gid = blockIdx.x, xcd = gid % kXcds, jx = gid / kXcds;
@@ -192,11 +230,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
     const int h = bh % H;
     const int tid = threadIdx.x, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int cw = wave & 3;                       // the compute wave a loader serves
     const int col = slice * 16 + ln;
     const T* dO = static_cast<const T*>(a.dO);
-    // the dO piece this thread stages: row tid / 4, columns 4 (tid % 4) .. + 3
     const int drow = tid >> 2, dcol = 4 * (tid & 3);
-    // this (sequence, head): chunk count, first token row, length, first unit
     const SeqPos sp = locate_seq(bh, H, a.T, a.NC, a.cu, a.cs);
     const int NCs = sp.nc;
     if (NCs == 0) {
@@ -216,7 +253,88 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
         }
         return;
     }
+    // the chunk of step i (steps run the chunks backwards), clamped so that the
+    // loads past the first chunk repeat it
+    auto chunk_of = [&](int i) { return max(NCs - 1 - i, 0); };
+    auto stg = [&](int i) { return fifo + (size_t)((i & 1) * 4 + cw) * L::STAGE; };
 
+    if (wave >= 4) {
+        // ---- loader wavefront ---------------------------------------------------
+        auto issue_a = [&](unsigned char* st, size_t unit) {
+            const int mt = cw < G::NM ? cw : G::NM - 1;
+            dma_run<G::NKC * L::FB>(static_cast<const unsigned char*>(a.PT) +
+                                        (unit * C * C + (size_t)mt * G::NKC * 64 * G::NV) * sizeof(T),
+                                    st + L::OPT, lane);
+            dma_run<G::NKD * L::FB>(static_cast<const unsigned char*>(a.Ktil) +
+                                        (unit * C * DK + (size_t)mt * G::NKD * 64 * G::NV) * sizeof(T),
+                                    st + L::OKT, lane);
+        };
+        auto issue_b = [&](unsigned char* st, size_t unit) {
+#pragma unroll
+            for (int u = 0; u < G::SPW; ++u) {
+                const int t = min(cw + 4 * u, G::NT - 1);
+                const size_t off = (unit * DK * C + (size_t)t * G::NKC * 64 * G::NV) * sizeof(T);
+                dma_run<G::NKC * L::FB>(static_cast<const unsigned char*>(a.QGT) + off,
+                                        st + L::OQT + u * G::NKC * L::FB, lane);
+                dma_run<G::NKC * L::FB>(static_cast<const unsigned char*>(a.WT) + off,
+                                        st + L::OWT + u * G::NKC * L::FB, lane);
+            }
+            // Gamma_C: lane j < 4 SPW fetches rows 16t + 4(j % 4) .. +3 of state
+            // tile u = j / 4; they land at OG + 16 j
+            if (lane < 4 * G::SPW) {
+                const int t = min(cw + 4 * (lane >> 2), G::NT - 1);
+                dma16(a.GC + unit * DK + 16 * t + 4 * (lane & 3), st + L::OG);
+            }
+        };
+        // L2 prefetch: 1 KB pieces of a chunk's P^T, Ktil, (Q*Gamma)^T, W^T; the
+        // column slices of one (b, h) share an XCD, so each takes every NS-th
+        // piece, its four loaders every fourth of those
+        constexpr int NPIECE = (C * C + 3 * C * DK) * (int)sizeof(T) / 1024;
+        const int per_wg = (NPIECE + NS - 1) / NS;
+        unsigned char* sink = fifo + L::SINK;
+        auto prefetch = [&](size_t unit) {
+#pragma unroll
+            for (int i = 0; i < L::KPF; ++i) {
+                const int q = cw + 4 * i;
+                int p = slice + NS * q;
+                if (q >= per_wg || p >= NPIECE) p = slice % NPIECE;
+                int off = p * 1024;
+                const unsigned char* base;
+                if (off < C * C * (int)sizeof(T)) {
+                    base = static_cast<const unsigned char*>(a.PT) + unit * C * C * sizeof(T);
+                } else {
+                    off -= C * C * (int)sizeof(T);
+                    const int blk = C * DK * (int)sizeof(T);
+                    const void* arr = off < blk ? a.Ktil : (off < 2 * blk ? a.QGT : a.WT);
+                    off %= blk;
+                    base = static_cast<const unsigned char*>(arr) + unit * C * DK * sizeof(T);
+                }
+                dma16(base + off + 16 * lane, sink);
+            }
+        };
+        issue_a(stg(0), sp.ubase + chunk_of(0));
+        issue_b(stg(0), sp.ubase + chunk_of(0));
+        issue_a(stg(1), sp.ubase + chunk_of(1));
+        issue_b(stg(1), sp.ubase + chunk_of(1));
+        prefetch(sp.ubase + chunk_of(2));
+        wait_vm<L::NDMA + L::KPF>();                  // step 0's chunk landed
+        lds_barrier();                                // B0: compute reads it
+        lds_barrier();                                // B1: stage 0 free
+        for (int i = 0; i < NCs; ++i) {
+            // step i + 2's chunk into the stage step i's chunk left; loads
+            // issued after step i + 1's chunk: the previous prefetch and part A
+            issue_a(stg(i), sp.ubase + chunk_of(i + 2));
+            wait_vm<L::NA + L::KPF>();                // step i + 1's chunk landed
+            lds_barrier();                            // barrier 1 of step i
+            issue_b(stg(i), sp.ubase + chunk_of(i + 2));
+            prefetch(sp.ubase + chunk_of(i + 5));
+            lds_barrier();                            // barrier 2 of step i
+        }
+        wait_vm<0>();   // no load may land in LDS after the workgroup ends
+        return;
+    }
+
+    // ---- compute wavefront ----------------------------------------------------------
     f32x4 dS[G::SPW];
 #pragma unroll
     for (int u = 0; u < G::SPW; ++u) {
@@ -226,43 +344,34 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
             dS[u][i] = (a.dST && t < G::NT) ? a.dST[((size_t)bh * DK + 16 * t + 4 * lg + i) * Dv + col] : 0.f;
         if (t < G::NT) put_tile<T, G::KB>(sSf, t, lane, dS[u]);
     }
-
-    // one chunk's operands in registers
     struct Ops {
         F pt[G::NKC], kt[G::NKD], qt[G::SPW][G::NKC], wt[G::SPW][G::NKC];
         f32x4 gc[G::SPW];
-        Vec4<T> dov;                     // this thread's dO piece of chunk n - 1
+    };
+    auto read_ops = [&](Ops& o, const unsigned char* st) {
+        const F* pt = reinterpret_cast<const F*>(st + L::OPT);
+        const F* kt = reinterpret_cast<const F*>(st + L::OKT);
+#pragma unroll
+        for (int s = 0; s < G::NKC; ++s) o.pt[s] = pt[s * 64 + lane];
+#pragma unroll
+        for (int s = 0; s < G::NKD; ++s) o.kt[s] = kt[s * 64 + lane];
+#pragma unroll
+        for (int u = 0; u < G::SPW; ++u) {
+            const F* qt = reinterpret_cast<const F*>(st + L::OQT + u * G::NKC * L::FB);
+            const F* wt = reinterpret_cast<const F*>(st + L::OWT + u * G::NKC * L::FB);
+#pragma unroll
+            for (int s = 0; s < G::NKC; ++s) {
+                o.qt[u][s] = qt[s * 64 + lane];
+                o.wt[u][s] = wt[s * 64 + lane];
+            }
+            o.gc[u] = *reinterpret_cast<const f32x4*>(st + L::OG + 16 * (4 * u + lg));
+        }
     };
     // this thread's dO piece of chunk m (rows past the end, and threads past
     // the chunk, read the sequence's last row; they are zeroed when staged)
     auto load_do = [&](int m) {
         const int row = min(m * C + min(drow, C - 1), sp.len - 1);
         return Vec4<T>::load(dO + (((size_t)sp.row0 + row) * H + h) * Dv + slice * 16 + dcol);
-    };
-    auto load_ops = [&](Ops& o, int n) {
-        const size_t unit = sp.ubase + n;
-        const int mt = wave < G::NM ? wave : G::NM - 1;
-        const T* pt = static_cast<const T*>(a.PT) + unit * C * C + (size_t)mt * G::NKC * 64 * G::NV;
-        const T* kt = static_cast<const T*>(a.Ktil) + unit * C * DK + (size_t)mt * G::NKD * 64 * G::NV;
-#pragma unroll
-        for (int s = 0; s < G::NKC; ++s) o.pt[s] = F::load(pt + (s * 64 + lane) * G::NV);
-#pragma unroll
-        for (int s = 0; s < G::NKD; ++s) o.kt[s] = F::load(kt + (s * 64 + lane) * G::NV);
-#pragma unroll
-        for (int u = 0; u < G::SPW; ++u) {
-            const int t = min(wave + 4 * u, G::NT - 1);
-            const T* qt = static_cast<const T*>(a.QGT) + unit * DK * C + (size_t)t * G::NKC * 64 * G::NV;
-            const T* wt = static_cast<const T*>(a.WT) + unit * DK * C + (size_t)t * G::NKC * 64 * G::NV;
-#pragma unroll
-            for (int s = 0; s < G::NKC; ++s) {
-                o.qt[u][s] = F::load(qt + (s * 64 + lane) * G::NV);
-                o.wt[u][s] = F::load(wt + (s * 64 + lane) * G::NV);
-            }
-            o.gc[u] = *reinterpret_cast<const f32x4*>(a.GC + unit * DK + 16 * t + 4 * lg);
-        }
-        // one chunk ahead of the operands: staged during the step on chunk n,
-        // a step after it was loaded
-        o.dov = load_do(n > 0 ? n - 1 : 0);
     };
     auto stage_do = [&](const Vec4<T>& dv, int n) {
         if (drow < C) {
@@ -271,7 +380,6 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
             for (int x = 0; x < 4; ++x) sDOt[n & 1][dcol + x][drow] = ok ? dv.elem(x) : from_f32<T>(0.f);
         }
     };
-    // dO B fragments of chunk n from the staged copy
     auto do_frags = [&](F* dof, int n) {
 #pragma unroll
         for (int s = 0; s < G::NKC; ++s) {
@@ -292,53 +400,22 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
         }
     };
 
-    // L2 prefetch of chunk n - 3: the column slices of one (b, h) share one
-    // XCD's L2, so each workgroup loads every NS-th kilobyte of that chunk's
-    // P^T, Ktil, (Q*Gamma)^T, W^T (one 16-byte piece per lane and kilobyte).
-    // Ordinary loads, consumed into pf one step later (a dependence the
-    // compiler keeps; the value is only stored if T < 0, which never holds).
-    constexpr int PBYTES = (C * C + 3 * C * DK) * (int)sizeof(T);
-    constexpr int NPIECE = PBYTES / 1024;
-    const int per_wg = (NPIECE + NS - 1) / NS;
-    unsigned pf = 0;
-    uint4 pfv[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
-    auto prefetch = [&](int n) {
+    stage_do(load_do(NCs - 1), NCs - 1);
+    Vec4<T> dnext = load_do(max(NCs - 2, 0));        // dO of the next step's chunk
+    Ops cur;
+    lds_barrier();                                    // B0: step 0's chunk is in stage 0
+    read_ops(cur, stg(0));
+    lds_barrier();                                    // B1: stage 0 may be refilled
+    for (int i = 0; i < NCs; ++i) {
+        const int n = NCs - 1 - i;
         const size_t unit = sp.ubase + n;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int q = wave + 4 * i;
-            int p = slice + NS * q;
-            if (q >= per_wg || p >= NPIECE) p = slice % NPIECE;
-            const unsigned char* base;
-            int off = p * 1024;
-            if (off < C * C * (int)sizeof(T)) {
-                base = static_cast<const unsigned char*>(a.PT) + unit * C * C * sizeof(T);
-            } else {
-                off -= C * C * (int)sizeof(T);
-                const int blk = C * DK * (int)sizeof(T);
-                const void* arr = off < blk ? a.Ktil : (off < 2 * blk ? a.QGT : a.WT);
-                off %= blk;
-                base = static_cast<const unsigned char*>(arr) + unit * C * DK * sizeof(T);
-            }
-            pfv[i] = *reinterpret_cast<const uint4*>(base + off + 16 * lane);
-        }
-    };
-    auto consume = [&]() { pf ^= pfv[0].x ^ pfv[1].y; };
-
-    // one step of the reverse chain on chunk n with its operands o; the next
-    // chunk's dO piece (o.dov, loaded with these operands a step earlier) is
-    // staged before the step's second barrier
-    auto step = [&](const Ops& o, int n) {
-        const size_t unit = sp.ubase + n;
-        consume();
-        if (n >= 3) prefetch(n - 3);
         // the gradient of the state leaving chunk n (rows 0 .. DK-1 of sOut)
 #pragma unroll
         for (int u = 0; u < G::SPW; ++u) {
             const int t = wave + 4 * u;
             if (t < G::NT) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sOut[(16 * t + 4 * lg + i) * 16 + ln] = dS[u][i];
+                for (int x = 0; x < 4; ++x) sOut[(16 * t + 4 * lg + x) * 16 + ln] = dS[u][x];
             }
         }
         F sf[G::NKD], dof[G::NKC];
@@ -349,20 +426,21 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
         if (G::NM == 4 || wave < G::NM) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int s = 0; s < G::NKC; ++s) acc = mma(o.pt[s], dof[s], acc);
+            for (int s = 0; s < G::NKC; ++s) acc = mma(cur.pt[s], dof[s], acc);
 #pragma unroll
-            for (int s = 0; s < G::NKD; ++s) acc = mma(o.kt[s], sf[s], acc);
+            for (int s = 0; s < G::NKD; ++s) acc = mma(cur.kt[s], sf[s], acc);
             f32x4 neg;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                sOut[(DK + 16 * wave + 4 * lg + i) * 16 + ln] = acc[i];
-                neg[i] = -acc[i];
+            for (int x = 0; x < 4; ++x) {
+                sOut[(DK + 16 * wave + 4 * lg + x) * 16 + ln] = acc[x];
+                neg[x] = -acc[x];
             }
             put_tile<T, G::KB>(sXf, wave, lane, neg);
         }
-        __syncthreads();
-        // dSn [DK][16] and X [C][16] of this column slice to memory
-        for (int e = tid; e < (DK + C) * 4; e += kBwdThreads) {
+        lds_barrier();                                // barrier 1
+        // dSn [DK][16] and X [C][16] of this column slice to memory (written by
+        // the loader waves instead, between the barriers: no faster)
+        for (int e = tid; e < (DK + C) * 4; e += 256) {
             const int r = e >> 2, c4 = 4 * (e & 3);
             const float4 v = *reinterpret_cast<const float4*>(&sOut[r * 16 + c4]);
             float* dst = r < DK ? a.DSN + (unit * DK + r) * Dv + slice * 16 + c4
@@ -379,41 +457,31 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_chain_kernel(BwdChainArgs a)
             if (G::NT % 4 == 0 || t < G::NT) {
                 f32x4 acc;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = o.gc[u][i] * dS[u][i];
+                for (int x = 0; x < 4; ++x) acc[x] = cur.gc[u][x] * dS[u][x];
 #pragma unroll
-                for (int s = 0; s < G::NKC; ++s) acc = mma(o.qt[u][s], dof[s], acc);
+                for (int s = 0; s < G::NKC; ++s) acc = mma(cur.qt[u][s], dof[s], acc);
 #pragma unroll
-                for (int s = 0; s < G::NKC; ++s) acc = mma(o.wt[u][s], xf[s], acc);
+                for (int s = 0; s < G::NKC; ++s) acc = mma(cur.wt[u][s], xf[s], acc);
                 dS[u] = acc;
                 put_tile<T, G::KB>(sSf, t, lane, acc);
             }
         }
-        if (n >= 1) stage_do(o.dov, n - 1);
-        __syncthreads();
-    };
-
-    // two operand sets used in turn (no register copies between steps)
-    Ops A, B;
-    load_ops(A, NCs - 1);
-    stage_do(load_do(NCs - 1), NCs - 1);
-    __syncthreads();
-    for (int n = NCs - 1; n >= 0; n -= 2) {
-        if (n >= 1) load_ops(B, n - 1);
-        step(A, n);
-        if (n < 1) break;
-        if (n >= 2) load_ops(A, n - 2);
-        step(B, n - 1);
+        if (n >= 1) {
+            stage_do(dnext, n - 1);
+            dnext = load_do(max(n - 2, 0));
+        }
+        // the next step's operands (its loader waited for them before barrier 1)
+        read_ops(cur, stg(i + 1));
+        lds_barrier();                                // barrier 2
     }
-    consume();
-    if (a.T < 0) a.XB[lane] = __uint_as_float(pf);
     if (a.dS0) {
 #pragma unroll
         for (int u = 0; u < G::SPW; ++u) {
             const int t = wave + 4 * u;
             if (t < G::NT) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    a.dS0[((size_t)bh * DK + 16 * t + 4 * lg + i) * Dv + col] = dS[u][i];
+                for (int x = 0; x < 4; ++x)
+                    a.dS0[((size_t)bh * DK + 16 * t + 4 * lg + x) * Dv + col] = dS[u][x];
             }
         }
     }
@@ -1362,7 +1430,11 @@ hipError_t launch_bwd_t(int stage, const ChunkShape& s, const ChunkWorkspace& ws
     case 1: {
         const int bh = s.B * s.H;
         const unsigned grid = (unsigned)(kXcds * (s.Dv / 16) * ((bh + kXcds - 1) / kXcds));
-        return launch_kernel(bwd_chain_kernel<T, C, DK>, dim3(grid), dim3(kBwdThreads), 0, stream, ca);
+        using L = RevFifo<T, C, DK>;
+        auto kern = bwd_chain_fifo_kernel<T, C, DK>;
+        const hipError_t e = set_lds(kern, L::BYTES);
+        if (e != hipSuccess) return e;
+        return launch_kernel(kern, dim3(grid), dim3(kRevThreads), (uint32_t)L::BYTES, stream, ca);
     }
     case 2: {
         using G = LocalGeom<T, C, DK>;
