@@ -2,14 +2,16 @@
 
 Headline workload: KDA bf16 prefill, B=1 H=32 T=8192 d_k=d_v=128, chunk 64
 (seeded synthetic inputs resident in HBM before timing).  One step = one
-kda_chunk_forward_side call over the whole batch in the streamed form
-(KDA_FLAG_STREAMED: gate summary and intra-chunk WY on a second stream while
-the state propagation and outputs consume each chunk as it is formed).  Every
-call is launched on a non-default stream of ours.  Prints ONE JSON line.
+kda_chunk_forward call over the whole batch (the two-pass form: gate summary
+and intra-chunk WY for every chunk, then state propagation and outputs).  The
+streamed form (kda_chunk_forward_side with KDA_FLAG_STREAMED, the two running
+at once on two streams) takes the same time at this shape and is reported
+beside it (--streamed makes it the headline).  Every call is launched on a
+non-default stream of ours.  Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-others] [--no-cpu]
                   [--backward] [--decode] [--gate-prep] [--copy-probe] [--mfma-probe]
-                  [--two-pass]
+                  [--streamed]
 
 Timing: W untimed calls, then K calls back to back, each bracketed by HIP
 events on the launch stream; ms_per_step is the median call.  The roofline
@@ -350,10 +352,11 @@ def main():
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--mfma-probe", action="store_true",
                     help="also measure the dense MFMA peak rates (bf16 and fp32)")
-    ap.add_argument("--two-pass", action="store_true",
-                    help="time the two-pass kda_chunk_forward as the headline call (for rocprofv3 "
-                         "counter passes, which run one dispatch at a time: the streamed call's "
-                         "chain would wait out its bound for a prep grid that cannot start)")
+    ap.add_argument("--streamed", action="store_true",
+                    help="time the streamed kda_chunk_forward_side call as the headline (not "
+                         "under rocprofv3 counter passes, which run one dispatch at a time: the "
+                         "streamed call's chain would wait out its bound for a prep grid that "
+                         "cannot start)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -372,11 +375,11 @@ def main():
     # stream's work: the overlapped forms need a non-default launch stream)
     torch.cuda.set_stream(torch.cuda.Stream())
     side = kda.SideStream()
-    if args.two_pass:
-        ms, mean_ms, per, out, st = time_forward(kda, torch, w, inp, args.steps, args.warmup)
-    else:
+    if args.streamed:
         ms, mean_ms, per, out, st = time_forward(kda, torch, w, inp, args.steps, args.warmup,
                                                  extra_flags=kda.STREAMED, side=side)
+    else:
+        ms, mean_ms, per, out, st = time_forward(kda, torch, w, inp, args.steps, args.warmup)
     tokens = w.B * w.T
     io_bytes = 2
     ab = algorithmic_bytes(w, io_bytes, inp["S0"] is not None, True)
@@ -414,23 +417,25 @@ def main():
                      "traffic_ratio": (traffic_total / ab["path"]) if traffic_total else None,
                      "mfma_bf16_frac": chunk_flops(w) / (ms / 1e3) / 1e12 / MFMA_BF16_TFLOPS},
         "timing": {"median_ms": ms, "mean_ms": mean_ms, "calls": args.steps,
-                   "call": "kda_chunk_forward (two-pass)" if args.two_pass
-                           else "kda_chunk_forward_side, KDA_FLAG_STREAMED"},
+                   "call": "kda_chunk_forward_side, KDA_FLAG_STREAMED" if args.streamed
+                           else "kda_chunk_forward (two-pass)"},
         "kernels": kernels,
         "kernels_ms": per,
     }
     if not args.no_others:
         others = {}
-        # the same workload in the two-pass form (kda_chunk_forward: the prep
-        # kernels, then the chain)
-        ms1, _, per1, _, _ = time_forward(kda, torch, w, inp, max(20, args.steps // 4), 3)
+        # the same workload in the other form (streamed: the prep on a second
+        # stream while the chain consumes each chunk; or two-pass)
+        ms1, _, per1, _, _ = time_forward(kda, torch, w, inp, max(20, args.steps // 4), 3,
+                                          extra_flags=0 if args.streamed else kda.STREAMED,
+                                          side=None if args.streamed else side)
         tr1 = [measured_traffic(n) for n in per1 if n in KERNEL_SOURCES]
         tr1 = None if (not tr1 or None in tr1) else sum(tr1)
-        others["kda_bf16_prefill_two_pass"] = {"ms": ms1, "tokens_per_s": tokens / (ms1 / 1e3),
-                                               "path_hbm_frac": ab["path"] / (ms1 / 1e3) / 1e9 / HBM_PEAK_GBS,
-                                               "traffic_bytes": tr1,
-                                               "traffic_ratio": tr1 / ab["path"] if tr1 else None,
-                                               "kernels_ms": per1}
+        others["kda_bf16_prefill_two_pass" if args.streamed else "kda_bf16_prefill_streamed"] = {
+            "ms": ms1, "tokens_per_s": tokens / (ms1 / 1e3),
+            "path_hbm_frac": ab["path"] / (ms1 / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "traffic_bytes": tr1, "traffic_ratio": tr1 / ab["path"] if tr1 else None,
+            "kernels_ms": per1}
         for wid in (3, 1, 0):
             wo = workloads.workload(wid)
             io = workloads.make_prefill(wo, device="cuda")

@@ -209,7 +209,8 @@ def test_streamed_not_taken():
 
 def test_streamed_kda_bf16_prefill_full():
     """KDA bf16 prefill, B=1 H=32 T=8192 d=128 chunk=64 through the streamed
-    call (the form the benchmark times), every head against the oracle."""
+    call (the form the benchmark reports beside the two-pass headline), every
+    head against the oracle."""
     w = workloads.workload(2)
     say(f"[streamed] kda_bf16_prefill full {w}")
     inp = workloads.make_prefill(w, device=DEV)
