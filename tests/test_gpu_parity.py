@@ -384,7 +384,8 @@ def test_forward_segmented_chunk_states_and_phase():
 
 
 def test_forward_kda_bf16_prefill_full():
-    """KDA bf16 prefill, B=1 H=32 T=8192 d=128 chunk=64, every head."""
+    """KDA bf16 prefill, B=1 H=32 T=8192 d=128 chunk=64, every head, through
+    the two-pass call the benchmark times for its headline."""
     w = workloads.workload(2)
     say(f"[forward] kda_bf16_prefill full {w}")
     inp = workloads.make_prefill(w, device=DEV)
