@@ -217,8 +217,10 @@ bool stream_shape(int B, int H, int Dk, int Dv, int chunk, kda_dtype_t dtype)
 // allowed width whose estimated call is shortest, the call being about the
 // longer of the chain (NC steps of 1.3, 1.6 or 2.9 us at 1, 2 or 4 tiles
 // beside the prep grid) and the prep grid on the compute units the chain
-// leaves (9.4 us of one compute unit per unit, 13.4 with zero-segment
-// columns).  Measured (bf16, d = 128; ms per call, two-pass against
+// leaves (8.6 us of one compute unit per unit, 11.2 with zero-segment
+// columns: the prep's time on the whole GPU at H=32, T=8192 and at H=16,
+// T=65536 CKDA; with the earlier 9.4 / 13.4 the long-context call took two
+// tiles, 1.60 ms, against 1.51 at one).  Measured (bf16, d = 128; ms per call, two-pass against
 // streamed at 1 / 2 / 4 tiles): H=32, T=8192: 0.327 against gives up (the
 // chain fills every compute unit) / 0.318 / 0.395; H=16, T=8192: 0.237
 // against 0.187 / 0.225 / 0.289; H=16, T=65536 (CKDA): 1.84 in parts
@@ -235,7 +237,7 @@ int stream_tiles(int B, int H, int Dk, int Dv)
 int stream_pick_tiles(int B, int H, int Dk, int Dv, int NC, bool zero_cols, int ncu)
 {
     const long long chains = (long long)B * H * (Dv / 16);
-    const double units = (double)B * H * NC, unit_cu_us = zero_cols ? 13.4 : 9.4;
+    const double units = (double)B * H * NC, unit_cu_us = zero_cols ? 11.2 : 8.6;
     const int maxt = Dk == 128 ? 4 : 2;
     int best = stream_tiles(B, H, Dk, Dv);
     double best_t = 1e30;
