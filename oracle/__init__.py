@@ -62,6 +62,9 @@ def _load():
         lib.kda_oracle_backward.argtypes = [fp, fp, fp, fp, fp, fp, fp, fp, dp, dp, dp, dp, dp,
                                             dp, i, i, i, i, i, i]
         lib.kda_oracle_backward.restype = i
+        lib.kda_oracle_backward_phase.argtypes = [fp, fp, fp, fp, fp, fp, fp, fp, fp, dp, dp, dp,
+                                                  dp, dp, dp, dp, i, i, i, i, i, i]
+        lib.kda_oracle_backward_phase.restype = i
         lib.kda_oracle_backward_prologue.argtypes = [fp, fp, fp, fp, fp, fp, fp, fp, d, d, d, d, i,
                                                      dp, dp, dp, dp, dp, dp, i, i, i, i, i, i]
         lib.kda_oracle_backward_prologue.restype = i
@@ -202,6 +205,41 @@ def backward(q, k, v, alpha, beta, dO, S0=None, dST=None, nthreads: int | None =
         _ptr(r["dbeta"], dp), _ptr(r["dS0"], dp), B, T, H, Dk, Dv, nthreads or default_threads())
     if rc != 0:
         raise RuntimeError("kda_oracle_backward failed")
+    return r
+
+
+def backward_phase(q, k, v, alpha, theta, beta, dO, S0=None, dST=None,
+                   nthreads: int | None = None):
+    """Gradients of L = sum <out, dO> + <ST, dST> for the phase-variant forward
+    (forward_phase) with respect to q, k, v, alpha, theta, beta and S0; alpha,
+    theta and their gradients are [B,T,H,Dk/2].  Returns a dict of float64
+    arrays dq, dk, dv, dalpha, dtheta, dbeta, dS0."""
+    lib = _load()
+    q, k, v, a, th, beta, dO = (_f32(x) for x in (q, k, v, alpha, theta, beta, dO))
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    assert Dk % 2 == 0 and k.shape == q.shape
+    assert a.shape == (B, T, H, Dk // 2) and th.shape == a.shape
+    assert v.shape == (B, T, H, Dv) and beta.shape == (B, T, H) and dO.shape == v.shape
+    s0 = None if S0 is None else _f32(S0)
+    ds = None if dST is None else _f32(dST)
+    for x in (s0, ds):
+        if x is not None:
+            assert x.shape == (B, H, Dk, Dv)
+    r = {"dq": np.empty((B, T, H, Dk)), "dk": np.empty((B, T, H, Dk)),
+         "dv": np.empty((B, T, H, Dv)), "dalpha": np.empty((B, T, H, Dk // 2)),
+         "dtheta": np.empty((B, T, H, Dk // 2)), "dbeta": np.empty((B, T, H)),
+         "dS0": np.empty((B, H, Dk, Dv))}
+    dp = ctypes.c_double
+    rc = lib.kda_oracle_backward_phase(
+        _ptr(q, ctypes.c_float), _ptr(k, ctypes.c_float), _ptr(v, ctypes.c_float),
+        _ptr(a, ctypes.c_float), _ptr(th, ctypes.c_float), _ptr(beta, ctypes.c_float),
+        _ptr(s0, ctypes.c_float), _ptr(dO, ctypes.c_float), _ptr(ds, ctypes.c_float),
+        _ptr(r["dq"], dp), _ptr(r["dk"], dp), _ptr(r["dv"], dp), _ptr(r["dalpha"], dp),
+        _ptr(r["dtheta"], dp), _ptr(r["dbeta"], dp), _ptr(r["dS0"], dp), B, T, H, Dk, Dv,
+        nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError("kda_oracle_backward_phase failed")
     return r
 
 

@@ -300,18 +300,50 @@ static void store_token_grads(const struct prologue* pro, const float* q, const 
  *                                 dSt  = G - beta_t k_t y^T
  *   St = diag(alpha_t) S_{t-1} -> dalpha_t[c] = <dSt[c,:], S_{t-1}[c,:]>,
  *                                 G_{t-1} = diag(alpha_t) dSt
- * and dS0 is the last G.  The states S_{t-1} are recomputed forward from
- * checkpoints taken every 64 tokens (the same forward arithmetic).
+ * and dS0 is the last G.  With theta (the phase variant, §3 eq. (13)) the
+ * decay of the row pair (2p, 2p+1) is the block alpha_p R(theta_p); with
+ * (x, y) that pair of S_{t-1}, (gx, gy) the same rows of dSt, c = cos theta_p,
+ * s = sin theta_p:
+ *   St = alpha_p [c x - s y ; s x + c y]
+ *     -> dalpha_p = <gx, c x - s y> + <gy, s x + c y>,
+ *        dtheta_p = alpha_p (<gx, -s x - c y> + <gy, c x - s y>),
+ *        G_{t-1} = alpha_p R(theta_p)^T dSt = alpha_p [c gx + s gy ; -s gx + c gy].
+ * The states S_{t-1} are recomputed forward from checkpoints taken every 64
+ * tokens (the same forward arithmetic).
  */
+static void decay_copy(double* St, const double* Sp, const double* ad, const double* td, int Dk,
+                       int Dv)
+{
+    if (!td) {
+        for (int c = 0; c < Dk; ++c)
+            for (int j = 0; j < Dv; ++j) St[(size_t)c * Dv + j] = ad[c] * Sp[(size_t)c * Dv + j];
+        return;
+    }
+    for (int p = 0; p < Dk / 2; ++p) {
+        const double c = ad[p] * cos(td[p]), sn = ad[p] * sin(td[p]);
+        const double* x = Sp + (size_t)(2 * p) * Dv;
+        const double* y = x + Dv;
+        double* r0 = St + (size_t)(2 * p) * Dv;
+        double* r1 = r0 + Dv;
+        for (int j = 0; j < Dv; ++j) {
+            r0[j] = c * x[j] - sn * y[j];
+            r1[j] = sn * x[j] + c * y[j];
+        }
+    }
+}
+
 static int backward_impl(const struct prologue* pro, const float* q, const float* k,
-                         const float* v, const float* alpha, const float* beta, const float* S0,
-                         const float* dO, const float* dST, double* dq, double* dk, double* dv,
-                         double* dalpha, double* dbeta, double* dS0, int B, int T, int H, int Dk,
-                         int Dv, int nthreads)
+                         const float* v, const float* alpha, const float* theta,
+                         const float* beta, const float* S0, const float* dO, const float* dST,
+                         double* dq, double* dk, double* dv, double* dalpha, double* dtheta,
+                         double* dbeta, double* dS0, int B, int T, int H, int Dk, int Dv,
+                         int nthreads)
 {
     if (!q || !k || !v || !alpha || !beta || !dO || !dq || !dk || !dv || !dalpha || !dbeta)
         return -1;
     if (B < 0 || T < 0 || H < 0 || Dk <= 0 || Dv <= 0) return -1;
+    if (theta && (Dk % 2 != 0 || pro || !dtheta)) return -1;
+    const int na = theta ? Dk / 2 : Dk;      /* gates per token */
     const int K = 64;
     const long nseg = (T + K - 1) / K;
     const size_t SZ = (size_t)Dk * Dv;
@@ -324,8 +356,8 @@ static int backward_impl(const struct prologue* pro, const float* q, const float
         const int b = (int)(bh / H), h = (int)(bh % H);
         /* checkpoints [nseg][SZ], states of one segment [K + 1][SZ], G, dSt,
          * and per-token vectors */
-        const size_t nd = (size_t)(nseg > 0 ? nseg : 1) * SZ + (size_t)(K + 1) * SZ + 2 * SZ +
-                          5 * (size_t)Dv + 6 * (size_t)Dk;
+        const size_t nd = (size_t)(nseg > 0 ? nseg : 1) * SZ + (size_t)(K + 1) * SZ + 3 * SZ +
+                          5 * (size_t)Dv + 8 * (size_t)Dk;
         double* ck = (double*)malloc(sizeof(double) * nd);
         if (!ck) {
 #pragma omp atomic write
@@ -335,7 +367,8 @@ static int backward_impl(const struct prologue* pro, const float* q, const float
         double* buf = ck + (size_t)(nseg > 0 ? nseg : 1) * SZ;
         double* G = buf + (size_t)(K + 1) * SZ;
         double* dSt = G + SZ;
-        double* pred = dSt + SZ;
+        double* St = dSt + SZ;      /* the decayed state of the token */
+        double* pred = St + SZ;
         double* vd = pred + Dv;
         double* u = vd + Dv;
         double* y = u + Dv;
@@ -346,6 +379,8 @@ static int backward_impl(const struct prologue* pro, const float* q, const float
         double* dqt = ad + Dk;      /* this token's gradients of q, k, alpha as used */
         double* dkt = dqt + Dk;
         double* dat = dkt + Dk;
+        double* td = dat + Dk;      /* phases of the token, and their gradients */
+        double* dtt = td + Dk;
 
         /* forward: checkpoint the state before tokens 0, K, 2K, ... */
         double* S = buf;
@@ -359,8 +394,10 @@ static int backward_impl(const struct prologue* pro, const float* q, const float
             const size_t tok = ((size_t)b * T + t) * H + h;
             if (t % K == 0) memcpy(ck + (size_t)(t / K) * SZ, S, sizeof(double) * SZ);
             const double bt = load_token(pro, q + tok * Dk, k + tok * Dk, v + tok * Dv,
-                                         alpha + tok * Dk, beta[tok], qd, kd, vd, ad, Dk, Dv, Dk);
-            token_update(S, qd, kd, vd, ad, NULL, bt, NULL, Dk, Dv, pred);
+                                         alpha + tok * na, beta[tok], qd, kd, vd, ad, Dk, Dv, na);
+            if (theta)
+                for (int p = 0; p < na; ++p) td[p] = (double)theta[tok * na + p];
+            token_update(S, qd, kd, vd, ad, theta ? td : NULL, bt, NULL, Dk, Dv, pred);
         }
 
         /* backward */
@@ -379,15 +416,20 @@ static int backward_impl(const struct prologue* pro, const float* q, const float
                 double* nx = buf + (size_t)(t - a + 1) * SZ;
                 memcpy(nx, buf + (size_t)(t - a) * SZ, sizeof(double) * SZ);
                 const double bt = load_token(pro, q + tok * Dk, k + tok * Dk, v + tok * Dv,
-                                             alpha + tok * Dk, beta[tok], qd, kd, vd, ad, Dk, Dv, Dk);
-                token_update(nx, qd, kd, vd, ad, NULL, bt, NULL, Dk, Dv, pred);
+                                             alpha + tok * na, beta[tok], qd, kd, vd, ad, Dk, Dv, na);
+                if (theta)
+                    for (int p = 0; p < na; ++p) td[p] = (double)theta[tok * na + p];
+                token_update(nx, qd, kd, vd, ad, theta ? td : NULL, bt, NULL, Dk, Dv, pred);
             }
             for (int t = e_ - 1; t >= a; --t) {
                 const size_t tok = ((size_t)b * T + t) * H + h;
                 const double* Sp = buf + (size_t)(t - a) * SZ;       /* S_{t-1} */
                 const double* Sn = Sp + SZ;                          /* S_t */
                 const double bt = load_token(pro, q + tok * Dk, k + tok * Dk, v + tok * Dv,
-                                             alpha + tok * Dk, beta[tok], qd, kd, vd, ad, Dk, Dv, Dk);
+                                             alpha + tok * na, beta[tok], qd, kd, vd, ad, Dk, Dv, na);
+                if (theta)
+                    for (int p = 0; p < na; ++p) td[p] = (double)theta[tok * na + p];
+                decay_copy(St, Sp, ad, theta ? td : NULL, Dk, Dv);
                 for (int j = 0; j < Dv; ++j) dod[j] = (double)dO[tok * Dv + j];
                 /* read-out o_t = S_t^T q_t */
                 for (int c = 0; c < Dk; ++c) {
@@ -396,11 +438,11 @@ static int backward_impl(const struct prologue* pro, const float* q, const float
                     dqt[c] = s;
                     for (int j = 0; j < Dv; ++j) G[(size_t)c * Dv + j] += qd[c] * dod[j];
                 }
-                /* delta correction of St = diag(alpha) S_{t-1} */
+                /* delta correction of the decayed state St */
                 for (int j = 0; j < Dv; ++j) {
                     double p = 0.0, yy = 0.0;
                     for (int c = 0; c < Dk; ++c) {
-                        p += kd[c] * ad[c] * Sp[(size_t)c * Dv + j];
+                        p += kd[c] * St[(size_t)c * Dv + j];
                         yy += G[(size_t)c * Dv + j] * kd[c];
                     }
                     u[j] = vd[j] - p;
@@ -415,23 +457,56 @@ static int backward_impl(const struct prologue* pro, const float* q, const float
                     double s1 = 0.0, s2 = 0.0;
                     for (int j = 0; j < Dv; ++j) {
                         s1 += G[(size_t)c * Dv + j] * bt * u[j];
-                        s2 += ad[c] * Sp[(size_t)c * Dv + j] * y[j];
+                        s2 += St[(size_t)c * Dv + j] * y[j];
                     }
                     dkt[c] = s1 - bt * s2;
                 }
                 for (int c = 0; c < Dk; ++c)
                     for (int j = 0; j < Dv; ++j)
                         dSt[(size_t)c * Dv + j] = G[(size_t)c * Dv + j] - bt * kd[c] * y[j];
-                /* decay: St = diag(alpha) S_{t-1} */
-                for (int c = 0; c < Dk; ++c) {
-                    double s = 0.0;
-                    for (int j = 0; j < Dv; ++j) s += dSt[(size_t)c * Dv + j] * Sp[(size_t)c * Dv + j];
-                    dat[c] = s;
-                    for (int j = 0; j < Dv; ++j) G[(size_t)c * Dv + j] = ad[c] * dSt[(size_t)c * Dv + j];
+                if (!theta) {
+                    /* decay: St = diag(alpha) S_{t-1} */
+                    for (int c = 0; c < Dk; ++c) {
+                        double s = 0.0;
+                        for (int j = 0; j < Dv; ++j) s += dSt[(size_t)c * Dv + j] * Sp[(size_t)c * Dv + j];
+                        dat[c] = s;
+                        for (int j = 0; j < Dv; ++j) G[(size_t)c * Dv + j] = ad[c] * dSt[(size_t)c * Dv + j];
+                    }
+                    store_token_grads(pro, q + tok * Dk, k + tok * Dk, alpha + tok * Dk, beta[tok],
+                                      qd, kd, dqt, dkt, dat, db, dq + tok * Dk, dk + tok * Dk,
+                                      dalpha + tok * Dk, dbeta + tok, Dk);
+                    continue;
                 }
-                store_token_grads(pro, q + tok * Dk, k + tok * Dk, alpha + tok * Dk, beta[tok],
-                                  qd, kd, dqt, dkt, dat, db, dq + tok * Dk, dk + tok * Dk,
-                                  dalpha + tok * Dk, dbeta + tok, Dk);
+                /* decay: the rows (2p, 2p+1) of St are alpha_p R(theta_p) of those of S_{t-1} */
+                for (int p = 0; p < na; ++p) {
+                    const double c = cos(td[p]), sn = sin(td[p]);
+                    const double* x = Sp + (size_t)(2 * p) * Dv;
+                    const double* yv = x + Dv;
+                    double* gx = dSt + (size_t)(2 * p) * Dv;
+                    double* gy = gx + Dv;
+                    double da = 0.0, dth = 0.0;
+                    for (int j = 0; j < Dv; ++j) {
+                        da += gx[j] * (c * x[j] - sn * yv[j]) + gy[j] * (sn * x[j] + c * yv[j]);
+                        dth += gx[j] * (-sn * x[j] - c * yv[j]) + gy[j] * (c * x[j] - sn * yv[j]);
+                    }
+                    dat[p] = da;
+                    dtt[p] = ad[p] * dth;
+                    double* G0 = G + (size_t)(2 * p) * Dv;
+                    double* G1 = G0 + Dv;
+                    for (int j = 0; j < Dv; ++j) {
+                        G0[j] = ad[p] * (c * gx[j] + sn * gy[j]);
+                        G1[j] = ad[p] * (-sn * gx[j] + c * gy[j]);
+                    }
+                }
+                for (int c = 0; c < Dk; ++c) {
+                    dq[tok * Dk + c] = dqt[c];
+                    dk[tok * Dk + c] = dkt[c];
+                }
+                for (int p = 0; p < na; ++p) {
+                    dalpha[tok * na + p] = dat[p];
+                    dtheta[tok * na + p] = dtt[p];
+                }
+                dbeta[tok] = db;
             }
         }
         if (dS0) memcpy(dS0 + (size_t)bh * SZ, G, sizeof(double) * SZ);
@@ -445,8 +520,19 @@ int kda_oracle_backward(const float* q, const float* k, const float* v, const fl
                         double* dq, double* dk, double* dv, double* dalpha, double* dbeta,
                         double* dS0, int B, int T, int H, int Dk, int Dv, int nthreads)
 {
-    return backward_impl(NULL, q, k, v, alpha, beta, S0, dO, dST, dq, dk, dv, dalpha, dbeta, dS0,
-                         B, T, H, Dk, Dv, nthreads);
+    return backward_impl(NULL, q, k, v, alpha, NULL, beta, S0, dO, dST, dq, dk, dv, dalpha, NULL,
+                         dbeta, dS0, B, T, H, Dk, Dv, nthreads);
+}
+
+int kda_oracle_backward_phase(const float* q, const float* k, const float* v, const float* alpha,
+                              const float* theta, const float* beta, const float* S0,
+                              const float* dO, const float* dST, double* dq, double* dk,
+                              double* dv, double* dalpha, double* dtheta, double* dbeta,
+                              double* dS0, int B, int T, int H, int Dk, int Dv, int nthreads)
+{
+    if (!theta) return -1;
+    return backward_impl(NULL, q, k, v, alpha, theta, beta, S0, dO, dST, dq, dk, dv, dalpha,
+                         dtheta, dbeta, dS0, B, T, H, Dk, Dv, nthreads);
 }
 
 int kda_oracle_backward_prologue(const float* q_raw, const float* k_raw, const float* v,
@@ -458,8 +544,8 @@ int kda_oracle_backward_prologue(const float* q_raw, const float* k_raw, const f
 {
     if (!(eps >= 0.0)) return -1;
     const struct prologue pro = {amin, amax, bmax, eps, normalize_q};
-    return backward_impl(&pro, q_raw, k_raw, v, gate, beta_logit, S0, dO, dST, dq_raw, dk_raw, dv,
-                         dgate, dbeta_logit, dS0, B, T, H, Dk, Dv, nthreads);
+    return backward_impl(&pro, q_raw, k_raw, v, gate, NULL, beta_logit, S0, dO, dST, dq_raw,
+                         dk_raw, dv, dgate, NULL, dbeta_logit, dS0, B, T, H, Dk, Dv, nthreads);
 }
 
 int kda_oracle_decode(const float* q, const float* k, const float* v,

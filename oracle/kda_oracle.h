@@ -79,6 +79,17 @@ int kda_oracle_backward(const float* q, const float* k, const float* v, const fl
                         double* dq, double* dk, double* dv, double* dalpha, double* dbeta,
                         double* dS0, int B, int T, int H, int Dk, int Dv, int nthreads);
 
+/* The same gradients for the phase variant (kda_oracle_forward_phase,
+ * "Semidirect Fourier Delta Attention" §3 eq. (13)): alpha, theta, dalpha and
+ * dtheta are [B, T, H, Dk/2], one decay and one phase per channel pair; every
+ * other layout as kda_oracle_backward.  The decay step's gradients take the
+ * 2x2 block alpha_p R(theta_p) in place of the diagonal. */
+int kda_oracle_backward_phase(const float* q, const float* k, const float* v, const float* alpha,
+                              const float* theta, const float* beta, const float* S0,
+                              const float* dO, const float* dST, double* dq, double* dk,
+                              double* dv, double* dalpha, double* dtheta, double* dbeta,
+                              double* dS0, int B, int T, int H, int Dk, int Dv, int nthreads);
+
 /* The same gradients for the forward from raw inputs
  * (kda_oracle_forward_prologue): with respect to q_raw, k_raw, v, the gate
  * logits, the beta logits and S0, by the chain rule through eqs. (15), (17)

@@ -209,3 +209,124 @@ def test_backward_prologue_key_gradient_is_tangent(oracle_lib):
         dots = np.sum(g[gr] * x[raw], axis=-1)
         scale = np.abs(g[gr]).max() * np.abs(x[raw]).max()
         assert np.abs(dots).max() <= 1e-12 * scale * x[raw].shape[-1]
+
+
+# ---- backward of the phase variant ("Semidirect Fourier Delta Attention" §3
+# eq. (13): the decay of channel pair p is alpha_p R(theta_p)) -------------------
+
+def _phase(seed, T=6, H=2, Dk=4, Dv=3):
+    rng = np.random.default_rng(seed)
+    P = Dk // 2
+    q = _grid(rng.uniform(-1.5, 1.5, (1, T, H, Dk)))
+    k = rng.standard_normal((1, T, H, Dk))
+    k = _grid(k / np.linalg.norm(k, axis=-1, keepdims=True))
+    x = dict(q=q, k=k, v=_grid(rng.uniform(-1.5, 1.5, (1, T, H, Dv))),
+             alpha=_grid(rng.uniform(-1, 1, (1, T, H, P))),
+             theta=_grid(rng.uniform(-np.pi, np.pi, (1, T, H, P))),
+             beta=_grid(rng.uniform(0, 2, (1, T, H))), S0=_grid(rng.uniform(-1, 1, (1, H, Dk, Dv))))
+    return x, _grid(rng.uniform(-1, 1, (1, T, H, Dv))), _grid(rng.uniform(-1, 1, (1, H, Dk, Dv)))
+
+
+def _loss_phase(oracle_lib, x, dO, dST):
+    out, ST = oracle_lib.forward_phase(x["q"], x["k"], x["v"], x["alpha"], x["theta"], x["beta"],
+                                       x["S0"], nthreads=1)
+    return float(np.sum(out * dO) + np.sum(ST * dST))
+
+
+@pytest.mark.parametrize("seed", [31, 32])
+def test_backward_phase_matches_differences(oracle_lib, seed):
+    """Every gradient of the phase variant against central differences of its
+    forward: exact two-point differences for q, k, v, alpha, beta, S0 (L is a
+    polynomial of degree at most two in each of them, the inputs lie on a 2^-12
+    grid), a 4-point difference (error O(h^4), h = 2^-7) for theta, which
+    enters through cos and sin."""
+    x, dO, dST = _phase(seed)
+    g = oracle_lib.backward_phase(x["q"], x["k"], x["v"], x["alpha"], x["theta"], x["beta"], dO,
+                                  x["S0"], dST, nthreads=1)
+    names = {"q": "dq", "k": "dk", "v": "dv", "alpha": "dalpha", "theta": "dtheta",
+             "beta": "dbeta", "S0": "dS0"}
+    for name, gname in names.items():
+        h, steps = (2.0 ** -7, (2, 1, -1, -2)) if name == "theta" else (H_STEP, (1, -1))
+        for idx in np.ndindex(x[name].shape):
+            vals = []
+            for m in steps:
+                xp = {n: a.copy() for n, a in x.items()}
+                xp[name][idx] += m * h
+                vals.append(_loss_phase(oracle_lib, xp, dO, dST))
+            if name == "theta":
+                fd = (-vals[0] + 8 * vals[1] - 8 * vals[2] + vals[3]) / (12 * h)
+                tol = 2e-6 * (1 + abs(fd))
+            else:
+                fd = (vals[0] - vals[1]) / (2 * h)
+                tol = 1e-9 * (1 + abs(fd))
+            assert abs(fd - g[gname][idx]) <= tol, (name, idx, fd, g[gname][idx])
+
+
+def test_backward_phase_zero_is_kda(oracle_lib):
+    """theta = 0: the plain backward with each pair's decay on both of its
+    channels; the pair's alpha gradient is the sum of the two channels'."""
+    x, dO, dST = _phase(33, T=9, H=2, Dk=6, Dv=4)
+    x["theta"][:] = 0.0
+    g = oracle_lib.backward_phase(x["q"], x["k"], x["v"], x["alpha"], x["theta"], x["beta"], dO,
+                                  x["S0"], dST)
+    a2 = np.repeat(x["alpha"], 2, axis=-1)
+    r = oracle_lib.backward(x["q"], x["k"], x["v"], a2, x["beta"], dO, x["S0"], dST)
+    for n in ("dq", "dk", "dv", "dbeta", "dS0"):
+        np.testing.assert_allclose(g[n], r[n], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(g["dalpha"], r["dalpha"][..., 0::2] + r["dalpha"][..., 1::2],
+                               rtol=1e-12, atol=1e-12)
+
+
+def _rotate_pairs(x, phi):
+    """Rotate every channel pair (2p, 2p+1) of x [..., Dk] by phi [..., Dk/2]."""
+    c, s = np.cos(phi), np.sin(phi)
+    a, b = x[..., 0::2], x[..., 1::2]
+    y = np.empty_like(x)
+    y[..., 0::2] = c * a - s * b
+    y[..., 1::2] = s * a + c * b
+    return y
+
+
+def test_backward_phase_by_rotated_inputs(oracle_lib):
+    """The phase variant is the plain recurrence on q, k rotated by minus the
+    running phase phi_t = theta_1 + ... + theta_t, with each pair's decay on
+    both channels, and its final state rotated by phi_T.  So the gradients
+    follow from the plain backward on those inputs: dq_t, dk_t rotated back by
+    phi_t, the alpha gradients of a pair summed, and dtheta_s the sum over
+    t >= s of d L / d phi_t, where d L / d phi_t = <dq'_t, -J q'_t> +
+    <dk'_t, -J k'_t> (+ <dS_T, J S_T> at the last token), J the rotation by a
+    right angle."""
+    x, dO, dST = _phase(34, T=11, H=2, Dk=6, Dv=4)
+    g = oracle_lib.backward_phase(x["q"], x["k"], x["v"], x["alpha"], x["theta"], x["beta"], dO,
+                                  x["S0"], dST)
+    phi = np.cumsum(x["theta"].astype(np.float64), axis=1)
+    qr, kr = _rotate_pairs(x["q"], -phi), _rotate_pairs(x["k"], -phi)
+    a2 = np.repeat(x["alpha"], 2, axis=-1)
+    # the plain oracle takes fp32 inputs: compare in double through the exact
+    # identity at the level of the rounded rotated inputs
+    qr32, kr32 = qr.astype(np.float32).astype(np.float64), kr.astype(np.float32).astype(np.float64)
+    out, STr = oracle_lib.forward(qr32, kr32, x["v"], a2, x["beta"], x["S0"])
+    out_p, ST_p = oracle_lib.forward_phase(x["q"], x["k"], x["v"], x["alpha"], x["theta"],
+                                           x["beta"], x["S0"])
+    np.testing.assert_allclose(out, out_p, rtol=0, atol=1e-5)
+    phiT = phi[:, -1]                                   # [1, H, P]
+    ST_rot = np.swapaxes(_rotate_pairs(np.swapaxes(STr, -1, -2), phiT[:, :, None, :]), -1, -2)
+    np.testing.assert_allclose(ST_rot, ST_p, rtol=0, atol=1e-5)
+    dSTr = np.swapaxes(_rotate_pairs(np.swapaxes(dST, -1, -2), -phiT[:, :, None, :]), -1, -2)
+    r = oracle_lib.backward(qr32, kr32, x["v"], a2, x["beta"], dO, x["S0"], dSTr)
+    tol = dict(rtol=0, atol=1e-4)
+    np.testing.assert_allclose(_rotate_pairs(r["dq"], phi), g["dq"], **tol)
+    np.testing.assert_allclose(_rotate_pairs(r["dk"], phi), g["dk"], **tol)
+    for n in ("dv", "dbeta", "dS0"):
+        np.testing.assert_allclose(r[n], g[n], **tol)
+    np.testing.assert_allclose(r["dalpha"][..., 0::2] + r["dalpha"][..., 1::2], g["dalpha"], **tol)
+
+    def perp(d, u):        # <d, -J u> per pair = d_0 u_1 - d_1 u_0
+        return d[..., 0::2] * u[..., 1::2] - d[..., 1::2] * u[..., 0::2]
+
+    gphi = perp(r["dq"], qr32) + perp(r["dk"], kr32)
+    # <dS'_T, J S'_T> per pair, summed over the value columns
+    gphi[:, -1] += np.sum(dSTr[:, :, 1::2, :] * STr[:, :, 0::2, :]
+                          - dSTr[:, :, 0::2, :] * STr[:, :, 1::2, :], axis=-1)
+    dtheta = np.flip(np.cumsum(np.flip(gphi, axis=1), axis=1), axis=1)
+    np.testing.assert_allclose(dtheta, g["dtheta"], **tol)
