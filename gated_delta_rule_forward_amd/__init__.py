@@ -19,7 +19,8 @@ import torch
 
 __all__ = [
     "KDA", "CKDA", "KdaError", "library_path", "load", "abi_version", "workspace_size",
-    "chunk_forward_save", "chunk_backward_saved",
+    "chunk_forward_save", "chunk_backward_saved", "chunk_backward_phase",
+    "backward_phase_workspace_size",
     "chunk_forward_noalloc", "NOALLOC_SCRATCH_BYTES", "SideStream", "SIDE_EVENTS",
     "chunk_forward", "chunk_forward_prologue", "chunk_forward_varlen", "chunk_forward_phase",
     "decode_step", "decode_step_phase", "decode_step_prologue", "gate_prep", "last_stage_times",
@@ -144,6 +145,11 @@ def load():
     lib.kda_chunk_backward_workspace_size.restype = i
     lib.kda_chunk_backward.argtypes = [vp] * 14 + [i] * 8 + [u, vp, sz, vp]
     lib.kda_chunk_backward.restype = i
+    lib.kda_chunk_backward_phase_workspace_size.argtypes = [i, i, i, i, i, i, i,
+                                                            ctypes.POINTER(sz)]
+    lib.kda_chunk_backward_phase_workspace_size.restype = i
+    lib.kda_chunk_backward_phase.argtypes = [vp] * 16 + [i] * 8 + [u, vp, sz, vp]
+    lib.kda_chunk_backward_phase.restype = i
     lib.kda_chunk_forward_save.argtypes = [vp] * 8 + [i] * 8 + [u, vp, sz, vp]
     lib.kda_chunk_forward_save.restype = i
     lib.kda_chunk_backward_saved.argtypes = [vp] * 13 + [i] * 8 + [u, vp, sz, vp]
@@ -488,6 +494,57 @@ def chunk_backward(q, k, v, alpha, beta, d_out, initial_state=None, d_final_stat
                                 B, T, H, Dk, Dv, chunk, _DT[q.dtype], mode, flags,
                                 _ptr(workspace), wsb, _stream(stream))
     _check("kda_chunk_backward", st)
+    return g
+
+
+def backward_phase_workspace_size(B: int, T: int, H: int, Dk: int, Dv: int, chunk: int,
+                                  dtype: torch.dtype) -> int:
+    lib = load()
+    n = ctypes.c_size_t(0)
+    st = lib.kda_chunk_backward_phase_workspace_size(B, T, H, Dk, Dv, chunk, _DT[dtype],
+                                                     ctypes.byref(n))
+    _check("kda_chunk_backward_phase_workspace_size", st)
+    return n.value
+
+
+def chunk_backward_phase(q, k, v, alpha, theta, beta, d_out, initial_state=None,
+                         d_final_state=None, *, chunk: int = 64, mode: int = CKDA,
+                         want_d_initial_state: bool = True, grads=None, workspace=None,
+                         stream=None, flags: int = 0):
+    """Backward of chunk_forward_phase (kda_chunk_backward_phase): gradients
+    with respect to q, k, v, alpha, theta ([B,T,H,Dk/2]), beta and
+    initial_state.  Returns a dict dq, dk, dv (q's dtype), d_alpha, d_theta,
+    d_beta, d_initial_state (fp32; None unless wanted)."""
+    lib = load()
+    B, T, H, Dk = q.shape
+    Dv = v.shape[-1]
+    dev = q.device
+    g = dict(grads or {})
+    g.setdefault("dq", torch.empty((B, T, H, Dk), dtype=q.dtype, device=dev))
+    g.setdefault("dk", torch.empty((B, T, H, Dk), dtype=q.dtype, device=dev))
+    g.setdefault("dv", torch.empty((B, T, H, Dv), dtype=q.dtype, device=dev))
+    g.setdefault("d_alpha", torch.empty((B, T, H, Dk // 2), dtype=torch.float32, device=dev))
+    g.setdefault("d_theta", torch.empty((B, T, H, Dk // 2), dtype=torch.float32, device=dev))
+    g.setdefault("d_beta", torch.empty((B, T, H), dtype=torch.float32, device=dev))
+    if want_d_initial_state:
+        g.setdefault("d_initial_state", torch.empty((B, H, Dk, Dv), dtype=torch.float32, device=dev))
+    else:
+        g["d_initial_state"] = None
+    if workspace is None:
+        nbytes = backward_phase_workspace_size(B, T, H, Dk, Dv, chunk, q.dtype)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    _dev(q, k, v, alpha, theta, beta, d_out, initial_state, d_final_state, workspace, *g.values())
+    if q.dtype not in _DT or k.dtype != q.dtype or v.dtype != q.dtype or d_out.dtype != q.dtype:
+        raise ValueError("q, k, v and d_out must share one dtype (float32 or bfloat16)")
+    wsb = workspace.numel() * workspace.element_size()
+    st = lib.kda_chunk_backward_phase(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(theta),
+                                      _ptr(beta), _ptr(initial_state), _ptr(d_out),
+                                      _ptr(d_final_state), _ptr(g["dq"]), _ptr(g["dk"]),
+                                      _ptr(g["dv"]), _ptr(g["d_alpha"]), _ptr(g["d_theta"]),
+                                      _ptr(g["d_beta"]), _ptr(g["d_initial_state"]),
+                                      B, T, H, Dk, Dv, chunk, _DT[q.dtype], mode, flags,
+                                      _ptr(workspace), wsb, _stream(stream))
+    _check("kda_chunk_backward_phase", st)
     return g
 
 

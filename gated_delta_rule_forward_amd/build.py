@@ -18,7 +18,7 @@ LIB = os.path.join(HERE, "libkda.so")
 PROBE_LIB = os.path.join(HERE, "libkda_probe.so")
 PROBE_SOURCE = "probe.hip"
 SOURCES = ["decode.hip", "gate_prep.hip", "prep_fast.hip", "prep_exact.hip", "chain.hip", "chain_wide.hip",
-           "chunk_util.hip", "bwd.hip", "range_check.hip", "kda_api.hip"]
+           "chunk_util.hip", "bwd.hip", "phase_bwd.hip", "range_check.hip", "kda_api.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops off: packed fp32 VALU forms are not emitted (the host pass

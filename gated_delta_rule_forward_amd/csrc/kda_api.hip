@@ -881,10 +881,10 @@ kda_status_t backward_enqueue(const void* q, const void* k, const void* v, const
                       0, sh.NC, 1, nullptr, nullptr};
     ca.CS32 = CS32;
     ca.DL = DL;
-    if (part == BwdPart::SAVE) {
-        ca.out = out;
-        ca.ST = final_state;
-    }
+    // the chain's final state (S_T of the saving forward, or of the rotated
+    // recurrence for the phase variant's backward)
+    ca.ST = final_state;
+    if (part == BwdPart::SAVE) ca.out = out;
     const kda::BwdChainArgs ra{ws.Kt, ws.P, ws.QG, ws.W, ws.GC, d_out, d_final_state,
                                d_initial_state, DSN, XB, B, T, H, Dv, sh.NC, cu_s, cs};
     const kda::BwdLocalArgs la{q, k, v, alpha, beta, d_out, Tm, CS32, DL, DSN, XB,
@@ -1112,6 +1112,123 @@ kda_status_t chunk_backward_varlen(const void* q, const void* k, const void* v, 
     return backward_enqueue(q, k, v, alpha, beta, initial_state, d_out, d_final_state, dq, dk, dv,
                             d_alpha, d_beta, d_initial_state, N, total_T, H, Dk, Dv, chunk, dtype,
                             mode, workspace, rec, s, total_T > 0 ? cu_seqlens : nullptr);
+}
+
+// the backward of the phase variant: workspace = the backward's, then the
+// rotated q', k' (io type), the per-channel gates alpha' (fp32), the plain
+// backward's dq', dk' (io type) and dalpha' (fp32), the two per-block tables
+// (fp64), dS'_T and S'_T (fp32) and the final-state term of d L / d phi
+size_t backward_phase_layout(int B, int T, int H, int Dk, int Dv, int chunk, IoType io,
+                             size_t xo[11])
+{
+    size_t off[kda::kWorkspaceRegions], boff[kBwdRegions];
+    size_t n = backward_layout(B, T, H, Dk, Dv, chunk, io, off, boff);
+    const size_t ntok = (size_t)B * T * H, e = io == IoType::F32 ? 4 : 2;
+    const size_t tab = (size_t)B * H * (kda::phase_blocks(T) + 1) * (Dk / 2) * 8;
+    const size_t st = (size_t)B * H * Dk * Dv * 4;
+    const size_t sz[11] = {ntok * Dk * e, ntok * Dk * e, ntok * Dk * 4, ntok * Dk * e,
+                           ntok * Dk * e, ntok * Dk * 4, tab, tab, st, st,
+                           (size_t)B * H * (Dk / 2) * 4};
+    for (int i = 0; i < 11; ++i) {
+        xo[i] = n;
+        n += (sz[i] + 255) & ~size_t(255);
+    }
+    return n;
+}
+
+// kda_chunk_backward_phase: the phase variant's backward as the plain backward
+// of the rotated recurrence (phase_bwd.hip states the reduction)
+kda_status_t chunk_backward_phase(const void* q, const void* k, const void* v, const float* alpha,
+                                  const float* theta, const float* beta,
+                                  const float* initial_state, const void* d_out,
+                                  const float* d_final_state, void* dq, void* dk, void* dv,
+                                  float* d_alpha, float* d_theta, float* d_beta,
+                                  float* d_initial_state, int B, int T, int H, int Dk, int Dv,
+                                  int chunk, kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
+                                  void* workspace, size_t workspace_bytes, void* stream)
+{
+    kda_status_t st = check_backward_shape(B, T, H, Dk, Dv, chunk, dtype);
+    if (st != KDA_OK) return st;
+    if (mode != KDA_MODE_KDA && mode != KDA_MODE_CKDA) return KDA_ERR_UNSUPPORTED;
+    if (flags & ~KDA_FLAG_STAGE_EVENTS) return KDA_ERR_UNSUPPORTED;
+    if (T > 0 && (!q || !k || !v || !alpha || !theta || !beta || !d_out || !dq || !dk || !dv ||
+                  !d_alpha || !d_theta || !d_beta))
+        return KDA_ERR_NULL_POINTER;
+    const IoType io = dtype == KDA_DTYPE_F32 ? IoType::F32 : IoType::BF16;
+    size_t xo[11];
+    const size_t ws_need = T == 0 ? 0 : backward_phase_layout(B, T, H, Dk, Dv, chunk, io, xo);
+    if (T > 0 && !workspace) return KDA_ERR_NULL_POINTER;
+    if (workspace_bytes < ws_need) return KDA_ERR_WORKSPACE_TOO_SMALL;
+
+    const size_t e = elem_size(dtype);
+    const size_t ntok = (size_t)B * T * H, np = (size_t)Dk / 2;
+    const size_t nstate = (size_t)B * H * Dk * Dv * 4;
+    const void* vec[] = {q, k, d_out, workspace};
+    for (const void* p : vec)
+        if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
+    const void* elt[] = {v, alpha, theta, beta, initial_state, d_final_state, dq, dk, dv,
+                         d_alpha, d_theta, d_beta, d_initial_state};
+    const uintptr_t ea[] = {e, 4, 4, 4, 4, 4, e, e, e, 4, 4, 4, 4};
+    for (int i = 0; i < 13; ++i)
+        if (elt[i] && !aligned(elt[i], ea[i])) return KDA_ERR_MISALIGNED;
+    struct R { const void* p; size_t n; };
+    const R in[] = {{q, ntok * Dk * e}, {k, ntok * Dk * e}, {v, ntok * Dv * e},
+                    {alpha, ntok * np * 4}, {theta, ntok * np * 4}, {beta, ntok * 4},
+                    {initial_state, initial_state ? nstate : 0}, {d_out, ntok * Dv * e},
+                    {d_final_state, d_final_state ? nstate : 0}};
+    const R outs[] = {{dq, ntok * Dk * e}, {dk, ntok * Dk * e}, {dv, ntok * Dv * e},
+                      {d_alpha, ntok * np * 4}, {d_theta, ntok * np * 4}, {d_beta, ntok * 4},
+                      {d_initial_state, d_initial_state ? nstate : 0}, {workspace, ws_need}};
+    constexpr int NO = sizeof(outs) / sizeof(outs[0]);
+    for (const R& o : outs)
+        for (const R& i : in)
+            if (overlaps(o.p, o.n, i.p, i.n)) return KDA_ERR_ALIAS;
+    for (int x = 0; x < NO; ++x)
+        for (int y = x + 1; y < NO; ++y)
+            if (overlaps(outs[x].p, outs[x].n, outs[y].p, outs[y].n)) return KDA_ERR_ALIAS;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    std::unique_lock<std::mutex> lock(g_stage.mu, std::defer_lock);
+    Recorder rec{(flags & KDA_FLAG_STAGE_EVENTS) != 0, s};
+    if (rec.on) {
+        lock.lock();
+        if (stage_begin() != hipSuccess) return KDA_ERR_HIP;
+    }
+    if (T == 0)
+        return backward_enqueue(nullptr, nullptr, nullptr, nullptr, nullptr, initial_state, nullptr,
+                                d_final_state, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                d_initial_state, B, T, H, Dk, Dv, chunk, dtype, mode, workspace,
+                                rec, s);
+    unsigned char* w = static_cast<unsigned char*>(workspace);
+    float* ar = reinterpret_cast<float*>(w + xo[2]);
+    float* dar = reinterpret_cast<float*>(w + xo[5]);
+    float* dstr = reinterpret_cast<float*>(w + xo[8]);
+    float* str = reinterpret_cast<float*>(w + xo[9]);
+    float* gT = reinterpret_cast<float*>(w + xo[10]);
+    const kda::PhaseArgs pa{q, k, alpha, theta, w + xo[0], w + xo[1], ar, w + xo[3], w + xo[4],
+                            dar, dq, dk, d_alpha, d_theta,
+                            reinterpret_cast<double*>(w + xo[6]),
+                            reinterpret_cast<double*>(w + xo[7]), d_final_state ? gT : nullptr,
+                            B, T, H, Dk / 2, kda::phase_blocks(T)};
+    auto stage = [&](int i, const char* name, const float* src, float* dst) -> bool {
+        return rec.mark(name) == hipSuccess &&
+               kda::launch_phase_bwd(i, io, pa, src, dst, gT, Dv, s) == hipSuccess &&
+               rec.done() == hipSuccess;
+    };
+    if (!stage(0, "phase_sums", nullptr, nullptr) || !stage(1, "phase_scan", nullptr, nullptr) ||
+        !stage(2, "phase_in", nullptr, nullptr))
+        return KDA_ERR_HIP;
+    if (d_final_state && !stage(3, "phase_state", d_final_state, dstr)) return KDA_ERR_HIP;
+    st = backward_enqueue(w + xo[0], w + xo[1], v, ar, beta, initial_state, d_out,
+                          d_final_state ? dstr : nullptr, w + xo[3], w + xo[4], dv, dar, d_beta,
+                          d_initial_state, B, T, H, Dk, Dv, chunk, dtype, mode, workspace, rec, s,
+                          nullptr, BwdPart::ALL, nullptr, d_final_state ? str : nullptr);
+    if (st != KDA_OK) return st;
+    if (d_final_state && !stage(4, "phase_final", dstr, str)) return KDA_ERR_HIP;
+    if (!stage(5, "phase_out", nullptr, nullptr) || !stage(6, "phase_suffix", nullptr, nullptr) ||
+        !stage(7, "phase_dtheta", nullptr, nullptr))
+        return KDA_ERR_HIP;
+    return KDA_OK;
 }
 
 // ---- scratch of kda_chunk_forward_noalloc -------------------------------------
@@ -1506,6 +1623,34 @@ kda_status_t kda_chunk_backward_workspace_size(int B, int T, int H, int Dk, int 
                     : backward_layout(B, T, H, Dk, Dv, chunk,
                                       dtype == KDA_DTYPE_F32 ? IoType::F32 : IoType::BF16, off, boff);
     return KDA_OK;
+}
+
+kda_status_t kda_chunk_backward_phase_workspace_size(int B, int T, int H, int Dk, int Dv, int chunk,
+                                                     kda_dtype_t dtype, size_t* bytes)
+{
+    if (!bytes) return KDA_ERR_NULL_POINTER;
+    const kda_status_t st = check_backward_shape(B, T, H, Dk, Dv, chunk, dtype);
+    if (st != KDA_OK) return st;
+    size_t xo[11];
+    *bytes = T == 0 ? 0
+                    : backward_phase_layout(B, T, H, Dk, Dv, chunk,
+                                            dtype == KDA_DTYPE_F32 ? IoType::F32 : IoType::BF16, xo);
+    return KDA_OK;
+}
+
+kda_status_t kda_chunk_backward_phase(const void* q, const void* k, const void* v,
+                                      const float* alpha, const float* theta, const float* beta,
+                                      const float* initial_state, const void* d_out,
+                                      const float* d_final_state, void* dq, void* dk, void* dv,
+                                      float* d_alpha, float* d_theta, float* d_beta,
+                                      float* d_initial_state, int B, int T, int H, int Dk, int Dv,
+                                      int chunk, kda_dtype_t dtype, kda_mode_t mode,
+                                      unsigned flags, void* workspace, size_t workspace_bytes,
+                                      void* stream)
+{
+    return chunk_backward_phase(q, k, v, alpha, theta, beta, initial_state, d_out, d_final_state,
+                                dq, dk, dv, d_alpha, d_theta, d_beta, d_initial_state, B, T, H, Dk,
+                                Dv, chunk, dtype, mode, flags, workspace, workspace_bytes, stream);
 }
 
 kda_status_t kda_chunk_backward(const void* q, const void* k, const void* v, const float* alpha,

@@ -106,6 +106,39 @@ hipError_t launch_backward_prologue(bool out, IoType io, int Dk, const ProArgs& 
 hipError_t launch_backward_stage(int stage, IoType io, const ChunkShape& s, const ChunkWorkspace& ws,
                                  const BwdChainArgs& ca, const BwdLocalArgs& la, hipStream_t stream);
 
+// The backward of the phase variant (phase_bwd.hip): the inputs, the rotated
+// inputs q', k' (io type) and per-channel gates alpha' (fp32) it forms, the
+// plain backward's gradients of those, the outputs, the per-block tables
+// [B H][NB + 1][P] (fp64: phases, then gradient sums) and the final-state
+// term of d L / d phi per (b, h, p) (null without d_final_state).  Stages,
+// one kernel each: 0 block sums of theta; 1 their prefix (the phases); 2 the
+// rotated inputs; 3 dS'_T = R(-phi_T) dS_T (src -> dst); 4 the final-state
+// term (src = dS'_T, dst = S'_T, into gT); 5 dq, dk, dalpha and the in-block
+// part of dtheta; 6 the suffix of the block totals; 7 dtheta completed.
+struct PhaseArgs {
+    const void* q;
+    const void* k;
+    const float* alpha;
+    const float* theta;
+    void* qr;
+    void* kr;
+    float* ar;
+    const void* dqr;
+    const void* dkr;
+    const float* dar;
+    void* dq;
+    void* dk;
+    float* dalpha;
+    float* dtheta;
+    double* tab;
+    double* tab2;
+    const float* gT;
+    int B, T, H, P, NB;
+};
+int phase_blocks(int T);   // 64-token blocks of a sequence of T tokens
+hipError_t launch_phase_bwd(int stage, IoType io, const PhaseArgs& a, const float* src, float* dst,
+                            float* gT, int Dv, hipStream_t stream);
+
 hipError_t launch_gate_prep(const float* alpha, float* L, uint8_t* meta, float* gend, int B,
                             int T, int H, int Dk, int C, hipStream_t stream);
 

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 17
+#define KDA_ABI_VERSION 18
 
 typedef enum {
     KDA_OK = 0,
@@ -499,6 +499,35 @@ kda_status_t kda_chunk_backward_saved(const void* q, const void* k, const void* 
                                       int B, int T, int H, int Dk, int Dv, int chunk,
                                       kda_dtype_t dtype, kda_mode_t mode, unsigned flags,
                                       void* saved, size_t saved_bytes, void* stream);
+
+/*
+ * Backward of kda_chunk_forward_phase ("Semidirect Fourier Delta Attention",
+ * §3 eq. (13): the decay of channel pair p is alpha_p R(theta_p)): the
+ * gradients of sum_t <o_t, d_out_t> + <S_T, d_final_state> with respect to q,
+ * k, v, alpha, theta, beta and initial_state.  With phi_t the running sum of
+ * a pair's phases over the sequence, the variant is the plain recurrence on q
+ * and k rotated pair by pair by -phi_t with alpha_p on both channels of the
+ * pair, its final state rotated back by phi_T; the call forms those inputs
+ * (rounded to dtype), runs the plain backward on them and maps its gradients
+ * back: dq_t, dk_t rotated by phi_t, the pair's two channel gradients summed
+ * into d_alpha, and d_theta_s the sum over t >= s of the derivative of the
+ * loss in phi_t.
+ *   alpha, theta, d_alpha, d_theta : [B,T,H,Dk/2] fp32 (the forward's layout);
+ *   every other argument, layout, rule and status code as kda_chunk_backward;
+ *   workspace: at least kda_chunk_backward_phase_workspace_size bytes.
+ * theta == NULL or d_theta == NULL with T > 0 is KDA_ERR_NULL_POINTER.
+ */
+kda_status_t kda_chunk_backward_phase_workspace_size(int B, int T, int H, int Dk, int Dv,
+                                                     int chunk, kda_dtype_t dtype, size_t* bytes);
+kda_status_t kda_chunk_backward_phase(const void* q, const void* k, const void* v,
+                                      const float* alpha, const float* theta, const float* beta,
+                                      const float* initial_state, const void* d_out,
+                                      const float* d_final_state, void* dq, void* dk, void* dv,
+                                      float* d_alpha, float* d_theta, float* d_beta,
+                                      float* d_initial_state, int B, int T, int H, int Dk, int Dv,
+                                      int chunk, kda_dtype_t dtype, kda_mode_t mode,
+                                      unsigned flags, void* workspace, size_t workspace_bytes,
+                                      void* stream);
 
 /*
  * Backward of kda_chunk_forward_prologue: the same loss gradients with respect

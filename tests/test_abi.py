@@ -53,7 +53,7 @@ def test_side_stream_helpers_refuse_null(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kda_abi_version() == 17
+    assert lib.kda_abi_version() == 18
     for s in range(10):
         assert lib.kda_status_string(s) != b"unknown status"
     assert lib.kda_status_string(99) == b"unknown status"
@@ -569,3 +569,45 @@ def test_side_stream_refusals_before_any_hip_call(lib):
     assert call(side) == NULLP                     # an event missing
     side.events[3] = f()
     assert call(side, D=24) == UNSUP               # the shape check still comes first
+
+
+def test_backward_phase_validation(lib):
+    """kda_chunk_backward_phase: the backward's supported set, theta and
+    d_theta required, the pair-sized gate arrays in the alias checks."""
+    f = Fake()
+    n = ctypes.c_size_t(0)
+    assert lib.kda_chunk_backward_phase_workspace_size(1, 64, 2, 64, 64, 64, F32, ctypes.byref(n)) == OK
+    need = n.value
+    m = ctypes.c_size_t(0)
+    lib.kda_chunk_backward_workspace_size(1, 64, 2, 64, 64, 64, F32, ctypes.byref(m))
+    assert need > m.value                       # the rotated inputs, their gradients, the tables
+    z = ctypes.c_size_t(1)
+    assert lib.kda_chunk_backward_phase_workspace_size(1, 0, 2, 64, 64, 64, F32, ctypes.byref(z)) == OK
+    assert z.value == 0
+    assert lib.kda_chunk_backward_phase_workspace_size(1, 64, 2, 16, 64, 64, F32, ctypes.byref(z)) == UNSUP
+
+    def bp(ptrs=None, T=64, Dk=64, chunk=64, mode=1, flags=0, ws=True, wsb=None):
+        p = ptrs if ptrs is not None else [f() for _ in range(16)]
+        return lib.kda_chunk_backward_phase(*p, 1, T, 2, Dk, 64, chunk, F32, mode, flags,
+                                            f(need + 4096) if ws else None,
+                                            need if wsb is None else wsb, None)
+
+    # q k v alpha theta beta S0 dO dST dq dk dv dalpha dtheta dbeta dS0
+    base = [f() for _ in range(16)]
+    for i in (0, 3, 4, 7, 9, 12, 13, 14):
+        assert bp(ptrs=base[:i] + [None] + base[i + 1:]) == NULLP, i
+    assert bp(ws=False) == NULLP
+    assert bp(wsb=need - 1) == WS
+    assert bp(chunk=16) == UNSUP
+    assert bp(Dk=16) == UNSUP
+    assert bp(mode=2) == UNSUP
+    assert bp(flags=4) == UNSUP
+    al = list(base)
+    al[13] = base[4]                                              # d_theta == theta
+    assert bp(ptrs=al) == ALIAS
+    al = list(base)
+    al[12] = base[13]                                             # d_alpha == d_theta
+    assert bp(ptrs=al) == ALIAS
+    opt = list(base)
+    opt[8] = opt[15] = None
+    assert bp(ptrs=opt, T=0) == OK                                # nothing to do, no HIP call
