@@ -11,9 +11,11 @@ non-default stream of ours.  Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-others] [--no-cpu]
                   [--backward] [--decode] [--gate-prep] [--copy-probe] [--mfma-probe]
-                  [--streamed]
+                  [--streamed] [--settle SECONDS]
 
-Timing: W untimed calls, then K calls back to back, each bracketed by HIP
+Timing: untimed calls for --settle seconds (default 0.25: a fresh process
+sees the device below its sustained clocks for about its first 100 calls),
+then W untimed calls, then K calls back to back, each bracketed by HIP
 events on the launch stream; ms_per_step is the median call.  The roofline
 object describes the whole call: its algorithmic bytes (read q, k, v, alpha,
 beta, S0 once; write o and S_T once; intermediates excluded) over the median
@@ -100,11 +102,28 @@ def chunk_flops(w):
     return w.B * w.T * w.H * per_tok
 
 
-def time_forward(kda, torch, w, inp, steps, warmup, extra_flags=0, side=None):
+def settle(torch, call, seconds):
+    """Run `call` back to back for about `seconds` of wall time before the
+    warm-up calls: a freshly started process sees the device below its
+    sustained clocks for its first ~100 headline calls (per-call medians
+    310-348 us over calls 0-20, 297 over calls 50-100, 289 from call 100 on).
+    Untimed; returns the number of calls made."""
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            call()
+        n += 10
+        torch.cuda.synchronize()
+    return n
+
+
+def time_forward(kda, torch, w, inp, steps, warmup, extra_flags=0, side=None, settle_s=0.0, info=None):
     # (on the current stream: main() makes it a non-default one)
     """Median and mean ms per kda_chunk_forward call (each call bracketed by
     events on the launch stream) and the mean duration of every kernel (a
-    separate pass with the library's per-launch events)."""
+    separate pass with the library's per-launch events).  With settle_s > 0
+    the device is first brought to its sustained clocks (settle()); the
+    number of those untimed calls goes to info["settle_calls"]."""
     stream = torch.cuda.current_stream()
     ws = torch.empty(kda.workspace_size(w.B, w.T, w.H, w.Dk, w.Dv, w.chunk, w.dtype),
                      dtype=torch.uint8, device="cuda")
@@ -116,6 +135,10 @@ def time_forward(kda, torch, w, inp, steps, warmup, extra_flags=0, side=None):
                           chunk=w.chunk, mode=w.mode, out=out, final_state=st, workspace=ws,
                           stream=stream, flags=flags | extra_flags, side=side)
 
+    if settle_s > 0:
+        n = settle(torch, call, settle_s)
+        if info is not None:
+            info["settle_calls"] = n
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -352,6 +375,9 @@ def main():
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--mfma-probe", action="store_true",
                     help="also measure the dense MFMA peak rates (bf16 and fp32)")
+    ap.add_argument("--settle", type=float, default=0.25,
+                    help="seconds of untimed headline calls before the warm-up calls, so the "
+                         "device runs at its sustained clocks (0: none)")
     ap.add_argument("--streamed", action="store_true",
                     help="time the streamed kda_chunk_forward_side call as the headline (not "
                          "under rocprofv3 counter passes, which run one dispatch at a time: the "
@@ -375,11 +401,14 @@ def main():
     # stream's work: the overlapped forms need a non-default launch stream)
     torch.cuda.set_stream(torch.cuda.Stream())
     side = kda.SideStream()
+    tinfo = {}
     if args.streamed:
         ms, mean_ms, per, out, st = time_forward(kda, torch, w, inp, args.steps, args.warmup,
-                                                 extra_flags=kda.STREAMED, side=side)
+                                                 extra_flags=kda.STREAMED, side=side,
+                                                 settle_s=args.settle, info=tinfo)
     else:
-        ms, mean_ms, per, out, st = time_forward(kda, torch, w, inp, args.steps, args.warmup)
+        ms, mean_ms, per, out, st = time_forward(kda, torch, w, inp, args.steps, args.warmup,
+                                                 settle_s=args.settle, info=tinfo)
     tokens = w.B * w.T
     io_bytes = 2
     ab = algorithmic_bytes(w, io_bytes, inp["S0"] is not None, True)
@@ -417,6 +446,7 @@ def main():
                      "traffic_ratio": (traffic_total / ab["path"]) if traffic_total else None,
                      "mfma_bf16_frac": chunk_flops(w) / (ms / 1e3) / 1e12 / MFMA_BF16_TFLOPS},
         "timing": {"median_ms": ms, "mean_ms": mean_ms, "calls": args.steps,
+                   "settle_s": args.settle, "settle_calls": tinfo.get("settle_calls", 0),
                    "call": "kda_chunk_forward_side, KDA_FLAG_STREAMED" if args.streamed
                            else "kda_chunk_forward (two-pass)"},
         "kernels": kernels,
