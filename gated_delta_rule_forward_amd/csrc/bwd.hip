@@ -260,24 +260,38 @@ __global__ __launch_bounds__(kRevThreads) void bwd_chain_fifo_kernel(BwdChainArg
 
     if (wave >= 4) {
         // ---- loader wavefront ---------------------------------------------------
+        // each column slice issues its runs of the shared blocks from another
+        // starting run (dma_runs_rot)
         auto issue_a = [&](unsigned char* st, size_t unit) {
             const int mt = cw < G::NM ? cw : G::NM - 1;
-            dma_run<G::NKC * L::FB>(static_cast<const unsigned char*>(a.PT) +
-                                        (unit * C * C + (size_t)mt * G::NKC * 64 * G::NV) * sizeof(T),
-                                    st + L::OPT, lane);
-            dma_run<G::NKD * L::FB>(static_cast<const unsigned char*>(a.Ktil) +
-                                        (unit * C * DK + (size_t)mt * G::NKD * 64 * G::NV) * sizeof(T),
-                                    st + L::OKT, lane);
+            const unsigned char* pt = static_cast<const unsigned char*>(a.PT) +
+                                      (unit * C * C + (size_t)mt * G::NKC * 64 * G::NV) * sizeof(T);
+            const unsigned char* kt = static_cast<const unsigned char*>(a.Ktil) +
+                                      (unit * C * DK + (size_t)mt * G::NKD * 64 * G::NV) * sizeof(T);
+            if constexpr ((G::NKC * L::FB) % 1024 == 0 && (G::NKD * L::FB) % 1024 == 0) {
+                dma_pair_rot<G::NKC * L::FB, G::NKD * L::FB>(pt, st + L::OPT, kt, st + L::OKT, lane, slice);
+            } else {
+                dma_run<G::NKC * L::FB>(pt, st + L::OPT, lane);
+                dma_run<G::NKD * L::FB>(kt, st + L::OKT, lane);
+            }
         };
         auto issue_b = [&](unsigned char* st, size_t unit) {
+            const unsigned char* bs[2 * G::SPW];
+            unsigned char* bd[2 * G::SPW];
 #pragma unroll
             for (int u = 0; u < G::SPW; ++u) {
                 const int t = min(cw + 4 * u, G::NT - 1);
                 const size_t off = (unit * DK * C + (size_t)t * G::NKC * 64 * G::NV) * sizeof(T);
-                dma_run<G::NKC * L::FB>(static_cast<const unsigned char*>(a.QGT) + off,
-                                        st + L::OQT + u * G::NKC * L::FB, lane);
-                dma_run<G::NKC * L::FB>(static_cast<const unsigned char*>(a.WT) + off,
-                                        st + L::OWT + u * G::NKC * L::FB, lane);
+                bs[2 * u] = static_cast<const unsigned char*>(a.QGT) + off;
+                bd[2 * u] = st + L::OQT + u * G::NKC * L::FB;
+                bs[2 * u + 1] = static_cast<const unsigned char*>(a.WT) + off;
+                bd[2 * u + 1] = st + L::OWT + u * G::NKC * L::FB;
+            }
+            if constexpr ((G::NKC * L::FB) % 1024 == 0) {
+                dma_runs_rot<2 * G::SPW, G::NKC * L::FB>(bs, bd, lane, slice);
+            } else {
+#pragma unroll
+                for (int x = 0; x < 2 * G::SPW; ++x) dma_run<G::NKC * L::FB>(bs[x], bd[x], lane);
             }
             // Gamma_C: lane j < 4 SPW fetches rows 16t + 4(j % 4) .. +3 of state
             // tile u = j / 4; they land at OG + 16 j

@@ -94,22 +94,43 @@ __device__ __forceinline__ void issue_chunk(unsigned char* st, const ChainArgs& 
     const int Dv = a.Dv;
     if constexpr (PART == 0) {
         const size_t off = (unit * C * DK + (size_t)mt * G::NKD * 64 * (G::KB / 4)) * sizeof(T);
-        dma_run<G::NKD * G::FB>(static_cast<const unsigned char*>(a.W) + off, st + G::OW, lane);
-        dma_run<G::NKD * G::FB>(static_cast<const unsigned char*>(a.QG) + off, st + G::OQ, lane);
+        if constexpr ((G::NKD * G::FB) % 1024 == 0) {
+            const unsigned char* const s2[2] = {static_cast<const unsigned char*>(a.W) + off,
+                                                static_cast<const unsigned char*>(a.QG) + off};
+            unsigned char* const d2[2] = {st + G::OW, st + G::OQ};
+            dma_runs_rot<2, G::NKD * G::FB>(s2, d2, lane, slice);
+        } else {
+            dma_run<G::NKD * G::FB>(static_cast<const unsigned char*>(a.W) + off, st + G::OW, lane);
+            dma_run<G::NKD * G::FB>(static_cast<const unsigned char*>(a.QG) + off, st + G::OQ, lane);
+        }
     } else if constexpr (PART == 1) {
         const unsigned char* P = static_cast<const unsigned char*>(a.P) +
                                  (unit * C * C + (size_t)mt * G::NKC * 64 * (G::KB / 4)) * sizeof(T);
         const unsigned char* U = reinterpret_cast<const unsigned char*>(
             static_cast<const T*>(a.U) + unit * C * Dv + (size_t)(mt * (Dv / 16) + slice) * 64 * 4);
-        dma_run<G::NKC * G::FB>(P, st + G::OP, lane);
+        if constexpr ((G::NKC * G::FB) % 1024 == 0) {
+            const unsigned char* const s1[1] = {P};
+            unsigned char* const d1[1] = {st + G::OP};
+            dma_runs_rot<1, G::NKC * G::FB>(s1, d1, lane, slice);
+        } else {
+            dma_run<G::NKC * G::FB>(P, st + G::OP, lane);
+        }
         dma_run<G::UB>(U, st + G::OU, lane);
     } else {
+        const unsigned char* ks[G::SPW];
+        unsigned char* kd[G::SPW];
 #pragma unroll
         for (int u = 0; u < G::SPW; ++u) {
             const int t = (wave + 4 * u) < G::NT ? wave + 4 * u : G::NT - 1;
-            const unsigned char* Kt = static_cast<const unsigned char*>(a.Kt) +
-                                      (unit * DK * C + (size_t)t * G::NKC * 64 * (G::KB / 4)) * sizeof(T);
-            dma_run<G::NKC * G::FB>(Kt, st + G::OK + u * G::NKC * G::FB, lane);
+            ks[u] = static_cast<const unsigned char*>(a.Kt) +
+                    (unit * DK * C + (size_t)t * G::NKC * 64 * (G::KB / 4)) * sizeof(T);
+            kd[u] = st + G::OK + u * G::NKC * G::FB;
+        }
+        if constexpr ((G::NKC * G::FB) % 1024 == 0) {
+            dma_runs_rot<G::SPW, G::NKC * G::FB>(ks, kd, lane, slice);
+        } else {
+#pragma unroll
+            for (int u = 0; u < G::SPW; ++u) dma_run<G::NKC * G::FB>(ks[u], kd[u], lane);
         }
         // Gamma_C: lane j < 4 SPW fetches rows 16t + 4(j % 4) .. +3 of state tile
         // u = j / 4; they land at OG + 16 j
