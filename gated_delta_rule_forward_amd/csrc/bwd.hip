@@ -578,7 +578,14 @@ __global__ __launch_bounds__(kLocalThreads) void bwd_local_kernel(BwdLocalArgs a
     constexpr int DKA = G::DKA, DKT = G::DKT;
 
     const int Dv = a.Dv, H = a.H, NVT = Dv / 16;
-    const size_t unit = blockIdx.x;
+    // dense batches: chunk index by chunk index, every (b, h) of one chunk
+    // index on consecutive workgroups, so the workgroups in flight read whole
+    // token rows of q, k, v, dO and alpha
+    size_t unit = blockIdx.x;
+    if (!a.cu) {
+        const int bhn = (int)gridDim.x / a.NC;
+        unit = (size_t)((int)blockIdx.x % bhn) * a.NC + (int)blockIdx.x / bhn;
+    }
     const UnitPos up = locate_unit((int)unit, H, a.T, a.NC, C, a.cu, a.cs, a.N);
     if (!up.valid) {                  // past the last sequence of a packed batch
         if (threadIdx.x == 0) a.FLB[unit] = 0;
