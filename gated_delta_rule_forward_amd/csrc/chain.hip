@@ -70,12 +70,13 @@ struct ChainGeom {
     static constexpr size_t LDS_TOTAL = SINK + 1024;
     // L2 prefetch: 1 KB pieces of a chunk's blocks shared by the column slices
     // (W, Q * Gamma, Ktil, P; only when whole kilobytes), plus each slice's U
-    // tiles; KPF prefetch loads per loader wavefront and step
+    // tiles; KPF prefetch loads per loader wavefront and step (one: with the
+    // rotated run order of the operand loads, two or three were slower)
     static constexpr int PW = C * DK * (int)sizeof(T) / 1024, PP = C * C * (int)sizeof(T) / 1024;
     static constexpr bool PREFETCH =
         (C * DK * (int)sizeof(T)) % 1024 == 0 && (C * C * (int)sizeof(T)) % 1024 == 0;
     static constexpr int PTOT = 3 * PW + PP;
-    static constexpr int KPF = PREFETCH ? 2 : 0;
+    static constexpr int KPF = PREFETCH ? 1 : 0;
     static_assert(NDMA <= 63, "vmcnt holds at most 63 outstanding loads");
 };
 
