@@ -78,6 +78,13 @@ struct ChainGeom {
     static constexpr int PTOT = 3 * PW + PP;
     static constexpr int KPF = PREFETCH ? 1 : 0;
     static_assert(NDMA <= 63, "vmcnt holds at most 63 outstanding loads");
+    // P (token tile mt's rows) is zero in the k blocks past its diagonal
+    // block: with one 1 KB run per k block those runs are not loaded, and the
+    // fragments are set to zero instead (the same MFMA products)
+    static constexpr bool PSKIP = FB == 1024;
+    __device__ static constexpr int nkp(int mt) {
+        return PSKIP ? ((16 * (mt + 1) + KB - 1) / KB < NKC ? (16 * (mt + 1) + KB - 1) / KB : NKC) : NKC;
+    }
 };
 
 
@@ -109,7 +116,18 @@ __device__ __forceinline__ void issue_chunk(unsigned char* st, const ChainArgs& 
                                  (unit * C * C + (size_t)mt * G::NKC * 64 * (G::KB / 4)) * sizeof(T);
         const unsigned char* U = reinterpret_cast<const unsigned char*>(
             static_cast<const T*>(a.U) + unit * C * Dv + (size_t)(mt * (Dv / 16) + slice) * 64 * 4);
-        if constexpr ((G::NKC * G::FB) % 1024 == 0) {
+        if constexpr (G::PSKIP) {
+            // the k blocks up to the diagonal block, from another run per slice
+            const int np = G::nkp(mt), r0 = slice % np;
+#pragma unroll
+            for (int i = 0; i < G::NKC; ++i) {
+                if (i < np) {
+                    int j = i + r0;
+                    if (j >= np) j -= np;
+                    dma16(P + j * 1024 + 16 * lane, st + G::OP + j * 1024);
+                }
+            }
+        } else if constexpr ((G::NKC * G::FB) % 1024 == 0) {
             const unsigned char* const s1[1] = {P};
             unsigned char* const d1[1] = {st + G::OP};
             dma_runs_rot<1, G::NKC * G::FB>(s1, d1, lane, slice);
@@ -198,7 +216,7 @@ struct ChainOps {
 };
 
 template <typename T, int C, int DK>
-__device__ __forceinline__ void read_ops(ChainOps<T, C, DK>& o, const unsigned char* st, int lane, int lg)
+__device__ __forceinline__ void read_ops(ChainOps<T, C, DK>& o, const unsigned char* st, int lane, int lg, int np)
 {
     using G = ChainGeom<T, C, DK>;
     using F = Frag<T, G::KB>;
@@ -209,7 +227,10 @@ __device__ __forceinline__ void read_ops(ChainOps<T, C, DK>& o, const unsigned c
     }
 #pragma unroll
     for (int s = 0; s < G::NKC; ++s)
-        o.p[s] = *reinterpret_cast<const F*>(st + G::OP + s * G::FB + lane * sizeof(F));
+    {
+        const float zf[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        o.p[s] = s < np ? *reinterpret_cast<const F*>(st + G::OP + s * G::FB + lane * sizeof(F)) : F::from(zf);
+    }
     {
         const Vec4<T> u4 = *reinterpret_cast<const Vec4<T>*>(st + G::OU + lane * 4 * sizeof(T));
         o.u = f32x4{u4.get(0), u4.get(1), u4.get(2), u4.get(3)};
@@ -298,7 +319,13 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
         prefetch_chunk<T, C, DK>(a, u0 + min(3, last), slice, NS, cw, lane, sink);
         issue_all<T, C, DK>(stg(1), a, u0 + min(1, last), cw, lane, slice);
         prefetch_chunk<T, C, DK>(a, u0 + min(4, last), slice, NS, cw, lane, sink);
-        wait_vm<G::NDMA + 3 * G::KPF>();             // chunk 0 landed
+        // chunk 0 landed: its loads are followed by chunk 1's and three prefetches
+        switch (G::NKC - G::nkp(cw < G::NM ? cw : G::NM - 1)) {
+        case 0: wait_vm<G::NDMA + 3 * G::KPF>(); break;
+        case 1: wait_vm<G::NDMA - 1 + 3 * G::KPF>(); break;
+        case 2: wait_vm<G::NDMA - 2 + 3 * G::KPF>(); break;
+        default: wait_vm<G::NDMA - 3 + 3 * G::KPF>(); break;
+        }
         lds_barrier();                               // B0: compute reads chunk 0
         lds_barrier();                               // B1: stage 0 free
         constexpr int N0 = 2 * G::runs(G::NKD * G::FB);   // loads of part 0
@@ -337,8 +364,9 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
     }
 
     ChainOps<T, C, DK> cur;
+    const int npw = G::nkp(wave < G::NM ? wave : G::NM - 1);   // nonzero P k blocks
     lds_barrier();                                   // B0: chunk 0 is in stage 0
-    read_ops<T, C, DK>(cur, stg(0), lane, lg);
+    read_ops<T, C, DK>(cur, stg(0), lane, lg, npw);
     lds_barrier();                                   // B1: stage 0 may be refilled
 
     T* out = static_cast<T*>(a.out);
@@ -445,7 +473,7 @@ __global__ __launch_bounds__(kChainThreads) void chain_kernel(ChainArgs a)
 #pragma unroll
         for (int s = 0; s < G::NKC; ++s) { pp[s] = cur.p[s]; pdf[s] = df[s]; }
         // next chunk's operands (its loader waited for them before barrier 1)
-        read_ops<T, C, DK>(cur, stg(nc + 1), lane, lg);
+        read_ops<T, C, DK>(cur, stg(nc + 1), lane, lg, npw);
         lds_barrier();
     }
     emit(NC - 1);
